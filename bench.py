@@ -1,0 +1,250 @@
+"""Decode-step weight-stream benchmark on one MI355X.
+
+One step = one pass of the single-token weight stream of the 4.5-bpw GEMV
+workload: y_up = W_up x_up (Q45, 12288 x 4096) and y_down = W_down x_down
+(Q65, 4096 x 12288), M = 1.  Weights rotate over >= 1 GiB of identical
+copies at distinct addresses, so no step can be served from the 256 MB
+Infinity Cache.  `value` is algorithmic bytes of the step / step time.
+
+Also measured in the same run and reported beside the headline:
+  * per-kernel average durations (HIP events on the launch stream);
+  * microseconds per 4096-wide RMSNorm row (one row per launch);
+  * the memory ceiling measured by a 4 GiB read probe;
+  * the CPU oracle on a bounded sample of the same step (cpu_baseline),
+    which also checks the GPU result on that sample before it is reported.
+
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "achieved HBM GB/s (% of peak) for M=1 4.5-bpw GEMV; µs per 4096 RMSNorm row"
+PEAK_HBM_GBS = 8000.0           # MI355X published HBM3E bandwidth
+ROTATION_BYTES = 1 << 30        # >= 4x the 256 MB Infinity Cache
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_m1.json")
+KERNEL_SOURCES = ["formats.h", "gemv_m1.hip", "device_common.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "memory_bound_quantized_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def gemv_bytes(W) -> int:
+    """Algorithmic bytes of one M=1 product: every weight byte once, x, y."""
+    return W.nbytes + 4 * W.K + 4 * W.N
+
+
+def traffic_for(kernel_key: str):
+    """HBM bytes per launch from committed rocprofv3 counters, if they were
+    taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    ent = t.get("kernels", {}).get(kernel_key)
+    return None if ent is None else ent.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, y_up_gpu, y_down_gpu, budget_s: float = 15.0):
+    """The oracle on a bounded sample of the step, on the host cores."""
+    import oracle
+    threads = max(1, min(16, os.cpu_count() or 1))
+    fmt_u, N_u, K_u, p_u = cfg["up"]
+    fmt_d, N_d, K_d, p_d = cfg["down"]
+    Wu = oracle.Planes(fmt_u, N_u, K_u, p_u)
+    Wd = oracle.Planes(fmt_d, N_d, K_d, p_d)
+    # sample: the first 1/8 of each table's rows, one pass each
+    ru, rd = N_u // 8, N_d // 8
+    import concurrent.futures as cf
+    L = oracle.lib()
+
+    def rows_job(W, x, y, r0, r1):
+        L.oracle_gemv(W.fmt, W.cptr, W.N, W.K, x.ctypes.data, 1, W.K, y.ctypes.data, W.N, 0, r0, r1)
+
+    xu = np.ascontiguousarray(cfg["x_up"], np.float32)
+    xd = np.ascontiguousarray(cfg["x_down"], np.float32)
+    yu = np.zeros(N_u, np.float32)
+    yd = np.zeros(N_d, np.float32)
+    reps, t_total = 0, 0.0
+    while True:
+        t0 = time.perf_counter()
+        with cf.ThreadPoolExecutor(threads) as ex:
+            bu = np.linspace(0, ru, threads + 1).astype(int)
+            bd = np.linspace(0, rd, threads + 1).astype(int)
+            futs = [ex.submit(rows_job, Wu, xu, yu, int(bu[i]), int(bu[i + 1])) for i in range(threads)]
+            futs += [ex.submit(rows_job, Wd, xd, yd, int(bd[i]), int(bd[i + 1])) for i in range(threads)]
+            for f in futs:
+                f.result()
+        t_total += time.perf_counter() - t0
+        reps += 1
+        if t_total >= budget_s or reps >= 50:
+            break
+    table_u = sum(p.nbytes for p in p_u if p is not None)
+    table_d = sum(p.nbytes for p in p_d if p is not None)
+    sample_bytes = table_u * ru // N_u + table_d * rd // N_d + 4 * (K_u + K_d + ru + rd)
+    gbs = sample_bytes * reps / t_total / 1e9
+
+    def rel(a, b):
+        a = np.asarray(a, np.float64)
+        b = np.asarray(b, np.float64)
+        return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+    err_u = rel(y_up_gpu[:ru], yu[:ru])
+    err_d = rel(y_down_gpu[:rd], yd[:rd])
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "rows [0, N/8) of both tables (%d of %d Q45 rows, %d of %d Q65 rows), "
+                      "%d passes in %.1f s, fp64 oracle, row-parallel over %d threads"
+                      % (ru, N_u, rd, N_d, reps, t_total, threads),
+            "checked_rel_l2": {"q45_up": err_u, "q65_down": err_d}}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(every box has one MI355X); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import memory_bound_quantized_amd as mbq
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    cfg = workloads.config2()
+    fu, Nu, Ku, pu = cfg["up"]
+    fd, Nd, Kd, pd = cfg["down"]
+    W_up0 = mbq.QWeight.from_host(fu, Nu, Ku, pu)
+    W_dn0 = mbq.QWeight.from_host(fd, Nd, Kd, pd)
+    per_copy = W_up0.nbytes + W_dn0.nbytes
+    ncopy = max(2, -(-ROTATION_BYTES // per_copy))
+    ups = [W_up0] + [W_up0.clone() for _ in range(ncopy - 1)]
+    dns = [W_dn0] + [W_dn0.clone() for _ in range(ncopy - 1)]
+    x_up = torch.from_numpy(cfg["x_up"]).to(dev)
+    x_dn = torch.from_numpy(cfg["x_down"]).to(dev)
+    y_up = torch.empty(Nu, device=dev)
+    y_dn = torch.empty(Nd, device=dev)
+
+    def step(i):
+        mbq.gemv_q(ups[i % ncopy], x_up, out=y_up)
+        mbq.gemv_q(dns[i % ncopy], x_dn, out=y_dn)
+
+    # warmup (also the first result that the CPU leg checks)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    y_up_first = y_up.cpu().numpy().copy()
+    y_dn_first = y_dn.cpu().numpy().copy()
+
+    # timed region: K steps, events around every launch on the launch stream
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        e = ev[i]
+        e[0].record(stream)
+        mbq.gemv_q(ups[i % ncopy], x_up, out=y_up)
+        e[1].record(stream)
+        mbq.gemv_q(dns[i % ncopy], x_dn, out=y_dn)
+        e[2].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    up_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    dn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    ms_per_step = total_ms / args.steps
+    b_up, b_dn = gemv_bytes(W_up0), gemv_bytes(W_dn0)
+    value = (b_up + b_dn) / (ms_per_step * 1e-3) / 1e9
+
+    # RMSNorm of one 4096-wide row (the metric's second part), one row per launch
+    c1 = workloads.config1()
+    xr = torch.from_numpy(c1["x"]).to(dev)
+    gr = torch.from_numpy(c1["gamma"]).to(dev)
+    yr = torch.empty_like(xr)
+    for _ in range(20):
+        mbq.rmsnorm(xr, gr, c1["eps"], out=yr)
+    nrep = 200
+    en = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nrep)]
+    torch.cuda.synchronize()
+    for a, b in en:
+        a.record(stream)
+        mbq.rmsnorm(xr, gr, c1["eps"], out=yr)
+        b.record(stream)
+    torch.cuda.synchronize()
+    rms_us = float(np.median([a.elapsed_time(b) for a, b in en])) * 1e3
+
+    # measured memory ceiling: 4 GiB read, best of 5
+    buf = torch.empty(1 << 32, dtype=torch.uint8, device=dev)
+    sink = torch.empty(4096, device=dev)
+    mbq.probe_read(buf, sink)
+    best = 0.0
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        mbq.probe_read(buf, sink)
+        b.record(stream)
+        torch.cuda.synchronize()
+        best = max(best, buf.numel() / (a.elapsed_time(b) * 1e-3) / 1e9)
+    del buf
+
+    kern = {"q45_up_12288x4096": (b_up, up_ms), "q65_down_4096x12288": (b_dn, dn_ms)}
+    dom = max(kern, key=lambda k: kern[k][1])
+    d_bytes, d_ms = kern[dom]
+    achieved = d_bytes / (d_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": traffic_for(dom), "algorithmic_bytes_per_launch": d_bytes,
+                "avg_launch_us": round(d_ms * 1e3, 3)}
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "M=1 GEMV: Q45 12288x4096 (4.5 bpw) + Q65 4096x12288 (6.5625 bpw), "
+                               "fp32 x and accumulation, weights rotated over %d copies (%.2f GB)"
+                               % (ncopy, ncopy * per_copy / 1e9),
+                   "global_batch": 1, "seq_len": 1, "parallelism": "none"},
+        "roofline": roofline,
+        "kernels": {k: {"avg_us": round(v[1] * 1e3, 3), "gbs": round(v[0] / (v[1] * 1e-3) / 1e9, 1),
+                        "frac_of_peak": round(v[0] / (v[1] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+                    for k, v in kern.items()},
+        "rmsnorm_us_per_4096_row": round(rms_us, 3),
+        "measured_read_peak_gbs": round(best, 1),
+        "q45_frac_of_measured_peak": round(b_up / (up_ms * 1e-3) / 1e9 / best, 4),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, y_up_first, y_dn_first)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,202 @@
+/*
+ * mbq.h -- C ABI of libmbq: the single-token / small-batch decode step on
+ * AMD Instinct MI355X (gfx950).  Block-quantized weights are streamed through
+ * matrix-vector products and dequantized in registers; RMSNorm and two-pass
+ * LayerNorm reduce rows cooperatively.
+ *
+ * Sources (web pages, cited by short tag and section):
+ *   [one-serial-kernel]  vocodex.ai, "From 22.8 to 42.8 tokens a second
+ *                        without touching a matrix multiply"
+ *   [mountain-runs]      coderlegion.com S-MoE diary #5, "The Mountain Runs"
+ *   [roofline-holds]     research.arkey.ai, "The roofline holds on a second GPU"
+ *
+ * Conventions for every entry point
+ *   - Plain C types only.  Pointers documented as "device" must point to GPU
+ *     memory the caller allocated; "host" pointers to CPU memory.  The library
+ *     never allocates or frees memory and keeps no state between calls beyond
+ *     its loaded code objects and a thread-local error string.
+ *   - Device work is enqueued asynchronously on `stream` (a hipStream_t cast
+ *     to void*; NULL selects the default stream).  Errors raised while a
+ *     kernel runs surface at the caller's next synchronisation.
+ *   - Arguments are checked on the host before anything is enqueued.  A
+ *     non-zero return means nothing was enqueued, except MBQ_EHIP, which
+ *     reports a failed launch.  mbq_last_error() gives the detail.
+ *   - Matrices are row-major.  A weight matrix W is N x K (N output rows,
+ *     K inputs); its blocks run along K and never span two rows.
+ *   - No C++ exception crosses this boundary.
+ */
+#ifndef MBQ_H
+#define MBQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------------ status */
+#define MBQ_OK            0
+#define MBQ_EINVAL       (-1) /* null pointer, bad format, bad shape or stride, overlap */
+#define MBQ_EALIGN       (-2) /* a pointer lacks the alignment stated below           */
+#define MBQ_EUNSUPPORTED (-3) /* valid request this build has no kernel for            */
+#define MBQ_EHIP         (-4) /* the HIP runtime reported an error at launch           */
+
+/* ----------------------------------------------------------------- formats
+ * Byte budgets per weight follow [roofline-holds] "The Math" (4.5 and 6.5625
+ * bits per weight, scales counted) and "The search space" (256 weights in
+ * 144 and in 210 bytes); 2- and 4-bit codes are unpacked in registers and
+ * never written out unpacked ([mountain-runs] section 3; [roofline-holds]
+ * "Hiding, fusing, and keeping the sums busy", Dtypes).  The block structure
+ * and bit order are this library's definition of those budgets.
+ *
+ * Every format is stored as up to four planes, each row-major over rows n:
+ *   plane 0 "codes", plane 1 "codes_hi", plane 2 "scales",
+ *   plane 3 "super_scales" (unused planes are NULL).
+ *
+ * MBQ_FMT_BF16  16 bits/weight.  codes: uint16 [N][K], w = float(word << 16).
+ * MBQ_FMT_Q45   4.5 bits/weight, blocks of 32.
+ *               codes:  uint8 [N][K/2]; weight k is nibble (k & 1) of byte
+ *                       k >> 1, low nibble first; q in 0..15
+ *               scales: fp16 [N][K/32];  w = s[k >> 5] * (q - 8)
+ * MBQ_FMT_Q65   6.5625 bits/weight, sub-blocks of 16, super-blocks of 256.
+ *               codes:    uint8 [N][K/2], low 4 bits of q, nibble order as Q45
+ *               codes_hi: uint8 [N][K/4], high 2 bits of q.  Each run of 16
+ *                         weights g = k >> 4 owns bytes [4g, 4g+4); with
+ *                         r = k & 15 and j = (r & 7) >> 1, byte 4g + j holds
+ *                         weight 16g+2j in bits 4-5, 16g+2j+1 in bits 6-7,
+ *                         16g+8+2j in bits 0-1 and 16g+8+2j+1 in bits 2-3
+ *               scales:       int8 [N][K/16] (signed sub-scale sc)
+ *               super_scales: fp16 [N][K/256] (d)
+ *               q = lo | hi << 4 in 0..63;  w = d[k >> 8] * sc[k >> 4] * (q - 32)
+ * MBQ_FMT_Q25   2.5 bits/weight, blocks of 32.
+ *               codes:  uint8 [N][K/4]; weight k is bits 2*(k & 3) of byte k >> 2
+ *               scales: fp16 [N][K/32];  w = s[k >> 5] * (q - 2)
+ * Every dequantized weight is exactly representable in binary32.
+ */
+#define MBQ_FMT_BF16 0
+#define MBQ_FMT_Q45  1
+#define MBQ_FMT_Q65  2
+#define MBQ_FMT_Q25  3
+
+/* A weight matrix resident on the device.  All plane pointers are device
+ * pointers owned by the caller and must stay valid until the enqueued work
+ * has run.  Planes 0 and 1 must be 16-byte aligned, planes 2 and 3 4-byte
+ * aligned (MBQ_EALIGN otherwise). */
+typedef struct mbq_qweight {
+    int32_t fmt;              /* MBQ_FMT_*                                    */
+    int32_t reserved;         /* must be 0                                    */
+    int64_t N;                /* output rows                                  */
+    int64_t K;                /* inputs per row                               */
+    const void* codes;        /* plane 0                                      */
+    const void* codes_hi;     /* plane 1 (Q65), else NULL                     */
+    const void* scales;       /* plane 2 (Q45, Q65, Q25), else NULL           */
+    const void* super_scales; /* plane 3 (Q65), else NULL                     */
+} mbq_qweight;
+
+/* Bits per weight and block length along K of a format (BF16: 16.0, 1;
+ * Q45: 4.5, 32; Q65: 6.5625, 256; Q25: 2.5, 32).  Host only.
+ * MBQ_EINVAL for an unknown format or a NULL output. */
+int mbq_format_info(int fmt, double* bits_per_weight, int* block_k);
+
+/* Byte size of each of the four planes of an N x K matrix (0 for planes the
+ * format does not use).  Their sum is N*K*bits_per_weight/8.  Host only.
+ * MBQ_EINVAL for an unknown format, negative sizes or K not a multiple of
+ * the block length. */
+int mbq_plane_sizes(int fmt, int64_t N, int64_t K, size_t sizes[4]);
+
+/* Host packer ([roofline-holds] "The search space": formats as byte budgets).
+ * codes: host, one byte per weight, row-major [N][K] (BF16: uint16 words).
+ * scales: host; Q45/Q25 fp16 bit patterns [N][K/32]; Q65 int8 [N][K/16];
+ *         NULL for BF16.  super_scales: host fp16 [N][K/256] for Q65, else NULL.
+ * planes: host buffers of the sizes mbq_plane_sizes gives (NULL where 0).
+ * MBQ_EINVAL if a code does not fit the format's bit width (nothing written
+ * is then meaningful), for NULL pointers or a bad shape. */
+int mbq_pack(int fmt, int64_t N, int64_t K, const void* codes, const void* scales,
+             const void* super_scales, void* const planes[4]);
+
+/* Exact inverse of mbq_pack: planes -> codes (one byte per weight, BF16 uint16
+ * words), scales and super_scales as described above.  Host only. */
+int mbq_unpack(int fmt, int64_t N, int64_t K, const void* const planes[4],
+               void* codes, void* scales, void* super_scales);
+
+/* y[m][n] = sum_k w[n][k] * x[m][k]   (accumulate = 0)
+ * y[m][n] += sum_k w[n][k] * x[m][k]  (accumulate = 1, a residual epilogue)
+ * for m < M, n < N: the decode-step matrix-vector product
+ * ([roofline-holds] "The tensor, the kernel, the token": multiply this tensor
+ * by this vector; [mountain-runs] section 3: a wave of lanes owns a row and
+ * reads consecutive 16-byte chunks; codes dequantized in registers).
+ * W: host pointer to a descriptor of device planes.
+ * x: device fp32 [M][ldx], 16-byte aligned, ldx >= K, ldx % 4 == 0.
+ * y: device fp32 [M][ldy], 4-byte aligned, ldy >= N; must not overlap x.
+ * Arithmetic: weights exact in fp32, fp32 accumulation; the order of the sum
+ * is unspecified.  M <= 8 runs on the vector units; M >= 16 (Q45 only) may use
+ * the matrix cores.  MBQ_EUNSUPPORTED for shapes without a kernel
+ * (K > 32768; Q25 with K % 64 != 0; BF16 with K % 8 != 0; 8 < M < 16; M > 64,
+ * or M >= 16 with a format other than Q45).  M == 0 or N == 0 enqueue
+ * nothing; K == 0 writes zeros (or leaves y for accumulate = 1). */
+int mbq_gemv_q(const mbq_qweight* W, const float* x, int64_t M, int64_t ldx,
+               float* y, int64_t ldy, int accumulate, void* stream);
+
+/* Selected experts in one launch ([mountain-runs] section 3: the expert FFN
+ * kernels with 2/4-bit codes; section 1: enough workgroups for the job).
+ * W_all stacks E experts of rows_per_expert rows each along N
+ * (W_all->N = E * rows_per_expert).  idx: device int32 [n_sel] expert ids;
+ * ids are not checked on the device and an id outside [0, E) is the caller's
+ * error.  x: device fp32 [K], 16-byte aligned.  y: device fp32
+ * [n_sel][rows_per_expert]; y[e][r] = sum_k W_all[idx[e]*R + r][k] * x[k].
+ * Same format and K limits as mbq_gemv_q with M = 1. */
+int mbq_gemv_q_gather(const mbq_qweight* W_all, int64_t rows_per_expert,
+                      const int32_t* idx, int64_t n_sel, const float* x,
+                      float* y, void* stream);
+
+/* RMSNorm of each row: y = gamma * x / sqrt(mean(x^2) + eps), one 256-thread
+ * workgroup per row ([one-serial-kernel] "One thread": many threads share the
+ * row, each sums its part, the parts are combined across the group).
+ * x, y: device fp32 [rows][n]; gamma: device fp32 [n]; all 4-byte aligned.
+ * y == x (in place) is allowed; any other overlap is MBQ_EINVAL.
+ * eps must be finite and >= 0. */
+int mbq_rmsnorm(const float* x, const float* gamma, float eps, int64_t rows,
+                int64_t n, float* y, void* stream);
+
+/* LayerNorm of each row in two passes, the mean first and then the biased
+ * variance of the centred values ([one-serial-kernel] "One thread"):
+ * y = (x - mean) / sqrt(var + eps) * gamma + beta.  Same layout, aliasing
+ * and eps rules as mbq_rmsnorm; beta: device fp32 [n]. */
+int mbq_layernorm(const float* x, const float* gamma, const float* beta, float eps,
+                  int64_t rows, int64_t n, float* y, void* stream);
+
+/* out[i] = silu(g[i]) * u[i], silu(t) = t / (1 + exp(-t)): the gated glue
+ * between the gate/up and down products of a decode layer ([roofline-holds]
+ * "Where the time goes": the small kernels between weight reads).
+ * g, u, out: device fp32 [n]; out may equal g or u. */
+int mbq_silu_mul(const float* g, const float* u, int64_t n, float* out, void* stream);
+
+/* Device decode exports for bit-exact checks of the in-register unpack.
+ * mbq_dequant_f32: w_out device fp32 [N][K] = every dequantized weight.
+ * mbq_unpack_codes: codes_out device uint8 [N][K] = every integer code
+ * (MBQ_EINVAL for BF16, which has none).  Same format limits as mbq_gemv_q. */
+int mbq_dequant_f32(const mbq_qweight* W, float* w_out, void* stream);
+int mbq_unpack_codes(const mbq_qweight* W, uint8_t* codes_out, void* stream);
+
+/* Measurement kit ([roofline-holds] "The Math" and "How I ran it": measure
+ * the ceiling, never quote it; a large in-device copy counts read and write).
+ * mbq_probe_read: reads `bytes` (a multiple of 16, buffer 16-byte aligned)
+ * and writes one float per workgroup into sink (device, >= 4096 floats).
+ * mbq_probe_copy: copies `bytes` (multiple of 16, both 16-byte aligned). */
+int mbq_probe_read(const void* buf, size_t bytes, float* sink, void* stream);
+int mbq_probe_copy(void* dst, const void* src, size_t bytes, void* stream);
+
+/* Static text for a status code, and the calling thread's last error detail
+ * (empty string if none). */
+const char* mbq_status_str(int status);
+const char* mbq_last_error(void);
+
+/* Library ABI version (this header: 1). */
+int mbq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MBQ_H */

@@ -1,0 +1,186 @@
+"""memory_bound_quantized_amd -- Python binding of libmbq (include/mbq.h).
+
+Argument marshalling only: every step runs in the library's HIP kernels on
+the caller's current torch stream.  torch supplies device memory and streams.
+If libmbq.so is missing, importing this package raises ImportError.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+
+from . import _lib
+from ._lib import BF16, Q25, Q45, Q65, EXPORTS, MbqError, QWeightDesc, check, lib
+
+__all__ = ["BF16", "Q45", "Q65", "Q25", "MbqError", "QWeight", "format_info", "plane_sizes",
+           "pack", "unpack", "gemv_q", "gemv_q_gather", "rmsnorm", "layernorm", "silu_mul",
+           "dequant_f32", "unpack_codes", "probe_read", "probe_copy", "version", "EXPORTS"]
+
+_vp = ctypes.c_void_p
+
+
+def version() -> int:
+    return lib.mbq_version()
+
+
+def _stream(stream=None):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return _vp(s.cuda_stream)
+
+
+def _ptr(t) -> _vp:
+    return _vp(0 if t is None else t.data_ptr())
+
+
+def format_info(fmt: int):
+    bpw = ctypes.c_double()
+    bk = ctypes.c_int()
+    check(lib.mbq_format_info(fmt, ctypes.byref(bpw), ctypes.byref(bk)))
+    return bpw.value, bk.value
+
+
+def plane_sizes(fmt: int, N: int, K: int):
+    out = (ctypes.c_size_t * 4)()
+    check(lib.mbq_plane_sizes(fmt, N, K, out))
+    return [int(v) for v in out]
+
+
+def pack(fmt: int, N: int, K: int, codes, scales=None, supers=None):
+    """Host packer: one byte per weight (uint16 words for BF16) -> 4 planes."""
+    sz = plane_sizes(fmt, N, K)
+    planes = [np.zeros(s, np.uint8) if s else None for s in sz]
+    codes = np.ascontiguousarray(codes, np.uint16 if fmt == BF16 else np.uint8)
+    sc = None if scales is None else np.ascontiguousarray(scales)
+    su = None if supers is None else np.ascontiguousarray(supers)
+    arr = (_vp * 4)(*[None if p is None else p.ctypes.data for p in planes])
+    check(lib.mbq_pack(fmt, N, K, codes.ctypes.data, None if sc is None else sc.ctypes.data,
+                       None if su is None else su.ctypes.data, arr))
+    return planes
+
+
+def unpack(fmt: int, N: int, K: int, planes):
+    """Exact inverse of pack: -> (codes, scales, super_scales) as numpy arrays."""
+    sz = plane_sizes(fmt, N, K)
+    keep = [None if p is None else np.ascontiguousarray(p, np.uint8) for p in planes]
+    arr = (_vp * 4)(*[None if p is None else p.ctypes.data for p in keep])
+    codes = np.zeros(N * K, np.uint16 if fmt == BF16 else np.uint8)
+    scales = np.zeros(sz[2], np.uint8)
+    supers = np.zeros(sz[3], np.uint8)
+    check(lib.mbq_unpack(fmt, N, K, arr, codes.ctypes.data, scales.ctypes.data if sz[2] else None,
+                         supers.ctypes.data if sz[3] else None))
+    if fmt == Q65:
+        return codes.reshape(N, K), scales.view(np.int8), supers.view(np.uint16)
+    if fmt == BF16:
+        return codes.reshape(N, K), None, None
+    return codes.reshape(N, K), scales.view(np.uint16), None
+
+
+class QWeight:
+    """A weight matrix resident on the device: its planes as torch uint8 tensors."""
+
+    def __init__(self, fmt: int, N: int, K: int, planes):
+        import torch
+        self.fmt, self.N, self.K = int(fmt), int(N), int(K)
+        self.planes = list(planes) + [None] * (4 - len(planes))
+        for p in self.planes:
+            if p is not None:
+                assert isinstance(p, torch.Tensor) and p.is_cuda and p.dtype == torch.uint8
+        self.desc = QWeightDesc(self.fmt, 0, self.N, self.K,
+                                *[None if p is None else p.data_ptr() for p in self.planes])
+
+    @classmethod
+    def from_host(cls, fmt: int, N: int, K: int, host_planes, device="cuda"):
+        import torch
+        dev = [None if p is None else torch.from_numpy(np.ascontiguousarray(p, np.uint8)).to(device)
+               for p in host_planes]
+        return cls(fmt, N, K, dev)
+
+    def clone(self):
+        return QWeight(self.fmt, self.N, self.K,
+                       [None if p is None else p.clone() for p in self.planes])
+
+    @property
+    def nbytes(self) -> int:
+        return sum(0 if p is None else p.numel() for p in self.planes)
+
+
+def gemv_q(W: QWeight, x, out=None, accumulate: bool = False, stream=None):
+    """y[M, N] (+)= x[M, K] @ W^T.  x: fp32 cuda tensor [K] or [M, K]."""
+    import torch
+    x2 = x if x.dim() == 2 else x.view(1, -1)
+    M = x2.shape[0]
+    if out is None:
+        out = torch.empty((M, W.N) if x.dim() == 2 else (W.N,), dtype=torch.float32, device=x.device)
+    y2 = out if out.dim() == 2 else out.view(1, -1)
+    check(lib.mbq_gemv_q(ctypes.byref(W.desc), _ptr(x2), M, x2.stride(0) if M > 1 else W.K,
+                         _ptr(y2), y2.stride(0) if M > 1 else W.N, int(bool(accumulate)),
+                         _stream(stream)))
+    return out
+
+
+def gemv_q_gather(W_all: QWeight, rows_per_expert: int, idx, x, out=None, stream=None):
+    """y[e, r] = W_all[idx[e] * R + r] . x; idx: int32 cuda tensor."""
+    import torch
+    n_sel = idx.numel()
+    if out is None:
+        out = torch.empty((n_sel, rows_per_expert), dtype=torch.float32, device=x.device)
+    check(lib.mbq_gemv_q_gather(ctypes.byref(W_all.desc), rows_per_expert, _ptr(idx), n_sel,
+                                _ptr(x), _ptr(out), _stream(stream)))
+    return out
+
+
+def rmsnorm(x, gamma, eps: float, out=None, stream=None):
+    import torch
+    n = x.shape[-1]
+    rows = x.numel() // n if n else 0
+    if out is None:
+        out = torch.empty_like(x)
+    check(lib.mbq_rmsnorm(_ptr(x), _ptr(gamma), eps, rows, n, _ptr(out), _stream(stream)))
+    return out
+
+
+def layernorm(x, gamma, beta, eps: float, out=None, stream=None):
+    import torch
+    n = x.shape[-1]
+    rows = x.numel() // n if n else 0
+    if out is None:
+        out = torch.empty_like(x)
+    check(lib.mbq_layernorm(_ptr(x), _ptr(gamma), _ptr(beta), eps, rows, n, _ptr(out),
+                            _stream(stream)))
+    return out
+
+
+def silu_mul(g, u, out=None, stream=None):
+    import torch
+    if out is None:
+        out = torch.empty_like(g)
+    check(lib.mbq_silu_mul(_ptr(g), _ptr(u), g.numel(), _ptr(out), _stream(stream)))
+    return out
+
+
+def dequant_f32(W: QWeight, out=None, stream=None):
+    import torch
+    if out is None:
+        out = torch.empty((W.N, W.K), dtype=torch.float32, device=W.planes[0].device)
+    check(lib.mbq_dequant_f32(ctypes.byref(W.desc), _ptr(out), _stream(stream)))
+    return out
+
+
+def unpack_codes(W: QWeight, out=None, stream=None):
+    import torch
+    if out is None:
+        out = torch.empty((W.N, W.K), dtype=torch.uint8, device=W.planes[0].device)
+    check(lib.mbq_unpack_codes(ctypes.byref(W.desc), _ptr(out), _stream(stream)))
+    return out
+
+
+def probe_read(buf, sink, stream=None):
+    check(lib.mbq_probe_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                             _stream(stream)))
+
+
+def probe_copy(dst, src, stream=None):
+    check(lib.mbq_probe_copy(_ptr(dst), _ptr(src), src.numel() * src.element_size(),
+                             _stream(stream)))

@@ -1,0 +1,400 @@
+// abi.cpp -- the C ABI of libmbq (include/mbq.h): argument validation, the
+// host packer/unpacker and dispatch to the HIP launchers.  Nothing is
+// enqueued unless every argument check passes.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "../../include/mbq.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int ok() {
+    g_err.clear();
+    return MBQ_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(MBQ_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool fmt_valid(int fmt) { return fmt >= MBQ_FMT_BF16 && fmt <= MBQ_FMT_Q25; }
+
+int64_t block_len(int fmt) {
+    switch (fmt) {
+    case MBQ_FMT_Q45: return 32;
+    case MBQ_FMT_Q65: return 256;
+    case MBQ_FMT_Q25: return 32;
+    default: return 1;
+    }
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
+    if (an == 0 || bn == 0) return false;
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + bn && b0 < a0 + an;
+}
+
+// Shape checks shared by every entry point taking an mbq_qweight.
+int check_weight(const mbq_qweight* W, const char* fn) {
+    if (!W) return fail(MBQ_EINVAL, "%s: W is NULL", fn);
+    if (!fmt_valid(W->fmt)) return fail(MBQ_EINVAL, "%s: unknown format %d", fn, W->fmt);
+    if (W->reserved != 0) return fail(MBQ_EINVAL, "%s: W->reserved must be 0", fn);
+    if (W->N < 0 || W->K < 0) return fail(MBQ_EINVAL, "%s: negative shape", fn);
+    if (W->K % block_len(W->fmt))
+        return fail(MBQ_EINVAL, "%s: K=%lld is not a multiple of the block length %lld", fn,
+                    (long long)W->K, (long long)block_len(W->fmt));
+    return MBQ_OK;
+}
+
+// Plane pointers and alignment (only when there is data to read).
+int check_planes(const mbq_qweight* W, const char* fn) {
+    const bool need1 = W->fmt == MBQ_FMT_Q65;
+    const bool need2 = W->fmt != MBQ_FMT_BF16;
+    const bool need3 = W->fmt == MBQ_FMT_Q65;
+    if (!W->codes || (need1 && !W->codes_hi) || (need2 && !W->scales) ||
+        (need3 && !W->super_scales))
+        return fail(MBQ_EINVAL, "%s: a plane the format needs is NULL", fn);
+    if (!aligned(W->codes, 16) || (need1 && !aligned(W->codes_hi, 16)))
+        return fail(MBQ_EALIGN, "%s: planes 0 and 1 must be 16-byte aligned", fn);
+    if ((need2 && !aligned(W->scales, 4)) || (need3 && !aligned(W->super_scales, 4)))
+        return fail(MBQ_EALIGN, "%s: planes 2 and 3 must be 4-byte aligned", fn);
+    return MBQ_OK;
+}
+
+// Kernel limits common to the GEMV paths and the device exports.
+int check_kernel_shape(const mbq_qweight* W, const char* fn) {
+    if (W->K > mbq::kMaxK)
+        return fail(MBQ_EUNSUPPORTED, "%s: K=%lld exceeds %lld", fn, (long long)W->K,
+                    (long long)mbq::kMaxK);
+    if (W->fmt == MBQ_FMT_Q25 && W->K % 64)
+        return fail(MBQ_EUNSUPPORTED, "%s: Q25 kernels need K %% 64 == 0", fn);
+    if (W->fmt == MBQ_FMT_BF16 && W->K % 8)
+        return fail(MBQ_EUNSUPPORTED, "%s: BF16 kernels need K %% 8 == 0", fn);
+    return MBQ_OK;
+}
+
+mbq::DevPlanes planes_of(const mbq_qweight* W) {
+    return mbq::DevPlanes{(const uint8_t*)W->codes, (const uint8_t*)W->codes_hi,
+                          (const uint8_t*)W->scales, (const uint8_t*)W->super_scales};
+}
+
+// Optional geometry override for tuning sweeps: MBQ_GEMV_GEOM="R,G".
+bool geom_override(mbq::GemvGeom* g) {
+    static int R = -1, G = -1;
+    static bool parsed = false;
+    if (!parsed) {
+        const char* s = getenv("MBQ_GEMV_GEOM");
+        int r = 0, gg = 0;
+        if (s && sscanf(s, "%d,%d", &r, &gg) == 2 && (r == 1 || r == 2 || r == 4) && gg >= 1) {
+            R = r;
+            G = gg;
+        }
+        parsed = true;
+    }
+    if (R < 0) return false;
+    g->rows_per_wave = R;
+    g->groups_per_wg = G;
+    return true;
+}
+
+// ------------------------------------------------------------ host packer
+
+void put16(uint8_t* p, uint16_t v) {
+    p[0] = (uint8_t)(v & 0xFF);
+    p[1] = (uint8_t)(v >> 8);
+}
+
+uint16_t get16(const uint8_t* p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+
+}  // namespace
+
+extern "C" {
+
+int mbq_version(void) { return 1; }
+
+const char* mbq_status_str(int status) {
+    switch (status) {
+    case MBQ_OK: return "MBQ_OK";
+    case MBQ_EINVAL: return "MBQ_EINVAL: invalid argument";
+    case MBQ_EALIGN: return "MBQ_EALIGN: misaligned pointer";
+    case MBQ_EUNSUPPORTED: return "MBQ_EUNSUPPORTED: no kernel for this request";
+    case MBQ_EHIP: return "MBQ_EHIP: HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+const char* mbq_last_error(void) { return g_err.c_str(); }
+
+int mbq_format_info(int fmt, double* bits_per_weight, int* block_k) {
+    if (!fmt_valid(fmt)) return fail(MBQ_EINVAL, "mbq_format_info: unknown format %d", fmt);
+    if (!bits_per_weight || !block_k) return fail(MBQ_EINVAL, "mbq_format_info: NULL output");
+    static const double bpw[4] = {16.0, 4.5, 6.5625, 2.5};
+    *bits_per_weight = bpw[fmt];
+    *block_k = (int)block_len(fmt);
+    return ok();
+}
+
+int mbq_plane_sizes(int fmt, int64_t N, int64_t K, size_t sizes[4]) {
+    if (!sizes) return fail(MBQ_EINVAL, "mbq_plane_sizes: NULL sizes");
+    if (!fmt_valid(fmt)) return fail(MBQ_EINVAL, "mbq_plane_sizes: unknown format %d", fmt);
+    if (N < 0 || K < 0) return fail(MBQ_EINVAL, "mbq_plane_sizes: negative shape");
+    if (K % block_len(fmt)) return fail(MBQ_EINVAL, "mbq_plane_sizes: K not a multiple of the block");
+    const size_t nk = (size_t)N * (size_t)K;
+    sizes[0] = sizes[1] = sizes[2] = sizes[3] = 0;
+    switch (fmt) {
+    case MBQ_FMT_BF16: sizes[0] = 2 * nk; break;
+    case MBQ_FMT_Q45: sizes[0] = nk / 2; sizes[2] = nk / 16; break;        // 2 B per 32
+    case MBQ_FMT_Q65: sizes[0] = nk / 2; sizes[1] = nk / 4; sizes[2] = nk / 16; sizes[3] = nk / 128; break;
+    case MBQ_FMT_Q25: sizes[0] = nk / 4; sizes[2] = nk / 16; break;
+    }
+    return ok();
+}
+
+int mbq_pack(int fmt, int64_t N, int64_t K, const void* codes, const void* scales,
+             const void* super_scales, void* const planes[4]) {
+    size_t sz[4];
+    int rc = mbq_plane_sizes(fmt, N, K, sz);
+    if (rc) return rc;
+    if (!planes || !codes) return fail(MBQ_EINVAL, "mbq_pack: NULL pointer");
+    for (int p = 0; p < 4; p++)
+        if (sz[p] && !planes[p]) return fail(MBQ_EINVAL, "mbq_pack: plane %d is NULL", p);
+    if (fmt != MBQ_FMT_BF16 && sz[2] && !scales) return fail(MBQ_EINVAL, "mbq_pack: NULL scales");
+    if (fmt == MBQ_FMT_Q65 && sz[3] && !super_scales)
+        return fail(MBQ_EINVAL, "mbq_pack: NULL super_scales");
+    const uint8_t* q = (const uint8_t*)codes;
+    const size_t nk = (size_t)N * (size_t)K;
+    if (fmt == MBQ_FMT_BF16) {
+        memcpy(planes[0], codes, sz[0]);
+        return ok();
+    }
+    const int bits = fmt == MBQ_FMT_Q45 ? 4 : fmt == MBQ_FMT_Q65 ? 6 : 2;
+    for (size_t i = 0; i < nk; i++)
+        if (q[i] >> bits) return fail(MBQ_EINVAL, "mbq_pack: code %u at %zu exceeds %d bits", q[i], i, bits);
+    uint8_t* p0 = (uint8_t*)planes[0];
+    if (fmt == MBQ_FMT_Q45) {
+        for (size_t i = 0; i < nk / 2; i++) p0[i] = (uint8_t)(q[2 * i] | (q[2 * i + 1] << 4));
+    } else if (fmt == MBQ_FMT_Q25) {
+        for (size_t i = 0; i < nk / 4; i++)
+            p0[i] = (uint8_t)(q[4 * i] | (q[4 * i + 1] << 2) | (q[4 * i + 2] << 4) | (q[4 * i + 3] << 6));
+    } else {
+        // Q65: runs of 16 weights (K % 256 == 0, so runs never span rows).
+        uint8_t* p1 = (uint8_t*)planes[1];
+        for (size_t r = 0; r < nk / 16; r++) {
+            const uint8_t* c = q + 16 * r;
+            for (int i = 0; i < 8; i++) p0[8 * r + i] = (uint8_t)((c[2 * i] & 15) | ((c[2 * i + 1] & 15) << 4));
+            for (int j = 0; j < 4; j++) {
+                const int a = c[2 * j] >> 4, b = c[2 * j + 1] >> 4;
+                const int e = c[8 + 2 * j] >> 4, f = c[8 + 2 * j + 1] >> 4;
+                p1[4 * r + j] = (uint8_t)(e | (f << 2) | (a << 4) | (b << 6));
+            }
+        }
+    }
+    memcpy(planes[2], scales, sz[2]);
+    if (fmt == MBQ_FMT_Q65) memcpy(planes[3], super_scales, sz[3]);
+    return ok();
+}
+
+int mbq_unpack(int fmt, int64_t N, int64_t K, const void* const planes[4], void* codes,
+               void* scales, void* super_scales) {
+    size_t sz[4];
+    int rc = mbq_plane_sizes(fmt, N, K, sz);
+    if (rc) return rc;
+    if (!planes || !codes) return fail(MBQ_EINVAL, "mbq_unpack: NULL pointer");
+    for (int p = 0; p < 4; p++)
+        if (sz[p] && !planes[p]) return fail(MBQ_EINVAL, "mbq_unpack: plane %d is NULL", p);
+    const size_t nk = (size_t)N * (size_t)K;
+    uint8_t* q = (uint8_t*)codes;
+    const uint8_t* p0 = (const uint8_t*)planes[0];
+    if (fmt == MBQ_FMT_BF16) {
+        memcpy(codes, planes[0], sz[0]);
+        return ok();
+    }
+    if ((sz[2] && !scales) || (fmt == MBQ_FMT_Q65 && !super_scales))
+        return fail(MBQ_EINVAL, "mbq_unpack: NULL scale output");
+    if (fmt == MBQ_FMT_Q45) {
+        for (size_t i = 0; i < nk; i++) q[i] = (uint8_t)((p0[i >> 1] >> ((i & 1) * 4)) & 15);
+    } else if (fmt == MBQ_FMT_Q25) {
+        for (size_t i = 0; i < nk; i++) q[i] = (uint8_t)((p0[i >> 2] >> ((i & 3) * 2)) & 3);
+    } else {
+        const uint8_t* p1 = (const uint8_t*)planes[1];
+        for (size_t r = 0; r < nk / 16; r++) {
+            uint8_t* c = q + 16 * r;
+            for (int i = 0; i < 8; i++) {
+                c[2 * i] = (uint8_t)(p0[8 * r + i] & 15);
+                c[2 * i + 1] = (uint8_t)(p0[8 * r + i] >> 4);
+            }
+            for (int j = 0; j < 4; j++) {
+                const uint8_t h = p1[4 * r + j];
+                c[8 + 2 * j] |= (uint8_t)((h & 3) << 4);
+                c[8 + 2 * j + 1] |= (uint8_t)(((h >> 2) & 3) << 4);
+                c[2 * j] |= (uint8_t)(((h >> 4) & 3) << 4);
+                c[2 * j + 1] |= (uint8_t)(((h >> 6) & 3) << 4);
+            }
+        }
+    }
+    memcpy(scales, planes[2], sz[2]);
+    if (fmt == MBQ_FMT_Q65) memcpy(super_scales, planes[3], sz[3]);
+    return ok();
+}
+
+int mbq_gemv_q(const mbq_qweight* W, const float* x, int64_t M, int64_t ldx, float* y,
+               int64_t ldy, int accumulate, void* stream) {
+    const char* fn = "mbq_gemv_q";
+    int rc = check_weight(W, fn);
+    if (rc) return rc;
+    if (M < 0) return fail(MBQ_EINVAL, "%s: M < 0", fn);
+    if (ldx < W->K || ldy < W->N) return fail(MBQ_EINVAL, "%s: ldx < K or ldy < N", fn);
+    if (accumulate != 0 && accumulate != 1) return fail(MBQ_EINVAL, "%s: accumulate must be 0 or 1", fn);
+    if (M == 0 || W->N == 0) return ok();
+    if (!x || !y) return fail(MBQ_EINVAL, "%s: x or y is NULL", fn);
+    if (!aligned(y, 4)) return fail(MBQ_EALIGN, "%s: y must be 4-byte aligned", fn);
+    const size_t ybytes = (size_t)((M - 1) * ldy + W->N) * 4;
+    hipStream_t s = (hipStream_t)stream;
+    if (W->K == 0) {
+        if (accumulate) return ok();
+        return hip_status(mbq::launch_fill_zero(y, M, W->N, ldy, s), fn);
+    }
+    if (!aligned(x, 16) || ldx % 4) return fail(MBQ_EALIGN, "%s: x must be 16-byte aligned with ldx %% 4 == 0", fn);
+    const size_t xbytes = (size_t)((M - 1) * ldx + W->K) * 4;
+    if (overlaps(x, xbytes, y, ybytes)) return fail(MBQ_EINVAL, "%s: x and y overlap", fn);
+    if ((rc = check_planes(W, fn))) return rc;
+    if ((rc = check_kernel_shape(W, fn))) return rc;
+    const mbq::DevPlanes P = planes_of(W);
+    if (M == 1) {
+        mbq::GemvGeom g = mbq::gemv_m1_default_geom(W->fmt, W->N, W->K);
+        geom_override(&g);
+        return hip_status(mbq::launch_gemv_m1(W->fmt, P, W->N, W->K, x, y, accumulate, nullptr,
+                                              1, g, s), fn);
+    }
+    return fail(MBQ_EUNSUPPORTED, "%s: no kernel for M=%lld with format %d", fn, (long long)M, W->fmt);
+}
+
+int mbq_gemv_q_gather(const mbq_qweight* W_all, int64_t rows_per_expert, const int32_t* idx,
+                      int64_t n_sel, const float* x, float* y, void* stream) {
+    const char* fn = "mbq_gemv_q_gather";
+    int rc = check_weight(W_all, fn);
+    if (rc) return rc;
+    if (rows_per_expert <= 0 || n_sel < 0) return fail(MBQ_EINVAL, "%s: bad rows_per_expert or n_sel", fn);
+    if (W_all->N % rows_per_expert) return fail(MBQ_EINVAL, "%s: N is not a multiple of rows_per_expert", fn);
+    if (n_sel == 0) return ok();
+    if (!idx || !x || !y) return fail(MBQ_EINVAL, "%s: NULL pointer", fn);
+    if (!aligned(idx, 4) || !aligned(y, 4)) return fail(MBQ_EALIGN, "%s: idx and y must be 4-byte aligned", fn);
+    const int64_t n_out = n_sel * rows_per_expert;
+    hipStream_t s = (hipStream_t)stream;
+    if (W_all->K == 0) return hip_status(mbq::launch_fill_zero(y, 1, n_out, n_out, s), fn);
+    if (!aligned(x, 16)) return fail(MBQ_EALIGN, "%s: x must be 16-byte aligned", fn);
+    if (overlaps(x, (size_t)W_all->K * 4, y, (size_t)n_out * 4)) return fail(MBQ_EINVAL, "%s: x and y overlap", fn);
+    if ((rc = check_planes(W_all, fn))) return rc;
+    if ((rc = check_kernel_shape(W_all, fn))) return rc;
+    mbq::GemvGeom g = mbq::gemv_m1_default_geom(W_all->fmt, n_out, W_all->K);
+    geom_override(&g);
+    return hip_status(mbq::launch_gemv_m1(W_all->fmt, planes_of(W_all), n_out, W_all->K, x, y, 0,
+                                          idx, rows_per_expert, g, s), fn);
+}
+
+static int check_norm(const float* x, const float* gamma, const float* beta, bool need_beta,
+                      float eps, int64_t rows, int64_t n, const float* y, const char* fn) {
+    if (rows < 0 || n < 0) return fail(MBQ_EINVAL, "%s: negative shape", fn);
+    if (rows > 0x7FFFFFFF) return fail(MBQ_EUNSUPPORTED, "%s: more than 2^31-1 rows", fn);
+    if (!(eps >= 0.f) || eps == __builtin_inff()) return fail(MBQ_EINVAL, "%s: eps must be finite and >= 0", fn);
+    if (rows == 0 || n == 0) return MBQ_OK;
+    if (!x || !gamma || !y || (need_beta && !beta)) return fail(MBQ_EINVAL, "%s: NULL pointer", fn);
+    if (!aligned(x, 4) || !aligned(y, 4) || !aligned(gamma, 4) || (need_beta && !aligned(beta, 4)))
+        return fail(MBQ_EALIGN, "%s: pointers must be 4-byte aligned", fn);
+    const size_t bytes = (size_t)rows * (size_t)n * 4;
+    if (x != y && overlaps(x, bytes, y, bytes)) return fail(MBQ_EINVAL, "%s: x and y partially overlap", fn);
+    return MBQ_OK;
+}
+
+int mbq_rmsnorm(const float* x, const float* gamma, float eps, int64_t rows, int64_t n, float* y,
+                void* stream) {
+    const char* fn = "mbq_rmsnorm";
+    int rc = check_norm(x, gamma, nullptr, false, eps, rows, n, y, fn);
+    if (rc) return rc;
+    if (rows == 0 || n == 0) return ok();
+    return hip_status(mbq::launch_rmsnorm(x, gamma, eps, rows, n, y, (hipStream_t)stream), fn);
+}
+
+int mbq_layernorm(const float* x, const float* gamma, const float* beta, float eps, int64_t rows,
+                  int64_t n, float* y, void* stream) {
+    const char* fn = "mbq_layernorm";
+    int rc = check_norm(x, gamma, beta, true, eps, rows, n, y, fn);
+    if (rc) return rc;
+    if (rows == 0 || n == 0) return ok();
+    return hip_status(mbq::launch_layernorm(x, gamma, beta, eps, rows, n, y, (hipStream_t)stream), fn);
+}
+
+int mbq_silu_mul(const float* g, const float* u, int64_t n, float* out, void* stream) {
+    const char* fn = "mbq_silu_mul";
+    if (n < 0) return fail(MBQ_EINVAL, "%s: n < 0", fn);
+    if (n == 0) return ok();
+    if (!g || !u || !out) return fail(MBQ_EINVAL, "%s: NULL pointer", fn);
+    if (!aligned(g, 4) || !aligned(u, 4) || !aligned(out, 4)) return fail(MBQ_EALIGN, "%s: misaligned", fn);
+    const size_t b = (size_t)n * 4;
+    if ((out != g && overlaps(out, b, g, b)) || (out != u && overlaps(out, b, u, b)))
+        return fail(MBQ_EINVAL, "%s: out partially overlaps an input", fn);
+    return hip_status(mbq::launch_silu_mul(g, u, n, out, (hipStream_t)stream), fn);
+}
+
+int mbq_dequant_f32(const mbq_qweight* W, float* w_out, void* stream) {
+    const char* fn = "mbq_dequant_f32";
+    int rc = check_weight(W, fn);
+    if (rc) return rc;
+    if (W->N == 0 || W->K == 0) return ok();
+    if (!w_out) return fail(MBQ_EINVAL, "%s: w_out is NULL", fn);
+    if (!aligned(w_out, 16)) return fail(MBQ_EALIGN, "%s: w_out must be 16-byte aligned", fn);
+    if ((rc = check_planes(W, fn))) return rc;
+    if ((rc = check_kernel_shape(W, fn))) return rc;
+    return hip_status(mbq::launch_dequant(W->fmt, planes_of(W), W->N, W->K, w_out, (hipStream_t)stream), fn);
+}
+
+int mbq_unpack_codes(const mbq_qweight* W, uint8_t* codes_out, void* stream) {
+    const char* fn = "mbq_unpack_codes";
+    int rc = check_weight(W, fn);
+    if (rc) return rc;
+    if (W->fmt == MBQ_FMT_BF16) return fail(MBQ_EINVAL, "%s: BF16 has no integer codes", fn);
+    if (W->N == 0 || W->K == 0) return ok();
+    if (!codes_out) return fail(MBQ_EINVAL, "%s: codes_out is NULL", fn);
+    if ((rc = check_planes(W, fn))) return rc;
+    if ((rc = check_kernel_shape(W, fn))) return rc;
+    return hip_status(mbq::launch_unpack_codes(W->fmt, planes_of(W), W->N, W->K, codes_out, (hipStream_t)stream), fn);
+}
+
+int mbq_probe_read(const void* buf, size_t bytes, float* sink, void* stream) {
+    const char* fn = "mbq_probe_read";
+    if (!buf || !sink) return fail(MBQ_EINVAL, "%s: NULL pointer", fn);
+    if (bytes % 16 || !aligned(buf, 16)) return fail(MBQ_EALIGN, "%s: 16-byte granularity", fn);
+    return hip_status(mbq::launch_probe_read(buf, bytes, sink, (hipStream_t)stream), fn);
+}
+
+int mbq_probe_copy(void* dst, const void* src, size_t bytes, void* stream) {
+    const char* fn = "mbq_probe_copy";
+    if (!dst || !src) return fail(MBQ_EINVAL, "%s: NULL pointer", fn);
+    if (bytes % 16 || !aligned(dst, 16) || !aligned(src, 16))
+        return fail(MBQ_EALIGN, "%s: 16-byte granularity", fn);
+    if (overlaps(dst, bytes, src, bytes)) return fail(MBQ_EINVAL, "%s: buffers overlap", fn);
+    return hip_status(mbq::launch_probe_copy(dst, src, bytes, (hipStream_t)stream), fn);
+}
+
+}  // extern "C"

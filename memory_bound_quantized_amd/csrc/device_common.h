@@ -1,0 +1,71 @@
+// device_common.h -- small device helpers shared by the libmbq kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mbq {
+
+constexpr int kWave = 64;        // CDNA wavefront width
+constexpr int kBlock = 256;      // threads per workgroup for every kernel here
+constexpr int kWavesPerBlock = kBlock / kWave;
+
+// Byte j of a dword -> float, one VALU op each (v_cvt_f32_ubyte{0..3}).  The
+// compiler folds masks into its own byte extraction when it can see them, so
+// the instructions are written out to keep one op per converted code.
+__device__ __forceinline__ float ub0(uint32_t v) {
+    float r;
+    asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(v));
+    return r;
+}
+__device__ __forceinline__ float ub1(uint32_t v) {
+    float r;
+    asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(v));
+    return r;
+}
+__device__ __forceinline__ float ub2(uint32_t v) {
+    float r;
+    asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(v));
+    return r;
+}
+__device__ __forceinline__ float ub3(uint32_t v) {
+    float r;
+    asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(v));
+    return r;
+}
+
+// fp16 bit pattern (low 16 bits) -> float (v_cvt_f32_f16, exact).
+__device__ __forceinline__ float h2f(uint32_t bits) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits & 0xFFFFu));
+}
+
+__device__ __forceinline__ float as_f(uint32_t bits) { return __builtin_bit_cast(float, bits); }
+
+// Sum over the 64 lanes of a wave; every lane receives the total.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+// Sum over aligned groups of G lanes (G a power of two <= 64).
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+    for (int o = G / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+// Sum over the 256 threads of a workgroup through LDS (red holds 4 floats).
+// Every thread receives the total.  Contains two barriers.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+    v = wave_sum(v);
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    float t = red[0] + red[1] + red[2] + red[3];
+    __syncthreads();
+    return t;
+}
+
+}  // namespace mbq

@@ -1,0 +1,66 @@
+// kernels.h -- internal launchers of libmbq (not part of the C ABI).
+// Every launcher enqueues on `stream` and returns hipGetLastError() after the
+// launch.  Arguments have been validated by the C-ABI layer (mbq_abi.cpp).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mbq {
+
+enum Fmt : int { kBF16 = 0, kQ45 = 1, kQ65 = 2, kQ25 = 3 };
+
+// Device planes of one weight matrix (see mbq.h for the layouts).
+struct DevPlanes {
+    const uint8_t* p0;  // codes
+    const uint8_t* p1;  // codes_hi
+    const uint8_t* p2;  // scales
+    const uint8_t* p3;  // super_scales
+};
+
+// Largest K the GEMV kernels stage in LDS.
+constexpr int64_t kMaxK = 32768;
+
+// Geometry of the M = 1 GEMV: rows per wave and row groups per workgroup.
+struct GemvGeom {
+    int rows_per_wave;   // 1, 2 or 4
+    int groups_per_wg;   // >= 1
+};
+
+GemvGeom gemv_m1_default_geom(int fmt, int64_t N, int64_t K);
+
+// y[n] (+)= W[row(n)] . x for n < N_out.  If gidx != nullptr the output row
+// n maps to weight row gidx[n / rpe] * rpe + n % rpe (gathered experts).
+hipError_t launch_gemv_m1(int fmt, DevPlanes P, int64_t N_out, int64_t K, const float* x,
+                          float* y, int accumulate, const int32_t* gidx, int64_t rpe,
+                          GemvGeom geom, hipStream_t stream);
+
+// Y[m][n] (+)= W[n] . X[m] for 2 <= M <= 8 (vector units).
+hipError_t launch_gemv_smallm(int fmt, DevPlanes P, int64_t N, int64_t K, const float* x,
+                              int64_t M, int64_t ldx, float* y, int64_t ldy, int accumulate,
+                              hipStream_t stream);
+
+// Y[m][n] (+)= W[n] . X[m] for 16 <= M <= 64, Q45 only (matrix cores).
+hipError_t launch_gemv_mfma_q45(DevPlanes P, int64_t N, int64_t K, const float* x, int64_t M,
+                                int64_t ldx, float* y, int64_t ldy, int accumulate,
+                                hipStream_t stream);
+
+// y[m][n] = 0 for the K == 0 case (rows of length ldy, first N entries).
+hipError_t launch_fill_zero(float* y, int64_t M, int64_t N, int64_t ldy, hipStream_t stream);
+
+hipError_t launch_rmsnorm(const float* x, const float* gamma, float eps, int64_t rows, int64_t n,
+                          float* y, hipStream_t stream);
+hipError_t launch_layernorm(const float* x, const float* gamma, const float* beta, float eps,
+                            int64_t rows, int64_t n, float* y, hipStream_t stream);
+hipError_t launch_silu_mul(const float* g, const float* u, int64_t n, float* out,
+                           hipStream_t stream);
+
+hipError_t launch_dequant(int fmt, DevPlanes P, int64_t N, int64_t K, float* w_out,
+                          hipStream_t stream);
+hipError_t launch_unpack_codes(int fmt, DevPlanes P, int64_t N, int64_t K, uint8_t* out,
+                               hipStream_t stream);
+
+hipError_t launch_probe_read(const void* buf, size_t bytes, float* sink, hipStream_t stream);
+hipError_t launch_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+
+}  // namespace mbq

@@ -1,0 +1,189 @@
+// norms.hip -- cooperative row norms and the gated glue.
+//
+// One 256-thread workgroup per row: each thread sums its share of the row
+// (held in registers), the partial sums are combined by a wave shuffle tree
+// and then across the 4 waves through LDS ([one-serial-kernel] "One thread":
+// the serial one-thread-per-row kernel was replaced by a group of 256 threads
+// that each sum their part and combine the parts).  LayerNorm makes two
+// passes over the register-resident values: the mean first, then the biased
+// variance of the centred values, so no E[x^2] - mean^2 cancellation occurs.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace mbq {
+
+template <int VEC>
+__global__ __launch_bounds__(kBlock) void rmsnorm_vec_kernel(const float* x,
+                                                             const float* __restrict__ gamma,
+                                                             float eps, int n, float* y) {
+    __shared__ float red[kWavesPerBlock];
+    const int64_t row = blockIdx.x;
+    const int n4 = n >> 2;
+    const float4* xr = (const float4*)(x + row * n);
+    float4 v[VEC];
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < VEC; i++) {
+        const int f = i * kBlock + (int)threadIdx.x;
+        v[i] = f < n4 ? xr[f] : make_float4(0.f, 0.f, 0.f, 0.f);
+        ss = fmaf(v[i].x, v[i].x, ss);
+        ss = fmaf(v[i].y, v[i].y, ss);
+        ss = fmaf(v[i].z, v[i].z, ss);
+        ss = fmaf(v[i].w, v[i].w, ss);
+    }
+    const float tot = block_sum(ss, red);
+    const float inv = 1.0f / sqrtf(tot / (float)n + eps);
+    float4* yr = (float4*)(y + row * n);
+    const float4* g4 = (const float4*)gamma;
+#pragma unroll
+    for (int i = 0; i < VEC; i++) {
+        const int f = i * kBlock + (int)threadIdx.x;
+        if (f < n4) {
+            const float4 g = g4[f];
+            yr[f] = make_float4(g.x * (v[i].x * inv), g.y * (v[i].y * inv), g.z * (v[i].z * inv),
+                                g.w * (v[i].w * inv));
+        }
+    }
+}
+
+// Any n and alignment: values re-read from memory for the second pass.
+__global__ __launch_bounds__(kBlock) void rmsnorm_any_kernel(const float* x,
+                                                             const float* __restrict__ gamma,
+                                                             float eps, int64_t n, float* y) {
+    __shared__ float red[kWavesPerBlock];
+    const int64_t row = blockIdx.x;
+    const float* xr = x + row * n;
+    float ss = 0.f;
+    for (int64_t i = threadIdx.x; i < n; i += kBlock) ss = fmaf(xr[i], xr[i], ss);
+    const float tot = block_sum(ss, red);
+    const float inv = 1.0f / sqrtf(tot / (float)n + eps);
+    float* yr = y + row * n;
+    for (int64_t i = threadIdx.x; i < n; i += kBlock) yr[i] = gamma[i] * (xr[i] * inv);
+}
+
+template <int VEC>
+__global__ __launch_bounds__(kBlock) void layernorm_vec_kernel(const float* x,
+                                                               const float* __restrict__ gamma,
+                                                               const float* __restrict__ beta,
+                                                               float eps, int n, float* y) {
+    __shared__ float red[kWavesPerBlock];
+    const int64_t row = blockIdx.x;
+    const int n4 = n >> 2;
+    const float4* xr = (const float4*)(x + row * n);
+    float4 v[VEC];
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < VEC; i++) {
+        const int f = i * kBlock + (int)threadIdx.x;
+        v[i] = f < n4 ? xr[f] : make_float4(0.f, 0.f, 0.f, 0.f);
+        s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+    }
+    const float mean = block_sum(s, red) / (float)n;
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < VEC; i++) {
+        const int f = i * kBlock + (int)threadIdx.x;
+        if (f < n4) {
+            const float a = v[i].x - mean, b = v[i].y - mean, c = v[i].z - mean, d = v[i].w - mean;
+            q = fmaf(a, a, q);
+            q = fmaf(b, b, q);
+            q = fmaf(c, c, q);
+            q = fmaf(d, d, q);
+        }
+    }
+    const float var = block_sum(q, red) / (float)n;
+    const float inv = 1.0f / sqrtf(var + eps);
+    float4* yr = (float4*)(y + row * n);
+    const float4* g4 = (const float4*)gamma;
+    const float4* b4 = (const float4*)beta;
+#pragma unroll
+    for (int i = 0; i < VEC; i++) {
+        const int f = i * kBlock + (int)threadIdx.x;
+        if (f < n4) {
+            const float4 g = g4[f], b = b4[f];
+            yr[f] = make_float4(fmaf((v[i].x - mean) * inv, g.x, b.x),
+                                fmaf((v[i].y - mean) * inv, g.y, b.y),
+                                fmaf((v[i].z - mean) * inv, g.z, b.z),
+                                fmaf((v[i].w - mean) * inv, g.w, b.w));
+        }
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void layernorm_any_kernel(const float* x,
+                                                               const float* __restrict__ gamma,
+                                                               const float* __restrict__ beta,
+                                                               float eps, int64_t n, float* y) {
+    __shared__ float red[kWavesPerBlock];
+    const int64_t row = blockIdx.x;
+    const float* xr = x + row * n;
+    float s = 0.f;
+    for (int64_t i = threadIdx.x; i < n; i += kBlock) s += xr[i];
+    const float mean = block_sum(s, red) / (float)n;
+    float q = 0.f;
+    for (int64_t i = threadIdx.x; i < n; i += kBlock) {
+        const float a = xr[i] - mean;
+        q = fmaf(a, a, q);
+    }
+    const float inv = 1.0f / sqrtf(block_sum(q, red) / (float)n + eps);
+    float* yr = y + row * n;
+    for (int64_t i = threadIdx.x; i < n; i += kBlock)
+        yr[i] = fmaf((xr[i] - mean) * inv, gamma[i], beta[i]);
+}
+
+static int vec_for(int64_t n) {
+    const int64_t n4 = n >> 2;
+    if (n4 <= kBlock) return 1;
+    if (n4 <= 2 * kBlock) return 2;
+    if (n4 <= 4 * kBlock) return 4;
+    if (n4 <= 8 * kBlock) return 8;
+    return 0;
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+hipError_t launch_rmsnorm(const float* x, const float* gamma, float eps, int64_t rows, int64_t n,
+                          float* y, hipStream_t stream) {
+    const int vec = (n % 4 == 0 && aligned16(x) && aligned16(y) && aligned16(gamma)) ? vec_for(n) : 0;
+    const dim3 grid((unsigned)rows), block(kBlock);
+    switch (vec) {
+    case 1: hipLaunchKernelGGL(rmsnorm_vec_kernel<1>, grid, block, 0, stream, x, gamma, eps, (int)n, y); break;
+    case 2: hipLaunchKernelGGL(rmsnorm_vec_kernel<2>, grid, block, 0, stream, x, gamma, eps, (int)n, y); break;
+    case 4: hipLaunchKernelGGL(rmsnorm_vec_kernel<4>, grid, block, 0, stream, x, gamma, eps, (int)n, y); break;
+    case 8: hipLaunchKernelGGL(rmsnorm_vec_kernel<8>, grid, block, 0, stream, x, gamma, eps, (int)n, y); break;
+    default: hipLaunchKernelGGL(rmsnorm_any_kernel, grid, block, 0, stream, x, gamma, eps, n, y); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_layernorm(const float* x, const float* gamma, const float* beta, float eps,
+                            int64_t rows, int64_t n, float* y, hipStream_t stream) {
+    const int vec = (n % 4 == 0 && aligned16(x) && aligned16(y) && aligned16(gamma) &&
+                     aligned16(beta)) ? vec_for(n) : 0;
+    const dim3 grid((unsigned)rows), block(kBlock);
+    switch (vec) {
+    case 1: hipLaunchKernelGGL(layernorm_vec_kernel<1>, grid, block, 0, stream, x, gamma, beta, eps, (int)n, y); break;
+    case 2: hipLaunchKernelGGL(layernorm_vec_kernel<2>, grid, block, 0, stream, x, gamma, beta, eps, (int)n, y); break;
+    case 4: hipLaunchKernelGGL(layernorm_vec_kernel<4>, grid, block, 0, stream, x, gamma, beta, eps, (int)n, y); break;
+    case 8: hipLaunchKernelGGL(layernorm_vec_kernel<8>, grid, block, 0, stream, x, gamma, beta, eps, (int)n, y); break;
+    default: hipLaunchKernelGGL(layernorm_any_kernel, grid, block, 0, stream, x, gamma, beta, eps, n, y); break;
+    }
+    return hipGetLastError();
+}
+
+__global__ __launch_bounds__(kBlock) void silu_mul_kernel(const float* g, const float* u, int64_t n,
+                                                          float* out) {
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i < n) {
+        const float t = g[i];
+        out[i] = t / (1.0f + expf(-t)) * u[i];
+    }
+}
+
+hipError_t launch_silu_mul(const float* g, const float* u, int64_t n, float* out,
+                           hipStream_t stream) {
+    hipLaunchKernelGGL(silu_mul_kernel, dim3((unsigned)((n + kBlock - 1) / kBlock)), dim3(kBlock),
+                       0, stream, g, u, n, out);
+    return hipGetLastError();
+}
+
+}  // namespace mbq

@@ -1,0 +1,203 @@
+"""Host-side tests of libmbq: it loads, exports every declared symbol, its
+packer/unpacker agree bit for bit with the oracle's, and every argument check
+returns its documented status before any device work is enqueued.
+
+No GPU is touched: pointer arguments here are fake device addresses that the
+library only inspects (alignment, overlap), never dereferences.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from memory_bound_quantized_amd import _lib
+import memory_bound_quantized_amd as mbq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+L = _lib.lib
+
+
+def _declared_symbols():
+    with open(os.path.join(ROOT, "include", "mbq.h")) as fh:
+        text = fh.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mbq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    declared = _declared_symbols()
+    assert len(declared) == 16
+    assert sorted(_lib.EXPORTS) == declared
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert mbq.version() == 1
+
+
+def test_format_info_and_plane_sizes_match_oracle():
+    for fmt, bpw, bk in [(0, 16.0, 1), (1, 4.5, 32), (2, 6.5625, 256), (3, 2.5, 32)]:
+        assert mbq.format_info(fmt) == (bpw, bk)
+        for N, K in [(0, 256), (1, 256), (7, 512), (12288, 4096), (4096, 12288)]:
+            assert mbq.plane_sizes(fmt, N, K) == oracle.plane_bytes(fmt, N, K)
+
+
+def _random_codes(fmt, N, K, rng):
+    if fmt == 0:
+        return rng.integers(0, 65536, size=(N, K), dtype=np.uint16), None, None
+    bits = {1: 4, 2: 6, 3: 2}[fmt]
+    codes = rng.integers(0, 1 << bits, size=(N, K), dtype=np.uint8)
+    if fmt == 2:
+        sc = rng.integers(-128, 128, size=N * K // 16).astype(np.int8)
+        su = np.float16(rng.uniform(0.001, 0.02, N * K // 256)).view(np.uint16)
+        return codes, sc, su
+    return codes, np.float16(rng.uniform(0.001, 0.02, N * K // 32)).view(np.uint16), None
+
+
+@pytest.mark.parametrize("fmt,N,K", [(1, 1, 32), (1, 5, 96), (1, 3, 4096), (2, 1, 256),
+                                     (2, 3, 512), (2, 2, 12288), (3, 1, 32), (3, 7, 160),
+                                     (0, 3, 24)])
+def test_host_pack_matches_oracle_pack_bit_for_bit(fmt, N, K):
+    rng = np.random.default_rng(fmt * 1000 + N * 10 + K)
+    codes, sc, su = _random_codes(fmt, N, K, rng)
+    mine = mbq.pack(fmt, N, K, codes, sc, su)
+    ref = oracle.pack(fmt, N, K, codes, sc, su)
+    for a, b in zip(mine, ref.planes):
+        assert (a is None) == (b is None)
+        if a is not None:
+            assert np.array_equal(a, b)
+    c2, s2, u2 = mbq.unpack(fmt, N, K, mine)
+    assert np.array_equal(c2, codes)
+    if sc is not None:
+        assert np.array_equal(s2.view(np.uint8), np.asarray(sc).view(np.uint8))
+    if su is not None:
+        assert np.array_equal(u2, su)
+
+
+@pytest.mark.parametrize("fmt", [1, 2, 3])
+def test_host_unpack_of_random_planes_matches_oracle_codes(fmt):
+    rng = np.random.default_rng(40 + fmt)
+    N, K = 6, 512
+    planes = workloads.weight_planes(rng, fmt, N, K)
+    codes, _, _ = mbq.unpack(fmt, N, K, planes)
+    assert np.array_equal(codes, oracle.codes(oracle.Planes(fmt, N, K, planes)))
+
+
+def test_pack_rejects_codes_wider_than_the_format():
+    for fmt, bad in [(1, 16), (2, 64), (3, 4)]:
+        N, K = 1, 256
+        codes = np.zeros((N, K), np.uint8)
+        codes[0, 100] = bad
+        sc = np.zeros(N * K // (16 if fmt == 2 else 32), np.uint16 if fmt != 2 else np.int8)
+        su = np.zeros(N * K // 256, np.uint16) if fmt == 2 else None
+        with pytest.raises(mbq.MbqError) as ei:
+            mbq.pack(fmt, N, K, codes, sc, su)
+        assert ei.value.status == _lib.EINVAL
+
+
+# --------------------------------------------------------------------------
+# argument checks (fake, never-dereferenced device addresses)
+# --------------------------------------------------------------------------
+
+BASE = 0x7F0000000000
+
+
+def _desc(fmt=1, N=64, K=256, off=0):
+    return _lib.QWeightDesc(fmt, 0, N, K, BASE + off, BASE + 0x100000 if fmt == 2 else 0,
+                            BASE + 0x200000, BASE + 0x300000 if fmt == 2 else 0)
+
+
+def _gemv(d, x=BASE + 0x400000, M=1, ldx=None, y=BASE + 0x800000, ldy=None, acc=0):
+    return L.mbq_gemv_q(ctypes.byref(d) if d is not None else None, x, M,
+                        d.K if ldx is None and d is not None else (ldx or 0), y,
+                        d.N if ldy is None and d is not None else (ldy or 0), acc, None)
+
+
+def test_gemv_argument_checks():
+    assert _gemv(None) == _lib.EINVAL
+    assert _gemv(_desc(fmt=7)) == _lib.EINVAL
+    assert _gemv(_desc(K=48)) == _lib.EINVAL                    # K not a block multiple
+    assert _gemv(_desc(fmt=2, K=128)) == _lib.EINVAL
+    d = _desc()
+    d.reserved = 1
+    assert _gemv(d) == _lib.EINVAL
+    assert _gemv(_desc(), M=-1) == _lib.EINVAL
+    assert _gemv(_desc(), ldx=100) == _lib.EINVAL               # ldx < K
+    assert _gemv(_desc(), acc=2) == _lib.EINVAL
+    assert _gemv(_desc(), M=0) == _lib.OK                       # empty: nothing enqueued
+    assert _gemv(_desc(N=0)) == _lib.OK
+    assert _gemv(_desc(), x=None) == _lib.EINVAL
+    assert _gemv(_desc(), x=BASE + 0x400004) == _lib.EALIGN     # x not 16-B aligned
+    assert _gemv(_desc(), y=BASE + 0x800002) == _lib.EALIGN
+    assert _gemv(_desc(), y=BASE + 0x400000 + 512) == _lib.EINVAL  # y overlaps x
+    assert _gemv(_desc(off=8)) == _lib.EALIGN                   # plane 0 misaligned
+    d = _desc()
+    d.scales = None
+    assert _gemv(d) == _lib.EINVAL
+    assert _gemv(_desc(fmt=3, K=96)) == _lib.EUNSUPPORTED       # Q25 kernels need K % 64
+    assert _gemv(_desc(fmt=0, K=12)) == _lib.EUNSUPPORTED       # BF16 kernels need K % 8
+    assert _gemv(_desc(K=65536)) == _lib.EUNSUPPORTED           # beyond the LDS-staged K
+    assert _gemv(_desc(), M=9, ldx=256, ldy=64) == _lib.EUNSUPPORTED
+    assert _gemv(_desc(), M=65, ldx=256, ldy=64) == _lib.EUNSUPPORTED
+    assert _gemv(_desc(fmt=2), M=16, ldx=256, ldy=64) == _lib.EUNSUPPORTED
+    assert L.mbq_last_error()
+
+
+def test_gather_argument_checks():
+    d = _desc(N=6 * 32)
+    g = lambda rpe=32, idx=BASE + 0x900000, n=3, x=BASE + 0x400000, y=BASE + 0x800000: \
+        L.mbq_gemv_q_gather(ctypes.byref(d), rpe, idx, n, x, y, None)
+    assert g(rpe=0) == _lib.EINVAL
+    assert g(rpe=40) == _lib.EINVAL                             # N not a multiple
+    assert g(n=0) == _lib.OK
+    assert g(idx=None) == _lib.EINVAL
+    assert g(idx=BASE + 0x900002) == _lib.EALIGN
+    assert g(x=BASE + 0x400008) == _lib.EALIGN
+    assert g(y=BASE + 0x400000) == _lib.EINVAL                  # overlap
+
+
+def test_norm_argument_checks():
+    x, gm, b, y = BASE, BASE + 0x100000, BASE + 0x200000, BASE + 0x300000
+    rms = lambda x=x, g=gm, eps=1e-6, rows=4, n=4096, y=y: L.mbq_rmsnorm(x, g, eps, rows, n, y, None)
+    assert rms(rows=-1) == _lib.EINVAL
+    assert rms(eps=-1.0) == _lib.EINVAL
+    assert rms(eps=float("nan")) == _lib.EINVAL
+    assert rms(eps=float("inf")) == _lib.EINVAL
+    assert rms(rows=0) == _lib.OK
+    assert rms(n=0) == _lib.OK
+    assert rms(g=None) == _lib.EINVAL
+    assert rms(y=x + 2) == _lib.EALIGN
+    assert rms(y=x + 4096) == _lib.EINVAL                      # partial overlap
+    ln = lambda beta=b, y=y: L.mbq_layernorm(x, gm, beta, 1e-5, 4, 2048, y, None)
+    assert ln(beta=None) == _lib.EINVAL
+    assert ln(y=x + 16) == _lib.EINVAL
+    assert L.mbq_silu_mul(x, gm, -1, y, None) == _lib.EINVAL
+    assert L.mbq_silu_mul(x, gm, 0, y, None) == _lib.OK
+    assert L.mbq_silu_mul(x, gm, 1024, x + 64, None) == _lib.EINVAL
+
+
+def test_export_and_probe_argument_checks():
+    d = _desc(fmt=0, K=64)
+    assert L.mbq_unpack_codes(ctypes.byref(d), BASE + 0x900000, None) == _lib.EINVAL  # BF16
+    assert L.mbq_dequant_f32(ctypes.byref(_desc()), BASE + 0x900004, None) == _lib.EALIGN
+    assert L.mbq_dequant_f32(ctypes.byref(_desc(N=0)), None, None) == _lib.OK
+    assert L.mbq_probe_read(BASE, 100, BASE + 0x100000, None) == _lib.EALIGN
+    assert L.mbq_probe_copy(BASE, BASE + 64, 128, None) == _lib.EINVAL
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4):
+        assert L.mbq_status_str(s).startswith(b"MBQ_")
+    assert L.mbq_status_str(5) == b"unknown status"
+
+
+def test_one_hip_runtime_in_the_process():
+    """libmbq binds to the HIP runtime torch already loaded (same SONAME);
+    a second runtime in the process would not see the device torch uses."""
+    import re
+    with open("/proc/self/maps") as fh:
+        libs = set(re.findall(r"\S*libamdhip64\S*", fh.read()))
+    assert len(libs) == 1, libs
