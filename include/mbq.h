@@ -62,10 +62,11 @@ extern "C" {
  * MBQ_FMT_Q65   6.5625 bits/weight, sub-blocks of 16, super-blocks of 256.
  *               codes:    uint8 [N][K/2], low 4 bits of q, nibble order as Q45
  *               codes_hi: uint8 [N][K/4], high 2 bits of q.  Each run of 16
- *                         weights g = k >> 4 owns bytes [4g, 4g+4); with
- *                         r = k & 15 and j = (r & 7) >> 1, byte 4g + j holds
- *                         weight 16g+2j in bits 4-5, 16g+2j+1 in bits 6-7,
- *                         16g+8+2j in bits 0-1 and 16g+8+2j+1 in bits 2-3
+ *                         weights g = k >> 4 owns bytes [4g, 4g+4), read as a
+ *                         little-endian 32-bit word W; weight r = k & 15 of
+ *                         the run keeps its 2 bits at bit pos(r) of W with
+ *                         pos = {4, 2, 12, 10, 20, 18, 28, 26,
+ *                                0, 6, 8, 14, 16, 22, 24, 30}
  *               scales:       int8 [N][K/16] (signed sub-scale sc)
  *               super_scales: fp16 [N][K/256] (d)
  *               q = lo | hi << 4 in 0..63;  w = d[k >> 8] * sc[k >> 4] * (q - 32)
@@ -132,7 +133,8 @@ int mbq_unpack(int fmt, int64_t N, int64_t K, const void* const planes[4],
  * Arithmetic: weights exact in fp32, fp32 accumulation; the order of the sum
  * is unspecified.  M <= 8 runs on the vector units; M >= 16 (Q45 only) may use
  * the matrix cores.  MBQ_EUNSUPPORTED for shapes without a kernel
- * (K > 32768; Q25 with K % 64 != 0; BF16 with K % 8 != 0; 8 < M < 16; M > 64,
+ * (K > 32768, or K > 16384 for BF16; Q25 with K % 64 != 0; BF16 with
+ * K % 8 != 0; 8 < M < 16; M > 64,
  * or M >= 16 with a format other than Q45).  M == 0 or N == 0 enqueue
  * nothing; K == 0 writes zeros (or leaves y for accumulate = 1). */
 int mbq_gemv_q(const mbq_qweight* W, const float* x, int64_t M, int64_t ldx,

@@ -84,9 +84,10 @@ int check_planes(const mbq_qweight* W, const char* fn) {
 
 // Kernel limits common to the GEMV paths and the device exports.
 int check_kernel_shape(const mbq_qweight* W, const char* fn) {
-    if (W->K > mbq::kMaxK)
+    const int64_t kmax = W->fmt == MBQ_FMT_BF16 ? mbq::kMaxKBF16 : mbq::kMaxK;
+    if (W->K > kmax)
         return fail(MBQ_EUNSUPPORTED, "%s: K=%lld exceeds %lld", fn, (long long)W->K,
-                    (long long)mbq::kMaxK);
+                    (long long)kmax);
     if (W->fmt == MBQ_FMT_Q25 && W->K % 64)
         return fail(MBQ_EUNSUPPORTED, "%s: Q25 kernels need K %% 64 == 0", fn);
     if (W->fmt == MBQ_FMT_BF16 && W->K % 8)
@@ -99,26 +100,27 @@ mbq::DevPlanes planes_of(const mbq_qweight* W) {
                           (const uint8_t*)W->scales, (const uint8_t*)W->super_scales};
 }
 
-// Optional geometry override for tuning sweeps: MBQ_GEMV_GEOM="R,G".
+// Optional geometry override for tuning sweeps: MBQ_GEMV_GEOM="R,G,D" (rows
+// per wave, row groups per workgroup, chunk units in flight), read at every
+// call.
 bool geom_override(mbq::GemvGeom* g) {
-    static int R = -1, G = -1;
-    static bool parsed = false;
-    if (!parsed) {
-        const char* s = getenv("MBQ_GEMV_GEOM");
-        int r = 0, gg = 0;
-        if (s && sscanf(s, "%d,%d", &r, &gg) == 2 && (r == 1 || r == 2 || r == 4) && gg >= 1) {
-            R = r;
-            G = gg;
-        }
-        parsed = true;
-    }
-    if (R < 0) return false;
-    g->rows_per_wave = R;
-    g->groups_per_wg = G;
+    const char* s = getenv("MBQ_GEMV_GEOM");
+    int r = 0, gg = 0, d = 2;
+    if (!s || sscanf(s, "%d,%d,%d", &r, &gg, &d) < 2 || !(r == 1 || r == 2 || r == 4) || gg < 1 ||
+        !(d == 2 || d == 4))
+        return false;
+    g->rows_per_wave = r;
+    g->groups_per_wg = gg;
+    g->prefetch = d;
     return true;
 }
 
 // ------------------------------------------------------------ host packer
+
+// Bit of the run's 32-bit high-bits word that holds weight r of a Q65 run of
+// 16 (mbq.h).  The order lets the device assemble four 6-bit codes in the
+// bytes of a dword with at most two shifts, one mask and one and-or.
+constexpr int kQ65HighBit[16] = {4, 2, 12, 10, 20, 18, 28, 26, 0, 6, 8, 14, 16, 22, 24, 30};
 
 void put16(uint8_t* p, uint16_t v) {
     p[0] = (uint8_t)(v & 0xFF);
@@ -198,16 +200,15 @@ int mbq_pack(int fmt, int64_t N, int64_t K, const void* codes, const void* scale
         for (size_t i = 0; i < nk / 4; i++)
             p0[i] = (uint8_t)(q[4 * i] | (q[4 * i + 1] << 2) | (q[4 * i + 2] << 4) | (q[4 * i + 3] << 6));
     } else {
-        // Q65: runs of 16 weights (K % 256 == 0, so runs never span rows).
+        // Q65: runs of 16 weights (K % 256 == 0, so runs never span rows);
+        // the high bits of a run form one little-endian 32-bit word.
         uint8_t* p1 = (uint8_t*)planes[1];
         for (size_t r = 0; r < nk / 16; r++) {
             const uint8_t* c = q + 16 * r;
             for (int i = 0; i < 8; i++) p0[8 * r + i] = (uint8_t)((c[2 * i] & 15) | ((c[2 * i + 1] & 15) << 4));
-            for (int j = 0; j < 4; j++) {
-                const int a = c[2 * j] >> 4, b = c[2 * j + 1] >> 4;
-                const int e = c[8 + 2 * j] >> 4, f = c[8 + 2 * j + 1] >> 4;
-                p1[4 * r + j] = (uint8_t)(e | (f << 2) | (a << 4) | (b << 6));
-            }
+            uint32_t w = 0;
+            for (int k = 0; k < 16; k++) w |= (uint32_t)(c[k] >> 4) << kQ65HighBit[k];
+            for (int j = 0; j < 4; j++) p1[4 * r + j] = (uint8_t)(w >> (8 * j));
         }
     }
     memcpy(planes[2], scales, sz[2]);
@@ -240,17 +241,13 @@ int mbq_unpack(int fmt, int64_t N, int64_t K, const void* const planes[4], void*
         const uint8_t* p1 = (const uint8_t*)planes[1];
         for (size_t r = 0; r < nk / 16; r++) {
             uint8_t* c = q + 16 * r;
+            const uint32_t w = (uint32_t)p1[4 * r] | ((uint32_t)p1[4 * r + 1] << 8) |
+                               ((uint32_t)p1[4 * r + 2] << 16) | ((uint32_t)p1[4 * r + 3] << 24);
             for (int i = 0; i < 8; i++) {
                 c[2 * i] = (uint8_t)(p0[8 * r + i] & 15);
                 c[2 * i + 1] = (uint8_t)(p0[8 * r + i] >> 4);
             }
-            for (int j = 0; j < 4; j++) {
-                const uint8_t h = p1[4 * r + j];
-                c[8 + 2 * j] |= (uint8_t)((h & 3) << 4);
-                c[8 + 2 * j + 1] |= (uint8_t)(((h >> 2) & 3) << 4);
-                c[2 * j] |= (uint8_t)(((h >> 4) & 3) << 4);
-                c[2 * j + 1] |= (uint8_t)(((h >> 6) & 3) << 4);
-            }
+            for (int k = 0; k < 16; k++) c[k] |= (uint8_t)(((w >> kQ65HighBit[k]) & 3) << 4);
         }
     }
     memcpy(scales, planes[2], sz[2]);

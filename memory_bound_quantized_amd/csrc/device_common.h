@@ -48,6 +48,25 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float v) {
+    const int s = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF,
+                                              false);
+    return v + __builtin_bit_cast(float, s);
+}
+
+// Sum over the 64 lanes of a wave with DPP row operations; the total is
+// returned as a wave-uniform value (read from lane 63).
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+    v = dpp_add<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]
+    v = dpp_add<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]
+    v = dpp_add<0x141, 0xF>(v);   // row_half_mirror: 8-lane sums
+    v = dpp_add<0x140, 0xF>(v);   // row_mirror: 16-lane sums
+    v = dpp_add<0x142, 0xA>(v);   // row_bcast:15 into rows 1, 3
+    v = dpp_add<0x143, 0xC>(v);   // row_bcast:31 into rows 2, 3
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
 // Sum over aligned groups of G lanes (G a power of two <= 64).
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {

@@ -41,11 +41,11 @@ __global__ __launch_bounds__(kBlock) void codes_kernel(DevPlanes P, int64_t N, i
     const int64_t row = t / nchunks, b = t - row * nchunks;
     typename T::Row r;
     T::load(r, T::base(P, row, K), (int)b);
-    float q[T::WPC];
+    int q[T::WPC];
     T::codes(r, q);
     uint8_t* o = out + row * K + b * T::WPC;
 #pragma unroll
-    for (int k = 0; k < T::WPC; k++) o[k] = (uint8_t)(int)q[k];
+    for (int k = 0; k < T::WPC; k++) o[k] = (uint8_t)q[k];
 }
 
 hipError_t launch_dequant(int fmt, DevPlanes P, int64_t N, int64_t K, float* w,

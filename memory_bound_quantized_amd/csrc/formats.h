@@ -7,12 +7,19 @@
 // section 3: lanes read consecutive 16-byte chunks).
 //
 // Codes are unpacked in registers and never stored ([roofline-holds]
-// "Hiding, fusing, and keeping the sums busy", Dtypes).  The unpack masks
-// codes into bytes and converts each byte with one v_cvt_f32_ubyteN; bytes
-// that hold a code times a power of two are accumulated separately and
-// rescaled once per block, which is exact.  The block offset is folded out
-// of the inner loop:  sum_k s (q_k - o) x_k = s (sum_k q_k x_k - o sum_k x_k),
-// with the per-block sums of x computed once per workgroup.
+// "Hiding, fusing, and keeping the sums busy", Dtypes).  For the quantized
+// formats the unpack masks four codes at once into the four bytes of a dword
+// ("code vector").  x is held per chunk as 24-bit fixed point: each value is
+// rounded to the integer n = rint(x * 2^e), e chosen per chunk so that the
+// chunk's largest |x| maps into [2^21, 2^22), and n is split into its three
+// two's-complement bytes n = b2 * 2^16 + b1 * 2^8 + b0 (b0, b1 unsigned, b2
+// signed).  One v_dot4_u32_u8 per low byte and one v_dot4_i32_i8 per top byte
+// then form the exact integer sums  sum_k q_k * b_p(k)  of four weights each,
+// so the whole chunk's  sum_k (q_k - offset) n_k  is exact; the offset term
+// -offset * sum_k b_p(k) is precomputed per block and starts the sums.  The
+// only rounding is x to 22 bits relative to its chunk maximum (the same
+// relative precision as the fp16 high/low split of an fp32 value) and the
+// final conversion of each chunk's integer to fp32.
 #pragma once
 
 #include "device_common.h"
@@ -20,17 +27,52 @@
 
 namespace mbq {
 
+__device__ __forceinline__ uint32_t udot4(uint32_t a, uint32_t b, uint32_t c) {
+    return __builtin_amdgcn_udot4(a, b, c, false);
+}
+__device__ __forceinline__ int32_t sdot4(uint32_t a, uint32_t b, int32_t c) {
+    return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
+}
+
+// Sums of the three digit planes of a code vector's chunk, started at the
+// precomputed offset terms i0, i1, i2 (held as raw 32-bit words).
+struct Acc3 {
+    uint32_t a0, a1;
+    int32_t a2;
+};
+
+__device__ __forceinline__ void acc_vec(Acc3& s, uint32_t codes, const uint32_t* dig) {
+    s.a0 = udot4(codes, dig[0], s.a0);
+    s.a1 = udot4(codes, dig[1], s.a1);
+    s.a2 = sdot4(codes, dig[2], s.a2);
+}
+
+// The chunk's integer  sum (q - offset) n  as fp32:  a2 * 2^16 + (a1 * 2^8 + a0).
+__device__ __forceinline__ float acc_value(const Acc3& s) {
+    const int32_t lo = (int32_t)(s.a1 * 256u + s.a0);
+    return fmaf((float)s.a2, 65536.f, (float)lo);
+}
+
 template <int FMT>
 struct Traits;
 
+// Staged x per chunk (dwords, LDS): for every code vector of the chunk its
+// three digit words, then the chunk's metadata.  Vector order per 8 weights
+// (Q45, Q65): the even weights (0, 2, 4, 6) then the odd ones (1, 3, 5, 7).
+
 // ----------------------------------------------------------------- Q45 ----
+// codes dword: byte j = weight 2j (low nibble), 2j+1 (high nibble).
+// Chunk x layout: 4 octets x {E digits 0-2, O digits 0-2} = 24 dwords, then
+// meta [24] = 2^-e (float bits), [25..27] = -8 * (block sums of digits 0-2).
 template <>
 struct Traits<kQ45> {
     static constexpr int WPC = 32;   // weights per chunk
-    static constexpr int F4 = 8;     // float4 of x per chunk
-    static constexpr int NBS = 1;    // block sums per chunk
-    static constexpr int BSG = 8;    // float4 per block sum
-    static constexpr float OFF = 8.f;
+    static constexpr int F4 = 8;     // 16-byte LDS slots per chunk
+    static constexpr int GX = 8;     // x values per staging group
+    static constexpr int BLK = 32;   // weights per offset block
+    static constexpr int OFF = 8;
+    static constexpr int META = 24;  // dword index of the metadata
+    static constexpr bool INT = true;
     struct Row {
         uint4 c;
         uint32_t s;
@@ -43,56 +85,65 @@ struct Traits<kQ45> {
         r.c = *(const uint4*)(B.p0 + 16 * b);
         r.s = *(const uint16_t*)(B.p2 + 2 * b);
     }
-    // dword i: byte j low nibble = weight 8i+2j, high nibble = weight 8i+2j+1
-    __device__ static __forceinline__ uint32_t lo(uint32_t d) { return d & 0x0F0F0F0Fu; }
-    __device__ static __forceinline__ uint32_t hi16(uint32_t d) { return d & 0xF0F0F0F0u; }
-    // sum over the chunk of w_k x_k; mbs[0] = -8 * (sum of the chunk's x)
-    __device__ static __forceinline__ float dot(const Row& r, const float* xv, const float* mbs) {
-        float ae = mbs[0], ao = 0.f;
+    // code vectors of dword d: even weights, odd weights
+    __device__ static __forceinline__ void vectors(uint32_t d, uint32_t& ev, uint32_t& od) {
+        ev = d & 0x0F0F0F0Fu;
+        od = (d >> 4) & 0x0F0F0F0Fu;
+    }
+    // The chunk's contribution to y (xv: the chunk's 32 staged dwords).
+    __device__ static __forceinline__ float dot(const Row& r, const uint32_t* xv) {
         const uint32_t* c = &r.c.x;
+        Acc3 s{xv[META + 1], xv[META + 2], (int32_t)xv[META + 3]};
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            const uint32_t l = lo(c[i]), h = hi16(c[i]);
-            ae = fmaf(ub0(l), xv[8 * i + 0], ae);
-            ao = fmaf(ub0(h), xv[8 * i + 1], ao);
-            ae = fmaf(ub1(l), xv[8 * i + 2], ae);
-            ao = fmaf(ub1(h), xv[8 * i + 3], ao);
-            ae = fmaf(ub2(l), xv[8 * i + 4], ae);
-            ao = fmaf(ub2(h), xv[8 * i + 5], ao);
-            ae = fmaf(ub3(l), xv[8 * i + 6], ae);
-            ao = fmaf(ub3(h), xv[8 * i + 7], ao);
+            uint32_t ev, od;
+            vectors(c[i], ev, od);
+            acc_vec(s, ev, xv + 6 * i);
+            acc_vec(s, od, xv + 6 * i + 3);
         }
-        return h2f(r.s) * fmaf(ao, 0.0625f, ae);
+        return (h2f(r.s) * as_f(xv[META])) * acc_value(s);
     }
     // integer codes of the chunk, through the same unpack as dot()
-    __device__ static __forceinline__ void codes(const Row& r, float* q) {
+    __device__ static __forceinline__ void codes(const Row& r, int* q) {
         const uint32_t* c = &r.c.x;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            const uint32_t l = lo(c[i]), h = hi16(c[i]);
-            q[8 * i + 0] = ub0(l); q[8 * i + 1] = ub0(h) * 0.0625f;
-            q[8 * i + 2] = ub1(l); q[8 * i + 3] = ub1(h) * 0.0625f;
-            q[8 * i + 4] = ub2(l); q[8 * i + 5] = ub2(h) * 0.0625f;
-            q[8 * i + 6] = ub3(l); q[8 * i + 7] = ub3(h) * 0.0625f;
+            uint32_t ev, od;
+            vectors(c[i], ev, od);
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                q[8 * i + 2 * j] = (int)((ev >> (8 * j)) & 0xFFu);
+                q[8 * i + 2 * j + 1] = (int)((od >> (8 * j)) & 0xFFu);
+            }
         }
     }
     __device__ static __forceinline__ void weights(const Row& r, float* w) {
-        float q[WPC];
+        int q[WPC];
         codes(r, q);
         const float s = h2f(r.s);
 #pragma unroll
-        for (int k = 0; k < WPC; k++) w[k] = s * (q[k] - OFF);
+        for (int k = 0; k < WPC; k++) w[k] = s * (float)(q[k] - OFF);
     }
 };
 
 // ----------------------------------------------------------------- Q65 ----
+// ql dwords as Q45 (low 4 bits).  One qh dword h holds the high 2 bits of a
+// 16-weight run whose low bits are ql dwords d0 (weights 0-7) and d1 (8-15):
+// byte j of h carries weight 2j in bits 4-5, 2j+1 in bits 2-3, 8+2j in bits
+// 0-1 and 8+2j+1 in bits 6-7, so every code vector is one mask (plus at most
+// two shifts) away:  q(2j) = lo | (h & 0x30) ...  for the four vectors
+//   E0 = even of d0, O0 = odd of d0, E1 = even of d1, O1 = odd of d1.
+// Chunk x layout as Q45; meta [24] = 2^-e, [25..27] offset terms of the first
+// 16-weight sub-block, [28..30] of the second.
 template <>
 struct Traits<kQ65> {
     static constexpr int WPC = 32;
     static constexpr int F4 = 8;
-    static constexpr int NBS = 2;    // one sum per 16-weight sub-block
-    static constexpr int BSG = 4;
-    static constexpr float OFF = 32.f;
+    static constexpr int GX = 8;
+    static constexpr int BLK = 16;
+    static constexpr int OFF = 32;
+    static constexpr int META = 24;
+    static constexpr bool INT = true;
     struct Row {
         uint4 ql;
         uint2 qh;
@@ -109,83 +160,70 @@ struct Traits<kQ65> {
         r.sc = *(const uint16_t*)(B.p2 + 2 * b);
         r.d = *(const uint16_t*)(B.p3 + 2 * (b >> 3));
     }
-    // One run of 16 weights: low bits in ql dwords d0 (weights 0-7) and d1
-    // (8-15), high bits in qh dword h.  Produces four dwords whose byte j holds
-    //   E0: q(2j)        O0: 4 q(2j+1)      E1: q(8+2j)      O1: 4 q(8+2j+1)
-    __device__ static __forceinline__ void run(uint32_t d0, uint32_t d1, uint32_t h,
-                                               uint32_t& E0, uint32_t& O0, uint32_t& E1,
-                                               uint32_t& O1) {
-        const uint32_t h4 = h << 4;
-        E0 = (d0 & 0x0F0F0F0Fu) | (h & 0x30303030u);
-        O0 = ((d0 >> 2) & 0x3C3C3C3Cu) | (h & 0xC0C0C0C0u);
-        E1 = (d1 & 0x0F0F0F0Fu) | (h4 & 0x30303030u);
-        O1 = ((d1 >> 2) & 0x3C3C3C3Cu) | (h4 & 0xC0C0C0C0u);
+    __device__ static __forceinline__ void vectors(uint32_t d0, uint32_t d1, uint32_t h,
+                                                   uint32_t* v) {
+        v[0] = (d0 & 0x0F0F0F0Fu) | (h & 0x30303030u);
+        v[1] = ((d0 >> 4) & 0x0F0F0F0Fu) | ((h << 2) & 0x30303030u);
+        v[2] = (d1 & 0x0F0F0F0Fu) | ((h << 4) & 0x30303030u);
+        v[3] = ((d1 >> 4) & 0x0F0F0F0Fu) | ((h >> 2) & 0x30303030u);
     }
     __device__ static __forceinline__ float sc_f(uint32_t sc, int sb) {
         return (float)(int)(int8_t)((sc >> (8 * sb)) & 0xFFu);
     }
-    // mbs[sb] = -32 * (sum of x over sub-block sb of the chunk)
-    __device__ static __forceinline__ float dot(const Row& r, const float* xv, const float* mbs) {
+    __device__ static __forceinline__ float dot(const Row& r, const uint32_t* xv) {
         const uint32_t* ql = &r.ql.x;
         const uint32_t* qh = &r.qh.x;
         float t[2];
 #pragma unroll
         for (int sb = 0; sb < 2; sb++) {
-            uint32_t E0, O0, E1, O1;
-            run(ql[2 * sb], ql[2 * sb + 1], qh[sb], E0, O0, E1, O1);
-            const float* xs = xv + 16 * sb;
-            float ae = mbs[sb], ao = 0.f;
-            ae = fmaf(ub0(E0), xs[0], ae);
-            ao = fmaf(ub0(O0), xs[1], ao);
-            ae = fmaf(ub1(E0), xs[2], ae);
-            ao = fmaf(ub1(O0), xs[3], ao);
-            ae = fmaf(ub2(E0), xs[4], ae);
-            ao = fmaf(ub2(O0), xs[5], ao);
-            ae = fmaf(ub3(E0), xs[6], ae);
-            ao = fmaf(ub3(O0), xs[7], ao);
-            ae = fmaf(ub0(E1), xs[8], ae);
-            ao = fmaf(ub0(O1), xs[9], ao);
-            ae = fmaf(ub1(E1), xs[10], ae);
-            ao = fmaf(ub1(O1), xs[11], ao);
-            ae = fmaf(ub2(E1), xs[12], ae);
-            ao = fmaf(ub2(O1), xs[13], ao);
-            ae = fmaf(ub3(E1), xs[14], ae);
-            ao = fmaf(ub3(O1), xs[15], ao);
-            t[sb] = fmaf(ao, 0.25f, ae);
+            uint32_t v[4];
+            vectors(ql[2 * sb], ql[2 * sb + 1], qh[sb], v);
+            Acc3 s{xv[META + 1 + 3 * sb], xv[META + 2 + 3 * sb], (int32_t)xv[META + 3 + 3 * sb]};
+#pragma unroll
+            for (int i = 0; i < 4; i++) acc_vec(s, v[i], xv + 12 * sb + 3 * i);
+            t[sb] = acc_value(s);
         }
-        return h2f(r.d) * fmaf(sc_f(r.sc, 1), t[1], sc_f(r.sc, 0) * t[0]);
+        return (h2f(r.d) * as_f(xv[META])) * fmaf(sc_f(r.sc, 1), t[1], sc_f(r.sc, 0) * t[0]);
     }
-    __device__ static __forceinline__ void codes(const Row& r, float* q) {
+    __device__ static __forceinline__ void codes(const Row& r, int* q) {
         const uint32_t* ql = &r.ql.x;
         const uint32_t* qh = &r.qh.x;
 #pragma unroll
         for (int sb = 0; sb < 2; sb++) {
-            uint32_t E0, O0, E1, O1;
-            run(ql[2 * sb], ql[2 * sb + 1], qh[sb], E0, O0, E1, O1);
-            float* o = q + 16 * sb;
-            o[0] = ub0(E0); o[1] = ub0(O0) * 0.25f; o[2] = ub1(E0); o[3] = ub1(O0) * 0.25f;
-            o[4] = ub2(E0); o[5] = ub2(O0) * 0.25f; o[6] = ub3(E0); o[7] = ub3(O0) * 0.25f;
-            o[8] = ub0(E1); o[9] = ub0(O1) * 0.25f; o[10] = ub1(E1); o[11] = ub1(O1) * 0.25f;
-            o[12] = ub2(E1); o[13] = ub2(O1) * 0.25f; o[14] = ub3(E1); o[15] = ub3(O1) * 0.25f;
+            uint32_t v[4];
+            vectors(ql[2 * sb], ql[2 * sb + 1], qh[sb], v);
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                q[16 * sb + 2 * j] = (int)((v[0] >> (8 * j)) & 0xFFu);
+                q[16 * sb + 2 * j + 1] = (int)((v[1] >> (8 * j)) & 0xFFu);
+                q[16 * sb + 8 + 2 * j] = (int)((v[2] >> (8 * j)) & 0xFFu);
+                q[16 * sb + 8 + 2 * j + 1] = (int)((v[3] >> (8 * j)) & 0xFFu);
+            }
         }
     }
     __device__ static __forceinline__ void weights(const Row& r, float* w) {
-        float q[WPC];
+        int q[WPC];
         codes(r, q);
         const float d = h2f(r.d);
 #pragma unroll
-        for (int k = 0; k < WPC; k++) w[k] = d * sc_f(r.sc, k >> 4) * (q[k] - OFF);
+        for (int k = 0; k < WPC; k++) w[k] = d * sc_f(r.sc, k >> 4) * (float)(q[k] - OFF);
     }
 };
 
 // ----------------------------------------------------------------- Q25 ----
+// codes dword: weights 0-15, byte j holds 4j..4j+3 in bits 0-1, 2-3, 4-5, 6-7;
+// code vector m (m = 0..3) = (d >> 2m) & 0x03030303 holds weights
+// (m, 4+m, 8+m, 12+m).  Chunk x layout: 4 dwords x 4 vectors x 3 digits = 48
+// dwords, meta [48] = 2^-e, [49..51] offset terms of block 0, [52..54] block 1.
 template <>
 struct Traits<kQ25> {
     static constexpr int WPC = 64;
     static constexpr int F4 = 16;
-    static constexpr int NBS = 2;    // one sum per 32-weight block
-    static constexpr int BSG = 8;
-    static constexpr float OFF = 2.f;
+    static constexpr int GX = 16;
+    static constexpr int BLK = 32;
+    static constexpr int OFF = 2;
+    static constexpr int META = 48;
+    static constexpr bool INT = true;
     struct Row {
         uint4 c;
         uint32_t s2;   // the chunk's two fp16 scales
@@ -197,65 +235,57 @@ struct Traits<kQ25> {
         r.c = *(const uint4*)(B.p0 + 16 * b);
         r.s2 = *(const uint32_t*)(B.p2 + 4 * b);
     }
-    // dword i holds weights 16i..16i+15; byte j holds 16i+4j+{0,1,2,3} in
-    // bits {0-1, 2-3, 4-5, 6-7}: masked, the byte is q, 4q, 16q or 64q.
-    __device__ static __forceinline__ float dot(const Row& r, const float* xv, const float* mbs) {
+    __device__ static __forceinline__ uint32_t vec(uint32_t d, int m) {
+        return (d >> (2 * m)) & 0x03030303u;
+    }
+    __device__ static __forceinline__ float dot(const Row& r, const uint32_t* xv) {
         const uint32_t* c = &r.c.x;
         float t[2];
 #pragma unroll
         for (int blk = 0; blk < 2; blk++) {
-            float a0 = mbs[blk], a1 = 0.f, a2 = 0.f, a3 = 0.f;
+            Acc3 s{xv[META + 1 + 3 * blk], xv[META + 2 + 3 * blk], (int32_t)xv[META + 3 + 3 * blk]};
 #pragma unroll
             for (int ii = 0; ii < 2; ii++) {
                 const int i = 2 * blk + ii;
-                const uint32_t d = c[i];
-                const uint32_t m0 = d & 0x03030303u, m1 = d & 0x0C0C0C0Cu;
-                const uint32_t m2 = d & 0x30303030u, m3 = d & 0xC0C0C0C0u;
-                const float* xs = xv + 16 * i;
-                a0 = fmaf(ub0(m0), xs[0], a0);  a1 = fmaf(ub0(m1), xs[1], a1);
-                a2 = fmaf(ub0(m2), xs[2], a2);  a3 = fmaf(ub0(m3), xs[3], a3);
-                a0 = fmaf(ub1(m0), xs[4], a0);  a1 = fmaf(ub1(m1), xs[5], a1);
-                a2 = fmaf(ub1(m2), xs[6], a2);  a3 = fmaf(ub1(m3), xs[7], a3);
-                a0 = fmaf(ub2(m0), xs[8], a0);  a1 = fmaf(ub2(m1), xs[9], a1);
-                a2 = fmaf(ub2(m2), xs[10], a2); a3 = fmaf(ub2(m3), xs[11], a3);
-                a0 = fmaf(ub3(m0), xs[12], a0); a1 = fmaf(ub3(m1), xs[13], a1);
-                a2 = fmaf(ub3(m2), xs[14], a2); a3 = fmaf(ub3(m3), xs[15], a3);
+#pragma unroll
+                for (int m = 0; m < 4; m++) acc_vec(s, vec(c[i], m), xv + 12 * i + 3 * m);
             }
-            t[blk] = fmaf(a3, 0.015625f, fmaf(a2, 0.0625f, fmaf(a1, 0.25f, a0)));
+            t[blk] = acc_value(s);
         }
-        return fmaf(h2f(r.s2 >> 16), t[1], h2f(r.s2) * t[0]);
+        return as_f(xv[META]) * fmaf(h2f(r.s2 >> 16), t[1], h2f(r.s2) * t[0]);
     }
-    __device__ static __forceinline__ void codes(const Row& r, float* q) {
+    __device__ static __forceinline__ void codes(const Row& r, int* q) {
         const uint32_t* c = &r.c.x;
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const uint32_t d = c[i];
-            const uint32_t m0 = d & 0x03030303u, m1 = d & 0x0C0C0C0Cu;
-            const uint32_t m2 = d & 0x30303030u, m3 = d & 0xC0C0C0C0u;
-            float* o = q + 16 * i;
-            o[0] = ub0(m0); o[1] = ub0(m1) * 0.25f; o[2] = ub0(m2) * 0.0625f; o[3] = ub0(m3) * 0.015625f;
-            o[4] = ub1(m0); o[5] = ub1(m1) * 0.25f; o[6] = ub1(m2) * 0.0625f; o[7] = ub1(m3) * 0.015625f;
-            o[8] = ub2(m0); o[9] = ub2(m1) * 0.25f; o[10] = ub2(m2) * 0.0625f; o[11] = ub2(m3) * 0.015625f;
-            o[12] = ub3(m0); o[13] = ub3(m1) * 0.25f; o[14] = ub3(m2) * 0.0625f; o[15] = ub3(m3) * 0.015625f;
-        }
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int m = 0; m < 4; m++) {
+                const uint32_t v = vec(c[i], m);
+#pragma unroll
+                for (int j = 0; j < 4; j++) q[16 * i + 4 * j + m] = (int)((v >> (8 * j)) & 0xFFu);
+            }
     }
     __device__ static __forceinline__ void weights(const Row& r, float* w) {
-        float q[WPC];
+        int q[WPC];
         codes(r, q);
         const float s0 = h2f(r.s2), s1 = h2f(r.s2 >> 16);
 #pragma unroll
-        for (int k = 0; k < WPC; k++) w[k] = (k < 32 ? s0 : s1) * (q[k] - OFF);
+        for (int k = 0; k < WPC; k++) w[k] = (k < 32 ? s0 : s1) * (float)(q[k] - OFF);
     }
 };
 
 // ---------------------------------------------------------------- BF16 ----
+// 16 bits per weight leave ample arithmetic per byte: x stays fp32 and each
+// weight is one shift or mask plus one fp32 FMA.  Chunk x layout: 8 floats.
 template <>
 struct Traits<kBF16> {
     static constexpr int WPC = 8;
     static constexpr int F4 = 2;
-    static constexpr int NBS = 0;
-    static constexpr int BSG = 1;
-    static constexpr float OFF = 0.f;
+    static constexpr int GX = 8;
+    static constexpr int BLK = 8;
+    static constexpr int OFF = 0;
+    static constexpr int META = 0;
+    static constexpr bool INT = false;
     struct Row {
         uint4 w;
     };
@@ -265,13 +295,13 @@ struct Traits<kBF16> {
     __device__ static __forceinline__ void load(Row& r, const DevPlanes& B, int b) {
         r.w = *(const uint4*)(B.p0 + 16 * b);
     }
-    __device__ static __forceinline__ float dot(const Row& r, const float* xv, const float*) {
+    __device__ static __forceinline__ float dot(const Row& r, const uint32_t* xv) {
         const uint32_t* c = &r.w.x;
         float a0 = 0.f, a1 = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            a0 = fmaf(as_f(c[i] << 16), xv[2 * i], a0);
-            a1 = fmaf(as_f(c[i] & 0xFFFF0000u), xv[2 * i + 1], a1);
+            a0 = fmaf(as_f(c[i] << 16), as_f(xv[2 * i]), a0);
+            a1 = fmaf(as_f(c[i] & 0xFFFF0000u), as_f(xv[2 * i + 1]), a1);
         }
         return a0 + a1;
     }
@@ -285,16 +315,47 @@ struct Traits<kBF16> {
     }
 };
 
-// Physical float4 slot, within LDS, of float4 j of chunk b.  Lanes read their
-// chunk's x at a stride of F4 float4; rotating the slot by the chunk index
-// spreads eight consecutive lanes over all banks.
+// ------------------------------------------------------------- x staging --
+
+// Chunk exponent for a largest |x| with biased exponent E (0: zero or
+// subnormal): e = 148 - E maps it into [2^21, 2^22); clamped to <= 126 so
+// 2^e and 2^-e are normal floats (values below 2^-126 then round to 0 or
+// +-1 units of 2^-126).
+__device__ __forceinline__ int chunk_exp(float amax) {
+    const int E = (int)((__builtin_bit_cast(uint32_t, amax) >> 23) & 0xFFu);
+    const int e = 148 - E;
+    return e > 126 ? 126 : e;
+}
+__device__ __forceinline__ float pow2f(int e) {
+    return __builtin_bit_cast(float, (uint32_t)(e + 127) << 23);
+}
+
+// Byte p (p = 0, 1, 2) of four 32-bit integers, packed into one word.
+__device__ __forceinline__ void digit_words(int32_t n0, int32_t n1, int32_t n2, int32_t n3,
+                                            uint32_t* dg) {
+    const uint32_t t01 = __builtin_amdgcn_perm((uint32_t)n1, (uint32_t)n0, 0x05010400u);
+    const uint32_t t23 = __builtin_amdgcn_perm((uint32_t)n3, (uint32_t)n2, 0x05010400u);
+    const uint32_t u01 = __builtin_amdgcn_perm((uint32_t)n1, (uint32_t)n0, 0x06020602u);
+    const uint32_t u23 = __builtin_amdgcn_perm((uint32_t)n3, (uint32_t)n2, 0x06020602u);
+    dg[0] = __builtin_amdgcn_perm(t23, t01, 0x05040100u);
+    dg[1] = __builtin_amdgcn_perm(t23, t01, 0x07060302u);
+    dg[2] = __builtin_amdgcn_perm(u23, u01, 0x05040100u);
+}
+
+// LDS slots (16 bytes) per chunk: one more than the chunk's data, so that
+// lanes reading consecutive chunks at that stride (36, 68 or 12 dwords) hit
+// distinct banks for any 16 consecutive lanes.
 template <int FMT>
-__device__ __forceinline__ int x_slot(int b, int j) {
-    constexpr int F4 = Traits<FMT>::F4;
-    if constexpr (F4 >= 8)
-        return F4 * b + (j ^ (b & 7));
-    else
-        return F4 * b + (j ^ ((b >> 2) & (F4 - 1)));
+struct Stride {
+    static constexpr int SLOTS = Traits<FMT>::F4 + 1;
+    static constexpr int DW = 4 * SLOTS;   // dwords per chunk
+};
+
+// Round x * 2^e to the nearest integer (ties to even) with one FMA: adding
+// 1.5 * 2^23 leaves the integer in the low mantissa bits for |x 2^e| < 2^22.
+__device__ __forceinline__ int32_t round_fixed(float v, float up) {
+    const float t = fmaf(v, up, 12582912.0f);
+    return (int32_t)(__builtin_bit_cast(uint32_t, t) - 0x4B400000u);
 }
 
 }  // namespace mbq

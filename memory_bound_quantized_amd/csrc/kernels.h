@@ -18,13 +18,16 @@ struct DevPlanes {
     const uint8_t* p3;  // super_scales
 };
 
-// Largest K the GEMV kernels stage in LDS.
+// Largest K the GEMV kernels stage in LDS (x takes 4.5 bytes per value for the
+// quantized formats, 6 for BF16, within the 160 KiB of LDS per workgroup).
 constexpr int64_t kMaxK = 32768;
+constexpr int64_t kMaxKBF16 = 16384;
 
 // Geometry of the M = 1 GEMV: rows per wave and row groups per workgroup.
 struct GemvGeom {
     int rows_per_wave;   // 1, 2 or 4
     int groups_per_wg;   // >= 1
+    int prefetch;        // chunk units in flight per wave: 2 or 4
 };
 
 GemvGeom gemv_m1_default_geom(int fmt, int64_t N, int64_t K);

@@ -83,19 +83,16 @@ static uint16_t rd16(const void* base, size_t idx)
 }
 
 /* High 2 bits of the 6-bit code of weight k within one row of a Q65 qh plane.
- * Each run of 16 weights g = k>>4 owns the 4 bytes qh[4g .. 4g+3].  With
- * r = k & 15, j = (r & 7) >> 1, byte qh[4g + j] holds:
- *   bits 4-5: weight 16g + 2j        bits 6-7: weight 16g + 2j + 1
- *   bits 0-1: weight 16g + 8 + 2j    bits 2-3: weight 16g + 8 + 2j + 1  */
+ * Each run of 16 weights g = k>>4 owns the 4 bytes qh[4g .. 4g+3], read as a
+ * little-endian 32-bit word W; weight r = k & 15 of the run keeps its high
+ * bits at bit Q65_POS[r] of W (bits POS and POS+1). */
+static const int Q65_POS[16] = {4, 2, 12, 10, 20, 18, 28, 26, 0, 6, 8, 14, 16, 22, 24, 30};
+
 static int q65_hi(const uint8_t* qh_row, int64_t k)
 {
     int64_t g = k >> 4;
-    int r = (int)(k & 15);
-    int j = (r & 7) >> 1;
-    int odd = r & 1;
-    int upper = r >> 3;
-    int shift = (upper ? 0 : 4) + (odd ? 2 : 0);
-    return (qh_row[4 * g + j] >> shift) & 3;
+    int pos = Q65_POS[k & 15];
+    return (qh_row[4 * g + pos / 8] >> (pos % 8)) & 3;
 }
 
 /* Integer code of weight (n, k).  BF16 has no code (returns -1). */
@@ -213,10 +210,8 @@ int oracle_pack(int fmt, int64_t N, int64_t K, const uint8_t* codes,
                 uint8_t* qh = (uint8_t*)planes[1] + n * (K / 4);
                 ql[k >> 1] |= (uint8_t)((q & 15) << (4 * (k & 1)));
                 int64_t g = k >> 4;
-                int r = (int)(k & 15);
-                int j = (r & 7) >> 1;
-                int shift = ((r >> 3) ? 0 : 4) + ((r & 1) ? 2 : 0);
-                qh[4 * g + j] |= (uint8_t)((q >> 4) << shift);
+                int pos = Q65_POS[k & 15];
+                qh[4 * g + pos / 8] |= (uint8_t)((q >> 4) << (pos % 8));
             }
         }
     }

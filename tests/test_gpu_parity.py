@@ -39,6 +39,32 @@ def rel_l2(got, ref):
     return np.linalg.norm(got - ref) / (den if den > 0 else 1.0)
 
 
+def check_gemv(y, ow, x, ref, y0=None):
+    """Two bars on a GEMV output.
+    (1) every element lies within the forward-error bound of fp32 arithmetic,
+        |y - y_ref| <= ((K + 4) 2^-24 + 2^-22) sum_k |w_k x_k| (+ |y0|), for any
+        summation order, plus the fp16 high/low split of x (relative 2^-22);
+    (2) the relative L2 error over the output vector is <= 1e-4 whenever the
+        vector has at least 16 entries.  A single output can be arbitrarily
+        ill-conditioned (its value near zero against large terms), so no fp32
+        kernel can promise (2) for one entry; (1) is the bar there."""
+    x = np.atleast_2d(np.asarray(x, np.float64))
+    y = np.atleast_2d(np.asarray(y, np.float64))
+    ref = np.atleast_2d(np.asarray(ref, np.float64))
+    absw = np.abs(oracle.dequant(ow).astype(np.float64))
+    mag = np.abs(x) @ absw.T
+    if y0 is not None:
+        mag = mag + np.abs(np.atleast_2d(np.asarray(y0, np.float64)))
+    bound = ((ow.K + 4) * 2.0 ** -24 + 2.0 ** -22) * mag + 1e-30
+    worst = np.max(np.abs(y - ref) / bound)
+    assert worst <= 1.0, "element outside the fp32 forward-error bound (ratio %.3g)" % worst
+    if y.size >= 16:
+        e = rel_l2(y, ref)
+        assert e <= GEMV_RTOL, "rel-L2 %.3e" % e
+        return e
+    return None
+
+
 def dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
@@ -83,11 +109,11 @@ def test_device_dequant_of_hand_fixtures(golden_dir):
 # --------------------------------------------------------------------------
 
 GEMV_CASES = [
-    (1, 1, 32), (1, 37, 512), (1, 300, 4096), (1, 1000, 2080), (1, 2500, 4096),
+    (1, 1, 32), (1, 64, 32), (1, 37, 512), (1, 300, 4096), (1, 1000, 2080), (1, 2500, 4096),
     (1, 9000, 256), (1, 70000, 256), (1, 64, 12288),
-    (2, 1, 256), (2, 37, 512), (2, 300, 4096), (2, 2500, 2304), (2, 9000, 256), (2, 40, 12288),
-    (3, 1, 64), (3, 37, 512), (3, 300, 4096), (3, 2500, 4160), (3, 9000, 256),
-    (0, 1, 8), (0, 37, 520), (0, 512, 4096), (0, 3000, 1024),
+    (2, 1, 256), (2, 64, 256), (2, 37, 512), (2, 300, 4096), (2, 2500, 2304), (2, 9000, 256), (2, 40, 12288),
+    (3, 1, 64), (3, 64, 64), (3, 37, 512), (3, 300, 4096), (3, 2500, 4160), (3, 9000, 256),
+    (0, 1, 8), (0, 64, 8), (0, 37, 520), (0, 512, 4096), (0, 3000, 1024),
 ]
 
 
@@ -97,7 +123,7 @@ def test_gemv_m1_matches_oracle(fmt, N, K):
     x = np.random.default_rng(N + K).normal(size=K).astype(np.float32)
     y = mbq().gemv_q(dw, dev(x)).cpu().numpy()
     ref = oracle.gemv_parallel(ow, x)[0]
-    assert rel_l2(y, ref) <= GEMV_RTOL
+    check_gemv(y, ow, x, ref)
 
 
 @pytest.mark.parametrize("fmt", [0, 1, 2, 3])
@@ -110,7 +136,7 @@ def test_gemv_m1_accumulate(fmt):
     yd = dev(y0)
     mbq().gemv_q(dw, dev(x), out=yd, accumulate=True)
     ref = oracle.gemv(ow, x, y0=y0)[0]
-    assert rel_l2(yd.cpu().numpy(), ref) <= GEMV_RTOL
+    check_gemv(yd.cpu().numpy(), ow, x, ref, y0=y0)
 
 
 def test_gemv_k_zero_and_empty():
@@ -150,9 +176,8 @@ def test_workload2_full_size():
         dw = mbq().QWeight.from_host(fmt, N, K, planes)
         y = mbq().gemv_q(dw, dev(cfg[xkey])).cpu().numpy()
         ref = oracle.gemv_parallel(ow, cfg[xkey])[0]
-        e = rel_l2(y, ref)
+        e = check_gemv(y, ow, cfg[xkey], ref)
         print("workload2 %s rel_l2=%.3e" % (key, e))
-        assert e <= GEMV_RTOL
 
 
 def test_workload1_full_size():
@@ -165,8 +190,11 @@ def test_workload1_full_size():
     fmt, N, K, planes = cfg["W"]
     dw = mbq().QWeight.from_host(fmt, N, K, planes)
     y = mbq().gemv_q(dw, h).cpu().numpy()
-    ref = oracle.gemv(oracle.Planes(fmt, N, K, planes), h_ref)[0]
-    assert rel_l2(y, ref) <= GEMV_RTOL
+    ow = oracle.Planes(fmt, N, K, planes)
+    ref = oracle.gemv(ow, h.cpu().numpy())[0]
+    check_gemv(y, ow, h.cpu().numpy(), ref)
+    # and against the chain computed entirely by the oracle
+    assert rel_l2(y, oracle.gemv(ow, h_ref)[0]) <= GEMV_RTOL
 
 
 def test_workload5_full_size():
@@ -181,7 +209,7 @@ def test_workload5_full_size():
     for i, e in enumerate(idx):
         sub = oracle.Planes(fmt, R, K, [None if p is None else p.reshape(N, -1)[e * R:(e + 1) * R].reshape(-1)
                                         for p in planes])
-        assert rel_l2(y[i], oracle.gemv_parallel(sub, cfg["x"])[0]) <= GEMV_RTOL
+        check_gemv(y[i], sub, cfg["x"], oracle.gemv_parallel(sub, cfg["x"])[0])
     yl = mbq().layernorm(dev(cfg["ln_x"]), dev(cfg["ln_gamma"]), dev(cfg["ln_beta"]), cfg["ln_eps"])
     ref = oracle.layernorm(cfg["ln_x"], cfg["ln_gamma"], cfg["ln_beta"], cfg["ln_eps"])
     assert np.max(np.abs(yl.cpu().numpy() - ref)) <= NORM_ATOL
@@ -195,6 +223,10 @@ def test_gather_small_matches_oracle_gather():
         x = np.random.default_rng(1).normal(size=K).astype(np.float32)
         y = mbq().gemv_q_gather(dw, R, dev(idx), dev(x)).cpu().numpy()
         assert rel_l2(y, oracle.gather(ow, R, idx, x)) <= GEMV_RTOL
+        for i, e in enumerate(idx):
+            sub = oracle.Planes(fmt, R, K, [None if p is None else p.reshape(E * R, -1)[e * R:(e + 1) * R].reshape(-1)
+                                            for p in ow.planes])
+            check_gemv(y[i], sub, x, oracle.gemv(sub, x)[0])
 
 
 # --------------------------------------------------------------------------
