@@ -118,17 +118,106 @@ def cpu_baseline(cfg, y_up_gpu, y_down_gpu, budget_s: float = 12.0):
             "checked_rel_l2": {"q45_up": err_u, "q65_down": err_d}}
 
 
+COPY_BYTES = 1 << 29            # plain copy of known size that calibrates the counters
+
+
+def kernel_key(name: str):
+    """Which GEMV of the step a counter row belongs to (by format argument)."""
+    if "gemv_m1_kernel<1," in name:
+        return "q45_up_12288x4096"
+    if "gemv_m1_kernel<2," in name:
+        return "q65_down_4096x12288"
+    if "probe_copy_kernel" in name:
+        return "copy"
+    return None
+
+
+def traffic_pass():
+    """Launches profiled by the counter runs: each GEMV once per rotated weight
+    copy (cold, no graph) and one copy of COPY_BYTES bytes."""
+    import torch
+    import memory_bound_quantized_amd as mbq
+    import workloads
+    dev = torch.device("cuda:0")
+    cfg = workloads.config2()
+    W_up0 = mbq.QWeight.from_host(*cfg["up"])
+    W_dn0 = mbq.QWeight.from_host(*cfg["down"])
+    ncopy = max(2, -(-ROTATION_BYTES // (W_up0.nbytes + W_dn0.nbytes)))
+    ups = [W_up0] + [W_up0.clone() for _ in range(ncopy - 1)]
+    dns = [W_dn0] + [W_dn0.clone() for _ in range(ncopy - 1)]
+    x_up = torch.from_numpy(cfg["x_up"]).to(dev)
+    x_dn = torch.from_numpy(cfg["x_down"]).to(dev)
+    y_up = torch.empty(W_up0.N, device=dev)
+    y_dn = torch.empty(W_dn0.N, device=dev)
+    for i in range(ncopy):
+        mbq.gemv_q(ups[i], x_up, out=y_up)
+        mbq.gemv_q(dns[i], x_dn, out=y_dn)
+    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    mbq.probe_copy(dst, src)
+    torch.cuda.synchronize()
+    print("traffic pass: %d launches of each GEMV, one %d-byte copy" % (ncopy, COPY_BYTES))
+
+
+def write_traffic(fetch_dir: str, write_dir: str):
+    """HBM bytes per launch from a FETCH_SIZE run and a WRITE_SIZE run of
+    traffic_pass (rocprofv3 --pmc, KiB per dispatch), each scaled by what
+    the same counter reads for the copy of COPY_BYTES bytes."""
+    import csv
+    import glob
+
+    def per_dispatch(d, counter):
+        acc = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    k = kernel_key(r.get("Kernel_Name", ""))
+                    if k is None or r["Counter_Name"] != counter:
+                        continue
+                    acc.setdefault(k, []).append(float(r["Counter_Value"]) * 1024.0)
+        return {k: sum(v) / len(v) for k, v in acc.items()}
+
+    fetch = per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = per_dispatch(write_dir, "WRITE_SIZE")
+    f_scale = COPY_BYTES / fetch["copy"]
+    w_scale = COPY_BYTES / write["copy"]
+    out = {"kernel_source_hash": kernel_source_hash(),
+           "copy_bytes": COPY_BYTES,
+           "copy_counter_bytes": {"FETCH_SIZE": fetch["copy"], "WRITE_SIZE": write["copy"]},
+           "scale": {"FETCH_SIZE": f_scale, "WRITE_SIZE": w_scale},
+           "kernels": {}}
+    for k in ("q45_up_12288x4096", "q65_down_4096x12288"):
+        fb, wb = fetch[k] * f_scale, write[k] * w_scale
+        out["kernels"][k] = {"fetch_bytes": round(fb), "write_bytes": round(wb),
+                             "hbm_bytes_per_launch": round(fb + wb)}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-pass", action="store_true",
+                    help="only the launches that the counter runs profile")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc outputs into the traffic file")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(every box has one MI355X); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    if args.traffic_pass:
+        traffic_pass()
+        return
 
     import torch
     import memory_bound_quantized_amd as mbq
