@@ -152,6 +152,51 @@ int mbq_gemv_q_gather(const mbq_qweight* W_all, int64_t rows_per_expert,
                       const int32_t* idx, int64_t n_sel, const float* x,
                       float* y, void* stream);
 
+/* ------------------------------------------------------------ staged x
+ * The quantized products consume x in a "staged" form: per chunk of 32
+ * values (64 for Q25) a power-of-two scale 2^-e and the 24-bit integers
+ * n = rint(x * 2^e) split into three byte digits, laid out in the order of the
+ * format's code vectors, plus the offset terms of each block.  e is chosen so
+ * the chunk's largest |x| lies in [2^21, 2^22) (x is rounded to 22 bits
+ * relative to its chunk maximum; nothing else is rounded before the fp32
+ * sums).  Staging once in the kernel that produces x, instead of in every
+ * workgroup of the product, is the fusion of the small kernels between weight
+ * reads into their neighbours ([roofline-holds] "Hiding, fusing, and keeping
+ * the sums busy").  The form is opaque and format-specific: stage for the
+ * format of the matrix that consumes it.  It takes 4 bytes per value
+ * (mbq_xq_bytes), rows back to back; for BF16 it is x itself in fp32.
+ */
+
+/* Bytes of staged x for M rows of K values: 4*M*K.  Host only.  MBQ_EINVAL
+ * for an unknown format or K not a multiple of the chunk (32; Q25 64; BF16 8). */
+int mbq_xq_bytes(int fmt, int64_t M, int64_t K, size_t* bytes);
+
+/* xq = staged form of x for fmt.  x: device fp32 [M][ldx], 16-byte aligned,
+ * ldx % 4 == 0, ldx >= K.  xq: device, mbq_xq_bytes(fmt, M, K) bytes, 16-byte
+ * aligned, not overlapping x.  K <= 32768, M <= 65535 (MBQ_EUNSUPPORTED). */
+int mbq_stage_x(int fmt, const float* x, int64_t M, int64_t ldx, int64_t K, void* xq,
+                void* stream);
+
+/* mbq_gemv_q with x given in staged form (staged for W->fmt, M rows of K):
+ * the same products, sums and limits; the result equals mbq_gemv_q's on the
+ * same x up to the order of the fp32 sums.  xq: device, 16-byte aligned, must
+ * not overlap y.  M == 1 in this version (MBQ_EUNSUPPORTED otherwise). */
+int mbq_gemv_xq(const mbq_qweight* W, const void* xq, int64_t M, float* y, int64_t ldy,
+                int accumulate, void* stream);
+
+/* RMSNorm of one row of n values (as mbq_rmsnorm) that also writes its output
+ * in staged form for fmt: the norm before a product, fused with the staging of
+ * the product's input.  y: device fp32 [n] or NULL (then only xq is written);
+ * y == x allowed.  x, gamma, y 16-byte aligned; n a multiple of the chunk and
+ * <= 8192; xq as in mbq_stage_x, overlapping none of x, gamma, y. */
+int mbq_rmsnorm_xq(const float* x, const float* gamma, float eps, int64_t n, float* y, int fmt,
+                   void* xq, void* stream);
+
+/* xq = staged form for fmt of silu(g) * u (as mbq_silu_mul, same arithmetic):
+ * the gated glue fused with the staging of the down product's input.
+ * g, u: device fp32 [n], 16-byte aligned; n a multiple of the chunk. */
+int mbq_silu_mul_xq(const float* g, const float* u, int64_t n, int fmt, void* xq, void* stream);
+
 /* RMSNorm of each row: y = gamma * x / sqrt(mean(x^2) + eps), one 256-thread
  * workgroup per row ([one-serial-kernel] "One thread": many threads share the
  * row, each sums its part, the parts are combined across the group).

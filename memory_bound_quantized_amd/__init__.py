@@ -14,7 +14,8 @@ from . import _lib
 from ._lib import BF16, Q25, Q45, Q65, EXPORTS, MbqError, QWeightDesc, check, lib
 
 __all__ = ["BF16", "Q45", "Q65", "Q25", "MbqError", "QWeight", "format_info", "plane_sizes",
-           "pack", "unpack", "gemv_q", "gemv_q_gather", "rmsnorm", "layernorm", "silu_mul",
+           "pack", "unpack", "gemv_q", "gemv_q_gather", "xq_bytes", "xq_empty", "stage_x",
+           "gemv_xq", "rmsnorm_xq", "silu_mul_xq", "rmsnorm", "layernorm", "silu_mul",
            "dequant_f32", "unpack_codes", "probe_read", "probe_copy", "version", "EXPORTS"]
 
 _vp = ctypes.c_void_p
@@ -129,6 +130,66 @@ def gemv_q_gather(W_all: QWeight, rows_per_expert: int, idx, x, out=None, stream
     check(lib.mbq_gemv_q_gather(ctypes.byref(W_all.desc), rows_per_expert, _ptr(idx), n_sel,
                                 _ptr(x), _ptr(out), _stream(stream)))
     return out
+
+
+def xq_bytes(fmt: int, M: int, K: int) -> int:
+    out = ctypes.c_size_t()
+    check(lib.mbq_xq_bytes(fmt, M, K, ctypes.byref(out)))
+    return int(out.value)
+
+
+def xq_empty(fmt: int, M: int, K: int, device="cuda"):
+    """Device buffer for staged x (opaque; 4 bytes per value) of M rows of K."""
+    import torch
+    n = xq_bytes(fmt, M, K) // 4
+    return torch.empty(n, dtype=torch.int32, device=device)
+
+
+def stage_x(fmt: int, x, out=None, stream=None):
+    """Staged form of fp32 x ([K] or [M, K]) for the products of format fmt."""
+    x2 = x if x.dim() == 2 else x.view(1, -1)
+    M, K = x2.shape
+    if out is None:
+        out = xq_empty(fmt, M, K, device=x.device)
+    check(lib.mbq_stage_x(fmt, _ptr(x2), M, x2.stride(0) if M > 1 else K, K, _ptr(out),
+                          _stream(stream)))
+    return out
+
+
+def gemv_xq(W: QWeight, xq, M: int = 1, out=None, accumulate: bool = False, stream=None):
+    """gemv_q with x already staged for W's format (stage_x, rmsnorm_xq, ...)."""
+    import torch
+    if out is None:
+        out = torch.empty((M, W.N) if M > 1 else (W.N,), dtype=torch.float32, device=xq.device)
+    y2 = out if out.dim() == 2 else out.view(1, -1)
+    check(lib.mbq_gemv_xq(ctypes.byref(W.desc), _ptr(xq), M, _ptr(y2),
+                          y2.stride(0) if M > 1 else W.N, int(bool(accumulate)), _stream(stream)))
+    return out
+
+
+def rmsnorm_xq(x, gamma, eps: float, fmt: int, xq=None, out=None, write_y: bool = True,
+               stream=None):
+    """One row: y = rmsnorm(x) (unless write_y is False) and its staged form for fmt.
+    Returns (y or None, xq)."""
+    import torch
+    n = x.numel()
+    if xq is None:
+        xq = xq_empty(fmt, 1, n, device=x.device)
+    if write_y and out is None:
+        out = torch.empty_like(x)
+    y = out if write_y else None
+    check(lib.mbq_rmsnorm_xq(_ptr(x), _ptr(gamma), eps, n, _ptr(y), fmt, _ptr(xq),
+                             _stream(stream)))
+    return y, xq
+
+
+def silu_mul_xq(g, u, fmt: int, xq=None, stream=None):
+    """Staged form for fmt of silu(g) * u."""
+    n = g.numel()
+    if xq is None:
+        xq = xq_empty(fmt, 1, n, device=g.device)
+    check(lib.mbq_silu_mul_xq(_ptr(g), _ptr(u), n, fmt, _ptr(xq), _stream(stream)))
+    return xq
 
 
 def rmsnorm(x, gamma, eps: float, out=None, stream=None):

@@ -17,7 +17,8 @@ BF16, Q45, Q65, Q25 = 0, 1, 2, 3
 # Every symbol include/mbq.h declares, in declaration order.
 EXPORTS = (
     "mbq_format_info", "mbq_plane_sizes", "mbq_pack", "mbq_unpack", "mbq_gemv_q",
-    "mbq_gemv_q_gather", "mbq_rmsnorm", "mbq_layernorm", "mbq_silu_mul", "mbq_dequant_f32",
+    "mbq_gemv_q_gather", "mbq_xq_bytes", "mbq_stage_x", "mbq_gemv_xq", "mbq_rmsnorm_xq",
+    "mbq_silu_mul_xq", "mbq_rmsnorm", "mbq_layernorm", "mbq_silu_mul", "mbq_dequant_f32",
     "mbq_unpack_codes", "mbq_probe_read", "mbq_probe_copy", "mbq_status_str",
     "mbq_last_error", "mbq_version",
 )
@@ -45,7 +46,7 @@ def _status_name(s):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError("libmbq.so is not built at %s; run "
-                          "`python -m memory_bound_quantized_amd.build` first" % LIB_PATH)
+                          "`python memory_bound_quantized_amd/build.py` first" % LIB_PATH)
     # torch supplies device memory and streams, so libmbq must run on torch's
     # HIP runtime.  torch bundles its own libamdhip64 with the same SONAME
     # (libamdhip64.so.7); once torch is loaded, libmbq's dependency resolves
@@ -61,6 +62,11 @@ def _load():
         "mbq_unpack": (i32, [i32, i64, i64, ctypes.POINTER(vp), vp, vp, vp]),
         "mbq_gemv_q": (i32, [ctypes.POINTER(QWeightDesc), vp, i64, i64, vp, i64, i32, vp]),
         "mbq_gemv_q_gather": (i32, [ctypes.POINTER(QWeightDesc), i64, vp, i64, vp, vp, vp]),
+        "mbq_xq_bytes": (i32, [i32, i64, i64, ctypes.POINTER(sz)]),
+        "mbq_stage_x": (i32, [i32, vp, i64, i64, i64, vp, vp]),
+        "mbq_gemv_xq": (i32, [ctypes.POINTER(QWeightDesc), vp, i64, vp, i64, i32, vp]),
+        "mbq_rmsnorm_xq": (i32, [vp, vp, f32, i64, vp, i32, vp, vp]),
+        "mbq_silu_mul_xq": (i32, [vp, vp, i64, i32, vp, vp]),
         "mbq_rmsnorm": (i32, [vp, vp, f32, i64, i64, vp, vp]),
         "mbq_layernorm": (i32, [vp, vp, vp, f32, i64, i64, vp, vp]),
         "mbq_silu_mul": (i32, [vp, vp, i64, vp, vp]),

@@ -1,6 +1,8 @@
 """Build libmbq.so in-tree with hipcc for gfx950.
 
-    python -m memory_bound_quantized_amd.build [--jobs N]
+    python memory_bound_quantized_amd/build.py [--jobs N]
+
+(run as a script: importing the package needs the library it builds).
 
 Every HIP source is compiled with packed-fp32 instruction selection switched
 off (the device pass honours the flag; the host pass only warns about it).
@@ -21,7 +23,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmbq.so")
 ARCH = "gfx950"
 
-SOURCES = ["abi.cpp", "gemv_m1.hip", "gemv_smallm.hip", "gemv_mfma.hip", "norms.hip", "exports.hip"]
+SOURCES = ["abi.cpp", "gemv_m1.hip", "gemv_smallm.hip", "gemv_mfma.hip", "stage.hip", "norms.hip",
+           "exports.hip"]
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH, "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -95,23 +95,28 @@ int check_kernel_shape(const mbq_qweight* W, const char* fn) {
     return MBQ_OK;
 }
 
+// Values per chunk of staged x (the unit of its fixed-point exponent).
+int64_t xq_chunk(int fmt) {
+    switch (fmt) {
+    case MBQ_FMT_Q45: return 32;
+    case MBQ_FMT_Q65: return 32;
+    case MBQ_FMT_Q25: return 64;
+    default: return 8;
+    }
+}
+
 mbq::DevPlanes planes_of(const mbq_qweight* W) {
     return mbq::DevPlanes{(const uint8_t*)W->codes, (const uint8_t*)W->codes_hi,
                           (const uint8_t*)W->scales, (const uint8_t*)W->super_scales};
 }
 
-// Optional geometry override for tuning sweeps: MBQ_GEMV_GEOM="R,G,D" (rows
-// per wave, row groups per workgroup, chunk units in flight), read at every
-// call.
+// Optional override of the rows per wave for tuning sweeps: MBQ_GEMV_ROWS=1,
+// 2 or 4, read at every call.
 bool geom_override(mbq::GemvGeom* g) {
-    const char* s = getenv("MBQ_GEMV_GEOM");
-    int r = 0, gg = 0, d = 2;
-    if (!s || sscanf(s, "%d,%d,%d", &r, &gg, &d) < 2 || !(r == 1 || r == 2 || r == 4) || gg < 1 ||
-        !(d == 2 || d == 4))
-        return false;
+    const char* s = getenv("MBQ_GEMV_ROWS");
+    int r = 0;
+    if (!s || sscanf(s, "%d", &r) != 1 || !(r == 1 || r == 2 || r == 4)) return false;
     g->rows_per_wave = r;
-    g->groups_per_wg = gg;
-    g->prefetch = d;
     return true;
 }
 
@@ -121,13 +126,6 @@ bool geom_override(mbq::GemvGeom* g) {
 // 16 (mbq.h).  The order lets the device assemble four 6-bit codes in the
 // bytes of a dword with at most two shifts, one mask and one and-or.
 constexpr int kQ65HighBit[16] = {4, 2, 12, 10, 20, 18, 28, 26, 0, 6, 8, 14, 16, 22, 24, 30};
-
-void put16(uint8_t* p, uint16_t v) {
-    p[0] = (uint8_t)(v & 0xFF);
-    p[1] = (uint8_t)(v >> 8);
-}
-
-uint16_t get16(const uint8_t* p) { return (uint16_t)(p[0] | (p[1] << 8)); }
 
 }  // namespace
 
@@ -281,8 +279,8 @@ int mbq_gemv_q(const mbq_qweight* W, const float* x, int64_t M, int64_t ldx, flo
     if (M == 1) {
         mbq::GemvGeom g = mbq::gemv_m1_default_geom(W->fmt, W->N, W->K);
         geom_override(&g);
-        return hip_status(mbq::launch_gemv_m1(W->fmt, P, W->N, W->K, x, y, accumulate, nullptr,
-                                              1, g, s), fn);
+        return hip_status(mbq::launch_gemv_m1(W->fmt, P, W->N, W->K, x, false, y, accumulate,
+                                              nullptr, 1, g, s), fn);
     }
     return fail(MBQ_EUNSUPPORTED, "%s: no kernel for M=%lld with format %d", fn, (long long)M, W->fmt);
 }
@@ -306,8 +304,69 @@ int mbq_gemv_q_gather(const mbq_qweight* W_all, int64_t rows_per_expert, const i
     if ((rc = check_kernel_shape(W_all, fn))) return rc;
     mbq::GemvGeom g = mbq::gemv_m1_default_geom(W_all->fmt, n_out, W_all->K);
     geom_override(&g);
-    return hip_status(mbq::launch_gemv_m1(W_all->fmt, planes_of(W_all), n_out, W_all->K, x, y, 0,
-                                          idx, rows_per_expert, g, s), fn);
+    return hip_status(mbq::launch_gemv_m1(W_all->fmt, planes_of(W_all), n_out, W_all->K, x, false,
+                                          y, 0, idx, rows_per_expert, g, s), fn);
+}
+
+int mbq_xq_bytes(int fmt, int64_t M, int64_t K, size_t* bytes) {
+    const char* fn = "mbq_xq_bytes";
+    if (!fmt_valid(fmt)) return fail(MBQ_EINVAL, "%s: unknown format %d", fn, fmt);
+    if (!bytes) return fail(MBQ_EINVAL, "%s: bytes is NULL", fn);
+    if (M < 0 || K < 0) return fail(MBQ_EINVAL, "%s: negative shape", fn);
+    if (K % xq_chunk(fmt))
+        return fail(MBQ_EINVAL, "%s: K=%lld is not a multiple of %lld", fn, (long long)K,
+                    (long long)xq_chunk(fmt));
+    *bytes = (size_t)M * (size_t)K * 4;
+    return ok();
+}
+
+int mbq_stage_x(int fmt, const float* x, int64_t M, int64_t ldx, int64_t K, void* xq,
+                void* stream) {
+    const char* fn = "mbq_stage_x";
+    size_t xqb = 0;
+    int rc = mbq_xq_bytes(fmt, M, K, &xqb);
+    if (rc) return fail(rc, "%s: %s", fn, g_err.c_str());
+    if (ldx < K) return fail(MBQ_EINVAL, "%s: ldx < K", fn);
+    if (M == 0 || K == 0) return ok();
+    if (M > 65535) return fail(MBQ_EUNSUPPORTED, "%s: M > 65535", fn);
+    if (K > mbq::kMaxK) return fail(MBQ_EUNSUPPORTED, "%s: K > %lld", fn, (long long)mbq::kMaxK);
+    if (!x || !xq) return fail(MBQ_EINVAL, "%s: NULL pointer", fn);
+    if (!aligned(x, 16) || ldx % 4 || !aligned(xq, 16))
+        return fail(MBQ_EALIGN, "%s: x and xq must be 16-byte aligned with ldx %% 4 == 0", fn);
+    if (overlaps(x, (size_t)((M - 1) * ldx + K) * 4, xq, xqb))
+        return fail(MBQ_EINVAL, "%s: x and xq overlap", fn);
+    return hip_status(mbq::launch_stage_x(fmt, x, M, ldx, K, xq, (hipStream_t)stream), fn);
+}
+
+int mbq_gemv_xq(const mbq_qweight* W, const void* xq, int64_t M, float* y, int64_t ldy,
+                int accumulate, void* stream) {
+    const char* fn = "mbq_gemv_xq";
+    int rc = check_weight(W, fn);
+    if (rc) return rc;
+    if (M < 0) return fail(MBQ_EINVAL, "%s: M < 0", fn);
+    if (ldy < W->N) return fail(MBQ_EINVAL, "%s: ldy < N", fn);
+    if (accumulate != 0 && accumulate != 1) return fail(MBQ_EINVAL, "%s: accumulate must be 0 or 1", fn);
+    if (M == 0 || W->N == 0) return ok();
+    if (!xq || !y) return fail(MBQ_EINVAL, "%s: xq or y is NULL", fn);
+    if (!aligned(y, 4)) return fail(MBQ_EALIGN, "%s: y must be 4-byte aligned", fn);
+    hipStream_t s = (hipStream_t)stream;
+    if (W->K == 0) {
+        if (accumulate) return ok();
+        return hip_status(mbq::launch_fill_zero(y, M, W->N, ldy, s), fn);
+    }
+    if (!aligned(xq, 16)) return fail(MBQ_EALIGN, "%s: xq must be 16-byte aligned", fn);
+    const size_t ybytes = (size_t)((M - 1) * ldy + W->N) * 4;
+    if (overlaps(xq, (size_t)(M * W->K) * 4, y, ybytes)) return fail(MBQ_EINVAL, "%s: xq and y overlap", fn);
+    if ((rc = check_planes(W, fn))) return rc;
+    if ((rc = check_kernel_shape(W, fn))) return rc;
+    const mbq::DevPlanes P = planes_of(W);
+    if (M == 1) {
+        mbq::GemvGeom g = mbq::gemv_m1_default_geom(W->fmt, W->N, W->K);
+        geom_override(&g);
+        return hip_status(mbq::launch_gemv_m1(W->fmt, P, W->N, W->K, xq, true, y, accumulate,
+                                              nullptr, 1, g, s), fn);
+    }
+    return fail(MBQ_EUNSUPPORTED, "%s: no kernel for M=%lld with format %d", fn, (long long)M, W->fmt);
 }
 
 static int check_norm(const float* x, const float* gamma, const float* beta, bool need_beta,
@@ -352,6 +411,50 @@ int mbq_silu_mul(const float* g, const float* u, int64_t n, float* out, void* st
     if ((out != g && overlaps(out, b, g, b)) || (out != u && overlaps(out, b, u, b)))
         return fail(MBQ_EINVAL, "%s: out partially overlaps an input", fn);
     return hip_status(mbq::launch_silu_mul(g, u, n, out, (hipStream_t)stream), fn);
+}
+
+// Shape and pointer checks of the producers of staged x.
+static int check_xq_out(int fmt, int64_t n, const void* xq, const char* fn) {
+    if (!fmt_valid(fmt)) return fail(MBQ_EINVAL, "%s: unknown format %d", fn, fmt);
+    if (n % xq_chunk(fmt))
+        return fail(MBQ_EINVAL, "%s: n=%lld is not a multiple of %lld", fn, (long long)n,
+                    (long long)xq_chunk(fmt));
+    if (!xq) return fail(MBQ_EINVAL, "%s: xq is NULL", fn);
+    if (!aligned(xq, 16)) return fail(MBQ_EALIGN, "%s: xq must be 16-byte aligned", fn);
+    return MBQ_OK;
+}
+
+int mbq_rmsnorm_xq(const float* x, const float* gamma, float eps, int64_t n, float* y, int fmt,
+                   void* xq, void* stream) {
+    const char* fn = "mbq_rmsnorm_xq";
+    if (n < 0) return fail(MBQ_EINVAL, "%s: n < 0", fn);
+    if (!(eps >= 0.f) || eps == __builtin_inff()) return fail(MBQ_EINVAL, "%s: eps must be finite and >= 0", fn);
+    if (n == 0) return ok();
+    int rc = check_xq_out(fmt, n, xq, fn);
+    if (rc) return rc;
+    if (n > 8192) return fail(MBQ_EUNSUPPORTED, "%s: n > 8192", fn);
+    if (!x || !gamma) return fail(MBQ_EINVAL, "%s: NULL pointer", fn);
+    if (!aligned(x, 16) || !aligned(gamma, 16) || (y && !aligned(y, 16)))
+        return fail(MBQ_EALIGN, "%s: x, gamma and y must be 16-byte aligned", fn);
+    const size_t b = (size_t)n * 4;
+    if (y && x != y && overlaps(x, b, y, b)) return fail(MBQ_EINVAL, "%s: x and y partially overlap", fn);
+    if (overlaps(xq, b, x, b) || (y && overlaps(xq, b, y, b)) || overlaps(xq, b, gamma, b))
+        return fail(MBQ_EINVAL, "%s: xq overlaps an input or y", fn);
+    return hip_status(mbq::launch_rmsnorm_xq(x, gamma, eps, n, y, fmt, xq, (hipStream_t)stream), fn);
+}
+
+int mbq_silu_mul_xq(const float* g, const float* u, int64_t n, int fmt, void* xq, void* stream) {
+    const char* fn = "mbq_silu_mul_xq";
+    if (n < 0) return fail(MBQ_EINVAL, "%s: n < 0", fn);
+    if (n == 0) return ok();
+    int rc = check_xq_out(fmt, n, xq, fn);
+    if (rc) return rc;
+    if (n > ((int64_t)1 << 30)) return fail(MBQ_EUNSUPPORTED, "%s: n > 2^30", fn);
+    if (!g || !u) return fail(MBQ_EINVAL, "%s: NULL pointer", fn);
+    if (!aligned(g, 16) || !aligned(u, 16)) return fail(MBQ_EALIGN, "%s: g and u must be 16-byte aligned", fn);
+    const size_t b = (size_t)n * 4;
+    if (overlaps(xq, b, g, b) || overlaps(xq, b, u, b)) return fail(MBQ_EINVAL, "%s: xq overlaps an input", fn);
+    return hip_status(mbq::launch_silu_mul_xq(g, u, n, fmt, xq, (hipStream_t)stream), fn);
 }
 
 int mbq_dequant_f32(const mbq_qweight* W, float* w_out, void* stream) {

@@ -315,47 +315,4 @@ struct Traits<kBF16> {
     }
 };
 
-// ------------------------------------------------------------- x staging --
-
-// Chunk exponent for a largest |x| with biased exponent E (0: zero or
-// subnormal): e = 148 - E maps it into [2^21, 2^22); clamped to <= 126 so
-// 2^e and 2^-e are normal floats (values below 2^-126 then round to 0 or
-// +-1 units of 2^-126).
-__device__ __forceinline__ int chunk_exp(float amax) {
-    const int E = (int)((__builtin_bit_cast(uint32_t, amax) >> 23) & 0xFFu);
-    const int e = 148 - E;
-    return e > 126 ? 126 : e;
-}
-__device__ __forceinline__ float pow2f(int e) {
-    return __builtin_bit_cast(float, (uint32_t)(e + 127) << 23);
-}
-
-// Byte p (p = 0, 1, 2) of four 32-bit integers, packed into one word.
-__device__ __forceinline__ void digit_words(int32_t n0, int32_t n1, int32_t n2, int32_t n3,
-                                            uint32_t* dg) {
-    const uint32_t t01 = __builtin_amdgcn_perm((uint32_t)n1, (uint32_t)n0, 0x05010400u);
-    const uint32_t t23 = __builtin_amdgcn_perm((uint32_t)n3, (uint32_t)n2, 0x05010400u);
-    const uint32_t u01 = __builtin_amdgcn_perm((uint32_t)n1, (uint32_t)n0, 0x06020602u);
-    const uint32_t u23 = __builtin_amdgcn_perm((uint32_t)n3, (uint32_t)n2, 0x06020602u);
-    dg[0] = __builtin_amdgcn_perm(t23, t01, 0x05040100u);
-    dg[1] = __builtin_amdgcn_perm(t23, t01, 0x07060302u);
-    dg[2] = __builtin_amdgcn_perm(u23, u01, 0x05040100u);
-}
-
-// LDS slots (16 bytes) per chunk: one more than the chunk's data, so that
-// lanes reading consecutive chunks at that stride (36, 68 or 12 dwords) hit
-// distinct banks for any 16 consecutive lanes.
-template <int FMT>
-struct Stride {
-    static constexpr int SLOTS = Traits<FMT>::F4 + 1;
-    static constexpr int DW = 4 * SLOTS;   // dwords per chunk
-};
-
-// Round x * 2^e to the nearest integer (ties to even) with one FMA: adding
-// 1.5 * 2^23 leaves the integer in the low mantissa bits for |x 2^e| < 2^22.
-__device__ __forceinline__ int32_t round_fixed(float v, float up) {
-    const float t = fmaf(v, up, 12582912.0f);
-    return (int32_t)(__builtin_bit_cast(uint32_t, t) - 0x4B400000u);
-}
-
 }  // namespace mbq

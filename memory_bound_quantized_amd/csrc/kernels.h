@@ -23,20 +23,32 @@ struct DevPlanes {
 constexpr int64_t kMaxK = 32768;
 constexpr int64_t kMaxKBF16 = 16384;
 
-// Geometry of the M = 1 GEMV: rows per wave and row groups per workgroup.
+// Geometry of the M = 1 GEMV: output rows per wave (4 waves per workgroup).
 struct GemvGeom {
     int rows_per_wave;   // 1, 2 or 4
-    int groups_per_wg;   // >= 1
-    int prefetch;        // chunk units in flight per wave: 2 or 4
 };
 
 GemvGeom gemv_m1_default_geom(int fmt, int64_t N, int64_t K);
 
 // y[n] (+)= W[row(n)] . x for n < N_out.  If gidx != nullptr the output row
 // n maps to weight row gidx[n / rpe] * rpe + n % rpe (gathered experts).
-hipError_t launch_gemv_m1(int fmt, DevPlanes P, int64_t N_out, int64_t K, const float* x,
-                          float* y, int accumulate, const int32_t* gidx, int64_t rpe,
-                          GemvGeom geom, hipStream_t stream);
+// x is fp32 [K], or x staged for fmt (staging.h) when x_staged.
+hipError_t launch_gemv_m1(int fmt, DevPlanes P, int64_t N_out, int64_t K, const void* x,
+                          bool x_staged, float* y, int accumulate, const int32_t* gidx,
+                          int64_t rpe, GemvGeom geom, hipStream_t stream);
+
+// Staged x for fmt (staging.h) of M rows of fp32 x: xq[m] = stage(x[m][0:K]),
+// rows of xq packed back to back (4*K bytes each).
+hipError_t launch_stage_x(int fmt, const float* x, int64_t M, int64_t ldx, int64_t K, void* xq,
+                          hipStream_t stream);
+
+// One row: y = RMSNorm(x) (skipped if y == nullptr) and xq = stage(y) for fmt.
+hipError_t launch_rmsnorm_xq(const float* x, const float* gamma, float eps, int64_t n, float* y,
+                             int fmt, void* xq, hipStream_t stream);
+
+// xq = stage(silu(g) * u) for fmt; n values.
+hipError_t launch_silu_mul_xq(const float* g, const float* u, int64_t n, int fmt, void* xq,
+                              hipStream_t stream);
 
 // Y[m][n] (+)= W[n] . X[m] for 2 <= M <= 8 (vector units).
 hipError_t launch_gemv_smallm(int fmt, DevPlanes P, int64_t N, int64_t K, const float* x,

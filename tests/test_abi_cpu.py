@@ -30,7 +30,7 @@ def _declared_symbols():
 
 def test_library_exports_every_declared_symbol():
     declared = _declared_symbols()
-    assert len(declared) == 16
+    assert len(declared) == 21
     assert sorted(_lib.EXPORTS) == declared
     lib = ctypes.CDLL(_lib.LIB_PATH)
     for name in declared:
@@ -177,6 +177,49 @@ def test_norm_argument_checks():
     assert L.mbq_silu_mul(x, gm, -1, y, None) == _lib.EINVAL
     assert L.mbq_silu_mul(x, gm, 0, y, None) == _lib.OK
     assert L.mbq_silu_mul(x, gm, 1024, x + 64, None) == _lib.EINVAL
+
+
+def test_staged_x_argument_checks():
+    sz = ctypes.c_size_t()
+    assert L.mbq_xq_bytes(1, 3, 4096, ctypes.byref(sz)) == _lib.OK and sz.value == 3 * 4096 * 4
+    assert L.mbq_xq_bytes(3, 1, 4096, ctypes.byref(sz)) == _lib.OK and sz.value == 4096 * 4
+    assert L.mbq_xq_bytes(3, 1, 96, ctypes.byref(sz)) == _lib.EINVAL       # Q25 chunk is 64
+    assert L.mbq_xq_bytes(1, 1, 48, ctypes.byref(sz)) == _lib.EINVAL
+    assert L.mbq_xq_bytes(9, 1, 64, ctypes.byref(sz)) == _lib.EINVAL
+    x, xq = BASE, BASE + 0x100000
+    st = lambda fmt=1, x=x, M=1, ldx=4096, K=4096, xq=xq: L.mbq_stage_x(fmt, x, M, ldx, K, xq, None)
+    assert st(K=4016) == _lib.EINVAL
+    assert st(ldx=100) == _lib.EINVAL
+    assert st(M=0) == _lib.OK
+    assert st(x=None) == _lib.EINVAL
+    assert st(x=x + 4) == _lib.EALIGN
+    assert st(xq=xq + 8) == _lib.EALIGN
+    assert st(xq=x + 4096) == _lib.EINVAL                                   # overlap
+    assert st(K=65536, ldx=65536) == _lib.EUNSUPPORTED
+    gx = lambda d, xq=xq, M=1, y=BASE + 0x800000, acc=0: \
+        L.mbq_gemv_xq(ctypes.byref(d), xq, M, y, d.N, acc, None)
+    assert gx(_desc(), xq=None) == _lib.EINVAL
+    assert gx(_desc(), xq=xq + 4) == _lib.EALIGN
+    assert gx(_desc(), y=xq + 64) == _lib.EINVAL                            # overlap
+    assert gx(_desc(), acc=3) == _lib.EINVAL
+    assert gx(_desc(), M=0) == _lib.OK
+    assert gx(_desc(fmt=3, K=96)) == _lib.EUNSUPPORTED
+    r = lambda n=4096, y=BASE + 0x200000, fmt=1, xq=xq, x=x, eps=1e-6: \
+        L.mbq_rmsnorm_xq(x, BASE + 0x300000, eps, n, y, fmt, xq, None)
+    assert r(n=-1) == _lib.EINVAL
+    assert r(n=0) == _lib.OK
+    assert r(eps=-1.0) == _lib.EINVAL
+    assert r(n=4016) == _lib.EINVAL                                         # not a chunk multiple
+    assert r(n=16384) == _lib.EUNSUPPORTED
+    assert r(xq=None) == _lib.EINVAL
+    assert r(y=BASE + 0x200004) == _lib.EALIGN
+    assert r(xq=x + 1024) == _lib.EINVAL                                    # xq overlaps x
+    assert r(y=x + 64) == _lib.EINVAL                                       # partial overlap
+    sm = lambda n=12288, fmt=2, xq=xq, g=BASE + 0x400000: L.mbq_silu_mul_xq(g, BASE + 0x500000, n, fmt, xq, None)
+    assert sm(n=0) == _lib.OK
+    assert sm(n=100) == _lib.EINVAL
+    assert sm(g=BASE + 0x400008) == _lib.EALIGN
+    assert sm(xq=BASE + 0x500000) == _lib.EINVAL                            # xq overlaps u
 
 
 def test_export_and_probe_argument_checks():
