@@ -152,6 +152,78 @@ int mbq_gemv_q_gather(const mbq_qweight* W_all, int64_t rows_per_expert,
                       const int32_t* idx, int64_t n_sel, const float* x,
                       float* y, void* stream);
 
+/* ---------------------------------------------------------- fused products
+ * One launch that does the work of several small kernels between weight
+ * reads ([roofline-holds] "Hiding, fusing, and keeping the sums busy";
+ * "Where the time goes": the norms and adds between the weight kernels).
+ *
+ * mbq_gemv_fused: M = 1.
+ *   gamma == NULL:  a = x;  else a = rmsnorm(x; gamma, eps) (as mbq_rmsnorm),
+ *                   computed inside every workgroup of the product.
+ *   epilogue MBQ_EPI_STORE:      y[n]  = W[n] . a,           n < N
+ *            MBQ_EPI_ACCUMULATE: y[n] += W[n] . a            (residual add)
+ *            MBQ_EPI_SILU_MUL:   y[i]  = silu(W[2i] . a) * (W[2i+1] . a),
+ *                                i < N/2: W holds the gate and up rows of a
+ *                                gated feed-forward interleaved (N even).
+ * x: device fp32 [K], 16-byte aligned; gamma: device fp32 [K], 16-byte
+ * aligned, or NULL; y: device fp32, 4-byte aligned, overlapping neither.
+ * With a norm or the silu epilogue only Q45 and Q65 with K = 4096 or 12288
+ * have kernels (MBQ_EUNSUPPORTED otherwise); without them every shape of
+ * mbq_gemv_q with M = 1 is accepted. */
+#define MBQ_EPI_STORE      0
+#define MBQ_EPI_ACCUMULATE 1
+#define MBQ_EPI_SILU_MUL   2
+
+int mbq_gemv_fused(const mbq_qweight* W, const float* x, const float* gamma, float eps,
+                   int epilogue, float* y, void* stream);
+
+/* ----------------------------------------------------------- decode step
+ * One token through a stack of decoder layers with attention left out: the
+ * weight stream whose rate the pages bound by BW/B ([roofline-holds] "The
+ * Math": tokens per second <= memory bandwidth / bytes read per token; "The
+ * tensor, the kernel, the token").  Per layer, with a = rmsnorm(h, gamma1),
+ * b = rmsnorm(h, gamma2):
+ *     q|k|v = Wqkv a;   h += Wo q   (q stands in for the attention output;
+ *                                    k and v are computed and not consumed)
+ *     h += Wdown (silu(Wgate b) * (Wup b))
+ * then logits = Wlm rmsnorm(h, gamma_f).  Four launches per layer: the norms
+ * run inside the qkv and gate/up products, silu * up in the gate/up product's
+ * epilogue, both residual adds in the o and down products' epilogues.
+ *
+ * Weights (device planes, caller-owned):
+ *   qkv     (dq + 2 dkv) x d: the q rows, then k, then v
+ *   o       d x dq
+ *   gate_up 2f x d: row 2i is gate row i, row 2i+1 is up row i
+ *   down    d x f
+ *   lm_head vocab x d
+ * qkv, gate_up and lm_head need fused kernels (Q45/Q65, d = 4096 or 12288).
+ * gamma1, gamma2, gamma_f: device fp32 [d], 16-byte aligned.
+ * h: device fp32 [d], 16-byte aligned, updated in place; logits: device fp32
+ * [vocab].  workspace: device, 256-byte aligned, at least
+ * mbq_decode_workspace_bytes bytes, not overlapping h or logits; it holds
+ * q|k|v and the gated activations of the layer being computed. */
+typedef struct mbq_decode_layer {
+    mbq_qweight qkv;
+    mbq_qweight o;
+    mbq_qweight gate_up;
+    mbq_qweight down;
+    const float* gamma1;
+    const float* gamma2;
+} mbq_decode_layer;
+
+typedef struct mbq_decode_model {
+    int32_t n_layers;
+    float eps;
+    int64_t d, dq, dkv, f, vocab;
+    const mbq_decode_layer* layers;   /* host array of n_layers */
+    const float* gamma_f;
+    mbq_qweight lm_head;
+} mbq_decode_model;
+
+int mbq_decode_workspace_bytes(const mbq_decode_model* model, size_t* bytes);
+int mbq_decode_step(const mbq_decode_model* model, float* h, float* logits, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------ staged x
  * The quantized products consume x in a "staged" form: per chunk of 32
  * values (64 for Q25) a power-of-two scale 2^-e and the 24-bit integers

@@ -13,8 +13,11 @@ import numpy as np
 from . import _lib
 from ._lib import BF16, Q25, Q45, Q65, EXPORTS, MbqError, QWeightDesc, check, lib
 
+EPI_STORE, EPI_ACCUMULATE, EPI_SILU_MUL = 0, 1, 2
+
 __all__ = ["BF16", "Q45", "Q65", "Q25", "MbqError", "QWeight", "format_info", "plane_sizes",
-           "pack", "unpack", "gemv_q", "gemv_q_gather", "xq_bytes", "xq_empty", "stage_x",
+           "pack", "unpack", "gemv_q", "gemv_q_gather", "gemv_fused", "EPI_STORE", "EPI_ACCUMULATE",
+           "EPI_SILU_MUL", "xq_bytes", "xq_empty", "stage_x",
            "gemv_xq", "rmsnorm_xq", "silu_mul_xq", "rmsnorm", "layernorm", "silu_mul",
            "dequant_f32", "unpack_codes", "probe_read", "probe_copy", "version", "EXPORTS"]
 
@@ -129,6 +132,19 @@ def gemv_q_gather(W_all: QWeight, rows_per_expert: int, idx, x, out=None, stream
         out = torch.empty((n_sel, rows_per_expert), dtype=torch.float32, device=x.device)
     check(lib.mbq_gemv_q_gather(ctypes.byref(W_all.desc), rows_per_expert, _ptr(idx), n_sel,
                                 _ptr(x), _ptr(out), _stream(stream)))
+    return out
+
+
+def gemv_fused(W: QWeight, x, gamma=None, eps: float = 0.0, epilogue: int = EPI_STORE,
+               out=None, stream=None):
+    """M = 1 product with an optional RMSNorm prologue (gamma) and a store,
+    accumulate or silu(gate) * up epilogue (mbq_gemv_fused)."""
+    import torch
+    n_out = W.N // 2 if epilogue == EPI_SILU_MUL else W.N
+    if out is None:
+        out = torch.empty(n_out, dtype=torch.float32, device=x.device)
+    check(lib.mbq_gemv_fused(ctypes.byref(W.desc), _ptr(x), _ptr(gamma), eps, epilogue,
+                             _ptr(out), _stream(stream)))
     return out
 
 

@@ -17,7 +17,8 @@ BF16, Q45, Q65, Q25 = 0, 1, 2, 3
 # Every symbol include/mbq.h declares, in declaration order.
 EXPORTS = (
     "mbq_format_info", "mbq_plane_sizes", "mbq_pack", "mbq_unpack", "mbq_gemv_q",
-    "mbq_gemv_q_gather", "mbq_xq_bytes", "mbq_stage_x", "mbq_gemv_xq", "mbq_rmsnorm_xq",
+    "mbq_gemv_q_gather", "mbq_gemv_fused", "mbq_decode_workspace_bytes", "mbq_decode_step",
+    "mbq_xq_bytes", "mbq_stage_x", "mbq_gemv_xq", "mbq_rmsnorm_xq",
     "mbq_silu_mul_xq", "mbq_rmsnorm", "mbq_layernorm", "mbq_silu_mul", "mbq_dequant_f32",
     "mbq_unpack_codes", "mbq_probe_read", "mbq_probe_copy", "mbq_status_str",
     "mbq_last_error", "mbq_version",
@@ -30,6 +31,21 @@ class QWeightDesc(ctypes.Structure):
                 ("N", ctypes.c_int64), ("K", ctypes.c_int64),
                 ("codes", ctypes.c_void_p), ("codes_hi", ctypes.c_void_p),
                 ("scales", ctypes.c_void_p), ("super_scales", ctypes.c_void_p)]
+
+
+class DecodeLayerDesc(ctypes.Structure):
+    """struct mbq_decode_layer."""
+    _fields_ = [("qkv", QWeightDesc), ("o", QWeightDesc), ("gate_up", QWeightDesc),
+                ("down", QWeightDesc), ("gamma1", ctypes.c_void_p), ("gamma2", ctypes.c_void_p)]
+
+
+class DecodeModelDesc(ctypes.Structure):
+    """struct mbq_decode_model."""
+    _fields_ = [("n_layers", ctypes.c_int32), ("eps", ctypes.c_float),
+                ("d", ctypes.c_int64), ("dq", ctypes.c_int64), ("dkv", ctypes.c_int64),
+                ("f", ctypes.c_int64), ("vocab", ctypes.c_int64),
+                ("layers", ctypes.POINTER(DecodeLayerDesc)), ("gamma_f", ctypes.c_void_p),
+                ("lm_head", QWeightDesc)]
 
 
 class MbqError(RuntimeError):
@@ -62,6 +78,9 @@ def _load():
         "mbq_unpack": (i32, [i32, i64, i64, ctypes.POINTER(vp), vp, vp, vp]),
         "mbq_gemv_q": (i32, [ctypes.POINTER(QWeightDesc), vp, i64, i64, vp, i64, i32, vp]),
         "mbq_gemv_q_gather": (i32, [ctypes.POINTER(QWeightDesc), i64, vp, i64, vp, vp, vp]),
+        "mbq_gemv_fused": (i32, [ctypes.POINTER(QWeightDesc), vp, vp, f32, i32, vp, vp]),
+        "mbq_decode_workspace_bytes": (i32, [ctypes.POINTER(DecodeModelDesc), ctypes.POINTER(sz)]),
+        "mbq_decode_step": (i32, [ctypes.POINTER(DecodeModelDesc), vp, vp, vp, sz, vp]),
         "mbq_xq_bytes": (i32, [i32, i64, i64, ctypes.POINTER(sz)]),
         "mbq_stage_x": (i32, [i32, vp, i64, i64, i64, vp, vp]),
         "mbq_gemv_xq": (i32, [ctypes.POINTER(QWeightDesc), vp, i64, vp, i64, i32, vp]),

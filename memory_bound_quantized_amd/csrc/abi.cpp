@@ -308,6 +308,137 @@ int mbq_gemv_q_gather(const mbq_qweight* W_all, int64_t rows_per_expert, const i
                                           y, 0, idx, rows_per_expert, g, s), fn);
 }
 
+int mbq_gemv_fused(const mbq_qweight* W, const float* x, const float* gamma, float eps,
+                   int epilogue, float* y, void* stream) {
+    const char* fn = "mbq_gemv_fused";
+    int rc = check_weight(W, fn);
+    if (rc) return rc;
+    if (epilogue < MBQ_EPI_STORE || epilogue > MBQ_EPI_SILU_MUL)
+        return fail(MBQ_EINVAL, "%s: unknown epilogue %d", fn, epilogue);
+    const bool silu = epilogue == MBQ_EPI_SILU_MUL;
+    if (silu && W->N % 2) return fail(MBQ_EINVAL, "%s: the silu epilogue needs an even N", fn);
+    if (gamma && (!(eps >= 0.f) || eps == __builtin_inff()))
+        return fail(MBQ_EINVAL, "%s: eps must be finite and >= 0", fn);
+    if (W->N == 0) return ok();
+    if (!x || !y) return fail(MBQ_EINVAL, "%s: x or y is NULL", fn);
+    if (!aligned(x, 16) || !aligned(y, 4) || (gamma && !aligned(gamma, 16)))
+        return fail(MBQ_EALIGN, "%s: x and gamma must be 16-byte aligned, y 4-byte", fn);
+    const int64_t n_out = silu ? W->N / 2 : W->N;
+    const size_t xb = (size_t)W->K * 4, yb = (size_t)n_out * 4;
+    if (overlaps(x, xb, y, yb) || (gamma && overlaps(gamma, xb, y, yb)))
+        return fail(MBQ_EINVAL, "%s: y overlaps x or gamma", fn);
+    if ((rc = check_planes(W, fn))) return rc;
+    if ((rc = check_kernel_shape(W, fn))) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    mbq::GemvGeom g = mbq::gemv_m1_default_geom(W->fmt, W->N, W->K);
+    geom_override(&g);
+    if (!gamma && !silu)
+        return hip_status(mbq::launch_gemv_m1(W->fmt, planes_of(W), W->N, W->K, x, false, y,
+                                              epilogue == MBQ_EPI_ACCUMULATE, nullptr, 1, g, s), fn);
+    if (!mbq::gemv_fused_supported(W->fmt, W->K))
+        return fail(MBQ_EUNSUPPORTED, "%s: fused kernels exist for Q45/Q65 with K = 4096 or 12288", fn);
+    return hip_status(mbq::launch_gemv_fused(W->fmt, planes_of(W), W->N, W->K, x, gamma, eps, silu,
+                                             y, epilogue == MBQ_EPI_ACCUMULATE, g, s), fn);
+}
+
+// ---------------------------------------------------------- decode step
+
+static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+static int check_decode(const mbq_decode_model* m, const char* fn) {
+    if (!m) return fail(MBQ_EINVAL, "%s: model is NULL", fn);
+    if (m->n_layers < 0 || m->d <= 0 || m->dq < 0 || m->dkv < 0 || m->f <= 0 || m->vocab < 0)
+        return fail(MBQ_EINVAL, "%s: bad model dimensions", fn);
+    if (!(m->eps >= 0.f) || m->eps == __builtin_inff()) return fail(MBQ_EINVAL, "%s: bad eps", fn);
+    if (m->n_layers > 0 && !m->layers) return fail(MBQ_EINVAL, "%s: layers is NULL", fn);
+    if (!m->gamma_f || !aligned(m->gamma_f, 16)) return fail(MBQ_EALIGN, "%s: gamma_f must be 16-byte aligned", fn);
+    auto shape = [&](const mbq_qweight& W, int64_t N, int64_t K, bool fused, const char* what) {
+        int rc = check_weight(&W, fn);
+        if (rc) return rc;
+        if (W.N != N || W.K != K)
+            return fail(MBQ_EINVAL, "%s: %s is %lldx%lld, expected %lldx%lld", fn, what,
+                        (long long)W.N, (long long)W.K, (long long)N, (long long)K);
+        if ((rc = check_planes(&W, fn)) || (rc = check_kernel_shape(&W, fn))) return rc;
+        if (fused && !mbq::gemv_fused_supported(W.fmt, W.K))
+            return fail(MBQ_EUNSUPPORTED, "%s: %s needs a fused kernel (Q45/Q65, K = 4096 or 12288)", fn, what);
+        return MBQ_OK;
+    };
+    for (int l = 0; l < m->n_layers; l++) {
+        const mbq_decode_layer& L = m->layers[l];
+        int rc;
+        if ((rc = shape(L.qkv, m->dq + 2 * m->dkv, m->d, true, "qkv")) ||
+            (rc = shape(L.o, m->d, m->dq, false, "o")) ||
+            (rc = shape(L.gate_up, 2 * m->f, m->d, true, "gate_up")) ||
+            (rc = shape(L.down, m->d, m->f, false, "down")))
+            return rc;
+        if (!L.gamma1 || !L.gamma2 || !aligned(L.gamma1, 16) || !aligned(L.gamma2, 16))
+            return fail(MBQ_EALIGN, "%s: layer gammas must be 16-byte aligned", fn);
+    }
+    if (m->vocab > 0) {
+        int rc = shape(m->lm_head, m->vocab, m->d, true, "lm_head");
+        if (rc) return rc;
+    }
+    return MBQ_OK;
+}
+
+int mbq_decode_workspace_bytes(const mbq_decode_model* m, size_t* bytes) {
+    const char* fn = "mbq_decode_workspace_bytes";
+    if (!m || !bytes) return fail(MBQ_EINVAL, "%s: NULL pointer", fn);
+    if (m->dq < 0 || m->dkv < 0 || m->f < 0) return fail(MBQ_EINVAL, "%s: bad dimensions", fn);
+    *bytes = align256((size_t)(m->dq + 2 * m->dkv) * 4) + align256((size_t)m->f * 4);
+    return ok();
+}
+
+int mbq_decode_step(const mbq_decode_model* m, float* h, float* logits, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    const char* fn = "mbq_decode_step";
+    int rc = check_decode(m, fn);
+    if (rc) return rc;
+    size_t need = 0;
+    mbq_decode_workspace_bytes(m, &need);
+    if (!h || !aligned(h, 16)) return fail(MBQ_EALIGN, "%s: h must be 16-byte aligned", fn);
+    if (m->vocab > 0 && (!logits || !aligned(logits, 4))) return fail(MBQ_EINVAL, "%s: bad logits", fn);
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < need)
+        return fail(MBQ_EINVAL, "%s: workspace must be 256-byte aligned and >= %zu bytes", fn, need);
+    const size_t hb = (size_t)m->d * 4;
+    if (overlaps(h, hb, workspace, need) || (m->vocab > 0 && (overlaps(logits, (size_t)m->vocab * 4, h, hb) ||
+                                                               overlaps(logits, (size_t)m->vocab * 4, workspace, need))))
+        return fail(MBQ_EINVAL, "%s: h, logits and workspace must not overlap", fn);
+    hipStream_t s = (hipStream_t)stream;
+    float* qkv = (float*)workspace;
+    float* mm = (float*)((char*)workspace + align256((size_t)(m->dq + 2 * m->dkv) * 4));
+    auto geom = [](const mbq_qweight& W) {
+        mbq::GemvGeom g = mbq::gemv_m1_default_geom(W.fmt, W.N, W.K);
+        geom_override(&g);
+        return g;
+    };
+    hipError_t e = hipSuccess;
+    for (int l = 0; l < m->n_layers && e == hipSuccess; l++) {
+        const mbq_decode_layer& L = m->layers[l];
+        // a = rmsnorm(h, gamma1); q|k|v = Wqkv a
+        e = mbq::launch_gemv_fused(L.qkv.fmt, planes_of(&L.qkv), L.qkv.N, L.qkv.K, h, L.gamma1,
+                                   m->eps, false, qkv, 0, geom(L.qkv), s);
+        // h += Wo q   (the attention output stands in as q)
+        if (e == hipSuccess)
+            e = mbq::launch_gemv_m1(L.o.fmt, planes_of(&L.o), L.o.N, L.o.K, qkv, false, h, 1,
+                                    nullptr, 1, geom(L.o), s);
+        // b = rmsnorm(h, gamma2); m = silu(Wg b) * (Wu b)
+        if (e == hipSuccess)
+            e = mbq::launch_gemv_fused(L.gate_up.fmt, planes_of(&L.gate_up), L.gate_up.N,
+                                       L.gate_up.K, h, L.gamma2, m->eps, true, mm, 0,
+                                       geom(L.gate_up), s);
+        // h += Wd m
+        if (e == hipSuccess)
+            e = mbq::launch_gemv_m1(L.down.fmt, planes_of(&L.down), L.down.N, L.down.K, mm, false,
+                                    h, 1, nullptr, 1, geom(L.down), s);
+    }
+    // logits = Wvocab rmsnorm(h, gamma_f)
+    if (e == hipSuccess && m->vocab > 0)
+        e = mbq::launch_gemv_fused(m->lm_head.fmt, planes_of(&m->lm_head), m->vocab, m->d, h,
+                                   m->gamma_f, m->eps, false, logits, 0, geom(m->lm_head), s);
+    return hip_status(e, fn);
+}
+
 int mbq_xq_bytes(int fmt, int64_t M, int64_t K, size_t* bytes) {
     const char* fn = "mbq_xq_bytes";
     if (!fmt_valid(fmt)) return fail(MBQ_EINVAL, "%s: unknown format %d", fn, fmt);

@@ -41,13 +41,27 @@ constexpr int kXPre = 12;
 // needs (vector-memory counters retire in order) -- x never waits for
 // weights and a chunk never waits for the chunks prefetched after it.
 // CS == 0 handles any K with the same steps in runtime loops.
-template <int FMT, int R, int CS, bool GATHER, bool XQ>
+//
+// Fusions (static K, fp32 x only):
+//   PRO == kProRms: x is replaced by RMSNorm(x) * gamma before staging; each
+//     workgroup normalises the whole row in registers (one block-wide sum)
+//     while its first weight loads are in flight, so the norm costs no launch
+//     ([roofline-holds] "Hiding, fusing, and keeping the sums busy").
+//   EPI == kEpiSilu: rows 2i and 2i+1 are the gate and up rows of output i;
+//     the wave that computes both writes y[i] = silu(gate) * up.
+constexpr int kProNone = 0, kProRms = 1;
+constexpr int kEpiStore = 0, kEpiSilu = 1;
+
+template <int FMT, int R, int CS, bool GATHER, bool XQ, int PRO = kProNone, int EPI = kEpiStore>
 __global__ __launch_bounds__(kBlock) void gemv_m1_kernel(DevPlanes P, int64_t N, int K,
                                                          const void* __restrict__ xsrc,
                                                          float* __restrict__ y, int accumulate,
                                                          const int32_t* __restrict__ gidx,
-                                                         int rpe) {
+                                                         int rpe, const float* __restrict__ gamma,
+                                                         float eps) {
     using T = Traits<FMT>;
+    static_assert(PRO == kProNone || (CS > 0 && !XQ), "the norm prologue needs static K, fp32 x");
+    static_assert(EPI == kEpiStore || R == 2, "the silu epilogue pairs two rows per wave");
     using XP = XPieces<FMT, XQ>;
     constexpr int D = 2;                                      // chunk steps in flight
     extern __shared__ float4 smem[];
@@ -70,6 +84,11 @@ __global__ __launch_bounds__(kBlock) void gemv_m1_kernel(DevPlanes P, int64_t N,
     uint4 xr[NX];
 #pragma unroll
     for (int i = 0; i < NX; i++) xr[i] = XP::load(xsrc4, i, npieces);
+    uint4 gr[PRO == kProRms ? NX : 1];
+    if constexpr (PRO == kProRms) {
+#pragma unroll
+        for (int i = 0; i < NX; i++) gr[i] = XP::load((const uint4*)gamma, i, npieces);
+    }
 
     // ---- y for an accumulating product (one load per lane, unconditional)
     const int64_t yrow = row0 + (lane < R ? lane : 0);
@@ -120,6 +139,27 @@ __global__ __launch_bounds__(kBlock) void gemv_m1_kernel(DevPlanes P, int64_t N,
         Slot<FMT, R> buf[DD];
 #pragma unroll
         for (int d = 0; d < DD; d++) load(buf[d], d);
+        if constexpr (PRO == kProRms) {
+            // RMSNorm of the row, as the stand-alone kernel: y = g * (x * inv)
+            __shared__ float red[kWavesPerBlock];
+            float ss = 0.f;
+#pragma unroll
+            for (int i = 0; i < NX; i++) {
+                const float4 v = __builtin_bit_cast(float4, xr[i]);
+                ss = fmaf(v.x, v.x, ss);
+                ss = fmaf(v.y, v.y, ss);
+                ss = fmaf(v.z, v.z, ss);
+                ss = fmaf(v.w, v.w, ss);
+            }
+            const float inv = 1.0f / sqrtf(block_sum(ss, red) / (float)K + eps);
+#pragma unroll
+            for (int i = 0; i < NX; i++) {
+                const float4 v = __builtin_bit_cast(float4, xr[i]);
+                const float4 g = __builtin_bit_cast(float4, gr[i]);
+                xr[i] = __builtin_bit_cast(uint4, make_float4(g.x * (v.x * inv), g.y * (v.y * inv),
+                                                              g.z * (v.z * inv), g.w * (v.w * inv)));
+            }
+        }
         XP::template store<NX, true>(xr, 0, npieces, xs);
         __syncthreads();
 #pragma unroll
@@ -153,10 +193,15 @@ __global__ __launch_bounds__(kBlock) void gemv_m1_kernel(DevPlanes P, int64_t N,
         }
     }
 
+    if constexpr (EPI == kEpiSilu) {
+        const float g = wave_sum_dpp(acc[0]), u = wave_sum_dpp(acc[1]);
+        if (lane == 0 && row0 + 1 < N) y[row0 / 2] = g / (1.0f + expf(-g)) * u;
+    } else {
 #pragma unroll
-    for (int r = 0; r < R; r++) {
-        const float s = wave_sum_dpp(acc[r]);
-        if (lane == r && row0 + r < N) y[row0 + r] = (accumulate ? yin : 0.f) + s;
+        for (int r = 0; r < R; r++) {
+            const float s = wave_sum_dpp(acc[r]);
+            if (lane == r && row0 + r < N) y[row0 + r] = (accumulate ? yin : 0.f) + s;
+        }
     }
 }
 
@@ -178,22 +223,24 @@ struct M1Args {
     int accumulate;
     const int32_t* gidx;
     int64_t rpe;
+    const float* gamma;
+    float eps;
 };
 
-template <int FMT, int R, int CS, bool GATHER, bool XQ>
+template <int FMT, int R, int CS, bool GATHER, bool XQ, int PRO = kProNone, int EPI = kEpiStore>
 static hipError_t launch_k(const M1Args& a, hipStream_t stream) {
     using T = Traits<FMT>;
     const int64_t rows_per_wg = (int64_t)kWavesPerBlock * R;
     const int64_t grid = (a.N + rows_per_wg - 1) / rows_per_wg;
     const size_t lds = (size_t)(a.K / T::WPC) * Stride<FMT>::DW * 4;
-    auto kern = gemv_m1_kernel<FMT, R, CS, GATHER, XQ>;
+    auto kern = gemv_m1_kernel<FMT, R, CS, GATHER, XQ, PRO, EPI>;
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute((const void*)kern,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBlock), lds, stream, a.P, a.N, (int)a.K,
-                       a.x, a.y, a.accumulate, a.gidx, (int)a.rpe);
+                       a.x, a.y, a.accumulate, a.gidx, (int)a.rpe, a.gamma, a.eps);
     return hipGetLastError();
 }
 
@@ -240,7 +287,7 @@ GemvGeom gemv_m1_default_geom(int fmt, int64_t N, int64_t K) {
 hipError_t launch_gemv_m1(int fmt, DevPlanes P, int64_t N_out, int64_t K, const void* x,
                           bool x_staged, float* y, int accumulate, const int32_t* gidx,
                           int64_t rpe, GemvGeom geom, hipStream_t stream) {
-    const M1Args a{P, N_out, K, x, y, accumulate, gidx, rpe};
+    const M1Args a{P, N_out, K, x, y, accumulate, gidx, rpe, nullptr, 0.f};
     switch (fmt) {
     case kQ45: return launch_f<kQ45>(a, x_staged, geom, stream);
     case kQ65: return launch_f<kQ65>(a, x_staged, geom, stream);
@@ -248,6 +295,48 @@ hipError_t launch_gemv_m1(int fmt, DevPlanes P, int64_t N_out, int64_t K, const 
     case kBF16: return launch_f<kBF16>(a, x_staged, geom, stream);
     }
     return hipErrorInvalidValue;
+}
+
+// ---- fused products ---------------------------------------------------
+template <int FMT, int CS, int PRO>
+static hipError_t launch_fused_cs(const M1Args& a, bool silu, int rows, hipStream_t s) {
+    if (silu) return launch_k<FMT, 2, CS, false, false, PRO, kEpiSilu>(a, s);
+    switch (rows) {
+    case 1: return launch_k<FMT, 1, CS, false, false, PRO, kEpiStore>(a, s);
+    case 2: return launch_k<FMT, 2, CS, false, false, PRO, kEpiStore>(a, s);
+    default: return launch_k<FMT, 4, CS, false, false, PRO, kEpiStore>(a, s);
+    }
+}
+
+template <int FMT>
+static hipError_t launch_fused_f(const M1Args& a, bool norm, bool silu, int rows, hipStream_t s) {
+    switch (static_steps<FMT>(a.K)) {
+    case 2:
+        return norm ? launch_fused_cs<FMT, 2, kProRms>(a, silu, rows, s)
+                    : launch_fused_cs<FMT, 2, kProNone>(a, silu, rows, s);
+    case 6:
+        return norm ? launch_fused_cs<FMT, 6, kProRms>(a, silu, rows, s)
+                    : launch_fused_cs<FMT, 6, kProNone>(a, silu, rows, s);
+    default: return hipErrorNotSupported;
+    }
+}
+
+bool gemv_fused_supported(int fmt, int64_t K) {
+    if (fmt == kQ45) return static_steps<kQ45>(K) == 2 || static_steps<kQ45>(K) == 6;
+    if (fmt == kQ65) return static_steps<kQ65>(K) == 2 || static_steps<kQ65>(K) == 6;
+    return false;
+}
+
+hipError_t launch_gemv_fused(int fmt, DevPlanes P, int64_t N, int64_t K, const float* x,
+                             const float* gamma, float eps, bool silu, float* y, int accumulate,
+                             GemvGeom geom, hipStream_t stream) {
+    const M1Args a{P, N, K, x, y, accumulate, nullptr, 1, gamma, eps};
+    const bool norm = gamma != nullptr;
+    switch (fmt) {
+    case kQ45: return launch_fused_f<kQ45>(a, norm, silu, geom.rows_per_wave, stream);
+    case kQ65: return launch_fused_f<kQ65>(a, norm, silu, geom.rows_per_wave, stream);
+    }
+    return hipErrorNotSupported;
 }
 
 // y[m][n] = 0, n < N (the K == 0 product).

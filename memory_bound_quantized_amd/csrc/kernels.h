@@ -37,6 +37,15 @@ hipError_t launch_gemv_m1(int fmt, DevPlanes P, int64_t N_out, int64_t K, const 
                           bool x_staged, float* y, int accumulate, const int32_t* gidx,
                           int64_t rpe, GemvGeom geom, hipStream_t stream);
 
+// Fused M = 1 product on fp32 x (Q45/Q65 with K = 4096 or 12288 only, see
+// gemv_fused_supported): y = W . rmsnorm(x; gamma, eps) when gamma != nullptr,
+// else W . x; silu: W's rows 2i, 2i+1 are gate and up rows and
+// y[i] = silu(gate . x) * (up . x) for i < N / 2 (accumulate must be 0).
+bool gemv_fused_supported(int fmt, int64_t K);
+hipError_t launch_gemv_fused(int fmt, DevPlanes P, int64_t N, int64_t K, const float* x,
+                             const float* gamma, float eps, bool silu, float* y, int accumulate,
+                             GemvGeom geom, hipStream_t stream);
+
 // Staged x for fmt (staging.h) of M rows of fp32 x: xq[m] = stage(x[m][0:K]),
 // rows of xq packed back to back (4*K bytes each).
 hipError_t launch_stage_x(int fmt, const float* x, int64_t M, int64_t ldx, int64_t K, void* xq,

@@ -18,7 +18,7 @@ def rel_l2(got, ref):
 X_CHUNK = {0: None, 1: 32, 2: 32, 3: 64}   # values per x rounding chunk, by format
 
 
-def check_gemv(y, ow, x, ref, y0=None):
+def check_gemv(y, ow, x, ref, y0=None, slack=None):
     """Two bars on a GEMV output.
     (1) every element lies within the forward-error bound of the kernel's
         arithmetic for any summation order: fp32 sums,
@@ -28,7 +28,9 @@ def check_gemv(y, ow, x, ref, y0=None):
     (2) the relative L2 error over the output vector is <= 1e-4 whenever the
         vector has at least 16 entries.  A single output can be arbitrarily
         ill-conditioned (its value near zero against large terms), so no fp32
-        kernel can promise (2) for one entry; (1) is the bar there."""
+        kernel can promise (2) for one entry; (1) is the bar there.
+    slack: added to the per-element bound, for inputs known only within a
+    tolerance (e.g. a norm computed on the device)."""
     x = np.atleast_2d(np.asarray(x, np.float64))
     y = np.atleast_2d(np.asarray(y, np.float64))
     ref = np.atleast_2d(np.asarray(ref, np.float64))
@@ -42,6 +44,8 @@ def check_gemv(y, ow, x, ref, y0=None):
         amax = np.abs(x).reshape(x.shape[0], -1, ch).max(axis=2)
         xmax = np.repeat(amax, ch, axis=1)
         bound = bound + 2.0 ** -22 * (xmax @ absw.T)
+    if slack is not None:          # a known perturbation of x (per output)
+        bound = bound + slack
     worst = np.max(np.abs(y - ref) / bound)
     assert worst <= 1.0, "element outside the fp32 forward-error bound (ratio %.3g)" % worst
     if y.size >= 16:

@@ -30,7 +30,7 @@ def _declared_symbols():
 
 def test_library_exports_every_declared_symbol():
     declared = _declared_symbols()
-    assert len(declared) == 21
+    assert len(declared) == 24
     assert sorted(_lib.EXPORTS) == declared
     lib = ctypes.CDLL(_lib.LIB_PATH)
     for name in declared:
@@ -220,6 +220,72 @@ def test_staged_x_argument_checks():
     assert sm(n=100) == _lib.EINVAL
     assert sm(g=BASE + 0x400008) == _lib.EALIGN
     assert sm(xq=BASE + 0x500000) == _lib.EINVAL                            # xq overlaps u
+
+
+def test_fused_gemv_argument_checks():
+    x, gm, y = BASE + 0x400000, BASE + 0x500000, BASE + 0x800000
+    fz = lambda d, x=x, g=gm, eps=1e-6, epi=0, y=y: L.mbq_gemv_fused(ctypes.byref(d), x, g, eps, epi, y, None)
+    assert fz(_desc(K=4096), epi=3) == _lib.EINVAL
+    assert fz(_desc(N=63, K=4096), epi=2) == _lib.EINVAL                    # silu needs even N
+    assert fz(_desc(K=4096), eps=-1.0) == _lib.EINVAL
+    assert fz(_desc(N=0, K=4096)) == _lib.OK
+    assert fz(_desc(K=4096), x=None) == _lib.EINVAL
+    assert fz(_desc(K=4096), g=gm + 4) == _lib.EALIGN
+    assert fz(_desc(K=4096), y=x + 64) == _lib.EINVAL                       # y overlaps x
+    assert fz(_desc(K=2048)) == _lib.EUNSUPPORTED                           # no fused kernel
+    assert fz(_desc(fmt=3, K=4096)) == _lib.EUNSUPPORTED
+    assert fz(_desc(fmt=0, K=4096), epi=2) == _lib.EUNSUPPORTED
+
+
+def _model(L=1, d=4096, dq=4096, dkv=1024, f=12288, vocab=1000, fmt_down=2):
+    lay = (_lib.DecodeLayerDesc * L)()
+    off = 0
+
+    def w(fmt, N, K):
+        nonlocal off
+        off += 0x10000000
+        return _desc(fmt=fmt, N=N, K=K, off=off)
+    for l in range(L):
+        lay[l] = _lib.DecodeLayerDesc(w(1, dq + 2 * dkv, d), w(1, d, dq), w(1, 2 * f, d),
+                                      w(fmt_down, d, f), BASE + 0x100, BASE + 0x200)
+    m = _lib.DecodeModelDesc(L, 1e-6, d, dq, dkv, f, vocab, ctypes.cast(lay, ctypes.POINTER(_lib.DecodeLayerDesc)),
+                             BASE + 0x300, w(2, vocab, d))
+    m._keep = lay
+    return m
+
+
+def test_decode_argument_checks():
+    m = _model()
+    nb = ctypes.c_size_t()
+    assert L.mbq_decode_workspace_bytes(ctypes.byref(m), ctypes.byref(nb)) == _lib.OK
+    assert nb.value == (4096 + 2048) * 4 + 12288 * 4
+    h, lg, ws = BASE + 0x7000000000, BASE + 0x7100000000, BASE + 0x7200000000
+    st = lambda m, h=h, lg=lg, ws=ws, n=nb.value: L.mbq_decode_step(ctypes.byref(m), h, lg, ws, n, None)
+    assert st(m, n=nb.value - 1) == _lib.EINVAL                             # workspace too small
+    assert st(m, ws=ws + 16) == _lib.EINVAL                                 # 256-byte alignment
+    assert st(m, h=h + 4) == _lib.EALIGN
+    assert st(m, lg=ws + 64) == _lib.EINVAL                                 # logits overlap workspace
+    bad = _model(dkv=512)
+    bad.layers[0].qkv.N = 4096 + 2048                                       # not dq + 2 dkv
+    assert st(bad) == _lib.EINVAL
+    assert st(_model(d=2048, dq=2048)) == _lib.EUNSUPPORTED                 # no fused kernel for d=2048
+    e = _model(vocab=0)
+    e.eps = float("nan")
+    assert st(e) == _lib.EINVAL
+    assert L.mbq_last_error()
+
+
+def test_row_concatenation_and_interleaving_match_the_oracle():
+    from memory_bound_quantized_amd.decode import concat_rows, interleave_rows
+    rng = np.random.default_rng(4)
+    mk = lambda fmt, N, K: (fmt, N, K, workloads.weight_planes(rng, fmt, N, K))
+    for fmt, K in ((1, 256), (2, 512), (3, 128), (0, 64)):
+        a, b, c = mk(fmt, 5, K), mk(fmt, 3, K), mk(fmt, 5, K)
+        wa, wb, wc = (oracle.dequant(oracle.Planes(*m)) for m in (a, b, c))
+        cat = oracle.dequant(oracle.Planes(*concat_rows([a, b])))
+        assert np.array_equal(cat, np.concatenate([wa, wb]))
+        il = oracle.dequant(oracle.Planes(*interleave_rows(a, c)))
+        assert np.array_equal(il[0::2], wa) and np.array_equal(il[1::2], wc)
 
 
 def test_export_and_probe_argument_checks():
