@@ -282,6 +282,13 @@ int mbq_gemv_q(const mbq_qweight* W, const float* x, int64_t M, int64_t ldx, flo
         return hip_status(mbq::launch_gemv_m1(W->fmt, P, W->N, W->K, x, false, y, accumulate,
                                               nullptr, 1, g, s), fn);
     }
+    if (M <= 8) {
+        if (!mbq::gemv_smallm_fits(W->fmt, M, W->K))
+            return fail(MBQ_EUNSUPPORTED, "%s: M=%lld tokens of K=%lld do not fit the LDS", fn,
+                        (long long)M, (long long)W->K);
+        return hip_status(mbq::launch_gemv_smallm(W->fmt, P, W->N, W->K, x, false, M, ldx, y, ldy,
+                                                  accumulate, s), fn);
+    }
     return fail(MBQ_EUNSUPPORTED, "%s: no kernel for M=%lld with format %d", fn, (long long)M, W->fmt);
 }
 
@@ -496,6 +503,13 @@ int mbq_gemv_xq(const mbq_qweight* W, const void* xq, int64_t M, float* y, int64
         geom_override(&g);
         return hip_status(mbq::launch_gemv_m1(W->fmt, P, W->N, W->K, xq, true, y, accumulate,
                                               nullptr, 1, g, s), fn);
+    }
+    if (M <= 8) {
+        if (!mbq::gemv_smallm_fits(W->fmt, M, W->K))
+            return fail(MBQ_EUNSUPPORTED, "%s: M=%lld tokens of K=%lld do not fit the LDS", fn,
+                        (long long)M, (long long)W->K);
+        return hip_status(mbq::launch_gemv_smallm(W->fmt, P, W->N, W->K, xq, true, M, W->K, y, ldy,
+                                                  accumulate, s), fn);
     }
     return fail(MBQ_EUNSUPPORTED, "%s: no kernel for M=%lld with format %d", fn, (long long)M, W->fmt);
 }

@@ -90,18 +90,26 @@ struct Traits<kQ45> {
         ev = d & 0x0F0F0F0Fu;
         od = (d >> 4) & 0x0F0F0F0Fu;
     }
-    // The chunk's contribution to y (xv: the chunk's 32 staged dwords).
-    __device__ static __forceinline__ float dot(const Row& r, const uint32_t* xv) {
+    // Code vectors of the chunk, in the order of the staged digit words.
+    static constexpr int NVEC = 8;
+    __device__ static __forceinline__ void unpack(const Row& r, uint32_t* v) {
         const uint32_t* c = &r.c.x;
+#pragma unroll
+        for (int i = 0; i < 4; i++) vectors(c[i], v[2 * i], v[2 * i + 1]);
+    }
+    // The chunk's contribution to y from its code vectors (xv: the chunk's
+    // 32 staged dwords).
+    __device__ static __forceinline__ float dot_vec(const Row& r, const uint32_t* v,
+                                                    const uint32_t* xv) {
         Acc3 s{xv[META + 1], xv[META + 2], (int32_t)xv[META + 3]};
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            uint32_t ev, od;
-            vectors(c[i], ev, od);
-            acc_vec(s, ev, xv + 6 * i);
-            acc_vec(s, od, xv + 6 * i + 3);
-        }
+        for (int j = 0; j < NVEC; j++) acc_vec(s, v[j], xv + 3 * j);
         return (h2f(r.s) * as_f(xv[META])) * acc_value(s);
+    }
+    __device__ static __forceinline__ float dot(const Row& r, const uint32_t* xv) {
+        uint32_t v[NVEC];
+        unpack(r, v);
+        return dot_vec(r, v, xv);
     }
     // integer codes of the chunk, through the same unpack as dot()
     __device__ static __forceinline__ void codes(const Row& r, int* q) {
@@ -170,20 +178,29 @@ struct Traits<kQ65> {
     __device__ static __forceinline__ float sc_f(uint32_t sc, int sb) {
         return (float)(int)(int8_t)((sc >> (8 * sb)) & 0xFFu);
     }
-    __device__ static __forceinline__ float dot(const Row& r, const uint32_t* xv) {
+    static constexpr int NVEC = 8;
+    __device__ static __forceinline__ void unpack(const Row& r, uint32_t* v) {
         const uint32_t* ql = &r.ql.x;
         const uint32_t* qh = &r.qh.x;
+#pragma unroll
+        for (int sb = 0; sb < 2; sb++) vectors(ql[2 * sb], ql[2 * sb + 1], qh[sb], v + 4 * sb);
+    }
+    __device__ static __forceinline__ float dot_vec(const Row& r, const uint32_t* v,
+                                                    const uint32_t* xv) {
         float t[2];
 #pragma unroll
         for (int sb = 0; sb < 2; sb++) {
-            uint32_t v[4];
-            vectors(ql[2 * sb], ql[2 * sb + 1], qh[sb], v);
             Acc3 s{xv[META + 1 + 3 * sb], xv[META + 2 + 3 * sb], (int32_t)xv[META + 3 + 3 * sb]};
 #pragma unroll
-            for (int i = 0; i < 4; i++) acc_vec(s, v[i], xv + 12 * sb + 3 * i);
+            for (int i = 0; i < 4; i++) acc_vec(s, v[4 * sb + i], xv + 12 * sb + 3 * i);
             t[sb] = acc_value(s);
         }
         return (h2f(r.d) * as_f(xv[META])) * fmaf(sc_f(r.sc, 1), t[1], sc_f(r.sc, 0) * t[0]);
+    }
+    __device__ static __forceinline__ float dot(const Row& r, const uint32_t* xv) {
+        uint32_t v[NVEC];
+        unpack(r, v);
+        return dot_vec(r, v, xv);
     }
     __device__ static __forceinline__ void codes(const Row& r, int* q) {
         const uint32_t* ql = &r.ql.x;
@@ -238,21 +255,30 @@ struct Traits<kQ25> {
     __device__ static __forceinline__ uint32_t vec(uint32_t d, int m) {
         return (d >> (2 * m)) & 0x03030303u;
     }
-    __device__ static __forceinline__ float dot(const Row& r, const uint32_t* xv) {
+    static constexpr int NVEC = 16;
+    __device__ static __forceinline__ void unpack(const Row& r, uint32_t* v) {
         const uint32_t* c = &r.c.x;
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int m = 0; m < 4; m++) v[4 * i + m] = vec(c[i], m);
+    }
+    __device__ static __forceinline__ float dot_vec(const Row& r, const uint32_t* v,
+                                                    const uint32_t* xv) {
         float t[2];
 #pragma unroll
         for (int blk = 0; blk < 2; blk++) {
             Acc3 s{xv[META + 1 + 3 * blk], xv[META + 2 + 3 * blk], (int32_t)xv[META + 3 + 3 * blk]};
 #pragma unroll
-            for (int ii = 0; ii < 2; ii++) {
-                const int i = 2 * blk + ii;
-#pragma unroll
-                for (int m = 0; m < 4; m++) acc_vec(s, vec(c[i], m), xv + 12 * i + 3 * m);
-            }
+            for (int j = 0; j < 8; j++) acc_vec(s, v[8 * blk + j], xv + 24 * blk + 3 * j);
             t[blk] = acc_value(s);
         }
         return as_f(xv[META]) * fmaf(h2f(r.s2 >> 16), t[1], h2f(r.s2) * t[0]);
+    }
+    __device__ static __forceinline__ float dot(const Row& r, const uint32_t* xv) {
+        uint32_t v[NVEC];
+        unpack(r, v);
+        return dot_vec(r, v, xv);
     }
     __device__ static __forceinline__ void codes(const Row& r, int* q) {
         const uint32_t* c = &r.c.x;
@@ -295,15 +321,30 @@ struct Traits<kBF16> {
     __device__ static __forceinline__ void load(Row& r, const DevPlanes& B, int b) {
         r.w = *(const uint4*)(B.p0 + 16 * b);
     }
-    __device__ static __forceinline__ float dot(const Row& r, const uint32_t* xv) {
+    static constexpr int NVEC = 8;   // the 8 weights as fp32 bit patterns
+    __device__ static __forceinline__ void unpack(const Row& r, uint32_t* v) {
         const uint32_t* c = &r.w.x;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            v[2 * i] = c[i] << 16;
+            v[2 * i + 1] = c[i] & 0xFFFF0000u;
+        }
+    }
+    __device__ static __forceinline__ float dot_vec(const Row& r, const uint32_t* v,
+                                                    const uint32_t* xv) {
+        (void)r;
         float a0 = 0.f, a1 = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            a0 = fmaf(as_f(c[i] << 16), as_f(xv[2 * i]), a0);
-            a1 = fmaf(as_f(c[i] & 0xFFFF0000u), as_f(xv[2 * i + 1]), a1);
+            a0 = fmaf(as_f(v[2 * i]), as_f(xv[2 * i]), a0);
+            a1 = fmaf(as_f(v[2 * i + 1]), as_f(xv[2 * i + 1]), a1);
         }
         return a0 + a1;
+    }
+    __device__ static __forceinline__ float dot(const Row& r, const uint32_t* xv) {
+        uint32_t v[NVEC];
+        unpack(r, v);
+        return dot_vec(r, v, xv);
     }
     __device__ static __forceinline__ void weights(const Row& r, float* w) {
         const uint32_t* c = &r.w.x;

@@ -59,10 +59,13 @@ hipError_t launch_rmsnorm_xq(const float* x, const float* gamma, float eps, int6
 hipError_t launch_silu_mul_xq(const float* g, const float* u, int64_t n, int fmt, void* xq,
                               hipStream_t stream);
 
-// Y[m][n] (+)= W[n] . X[m] for 2 <= M <= 8 (vector units).
-hipError_t launch_gemv_smallm(int fmt, DevPlanes P, int64_t N, int64_t K, const float* x,
-                              int64_t M, int64_t ldx, float* y, int64_t ldy, int accumulate,
-                              hipStream_t stream);
+// Y[m][n] (+)= W[n] . X[m] for 2 <= M <= 8 (vector units).  X is fp32
+// [M][ldx], or staged for fmt (M rows of K) when x_staged.  All M tokens are
+// staged in LDS: gemv_smallm_fits tells whether they fit.
+bool gemv_smallm_fits(int fmt, int64_t M, int64_t K);
+hipError_t launch_gemv_smallm(int fmt, DevPlanes P, int64_t N, int64_t K, const void* x,
+                              bool x_staged, int64_t M, int64_t ldx, float* y, int64_t ldy,
+                              int accumulate, hipStream_t stream);
 
 // Y[m][n] (+)= W[n] . X[m] for 16 <= M <= 64, Q45 only (matrix cores).
 hipError_t launch_gemv_mfma_q45(DevPlanes P, int64_t N, int64_t K, const float* x, int64_t M,

@@ -142,6 +142,7 @@ def test_gemv_argument_checks():
     assert _gemv(_desc(K=65536)) == _lib.EUNSUPPORTED           # beyond the LDS-staged K
     assert _gemv(_desc(), M=9, ldx=256, ldy=64) == _lib.EUNSUPPORTED
     assert _gemv(_desc(), M=65, ldx=256, ldy=64) == _lib.EUNSUPPORTED
+    assert _gemv(_desc(K=32768), M=8, ldx=32768, ldy=64) == _lib.EUNSUPPORTED   # LDS capacity
     assert _gemv(_desc(fmt=2), M=16, ldx=256, ldy=64) == _lib.EUNSUPPORTED
     assert L.mbq_last_error()
 
