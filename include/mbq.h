@@ -131,12 +131,13 @@ int mbq_unpack(int fmt, int64_t N, int64_t K, const void* const planes[4],
  * x: device fp32 [M][ldx], 16-byte aligned, ldx >= K, ldx % 4 == 0.
  * y: device fp32 [M][ldy], 4-byte aligned, ldy >= N; must not overlap x.
  * Arithmetic: weights exact in fp32, fp32 accumulation; the order of the sum
- * is unspecified.  M <= 8 runs on the vector units; M >= 16 (Q45 only) may use
- * the matrix cores.  MBQ_EUNSUPPORTED for shapes without a kernel
- * (K > 32768, or K > 16384 for BF16; Q25 with K % 64 != 0; BF16 with
- * K % 8 != 0; 8 < M < 16; M > 64,
- * or M >= 16 with a format other than Q45).  M == 0 or N == 0 enqueue
- * nothing; K == 0 writes zeros (or leaves y for accumulate = 1). */
+ * is unspecified.  Tokens run on the vector units, up to 8 per launch (as many
+ * as fit staged in LDS: all 8 for K = 4096, 2 for K = 12288), each weight
+ * read once per launch and unpacked once for all its tokens.  Matrix cores
+ * take Q45 batches of 16 or more through mbq_stage_x + mbq_gemv_xq.
+ * MBQ_EUNSUPPORTED for shapes without a kernel (K > 32768, or K > 16384 for
+ * BF16; Q25 with K % 64 != 0; BF16 with K % 8 != 0).  M == 0 or N == 0
+ * enqueue nothing; K == 0 writes zeros (or leaves y for accumulate = 1). */
 int mbq_gemv_q(const mbq_qweight* W, const float* x, int64_t M, int64_t ldx,
                float* y, int64_t ldy, int accumulate, void* stream);
 
@@ -237,10 +238,16 @@ int mbq_decode_step(const mbq_decode_model* model, float* h, float* logits, void
  * the sums busy").  The form is opaque and format-specific: stage for the
  * format of the matrix that consumes it.  It takes 4 bytes per value
  * (mbq_xq_bytes), rows back to back; for BF16 it is x itself in fp32.
+ * For Q45 with M >= 16 tokens it is the matrix-core tile form instead: per
+ * tile of 16 tokens and block of 32 values, each token scaled by a power of
+ * two (its largest |x| in [2^14, 2^15)) and split into fp16 high and low
+ * parts in the MFMA operand order, then one float 2^-e per token slot
+ * (mbq_xq_bytes gives its size; it needs K % 1024 == 0).
  */
 
-/* Bytes of staged x for M rows of K values: 4*M*K.  Host only.  MBQ_EINVAL
- * for an unknown format or K not a multiple of the chunk (32; Q25 64; BF16 8). */
+/* Bytes of staged x for M rows of K values: 4*M*K, or for Q45 with M >= 16
+ * ceil(M/16) * (K/32 * 2048 + 64).  Host only.  MBQ_EINVAL for an unknown
+ * format or K not a multiple of the chunk (32; Q25 64; BF16 8). */
 int mbq_xq_bytes(int fmt, int64_t M, int64_t K, size_t* bytes);
 
 /* xq = staged form of x for fmt.  x: device fp32 [M][ldx], 16-byte aligned,
@@ -250,9 +257,13 @@ int mbq_stage_x(int fmt, const float* x, int64_t M, int64_t ldx, int64_t K, void
                 void* stream);
 
 /* mbq_gemv_q with x given in staged form (staged for W->fmt, M rows of K):
- * the same products, sums and limits; the result equals mbq_gemv_q's on the
- * same x up to the order of the fp32 sums.  xq: device, 16-byte aligned, must
- * not overlap y.  M == 1 in this version (MBQ_EUNSUPPORTED otherwise). */
+ * the same products, sums and limits.  With the row form the result is bit
+ * for bit mbq_gemv_q's on the same x.  Q45 with M >= 16 (tile form) runs on
+ * the matrix cores ([roofline-holds] "The Math": past M* the sums, not the
+ * bytes, bound the product): fp16 (q - 8) codes, which are exact, against
+ * the fp16 high and low parts of x, fp32 results, each block's scale applied
+ * to its fp32 block sum; it needs K % 1024 == 0 and 8-byte aligned scales.
+ * xq: device, 16-byte aligned, must not overlap y. */
 int mbq_gemv_xq(const mbq_qweight* W, const void* xq, int64_t M, float* y, int64_t ldy,
                 int accumulate, void* stream);
 

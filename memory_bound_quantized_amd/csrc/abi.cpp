@@ -95,6 +95,9 @@ int check_kernel_shape(const mbq_qweight* W, const char* fn) {
     return MBQ_OK;
 }
 
+// Staged x of M >= 16 Q45 tokens takes the matrix-core tile form.
+bool xq_tiled(int fmt, int64_t M) { return fmt == MBQ_FMT_Q45 && M >= 16; }
+
 // Values per chunk of staged x (the unit of its fixed-point exponent).
 int64_t xq_chunk(int fmt) {
     switch (fmt) {
@@ -282,14 +285,20 @@ int mbq_gemv_q(const mbq_qweight* W, const float* x, int64_t M, int64_t ldx, flo
         return hip_status(mbq::launch_gemv_m1(W->fmt, P, W->N, W->K, x, false, y, accumulate,
                                               nullptr, 1, g, s), fn);
     }
-    if (M <= 8) {
-        if (!mbq::gemv_smallm_fits(W->fmt, M, W->K))
-            return fail(MBQ_EUNSUPPORTED, "%s: M=%lld tokens of K=%lld do not fit the LDS", fn,
-                        (long long)M, (long long)W->K);
-        return hip_status(mbq::launch_gemv_smallm(W->fmt, P, W->N, W->K, x, false, M, ldx, y, ldy,
-                                                  accumulate, s), fn);
+    // 2 <= M: passes of up to 8 tokens on the vector units, as many as the
+    // LDS holds staged (a single token always fits: K <= kMaxK)
+    int64_t mp = M < 8 ? M : 8;
+    while (mp > 1 && !mbq::gemv_smallm_fits(W->fmt, mp, W->K)) mp--;
+    for (int64_t m0 = 0; m0 < M; m0 += mp) {
+        const int64_t mm = M - m0 < mp ? M - m0 : mp;
+        hipError_t e = mm == 1 ? mbq::launch_gemv_m1(W->fmt, P, W->N, W->K, x + m0 * ldx, false,
+                                                     y + m0 * ldy, accumulate, nullptr, 1,
+                                                     mbq::gemv_m1_default_geom(W->fmt, W->N, W->K), s)
+                               : mbq::launch_gemv_smallm(W->fmt, P, W->N, W->K, x + m0 * ldx, false,
+                                                         mm, ldx, y + m0 * ldy, ldy, accumulate, s);
+        if (e != hipSuccess) return hip_status(e, fn);
     }
-    return fail(MBQ_EUNSUPPORTED, "%s: no kernel for M=%lld with format %d", fn, (long long)M, W->fmt);
+    return ok();
 }
 
 int mbq_gemv_q_gather(const mbq_qweight* W_all, int64_t rows_per_expert, const int32_t* idx,
@@ -454,7 +463,7 @@ int mbq_xq_bytes(int fmt, int64_t M, int64_t K, size_t* bytes) {
     if (K % xq_chunk(fmt))
         return fail(MBQ_EINVAL, "%s: K=%lld is not a multiple of %lld", fn, (long long)K,
                     (long long)xq_chunk(fmt));
-    *bytes = (size_t)M * (size_t)K * 4;
+    *bytes = xq_tiled(fmt, M) ? (size_t)mbq::xt_bytes(M, K) : (size_t)M * (size_t)K * 4;
     return ok();
 }
 
@@ -473,6 +482,10 @@ int mbq_stage_x(int fmt, const float* x, int64_t M, int64_t ldx, int64_t K, void
         return fail(MBQ_EALIGN, "%s: x and xq must be 16-byte aligned with ldx %% 4 == 0", fn);
     if (overlaps(x, (size_t)((M - 1) * ldx + K) * 4, xq, xqb))
         return fail(MBQ_EINVAL, "%s: x and xq overlap", fn);
+    if (xq_tiled(fmt, M)) {
+        if (K % 1024) return fail(MBQ_EUNSUPPORTED, "%s: the tile form needs K %% 1024 == 0", fn);
+        return hip_status(mbq::launch_stage_x_mfma(x, M, ldx, K, xq, (hipStream_t)stream), fn);
+    }
     return hip_status(mbq::launch_stage_x(fmt, x, M, ldx, K, xq, (hipStream_t)stream), fn);
 }
 
@@ -494,7 +507,8 @@ int mbq_gemv_xq(const mbq_qweight* W, const void* xq, int64_t M, float* y, int64
     }
     if (!aligned(xq, 16)) return fail(MBQ_EALIGN, "%s: xq must be 16-byte aligned", fn);
     const size_t ybytes = (size_t)((M - 1) * ldy + W->N) * 4;
-    if (overlaps(xq, (size_t)(M * W->K) * 4, y, ybytes)) return fail(MBQ_EINVAL, "%s: xq and y overlap", fn);
+    const size_t xqb = xq_tiled(W->fmt, M) ? (size_t)mbq::xt_bytes(M, W->K) : (size_t)(M * W->K) * 4;
+    if (overlaps(xq, xqb, y, ybytes)) return fail(MBQ_EINVAL, "%s: xq and y overlap", fn);
     if ((rc = check_planes(W, fn))) return rc;
     if ((rc = check_kernel_shape(W, fn))) return rc;
     const mbq::DevPlanes P = planes_of(W);
@@ -504,14 +518,26 @@ int mbq_gemv_xq(const mbq_qweight* W, const void* xq, int64_t M, float* y, int64
         return hip_status(mbq::launch_gemv_m1(W->fmt, P, W->N, W->K, xq, true, y, accumulate,
                                               nullptr, 1, g, s), fn);
     }
-    if (M <= 8) {
-        if (!mbq::gemv_smallm_fits(W->fmt, M, W->K))
-            return fail(MBQ_EUNSUPPORTED, "%s: M=%lld tokens of K=%lld do not fit the LDS", fn,
-                        (long long)M, (long long)W->K);
-        return hip_status(mbq::launch_gemv_smallm(W->fmt, P, W->N, W->K, xq, true, M, W->K, y, ldy,
-                                                  accumulate, s), fn);
+    if (xq_tiled(W->fmt, M)) {
+        if (W->K % 1024) return fail(MBQ_EUNSUPPORTED, "%s: the matrix-core kernel needs K %% 1024 == 0", fn);
+        if (!aligned(W->scales, 8)) return fail(MBQ_EALIGN, "%s: the matrix-core kernel needs 8-byte aligned scales", fn);
+        return hip_status(mbq::launch_gemv_mfma_q45(P, W->N, W->K, xq, M, y, ldy, accumulate, s), fn);
     }
-    return fail(MBQ_EUNSUPPORTED, "%s: no kernel for M=%lld with format %d", fn, (long long)M, W->fmt);
+    // row form: passes of up to 8 tokens on the vector units
+    int64_t mp = M < 8 ? M : 8;
+    while (mp > 1 && !mbq::gemv_smallm_fits(W->fmt, mp, W->K)) mp--;
+    const uint8_t* xb = (const uint8_t*)xq;
+    for (int64_t m0 = 0; m0 < M; m0 += mp) {
+        const int64_t mm = M - m0 < mp ? M - m0 : mp;
+        const void* xm = xb + m0 * W->K * 4;
+        mbq::GemvGeom g1 = mbq::gemv_m1_default_geom(W->fmt, W->N, W->K);
+        hipError_t e = mm == 1 ? mbq::launch_gemv_m1(W->fmt, P, W->N, W->K, xm, true, y + m0 * ldy,
+                                                     accumulate, nullptr, 1, g1, s)
+                               : mbq::launch_gemv_smallm(W->fmt, P, W->N, W->K, xm, true, mm, W->K,
+                                                         y + m0 * ldy, ldy, accumulate, s);
+        if (e != hipSuccess) return hip_status(e, fn);
+    }
+    return ok();
 }
 
 static int check_norm(const float* x, const float* gamma, const float* beta, bool need_beta,

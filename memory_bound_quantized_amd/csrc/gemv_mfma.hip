@@ -1,0 +1,298 @@
+// gemv_mfma.hip -- Y[m][n] (+)= W[n] . X[m] for M >= 16 tokens of a Q45
+// matrix on the matrix cores (v_mfma_f32_16x16x32_f16).
+//
+// With 16 or more tokens the sums per weight byte pass what the vector units
+// sustain, so the contraction goes to the matrix units ([roofline-holds]
+// "The Math": above M* = (w/16)(R/BW) the sums, not the memory, are the wall;
+// "Two different problems").  Exactness is kept as in the vector kernels:
+//   * A (weights): a Q45 code q becomes the fp16 value q - 8 exactly (the
+//     bits 0x6400 | q are 1024 + q; subtracting 1032 is exact);
+//   * B (tokens): each token is scaled by a power of two 2^e (its largest |x|
+//     lands in [2^14, 2^15)) and split into fp16 hi + lo, 22 bits of x;
+//   * one MFMA covers exactly one 32-weight block, so the block's fp16 scale
+//     multiplies the fp32 block result in the epilogue: acc = fma(s, D, acc).
+//
+// Staged tile form ("xt", written by stage_x_mfma_kernel): for token tile tt
+// (16 tokens) and block b, 2 KB = [hi, lo] x 64 lanes x 8 halfs, lane
+// j + 16 g holding token 16 tt + j at k = 32 b + 8 g + {0,4,1,5,2,6,3,7} (the
+// order in which a lane unpacks the 8 codes of one dword); then one float per
+// token slot, 2^-e (0 for slots past M).
+//
+// Kernel geometry: 4 waves per workgroup, one 16-row tile per wave, all K.
+// The workgroup copies 8-block slabs of xt into LDS (double-buffered); each
+// wave streams its rows' codes as 16-byte loads (one block per lane, 4 blocks
+// per row per load), 8 loads ahead, and turns them into MFMA A operands
+// through a small per-wave LDS transpose.
+#include "device_common.h"
+#include "formats.h"
+#include "kernels.h"
+
+namespace mbq {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+typedef float f4v __attribute__((ext_vector_type(4)));
+// Native vector types for the register arrays (HIP's uint4 is a union-based
+// struct that keeps arrays of it out of registers here).
+typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+
+constexpr int kSB = 8;                  // blocks per xt slab
+constexpr int kGB = 4;                  // blocks per weight load (one per lane)
+constexpr int kPG = 8;                  // weight loads in flight per wave
+constexpr int kUS = kPG * kGB / kSB;    // slabs per unrolled loop body
+constexpr int kScrStride = 20;          // dwords per row of the transpose scratch
+
+__device__ __forceinline__ int64_t xt_tile_bytes(int64_t K) { return (K / 32) * 2048; }
+
+// ---- staging: one workgroup per token slot ------------------------------
+__global__ __launch_bounds__(kBlock) void stage_x_mfma_kernel(const float* __restrict__ x,
+                                                              int64_t ldx, int M, int K,
+                                                              uint8_t* __restrict__ xt,
+                                                              float* __restrict__ tscale) {
+    __shared__ float red[kWavesPerBlock];
+    const int m = blockIdx.x;                       // token slot
+    const int tt = m / 16, j = m % 16;
+    const int nb = K / 32;
+    const bool real = m < M;
+    const float* xr = x + (int64_t)(real ? m : 0) * ldx;
+    float amax = 0.f;
+    for (int k = 4 * (int)threadIdx.x; k < K; k += 4 * kBlock) {
+        const float4 v = *(const float4*)(xr + k);
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
+    if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    // 2^e puts the largest |x| into [2^14, 2^15); e within the normal range
+    int e = 141 - (int)((__builtin_bit_cast(uint32_t, amax) >> 23) & 0xFFu);
+    e = e > 126 ? 126 : (e < -126 ? -126 : e);
+    const float up = __builtin_bit_cast(float, (uint32_t)(e + 127) << 23);
+    if (threadIdx.x == 0) tscale[m] = real ? __builtin_bit_cast(float, (uint32_t)(127 - e) << 23) : 0.f;
+    // half slot of weight m8 = k % 8 within a lane's 8 values
+    constexpr int kSlot[8] = {0, 2, 4, 6, 1, 3, 5, 7};
+    _Float16* base = (_Float16*)(xt + (int64_t)tt * nb * 2048);
+    for (int k = 4 * (int)threadIdx.x; k < K; k += 4 * kBlock) {
+        float4 v = real ? *(const float4*)(xr + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float vv[4] = {v.x, v.y, v.z, v.w};
+        const int b = k / 32, g = (k % 32) / 8, lane = j + 16 * g;
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const float xs = vv[q] * up;
+            const _Float16 hi = (_Float16)xs;
+            const _Float16 lo = (_Float16)(xs - (float)hi);
+            const int slot = kSlot[(k + q) % 8];
+            _Float16* p = base + (int64_t)b * 1024 + lane * 8 + slot;
+            p[0] = hi;          // part 0
+            p[512] = lo;        // part 1 (1024 bytes on)
+        }
+    }
+}
+
+int64_t xt_bytes(int64_t M, int64_t K) {
+    const int64_t TT = (M + 15) / 16;
+    return TT * (K / 32) * 2048 + TT * 16 * 4;
+}
+
+hipError_t launch_stage_x_mfma(const float* x, int64_t M, int64_t ldx, int64_t K, void* xt,
+                               hipStream_t stream) {
+    const int64_t TT = (M + 15) / 16;
+    uint8_t* p = (uint8_t*)xt;
+    float* ts = (float*)(p + TT * (K / 32) * 2048);
+    hipLaunchKernelGGL(stage_x_mfma_kernel, dim3((unsigned)(TT * 16)), dim3(kBlock), 0, stream, x,
+                       ldx, (int)M, (int)K, p, ts);
+    return hipGetLastError();
+}
+
+// ---- the product ---------------------------------------------------------
+// Compile-time loop: f(IC<I>{}) for I = B .. E-1, so indices into register
+// arrays are constants (the ring slots stay in registers).
+template <int V>
+struct IC {
+    static constexpr int value = V;
+};
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(IC<B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// 8 codes of one dword as fp16 (q - 8), in the order {0,4,1,5,2,6,3,7}.
+__device__ __forceinline__ h8 codes_to_a(uint32_t a) {
+    const h2v off = {(_Float16)1032.0f, (_Float16)1032.0f};
+    h2v w[4];
+#pragma unroll
+    for (int s = 0; s < 4; s++)
+        w[s] = __builtin_bit_cast(h2v, ((a >> (4 * s)) & 0x000F000Fu) | 0x64006400u) - off;
+    return h8{w[0][0], w[0][1], w[1][0], w[1][1], w[2][0], w[2][1], w[3][0], w[3][1]};
+}
+
+// K % 1024 == 0 (nslab a multiple of kUS).  One workgroup per compute unit
+// at most (the grid is N / 64 workgroups and the LDS holds the slabs), so each
+// wave may use a whole SIMD's registers: prefetched codes and scales and the
+// next slab of xt all stay in registers.
+template <int TT>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemv_mfma_q45_kernel(DevPlanes P, int64_t N, int K,
+                                                               const u4v* __restrict__ xt,
+                                                               const float* __restrict__ tscale,
+                                                               int M, float* __restrict__ y,
+                                                               int64_t ldy, int accumulate) {
+    extern __shared__ u4v lds[];
+    constexpr int XSB = TT * kSB * 128;               // uint4 per slab buffer
+    constexpr int XPT = XSB / kBlock;                 // uint4 per thread per slab (TT * 4)
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int i = lane & 15, g = lane >> 4;
+    uint32_t* scr = (uint32_t*)(lds + 2 * XSB) + wave * 16 * kScrStride;
+    const int nb = K / 32, ngroups = nb / kGB, nslab = nb / kSB;
+    const int64_t row0 = ((int64_t)blockIdx.x * kWavesPerBlock + wave) * 16;
+
+    // A side: row i's codes, 16 bytes (one block) per lane per load
+    const int64_t ra = row0 + i < N ? row0 + i : N - 1;
+    const u4v* wq = (const u4v*)(P.p0 + ra * (K >> 1));
+    // D side: the scales of rows 4g + v, 4 blocks (8 bytes) per load
+    const u2v* sq[4];
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+        const int64_t rs = row0 + 4 * g + v < N ? row0 + 4 * g + v : N - 1;
+        sq[v] = (const u2v*)(P.p2 + rs * (K >> 5) * 2);
+    }
+    // xt slab s of this thread: tile q / 4, 256-uint4 part q % 4
+    auto xt_at = [&](int s, int q) {
+        return xt + (int64_t)(q / 4) * nb * 128 + (int64_t)s * kSB * 128 + (q % 4) * kBlock + tid;
+    };
+
+    u4v xr[XPT];
+#pragma unroll
+    for (int q = 0; q < XPT; q++) xr[q] = *xt_at(0, q);
+    u4v wr[kPG];
+    u2v sr[kPG][4];
+#pragma unroll
+    for (int t = 0; t < kPG; t++) {
+        const int tc = t < ngroups ? t : ngroups - 1;
+        wr[t] = wq[kGB * tc + g];
+#pragma unroll
+        for (int v = 0; v < 4; v++) sr[t][v] = sq[v][tc];
+    }
+#pragma unroll
+    for (int q = 0; q < XPT; q++) lds[q * kBlock + tid] = xr[q];
+    __syncthreads();
+
+    f4v acc[TT];
+#pragma unroll
+    for (int tt = 0; tt < TT; tt++) acc[tt] = f4v{0.f, 0.f, 0.f, 0.f};
+    const f4v zero = {0.f, 0.f, 0.f, 0.f};
+
+    for (int s0 = 0; s0 < nslab; s0 += kUS) {
+        static_for<0, kUS>([&](auto su_c) {
+            constexpr int su = decltype(su_c)::value;
+            const int s = s0 + su;
+            constexpr int buf = su & 1;
+            // next slab of xt (the last one reloads itself; it is not stored)
+            const int sn = s + 1 < nslab ? s + 1 : s;
+#pragma unroll
+            for (int q = 0; q < XPT; q++) xr[q] = *xt_at(sn, q);
+            static_for<0, kSB / kGB>([&](auto tg_c) {
+                constexpr int tg = decltype(tg_c)::value;
+                constexpr int tl = su * (kSB / kGB) + tg;        // ring slot
+                const int t = s * (kSB / kGB) + tg;              // weight group
+                // transpose: lane (i, g) holds block 4t + g of row i; each
+                // MFMA needs dword g of one block from every lane of row i
+                *(u4v*)(scr + i * kScrStride + 4 * g) = wr[tl];
+                u2v sc[4];
+#pragma unroll
+                for (int v = 0; v < 4; v++) sc[v] = sr[tl][v];
+                const int tn = t + kPG < ngroups ? t + kPG : ngroups - 1;
+                wr[tl] = wq[kGB * tn + g];
+#pragma unroll
+                for (int v = 0; v < 4; v++) sr[tl][v] = sq[v][tn];
+#pragma unroll
+                for (int b4 = 0; b4 < kGB; b4++) {
+                    const h8 a = codes_to_a(scr[i * kScrStride + 4 * b4 + g]);
+                    float sv[4];
+#pragma unroll
+                    for (int v = 0; v < 4; v++)
+                        sv[v] = h2f((b4 < 2 ? sc[v].x : sc[v].y) >> (16 * (b4 & 1)));
+                    const int lb = tg * kGB + b4;                // block within the slab
+#pragma unroll
+                    for (int tt = 0; tt < TT; tt++) {
+                        const u4v* bp = lds + buf * XSB + (tt * kSB + lb) * 128;
+                        const h8 bh = __builtin_bit_cast(h8, bp[lane]);
+                        const h8 bl = __builtin_bit_cast(h8, bp[64 + lane]);
+                        f4v d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bh, zero, 0, 0, 0);
+                        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bl, d, 0, 0, 0);
+#pragma unroll
+                        for (int v = 0; v < 4; v++) acc[tt][v] = fmaf(sv[v], d[v], acc[tt][v]);
+                    }
+                }
+            });
+#pragma unroll
+            for (int q = 0; q < XPT; q++) lds[(buf ^ 1) * XSB + q * kBlock + tid] = xr[q];
+            __syncthreads();
+        });
+    }
+
+    // lane j + 16 g holds rows 4g + v of token column j
+    const int j = lane & 15;
+#pragma unroll
+    for (int tt = 0; tt < TT; tt++) {
+        const int m = 16 * tt + j;
+        if (m >= M) continue;
+        const float ts = tscale[m];
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+            const int64_t n = row0 + 4 * g + v;
+            if (n < N) {
+                float* dst = y + (int64_t)m * ldy + n;
+                const float val = acc[tt][v] * ts;
+                *dst = accumulate ? *dst + val : val;
+            }
+        }
+    }
+}
+
+template <int TT>
+static hipError_t launch_mfma_tt(DevPlanes P, int64_t N, int64_t K, const u4v* xt,
+                                 const float* ts, int M, float* y, int64_t ldy, int accumulate,
+                                 hipStream_t stream) {
+    const size_t lds = (size_t)2 * TT * kSB * 128 * 16 + (size_t)kWavesPerBlock * 16 * kScrStride * 4;
+    auto kern = gemv_mfma_q45_kernel<TT>;
+    if (lds > 65536) {
+        hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    const int64_t grid = (N + 63) / 64;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBlock), lds, stream, P, N, (int)K, xt, ts,
+                       M, y, ldy, accumulate);
+    return hipGetLastError();
+}
+
+// Tokens in groups of 64 (four tiles) per launch.
+hipError_t launch_gemv_mfma_q45(DevPlanes P, int64_t N, int64_t K, const void* xt, int64_t M,
+                                float* y, int64_t ldy, int accumulate, hipStream_t stream) {
+    const int64_t TT = (M + 15) / 16;
+    const uint8_t* base = (const uint8_t*)xt;
+    const float* ts = (const float*)(base + TT * (K / 32) * 2048);
+    for (int64_t m0 = 0; m0 < M; m0 += 64) {
+        const int mg = (int)(M - m0 < 64 ? M - m0 : 64);
+        const u4v* xg = (const u4v*)(base + (m0 / 16) * (K / 32) * 2048);
+        hipError_t e;
+        switch ((mg + 15) / 16) {
+        case 1: e = launch_mfma_tt<1>(P, N, K, xg, ts + m0, mg, y + m0 * ldy, ldy, accumulate, stream); break;
+        case 2: e = launch_mfma_tt<2>(P, N, K, xg, ts + m0, mg, y + m0 * ldy, ldy, accumulate, stream); break;
+        case 3: e = launch_mfma_tt<3>(P, N, K, xg, ts + m0, mg, y + m0 * ldy, ldy, accumulate, stream); break;
+        default: e = launch_mfma_tt<4>(P, N, K, xg, ts + m0, mg, y + m0 * ldy, ldy, accumulate, stream); break;
+        }
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace mbq

@@ -67,10 +67,14 @@ hipError_t launch_gemv_smallm(int fmt, DevPlanes P, int64_t N, int64_t K, const 
                               bool x_staged, int64_t M, int64_t ldx, float* y, int64_t ldy,
                               int accumulate, hipStream_t stream);
 
-// Y[m][n] (+)= W[n] . X[m] for 16 <= M <= 64, Q45 only (matrix cores).
-hipError_t launch_gemv_mfma_q45(DevPlanes P, int64_t N, int64_t K, const float* x, int64_t M,
-                                int64_t ldx, float* y, int64_t ldy, int accumulate,
-                                hipStream_t stream);
+// Matrix-core product for Q45 and M >= 16 tokens (gemv_mfma.hip).  X comes in
+// the staged tile form: xt_bytes(M, K) bytes written by launch_stage_x_mfma.
+// K % 1024 == 0; plane 2 8-byte aligned.
+int64_t xt_bytes(int64_t M, int64_t K);
+hipError_t launch_stage_x_mfma(const float* x, int64_t M, int64_t ldx, int64_t K, void* xt,
+                               hipStream_t stream);
+hipError_t launch_gemv_mfma_q45(DevPlanes P, int64_t N, int64_t K, const void* xt, int64_t M,
+                                float* y, int64_t ldy, int accumulate, hipStream_t stream);
 
 // y[m][n] = 0 for the K == 0 case (rows of length ldy, first N entries).
 hipError_t launch_fill_zero(float* y, int64_t M, int64_t N, int64_t ldy, hipStream_t stream);

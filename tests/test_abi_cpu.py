@@ -140,10 +140,7 @@ def test_gemv_argument_checks():
     assert _gemv(_desc(fmt=3, K=96)) == _lib.EUNSUPPORTED       # Q25 kernels need K % 64
     assert _gemv(_desc(fmt=0, K=12)) == _lib.EUNSUPPORTED       # BF16 kernels need K % 8
     assert _gemv(_desc(K=65536)) == _lib.EUNSUPPORTED           # beyond the LDS-staged K
-    assert _gemv(_desc(), M=9, ldx=256, ldy=64) == _lib.EUNSUPPORTED
-    assert _gemv(_desc(), M=65, ldx=256, ldy=64) == _lib.EUNSUPPORTED
-    assert _gemv(_desc(K=32768), M=8, ldx=32768, ldy=64) == _lib.EUNSUPPORTED   # LDS capacity
-    assert _gemv(_desc(fmt=2), M=16, ldx=256, ldy=64) == _lib.EUNSUPPORTED
+    assert _gemv(_desc(), M=9, ldx=256, ldy=63) == _lib.EINVAL      # ldy < N
     assert L.mbq_last_error()
 
 
@@ -187,6 +184,10 @@ def test_staged_x_argument_checks():
     assert L.mbq_xq_bytes(3, 1, 96, ctypes.byref(sz)) == _lib.EINVAL       # Q25 chunk is 64
     assert L.mbq_xq_bytes(1, 1, 48, ctypes.byref(sz)) == _lib.EINVAL
     assert L.mbq_xq_bytes(9, 1, 64, ctypes.byref(sz)) == _lib.EINVAL
+    # Q45 with 16 or more tokens: the matrix-core tile form (2 KB per 16 tokens
+    # and 32 values, plus one float per token slot)
+    assert L.mbq_xq_bytes(1, 17, 4096, ctypes.byref(sz)) == _lib.OK and sz.value == 2 * (128 * 2048 + 64)
+    assert L.mbq_xq_bytes(2, 17, 4096, ctypes.byref(sz)) == _lib.OK and sz.value == 17 * 4096 * 4
     x, xq = BASE, BASE + 0x100000
     st = lambda fmt=1, x=x, M=1, ldx=4096, K=4096, xq=xq: L.mbq_stage_x(fmt, x, M, ldx, K, xq, None)
     assert st(K=4016) == _lib.EINVAL
@@ -197,6 +198,7 @@ def test_staged_x_argument_checks():
     assert st(xq=xq + 8) == _lib.EALIGN
     assert st(xq=x + 4096) == _lib.EINVAL                                   # overlap
     assert st(K=65536, ldx=65536) == _lib.EUNSUPPORTED
+    assert st(M=16, K=2080, ldx=2080) == _lib.EUNSUPPORTED                  # tile form needs K % 1024
     gx = lambda d, xq=xq, M=1, y=BASE + 0x800000, acc=0: \
         L.mbq_gemv_xq(ctypes.byref(d), xq, M, y, d.N, acc, None)
     assert gx(_desc(), xq=None) == _lib.EINVAL
@@ -205,6 +207,10 @@ def test_staged_x_argument_checks():
     assert gx(_desc(), acc=3) == _lib.EINVAL
     assert gx(_desc(), M=0) == _lib.OK
     assert gx(_desc(fmt=3, K=96)) == _lib.EUNSUPPORTED
+    assert gx(_desc(K=2080), M=16) == _lib.EUNSUPPORTED                     # matrix cores: K % 1024
+    d = _desc(K=4096)
+    d.scales = BASE + 0x200004
+    assert gx(d, M=16) == _lib.EALIGN                                       # 8-byte aligned scales
     r = lambda n=4096, y=BASE + 0x200000, fmt=1, xq=xq, x=x, eps=1e-6: \
         L.mbq_rmsnorm_xq(x, BASE + 0x300000, eps, n, y, fmt, xq, None)
     assert r(n=-1) == _lib.EINVAL

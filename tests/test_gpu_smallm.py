@@ -83,3 +83,46 @@ def test_workload4_full_size_small_batches():
         Y = mbq().gemv_q(dw, dev(cfg["X"])).cpu().numpy()
         ref = oracle.gemv_parallel(ow, cfg["X"])
         check_gemv(Y, ow, cfg["X"], ref)
+
+
+# --------------------------------------------------------------------------
+# M >= 16: Q45 on the matrix cores (tile-staged X), and fp32 X in passes of 8
+# --------------------------------------------------------------------------
+
+MFMA_CASES = [(16, 64, 4096), (17, 1000, 4096), (31, 130, 1024), (48, 64, 2048),
+              (64, 12288, 4096), (80, 300, 4096), (16, 4096, 12288)]
+
+
+@pytest.mark.parametrize("M,N,K", MFMA_CASES)
+def test_mfma_matches_oracle(M, N, K):
+    print("mfma M=%d N=%d K=%d" % (M, N, K), flush=True)
+    planes = workloads.weight_planes(np.random.default_rng(9500 + M + N), 1, N, K)
+    ow, dw = oracle.Planes(1, N, K, planes), mbq().QWeight.from_host(1, N, K, planes)
+    X = np.random.default_rng(M + K).normal(size=(M, K)).astype(np.float32)
+    Xd = dev(X)
+    Xt = mbq().stage_x(1, Xd)
+    assert Xt.numel() * 4 == mbq().xq_bytes(1, M, K)
+    Y = mbq().gemv_xq(dw, Xt, M=M).cpu().numpy()
+    ref = oracle.gemv_parallel(ow, X) if N * K > 1 << 24 else oracle.gemv(ow, X)
+    check_gemv(Y, ow, X, ref)
+    # fp32 X runs passes of 8 tokens on the vector units: same bar
+    Yv = mbq().gemv_q(dw, Xd).cpu().numpy()
+    check_gemv(Yv, ow, X, ref)
+
+
+def test_mfma_token_scales_and_accumulate():
+    """Tokens of very different magnitudes (each has its own power-of-two
+    scale), an all-zero token, and the accumulate epilogue."""
+    M, N, K = 20, 256, 4096
+    planes = workloads.weight_planes(np.random.default_rng(9600), 1, N, K)
+    ow, dw = oracle.Planes(1, N, K, planes), mbq().QWeight.from_host(1, N, K, planes)
+    rng = np.random.default_rng(7)
+    X = rng.normal(size=(M, K)).astype(np.float32)
+    X[3] *= np.float32(1e25)
+    X[4] *= np.float32(1e-25)
+    X[5] = 0.0
+    X[6, ::7] *= np.float32(2.0 ** 30)
+    Y0 = rng.normal(size=(M, N)).astype(np.float32)
+    Yd = dev(Y0)
+    mbq().gemv_xq(dw, mbq().stage_x(1, dev(X)), M=M, out=Yd, accumulate=True)
+    check_gemv(Yd.cpu().numpy(), ow, X, oracle.gemv(ow, X, y0=Y0), y0=Y0)
