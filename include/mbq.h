@@ -225,6 +225,30 @@ int mbq_decode_workspace_bytes(const mbq_decode_model* model, size_t* bytes);
 int mbq_decode_step(const mbq_decode_model* model, float* h, float* logits, void* workspace,
                     size_t workspace_bytes, void* stream);
 
+/* The same token in ONE launch ([one-serial-kernel] "The kernel that was never
+ * built": the token's pieces of work without a return to the host between
+ * them; [roofline-holds] "Where the time goes": the per-kernel toll).  Every
+ * workgroup stays resident (cooperative launch); the four steps of a layer
+ * are separated by grid-wide barriers, and each wave issues the loads of its
+ * next table's weights before it waits at the barrier, so the weight stream
+ * does not stop between tables.  Same arithmetic and the same results within
+ * tolerance as mbq_decode_step (the norm is computed inside every workgroup).
+ *
+ * mbq_decode_prepare writes the device table of the layers into the
+ * workspace (a copy and a stream synchronisation; call it once per model and
+ * again whenever a descriptor changes).  mbq_decode_step_persistent checks
+ * that the workspace holds the table of this model (by an identity of its
+ * pointers) and does nothing but set the status word otherwise.
+ * Needs d = dq = 4096, f = 12288, Q45 qkv / o / gate_up, Q45 or Q65 down
+ * and lm_head, an even dq + 2 dkv and an even vocab (MBQ_EUNSUPPORTED).
+ * After the step the 32-bit word at byte 4 of the workspace is 0 on success,
+ * bit 0 set if a barrier wait gave up (every wave still ends), bit 1 set if
+ * the table did not match.  Not for graph capture (cooperative launch). */
+int mbq_decode_prepare(const mbq_decode_model* model, void* workspace, size_t workspace_bytes,
+                       void* stream);
+int mbq_decode_step_persistent(const mbq_decode_model* model, float* h, float* logits,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------ staged x
  * The quantized products consume x in a "staged" form: per chunk of 32
  * values (64 for Q25) a power-of-two scale 2^-e and the 24-bit integers

@@ -23,7 +23,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmbq.so")
 ARCH = "gfx950"
 
-SOURCES = ["abi.cpp", "gemv_m1.hip", "gemv_smallm.hip", "gemv_mfma.hip", "stage.hip", "norms.hip",
+SOURCES = ["abi.cpp", "gemv_m1.hip", "gemv_smallm.hip", "gemv_mfma.hip", "stage.hip", "decode_persistent.hip",
+           "norms.hip",
            "exports.hip"]
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH, "-Wall", "-Wno-unused-function",

@@ -8,6 +8,8 @@
 #include <cstdlib>
 #include <cstring>
 #include <string>
+#include <vector>
+#include <cstddef>
 
 #include "../../include/mbq.h"
 #include "kernels.h"
@@ -61,6 +63,7 @@ int check_weight(const mbq_qweight* W, const char* fn) {
     if (!fmt_valid(W->fmt)) return fail(MBQ_EINVAL, "%s: unknown format %d", fn, W->fmt);
     if (W->reserved != 0) return fail(MBQ_EINVAL, "%s: W->reserved must be 0", fn);
     if (W->N < 0 || W->K < 0) return fail(MBQ_EINVAL, "%s: negative shape", fn);
+    if (W->N > 0x7FFFFFFF) return fail(MBQ_EUNSUPPORTED, "%s: N >= 2^31", fn);
     if (W->K % block_len(W->fmt))
         return fail(MBQ_EINVAL, "%s: K=%lld is not a multiple of the block length %lld", fn,
                     (long long)W->K, (long long)block_len(W->fmt));
@@ -92,6 +95,10 @@ int check_kernel_shape(const mbq_qweight* W, const char* fn) {
         return fail(MBQ_EUNSUPPORTED, "%s: Q25 kernels need K %% 64 == 0", fn);
     if (W->fmt == MBQ_FMT_BF16 && W->K % 8)
         return fail(MBQ_EUNSUPPORTED, "%s: BF16 kernels need K %% 8 == 0", fn);
+    size_t sz[4];
+    mbq_plane_sizes(W->fmt, W->N, W->K, sz);
+    for (int p = 0; p < 4; p++)
+        if (sz[p] > 0xFFFFFFFFull) return fail(MBQ_EUNSUPPORTED, "%s: a plane of 4 GiB or more", fn);
     return MBQ_OK;
 }
 
@@ -113,14 +120,24 @@ mbq::DevPlanes planes_of(const mbq_qweight* W) {
                           (const uint8_t*)W->scales, (const uint8_t*)W->super_scales};
 }
 
-// Optional override of the rows per wave for tuning sweeps: MBQ_GEMV_ROWS=1,
-// 2 or 4, read at every call.
+// Optional geometry overrides for tuning sweeps, read at every call:
+// MBQ_GEMV_ROWS = 1, 2 or 4 rows per wave; MBQ_GEMV_GROUPS = row groups per
+// wave.
 bool geom_override(mbq::GemvGeom* g) {
+    bool any = false;
     const char* s = getenv("MBQ_GEMV_ROWS");
     int r = 0;
-    if (!s || sscanf(s, "%d", &r) != 1 || !(r == 1 || r == 2 || r == 4)) return false;
-    g->rows_per_wave = r;
-    return true;
+    if (s && sscanf(s, "%d", &r) == 1 && (r == 1 || r == 2 || r == 4)) {
+        g->rows_per_wave = r;
+        any = true;
+    }
+    const char* t = getenv("MBQ_GEMV_GROUPS");
+    int gg = 0;
+    if (t && sscanf(t, "%d", &gg) == 1 && gg >= 1 && gg <= 64) {
+        g->groups = gg;
+        any = true;
+    }
+    return any;
 }
 
 // ------------------------------------------------------------ host packer
@@ -321,7 +338,7 @@ int mbq_gemv_q_gather(const mbq_qweight* W_all, int64_t rows_per_expert, const i
     mbq::GemvGeom g = mbq::gemv_m1_default_geom(W_all->fmt, n_out, W_all->K);
     geom_override(&g);
     return hip_status(mbq::launch_gemv_m1(W_all->fmt, planes_of(W_all), n_out, W_all->K, x, false,
-                                          y, 0, idx, rows_per_expert, g, s), fn);
+                                          y, 0, idx, rows_per_expert, g, s, W_all->N), fn);
 }
 
 int mbq_gemv_fused(const mbq_qweight* W, const float* x, const float* gamma, float eps,
@@ -346,7 +363,7 @@ int mbq_gemv_fused(const mbq_qweight* W, const float* x, const float* gamma, flo
     if ((rc = check_planes(W, fn))) return rc;
     if ((rc = check_kernel_shape(W, fn))) return rc;
     hipStream_t s = (hipStream_t)stream;
-    mbq::GemvGeom g = mbq::gemv_m1_default_geom(W->fmt, W->N, W->K);
+    mbq::GemvGeom g = mbq::gemv_m1_default_geom(W->fmt, W->N, W->K, silu);
     geom_override(&g);
     if (!gamma && !silu)
         return hip_status(mbq::launch_gemv_m1(W->fmt, planes_of(W), W->N, W->K, x, false, y,
@@ -397,21 +414,35 @@ static int check_decode(const mbq_decode_model* m, const char* fn) {
     return MBQ_OK;
 }
 
+// Workspace of the decode step: [0, 256) barrier counter and status word;
+// then q|k|v, the gated activations, and the layer table of the one-launch
+// step.
+struct DecodeLayout {
+    size_t qkv, m, table, total;
+};
+
+static DecodeLayout decode_layout(const mbq_decode_model* m) {
+    DecodeLayout L;
+    L.qkv = 256;
+    L.m = L.qkv + align256((size_t)(m->dq + 2 * m->dkv) * 4);
+    L.table = L.m + align256((size_t)m->f * 4);
+    L.total = L.table + align256(offsetof(mbq::DecTable, layers) +
+                                 (size_t)(m->n_layers > 0 ? m->n_layers : 1) * sizeof(mbq::DecLayer));
+    return L;
+}
+
 int mbq_decode_workspace_bytes(const mbq_decode_model* m, size_t* bytes) {
     const char* fn = "mbq_decode_workspace_bytes";
     if (!m || !bytes) return fail(MBQ_EINVAL, "%s: NULL pointer", fn);
-    if (m->dq < 0 || m->dkv < 0 || m->f < 0) return fail(MBQ_EINVAL, "%s: bad dimensions", fn);
-    *bytes = align256((size_t)(m->dq + 2 * m->dkv) * 4) + align256((size_t)m->f * 4);
+    if (m->n_layers < 0 || m->dq < 0 || m->dkv < 0 || m->f < 0)
+        return fail(MBQ_EINVAL, "%s: bad dimensions", fn);
+    *bytes = decode_layout(m).total;
     return ok();
 }
 
-int mbq_decode_step(const mbq_decode_model* m, float* h, float* logits, void* workspace,
-                    size_t workspace_bytes, void* stream) {
-    const char* fn = "mbq_decode_step";
-    int rc = check_decode(m, fn);
-    if (rc) return rc;
-    size_t need = 0;
-    mbq_decode_workspace_bytes(m, &need);
+static int check_workspace(const mbq_decode_model* m, const float* h, const float* logits,
+                           const void* workspace, size_t workspace_bytes, const char* fn) {
+    const size_t need = decode_layout(m).total;
     if (!h || !aligned(h, 16)) return fail(MBQ_EALIGN, "%s: h must be 16-byte aligned", fn);
     if (m->vocab > 0 && (!logits || !aligned(logits, 4))) return fail(MBQ_EINVAL, "%s: bad logits", fn);
     if (!workspace || !aligned(workspace, 256) || workspace_bytes < need)
@@ -420,11 +451,21 @@ int mbq_decode_step(const mbq_decode_model* m, float* h, float* logits, void* wo
     if (overlaps(h, hb, workspace, need) || (m->vocab > 0 && (overlaps(logits, (size_t)m->vocab * 4, h, hb) ||
                                                                overlaps(logits, (size_t)m->vocab * 4, workspace, need))))
         return fail(MBQ_EINVAL, "%s: h, logits and workspace must not overlap", fn);
+    return MBQ_OK;
+}
+
+int mbq_decode_step(const mbq_decode_model* m, float* h, float* logits, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    const char* fn = "mbq_decode_step";
+    int rc = check_decode(m, fn);
+    if (rc) return rc;
+    if ((rc = check_workspace(m, h, logits, workspace, workspace_bytes, fn))) return rc;
+    const DecodeLayout lay = decode_layout(m);
     hipStream_t s = (hipStream_t)stream;
-    float* qkv = (float*)workspace;
-    float* mm = (float*)((char*)workspace + align256((size_t)(m->dq + 2 * m->dkv) * 4));
-    auto geom = [](const mbq_qweight& W) {
-        mbq::GemvGeom g = mbq::gemv_m1_default_geom(W.fmt, W.N, W.K);
+    float* qkv = (float*)((char*)workspace + lay.qkv);
+    float* mm = (float*)((char*)workspace + lay.m);
+    auto geom = [](const mbq_qweight& W, bool pairs = false) {
+        mbq::GemvGeom g = mbq::gemv_m1_default_geom(W.fmt, W.N, W.K, pairs);
         geom_override(&g);
         return g;
     };
@@ -442,7 +483,7 @@ int mbq_decode_step(const mbq_decode_model* m, float* h, float* logits, void* wo
         if (e == hipSuccess)
             e = mbq::launch_gemv_fused(L.gate_up.fmt, planes_of(&L.gate_up), L.gate_up.N,
                                        L.gate_up.K, h, L.gamma2, m->eps, true, mm, 0,
-                                       geom(L.gate_up), s);
+                                       geom(L.gate_up, true), s);
         // h += Wd m
         if (e == hipSuccess)
             e = mbq::launch_gemv_m1(L.down.fmt, planes_of(&L.down), L.down.N, L.down.K, mm, false,
@@ -453,6 +494,96 @@ int mbq_decode_step(const mbq_decode_model* m, float* h, float* logits, void* wo
         e = mbq::launch_gemv_fused(m->lm_head.fmt, planes_of(&m->lm_head), m->vocab, m->d, h,
                                    m->gamma_f, m->eps, false, logits, 0, geom(m->lm_head), s);
     return hip_status(e, fn);
+}
+
+// Identity of a model's device pointers (FNV-1a over every plane and gamma).
+static uint64_t decode_tag(const mbq_decode_model* m) {
+    uint64_t hsh = 1469598103934665603ull;
+    auto mix = [&](const void* p) {
+        uint64_t v = (uint64_t)(uintptr_t)p;
+        for (int b = 0; b < 8; b++) {
+            hsh ^= (v >> (8 * b)) & 0xFF;
+            hsh *= 1099511628211ull;
+        }
+    };
+    auto mixw = [&](const mbq_qweight& W) {
+        mix(W.codes); mix(W.codes_hi); mix(W.scales); mix(W.super_scales);
+    };
+    for (int l = 0; l < m->n_layers; l++) {
+        const mbq_decode_layer& L = m->layers[l];
+        mixw(L.qkv); mixw(L.o); mixw(L.gate_up); mixw(L.down);
+        mix(L.gamma1); mix(L.gamma2);
+    }
+    mix((const void*)(uintptr_t)m->n_layers);
+    return hsh;
+}
+
+int mbq_decode_prepare(const mbq_decode_model* m, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+    const char* fn = "mbq_decode_prepare";
+    int rc = check_decode(m, fn);
+    if (rc) return rc;
+    const DecodeLayout lay = decode_layout(m);
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < lay.total)
+        return fail(MBQ_EINVAL, "%s: workspace must be 256-byte aligned and >= %zu bytes", fn, lay.total);
+    std::vector<uint8_t> host(lay.total - lay.table, 0);
+    mbq::DecTable* t = (mbq::DecTable*)host.data();
+    t->magic = mbq::kDecMagic;
+    t->n_layers = m->n_layers;
+    t->tag = decode_tag(m);
+    for (int l = 0; l < m->n_layers; l++) {
+        const mbq_decode_layer& L = m->layers[l];
+        mbq::DecLayer& D = t->layers[l];
+        D.qkv = planes_of(&L.qkv);
+        D.o = planes_of(&L.o);
+        D.gu = planes_of(&L.gate_up);
+        D.dn = planes_of(&L.down);
+        D.g1 = L.gamma1;
+        D.g2 = L.gamma2;
+        D.fmt_dn = L.down.fmt;
+    }
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hipMemcpyAsync((char*)workspace + lay.table, host.data(), host.size(),
+                                  hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    return hip_status(e, fn);
+}
+
+int mbq_decode_step_persistent(const mbq_decode_model* m, float* h, float* logits, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    const char* fn = "mbq_decode_step_persistent";
+    int rc = check_decode(m, fn);
+    if (rc) return rc;
+    if ((rc = check_workspace(m, h, logits, workspace, workspace_bytes, fn))) return rc;
+    if (m->d != 4096 || m->dq != 4096 || m->f != 12288 || (m->dq + 2 * m->dkv) % 2 || m->vocab % 2)
+        return fail(MBQ_EUNSUPPORTED, "%s: the one-launch step needs d = dq = 4096, f = 12288 and even row counts", fn);
+    for (int l = 0; l < m->n_layers; l++) {
+        const mbq_decode_layer& L = m->layers[l];
+        if (L.qkv.fmt != MBQ_FMT_Q45 || L.o.fmt != MBQ_FMT_Q45 || L.gate_up.fmt != MBQ_FMT_Q45 ||
+            (L.down.fmt != MBQ_FMT_Q45 && L.down.fmt != MBQ_FMT_Q65))
+            return fail(MBQ_EUNSUPPORTED, "%s: layer %d: qkv, o, gate_up must be Q45 and down Q45 or Q65", fn, l);
+    }
+    if (m->vocab > 0 && m->lm_head.fmt != MBQ_FMT_Q45 && m->lm_head.fmt != MBQ_FMT_Q65)
+        return fail(MBQ_EUNSUPPORTED, "%s: lm_head must be Q45 or Q65", fn);
+    const DecodeLayout lay = decode_layout(m);
+    char* ws = (char*)workspace;
+    mbq::DecTable expect;
+    memset(&expect, 0, sizeof expect);
+    expect.magic = mbq::kDecMagic;
+    expect.n_layers = m->n_layers;
+    expect.tag = decode_tag(m);
+    mbq::DecHead head;
+    memset(&head, 0, sizeof head);
+    if (m->vocab > 0) {
+        head.lm = planes_of(&m->lm_head);
+        head.fmt_lm = m->lm_head.fmt;
+    }
+    head.gf = m->gamma_f;
+    return hip_status(mbq::launch_decode_persistent(
+                          (const mbq::DecTable*)(ws + lay.table), expect, head, m->eps, h, logits,
+                          m->vocab, m->dq + 2 * m->dkv, (float*)(ws + lay.qkv), (float*)(ws + lay.m),
+                          (uint32_t*)ws, (uint32_t*)(ws + 4), (hipStream_t)stream),
+                      fn);
 }
 
 int mbq_xq_bytes(int fmt, int64_t M, int64_t K, size_t* bytes) {

@@ -77,12 +77,15 @@ __device__ __forceinline__ float group_sum(float v) {
 
 // Sum over the 256 threads of a workgroup through LDS (red holds 4 floats).
 // Every thread receives the total.  Contains two barriers.
+template <int NW = kWavesPerBlock>
 __device__ __forceinline__ float block_sum(float v, float* red) {
     v = wave_sum(v);
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     if (lane == 0) red[wave] = v;
     __syncthreads();
-    float t = red[0] + red[1] + red[2] + red[3];
+    float t = red[0];
+#pragma unroll
+    for (int w = 1; w < NW; w++) t += red[w];
     __syncthreads();
     return t;
 }

@@ -22,7 +22,7 @@ __global__ __launch_bounds__(kBlock) void dequant_kernel(DevPlanes P, int64_t N,
     if (t >= N * nchunks) return;
     const int64_t row = t / nchunks, b = t - row * nchunks;
     typename T::Row r;
-    T::load(r, T::base(P, row, K), (int)b);
+    T::template load<false>(r, T::planes(P, N, K), T::row_off(row, K), (int)b);
     float v[T::WPC];
     T::weights(r, v);
     float4* o = (float4*)(w + row * K + b * T::WPC);
@@ -40,7 +40,7 @@ __global__ __launch_bounds__(kBlock) void codes_kernel(DevPlanes P, int64_t N, i
     if (t >= N * nchunks) return;
     const int64_t row = t / nchunks, b = t - row * nchunks;
     typename T::Row r;
-    T::load(r, T::base(P, row, K), (int)b);
+    T::template load<false>(r, T::planes(P, N, K), T::row_off(row, K), (int)b);
     int q[T::WPC];
     T::codes(r, q);
     uint8_t* o = out + row * K + b * T::WPC;

@@ -53,6 +53,64 @@ __device__ __forceinline__ float acc_value(const Acc3& s) {
     return fmaf((float)s.a2, 65536.f, (float)lo);
 }
 
+// Load from device memory through a global (address space 1) pointer, so the
+// access is a global load even where the plane pointer came from memory (a
+// generic pointer would be a flat load).
+typedef uint32_t gu4 __attribute__((ext_vector_type(4)));
+typedef uint32_t gu2 __attribute__((ext_vector_type(2)));
+typedef const uint8_t __attribute__((address_space(1)))* gbyte;
+// base (uniform) + off (per lane, 32-bit): the form of a scalar-base global load
+template <class V>
+__device__ __forceinline__ V gload(const uint8_t* base, uint32_t off) {
+    const gbyte p = (gbyte)base + off;
+    if constexpr (sizeof(V) == 16) {
+        return __builtin_bit_cast(V, *(const __attribute__((address_space(1))) gu4*)p);
+    } else if constexpr (sizeof(V) == 8) {
+        return __builtin_bit_cast(V, *(const __attribute__((address_space(1))) gu2*)p);
+    } else {
+        return *(const __attribute__((address_space(1))) V*)p;
+    }
+}
+template <class V>
+__device__ __forceinline__ V gload(const uint8_t* p) {
+    return gload<V>(p, 0u);
+}
+
+// ---- buffer loads ----------------------------------------------------------
+// Weight planes are read through buffer resources: a scalar descriptor per
+// plane, the row's byte offset in a scalar register and the lane's 32-bit
+// offset in a vector register.  No 64-bit per-lane address is ever formed.
+// Every plane must be smaller than 4 GiB.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+struct BufPlanes {
+    Rsrc p0, p1, p2, p3;
+};
+// Byte offset of one row in each plane.
+struct RowOff {
+    uint32_t o0, o1, o2, o3;
+};
+__device__ __forceinline__ Rsrc make_rsrc(const uint8_t* p, uint64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0,
+                                             (int)(bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : bytes),
+                                             0x00020000);
+}
+// UNI: soff is the same in every lane (scalar offset); otherwise it is added
+// to the lane's offset.
+template <class V, bool UNI>
+__device__ __forceinline__ V bload(Rsrc r, uint32_t voff, uint32_t soff) {
+    const uint32_t vo = UNI ? voff : voff + soff;
+    const uint32_t so = UNI ? soff : 0u;
+    if constexpr (sizeof(V) == 16) {
+        return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(r, vo, so, 0));
+    } else if constexpr (sizeof(V) == 8) {
+        return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b64(r, vo, so, 0));
+    } else if constexpr (sizeof(V) == 4) {
+        return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b32(r, vo, so, 0));
+    } else {
+        return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b16(r, vo, so, 0));
+    }
+}
+
 template <int FMT>
 struct Traits;
 
@@ -77,13 +135,20 @@ struct Traits<kQ45> {
         uint4 c;
         uint32_t s;
     };
-    // Start of one row in each plane the format uses.
-    __device__ static __forceinline__ DevPlanes base(const DevPlanes& P, int64_t row, int64_t K) {
-        return DevPlanes{P.p0 + row * (K >> 1), nullptr, P.p2 + 2 * row * (K >> 5), nullptr};
+    // Resources of the planes the format uses, for an N x K matrix.
+    __device__ static __forceinline__ BufPlanes planes(const DevPlanes& P, int64_t N, int64_t K) {
+        const uint64_t nk = (uint64_t)N * (uint64_t)K;
+        return BufPlanes{make_rsrc(P.p0, nk / 2), make_rsrc(P.p0, 0), make_rsrc(P.p2, nk / 16),
+                         make_rsrc(P.p0, 0)};
     }
-    __device__ static __forceinline__ void load(Row& r, const DevPlanes& B, int b) {
-        r.c = *(const uint4*)(B.p0 + 16 * b);
-        r.s = *(const uint16_t*)(B.p2 + 2 * b);
+    // Start of one row in each plane.
+    __device__ static __forceinline__ RowOff row_off(int64_t row, int64_t K) {
+        return RowOff{(uint32_t)(row * (K >> 1)), 0u, (uint32_t)(row * (K >> 4)), 0u};
+    }
+    template <bool UNI = true>
+    __device__ static __forceinline__ void load(Row& r, const BufPlanes& B, const RowOff& o, int b) {
+        r.c = bload<uint4, UNI>(B.p0, 16u * (uint32_t)b, o.o0);
+        r.s = bload<uint16_t, UNI>(B.p2, 2u * (uint32_t)b, o.o2);
     }
     // code vectors of dword d: even weights, odd weights
     __device__ static __forceinline__ void vectors(uint32_t d, uint32_t& ev, uint32_t& od) {
@@ -158,15 +223,21 @@ struct Traits<kQ65> {
         uint32_t sc;   // two int8 sub-scales (low byte: first 16 weights)
         uint32_t d;    // fp16 super-scale of the chunk's 256-weight block
     };
-    __device__ static __forceinline__ DevPlanes base(const DevPlanes& P, int64_t row, int64_t K) {
-        return DevPlanes{P.p0 + row * (K >> 1), P.p1 + row * (K >> 2), P.p2 + row * (K >> 4),
-                         P.p3 + 2 * row * (K >> 8)};
+    __device__ static __forceinline__ BufPlanes planes(const DevPlanes& P, int64_t N, int64_t K) {
+        const uint64_t nk = (uint64_t)N * (uint64_t)K;
+        return BufPlanes{make_rsrc(P.p0, nk / 2), make_rsrc(P.p1, nk / 4), make_rsrc(P.p2, nk / 16),
+                         make_rsrc(P.p3, nk / 128)};
     }
-    __device__ static __forceinline__ void load(Row& r, const DevPlanes& B, int b) {
-        r.ql = *(const uint4*)(B.p0 + 16 * b);
-        r.qh = *(const uint2*)(B.p1 + 8 * b);
-        r.sc = *(const uint16_t*)(B.p2 + 2 * b);
-        r.d = *(const uint16_t*)(B.p3 + 2 * (b >> 3));
+    __device__ static __forceinline__ RowOff row_off(int64_t row, int64_t K) {
+        return RowOff{(uint32_t)(row * (K >> 1)), (uint32_t)(row * (K >> 2)),
+                      (uint32_t)(row * (K >> 4)), (uint32_t)(row * (K >> 7))};
+    }
+    template <bool UNI = true>
+    __device__ static __forceinline__ void load(Row& r, const BufPlanes& B, const RowOff& o, int b) {
+        r.ql = bload<uint4, UNI>(B.p0, 16u * (uint32_t)b, o.o0);
+        r.qh = bload<uint2, UNI>(B.p1, 8u * (uint32_t)b, o.o1);
+        r.sc = bload<uint16_t, UNI>(B.p2, 2u * (uint32_t)b, o.o2);
+        r.d = bload<uint16_t, UNI>(B.p3, 2u * ((uint32_t)b >> 3), o.o3);
     }
     __device__ static __forceinline__ void vectors(uint32_t d0, uint32_t d1, uint32_t h,
                                                    uint32_t* v) {
@@ -245,12 +316,18 @@ struct Traits<kQ25> {
         uint4 c;
         uint32_t s2;   // the chunk's two fp16 scales
     };
-    __device__ static __forceinline__ DevPlanes base(const DevPlanes& P, int64_t row, int64_t K) {
-        return DevPlanes{P.p0 + row * (K >> 2), nullptr, P.p2 + 2 * row * (K >> 5), nullptr};
+    __device__ static __forceinline__ BufPlanes planes(const DevPlanes& P, int64_t N, int64_t K) {
+        const uint64_t nk = (uint64_t)N * (uint64_t)K;
+        return BufPlanes{make_rsrc(P.p0, nk / 4), make_rsrc(P.p0, 0), make_rsrc(P.p2, nk / 16),
+                         make_rsrc(P.p0, 0)};
     }
-    __device__ static __forceinline__ void load(Row& r, const DevPlanes& B, int b) {
-        r.c = *(const uint4*)(B.p0 + 16 * b);
-        r.s2 = *(const uint32_t*)(B.p2 + 4 * b);
+    __device__ static __forceinline__ RowOff row_off(int64_t row, int64_t K) {
+        return RowOff{(uint32_t)(row * (K >> 2)), 0u, (uint32_t)(row * (K >> 4)), 0u};
+    }
+    template <bool UNI = true>
+    __device__ static __forceinline__ void load(Row& r, const BufPlanes& B, const RowOff& o, int b) {
+        r.c = bload<uint4, UNI>(B.p0, 16u * (uint32_t)b, o.o0);
+        r.s2 = bload<uint32_t, UNI>(B.p2, 4u * (uint32_t)b, o.o2);
     }
     __device__ static __forceinline__ uint32_t vec(uint32_t d, int m) {
         return (d >> (2 * m)) & 0x03030303u;
@@ -315,11 +392,17 @@ struct Traits<kBF16> {
     struct Row {
         uint4 w;
     };
-    __device__ static __forceinline__ DevPlanes base(const DevPlanes& P, int64_t row, int64_t K) {
-        return DevPlanes{P.p0 + 2 * row * K, nullptr, nullptr, nullptr};
+    __device__ static __forceinline__ BufPlanes planes(const DevPlanes& P, int64_t N, int64_t K) {
+        const uint64_t nk = (uint64_t)N * (uint64_t)K;
+        return BufPlanes{make_rsrc(P.p0, 2 * nk), make_rsrc(P.p0, 0), make_rsrc(P.p0, 0),
+                         make_rsrc(P.p0, 0)};
     }
-    __device__ static __forceinline__ void load(Row& r, const DevPlanes& B, int b) {
-        r.w = *(const uint4*)(B.p0 + 16 * b);
+    __device__ static __forceinline__ RowOff row_off(int64_t row, int64_t K) {
+        return RowOff{(uint32_t)(2 * row * K), 0u, 0u, 0u};
+    }
+    template <bool UNI = true>
+    __device__ static __forceinline__ void load(Row& r, const BufPlanes& B, const RowOff& o, int b) {
+        r.w = bload<uint4, UNI>(B.p0, 16u * (uint32_t)b, o.o0);
     }
     static constexpr int NVEC = 8;   // the 8 weights as fp32 bit patterns
     __device__ static __forceinline__ void unpack(const Row& r, uint32_t* v) {

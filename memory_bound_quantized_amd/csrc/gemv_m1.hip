@@ -52,26 +52,44 @@ constexpr int kXPre = 12;
 constexpr int kProNone = 0, kProRms = 1;
 constexpr int kEpiStore = 0, kEpiSilu = 1;
 
+// Row groups and K slices (static K of 2 or 6 chunk steps, or 1 for Q25).
+// A workgroup holds S x 4 waves; wave w works on K slice w / 4 (chunk steps
+// [CSS * s, CSS * (s + 1)) of every row, CSS = CS / S) and on row block w % 4
+// of each of its G row groups.  x is staged once per workgroup for all of
+// them.  Six-step K (12288) takes S = 3 slices of two steps, so each wave
+// keeps the short, register-resident loop of the K = 4096 tables; the slice
+// partial sums meet in LDS and are added in slice order.
+constexpr bool grouped_form(int CS) { return CS == 1 || CS == 2 || CS == 6; }
+constexpr int k_slices(int CS) { return CS == 6 ? 3 : 1; }
+
 template <int FMT, int R, int CS, bool GATHER, bool XQ, int PRO = kProNone, int EPI = kEpiStore>
-__global__ __launch_bounds__(kBlock) void gemv_m1_kernel(DevPlanes P, int64_t N, int K,
+__global__ __launch_bounds__(kBlock * k_slices(CS)) void gemv_m1_kernel(DevPlanes P, int64_t N, int K,
                                                          const void* __restrict__ xsrc,
                                                          float* __restrict__ y, int accumulate,
                                                          const int32_t* __restrict__ gidx,
                                                          int rpe, const float* __restrict__ gamma,
-                                                         float eps) {
+                                                         float eps, int groups, int64_t nw) {
     using T = Traits<FMT>;
     static_assert(PRO == kProNone || (CS > 0 && !XQ), "the norm prologue needs static K, fp32 x");
     static_assert(EPI == kEpiStore || R == 2, "the silu epilogue pairs two rows per wave");
-    using XP = XPieces<FMT, XQ>;
+    constexpr bool GROUPED = grouped_form(CS);
+    constexpr int S = k_slices(CS);                           // K slices per workgroup
+    constexpr int CSS = CS / S;                               // chunk steps per slice
+    constexpr int NT = kBlock * S;                            // threads per workgroup
+    using XP = XPieces<FMT, XQ, NT>;
     constexpr int D = 2;                                      // chunk steps in flight
     extern __shared__ float4 smem[];
     uint32_t* xs = (uint32_t*)smem;
 
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int wave = wid % kWavesPerBlock;                    // row block of the wave
+    const int slice = wid / kWavesPerBlock;                   // K slice of the wave
+    const int c0 = slice * CSS;                               // its first chunk step
     const int nchunks = K / T::WPC;
     const int C = CS > 0 ? CS : (nchunks + kWave - 1) / kWave;
-    const int64_t row0 = ((int64_t)blockIdx.x * kWavesPerBlock + wave) * R;
+    const int G = GROUPED ? groups : 1;
+    const int64_t row0 = ((int64_t)blockIdx.x * G * kWavesPerBlock + wave) * R;
 
     // ---- x: the first pieces, before any weight load
     const uint4* xsrc4 = (const uint4*)xsrc;
@@ -79,7 +97,7 @@ __global__ __launch_bounds__(kBlock) void gemv_m1_kernel(DevPlanes P, int64_t N,
     constexpr int GF4 = XP::GF4;
     constexpr int NR = 4;                                     // pieces per runtime round
     // pieces per thread: all of them (static K), or the first round
-    constexpr int NX = CS > 0 ? (XQ ? CS * T::F4 / 4 : CS * T::WPC / 16) : NR;
+    constexpr int NX = CS > 0 ? (XQ ? CSS * T::F4 / 4 : CSS * T::WPC / 16) : NR;
     static_assert(NX <= kXPre && NX % GF4 == 0, "x pieces per thread");
     uint4 xr[NX];
 #pragma unroll
@@ -91,32 +109,43 @@ __global__ __launch_bounds__(kBlock) void gemv_m1_kernel(DevPlanes P, int64_t N,
     }
 
     // ---- y for an accumulating product (one load per lane, unconditional)
-    const int64_t yrow = row0 + (lane < R ? lane : 0);
-    const float yin = y[yrow < N ? yrow : N - 1];
+    auto y_of = [&](int64_t r0) {
+        const int64_t yrow = r0 + (lane < R ? lane : 0);
+        return y[yrow < N ? yrow : N - 1];
+    };
+    float yin = y_of(row0);
 
     // ---- weight rows: rows past N re-read row N-1 (their results are not stored)
-    DevPlanes base[R];
+    const BufPlanes B = T::planes(P, nw, K);
+    RowOff ro[R];
+    // Row indices fit in 32 bits (N < 2^31), which keeps the clamps on the
+    // scalar unit.
+    const int n32 = (int)N;
+    auto set_rows = [&](int64_t r0) {
 #pragma unroll
-    for (int r = 0; r < R; r++) {
-        int64_t n = row0 + r < N ? row0 + r : N - 1;
-        if constexpr (GATHER) {
-            const int e = (int)(n / rpe);
-            n = (int64_t)gidx[e] * rpe + (n - (int64_t)e * rpe);
+        for (int r = 0; r < R; r++) {
+            const int rr = (int)r0 + r;
+            int n = rr < n32 ? rr : n32 - 1;
+            if constexpr (GATHER) {
+                const int e = n / rpe;
+                n = gidx[e] * rpe + (n - e * rpe);
+            }
+            ro[r] = T::row_off(n, K);
         }
-        base[r] = T::base(P, n, K);
-    }
+    };
+    set_rows(row0);
     auto load = [&](Slot<FMT, R>& sl, int c) {
-        const int b = c * kWave + lane;
+        const int b = (c0 + c) * kWave + lane;
         const int bb = b < nchunks ? b : 0;
 #pragma unroll
-        for (int r = 0; r < R; r++) T::load(sl.row[r], base[r], bb);
+        for (int r = 0; r < R; r++) T::load(sl.row[r], B, ro[r], bb);
     };
 
     float acc[R];
 #pragma unroll
     for (int r = 0; r < R; r++) acc[r] = 0.f;
     auto compute = [&](const Slot<FMT, R>& sl, int c) {
-        const int b = c * kWave + lane;
+        const int b = (c0 + c) * kWave + lane;
         const bool ok = b < nchunks;
         uint32_t xv[4 * T::F4];
         read_x<FMT>(xs, ok ? b : 0, xv);
@@ -134,14 +163,14 @@ __global__ __launch_bounds__(kBlock) void gemv_m1_kernel(DevPlanes P, int64_t N,
     };
 
     if constexpr (CS > 0) {
-        // All of the row's chunks in flight when they fit (C <= 2), else D.
-        constexpr int DD = CS <= 2 ? CS : D;
+        // All of a slice's chunks in flight in the grouped form, else D.
+        constexpr int DD = GROUPED ? CSS : D;
         Slot<FMT, R> buf[DD];
 #pragma unroll
         for (int d = 0; d < DD; d++) load(buf[d], d);
         if constexpr (PRO == kProRms) {
             // RMSNorm of the row, as the stand-alone kernel: y = g * (x * inv)
-            __shared__ float red[kWavesPerBlock];
+            __shared__ float red[kWavesPerBlock * S];
             float ss = 0.f;
 #pragma unroll
             for (int i = 0; i < NX; i++) {
@@ -151,7 +180,7 @@ __global__ __launch_bounds__(kBlock) void gemv_m1_kernel(DevPlanes P, int64_t N,
                 ss = fmaf(v.z, v.z, ss);
                 ss = fmaf(v.w, v.w, ss);
             }
-            const float inv = 1.0f / sqrtf(block_sum(ss, red) / (float)K + eps);
+            const float inv = 1.0f / sqrtf(block_sum<kWavesPerBlock * S>(ss, red) / (float)K + eps);
 #pragma unroll
             for (int i = 0; i < NX; i++) {
                 const float4 v = __builtin_bit_cast(float4, xr[i]);
@@ -162,10 +191,76 @@ __global__ __launch_bounds__(kBlock) void gemv_m1_kernel(DevPlanes P, int64_t N,
         }
         XP::template store<NX, true>(xr, 0, npieces, xs);
         __syncthreads();
+        if constexpr (GROUPED) {
+            // Row groups: group g of this wave is rows ((blk * G + g) * 4 + wave) * R,
+            // so the workgroup's rows are one contiguous block.  Each group's
+            // chunks (of the wave's slice) are all in flight, two groups deep:
+            // the loads of group g + 1 are issued before group g is computed
+            // (the last group reloads itself; that copy is never used).  Slice
+            // sums go to LDS and the block is written once at the end,
+            // coalesced, so no store sits between the loads of the loop.
+            const int64_t gstride = (int64_t)kWavesPerBlock * R;
+            const int64_t rbase = row0;
+            // G * 4 * R <= 1024 rows per workgroup (G <= 64, R <= 4)
+            __shared__ float outs[S][kWavesPerBlock * 4 * 64];
+            Slot<FMT, R> alt[DD];
+            auto load_group = [&](Slot<FMT, R>* b, int g) {
+                const int gc = g < G ? g : G - 1;
+                set_rows(rbase + (int64_t)gc * gstride);
 #pragma unroll
-        for (int c = 0; c < CS; c++) {
-            compute(buf[c % DD], c);
-            if (c + DD < CS) load(buf[c % DD], c + DD);
+                for (int d = 0; d < DD; d++) load(b[d], d);
+            };
+            auto finish = [&](int g) {
+#pragma unroll
+                for (int r = 0; r < R; r++) {
+                    const float sr = wave_sum_dpp(acc[r]);
+                    if (lane == r) outs[slice][g * kWavesPerBlock * R + wave * R + r] = sr;
+                    acc[r] = 0.f;
+                }
+            };
+            for (int g = 0; g < G; g += 2) {
+                load_group(alt, g + 1);
+#pragma unroll
+                for (int c = 0; c < CSS; c++) compute(buf[c], c);
+                finish(g);
+                if (g + 1 >= G) break;
+                load_group(buf, g + 2);
+#pragma unroll
+                for (int c = 0; c < CSS; c++) compute(alt[c], c);
+                finish(g + 1);
+            }
+            __syncthreads();
+            // the workgroup's rows [blk G 4R, +G 4R): slice sums in slice order
+            const int per = G * kWavesPerBlock * R;
+            const int64_t rwg = (int64_t)blockIdx.x * per;
+            if constexpr (EPI == kEpiSilu) {
+                // rows 2t and 2t + 1 of the block are the gate and up rows of output rwg / 2 + t
+                for (int t = threadIdx.x; t < per / 2; t += NT) {
+                    float gs = outs[0][2 * t], us = outs[0][2 * t + 1];
+#pragma unroll
+                    for (int q = 1; q < S; q++) {
+                        gs += outs[q][2 * t];
+                        us += outs[q][2 * t + 1];
+                    }
+                    const int64_t n = rwg / 2 + t;
+                    if (n < N / 2) y[n] = (accumulate ? y[n] : 0.f) + gs / (1.0f + expf(-gs)) * us;
+                }
+            } else {
+                for (int t = threadIdx.x; t < per; t += NT) {
+                    float v = outs[0][t];
+#pragma unroll
+                    for (int q = 1; q < S; q++) v += outs[q][t];
+                    const int64_t n = rwg + t;
+                    if (n < N) y[n] = (accumulate ? y[n] : 0.f) + v;
+                }
+            }
+            return;
+        } else {
+#pragma unroll
+            for (int c = 0; c < CS; c++) {
+                compute(buf[c % DD], c);
+                if (c + DD < CS) load(buf[c % DD], c + DD);
+            }
         }
     } else {
         Slot<FMT, R> buf[D];
@@ -225,12 +320,15 @@ struct M1Args {
     int64_t rpe;
     const float* gamma;
     float eps;
+    int groups;          // row groups per wave (static K with C <= 2 only)
+    int64_t nw;          // rows of the weight table (N, or all experts for a gather)
 };
 
 template <int FMT, int R, int CS, bool GATHER, bool XQ, int PRO = kProNone, int EPI = kEpiStore>
 static hipError_t launch_k(const M1Args& a, hipStream_t stream) {
     using T = Traits<FMT>;
-    const int64_t rows_per_wg = (int64_t)kWavesPerBlock * R;
+    const int G = grouped_form(CS) ? (a.groups > 0 ? a.groups : 1) : 1;
+    const int64_t rows_per_wg = (int64_t)kWavesPerBlock * R * G;
     const int64_t grid = (a.N + rows_per_wg - 1) / rows_per_wg;
     const size_t lds = (size_t)(a.K / T::WPC) * Stride<FMT>::DW * 4;
     auto kern = gemv_m1_kernel<FMT, R, CS, GATHER, XQ, PRO, EPI>;
@@ -239,8 +337,8 @@ static hipError_t launch_k(const M1Args& a, hipStream_t stream) {
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBlock), lds, stream, a.P, a.N, (int)a.K,
-                       a.x, a.y, a.accumulate, a.gidx, (int)a.rpe, a.gamma, a.eps);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBlock * k_slices(CS)), lds, stream, a.P, a.N, (int)a.K,
+                       a.x, a.y, a.accumulate, a.gidx, (int)a.rpe, a.gamma, a.eps, G, a.nw);
     return hipGetLastError();
 }
 
@@ -274,20 +372,52 @@ static hipError_t launch_f(const M1Args& a, bool xq, GemvGeom geom, hipStream_t 
     }
 }
 
-// Default rows per wave, from cold-cache sweeps on MI355X: many small
-// workgroups hide latency better than few large ones, so R = 2 only for the
-// larger tables.
-GemvGeom gemv_m1_default_geom(int fmt, int64_t N, int64_t K) {
-    (void)fmt;
+// Default geometry, from cold-weight sweeps on MI355X.  Tables whose K
+// takes at most two unrolled chunk steps use row groups: about 512
+// workgroups of 4 waves (N / 2048 rows per wave, at most 4) beat both many
+// small workgroups, which each stage x again, and few large ones, which
+// leave CUs idle at the tail.  The largest tables (a vocabulary head) take
+// 8 rows per wave.  Six-step K (12288) runs three K slices per workgroup
+// and N / 1024 single-row groups, at most 4.
+// Other K keep one group and 1, 2 or 4 rows per wave.  The silu product
+// (pairs) takes its rows two at a time, N / 4096 pairs per wave up to 6.
+GemvGeom gemv_m1_default_geom(int fmt, int64_t N, int64_t K, bool pairs) {
     GemvGeom g;
-    g.rows_per_wave = N >= 65536 ? 4 : N * K >= ((int64_t)32 << 20) ? 2 : 1;
+    g.groups = 1;
+    int steps = 0;
+    switch (fmt) {
+    case kQ45: steps = static_steps<kQ45>(K); break;
+    case kQ65: steps = static_steps<kQ65>(K); break;
+    case kQ25: steps = static_steps<kQ25>(K); break;
+    case kBF16: steps = static_steps<kBF16>(K); break;
+    }
+    if (!grouped_form(steps)) {
+        g.rows_per_wave = N >= 65536 ? 4 : N * K >= ((int64_t)32 << 20) ? 2 : 1;
+        return g;
+    }
+    if (pairs) {
+        g.rows_per_wave = 2;
+        g.groups = N / 4096 < 1 ? 1 : N / 4096 > 6 ? 6 : (int)(N / 4096);
+        return g;
+    }
+    g.rows_per_wave = 1;
+    if (steps == 6) {
+        g.groups = N / 1024 < 1 ? 1 : N / 1024 > 4 ? 4 : (int)(N / 1024);
+        return g;
+    }
+    if (N >= 65536) {
+        g.groups = 8;
+        return g;
+    }
+    g.groups = N / 2048 < 1 ? 1 : N / 2048 > 4 ? 4 : (int)(N / 2048);
     return g;
 }
 
 hipError_t launch_gemv_m1(int fmt, DevPlanes P, int64_t N_out, int64_t K, const void* x,
                           bool x_staged, float* y, int accumulate, const int32_t* gidx,
-                          int64_t rpe, GemvGeom geom, hipStream_t stream) {
-    const M1Args a{P, N_out, K, x, y, accumulate, gidx, rpe, nullptr, 0.f};
+                          int64_t rpe, GemvGeom geom, hipStream_t stream, int64_t n_weight_rows) {
+    const M1Args a{P, N_out, K, x, y, accumulate, gidx, rpe, nullptr, 0.f, geom.groups,
+                   n_weight_rows > 0 ? n_weight_rows : N_out};
     switch (fmt) {
     case kQ45: return launch_f<kQ45>(a, x_staged, geom, stream);
     case kQ65: return launch_f<kQ65>(a, x_staged, geom, stream);
@@ -330,7 +460,11 @@ bool gemv_fused_supported(int fmt, int64_t K) {
 hipError_t launch_gemv_fused(int fmt, DevPlanes P, int64_t N, int64_t K, const float* x,
                              const float* gamma, float eps, bool silu, float* y, int accumulate,
                              GemvGeom geom, hipStream_t stream) {
-    const M1Args a{P, N, K, x, y, accumulate, nullptr, 1, gamma, eps};
+    // the silu epilogue takes its gate/up rows in pairs (R = 2): keep the
+    // rows per wave of the geometry asked for
+    int groups = geom.groups;
+    if (silu && geom.rows_per_wave != 2) groups = (groups * geom.rows_per_wave + 1) / 2;
+    const M1Args a{P, N, K, x, y, accumulate, nullptr, 1, gamma, eps, groups, N};
     const bool norm = gamma != nullptr;
     switch (fmt) {
     case kQ45: return launch_fused_f<kQ45>(a, norm, silu, geom.rows_per_wave, stream);

@@ -21,7 +21,9 @@ struct SlotM {
     typename Traits<FMT>::Row row[R];
 };
 
-// CS > 0: K = 64 * CS * WPC, every loop unrolled (see gemv_m1.hip).
+// CS > 0: K = 64 * CS * WPC, every loop unrolled (see gemv_m1.hip).  Row sums
+// follow the single-token kernel's order, so each token's row is bit-identical
+// to its M = 1 product.
 template <int FMT, int R, int M, int CS, bool XQ>
 __global__ __launch_bounds__(kBlock) void gemv_smallm_kernel(DevPlanes P, int64_t N, int K,
                                                              const void* __restrict__ xsrc,
@@ -57,14 +59,15 @@ __global__ __launch_bounds__(kBlock) void gemv_smallm_kernel(DevPlanes P, int64_
             for (int i = 0; i < NX; i++) xr[m * NX + i] = XP::load(xrow(m), i, npieces);
     }
 
-    DevPlanes base[R];
+    const BufPlanes B = T::planes(P, N, K);
+    RowOff ro[R];
 #pragma unroll
-    for (int r = 0; r < R; r++) base[r] = T::base(P, row0 + r < N ? row0 + r : N - 1, K);
+    for (int r = 0; r < R; r++) ro[r] = T::row_off(row0 + r < N ? row0 + r : N - 1, K);
     auto load = [&](SlotM<FMT, R>& sl, int c) {
         const int b = c * kWave + lane;
         const int bb = b < nchunks ? b : 0;
 #pragma unroll
-        for (int r = 0; r < R; r++) T::load(sl.row[r], base[r], bb);
+        for (int r = 0; r < R; r++) T::load(sl.row[r], B, ro[r], bb);
     };
 
     SlotM<FMT, R> buf[D];
@@ -117,11 +120,25 @@ __global__ __launch_bounds__(kBlock) void gemv_smallm_kernel(DevPlanes P, int64_
         }
     };
 
+    // Six-step K sums as the single-token kernel does: per two-step slice
+    // across the wave, then the slices in order.
+    constexpr int SL = CS == 6 ? 2 : CS;
+    float tot[R][M];
     if constexpr (CS > 0) {
 #pragma unroll
         for (int c = 0; c < CS; c++) {
             compute(buf[c % D], c);
             if (c + D < CS) load(buf[c % D], c + D);
+            if (SL < CS && (c + 1) % SL == 0) {
+#pragma unroll
+                for (int r = 0; r < R; r++)
+#pragma unroll
+                    for (int m = 0; m < M; m++) {
+                        const float w = wave_sum_dpp(acc[r][m]);
+                        tot[r][m] = c + 1 == SL ? w : tot[r][m] + w;
+                        acc[r][m] = 0.f;
+                    }
+            }
         }
     } else {
         for (int c = 0; c < C; c += D) {
@@ -140,7 +157,7 @@ __global__ __launch_bounds__(kBlock) void gemv_smallm_kernel(DevPlanes P, int64_
     for (int r = 0; r < R; r++)
 #pragma unroll
         for (int m = 0; m < M; m++) {
-            const float s = wave_sum_dpp(acc[r][m]);
+            const float s = SL < CS ? tot[r][m] : wave_sum_dpp(acc[r][m]);
             if (lane == r * M + m && row0 + r < N) {
                 float* dst = y + (int64_t)m * ldy + row0 + r;
                 *dst = accumulate ? *dst + s : s;
@@ -186,6 +203,7 @@ static hipError_t launch_sm(DevPlanes P, int64_t N, int64_t K, const void* x, in
     constexpr int per = 64 * Traits<FMT>::WPC;
     if constexpr (FMT == kQ45 || FMT == kQ65) {
         if (K == 2 * per) return launch_sc<FMT, M, 2>(P, N, K, x, ldx, xq, y, ldy, accumulate, s);
+        if (K == 6 * per) return launch_sc<FMT, M, 6>(P, N, K, x, ldx, xq, y, ldy, accumulate, s);
     }
     if constexpr (FMT == kQ25) {
         if (K == per) return launch_sc<FMT, M, 1>(P, N, K, x, ldx, xq, y, ldy, accumulate, s);

@@ -26,16 +26,20 @@ constexpr int64_t kMaxKBF16 = 16384;
 // Geometry of the M = 1 GEMV: output rows per wave (4 waves per workgroup).
 struct GemvGeom {
     int rows_per_wave;   // 1, 2 or 4
+    int groups;          // row groups per wave (K = 4096-class tables; 1 otherwise)
 };
 
-GemvGeom gemv_m1_default_geom(int fmt, int64_t N, int64_t K);
+GemvGeom gemv_m1_default_geom(int fmt, int64_t N, int64_t K, bool pairs = false);
 
 // y[n] (+)= W[row(n)] . x for n < N_out.  If gidx != nullptr the output row
 // n maps to weight row gidx[n / rpe] * rpe + n % rpe (gathered experts).
 // x is fp32 [K], or x staged for fmt (staging.h) when x_staged.
+// n_weight_rows: rows of the weight table when it differs from N_out (a
+// gather over stacked experts); 0 means N_out.
 hipError_t launch_gemv_m1(int fmt, DevPlanes P, int64_t N_out, int64_t K, const void* x,
                           bool x_staged, float* y, int accumulate, const int32_t* gidx,
-                          int64_t rpe, GemvGeom geom, hipStream_t stream);
+                          int64_t rpe, GemvGeom geom, hipStream_t stream,
+                          int64_t n_weight_rows = 0);
 
 // Fused M = 1 product on fp32 x (Q45/Q65 with K = 4096 or 12288 only, see
 // gemv_fused_supported): y = W . rmsnorm(x; gamma, eps) when gamma != nullptr,
@@ -75,6 +79,40 @@ hipError_t launch_stage_x_mfma(const float* x, int64_t M, int64_t ldx, int64_t K
                                hipStream_t stream);
 hipError_t launch_gemv_mfma_q45(DevPlanes P, int64_t N, int64_t K, const void* xt, int64_t M,
                                 float* y, int64_t ldy, int accumulate, hipStream_t stream);
+
+// ---- one decode token in one launch (decode_persistent.hip) --------------
+// Device-side description of a decoder layer; the table lives in the
+// caller's workspace, written by the prepare call.
+struct DecLayer {
+    DevPlanes qkv, o, gu, dn;   // gu: gate/up rows interleaved
+    const float* g1;
+    const float* g2;
+    int32_t fmt_dn;
+    int32_t pad;
+};
+struct DecTable {
+    uint64_t magic;             // kDecMagic once prepared
+    int64_t n_layers;
+    uint64_t tag;               // identifies the model the table was written for
+    uint64_t pad;
+    DecLayer layers[1];         // n_layers entries
+};
+struct DecHead {
+    DevPlanes lm;
+    const float* gf;
+    int32_t fmt_lm;
+    int32_t pad;
+};
+constexpr uint64_t kDecMagic = 0x31706564716d6266ull;
+
+// Requires d = dq = 4096, f = 12288, Q45 qkv/o/gate-up, Q45 or Q65 down and
+// lm head, an even number of qkv rows and of vocab rows.  ctr and err are
+// zeroed by a small kernel first; err != 0 afterwards means a barrier spin
+// gave up (1) or the table did not match (2).
+hipError_t launch_decode_persistent(const DecTable* table, DecTable expect, DecHead head,
+                                    float eps, float* h, float* logits, int64_t vocab,
+                                    int64_t nqkv, float* qkv, float* mbuf, uint32_t* ctr,
+                                    uint32_t* err, hipStream_t stream);
 
 // y[m][n] = 0 for the K == 0 case (rows of length ldy, first N entries).
 hipError_t launch_fill_zero(float* y, int64_t M, int64_t N, int64_t ldy, hipStream_t stream);

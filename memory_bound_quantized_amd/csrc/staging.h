@@ -171,19 +171,19 @@ __device__ __forceinline__ void read_x(const uint32_t* xs, int b, uint32_t* xv) 
 
 // ---- x into LDS, inside a workgroup --------------------------------------
 // x arrives as 16-byte pieces: float4 of fp32 x, or 16-byte slots of staged x
-// (XQ).  Piece i of a thread (i = 0, 1, ...) is
-//   staged: slot i * 256 + tid of the row (consecutive threads, consecutive
+// (XQ).  Piece i of a thread (i = 0, 1, ...) of a workgroup of NT threads is
+//   staged: slot i * NT + tid of the row (consecutive threads, consecutive
 //           slots: coalesced);
-//   fp32:   float4 j = i % GF4 of group (i / GF4) * 256 + tid, so each thread
+//   fp32:   float4 j = i % GF4 of group (i / GF4) * NT + tid, so each thread
 //           holds the GF4 float4 of whole groups of GX values.
-template <int FMT, bool XQ>
+template <int FMT, bool XQ, int NT = kBlock>
 struct XPieces {
     static constexpr int GF4 = Traits<FMT>::GX / 4;
     __device__ static __forceinline__ int index(int i) {
         if constexpr (XQ)
-            return i * kBlock + (int)threadIdx.x;
+            return i * NT + (int)threadIdx.x;
         else
-            return ((i / GF4) * kBlock + (int)threadIdx.x) * GF4 + i % GF4;
+            return ((i / GF4) * NT + (int)threadIdx.x) * GF4 + i % GF4;
     }
     // pieces in a row of K values
     __device__ static __forceinline__ int count(int K) {
@@ -192,7 +192,7 @@ struct XPieces {
     // Load piece i (index clamped into the row, so the load is unconditional).
     __device__ static __forceinline__ uint4 load(const uint4* __restrict__ src, int i, int n) {
         const int p = index(i);
-        return src[p < n ? p : n - 1];
+        return gload<uint4>((const uint8_t*)src, 16u * (uint32_t)(p < n ? p : n - 1));
     }
     // Store pieces [i0, i0 + NI) (NI a multiple of GF4 for fp32) into LDS.
     // ALL: every piece is known to lie inside the row (no bounds test, so the
@@ -210,7 +210,7 @@ struct XPieces {
             const int ngroups = n / GF4;
 #pragma unroll
             for (int i = 0; i < NI; i += GF4) {
-                const int og = ((i0 + i) / GF4) * kBlock + (int)threadIdx.x;
+                const int og = ((i0 + i) / GF4) * NT + (int)threadIdx.x;
                 stage_group<FMT>((const float*)(v + i), og, ALL || og < ngroups, LdsDst<FMT>{xs});
             }
         }

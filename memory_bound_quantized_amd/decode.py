@@ -94,7 +94,27 @@ class DecodeModel:
         return int(n)
 
     def step(self, h, logits, stream=None):
-        """One token: h (fp32 [d], updated in place) -> logits (fp32 [vocab])."""
+        """One token: h (fp32 [d], updated in place) -> logits (fp32 [vocab]);
+        four launches per layer."""
         check(lib.mbq_decode_step(ctypes.byref(self.desc), _ptr(h), _ptr(logits),
                                   _ptr(self.workspace), self.workspace.numel(), _stream(stream)))
         return logits
+
+    def prepare(self, stream=None):
+        """Write the layer table the one-launch step reads into the workspace."""
+        check(lib.mbq_decode_prepare(ctypes.byref(self.desc), _ptr(self.workspace),
+                                     self.workspace.numel(), _stream(stream)))
+        self._prepared = True
+
+    def step_persistent(self, h, logits, stream=None):
+        """One token in one launch (mbq_decode_step_persistent)."""
+        if not getattr(self, "_prepared", False):
+            self.prepare(stream)
+        check(lib.mbq_decode_step_persistent(ctypes.byref(self.desc), _ptr(h), _ptr(logits),
+                                             _ptr(self.workspace), self.workspace.numel(),
+                                             _stream(stream)))
+        return logits
+
+    def status(self) -> int:
+        """The one-launch step's status word (0: success), read after a sync."""
+        return int(self.workspace[4:8].view(__import__("torch").int32).item())

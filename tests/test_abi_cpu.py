@@ -30,7 +30,7 @@ def _declared_symbols():
 
 def test_library_exports_every_declared_symbol():
     declared = _declared_symbols()
-    assert len(declared) == 24
+    assert len(declared) == 26
     assert sorted(_lib.EXPORTS) == declared
     lib = ctypes.CDLL(_lib.LIB_PATH)
     for name in declared:
@@ -265,7 +265,9 @@ def test_decode_argument_checks():
     m = _model()
     nb = ctypes.c_size_t()
     assert L.mbq_decode_workspace_bytes(ctypes.byref(m), ctypes.byref(nb)) == _lib.OK
-    assert nb.value == (4096 + 2048) * 4 + 12288 * 4
+    # status words, q|k|v, gated activations, then the one-launch step's layer table
+    table = 32 + 1 * 152
+    assert nb.value == 256 + (4096 + 2048) * 4 + 12288 * 4 + (table + 255) // 256 * 256
     h, lg, ws = BASE + 0x7000000000, BASE + 0x7100000000, BASE + 0x7200000000
     st = lambda m, h=h, lg=lg, ws=ws, n=nb.value: L.mbq_decode_step(ctypes.byref(m), h, lg, ws, n, None)
     assert st(m, n=nb.value - 1) == _lib.EINVAL                             # workspace too small
@@ -279,6 +281,18 @@ def test_decode_argument_checks():
     e = _model(vocab=0)
     e.eps = float("nan")
     assert st(e) == _lib.EINVAL
+    # the one-launch step: same checks, plus its shape limits
+    ps = lambda m, h=h, lg=lg, ws=ws, n=nb.value: L.mbq_decode_step_persistent(ctypes.byref(m), h, lg, ws, n, None)
+    assert ps(m, n=nb.value - 1) == _lib.EINVAL
+    assert ps(_model(dkv=512, f=8192)) in (_lib.EUNSUPPORTED,)               # f must be 12288
+    odd = _model(vocab=1001)
+    assert ps(odd) == _lib.EUNSUPPORTED                                     # even vocab rows
+    q65o = _model()
+    q65o.layers[0].o.fmt = 2
+    q65o.layers[0].o.codes_hi = BASE + 0x900000
+    q65o.layers[0].o.super_scales = BASE + 0xA00000
+    assert ps(q65o) == _lib.EUNSUPPORTED                                    # o must be Q45
+    assert L.mbq_decode_prepare(ctypes.byref(m), ws + 16, nb.value, None) == _lib.EINVAL
     assert L.mbq_last_error()
 
 

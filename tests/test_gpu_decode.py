@@ -144,3 +144,55 @@ def test_decode_step_graph_replays_match_eager():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(h, h_e) and torch.equal(lg, lg_e)
+
+
+# --------------------------------------------------------------------------
+# the one-launch step (mbq_decode_step_persistent)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("layers,vocab", [(2, 1000), (3, 4096)])
+def test_persistent_step_matches_oracle_chain(layers, vocab):
+    from memory_bound_quantized_amd.decode import DecodeModel
+    print("persistent layers=%d vocab=%d" % (layers, vocab), flush=True)
+    cfg = workloads.config3(layers=layers, vocab=vocab)
+    model = DecodeModel(cfg["layers"], cfg["vocab"], cfg["g1"], cfg["g2"], cfg["gf"], cfg["eps"])
+    h = dev(cfg["h0"])
+    logits = torch.empty(vocab, device="cuda")
+    model.step_persistent(h, logits)
+    torch.cuda.synchronize()
+    assert model.status() == 0
+    h_ref, lg_ref = _oracle_chain(cfg)
+    e_h = rel_l2(h.cpu().numpy(), h_ref)
+    e_l = rel_l2(logits.cpu().numpy(), lg_ref)
+    print("  rel-L2 h %.2e logits %.2e" % (e_h, e_l), flush=True)
+    assert e_h <= 1e-4 and e_l <= 1e-4
+    # the launch-per-step path on the same model agrees within the same bar
+    h2 = dev(cfg["h0"])
+    lg2 = torch.empty(vocab, device="cuda")
+    model.step(h2, lg2)
+    assert rel_l2(lg2.cpu().numpy(), logits.cpu().numpy()) <= 1e-4
+
+
+def test_persistent_step_repeated_tokens_and_table_guard():
+    """Several tokens in a row reuse the prepared table; a workspace prepared
+    for another model is refused on the device (status bit 1, h untouched)."""
+    from memory_bound_quantized_amd.decode import DecodeModel
+    cfg = workloads.config3(layers=1, vocab=512)
+    a = DecodeModel(cfg["layers"], cfg["vocab"], cfg["g1"], cfg["g2"], cfg["gf"], cfg["eps"])
+    h = dev(cfg["h0"])
+    lg = torch.empty(512, device="cuda")
+    hp, lp = h.clone(), torch.empty(512, device="cuda")
+    for _ in range(3):
+        a.step_persistent(h, lg)
+        a.step(hp, lp)
+    torch.cuda.synchronize()
+    assert a.status() == 0
+    assert rel_l2(h.cpu().numpy(), hp.cpu().numpy()) <= 1e-4
+    b = DecodeModel(cfg["layers"], cfg["vocab"], cfg["g1"], cfg["g2"], cfg["gf"], cfg["eps"])
+    b.workspace = a.workspace                      # a's table, b's pointers
+    b._prepared = True
+    h0 = h.clone()
+    b.step_persistent(h, lg)
+    torch.cuda.synchronize()
+    assert b.status() & 2
+    assert torch.equal(h, h0)
