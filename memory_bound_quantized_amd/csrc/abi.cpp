@@ -140,6 +140,20 @@ bool geom_override(mbq::GemvGeom* g) {
     return any;
 }
 
+// Small-batch geometry: defaults, or MBQ_SMALLM_ROWS (1 or 2) and
+// MBQ_SMALLM_GROUPS for tuning sweeps; an override that does not fit the
+// kernel's row-sum buffer is ignored.
+mbq::GemvGeom smallm_geom(int fmt, int64_t M, int64_t N) {
+    mbq::GemvGeom g = mbq::gemv_smallm_default_geom(fmt, M, N);
+    mbq::GemvGeom o = g;
+    int v = 0;
+    const char* s = getenv("MBQ_SMALLM_ROWS");
+    if (s && sscanf(s, "%d", &v) == 1) o.rows_per_wave = v;
+    const char* t = getenv("MBQ_SMALLM_GROUPS");
+    if (t && sscanf(t, "%d", &v) == 1) o.groups = v;
+    return mbq::gemv_smallm_geom_ok(M, o) ? o : g;
+}
+
 // ------------------------------------------------------------ host packer
 
 // Bit of the run's 32-bit high-bits word that holds weight r of a Q65 run of
@@ -312,7 +326,8 @@ int mbq_gemv_q(const mbq_qweight* W, const float* x, int64_t M, int64_t ldx, flo
                                                      y + m0 * ldy, accumulate, nullptr, 1,
                                                      mbq::gemv_m1_default_geom(W->fmt, W->N, W->K), s)
                                : mbq::launch_gemv_smallm(W->fmt, P, W->N, W->K, x + m0 * ldx, false,
-                                                         mm, ldx, y + m0 * ldy, ldy, accumulate, s);
+                                                         mm, ldx, y + m0 * ldy, ldy, accumulate,
+                                                         smallm_geom(W->fmt, mm, W->N), s);
         if (e != hipSuccess) return hip_status(e, fn);
     }
     return ok();
@@ -665,7 +680,8 @@ int mbq_gemv_xq(const mbq_qweight* W, const void* xq, int64_t M, float* y, int64
         hipError_t e = mm == 1 ? mbq::launch_gemv_m1(W->fmt, P, W->N, W->K, xm, true, y + m0 * ldy,
                                                      accumulate, nullptr, 1, g1, s)
                                : mbq::launch_gemv_smallm(W->fmt, P, W->N, W->K, xm, true, mm, W->K,
-                                                         y + m0 * ldy, ldy, accumulate, s);
+                                                         y + m0 * ldy, ldy, accumulate,
+                                                         smallm_geom(W->fmt, mm, W->N), s);
         if (e != hipSuccess) return hip_status(e, fn);
     }
     return ok();

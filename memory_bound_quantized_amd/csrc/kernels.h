@@ -65,11 +65,14 @@ hipError_t launch_silu_mul_xq(const float* g, const float* u, int64_t n, int fmt
 
 // Y[m][n] (+)= W[n] . X[m] for 2 <= M <= 8 (vector units).  X is fp32
 // [M][ldx], or staged for fmt (M rows of K) when x_staged.  All M tokens are
-// staged in LDS: gemv_smallm_fits tells whether they fit.
+// staged in LDS: gemv_smallm_fits tells whether they fit.  Geometry: 1 or 2
+// rows per wave, row groups per 16-wave workgroup (gemv_smallm_geom_ok).
 bool gemv_smallm_fits(int fmt, int64_t M, int64_t K);
+GemvGeom gemv_smallm_default_geom(int fmt, int64_t M, int64_t N);
+bool gemv_smallm_geom_ok(int64_t M, GemvGeom g);
 hipError_t launch_gemv_smallm(int fmt, DevPlanes P, int64_t N, int64_t K, const void* x,
                               bool x_staged, int64_t M, int64_t ldx, float* y, int64_t ldy,
-                              int accumulate, hipStream_t stream);
+                              int accumulate, GemvGeom g, hipStream_t stream);
 
 // Matrix-core product for Q45 and M >= 16 tokens (gemv_mfma.hip).  X comes in
 // the staged tile form: xt_bytes(M, K) bytes written by launch_stage_x_mfma.
