@@ -18,11 +18,7 @@
 // order in which a lane unpacks the 8 codes of one dword); then one float per
 // token slot, 2^-e (0 for slots past M).
 //
-// Kernel geometry: 4 waves per workgroup, one 16-row tile per wave, all K.
-// The workgroup copies 8-block slabs of xt into LDS (double-buffered); each
-// wave streams its rows' codes as 16-byte loads (one block per lane, 4 blocks
-// per row per load), 8 loads ahead, and turns them into MFMA A operands
-// through a small per-wave LDS transpose.
+// Kernel geometry: TR row tiles x S K parts of waves per workgroup (below).
 #include "device_common.h"
 #include "formats.h"
 #include "kernels.h"
@@ -37,21 +33,24 @@ typedef float f4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u2v __attribute__((ext_vector_type(2)));
 
-constexpr int kSB = 8;                  // blocks per xt slab
 constexpr int kGB = 4;                  // blocks per weight load (one per lane)
-constexpr int kPG = 8;                  // weight loads in flight per wave
-constexpr int kUS = kPG * kGB / kSB;    // slabs per unrolled loop body
 constexpr int kScrStride = 20;          // dwords per row of the transpose scratch
 
 __device__ __forceinline__ int64_t xt_tile_bytes(int64_t K) { return (K / 32) * 2048; }
 
-// ---- staging: one workgroup per token slot ------------------------------
+// ---- staging: one workgroup per token slot and 1024-value chunk of K ------
+// Each workgroup finds its token's largest |x| over the whole row (the row is
+// read from L2 by every chunk's workgroup) and converts its own chunk, so
+// the staging of 16 tokens runs on 16 x K / 1024 workgroups.
+constexpr int kStageChunk = 1024;
+
 __global__ __launch_bounds__(kBlock) void stage_x_mfma_kernel(const float* __restrict__ x,
                                                               int64_t ldx, int M, int K,
                                                               uint8_t* __restrict__ xt,
                                                               float* __restrict__ tscale) {
     __shared__ float red[kWavesPerBlock];
     const int m = blockIdx.x;                       // token slot
+    const int k0 = blockIdx.y * kStageChunk;        // this workgroup's chunk
     const int tt = m / 16, j = m % 16;
     const int nb = K / 32;
     const bool real = m < M;
@@ -70,11 +69,13 @@ __global__ __launch_bounds__(kBlock) void stage_x_mfma_kernel(const float* __res
     int e = 141 - (int)((__builtin_bit_cast(uint32_t, amax) >> 23) & 0xFFu);
     e = e > 126 ? 126 : (e < -126 ? -126 : e);
     const float up = __builtin_bit_cast(float, (uint32_t)(e + 127) << 23);
-    if (threadIdx.x == 0) tscale[m] = real ? __builtin_bit_cast(float, (uint32_t)(127 - e) << 23) : 0.f;
+    if (threadIdx.x == 0 && blockIdx.y == 0)
+        tscale[m] = real ? __builtin_bit_cast(float, (uint32_t)(127 - e) << 23) : 0.f;
     // half slot of weight m8 = k % 8 within a lane's 8 values
     constexpr int kSlot[8] = {0, 2, 4, 6, 1, 3, 5, 7};
     _Float16* base = (_Float16*)(xt + (int64_t)tt * nb * 2048);
-    for (int k = 4 * (int)threadIdx.x; k < K; k += 4 * kBlock) {
+    const int k1 = k0 + kStageChunk < K ? k0 + kStageChunk : K;
+    for (int k = k0 + 4 * (int)threadIdx.x; k < k1; k += 4 * kBlock) {
         float4 v = real ? *(const float4*)(xr + k) : make_float4(0.f, 0.f, 0.f, 0.f);
         const float vv[4] = {v.x, v.y, v.z, v.w};
         const int b = k / 32, g = (k % 32) / 8, lane = j + 16 * g;
@@ -101,8 +102,9 @@ hipError_t launch_stage_x_mfma(const float* x, int64_t M, int64_t ldx, int64_t K
     const int64_t TT = (M + 15) / 16;
     uint8_t* p = (uint8_t*)xt;
     float* ts = (float*)(p + TT * (K / 32) * 2048);
-    hipLaunchKernelGGL(stage_x_mfma_kernel, dim3((unsigned)(TT * 16)), dim3(kBlock), 0, stream, x,
-                       ldx, (int)M, (int)K, p, ts);
+    const unsigned chunks = (unsigned)((K + kStageChunk - 1) / kStageChunk);
+    hipLaunchKernelGGL(stage_x_mfma_kernel, dim3((unsigned)(TT * 16), chunks), dim3(kBlock), 0, stream,
+                       x, ldx, (int)M, (int)K, p, ts);
     return hipGetLastError();
 }
 
@@ -131,57 +133,80 @@ __device__ __forceinline__ h8 codes_to_a(uint32_t a) {
     return h8{w[0][0], w[0][1], w[1][0], w[1][1], w[2][0], w[2][1], w[3][0], w[3][1]};
 }
 
-// K % 1024 == 0 (nslab a multiple of kUS).  One workgroup per compute unit
-// at most (the grid is N / 64 workgroups and the LDS holds the slabs), so each
-// wave may use a whole SIMD's registers: prefetched codes and scales and the
-// next slab of xt all stay in registers.
-template <int TT>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gemv_mfma_q45_kernel(DevPlanes P, int64_t N, int K,
-                                                               const u4v* __restrict__ xt,
-                                                               const float* __restrict__ tscale,
-                                                               int M, float* __restrict__ y,
-                                                               int64_t ldy, int accumulate) {
+// Workgroup = TR row tiles x S K parts of waves (TR * S waves).  Wave w takes
+// row tile w % TR (16 rows) over K part w / TR (nb / S blocks); the waves of
+// one K part share its xt slabs (SB blocks of every token tile), which the
+// workgroup copies into LDS one step ahead (double-buffered).  Each wave
+// streams its rows' codes as 16-byte loads (one block per lane, 4 blocks per
+// row per load), kPG loads ahead, and turns them into MFMA A operands through
+// a small per-wave LDS transpose.  The S partial tiles of a row tile are
+// added in part order through LDS at the end.
+//
+// Requires K % 1024 == 0 and (nb / S) a multiple of kPG * kGB and of SB.
+constexpr int kPGv2 = 4;                   // weight loads in flight per wave
+
+template <int TT, int TR, int S, int SB>
+__global__ __launch_bounds__(kWave * TR * S) void gemv_mfma_q45_kernel(
+        DevPlanes P, int64_t N, int K, const u4v* __restrict__ xt, const float* __restrict__ tscale,
+        int M, float* __restrict__ y, int64_t ldy, int accumulate) {
+    constexpr int NW = TR * S;
+    constexpr int NT = kWave * NW;
+    constexpr int XSB = TT * SB * 128;                // uint4 per slab of one K part
+    constexpr int XALL = S * XSB;                     // uint4 per slab step, all parts
+    constexpr int XPT = (XALL + NT - 1) / NT;         // per thread (last round guarded)
+    constexpr int GPS = SB / kGB;                     // weight groups per slab
+    constexpr int kUSv = kPGv2 / GPS > 0 ? kPGv2 / GPS : 1;   // slabs per unrolled body
+    constexpr int RING = kUSv * GPS;                  // ring slots (>= kPGv2)
+    static_assert(SB % kGB == 0 && RING >= kPGv2, "slab and ring geometry");
     extern __shared__ u4v lds[];
-    constexpr int XSB = TT * kSB * 128;               // uint4 per slab buffer
-    constexpr int XPT = XSB / kBlock;                 // uint4 per thread per slab (TT * 4)
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int tr = wave % TR, part = wave / TR;
     const int i = lane & 15, g = lane >> 4;
-    uint32_t* scr = (uint32_t*)(lds + 2 * XSB) + wave * 16 * kScrStride;
-    const int nb = K / 32, ngroups = nb / kGB, nslab = nb / kSB;
-    const int64_t row0 = ((int64_t)blockIdx.x * kWavesPerBlock + wave) * 16;
+    uint32_t* scr = (uint32_t*)(lds + 2 * XALL) + wave * 16 * kScrStride;
+    const int nb = K / 32, nbp = nb / S;              // blocks per K part
+    const int ngroups = nbp / kGB, nslab = nbp / SB;
+    const int b0 = part * nbp;                        // first block of this wave's part
+    const int64_t row0 = ((int64_t)blockIdx.x * TR + tr) * 16;
 
-    // A side: row i's codes, 16 bytes (one block) per lane per load
+    // A side: row i's codes from block b0, 16 bytes (one block) per lane per load
     const int64_t ra = row0 + i < N ? row0 + i : N - 1;
-    const u4v* wq = (const u4v*)(P.p0 + ra * (K >> 1));
+    const u4v* wq = (const u4v*)(P.p0 + ra * (K >> 1)) + b0;
     // D side: the scales of rows 4g + v, 4 blocks (8 bytes) per load
     const u2v* sq[4];
 #pragma unroll
     for (int v = 0; v < 4; v++) {
         const int64_t rs = row0 + 4 * g + v < N ? row0 + 4 * g + v : N - 1;
-        sq[v] = (const u2v*)(P.p2 + rs * (K >> 5) * 2);
+        sq[v] = (const u2v*)(P.p2 + rs * (K >> 5) * 2) + b0 / kGB;
     }
-    // xt slab s of this thread: tile q / 4, 256-uint4 part q % 4
-    auto xt_at = [&](int s, int q) {
-        return xt + (int64_t)(q / 4) * nb * 128 + (int64_t)s * kSB * 128 + (q % 4) * kBlock + tid;
+    // slab step s: element e of the step is part e / XSB, tile (e % XSB) / (SB * 128)
+    auto xt_el = [&](int st, int e) {
+        const int p = e / XSB, r = e - p * XSB;
+        const int t = r / (SB * 128), w = r - t * (SB * 128);
+        return xt + (int64_t)t * nb * 128 + (int64_t)(p * nbp + st * SB) * 128 + w;
     };
 
     u4v xr[XPT];
 #pragma unroll
-    for (int q = 0; q < XPT; q++) xr[q] = *xt_at(0, q);
-    u4v wr[kPG];
-    u2v sr[kPG][4];
+    for (int q = 0; q < XPT; q++) {
+        const int e = q * NT + tid;
+        if (XALL % NT == 0 || e < XALL) xr[q] = *xt_el(0, e);
+    }
+    u4v wr[RING];
+    u2v sr[RING][4];
 #pragma unroll
-    for (int t = 0; t < kPG; t++) {
+    for (int t = 0; t < kPGv2; t++) {
         const int tc = t < ngroups ? t : ngroups - 1;
         wr[t] = wq[kGB * tc + g];
 #pragma unroll
         for (int v = 0; v < 4; v++) sr[t][v] = sq[v][tc];
     }
 #pragma unroll
-    for (int q = 0; q < XPT; q++) lds[q * kBlock + tid] = xr[q];
+    for (int q = 0; q < XPT; q++) {
+        const int e = q * NT + tid;
+        if (XALL % NT == 0 || e < XALL) lds[e] = xr[q];
+    }
     __syncthreads();
 
     f4v acc[TT];
@@ -189,29 +214,33 @@ void gemv_mfma_q45_kernel(DevPlanes P, int64_t N, int K,
     for (int tt = 0; tt < TT; tt++) acc[tt] = f4v{0.f, 0.f, 0.f, 0.f};
     const f4v zero = {0.f, 0.f, 0.f, 0.f};
 
-    for (int s0 = 0; s0 < nslab; s0 += kUS) {
-        static_for<0, kUS>([&](auto su_c) {
+    for (int s0 = 0; s0 < nslab; s0 += kUSv) {
+        static_for<0, kUSv>([&](auto su_c) {
             constexpr int su = decltype(su_c)::value;
-            const int s = s0 + su;
+            const int st = s0 + su;
             constexpr int buf = su & 1;
-            // next slab of xt (the last one reloads itself; it is not stored)
-            const int sn = s + 1 < nslab ? s + 1 : s;
+            // next slab step (the last one reloads itself; it is not stored)
+            const int sn = st + 1 < nslab ? st + 1 : st;
 #pragma unroll
-            for (int q = 0; q < XPT; q++) xr[q] = *xt_at(sn, q);
-            static_for<0, kSB / kGB>([&](auto tg_c) {
+            for (int q = 0; q < XPT; q++) {
+                const int e = q * NT + tid;
+                if (XALL % NT == 0 || e < XALL) xr[q] = *xt_el(sn, e);
+            }
+            static_for<0, GPS>([&](auto tg_c) {
                 constexpr int tg = decltype(tg_c)::value;
-                constexpr int tl = su * (kSB / kGB) + tg;        // ring slot
-                const int t = s * (kSB / kGB) + tg;              // weight group
+                constexpr int tl = (su * GPS + tg) % RING;          // ring slot
+                constexpr int tf = (su * GPS + tg + kPGv2) % RING;  // slot of the group kPG ahead
+                const int t = st * GPS + tg;                        // weight group
                 // transpose: lane (i, g) holds block 4t + g of row i; each
                 // MFMA needs dword g of one block from every lane of row i
                 *(u4v*)(scr + i * kScrStride + 4 * g) = wr[tl];
                 u2v sc[4];
 #pragma unroll
                 for (int v = 0; v < 4; v++) sc[v] = sr[tl][v];
-                const int tn = t + kPG < ngroups ? t + kPG : ngroups - 1;
-                wr[tl] = wq[kGB * tn + g];
+                const int tn = t + kPGv2 < ngroups ? t + kPGv2 : ngroups - 1;
+                wr[tf] = wq[kGB * tn + g];
 #pragma unroll
-                for (int v = 0; v < 4; v++) sr[tl][v] = sq[v][tn];
+                for (int v = 0; v < 4; v++) sr[tf][v] = sq[v][tn];
 #pragma unroll
                 for (int b4 = 0; b4 < kGB; b4++) {
                     const h8 a = codes_to_a(scr[i * kScrStride + 4 * b4 + g]);
@@ -219,10 +248,10 @@ void gemv_mfma_q45_kernel(DevPlanes P, int64_t N, int K,
 #pragma unroll
                     for (int v = 0; v < 4; v++)
                         sv[v] = h2f((b4 < 2 ? sc[v].x : sc[v].y) >> (16 * (b4 & 1)));
-                    const int lb = tg * kGB + b4;                // block within the slab
+                    const int lb = tg * kGB + b4;                   // block within the slab
 #pragma unroll
                     for (int tt = 0; tt < TT; tt++) {
-                        const u4v* bp = lds + buf * XSB + (tt * kSB + lb) * 128;
+                        const u4v* bp = lds + buf * XALL + part * XSB + (tt * SB + lb) * 128;
                         const h8 bh = __builtin_bit_cast(h8, bp[lane]);
                         const h8 bl = __builtin_bit_cast(h8, bp[64 + lane]);
                         f4v d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bh, zero, 0, 0, 0);
@@ -233,9 +262,32 @@ void gemv_mfma_q45_kernel(DevPlanes P, int64_t N, int K,
                 }
             });
 #pragma unroll
-            for (int q = 0; q < XPT; q++) lds[(buf ^ 1) * XSB + q * kBlock + tid] = xr[q];
+            for (int q = 0; q < XPT; q++) {
+                const int e = q * NT + tid;
+                if (XALL % NT == 0 || e < XALL) lds[(buf ^ 1) * XALL + e] = xr[q];
+            }
             __syncthreads();
         });
+    }
+
+    // K parts 1 .. S-1 leave their tiles in LDS (the slab area is free now);
+    // part 0 adds them in part order.
+    f4v* red = (f4v*)lds;                              // [S - 1][TR][TT][64]
+    if constexpr (S > 1) {
+        if (part > 0) {
+#pragma unroll
+            for (int tt = 0; tt < TT; tt++) red[(((part - 1) * TR + tr) * TT + tt) * kWave + lane] = acc[tt];
+        }
+        __syncthreads();
+        if (part > 0) return;
+#pragma unroll
+        for (int q = 1; q < S; q++)
+#pragma unroll
+            for (int tt = 0; tt < TT; tt++) {
+                const f4v o = red[(((q - 1) * TR + tr) * TT + tt) * kWave + lane];
+#pragma unroll
+                for (int v = 0; v < 4; v++) acc[tt][v] += o[v];
+            }
     }
 
     // lane j + 16 g holds rows 4g + v of token column j
@@ -257,21 +309,56 @@ void gemv_mfma_q45_kernel(DevPlanes P, int64_t N, int K,
     }
 }
 
-template <int TT>
-static hipError_t launch_mfma_tt(DevPlanes P, int64_t N, int64_t K, const u4v* xt,
-                                 const float* ts, int M, float* y, int64_t ldy, int accumulate,
-                                 hipStream_t stream) {
-    const size_t lds = (size_t)2 * TT * kSB * 128 * 16 + (size_t)kWavesPerBlock * 16 * kScrStride * 4;
-    auto kern = gemv_mfma_q45_kernel<TT>;
+template <int TT, int TR, int S, int SB>
+static hipError_t launch_mfma_k(DevPlanes P, int64_t N, int64_t K, const u4v* xt, const float* ts,
+                                int M, float* y, int64_t ldy, int accumulate, hipStream_t stream) {
+    const size_t lds = (size_t)2 * S * TT * SB * 128 * 16 + (size_t)TR * S * 16 * kScrStride * 4;
+    auto kern = gemv_mfma_q45_kernel<TT, TR, S, SB>;
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute((const void*)kern,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    const int64_t grid = (N + 63) / 64;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBlock), lds, stream, P, N, (int)K, xt, ts,
-                       M, y, ldy, accumulate);
+    const int64_t grid = (N + 16 * TR - 1) / (16 * TR);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kWave * TR * S), lds, stream, P, N, (int)K,
+                       xt, ts, M, y, ldy, accumulate);
     return hipGetLastError();
+}
+
+// K parts and slab size (LDS: 2 * S * TT * SB * 2 KB <= 128 KB): one or two
+// token tiles take S = 4 parts when a workgroup has at most two row tiles,
+// else 2; three or four token tiles take 2; K = 1024 (32 blocks) takes 2.
+// MBQ_MFMA_S = 2 forces two parts (tuning sweeps).
+template <int TT, int TR>
+static hipError_t launch_mfma_tr(DevPlanes P, int64_t N, int64_t K, const u4v* xt, const float* ts,
+                                 int M, float* y, int64_t ldy, int accumulate, hipStream_t s) {
+    bool four = TT <= 2 && TR <= 2 && (K / 32) % 64 == 0;
+    if (const char* e = getenv("MBQ_MFMA_S")) four = TT <= 2 && (K / 32) % 64 == 0 && atoi(e) == 4;
+    if constexpr (TT == 1) {
+        if (four) return launch_mfma_k<1, TR, 4, 8>(P, N, K, xt, ts, M, y, ldy, accumulate, s);
+        return launch_mfma_k<1, TR, 2, 8>(P, N, K, xt, ts, M, y, ldy, accumulate, s);
+    } else if constexpr (TT == 2) {
+        if (four) return launch_mfma_k<2, TR, 4, 4>(P, N, K, xt, ts, M, y, ldy, accumulate, s);
+        return launch_mfma_k<2, TR, 2, 4>(P, N, K, xt, ts, M, y, ldy, accumulate, s);
+    } else {
+        return launch_mfma_k<TT, TR, 2, 4>(P, N, K, xt, ts, M, y, ldy, accumulate, s);
+    }
+}
+
+// Row tiles per workgroup, from sweeps on MI355X (N = 4096 and 12288): one
+// workgroup per 192 tiles' worth of rows for one or two token tiles, per 128
+// for more, at most 4 (three would spill at 768 threads); MBQ_MFMA_TR
+// overrides (tuning sweeps).
+template <int TT>
+static hipError_t launch_mfma_tt(DevPlanes P, int64_t N, int64_t K, const u4v* xt, const float* ts,
+                                 int M, float* y, int64_t ldy, int accumulate, hipStream_t s) {
+    int64_t tr = TT <= 2 ? N / (16 * 192) : N / (16 * 128);
+    if (const char* e = getenv("MBQ_MFMA_TR")) tr = atoi(e);
+    switch (tr <= 1 ? 1 : tr == 2 ? 2 : 4) {
+    case 1: return launch_mfma_tr<TT, 1>(P, N, K, xt, ts, M, y, ldy, accumulate, s);
+    case 2: return launch_mfma_tr<TT, 2>(P, N, K, xt, ts, M, y, ldy, accumulate, s);
+    default: return launch_mfma_tr<TT, 4>(P, N, K, xt, ts, M, y, ldy, accumulate, s);
+    }
 }
 
 // Tokens in groups of 64 (four tiles) per launch.
