@@ -429,7 +429,8 @@ static int check_decode(const mbq_decode_model* m, const char* fn) {
     return MBQ_OK;
 }
 
-// Workspace of the decode step: [0, 256) barrier counter and status word;
+// Workspace of the decode step: [0, 2048) the one-launch step's barrier
+// counters (global at 0, group g at 128 (g + 1)) and status word (at 4);
 // then q|k|v, the gated activations, and the layer table of the one-launch
 // step.
 struct DecodeLayout {
@@ -438,7 +439,7 @@ struct DecodeLayout {
 
 static DecodeLayout decode_layout(const mbq_decode_model* m) {
     DecodeLayout L;
-    L.qkv = 256;
+    L.qkv = 2048;
     L.m = L.qkv + align256((size_t)(m->dq + 2 * m->dkv) * 4);
     L.table = L.m + align256((size_t)m->f * 4);
     L.total = L.table + align256(offsetof(mbq::DecTable, layers) +

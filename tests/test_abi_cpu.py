@@ -267,7 +267,7 @@ def test_decode_argument_checks():
     assert L.mbq_decode_workspace_bytes(ctypes.byref(m), ctypes.byref(nb)) == _lib.OK
     # status words, q|k|v, gated activations, then the one-launch step's layer table
     table = 32 + 1 * 152
-    assert nb.value == 256 + (4096 + 2048) * 4 + 12288 * 4 + (table + 255) // 256 * 256
+    assert nb.value == 2048 + (4096 + 2048) * 4 + 12288 * 4 + (table + 255) // 256 * 256
     h, lg, ws = BASE + 0x7000000000, BASE + 0x7100000000, BASE + 0x7200000000
     st = lambda m, h=h, lg=lg, ws=ws, n=nb.value: L.mbq_decode_step(ctypes.byref(m), h, lg, ws, n, None)
     assert st(m, n=nb.value - 1) == _lib.EINVAL                             # workspace too small
