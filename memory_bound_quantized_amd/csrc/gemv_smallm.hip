@@ -54,7 +54,11 @@ static int slice_steps(int64_t K, int C) {
     return C;
 }
 
-template <int FMT, int R, int M, bool XQ>
+// Chunk steps of weight loads in flight per wave (four measured 4-8 %
+// slower than two at M = 2..8: more registers, no more bandwidth).
+constexpr int kSmDepth = 2;
+
+template <int FMT, int R, int M, bool XQ, int PD = kSmDepth>
 __global__ __launch_bounds__(kSmBlock) void gemv_smallm_kernel(DevPlanes P, int64_t N, int K,
                                                                const void* __restrict__ xsrc,
                                                                int64_t ldx, float* __restrict__ y,
@@ -106,9 +110,9 @@ __global__ __launch_bounds__(kSmBlock) void gemv_smallm_kernel(DevPlanes P, int6
             set_rows(lg);
         }
     };
-    SlotM<FMT, R> buf[2];
-    next_load(buf[0]);
-    next_load(buf[1]);
+    SlotM<FMT, R> buf[PD];
+#pragma unroll
+    for (int d = 0; d < PD; d++) next_load(buf[d]);
 
     // ---- x of every token into LDS, in rounds of 4 pieces per thread
     auto xrow = [&](int m) {
@@ -188,9 +192,9 @@ __global__ __launch_bounds__(kSmBlock) void gemv_smallm_kernel(DevPlanes P, int6
 
     const int total = G * C;
     int cg = 0, cc = 0;
-    for (int j = 0; j < total; j += 2) {
+    for (int j = 0; j < total; j += PD) {
 #pragma unroll
-        for (int d = 0; d < 2; d++) {
+        for (int d = 0; d < PD; d++) {
             if (j + d < total) {
                 compute(buf[d], cc);
                 next_load(buf[d]);
