@@ -20,12 +20,19 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_vec_kernel(const float* x,
     const int64_t row = blockIdx.x;
     const int n4 = n >> 2;
     const float4* xr = (const float4*)(x + row * n);
-    float4 v[VEC];
-    float ss = 0.f;
+    const float4* g4 = (const float4*)gamma;
+    // gamma is requested with x, so no memory round trip follows the
+    // block-wide sum on the single-row critical path
+    float4 v[VEC], g[VEC];
 #pragma unroll
     for (int i = 0; i < VEC; i++) {
         const int f = i * kBlock + (int)threadIdx.x;
         v[i] = f < n4 ? xr[f] : make_float4(0.f, 0.f, 0.f, 0.f);
+        g[i] = f < n4 ? g4[f] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < VEC; i++) {
         ss = fmaf(v[i].x, v[i].x, ss);
         ss = fmaf(v[i].y, v[i].y, ss);
         ss = fmaf(v[i].z, v[i].z, ss);
@@ -34,15 +41,12 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_vec_kernel(const float* x,
     const float tot = block_sum(ss, red);
     const float inv = 1.0f / sqrtf(tot / (float)n + eps);
     float4* yr = (float4*)(y + row * n);
-    const float4* g4 = (const float4*)gamma;
 #pragma unroll
     for (int i = 0; i < VEC; i++) {
         const int f = i * kBlock + (int)threadIdx.x;
-        if (f < n4) {
-            const float4 g = g4[f];
-            yr[f] = make_float4(g.x * (v[i].x * inv), g.y * (v[i].y * inv), g.z * (v[i].z * inv),
-                                g.w * (v[i].w * inv));
-        }
+        if (f < n4)
+            yr[f] = make_float4(g[i].x * (v[i].x * inv), g[i].y * (v[i].y * inv),
+                                g[i].z * (v[i].z * inv), g[i].w * (v[i].w * inv));
     }
 }
 
