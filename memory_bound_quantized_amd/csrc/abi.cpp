@@ -120,18 +120,18 @@ mbq::DevPlanes planes_of(const mbq_qweight* W) {
                           (const uint8_t*)W->scales, (const uint8_t*)W->super_scales};
 }
 
-// Optional geometry overrides for tuning sweeps, read at every call:
+// Optional geometry overrides for tuning sweeps (with MBQ_TUNING set):
 // MBQ_GEMV_ROWS = 1, 2 or 4 rows per wave; MBQ_GEMV_GROUPS = row groups per
 // wave.
 bool geom_override(mbq::GemvGeom* g) {
     bool any = false;
-    const char* s = getenv("MBQ_GEMV_ROWS");
+    const char* s = mbq::tuning_var("MBQ_GEMV_ROWS");
     int r = 0;
     if (s && sscanf(s, "%d", &r) == 1 && (r == 1 || r == 2 || r == 4)) {
         g->rows_per_wave = r;
         any = true;
     }
-    const char* t = getenv("MBQ_GEMV_GROUPS");
+    const char* t = mbq::tuning_var("MBQ_GEMV_GROUPS");
     int gg = 0;
     if (t && sscanf(t, "%d", &gg) == 1 && gg >= 1 && gg <= 64) {
         g->groups = gg;
@@ -140,16 +140,16 @@ bool geom_override(mbq::GemvGeom* g) {
     return any;
 }
 
-// Small-batch geometry: defaults, or MBQ_SMALLM_ROWS (1 or 2) and
-// MBQ_SMALLM_GROUPS for tuning sweeps; an override that does not fit the
+// Small-batch geometry: defaults, or (with MBQ_TUNING set) MBQ_SMALLM_ROWS
+// (1 to 3) and MBQ_SMALLM_GROUPS; an override that does not fit the
 // kernel's row-sum buffer is ignored.
 mbq::GemvGeom smallm_geom(int fmt, int64_t M, int64_t N) {
     mbq::GemvGeom g = mbq::gemv_smallm_default_geom(fmt, M, N);
     mbq::GemvGeom o = g;
     int v = 0;
-    const char* s = getenv("MBQ_SMALLM_ROWS");
+    const char* s = mbq::tuning_var("MBQ_SMALLM_ROWS");
     if (s && sscanf(s, "%d", &v) == 1) o.rows_per_wave = v;
-    const char* t = getenv("MBQ_SMALLM_GROUPS");
+    const char* t = mbq::tuning_var("MBQ_SMALLM_GROUPS");
     if (t && sscanf(t, "%d", &v) == 1) o.groups = v;
     return mbq::gemv_smallm_geom_ok(M, o) ? o : g;
 }

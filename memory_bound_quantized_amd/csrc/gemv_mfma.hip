@@ -333,7 +333,7 @@ template <int TT, int TR>
 static hipError_t launch_mfma_tr(DevPlanes P, int64_t N, int64_t K, const u4v* xt, const float* ts,
                                  int M, float* y, int64_t ldy, int accumulate, hipStream_t s) {
     bool four = TT <= 2 && TR <= 2 && (K / 32) % 64 == 0;
-    if (const char* e = getenv("MBQ_MFMA_S")) four = TT <= 2 && (K / 32) % 64 == 0 && atoi(e) == 4;
+    if (const char* e = tuning_var("MBQ_MFMA_S")) four = TT <= 2 && (K / 32) % 64 == 0 && atoi(e) == 4;
     if constexpr (TT == 1) {
         if (four) return launch_mfma_k<1, TR, 4, 8>(P, N, K, xt, ts, M, y, ldy, accumulate, s);
         return launch_mfma_k<1, TR, 2, 8>(P, N, K, xt, ts, M, y, ldy, accumulate, s);
@@ -353,7 +353,7 @@ template <int TT>
 static hipError_t launch_mfma_tt(DevPlanes P, int64_t N, int64_t K, const u4v* xt, const float* ts,
                                  int M, float* y, int64_t ldy, int accumulate, hipStream_t s) {
     int64_t tr = TT <= 2 ? N / (16 * 192) : N / (16 * 128);
-    if (const char* e = getenv("MBQ_MFMA_TR")) tr = atoi(e);
+    if (const char* e = tuning_var("MBQ_MFMA_TR")) tr = atoi(e);
     switch (tr <= 1 ? 1 : tr == 2 ? 2 : 4) {
     case 1: return launch_mfma_tr<TT, 1>(P, N, K, xt, ts, M, y, ldy, accumulate, s);
     case 2: return launch_mfma_tr<TT, 2>(P, N, K, xt, ts, M, y, ldy, accumulate, s);

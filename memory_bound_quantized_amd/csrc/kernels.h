@@ -1,7 +1,8 @@
 // kernels.h -- internal launchers of libmbq (not part of the C ABI).
 // Every launcher enqueues on `stream` and returns hipGetLastError() after the
-// launch.  Arguments have been validated by the C-ABI layer (mbq_abi.cpp).
+// launch.  Arguments have been validated by the C-ABI layer (abi.cpp).
 #pragma once
+#include <cstdlib>
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -30,6 +31,15 @@ struct GemvGeom {
 };
 
 GemvGeom gemv_m1_default_geom(int fmt, int64_t N, int64_t K, bool pairs = false);
+
+// Geometry overrides for tuning sweeps (MBQ_GEMV_*, MBQ_SMALLM_*, MBQ_MFMA_*)
+// are read at each call only when MBQ_TUNING is set when the library first
+// asks; otherwise no environment variable is read.
+inline bool tuning_env() {
+    static const bool on = getenv("MBQ_TUNING") != nullptr;
+    return on;
+}
+inline const char* tuning_var(const char* name) { return tuning_env() ? getenv(name) : nullptr; }
 
 // y[n] (+)= W[row(n)] . x for n < N_out.  If gidx != nullptr the output row
 // n maps to weight row gidx[n / rpe] * rpe + n % rpe (gathered experts).
