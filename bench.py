@@ -40,6 +40,7 @@ sys.path.insert(0, ROOT)
 METRIC = "achieved HBM GB/s (% of peak) for M=1 4.5-bpw GEMV; µs per 4096 RMSNorm row"
 PEAK_HBM_GBS = 8000.0           # MI355X published HBM3E bandwidth
 ROTATION_BYTES = 1 << 30        # >= 4x the 256 MB Infinity Cache
+MEASURED_READ_PEAK_GBS = 6080.0  # 4 GiB read on MI355X; the full run measures it live
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_m1.json")
 KERNEL_SOURCES = ["formats.h", "gemv_m1.hip", "staging.h", "device_common.h"]
 
@@ -245,6 +246,30 @@ def rotated(W0, min_bytes=ROTATION_BYTES):
     return [W0] + [W0.clone() for _ in range(n - 1)]
 
 
+def decode_row(workloads, torch, dev, read_peak, ntok=20):
+    """Workload 3: ms per token of the 36-layer step, one HIP graph per token."""
+    from memory_bound_quantized_amd.decode import DecodeModel
+    c3 = workloads.config3()
+    model = DecodeModel(c3["layers"], c3["vocab"], c3["g1"], c3["g2"], c3["gf"], c3["eps"])
+    del c3["layers"]
+    h = torch.from_numpy(c3["h0"]).to(dev)
+    logits = torch.empty(model.vocab, device=dev)
+    g = capture(lambda: model.step(h, logits))
+    g.replay()
+    ms = timed(g, ntok) / ntok
+    B = model.weight_bytes + 4 * 36 * 2 * model.d + 4 * model.d
+    B_all = B + 4 * (36 * (model.dq + 2 * model.dkv + model.f + 6 * model.d) + model.vocab)
+    floor_ms = B / (read_peak * 1e9) * 1e3
+    row = {"ms_per_token": round(ms, 4), "tokens_per_s": round(1e3 / ms, 1),
+           "weight_bytes": model.weight_bytes, "bytes_per_token": int(B_all),
+           "gbs": round(B_all / (ms * 1e-3) / 1e9, 1),
+           "floor_ms_at_read_peak": round(floor_ms, 4), "ratio_to_floor": round(ms / floor_ms, 3),
+           "launches_per_token": 4 * 36 + 1, "tokens_timed": ntok}
+    del model, g
+    torch.cuda.empty_cache()
+    return row
+
+
 def rows_bench(mbq, workloads, torch, dev, read_peak):
     """Every other step of the hot path, each on cold weights."""
     from memory_bound_quantized_amd.decode import DecodeModel, interleave_rows, concat_rows
@@ -346,26 +371,7 @@ def rows_bench(mbq, workloads, torch, dev, read_peak):
     torch.cuda.empty_cache()
 
     # ---- workload 3: one token through the 36-layer stream
-    c3 = workloads.config3()
-    model = DecodeModel(c3["layers"], c3["vocab"], c3["g1"], c3["g2"], c3["gf"], c3["eps"])
-    del c3["layers"]
-    h = torch.from_numpy(c3["h0"]).to(dev)
-    logits = torch.empty(model.vocab, device=dev)
-    g = capture(lambda: model.step(h, logits))
-    g.replay()
-    ntok = 20
-    ms = timed(g, ntok) / ntok
-    B = model.weight_bytes + 4 * 36 * 2 * model.d + 4 * model.d
-    B_all = B + 4 * (36 * (model.dq + 2 * model.dkv + model.f + 6 * model.d) + model.vocab)
-    floor_ms = B / (read_peak * 1e9) * 1e3
-    rows["decode_36_layers"] = {
-        "ms_per_token": round(ms, 4), "tokens_per_s": round(1e3 / ms, 1),
-        "weight_bytes": model.weight_bytes, "bytes_per_token": int(B_all),
-        "gbs": round(B_all / (ms * 1e-3) / 1e9, 1),
-        "floor_ms_at_read_peak": round(floor_ms, 4), "ratio_to_floor": round(ms / floor_ms, 3),
-        "launches_per_token": 4 * 36 + 1}
-    del model, g
-    torch.cuda.empty_cache()
+    rows["decode_36_layers"] = decode_row(workloads, torch, dev, read_peak)
     return rows
 
 
@@ -378,6 +384,8 @@ def main():
     ap.add_argument("--no-rows", action="store_true", help="headline step only")
     ap.add_argument("--traffic-pass", action="store_true",
                     help="only the launches that the counter runs profile")
+    ap.add_argument("--decode-only", type=int, metavar="TOKENS", default=0,
+                    help="only the 36-layer decode step, TOKENS graph replays (for profiling)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc outputs into the traffic file")
     args = ap.parse_args()
@@ -399,6 +407,11 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    if args.decode_only:
+        torch.cuda.set_device(dev)
+        print(json.dumps({"decode_36_layers": decode_row(workloads, torch, dev, MEASURED_READ_PEAK_GBS,
+                                                          ntok=args.decode_only)}))
+        return
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
 
