@@ -7,6 +7,11 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+# The library reads its geometry overrides only if MBQ_TUNING is set when it
+# first asks; set here, before any test loads it, so that the geometry tests
+# can run every kernel shape.  Without override variables nothing changes.
+os.environ.setdefault("MBQ_TUNING", "1")
+
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
