@@ -332,11 +332,7 @@ static hipError_t launch_k(const M1Args& a, hipStream_t stream) {
     const int64_t grid = (a.N + rows_per_wg - 1) / rows_per_wg;
     const size_t lds = (size_t)(a.K / T::WPC) * Stride<FMT>::DW * 4;
     auto kern = gemv_m1_kernel<FMT, R, CS, GATHER, XQ, PRO, EPI>;
-    if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
+    if (hipError_t e = ensure_lds<gemv_m1_kernel<FMT, R, CS, GATHER, XQ, PRO, EPI>>(lds)) return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBlock * k_slices(CS)), lds, stream, a.P, a.N, (int)a.K,
                        a.x, a.y, a.accumulate, a.gidx, (int)a.rpe, a.gamma, a.eps, G, a.nw);
     return hipGetLastError();

@@ -314,11 +314,7 @@ static hipError_t launch_mfma_k(DevPlanes P, int64_t N, int64_t K, const u4v* xt
                                 int M, float* y, int64_t ldy, int accumulate, hipStream_t stream) {
     const size_t lds = (size_t)2 * S * TT * SB * 128 * 16 + (size_t)TR * S * 16 * kScrStride * 4;
     auto kern = gemv_mfma_q45_kernel<TT, TR, S, SB>;
-    if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
+    if (hipError_t e = ensure_lds<gemv_mfma_q45_kernel<TT, TR, S, SB>>(lds)) return e;
     const int64_t grid = (N + 16 * TR - 1) / (16 * TR);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kWave * TR * S), lds, stream, P, N, (int)K,
                        xt, ts, M, y, ldy, accumulate);

@@ -230,11 +230,7 @@ static hipError_t launch_sk(DevPlanes P, int64_t N, int64_t K, const void* x, in
     const int nchunks = (int)(K / Traits<FMT>::WPC);
     const int sl = slice_steps<FMT>(K, (nchunks + kWave - 1) / kWave);
     auto kern = gemv_smallm_kernel<FMT, R, M, XQ>;
-    if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
+    if (hipError_t e = ensure_lds<gemv_smallm_kernel<FMT, R, M, XQ>>(lds)) return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kSmBlock), lds, stream, P, N, (int)K, x, ldx,
                        y, ldy, accumulate, G, sl);
     return hipGetLastError();

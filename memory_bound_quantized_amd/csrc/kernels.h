@@ -2,6 +2,7 @@
 // Every launcher enqueues on `stream` and returns hipGetLastError() after the
 // launch.  Arguments have been validated by the C-ABI layer (abi.cpp).
 #pragma once
+#include <atomic>
 #include <cstdlib>
 
 #include <hip/hip_runtime.h>
@@ -40,6 +41,23 @@ inline bool tuning_env() {
     return on;
 }
 inline const char* tuning_var(const char* name) { return tuning_env() ? getenv(name) : nullptr; }
+
+// Dynamic LDS above 64 KB needs the kernel's attribute raised first; each
+// kernel remembers the largest size it was given, so the call is made only
+// when a launch needs more than any before it.
+template <auto KERN>
+hipError_t ensure_lds(size_t lds) {
+    static std::atomic<size_t> have{65536};
+    if (lds <= have.load(std::memory_order_relaxed)) return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute((const void*)KERN,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e == hipSuccess) {
+        size_t h = have.load(std::memory_order_relaxed);
+        while (h < lds && !have.compare_exchange_weak(h, lds, std::memory_order_relaxed)) {
+        }
+    }
+    return e;
+}
 
 // y[n] (+)= W[row(n)] . x for n < N_out.  If gidx != nullptr the output row
 // n maps to weight row gidx[n / rpe] * rpe + n % rpe (gathered experts).
