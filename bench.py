@@ -12,8 +12,9 @@ Every other step of the hot path is measured in the same run, in the same way
 (graph replays, cold weights), under "rows":
   * RMSNorm of one 4096 row (us per row) and the bf16 512 x 4096 product;
   * M = 1 products at each decode table shape, fused forms included;
-  * small batches M = 1 .. 64 of the 12288 x 4096 Q45 table (vector units to
-    M = 8, matrix cores from M = 16);
+  * small batches M = 1 .. 64 of the 12288 x 4096 Q45 table (staged x on the
+    vector units below M = 6, on the matrix cores from M = 6; fp32 x on the
+    vector units up to M = 8);
   * 8 gathered Q25 experts of 1536 x 4096; LayerNorm of 4096 rows of 2048;
   * one token through the 36-layer decode stream (ms per token, tokens/s,
     against the measured read ceiling).
@@ -319,7 +320,7 @@ def rows_bench(mbq, workloads, torch, dev, read_peak):
 
     # ---- small batches of the 12288 x 4096 Q45 table
     small = {}
-    for M in (1, 2, 4, 8, 16, 64):
+    for M in (1, 2, 4, 6, 8, 16, 64):
         c4 = workloads.config4(M)
         fmt, N, K, planes = c4["W"]
         Ws = rotated(mbq.QWeight.from_host(fmt, N, K, planes))
@@ -333,14 +334,16 @@ def rows_bench(mbq, workloads, torch, dev, read_peak):
         b = Ws[0].nbytes + 4 * M * (N + K)
         ent = {"stage_plus_product_us": round(step_us, 3), "product_us": round(kern_us, 3),
                "us_per_token": round(step_us / M, 3), "product_gbs": gbs(b, kern_us),
-               "path": "matrix cores" if M >= 16 else "vector units"}
+               "path": "matrix cores" if M >= 6 else "vector units"}
         if fp32_us is not None:
             ent["fp32_x_us"] = round(fp32_us, 3)
-        if M >= 16:
+        if M >= 6:
             tf = 2.0 * M * N * K / (kern_us * 1e-6) / 1e12
             ent["useful_tflops"] = round(tf, 2)
-            # two fp16 MFMAs (x high and low parts) per block: issued rate vs the 2.5 PF/s fp16 peak
-            ent["mfma_busy_frac_of_fp16_peak"] = round(2 * tf / 2500.0, 4)
+            # issued: 16-token tiles, two fp16 MFMAs (x high and low parts) per
+            # block, against the 2.5 PF/s fp16 peak
+            issued = 16 * ((M + 15) // 16)
+            ent["mfma_busy_frac_of_fp16_peak"] = round(2 * tf * issued / M / 2500.0, 4)
         small["M%d" % M] = ent
         del Ws
         torch.cuda.empty_cache()

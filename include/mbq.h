@@ -134,7 +134,8 @@ int mbq_unpack(int fmt, int64_t N, int64_t K, const void* const planes[4],
  * is unspecified.  Tokens run on the vector units, up to 8 per launch (as many
  * as fit staged in LDS: all 8 for K = 4096, 2 for K = 12288), each weight
  * read once per launch and unpacked once for all its tokens.  Matrix cores
- * take Q45 batches of 16 or more through mbq_stage_x + mbq_gemv_xq.
+ * take Q45 batches through mbq_stage_x + mbq_gemv_xq (from 16 tokens, and
+ * from 6 when K % 1024 == 0).
  * MBQ_EUNSUPPORTED for shapes without a kernel (K > 32768, or K > 16384 for
  * BF16; Q25 with K % 64 != 0; BF16 with K % 8 != 0).  M == 0 or N == 0
  * enqueue nothing; K == 0 writes zeros (or leaves y for accumulate = 1). */
@@ -262,15 +263,18 @@ int mbq_decode_step_persistent(const mbq_decode_model* model, float* h, float* l
  * the sums busy").  The form is opaque and format-specific: stage for the
  * format of the matrix that consumes it.  It takes 4 bytes per value
  * (mbq_xq_bytes), rows back to back; for BF16 it is x itself in fp32.
- * For Q45 with M >= 16 tokens it is the matrix-core tile form instead: per
+ * For Q45 with M >= 16 tokens, or 6 <= M < 16 and K % 1024 == 0, it is the
+ * matrix-core tile form instead (one 16-token tile outruns the vector units
+ * from about 6 tokens on MI355X): per
  * tile of 16 tokens and block of 32 values, each token scaled by a power of
  * two (its largest |x| in [2^14, 2^15)) and split into fp16 high and low
  * parts in the MFMA operand order, then one float 2^-e per token slot
  * (mbq_xq_bytes gives its size; it needs K % 1024 == 0).
  */
 
-/* Bytes of staged x for M rows of K values: 4*M*K, or for Q45 with M >= 16
- * ceil(M/16) * (K/32 * 2048 + 64).  Host only.  MBQ_EINVAL for an unknown
+/* Bytes of staged x for M rows of K values: 4*M*K, or for the Q45 tile form
+ * (M >= 16, or 6 <= M < 16 with K % 1024 == 0) ceil(M/16) * (K/32 * 2048 + 64).
+ * Host only.  MBQ_EINVAL for an unknown
  * format or K not a multiple of the chunk (32; Q25 64; BF16 8). */
 int mbq_xq_bytes(int fmt, int64_t M, int64_t K, size_t* bytes);
 
@@ -282,7 +286,7 @@ int mbq_stage_x(int fmt, const float* x, int64_t M, int64_t ldx, int64_t K, void
 
 /* mbq_gemv_q with x given in staged form (staged for W->fmt, M rows of K):
  * the same products, sums and limits.  With the row form the result is bit
- * for bit mbq_gemv_q's on the same x.  Q45 with M >= 16 (tile form) runs on
+ * for bit mbq_gemv_q's on the same x.  Q45 in the tile form runs on
  * the matrix cores ([roofline-holds] "The Math": past M* the sums, not the
  * bytes, bound the product): fp16 (q - 8) codes, which are exact, against
  * the fp16 high and low parts of x, fp32 results, each block's scale applied

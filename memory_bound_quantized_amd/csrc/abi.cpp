@@ -103,7 +103,13 @@ int check_kernel_shape(const mbq_qweight* W, const char* fn) {
 }
 
 // Staged x of M >= 16 Q45 tokens takes the matrix-core tile form.
-bool xq_tiled(int fmt, int64_t M) { return fmt == MBQ_FMT_Q45 && M >= 16; }
+// Staged x takes the matrix-core tile form for Q45 batches from 16 tokens,
+// and from 6 tokens where the matrix-core kernel takes the shape (K % 1024
+// == 0): on MI355X one 16-token tile (19.7 us on 12288 x 4096) beats the
+// vector units from about 6 tokens (M = 6: 22 us, M = 8: 29 us).
+bool xq_tiled(int fmt, int64_t M, int64_t K) {
+    return fmt == MBQ_FMT_Q45 && (M >= 16 || (M >= 6 && K % 1024 == 0));
+}
 
 // Values per chunk of staged x (the unit of its fixed-point exponent).
 int64_t xq_chunk(int fmt) {
@@ -610,7 +616,7 @@ int mbq_xq_bytes(int fmt, int64_t M, int64_t K, size_t* bytes) {
     if (K % xq_chunk(fmt))
         return fail(MBQ_EINVAL, "%s: K=%lld is not a multiple of %lld", fn, (long long)K,
                     (long long)xq_chunk(fmt));
-    *bytes = xq_tiled(fmt, M) ? (size_t)mbq::xt_bytes(M, K) : (size_t)M * (size_t)K * 4;
+    *bytes = xq_tiled(fmt, M, K) ? (size_t)mbq::xt_bytes(M, K) : (size_t)M * (size_t)K * 4;
     return ok();
 }
 
@@ -629,7 +635,7 @@ int mbq_stage_x(int fmt, const float* x, int64_t M, int64_t ldx, int64_t K, void
         return fail(MBQ_EALIGN, "%s: x and xq must be 16-byte aligned with ldx %% 4 == 0", fn);
     if (overlaps(x, (size_t)((M - 1) * ldx + K) * 4, xq, xqb))
         return fail(MBQ_EINVAL, "%s: x and xq overlap", fn);
-    if (xq_tiled(fmt, M)) {
+    if (xq_tiled(fmt, M, K)) {
         if (K % 1024) return fail(MBQ_EUNSUPPORTED, "%s: the tile form needs K %% 1024 == 0", fn);
         return hip_status(mbq::launch_stage_x_mfma(x, M, ldx, K, xq, (hipStream_t)stream), fn);
     }
@@ -654,7 +660,7 @@ int mbq_gemv_xq(const mbq_qweight* W, const void* xq, int64_t M, float* y, int64
     }
     if (!aligned(xq, 16)) return fail(MBQ_EALIGN, "%s: xq must be 16-byte aligned", fn);
     const size_t ybytes = (size_t)((M - 1) * ldy + W->N) * 4;
-    const size_t xqb = xq_tiled(W->fmt, M) ? (size_t)mbq::xt_bytes(M, W->K) : (size_t)(M * W->K) * 4;
+    const size_t xqb = xq_tiled(W->fmt, M, W->K) ? (size_t)mbq::xt_bytes(M, W->K) : (size_t)(M * W->K) * 4;
     if (overlaps(xq, xqb, y, ybytes)) return fail(MBQ_EINVAL, "%s: xq and y overlap", fn);
     if ((rc = check_planes(W, fn))) return rc;
     if ((rc = check_kernel_shape(W, fn))) return rc;
@@ -665,7 +671,7 @@ int mbq_gemv_xq(const mbq_qweight* W, const void* xq, int64_t M, float* y, int64
         return hip_status(mbq::launch_gemv_m1(W->fmt, P, W->N, W->K, xq, true, y, accumulate,
                                               nullptr, 1, g, s), fn);
     }
-    if (xq_tiled(W->fmt, M)) {
+    if (xq_tiled(W->fmt, M, W->K)) {
         if (W->K % 1024) return fail(MBQ_EUNSUPPORTED, "%s: the matrix-core kernel needs K %% 1024 == 0", fn);
         if (!aligned(W->scales, 8)) return fail(MBQ_EALIGN, "%s: the matrix-core kernel needs 8-byte aligned scales", fn);
         return hip_status(mbq::launch_gemv_mfma_q45(P, W->N, W->K, xq, M, y, ldy, accumulate, s), fn);

@@ -187,6 +187,10 @@ def test_staged_x_argument_checks():
     # Q45 with 16 or more tokens: the matrix-core tile form (2 KB per 16 tokens
     # and 32 values, plus one float per token slot)
     assert L.mbq_xq_bytes(1, 17, 4096, ctypes.byref(sz)) == _lib.OK and sz.value == 2 * (128 * 2048 + 64)
+    # Q45 tile form from 6 tokens when K % 1024 == 0; the row form otherwise
+    assert L.mbq_xq_bytes(1, 6, 4096, ctypes.byref(sz)) == _lib.OK and sz.value == 128 * 2048 + 64
+    assert L.mbq_xq_bytes(1, 5, 4096, ctypes.byref(sz)) == _lib.OK and sz.value == 5 * 4096 * 4
+    assert L.mbq_xq_bytes(1, 8, 2080, ctypes.byref(sz)) == _lib.OK and sz.value == 8 * 2080 * 4
     assert L.mbq_xq_bytes(2, 17, 4096, ctypes.byref(sz)) == _lib.OK and sz.value == 17 * 4096 * 4
     x, xq = BASE, BASE + 0x100000
     st = lambda fmt=1, x=x, M=1, ldx=4096, K=4096, xq=xq: L.mbq_stage_x(fmt, x, M, ldx, K, xq, None)
