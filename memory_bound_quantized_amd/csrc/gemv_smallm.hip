@@ -94,7 +94,8 @@ __global__ __launch_bounds__(kSmBlock) void gemv_smallm_kernel(DevPlanes P, int6
         }
     };
     // Loads walk (group, step) in order; past the last step the last one is
-    // reloaded (never used), so every load is unconditional.
+    // reloaded (never used).  No branch sits between loads (cursors advance by
+    // selects), so each wait for loaded data names only the loads it needs.
     int lg = 0, lc = 0;
     set_rows(0);
     auto next_load = [&](SlotM<FMT, R>& sl) {
@@ -102,13 +103,11 @@ __global__ __launch_bounds__(kSmBlock) void gemv_smallm_kernel(DevPlanes P, int6
         const int bb = b < nchunks ? b : 0;
 #pragma unroll
         for (int r = 0; r < R; r++) T::load(sl.row[r], B, ro[r], bb);
-        if (lc + 1 < C) {
-            lc++;
-        } else if (lg + 1 < G) {
-            lc = 0;
-            lg++;
-            set_rows(lg);
-        }
+        const bool wrap = lc + 1 >= C;
+        const bool last = wrap && lg + 1 >= G;
+        lc = last ? lc : (wrap ? 0 : lc + 1);
+        lg = wrap && !last ? lg + 1 : lg;
+        set_rows(lg);
     };
     SlotM<FMT, R> buf[PD];
 #pragma unroll
@@ -181,7 +180,7 @@ __global__ __launch_bounds__(kSmBlock) void gemv_smallm_kernel(DevPlanes P, int6
                     acc[r][m] = 0.f;
                 }
         }
-        if (c + 1 == C) {
+        if (c + 1 == C && g < G) {
 #pragma unroll
             for (int r = 0; r < R; r++)
 #pragma unroll
@@ -190,22 +189,20 @@ __global__ __launch_bounds__(kSmBlock) void gemv_smallm_kernel(DevPlanes P, int6
         }
     };
 
+    // Steps in whole rounds of PD: a round past the last step computes the
+    // reloaded last step again, and its sums are not stored.
     const int total = G * C;
+    const int rounds = (total + PD - 1) / PD;
     int cg = 0, cc = 0;
-    for (int j = 0; j < total; j += PD) {
+    for (int j = 0; j < rounds; j++) {
 #pragma unroll
         for (int d = 0; d < PD; d++) {
-            if (j + d < total) {
-                compute(buf[d], cc);
-                next_load(buf[d]);
-                after_step(cg, cc);
-                if (cc + 1 < C) {
-                    cc++;
-                } else {
-                    cc = 0;
-                    cg++;
-                }
-            }
+            compute(buf[d], cc);
+            next_load(buf[d]);
+            after_step(cg, cc);
+            const bool wrap = cc + 1 >= C;
+            cc = wrap ? 0 : cc + 1;
+            cg = wrap ? cg + 1 : cg;
         }
     }
     __syncthreads();
