@@ -196,3 +196,36 @@ def test_persistent_step_repeated_tokens_and_table_guard():
     torch.cuda.synchronize()
     assert b.status() & 2
     assert torch.equal(h, h0)
+
+
+def test_workload3_full_size_layers():
+    """Workload 3 at its full shapes.  Layers 0 (Q65 down), 1 (Q45 down) and
+    35 of the 36-layer stack, each as a one-layer step from h0 (the layer's
+    own weights and gammas, every matrix at full size), against the oracle's
+    one-layer chain; layer 0 with the full 151936-row vocabulary product, the
+    others with its first 512 rows.  (The whole 36-layer chain is one
+    single-threaded oracle call of about a minute; the layers cover every
+    shape of it.)"""
+    from memory_bound_quantized_amd.decode import DecodeModel
+    cfg = workloads.config3(only=(0, 1, 35))
+    d = 4096
+    fmtv, V, K, pv = cfg["vocab"]
+    rows = lambda p, n: None if p is None else p.reshape(V, -1)[:n].reshape(-1)
+    small_vocab = (fmtv, 512, K, [rows(p, 512) for p in pv])
+    for lay, l in zip(cfg["layers"], cfg["layer_ids"]):
+        vocab = cfg["vocab"] if l == 0 else small_vocab
+        print("workload3 layer %d vocab %d" % (l, vocab[1]), flush=True)
+        g1, g2 = cfg["g1"][l * d:(l + 1) * d], cfg["g2"][l * d:(l + 1) * d]
+        model = DecodeModel([lay], vocab, g1, g2, cfg["gf"], cfg["eps"])
+        h = dev(cfg["h0"])
+        logits = torch.empty(vocab[1], device="cuda")
+        model.step(h, logits)
+        torch.cuda.synchronize()
+        lay_o = {k: oracle.Planes(*v) for k, v in lay.items()}
+        h_ref, lg_ref = oracle.decode_token([lay_o], oracle.Planes(*vocab), g1, g2, cfg["gf"],
+                                            cfg["eps"], cfg["h0"])
+        e_h = rel_l2(h.cpu().numpy(), h_ref)
+        e_l = rel_l2(logits.cpu().numpy(), lg_ref)
+        print("  rel-L2 h %.2e logits %.2e" % (e_h, e_l), flush=True)
+        assert e_h <= 1e-4 and e_l <= 1e-4
+        del model

@@ -99,29 +99,31 @@ def config2(n_up: int = 12288, k_up: int = 4096, n_down: int = 4096, k_down: int
 
 
 def config3(layers: int = 36, d: int = 4096, dq: int = 4096, dkv: int = 1024,
-            f: int = 12288, vocab: int = 151936):
+            f: int = 12288, vocab: int = 151936, only=None):
     """The synthetic 36-layer stack: per layer q, k, v, o, gate, up at Q45, down
     at Q65 in even layers and Q45 in odd ones; vocab at Q65; gammas
-    ~U(0.5,1.5); h0 ~N(0,1); eps 1e-6."""
+    ~U(0.5,1.5); h0 ~N(0,1); eps 1e-6.  only: generate just these layer
+    indices (the same bytes as in the full stack; "layers" then lists them in
+    that order and "layer_ids" names them)."""
     r = _children(3, 7 * layers + 5)
     lay = []
-    i = 0
-    for l in range(layers):
+    ids = list(range(layers)) if only is None else list(only)
+    for l in ids:
         shapes = dict(q=(Q45, dq, d), k=(Q45, dkv, d), v=(Q45, dkv, d), o=(Q45, d, dq),
                       gate=(Q45, f, d), up=(Q45, f, d),
                       down=(Q65 if l % 2 == 0 else Q45, d, f))
         entry = {}
-        for name in ("q", "k", "v", "o", "gate", "up", "down"):
+        for j, name in enumerate(("q", "k", "v", "o", "gate", "up", "down")):
             fmt, N, K = shapes[name]
-            entry[name] = (fmt, N, K, weight_planes(r[i], fmt, N, K))
-            i += 1
+            entry[name] = (fmt, N, K, weight_planes(r[7 * l + j], fmt, N, K))
         lay.append(entry)
+    i = 7 * layers
     V = (Q65, vocab, d, weight_planes(r[i], Q65, vocab, d))
     g1 = uniform(r[i + 1], layers * d, 0.5, 1.5)
     g2 = uniform(r[i + 2], layers * d, 0.5, 1.5)
     gf = uniform(r[i + 3], d, 0.5, 1.5)
     h0 = normal(r[i + 4], d)
-    return dict(layers=lay, vocab=V, g1=g1, g2=g2, gf=gf, h0=h0, eps=1e-6)
+    return dict(layers=lay, layer_ids=ids, vocab=V, g1=g1, g2=g2, gf=gf, h0=h0, eps=1e-6)
 
 
 def config4(M: int, n: int = 12288, k: int = 4096):
