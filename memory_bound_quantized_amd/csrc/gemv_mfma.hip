@@ -143,7 +143,7 @@ __device__ __forceinline__ h8 codes_to_a(uint32_t a) {
 // added in part order through LDS at the end.
 //
 // Requires K % 1024 == 0 and (nb / S) a multiple of kPG * kGB and of SB.
-constexpr int kPGv2 = 4;                   // weight loads in flight per wave
+constexpr int kPG = 4;                   // weight loads in flight per wave
 
 template <int TT, int TR, int S, int SB>
 __global__ __launch_bounds__(kWave * TR * S) void gemv_mfma_q45_kernel(
@@ -155,9 +155,9 @@ __global__ __launch_bounds__(kWave * TR * S) void gemv_mfma_q45_kernel(
     constexpr int XALL = S * XSB;                     // uint4 per slab step, all parts
     constexpr int XPT = (XALL + NT - 1) / NT;         // per thread (last round guarded)
     constexpr int GPS = SB / kGB;                     // weight groups per slab
-    constexpr int kUSv = kPGv2 / GPS > 0 ? kPGv2 / GPS : 1;   // slabs per unrolled body
-    constexpr int RING = kUSv * GPS;                  // ring slots (>= kPGv2)
-    static_assert(SB % kGB == 0 && RING >= kPGv2, "slab and ring geometry");
+    constexpr int kUS = kPG / GPS > 0 ? kPG / GPS : 1;   // slabs per unrolled body
+    constexpr int RING = kUS * GPS;                  // ring slots (>= kPG)
+    static_assert(SB % kGB == 0 && RING >= kPG, "slab and ring geometry");
     extern __shared__ u4v lds[];
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(kWave * TR * S) void gemv_mfma_q45_kernel(
     u4v wr[RING];
     u2v sr[RING][4];
 #pragma unroll
-    for (int t = 0; t < kPGv2; t++) {
+    for (int t = 0; t < kPG; t++) {
         const int tc = t < ngroups ? t : ngroups - 1;
         wr[t] = wq[kGB * tc + g];
 #pragma unroll
@@ -214,8 +214,8 @@ __global__ __launch_bounds__(kWave * TR * S) void gemv_mfma_q45_kernel(
     for (int tt = 0; tt < TT; tt++) acc[tt] = f4v{0.f, 0.f, 0.f, 0.f};
     const f4v zero = {0.f, 0.f, 0.f, 0.f};
 
-    for (int s0 = 0; s0 < nslab; s0 += kUSv) {
-        static_for<0, kUSv>([&](auto su_c) {
+    for (int s0 = 0; s0 < nslab; s0 += kUS) {
+        static_for<0, kUS>([&](auto su_c) {
             constexpr int su = decltype(su_c)::value;
             const int st = s0 + su;
             constexpr int buf = su & 1;
@@ -229,7 +229,7 @@ __global__ __launch_bounds__(kWave * TR * S) void gemv_mfma_q45_kernel(
             static_for<0, GPS>([&](auto tg_c) {
                 constexpr int tg = decltype(tg_c)::value;
                 constexpr int tl = (su * GPS + tg) % RING;          // ring slot
-                constexpr int tf = (su * GPS + tg + kPGv2) % RING;  // slot of the group kPG ahead
+                constexpr int tf = (su * GPS + tg + kPG) % RING;  // slot of the group kPG ahead
                 const int t = st * GPS + tg;                        // weight group
                 // transpose: lane (i, g) holds block 4t + g of row i; each
                 // MFMA needs dword g of one block from every lane of row i
@@ -237,7 +237,7 @@ __global__ __launch_bounds__(kWave * TR * S) void gemv_mfma_q45_kernel(
                 u2v sc[4];
 #pragma unroll
                 for (int v = 0; v < 4; v++) sc[v] = sr[tl][v];
-                const int tn = t + kPGv2 < ngroups ? t + kPGv2 : ngroups - 1;
+                const int tn = t + kPG < ngroups ? t + kPG : ngroups - 1;
                 wr[tf] = wq[kGB * tn + g];
 #pragma unroll
                 for (int v = 0; v < 4; v++) sr[tf][v] = sq[v][tn];
