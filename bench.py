@@ -508,7 +508,7 @@ def main():
         "config": {"workload": "M=1 GEMV: Q45 12288x4096 (4.5 bpw) + Q65 4096x12288 (6.5625 bpw), "
                                "fp32 x and accumulation, weights rotated over %d copies (%.2f GB)"
                                % (ncopy, ncopy * per_copy / 1e9),
-                   "global_batch": 1, "seq_len": 1, "parallelism": "none"},
+                   "tokens_per_product": 1, "gpus": 1},
         "roofline": roofline,
         "kernels": {k: {"avg_us": round(v[1] * 1e3, 3), "gbs": round(v[0] / (v[1] * 1e-3) / 1e9, 1),
                         "frac_of_peak": round(v[0] / (v[1] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
