@@ -499,6 +499,17 @@ def main():
                 "traffic": traffic_for(dom), "algorithmic_bytes_per_launch": d_bytes,
                 "avg_launch_us": round(d_ms * 1e3, 3),
                 "frac_of_measured_read_peak": round(achieved / best, 4)}
+    # what a plain read of the same byte count achieves per launch, timed the
+    # same way (graph of cold launches over >= 1 GiB of distinct buffers)
+    rd_bytes = d_bytes
+    n_rd = max(2, -(-ROTATION_BYTES // rd_bytes))
+    rbufs = [torch.empty(rd_bytes, dtype=torch.uint8, device=dev) for _ in range(n_rd)]
+    rd_sink = torch.empty(4096, device=dev)
+    rd_us = per_launch_us(lambda b: mbq.probe_read(b, rd_sink), rbufs)
+    del rbufs
+    torch.cuda.empty_cache()
+    roofline["same_size_read_us"] = round(rd_us, 3)
+    roofline["frac_of_same_size_read"] = round(rd_us / (d_ms * 1e3), 4)
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
