@@ -437,19 +437,25 @@ static int check_decode(const mbq_decode_model* m, const char* fn) {
 
 // Workspace of the decode step: [0, 2048) the one-launch step's barrier
 // counters (global at 0, group g at 128 (g + 1)) and status word (at 4);
-// then q|k|v, the gated activations, and the layer table of the one-launch
-// step.
+// then q|k|v and the gated activations of each layer (the launch chain uses
+// the first layer's), the h versions of the one-launch step (one per
+// residual add), and its layer table.
 struct DecodeLayout {
-    size_t qkv, m, table, total;
+    size_t qkv, m, hv, table, total;
+    size_t qs, ms, hs;   // bytes between layers / versions
 };
 
 static DecodeLayout decode_layout(const mbq_decode_model* m) {
     DecodeLayout L;
+    const size_t nl = (size_t)(m->n_layers > 0 ? m->n_layers : 1);
+    L.qs = align256((size_t)(m->dq + 2 * m->dkv) * 4);
+    L.ms = align256((size_t)m->f * 4);
+    L.hs = align256((size_t)m->d * 4);
     L.qkv = 2048;
-    L.m = L.qkv + align256((size_t)(m->dq + 2 * m->dkv) * 4);
-    L.table = L.m + align256((size_t)m->f * 4);
-    L.total = L.table + align256(offsetof(mbq::DecTable, layers) +
-                                 (size_t)(m->n_layers > 0 ? m->n_layers : 1) * sizeof(mbq::DecLayer));
+    L.m = L.qkv + nl * L.qs;
+    L.hv = L.m + nl * L.ms;
+    L.table = L.hv + 2 * nl * L.hs;
+    L.total = L.table + align256(offsetof(mbq::DecTable, layers) + nl * sizeof(mbq::DecLayer));
     return L;
 }
 
@@ -537,6 +543,9 @@ static uint64_t decode_tag(const mbq_decode_model* m) {
         mix(L.gamma1); mix(L.gamma2);
     }
     mix((const void*)(uintptr_t)m->n_layers);
+    if (m->vocab > 0) mixw(m->lm_head);
+    mix(m->gamma_f);
+    mix((const void*)(uintptr_t)m->vocab);
     return hsh;
 }
 
@@ -553,6 +562,11 @@ int mbq_decode_prepare(const mbq_decode_model* m, void* workspace, size_t worksp
     t->magic = mbq::kDecMagic;
     t->n_layers = m->n_layers;
     t->tag = decode_tag(m);
+    if (m->vocab > 0) {
+        t->head.lm = planes_of(&m->lm_head);
+        t->head.fmt_lm = m->lm_head.fmt;
+    }
+    t->head.gf = m->gamma_f;
     for (int l = 0; l < m->n_layers; l++) {
         const mbq_decode_layer& L = m->layers[l];
         mbq::DecLayer& D = t->layers[l];
@@ -577,8 +591,8 @@ int mbq_decode_step_persistent(const mbq_decode_model* m, float* h, float* logit
     int rc = check_decode(m, fn);
     if (rc) return rc;
     if ((rc = check_workspace(m, h, logits, workspace, workspace_bytes, fn))) return rc;
-    if (m->d != 4096 || m->dq != 4096 || m->f != 12288 || (m->dq + 2 * m->dkv) % 2 || m->vocab % 2)
-        return fail(MBQ_EUNSUPPORTED, "%s: the one-launch step needs d = dq = 4096, f = 12288 and even row counts", fn);
+    if (m->d != 4096 || m->dq != 4096 || m->f != 12288)
+        return fail(MBQ_EUNSUPPORTED, "%s: the one-launch step needs d = dq = 4096 and f = 12288", fn);
     for (int l = 0; l < m->n_layers; l++) {
         const mbq_decode_layer& L = m->layers[l];
         if (L.qkv.fmt != MBQ_FMT_Q45 || L.o.fmt != MBQ_FMT_Q45 || L.gate_up.fmt != MBQ_FMT_Q45 ||
@@ -594,18 +608,14 @@ int mbq_decode_step_persistent(const mbq_decode_model* m, float* h, float* logit
     expect.magic = mbq::kDecMagic;
     expect.n_layers = m->n_layers;
     expect.tag = decode_tag(m);
-    mbq::DecHead head;
-    memset(&head, 0, sizeof head);
-    if (m->vocab > 0) {
-        head.lm = planes_of(&m->lm_head);
-        head.fmt_lm = m->lm_head.fmt;
-    }
-    head.gf = m->gamma_f;
-    return hip_status(mbq::launch_decode_persistent(
-                          (const mbq::DecTable*)(ws + lay.table), expect, head, m->eps, h, logits,
-                          m->vocab, m->dq + 2 * m->dkv, (float*)(ws + lay.qkv), (float*)(ws + lay.m),
-                          (uint32_t*)ws, (uint32_t*)(ws + 4), (hipStream_t)stream),
-                      fn);
+    mbq::DecodeBuffers db{(float*)(ws + lay.hv), (float*)(ws + lay.qkv), (float*)(ws + lay.m),
+                          (int64_t)(lay.hs / 4), (int64_t)(lay.qs / 4), (int64_t)(lay.ms / 4)};
+    const hipError_t e = mbq::launch_decode_persistent(
+        (const mbq::DecTable*)(ws + lay.table), expect, m->eps, h, logits, m->vocab,
+        m->dq + 2 * m->dkv, db, (uint32_t*)ws, (uint32_t*)(ws + 4), (hipStream_t)stream);
+    if (e == hipErrorInvalidConfiguration)
+        return fail(MBQ_EUNSUPPORTED, "%s: the model's row counts or this device's compute-unit count do not fit the one-launch step", fn);
+    return hip_status(e, fn);
 }
 
 int mbq_xq_bytes(int fmt, int64_t M, int64_t K, size_t* bytes) {

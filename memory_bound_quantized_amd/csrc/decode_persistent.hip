@@ -1,33 +1,44 @@
 // decode_persistent.hip -- one token through the decoder stack in one launch.
 //
 // The pages' unbuilt kernel ([one-serial-kernel] "The kernel that was never
-// built": one kernel doing the token's work without returning to the host
-// between steps; [roofline-holds] "Where the time goes": a fixed toll per
-// weight kernel, and fusion as its cure).  Weights never depend on
-// activations, so each wave issues the loads of its next table before it
-// waits for the grid-wide barrier that publishes that table's input: the
-// barrier's latency, the x staging and the norm overlap with the weight
-// stream instead of adding to it.
+// built": the token's work in one kernel, no return to the host between
+// steps; [roofline-holds] "Where the time goes": a fixed toll per weight
+// kernel, with fusion as the cure).  Weights never depend on activations, so
+// the weight stream need not stop at the grid-wide barrier that publishes a
+// table's input: each compute wave walks ONE stream of units that runs
+// through all tables of the token, and keeps kDD units in flight across
+// every barrier ([roofline-holds] "How the breakouts tie out: Little and
+// Volkov": bandwidth x latency bytes must stay in flight).
 //
-// Grid: every workgroup resident at once (cooperative launch), a few per
-// compute unit.  Per layer four phases separated by grid barriers:
-//   P1  a = rmsnorm(h, gamma1) staged in each workgroup; q|k|v = Wqkv a
-//   P2  q staged; h += Wo q
-//   P3  b = rmsnorm(h, gamma2) staged; m = silu(Wg b) * (Wu b) (gate/up rows
-//       interleaved, so one wave computes both rows of an output)
-//   P4  m staged; h += Wdown m
-// then logits = Wlm rmsnorm(h, gamma_f).  Each phase splits its table's rows
-// over the workgroups in pairs; inside a workgroup the 4 waves take pairs in
-// turn.  Every wave streams its rows as in the M = 1 kernel (gemv_m1.hip):
-// lane l takes chunk 64 c + l, codes unpacked in registers, integer-digit
-// dots against the staged x in LDS, a DPP reduction per row.
+// Grid: one workgroup of 16 waves per compute unit, all resident
+// (cooperative launch).  Per layer four phases, then the vocabulary:
+//   qkv  q|k|v = Wqkv rmsnorm(h, gamma1)
+//   o    h' = h + Wo q                  (q stands in for attention's output)
+//   gu   m = silu(Wg b) * (Wu b), b = rmsnorm(h', gamma2)   (rows interleaved)
+//   dn   h'' = h' + Wdown m
+//   lm   logits = Wlm rmsnorm(h, gamma_f)
+// Phase p's rows are split into one contiguous block per workgroup (row
+// pairs for gu).  A unit is one chunk step of one row (lane l reads chunk
+// 64 c + l: a 1 KiB burst per wave, [mountain-runs] section 3); the
+// workgroup's units are split evenly over its 15 compute waves, so a row can
+// be shared by two waves, whose partial sums meet in LDS.
 //
-// Barrier: a monotone counter in the caller's workspace.  The activations
-// that cross workgroups are written and read with device-coherent accesses,
-// so arriving is: wait for one's own writes to complete, meet the workgroup,
-// add 1; waiting is a bounded spin on the counter.  A spin that exceeds its
-// bound sets the error word and gives up, so every wave always reaches the
-// end of the kernel.
+// Wave 15 is the control wave.  It streams no weights; at each phase
+// boundary it applies the finished phase's epilogue (store, residual add or
+// silu * up) to the workgroup's rows, writes them through to device-coherent
+// memory, waits for those stores only, arrives at the grid barrier, waits for
+// every workgroup, and copies the next phase's input vector (and gamma) into
+// LDS with direct-to-LDS loads.  The compute waves meanwhile hold their next
+// kDD units of weights in flight.  Then all 16 waves stage x (RMSNorm
+// included) from LDS into the integer-digit form of formats.h.
+//
+// Activations that cross workgroups (h after each residual add, q|k|v, m)
+// are written once each per token into buffers of their own, with
+// device-scope stores, and read with device-scope loads, which the 8 XCDs'
+// separate L2 caches cannot serve stale.  The barrier: a workgroup arrives
+// on the counter of its group (block % 8), the last of a group on the
+// global counter; waiting is a bounded spin, and a spin that gives up sets
+// the status word so every wave still reaches the end of the kernel.
 #include "device_common.h"
 #include "formats.h"
 #include "kernels.h"
@@ -37,62 +48,384 @@ namespace mbq {
 
 namespace {
 
-template <int V>
-struct ICd {
-    static constexpr int value = V;
+constexpr int kPW = 16;                 // waves per workgroup
+constexpr int kPT = kPW * kWave;        // threads per workgroup
+constexpr int kCW = kPW - 1;            // compute waves; wave kCW is the control wave
+constexpr int kDD = 5;                  // units in flight per compute wave
+constexpr int kD = 4096, kF = 12288;
+constexpr int kMaxRowsWG = 1024;        // rows of one phase per workgroup
+constexpr uint32_t kSpinLimit = 1u << 22;   // about 0.2 s of 64-cycle sleeps
+constexpr int kBarGroups = 8;
+constexpr int kBarStride = 32;          // uint32 between counters (128 bytes)
+
+enum Kind : int { kQKV = 0, kO = 1, kGU = 2, kDN = 3, kLM = 4 };
+
+// LDS layout (bytes).  The staged x takes 36 dwords per 32 values (Q45 and
+// Q65 alike, staging.h), up to K = 12288.
+constexpr int kLdsH = 0;                               // fp32 h being normalised [4096]
+constexpr int kLdsX = kLdsH + 4 * kD;                  // fp32 q or m [12288]
+constexpr int kLdsG = kLdsX + 4 * kF;                  // fp32 gamma [4096]
+constexpr int kLdsS = kLdsG + 4 * kD;                  // staged x
+constexpr int kLdsP = kLdsS + (kF / 32) * Stride<kQ65>::DW * 4;   // row partials [2][kMaxRowsWG]
+constexpr int kLdsR = kLdsP + 2 * 4 * kMaxRowsWG;      // block-sum scratch [16]
+constexpr int kLdsTotal = kLdsR + 4 * kPW;
+static_assert(Stride<kQ45>::DW == Stride<kQ65>::DW, "one staged stride for both formats");
+
+// Raw registers of one unit, in one shape for both formats: a = 16 code
+// bytes (Q45 codes, Q65 low bits), qh = Q65 high bits, then the scale bytes
+// (Q45: fp16 scale; Q65: two int8 sub-scales) and the Q65 super-scale.
+// A Q45 table's high-bit and super-scale planes are zero-size buffer
+// resources: those loads return 0 without a memory access, so every unit
+// issues the same four loads into the same registers.
+struct Raw {
+    uint4 a;
+    uint2 qh;
+    uint32_t sc2, d2;   // the aligned dwords holding the 16-bit scale fields
 };
-template <int B, int E, class F>
-__device__ __forceinline__ void sfor(F&& f) {
-    if constexpr (B < E) {
-        f(ICd<B>{});
-        sfor<B + 1, E>(f);
+// The 16-bit fields are read as the aligned dword that holds them and picked
+// out where they are used (the half is fixed by the lane), so no operation
+// on a loaded register sits between the load and its use.
+__device__ __forceinline__ Traits<kQ45>::Row as_q45(const Raw& r, int lane) {
+    return {r.a, r.sc2 >> (16 * (lane & 1))};
+}
+__device__ __forceinline__ Traits<kQ65>::Row as_q65(const Raw& r, int lane) {
+    return {r.a, r.qh, r.sc2 >> (16 * (lane & 1)), r.d2 >> (16 * ((lane >> 3) & 1))};
+}
+
+// What phase p reads and where it goes.
+struct PhaseInfo {
+    int kind, layer, fmt, N, CS, Q;   // Q: rows that must share a workgroup
+    DevPlanes P;
+};
+
+// The layer table is written by the host before the launch and only read
+// here: reading it through the constant address space lets every access be a
+// scalar load, which never waits behind the weight loads in flight.
+typedef const DecTable __attribute__((address_space(4)))* CTable;
+__device__ __forceinline__ DevPlanes planes_at(const DevPlanes __attribute__((address_space(4)))& q) {
+    return DevPlanes{q.p0, q.p1, q.p2, q.p3};
+}
+
+struct Ctx {
+    CTable t;
+    int L, P, nqkv, vocab, G;
+    __device__ __forceinline__ static int rows_total(int k, int nqkv, int vocab) {
+        return k == kQKV ? nqkv : k == kGU ? 2 * kF : k == kLM ? vocab : kD;
+    }
+    // This workgroup's rows of a kind of phase, [row_base, row_base + rows):
+    // the rows split into G contiguous blocks (row pairs for gate/up).
+    __device__ __forceinline__ void rows_of(int k, int& row_base, int& rows) const {
+        const int Q = k == kGU ? 2 : 1;
+        const int NQ = rows_total(k, nqkv, vocab) / Q;
+        const int b = (int)blockIdx.x;
+        const int q0 = (int)((uint32_t)(NQ * b) / (uint32_t)G);
+        const int q1 = (int)((uint32_t)(NQ * (b + 1)) / (uint32_t)G);
+        row_base = Q * q0;
+        rows = Q * (q1 - q0);
+    }
+    __device__ __forceinline__ PhaseInfo info(int p) const {
+        PhaseInfo f;
+        if (p >= 4 * L) {
+            f.kind = kLM;
+            f.layer = L;
+            f.fmt = t->head.fmt_lm;
+            f.N = vocab;
+            f.CS = 2;
+            f.Q = 1;
+            f.P = planes_at(t->head.lm);
+            return f;
+        }
+        f.layer = p >> 2;
+        f.kind = p & 3;
+        const DecLayer __attribute__((address_space(4)))* ly = t->layers + f.layer;
+        f.CS = 2;
+        f.Q = 1;
+        f.fmt = kQ45;
+        if (f.kind == kQKV) {
+            f.N = nqkv;
+            f.P = planes_at(ly->qkv);
+        } else if (f.kind == kO) {
+            f.N = kD;
+            f.P = planes_at(ly->o);
+        } else if (f.kind == kGU) {
+            f.N = 2 * kF;
+            f.Q = 2;
+            f.P = planes_at(ly->gu);
+        } else {
+            f.N = kD;
+            f.CS = 6;
+            f.fmt = ly->fmt_dn;
+            f.P = planes_at(ly->dn);
+        }
+        return f;
+    }
+};
+
+// Device buffers of the token's activations.
+struct Bufs {
+    float* h_in;        // caller's h: version 0 in, the last version out
+    float* hv;          // versions 1 .. 2L, hs floats apart
+    float* qkv;         // per layer, qs floats apart
+    float* m;           // per layer, ms floats apart
+    float* logits;
+    int64_t hs, qs, ms;
+    __device__ __forceinline__ float* h(int v) const { return v == 0 ? h_in : hv + (int64_t)(v - 1) * hs; }
+};
+
+// ---- one compute wave's share of one phase ---------------------------------
+// The workgroup's units of a phase (rows x chunk steps, row-major) are split
+// evenly over the compute waves: this wave takes U of them, starting at row
+// row0 (relative to the workgroup's first row) and chunk step cs0.  Upad
+// rounds U up to a multiple of kDD (at least kDD) with units that compute
+// nothing, so that the unit stream crosses into the next phase with its
+// slots in order: the loads of the next phase's first kDD units are issued
+// in the last kDD steps of this one.
+struct Span {
+    int U, Upad, CS, row_base, row0, cs0;
+    BufPlanes B;
+    int fmt;
+};
+
+__device__ __forceinline__ Span span_of(const Ctx& c, int p, int w) {
+    Span s;
+    const PhaseInfo f = c.info(p);
+    const int k = f.kind;
+    s.CS = f.CS;
+    s.fmt = f.fmt;
+    int rows;
+    c.rows_of(k, s.row_base, rows);
+    const int Uwg = rows * f.CS;
+    const int u0 = Uwg * w / kCW, u1 = Uwg * (w + 1) / kCW;
+    s.U = u1 - u0;
+    s.Upad = s.U <= kDD ? kDD : (s.U + kDD - 1) / kDD * kDD;
+    s.row0 = f.CS == 6 ? u0 / 6 : u0 >> 1;
+    s.cs0 = u0 - s.row0 * f.CS;
+    const int K = 2048 * f.CS;
+    s.B = f.fmt == kQ65 ? Traits<kQ65>::planes(f.P, f.N, K) : Traits<kQ45>::planes(f.P, f.N, K);
+    return s;
+}
+
+// Issue the loads of one unit (row relative to the span's base, chunk step
+// cs) into r.  Padding units past the table read outside its buffer
+// resources, which returns 0 without a memory access; their data is never
+// used, and every unit issues the same loads.  Per row a table holds K/2
+// code bytes, K/4 high-bit bytes, K/16 scale bytes and K/128 super-scale
+// bytes (Q45 and Q65 alike), K = 2048 CS.
+__device__ __forceinline__ void load_unit(Raw& r, const Span& s, int row, int cs) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint32_t o3 = (uint32_t)(s.row_base + row) * (uint32_t)(16 * s.CS);
+    const uint32_t b = (uint32_t)(cs * kWave + lane);
+    r.a = bload<uint4, true>(s.B.p0, 16u * b, o3 << 6);
+    r.qh = bload<uint2, true>(s.B.p1, 8u * b, o3 << 5);
+    r.sc2 = bload<uint32_t, true>(s.B.p2, 4u * (b >> 1), o3 << 3);
+    r.d2 = bload<uint32_t, true>(s.B.p3, 4u * (b >> 4), o3);
+}
+
+__device__ __forceinline__ void step(int& row, int& cs, int CS) {
+    if (++cs == CS) {
+        cs = 0;
+        row++;
     }
 }
 
-constexpr int kRows = 2;                 // rows per wave step (a gate/up pair)
-constexpr uint32_t kSpinLimit = 1u << 22;   // about 0.2 s of 128-cycle sleeps
+// The first kDD units of a span into the slots.
+__device__ __forceinline__ void load_first(Raw (&buf)[kDD], const Span& s) {
+    int row = s.row0, cs = s.cs0;
+#pragma unroll
+    for (int d = 0; d < kDD; d++) {
+        load_unit(buf[d], s, row, cs);
+        step(row, cs, s.CS);
+    }
+}
 
-template <int FMT, int R>
-struct PSlot {
-    typename Traits<FMT>::Row row[R];
+// Where a compute wave is in the current phase.
+struct Pos {
+    int rc, cc;          // unit being computed (row, chunk step)
+    bool shared;         // row rc began in the previous wave's range
+    int rl, cl;          // unit being loaded, kDD ahead
+    float acc;
 };
 
-// ---- device-coherent activations -------------------------------------------
-// h, q and the gated activations cross workgroups (and the 8 XCDs' separate
-// L2 caches).  They are written and read with agent-scope atomic accesses,
-// which bypass the non-coherent cache levels, so a barrier needs no cache
-// write-back or invalidation: only that the writes have completed.
-__device__ __forceinline__ float coh_load(const float* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Compute unit u of C from slot r, with the row sum to LDS at the row's end
+// or the range's end: part[0][row] for a row that starts in this wave's
+// range, part[1][row] for the first row when it began in the previous one.
+__device__ __forceinline__ void compute_unit(const Raw& r, const Span& C, int u, Pos& q,
+                                             const uint32_t* xs, float* part) {
+    const int lane = threadIdx.x & (kWave - 1);
+    if (u < C.U) {
+        uint32_t xv[4 * Traits<kQ45>::F4];
+        read_x<kQ45>(xs, q.cc * kWave + lane, xv);
+        if (C.fmt == kQ65)
+            q.acc += Traits<kQ65>::dot(as_q65(r, lane), xv);
+        else
+            q.acc += Traits<kQ45>::dot(as_q45(r, lane), xv);
+        if (q.cc == C.CS - 1 || u == C.U - 1) {
+            const float sum = wave_sum_dpp(q.acc);
+            if (lane == 0) part[(q.shared ? kMaxRowsWG : 0) + q.rc] = sum;
+            q.acc = 0.f;
+            q.shared = false;
+        }
+        step(q.rc, q.cc, C.CS);
+    }
 }
+
+// All but the last kDD units of a phase: each slot is refilled from the
+// same phase, kDD units ahead.
+__device__ __forceinline__ void run_main(Raw (&buf)[kDD], const Span& C, Pos& q,
+                                         const uint32_t* xs, float* part) {
+    for (int g = 0; g + kDD < C.Upad; g += kDD) {
+#pragma unroll
+        for (int d = 0; d < kDD; d++) {
+            compute_unit(buf[d], C, g + d, q, xs, part);
+            load_unit(buf[d], C, q.rl, q.cl);
+            step(q.rl, q.cl, C.CS);
+        }
+    }
+}
+
+// The last kDD units of a phase: each slot is refilled with the next phase's
+// first units.
+__device__ __forceinline__ void run_tail(Raw (&buf)[kDD], const Span& C, const Span& Nx, Pos& q,
+                                         const uint32_t* xs, float* part) {
+    const int g = C.Upad - kDD;
+    int rn = Nx.row0, cn = Nx.cs0;
+#pragma unroll
+    for (int d = 0; d < kDD; d++) {
+        compute_unit(buf[d], C, g + d, q, xs, part);
+        load_unit(buf[d], Nx, rn, cn);
+        step(rn, cn, Nx.CS);
+    }
+}
+
+// ---- workgroup barriers without memory fences ------------------------------
+// LDS traffic is ordered by waiting for this wave's LDS operations; nothing
+// waits for the weight loads in flight.
+__device__ __forceinline__ void wg_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ float block_sum16(float v, float* red) {
+    v = wave_sum(v);
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    if (lane == 0) red[wave] = v;
+    wg_barrier();
+    float t = red[0];
+#pragma unroll
+    for (int w = 1; w < kPW; w++) t += red[w];
+    wg_barrier();
+    return t;
+}
+
+// ---- x: fp32 row in LDS -> staged form in LDS (all 1024 threads) ----------
+// Each thread stages groups of 8 values (og = tid, tid + 1024, ...), in the
+// layout of staging.h; Q45 and Q65 share the digit words and differ only in
+// the offset terms of the metadata (one 32-value block times -8, or two
+// 16-value blocks times -32), chosen at run time so that one copy of the
+// code serves every phase.  With a gamma, x is first replaced by
+// gamma * (x * r), r = 1/sqrt(mean(x^2) + eps) ([one-serial-kernel] "One
+// thread": the norm as a cooperative reduction).
+__device__ __forceinline__ void stage_group_rt(const float* v, int og, bool ok, bool q65,
+                                               uint32_t* xs) {
+    constexpr int DW = Stride<kQ45>::DW;
+    const int b = og >> 2, gi = og & 3;
+    float amax = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; k++) amax = fmaxf(amax, fabsf(v[k]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
+    const int e = chunk_exp(amax);
+    const float up = pow2f(e);
+    int32_t n[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) n[k] = round_fixed(v[k], up);
+    uint32_t dg[6];
+    digit_words(n[0], n[2], n[4], n[6], dg);
+    digit_words(n[1], n[3], n[5], n[7], dg + 3);
+    int32_t S[3];
+#pragma unroll
+    for (int p = 0; p < 3; p++) {
+        S[p] = p < 2 ? (int32_t)udot4(dg[p], 0x01010101u, udot4(dg[3 + p], 0x01010101u, 0u))
+                     : sdot4(dg[2], 0x01010101u, sdot4(dg[5], 0x01010101u, 0));
+    }
+    int32_t B01[3], B23[3];
+#pragma unroll
+    for (int p = 0; p < 3; p++) {
+        B01[p] = S[p] + __shfl_xor(S[p], 1, kWave);
+        B23[p] = __shfl_xor(B01[p], 2, kWave);
+    }
+    if (ok) {
+        uint32_t* o = xs + DW * b + 6 * gi;
+#pragma unroll
+        for (int t = 0; t < 6; t += 2) *(uint2*)(o + t) = make_uint2(dg[t], dg[t + 1]);
+        if (gi == 0) {
+            uint32_t m[8];
+            m[0] = __builtin_bit_cast(uint32_t, pow2f(-e));
+#pragma unroll
+            for (int p = 0; p < 3; p++) {
+                m[1 + p] = q65 ? (uint32_t)(-32 * B01[p]) : (uint32_t)(-8 * (B01[p] + B23[p]));
+                m[4 + p] = q65 ? (uint32_t)(-32 * B23[p]) : 0u;
+            }
+            m[7] = 0u;
+            uint32_t* md = xs + DW * b + Traits<kQ45>::META;
+            *(uint4*)md = make_uint4(m[0], m[1], m[2], m[3]);
+            *(uint4*)(md + 4) = make_uint4(m[4], m[5], m[6], m[7]);
+        }
+    }
+}
+
+__device__ __forceinline__ void stage_lds(const float* raw, int K, const float* gam, float eps,
+                                          bool q65, uint32_t* xs, float* red) {
+    const int ng = K / 8;
+    const int tid = threadIdx.x;
+    float inv = 1.f;
+    if (gam) {
+        float ss = 0.f;
+        for (int og = tid; og < ng; og += kPT) {
+            const float4 a = *(const float4*)(raw + 8 * og), b = *(const float4*)(raw + 8 * og + 4);
+            ss = fmaf(a.x, a.x, ss); ss = fmaf(a.y, a.y, ss); ss = fmaf(a.z, a.z, ss); ss = fmaf(a.w, a.w, ss);
+            ss = fmaf(b.x, b.x, ss); ss = fmaf(b.y, b.y, ss); ss = fmaf(b.z, b.z, ss); ss = fmaf(b.w, b.w, ss);
+        }
+        inv = 1.0f / sqrtf(block_sum16(ss, red) / (float)K + eps);
+    }
+    // every lane of a wave runs the same rounds (the shuffles need whole waves)
+    const int rounds = (ng + kPT - 1) / kPT;
+    for (int r = 0; r < rounds; r++) {
+        const int og = r * kPT + tid;
+        const bool ok = og < ng;
+        const int src = ok ? og : 0;
+        const float4 a = *(const float4*)(raw + 8 * src), b = *(const float4*)(raw + 8 * src + 4);
+        float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        if (gam) {
+            const float4 ga = *(const float4*)(gam + 8 * src), gb = *(const float4*)(gam + 8 * src + 4);
+            const float g[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+#pragma unroll
+            for (int k = 0; k < 8; k++) v[k] = g[k] * (v[k] * inv);
+        }
+        stage_group_rt(v, og, ok, q65, xs);
+    }
+}
+
+// ---- control wave: device-coherent stores, barrier, LDS copies -------------
 __device__ __forceinline__ void coh_store(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint4 coh_load16(const float* p) {
-    const uint64_t* q = (const uint64_t*)p;
-    const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return make_uint4((uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32));
+
+typedef const void __attribute__((address_space(1)))* gvoid;
+typedef void __attribute__((address_space(3)))* lvoid;
+// n floats (n % 256 == 0) from global src to LDS dst, 1 KiB per wave
+// instruction, straight into LDS.  COH: device-scope loads (sc1).
+template <bool COH>
+__device__ __forceinline__ void copy_to_lds(const float* src, float* dst, int n) {
+    const int lane = threadIdx.x & (kWave - 1);
+    for (int i = 0; i < n; i += 256)
+        __builtin_amdgcn_global_load_lds((gvoid)(src + i + 4 * lane), (lvoid)(dst + i), 16, 0,
+                                         COH ? 16 : 0);
 }
 
-// ---- grid barrier ---------------------------------------------------------
-// Two levels: workgroup b arrives on the counter of group b % kBarGroups,
-// and the last arrival of each group adds 1 to the global counter, which the
-// workgroups wait on.  Atomics on one address are serialized (about 15 ns
-// each on MI355X), so one counter for 512 workgroups costs 7.8 us per
-// barrier; eight groups cost 2.6 us.  Counters sit 128 bytes apart.
-constexpr int kBarGroups = 8;
-constexpr int kBarStride = 32;           // uint32 between counters
-
-// Arrive: every thread waits until its own memory operations have completed
-// (so its coherent stores are visible device-wide), the workgroup meets, and
-// thread 0 arrives.  k = the workgroup's earlier arrivals, G = grid size.
 __device__ __forceinline__ void barrier_arrive(uint32_t* ctr, int G, uint32_t k) {
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __syncthreads();
-    if (threadIdx.x == 0) {
+    if ((threadIdx.x & (kWave - 1)) == 0) {
         const int ng = G < kBarGroups ? G : kBarGroups;
         const int grp = (int)blockIdx.x % ng;
         const uint32_t members = (uint32_t)(G / ng + (grp < G % ng ? 1 : 0));
@@ -103,230 +436,171 @@ __device__ __forceinline__ void barrier_arrive(uint32_t* ctr, int G, uint32_t k)
     }
 }
 
-// Wait: thread 0 spins until the global counter reaches target (bounded).
-// Once any wait has given up (err bit 0), every later wait returns at once,
-// so a broken barrier costs one spin bound, not one per barrier.
 __device__ __forceinline__ void barrier_wait(uint32_t* ctr, uint32_t target, uint32_t* err) {
-    if (threadIdx.x == 0) {
+    if ((threadIdx.x & (kWave - 1)) == 0) {
         uint32_t spins = 0;
         while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
             if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 1u) break;
             __builtin_amdgcn_s_sleep(1);
             if (++spins > kSpinLimit) {
-                atomicOr(err, 1u);
+                __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 break;
             }
         }
     }
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __syncthreads();
 }
 
-// ---- x into LDS: fp32 row of KS values, optionally RMSNorm-ed -------------
-// x is read with coherent loads (it was written by other workgroups).
-template <int FMT, int KS, bool NORM>
-__device__ __forceinline__ void stage_row(const float* x, const float* gamma, float eps,
-                                          uint32_t* xs, float* red) {
-    using XP = XPieces<FMT, false>;
-    constexpr int NX = KS / 4 / kBlock;
-    constexpr int NP = KS / 4;
-    uint4 xr[NX], gr[NORM ? NX : 1];
-#pragma unroll
-    for (int i = 0; i < NX; i++) xr[i] = coh_load16(x + 4 * XP::index(i));
-    if constexpr (NORM) {
-#pragma unroll
-        for (int i = 0; i < NX; i++) gr[i] = XP::load((const uint4*)gamma, i, NP);
-        float ss = 0.f;
-#pragma unroll
-        for (int i = 0; i < NX; i++) {
-            const float4 v = __builtin_bit_cast(float4, xr[i]);
-            ss = fmaf(v.x, v.x, ss);
-            ss = fmaf(v.y, v.y, ss);
-            ss = fmaf(v.z, v.z, ss);
-            ss = fmaf(v.w, v.w, ss);
-        }
-        const float inv = 1.0f / sqrtf(block_sum(ss, red) / (float)KS + eps);
-#pragma unroll
-        for (int i = 0; i < NX; i++) {
-            const float4 v = __builtin_bit_cast(float4, xr[i]);
-            const float4 g = __builtin_bit_cast(float4, gr[i]);
-            xr[i] = __builtin_bit_cast(uint4, make_float4(g.x * (v.x * inv), g.y * (v.y * inv),
-                                                          g.z * (v.z * inv), g.w * (v.w * inv)));
-        }
-    }
-    XP::template store<NX, true>(xr, 0, NP, xs);
-    __syncthreads();
-}
-
-// ---- one wave's share of one table ----------------------------------------
-// Row pairs of the table are split over the workgroups; pair p of this
-// workgroup's range goes to wave p % 4.  A unit is one chunk step of the
-// wave's current pair; units are pipelined DD deep.
-template <int FMT, int CS>
-struct Stream {
-    using T = Traits<FMT>;
-    static constexpr int K = 64 * CS * T::WPC;
-    static constexpr int DD = 4;         // units in flight per wave
-    PSlot<FMT, kRows> buf[DD];
-    BufPlanes B;
-    int64_t N, pair0;   // first pair of this wave
-    int np, U;          // pairs of this wave, units
-
-    __device__ __forceinline__ void setup(DevPlanes P_, int64_t N_, int G) {
-        B = T::planes(P_, N_, K);
-        N = N_;
-        const int64_t pairs = N / kRows;
-        const int64_t b0 = pairs * blockIdx.x / G, b1 = pairs * (blockIdx.x + 1) / G;
-        const int wave = threadIdx.x / kWave;
-        const int64_t cnt = b1 - b0;
-        np = cnt > wave ? (int)((cnt - wave + kWavesPerBlock - 1) / kWavesPerBlock) : 0;
-        pair0 = b0 + wave;
-        U = np * CS;
-    }
-    __device__ __forceinline__ void load(PSlot<FMT, kRows>& s, int u) {
-        const int lane = threadIdx.x & (kWave - 1);
-        const int uu = U == 0 ? 0 : (u < U ? u : U - 1);
-        const int pi = uu / CS, c = uu - pi * CS;
-        const int64_t pr = pair0 + (int64_t)pi * kWavesPerBlock;
-#pragma unroll
-        for (int r = 0; r < kRows; r++) {
-            int64_t n = pr * kRows + r;
-            n = n < N ? n : N - 1;
-            T::load(s.row[r], B, T::row_off(n, K), c * kWave + lane);
-        }
-    }
-    __device__ __forceinline__ void prefetch() {
-#pragma unroll
-        for (int d = 0; d < DD; d++) load(buf[d], d);
-    }
-    // EPI: store(row pair index, sum of row 0, sum of row 1), called by every lane
-    template <class Epi>
-    __device__ __forceinline__ void run(const uint32_t* xs, Epi&& epi) {
-        const int lane = threadIdx.x & (kWave - 1);
-        float acc[kRows] = {0.f, 0.f};
-        for (int u0 = 0; u0 < U; u0 += DD) {
-            sfor<0, DD>([&](auto dc) {
-                constexpr int d = decltype(dc)::value;
-                const int u = u0 + d;
-                if (u < U) {
-                    const int pi = u / CS, c = u - pi * CS;
-                    uint32_t xv[4 * T::F4];
-                    read_x<FMT>(xs, c * kWave + lane, xv);
-#pragma unroll
-                    for (int r = 0; r < kRows; r++) acc[r] += T::dot(buf[d].row[r], xv);
-                    if (c == CS - 1) {
-                        const float s0 = wave_sum_dpp(acc[0]), s1 = wave_sum_dpp(acc[1]);
-                        epi(pair0 + (int64_t)pi * kWavesPerBlock, s0, s1);
-                        acc[0] = acc[1] = 0.f;
-                    }
-                    load(buf[d], u + DD);
-                }
-            });
-        }
-    }
+struct Lds {
+    float* h;
+    float* x;
+    float* g;
+    uint32_t* xs;
+    float* part;     // [2][kMaxRowsWG]
+    float* red;
 };
+
+// Epilogue of phase f for this workgroup's rows (control wave).  part[0] holds
+// each row's first partial sum, part[1] the second (0 if the row was not
+// shared); part[1] is cleared for the next phase.
+__device__ __forceinline__ void epilogue(const Ctx& c, const PhaseInfo& f, const Bufs& bf,
+                                         const Lds& s, float eps) {
+    (void)eps;
+    const int lane = threadIdx.x & (kWave - 1);
+    int rb, rows;
+    c.rows_of(f.kind, rb, rows);
+    float* p0 = s.part;
+    float* p1 = s.part + kMaxRowsWG;
+    if (f.kind == kGU) {
+        float* m = bf.m + (int64_t)f.layer * bf.ms;
+        for (int i = lane; i < rows / 2; i += kWave) {
+            const float g = p0[2 * i] + p1[2 * i], u = p0[2 * i + 1] + p1[2 * i + 1];
+            coh_store(m + rb / 2 + i, g / (1.0f + expf(-g)) * u);
+        }
+    } else {
+        for (int i = lane; i < rows; i += kWave) {
+            const float v = p0[i] + p1[i];
+            const int n = rb + i;
+            if (f.kind == kQKV) {
+                coh_store(bf.qkv + (int64_t)f.layer * bf.qs + n, v);
+            } else if (f.kind == kLM) {
+                bf.logits[n] = v;
+            } else {
+                // residual add on the h this layer's norm read (held in LDS)
+                const float hn = s.h[n] + v;
+                const int ver = 2 * f.layer + (f.kind == kO ? 1 : 2);
+                coh_store(bf.h(ver) + n, hn);
+                if (f.kind == kDN && f.layer == c.L - 1) bf.h_in[n] = hn;
+            }
+        }
+    }
+    for (int i = lane; i < rows; i += kWave) p1[i] = 0.f;
+}
+
+// Input of phase f into LDS (control wave): the fp32 vector, and gamma for
+// the norm phases (gamma is issued first; it does not wait for the barrier).
+__device__ __forceinline__ void input_gamma(const Ctx& c, const PhaseInfo& f, const Lds& s) {
+    if (f.kind == kQKV) copy_to_lds<false>(c.t->layers[f.layer].g1, s.g, kD);
+    if (f.kind == kGU) copy_to_lds<false>(c.t->layers[f.layer].g2, s.g, kD);
+    if (f.kind == kLM) copy_to_lds<false>(c.t->head.gf, s.g, kD);
+}
+__device__ __forceinline__ void input_x(const PhaseInfo& f, const Bufs& bf, const Lds& s) {
+    if (f.kind == kQKV) copy_to_lds<true>(bf.h(2 * f.layer), s.h, kD);
+    if (f.kind == kO) copy_to_lds<true>(bf.qkv + (int64_t)f.layer * bf.qs, s.x, kD);
+    if (f.kind == kGU) copy_to_lds<true>(bf.h(2 * f.layer + 1), s.h, kD);
+    if (f.kind == kDN) copy_to_lds<true>(bf.m + (int64_t)f.layer * bf.ms, s.x, kF);
+    if (f.kind == kLM) copy_to_lds<true>(bf.h(2 * f.layer), s.h, kD);
+}
+
+// Stage phase f's x (all waves).
+__device__ __forceinline__ void stage_phase(const PhaseInfo& f, float eps, const Lds& s) {
+    const bool norm = f.kind == kQKV || f.kind == kGU || f.kind == kLM;
+    const float* raw = (f.kind == kO || f.kind == kDN) ? s.x : s.h;
+    const int K = f.kind == kDN ? kF : kD;
+    stage_lds(raw, K, norm ? s.g : nullptr, eps, f.fmt == kQ65, s.xs, s.red);
+}
 
 }  // namespace
 
-template <int FMT_LM>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 1))) void decode_persistent_kernel(
-    const DecTable* __restrict__ table, DecTable expect, DecHead head, float eps, float* h,
-    float* logits, int64_t vocab, int64_t nqkv, float* qkv, float* mbuf, uint32_t* ctr,
-    uint32_t* err, int G) {
+__global__ __launch_bounds__(kPT) void decode_persistent_kernel(
+    const DecTable* __restrict__ table, DecTable expect, float eps, Bufs bf,
+    int nqkv, int vocab, uint32_t* ctr, uint32_t* err, int G) {
     extern __shared__ float4 smem[];
-    uint32_t* xs = (uint32_t*)smem;
-    __shared__ float red[kWavesPerBlock];
-    const int lane = threadIdx.x & (kWave - 1);
-    constexpr int D = 4096, F = 12288;
+    char* sb = (char*)smem;
+    const Lds s{(float*)(sb + kLdsH), (float*)(sb + kLdsX), (float*)(sb + kLdsG),
+                (uint32_t*)(sb + kLdsS), (float*)(sb + kLdsP), (float*)(sb + kLdsR)};
     // the layer table in the workspace must be the one prepared for this model
     if (table->magic != expect.magic || table->n_layers != expect.n_layers ||
         table->tag != expect.tag) {
         if (threadIdx.x == 0 && blockIdx.x == 0) atomicOr(err, 2u);
         return;
     }
-    const int n_layers = (int)expect.n_layers;
-    const DecLayer* layers = table->layers;
-    uint32_t target = 0;                 // global counter after the barriers so far
-    uint32_t nbar = 0;                   // this workgroup's arrivals so far
-    const uint32_t per_bar = (uint32_t)(G < kBarGroups ? G : kBarGroups);
+    Ctx c;
+    c.t = (CTable)table;
+    c.L = (int)expect.n_layers;
+    c.P = 4 * c.L + (vocab > 0 ? 1 : 0);
+    c.nqkv = nqkv;
+    c.vocab = vocab;
+    c.G = G;
+    if (c.P == 0) return;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+    for (int i = threadIdx.x; i < 2 * kMaxRowsWG; i += kPT) s.part[i] = 0.f;
 
-    for (int l = 0; l < n_layers; l++) {
-        const DecLayer L = layers[l];
-        // P1: q|k|v = Wqkv rmsnorm(h, gamma1)
-        {
-            Stream<kQ45, 2> st;
-            st.setup(L.qkv, nqkv, G);
-            st.prefetch();
-            if (l > 0) barrier_wait(ctr, target, err);
-            stage_row<kQ45, D, true>(h, L.g1, eps, xs, red);
-            st.run(xs, [&](int64_t p, float s0, float s1) {
-                if (lane == 0) coh_store(qkv + 2 * p, s0);
-                if (lane == 1) coh_store(qkv + 2 * p + 1, s1);
-            });
-            barrier_arrive(ctr, G, nbar++);
-            target += per_bar;
+    if (wave == kCW) {
+        // ------------------------------------------------ control wave
+        const uint32_t per_bar = (uint32_t)(G < kBarGroups ? G : kBarGroups);
+        PhaseInfo f = c.info(0);
+        input_gamma(c, f, s);
+        input_x(f, bf, s);
+        __builtin_amdgcn_s_waitcnt(0);
+        wg_barrier();
+        stage_phase(f, eps, s);
+        wg_barrier();
+        for (int q = 1; q < c.P; q++) {
+            wg_barrier();                                  // phase q-1's partials are in LDS
+            const PhaseInfo n = c.info(q);
+            input_gamma(c, n, s);                          // independent of the barrier
+            epilogue(c, f, bf, s, eps);
+            __builtin_amdgcn_s_waitcnt(0);                 // own stores and gamma complete
+            barrier_arrive(ctr, G, (uint32_t)(q - 1));
+            barrier_wait(ctr, per_bar * (uint32_t)q, err);
+            input_x(n, bf, s);
+            __builtin_amdgcn_s_waitcnt(0);
+            wg_barrier();
+            stage_phase(n, eps, s);
+            wg_barrier();
+            f = n;
         }
-        // P2: h += Wo q
-        {
-            Stream<kQ45, 2> st;
-            st.setup(L.o, D, G);
-            st.prefetch();
-            barrier_wait(ctr, target, err);
-            stage_row<kQ45, D, false>(qkv, nullptr, 0.f, xs, red);
-            st.run(xs, [&](int64_t p, float s0, float s1) {
-                if (lane == 0) coh_store(h + 2 * p, coh_load(h + 2 * p) + s0);
-                if (lane == 1) coh_store(h + 2 * p + 1, coh_load(h + 2 * p + 1) + s1);
-            });
-            barrier_arrive(ctr, G, nbar++);
-            target += per_bar;
-        }
-        // P3: m = silu(Wg b) * (Wu b), b = rmsnorm(h, gamma2)
-        {
-            Stream<kQ45, 2> st;
-            st.setup(L.gu, 2 * F, G);
-            st.prefetch();
-            barrier_wait(ctr, target, err);
-            stage_row<kQ45, D, true>(h, L.g2, eps, xs, red);
-            st.run(xs, [&](int64_t p, float g, float u) {
-                if (lane == 0) coh_store(mbuf + p, g / (1.0f + expf(-g)) * u);
-            });
-            barrier_arrive(ctr, G, nbar++);
-            target += per_bar;
-        }
-        // P4: h += Wdown m
-        {
-            auto down = [&](auto fc) {
-                constexpr int FMT = decltype(fc)::value;
-                Stream<FMT, 6> st;
-                st.setup(L.dn, D, G);
-                st.prefetch();
-                barrier_wait(ctr, target, err);
-                stage_row<FMT, F, false>(mbuf, nullptr, 0.f, xs, red);
-                st.run(xs, [&](int64_t p, float s0, float s1) {
-                    if (lane == 0) coh_store(h + 2 * p, coh_load(h + 2 * p) + s0);
-                    if (lane == 1) coh_store(h + 2 * p + 1, coh_load(h + 2 * p + 1) + s1);
-                });
-            };
-            if (L.fmt_dn == kQ65)
-                down(ICd<kQ65>{});
-            else
-                down(ICd<kQ45>{});
-            barrier_arrive(ctr, G, nbar++);
-            target += per_bar;
-        }
+        wg_barrier();
+        epilogue(c, f, bf, s, eps);
+        return;
     }
-    // logits = Wlm rmsnorm(h, gamma_f)
-    if (vocab > 0) {
-        Stream<FMT_LM, 2> st;
-        st.setup(head.lm, vocab, G);
-        st.prefetch();
-        if (n_layers > 0) barrier_wait(ctr, target, err);
-        stage_row<FMT_LM, D, true>(h, head.gf, eps, xs, red);
-        st.run(xs, [&](int64_t p, float s0, float s1) {
-            if (lane == 0) logits[2 * p] = s0;
-            if (lane == 1) logits[2 * p + 1] = s1;
-        });
+
+    // ---------------------------------------------------- compute waves
+    Raw buf[kDD];
+    load_first(buf, span_of(c, 0, wave));
+    wg_barrier();                                          // x of phase 0 in LDS
+    stage_phase(c.info(0), eps, s);
+    wg_barrier();
+    for (int p = 0; p < c.P; p++) {
+        if (p > 0) {
+            wg_barrier();                                  // B1: partials of p-1 written
+            wg_barrier();                                  // B2: x of p in LDS
+            stage_phase(c.info(p), eps, s);
+            wg_barrier();                                  // B3: staged
+        }
+        const Span C = span_of(c, p, wave);
+        Pos q;
+        q.rc = q.rl = C.row0;
+        q.cc = q.cl = C.cs0;
+        q.shared = C.cs0 != 0;
+        q.acc = 0.f;
+#pragma unroll
+        for (int d = 0; d < kDD; d++) step(q.rl, q.cl, C.CS);
+        run_main(buf, C, q, s.xs, s.part);
+        // the last phase refills from itself (loads that are never used)
+        run_tail(buf, C, span_of(c, p + 1 < c.P ? p + 1 : p, wave), q, s.xs, s.part);
     }
+    wg_barrier();                                          // partials of the last phase
 }
 
 __global__ void decode_reset_kernel(uint32_t* ctr, uint32_t* err) {
@@ -337,43 +611,39 @@ __global__ void decode_reset_kernel(uint32_t* ctr, uint32_t* err) {
     if (threadIdx.x < kBarGroups) ctr[kBarStride * (1 + threadIdx.x)] = 0u;
 }
 
-template <int FMT_LM>
-static hipError_t launch_persistent_lm(const DecTable* table, DecTable expect, DecHead head,
-                                       float eps, float* h, float* logits, int64_t vocab,
-                                       int64_t nqkv, float* qkv, float* mbuf, uint32_t* ctr,
-                                       uint32_t* err, hipStream_t stream) {
-    auto kern = decode_persistent_kernel<FMT_LM>;
-    const size_t lds = (size_t)(12288 / 32) * Stride<kQ65>::DW * 4;   // K = 12288 staged
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
+hipError_t launch_decode_persistent(const DecTable* table, DecTable expect,
+                                    float eps, float* h, float* logits, int64_t vocab,
+                                    int64_t nqkv, const DecodeBuffers& db, uint32_t* ctr,
+                                    uint32_t* err, hipStream_t stream) {
+    auto kern = decode_persistent_kernel;
+    const size_t lds = kLdsTotal;
+    hipError_t e = ensure_lds<decode_persistent_kernel>(lds);
     if (e != hipSuccess) return e;
+    int dev = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
     int cus = 0, per_cu = 0;
     if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
         return e;
-    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kern, kBlock, lds)) !=
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kern, kPT, lds)) !=
         hipSuccess)
         return e;
     if (per_cu < 1) return hipErrorInvalidConfiguration;
-    const int per = per_cu < 2 ? per_cu : 2;
-    int G = cus * per;
+    int G = cus;
+    // every phase's rows per workgroup must fit the LDS partials
+    auto fits = [&](int64_t n, int64_t q) { return q * ((n / q + G - 1) / G) <= kMaxRowsWG; };
+    if (!fits(vocab, 1) || !fits(nqkv, 1) || !fits(2 * kF, 2)) return hipErrorInvalidConfiguration;
+    // a row is shared by at most two waves (so its two partial sums add in
+    // either order to the same value): every wave takes at least CS - 1 = 5
+    // units of the down product's six-step rows
+    if ((kD / G) * 6 / kCW < 5) return hipErrorInvalidConfiguration;
+    Bufs bf{h, db.hv, db.qkv, db.m, logits, db.hs, db.qs, db.ms};
+    int nq = (int)nqkv, nv = (int)vocab;
     hipLaunchKernelGGL(decode_reset_kernel, dim3(1), dim3(64), 0, stream, ctr, err);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    void* args[] = {(void*)&table, (void*)&expect, (void*)&head, (void*)&eps, (void*)&h,
-                    (void*)&logits, (void*)&vocab, (void*)&nqkv, (void*)&qkv, (void*)&mbuf,
-                    (void*)&ctr, (void*)&err, (void*)&G};
-    return hipLaunchCooperativeKernel((const void*)kern, dim3(G), dim3(kBlock), args, (unsigned)lds,
+    void* args[] = {(void*)&table, (void*)&expect, (void*)&eps, (void*)&bf,
+                    (void*)&nq, (void*)&nv, (void*)&ctr, (void*)&err, (void*)&G};
+    return hipLaunchCooperativeKernel((const void*)kern, dim3(G), dim3(kPT), args, (unsigned)lds,
                                       stream);
-}
-
-hipError_t launch_decode_persistent(const DecTable* table, DecTable expect, DecHead head,
-                                    float eps, float* h, float* logits, int64_t vocab,
-                                    int64_t nqkv, float* qkv, float* mbuf, uint32_t* ctr,
-                                    uint32_t* err, hipStream_t stream) {
-    if (head.fmt_lm == kQ65)
-        return launch_persistent_lm<kQ65>(table, expect, head, eps, h, logits, vocab, nqkv, qkv,
-                                          mbuf, ctr, err, stream);
-    return launch_persistent_lm<kQ45>(table, expect, head, eps, h, logits, vocab, nqkv, qkv, mbuf,
-                                      ctr, err, stream);
 }
 
 }  // namespace mbq

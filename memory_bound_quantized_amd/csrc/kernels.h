@@ -121,28 +121,35 @@ struct DecLayer {
     int32_t fmt_dn;
     int32_t pad;
 };
-struct DecTable {
-    uint64_t magic;             // kDecMagic once prepared
-    int64_t n_layers;
-    uint64_t tag;               // identifies the model the table was written for
-    uint64_t pad;
-    DecLayer layers[1];         // n_layers entries
-};
 struct DecHead {
     DevPlanes lm;
     const float* gf;
     int32_t fmt_lm;
     int32_t pad;
 };
+struct DecTable {
+    uint64_t magic;             // kDecMagic once prepared
+    int64_t n_layers;
+    uint64_t tag;               // identifies the model the table was written for
+    uint64_t pad;
+    DecHead head;               // the vocabulary product and the final norm
+    DecLayer layers[1];         // n_layers entries
+};
 constexpr uint64_t kDecMagic = 0x31706564716d6266ull;
 
 // Requires d = dq = 4096, f = 12288, Q45 qkv/o/gate-up, Q45 or Q65 down and
-// lm head, an even number of qkv rows and of vocab rows.  ctr and err are
-// zeroed by a small kernel first; err != 0 afterwards means a barrier spin
-// gave up (1) or the table did not match (2).
-hipError_t launch_decode_persistent(const DecTable* table, DecTable expect, DecHead head,
-                                    float eps, float* h, float* logits, int64_t vocab,
-                                    int64_t nqkv, float* qkv, float* mbuf, uint32_t* ctr,
+// lm head.  ctr and err are zeroed by a small kernel first; err != 0
+// afterwards means a barrier spin gave up (1) or the table did not match (2).
+// Activation buffers of the one-launch step, each written once per token:
+// h versions 1 .. 2L (after each residual add), q|k|v and m per layer.
+struct DecodeBuffers {
+    float* hv;
+    float* qkv;
+    float* m;
+    int64_t hs, qs, ms;   // floats between consecutive versions / layers
+};
+hipError_t launch_decode_persistent(const DecTable* table, DecTable expect, float eps, float* h,
+                                    float* logits, int64_t vocab, int64_t nqkv, const DecodeBuffers& bufs, uint32_t* ctr,
                                     uint32_t* err, hipStream_t stream);
 
 // y[m][n] = 0 for the K == 0 case (rows of length ldy, first N entries).

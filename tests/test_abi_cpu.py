@@ -269,9 +269,10 @@ def test_decode_argument_checks():
     m = _model()
     nb = ctypes.c_size_t()
     assert L.mbq_decode_workspace_bytes(ctypes.byref(m), ctypes.byref(nb)) == _lib.OK
-    # status words, q|k|v, gated activations, then the one-launch step's layer table
-    table = 32 + 1 * 152
-    assert nb.value == 2048 + (4096 + 2048) * 4 + 12288 * 4 + (table + 255) // 256 * 256
+    # status words, q|k|v and gated activations per layer, two h versions per
+    # layer, then the one-launch step's table (header, vocabulary head, layers)
+    table = 32 + 48 + 1 * 152
+    assert nb.value == 2048 + (4096 + 2048) * 4 + 12288 * 4 + 2 * 4096 * 4 + (table + 255) // 256 * 256
     h, lg, ws = BASE + 0x7000000000, BASE + 0x7100000000, BASE + 0x7200000000
     st = lambda m, h=h, lg=lg, ws=ws, n=nb.value: L.mbq_decode_step(ctypes.byref(m), h, lg, ws, n, None)
     assert st(m, n=nb.value - 1) == _lib.EINVAL                             # workspace too small
@@ -289,8 +290,6 @@ def test_decode_argument_checks():
     ps = lambda m, h=h, lg=lg, ws=ws, n=nb.value: L.mbq_decode_step_persistent(ctypes.byref(m), h, lg, ws, n, None)
     assert ps(m, n=nb.value - 1) == _lib.EINVAL
     assert ps(_model(dkv=512, f=8192)) in (_lib.EUNSUPPORTED,)               # f must be 12288
-    odd = _model(vocab=1001)
-    assert ps(odd) == _lib.EUNSUPPORTED                                     # even vocab rows
     q65o = _model()
     q65o.layers[0].o.fmt = 2
     q65o.layers[0].o.codes_hi = BASE + 0x900000
