@@ -261,11 +261,26 @@ def decode_row(workloads, torch, dev, read_peak, ntok=20):
     B = model.weight_bytes + 4 * 36 * 2 * model.d + 4 * model.d
     B_all = B + 4 * (36 * (model.dq + 2 * model.dkv + model.f + 6 * model.d) + model.vocab)
     floor_ms = B / (read_peak * 1e9) * 1e3
+    # the same token in one cooperative launch (not capturable: timed as
+    # back-to-back launches between HIP events on the current stream)
+    hp, lp = h.clone(), torch.empty_like(logits)
+    model.step_persistent(hp, lp)
+    torch.cuda.synchronize()
+    ok = model.status() == 0
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(ntok):
+        model.step_persistent(hp, lp)
+    b.record()
+    torch.cuda.synchronize()
+    ms_p = a.elapsed_time(b) / ntok
     row = {"ms_per_token": round(ms, 4), "tokens_per_s": round(1e3 / ms, 1),
            "weight_bytes": model.weight_bytes, "bytes_per_token": int(B_all),
            "gbs": round(B_all / (ms * 1e-3) / 1e9, 1),
            "floor_ms_at_read_peak": round(floor_ms, 4), "ratio_to_floor": round(ms / floor_ms, 3),
-           "launches_per_token": 4 * 36 + 1, "tokens_timed": ntok}
+           "launches_per_token": 4 * 36 + 1, "tokens_timed": ntok,
+           "one_launch": {"ms_per_token": round(ms_p, 4), "ratio_to_floor": round(ms_p / floor_ms, 3),
+                          "status_ok": ok}}
     del model, g
     torch.cuda.empty_cache()
     return row

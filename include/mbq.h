@@ -203,7 +203,8 @@ int mbq_gemv_fused(const mbq_qweight* W, const float* x, const float* gamma, flo
  * h: device fp32 [d], 16-byte aligned, updated in place; logits: device fp32
  * [vocab].  workspace: device, 256-byte aligned, at least
  * mbq_decode_workspace_bytes bytes, not overlapping h or logits; it holds
- * q|k|v and the gated activations of the layer being computed. */
+ * q|k|v and the gated activations (the launch chain uses the first layer's
+ * slots; the one-launch step below uses all of them). */
 typedef struct mbq_decode_layer {
     mbq_qweight qkv;
     mbq_qweight o;
@@ -229,19 +230,26 @@ int mbq_decode_step(const mbq_decode_model* model, float* h, float* logits, void
 /* The same token in ONE launch ([one-serial-kernel] "The kernel that was never
  * built": the token's pieces of work without a return to the host between
  * them; [roofline-holds] "Where the time goes": the per-kernel toll).  Every
- * workgroup stays resident (cooperative launch); the four steps of a layer
- * are separated by grid-wide barriers, and each wave issues the loads of its
- * next table's weights before it waits at the barrier, so the weight stream
- * does not stop between tables.  Same arithmetic and the same results within
- * tolerance as mbq_decode_step (the norm is computed inside every workgroup).
+ * workgroup stays resident (cooperative launch, one per compute unit); the
+ * four steps of a layer and the vocabulary product are phases separated by
+ * grid-wide barriers.  Each compute wave walks one stream of weight chunks
+ * through all phases and keeps its next chunks in flight across every
+ * barrier, so the weight stream does not stop between tables; one control
+ * wave per workgroup applies each phase's epilogue, meets the barrier and
+ * brings the next input into LDS.  Same arithmetic and the same results
+ * within tolerance as mbq_decode_step (the norm is computed inside every
+ * workgroup; a row's sum may be split between two waves).
  *
- * mbq_decode_prepare writes the device table of the layers into the
- * workspace (a copy and a stream synchronisation; call it once per model and
- * again whenever a descriptor changes).  mbq_decode_step_persistent checks
- * that the workspace holds the table of this model (by an identity of its
- * pointers) and does nothing but set the status word otherwise.
+ * mbq_decode_prepare writes the device table of the layers and the
+ * vocabulary product into the workspace (a copy and a stream
+ * synchronisation; call it once per model and again whenever a descriptor
+ * changes).  mbq_decode_step_persistent checks that the workspace holds the
+ * table of this model (by an identity of its pointers) and does nothing but
+ * set the status word otherwise.  The workspace also holds each layer's
+ * q|k|v and gated activations and two versions of h per layer: every
+ * activation that crosses workgroups is written once per token.
  * Needs d = dq = 4096, f = 12288, Q45 qkv / o / gate_up, Q45 or Q65 down
- * and lm_head, an even dq + 2 dkv and an even vocab (MBQ_EUNSUPPORTED).
+ * and lm_head, and row counts that fit the device (MBQ_EUNSUPPORTED).
  * After the step the 32-bit word at byte 4 of the workspace is 0 on success,
  * bit 0 set if a barrier wait gave up (every wave still ends), bit 1 set if
  * the table did not match.  Not for graph capture (cooperative launch). */

@@ -20,8 +20,10 @@
 // Phase p's rows are split into one contiguous block per workgroup (row
 // pairs for gu).  A unit is one chunk step of one row (lane l reads chunk
 // 64 c + l: a 1 KiB burst per wave, [mountain-runs] section 3); the
-// workgroup's units are split evenly over its 15 compute waves, so a row can
-// be shared by two waves, whose partial sums meet in LDS.
+// workgroup's units (row-major) are dealt round-robin to its 15 compute
+// waves, so at any moment the workgroup reads one contiguous window of the
+// table.  Each unit's sum goes to its own LDS slot, and the control wave adds
+// a row's chunk steps in order.
 //
 // Wave 15 is the control wave.  It streams no weights; at each phase
 // boundary it applies the finished phase's epilogue (store, residual add or
@@ -51,7 +53,7 @@ namespace {
 constexpr int kPW = 16;                 // waves per workgroup
 constexpr int kPT = kPW * kWave;        // threads per workgroup
 constexpr int kCW = kPW - 1;            // compute waves; wave kCW is the control wave
-constexpr int kDD = 5;                  // units in flight per compute wave
+constexpr int kDD = 4;                  // units in flight per compute wave (4 measured faster than 5)
 constexpr int kD = 4096, kF = 12288;
 constexpr int kMaxRowsWG = 1024;        // rows of one phase per workgroup
 constexpr uint32_t kSpinLimit = 1u << 22;   // about 0.2 s of 64-cycle sleeps
@@ -66,7 +68,7 @@ constexpr int kLdsH = 0;                               // fp32 h being normalise
 constexpr int kLdsX = kLdsH + 4 * kD;                  // fp32 q or m [12288]
 constexpr int kLdsG = kLdsX + 4 * kF;                  // fp32 gamma [4096]
 constexpr int kLdsS = kLdsG + 4 * kD;                  // staged x
-constexpr int kLdsP = kLdsS + (kF / 32) * Stride<kQ65>::DW * 4;   // row partials [2][kMaxRowsWG]
+constexpr int kLdsP = kLdsS + (kF / 32) * Stride<kQ65>::DW * 4;   // unit sums [CS][rows]
 constexpr int kLdsR = kLdsP + 2 * 4 * kMaxRowsWG;      // block-sum scratch [16]
 constexpr int kLdsTotal = kLdsR + 4 * kPW;
 static_assert(Stride<kQ45>::DW == Stride<kQ65>::DW, "one staged stride for both formats");
@@ -173,15 +175,15 @@ struct Bufs {
 };
 
 // ---- one compute wave's share of one phase ---------------------------------
-// The workgroup's units of a phase (rows x chunk steps, row-major) are split
-// evenly over the compute waves: this wave takes U of them, starting at row
-// row0 (relative to the workgroup's first row) and chunk step cs0.  Upad
-// rounds U up to a multiple of kDD (at least kDD) with units that compute
-// nothing, so that the unit stream crosses into the next phase with its
-// slots in order: the loads of the next phase's first kDD units are issued
-// in the last kDD steps of this one.
+// The workgroup's units of a phase (rows x chunk steps, row-major) are dealt
+// round-robin: compute wave w takes units w, w + 15, w + 30, ...: U of them,
+// the first at row row0 (relative to the workgroup's first row) and chunk
+// step cs0.  Upad rounds U up to a multiple of kDD (at least kDD) with units
+// that compute nothing, so that the unit stream crosses into the next phase
+// with its slots in order: the loads of the next phase's first kDD units are
+// issued in the last kDD steps of this one.
 struct Span {
-    int U, Upad, CS, row_base, row0, cs0;
+    int U, Upad, CS, rows, row_base, row0, cs0;
     BufPlanes B;
     int fmt;
 };
@@ -192,38 +194,43 @@ __device__ __forceinline__ Span span_of(const Ctx& c, int p, int w) {
     const int k = f.kind;
     s.CS = f.CS;
     s.fmt = f.fmt;
-    int rows;
-    c.rows_of(k, s.row_base, rows);
-    const int Uwg = rows * f.CS;
-    const int u0 = Uwg * w / kCW, u1 = Uwg * (w + 1) / kCW;
-    s.U = u1 - u0;
+    c.rows_of(k, s.row_base, s.rows);
+    const int Uwg = s.rows * f.CS;
+    s.U = Uwg > w ? (Uwg - w + kCW - 1) / kCW : 0;
     s.Upad = s.U <= kDD ? kDD : (s.U + kDD - 1) / kDD * kDD;
-    s.row0 = f.CS == 6 ? u0 / 6 : u0 >> 1;
-    s.cs0 = u0 - s.row0 * f.CS;
+    s.row0 = f.CS == 6 ? w / 6 : w >> 1;
+    s.cs0 = w - s.row0 * f.CS;
     const int K = 2048 * f.CS;
     s.B = f.fmt == kQ65 ? Traits<kQ65>::planes(f.P, f.N, K) : Traits<kQ45>::planes(f.P, f.N, K);
     return s;
 }
 
 // Issue the loads of one unit (row relative to the span's base, chunk step
-// cs) into r.  Padding units past the table read outside its buffer
-// resources, which returns 0 without a memory access; their data is never
-// used, and every unit issues the same loads.  Per row a table holds K/2
+// cs) into r.  A padding unit (real == false) reads outside the table's
+// buffer resources, which returns 0 without a memory access; its data is
+// never used, and every unit issues the same loads.  Per row a table holds K/2
 // code bytes, K/4 high-bit bytes, K/16 scale bytes and K/128 super-scale
 // bytes (Q45 and Q65 alike), K = 2048 CS.
-__device__ __forceinline__ void load_unit(Raw& r, const Span& s, int row, int cs) {
+__device__ __forceinline__ void load_unit(Raw& r, const Span& s, int row, int cs, bool real) {
     const int lane = threadIdx.x & (kWave - 1);
     const uint32_t o3 = (uint32_t)(s.row_base + row) * (uint32_t)(16 * s.CS);
     const uint32_t b = (uint32_t)(cs * kWave + lane);
-    r.a = bload<uint4, true>(s.B.p0, 16u * b, o3 << 6);
-    r.qh = bload<uint2, true>(s.B.p1, 8u * b, o3 << 5);
-    r.sc2 = bload<uint32_t, true>(s.B.p2, 4u * (b >> 1), o3 << 3);
-    r.d2 = bload<uint32_t, true>(s.B.p3, 4u * (b >> 4), o3);
+    // a padding unit reads past every plane (0xF0000000 exceeds any plane's
+    // size; the lane offsets are below 2^16, so the sum cannot wrap)
+    const uint32_t pad = real ? 0u : 0xF0000000u;
+    r.a = bload<uint4, true>(s.B.p0, 16u * b, real ? o3 << 6 : pad);
+    r.qh = bload<uint2, true>(s.B.p1, 8u * b, real ? o3 << 5 : pad);
+    r.sc2 = bload<uint32_t, true>(s.B.p2, 4u * (b >> 1), real ? o3 << 3 : pad);
+    r.d2 = bload<uint32_t, true>(s.B.p3, 4u * (b >> 4), real ? o3 : pad);
 }
 
+// The wave's next unit: kCW units on in the workgroup's row-major order.
 __device__ __forceinline__ void step(int& row, int& cs, int CS) {
-    if (++cs == CS) {
-        cs = 0;
+    static_assert(kCW == 15, "strides below are for 15 compute waves");
+    cs += CS == 6 ? 3 : 1;           // 15 = 2 * 6 + 3 = 7 * 2 + 1
+    row += CS == 6 ? 2 : 7;
+    if (cs >= CS) {
+        cs -= CS;
         row++;
     }
 }
@@ -233,7 +240,7 @@ __device__ __forceinline__ void load_first(Raw (&buf)[kDD], const Span& s) {
     int row = s.row0, cs = s.cs0;
 #pragma unroll
     for (int d = 0; d < kDD; d++) {
-        load_unit(buf[d], s, row, cs);
+        load_unit(buf[d], s, row, cs, d < s.U);
         step(row, cs, s.CS);
     }
 }
@@ -241,30 +248,20 @@ __device__ __forceinline__ void load_first(Raw (&buf)[kDD], const Span& s) {
 // Where a compute wave is in the current phase.
 struct Pos {
     int rc, cc;          // unit being computed (row, chunk step)
-    bool shared;         // row rc began in the previous wave's range
     int rl, cl;          // unit being loaded, kDD ahead
-    float acc;
 };
 
-// Compute unit u of C from slot r, with the row sum to LDS at the row's end
-// or the range's end: part[0][row] for a row that starts in this wave's
-// range, part[1][row] for the first row when it began in the previous one.
+// Compute unit u of C from slot r; its sum goes to part[cc][row].
 __device__ __forceinline__ void compute_unit(const Raw& r, const Span& C, int u, Pos& q,
                                              const uint32_t* xs, float* part) {
     const int lane = threadIdx.x & (kWave - 1);
     if (u < C.U) {
         uint32_t xv[4 * Traits<kQ45>::F4];
         read_x<kQ45>(xs, q.cc * kWave + lane, xv);
-        if (C.fmt == kQ65)
-            q.acc += Traits<kQ65>::dot(as_q65(r, lane), xv);
-        else
-            q.acc += Traits<kQ45>::dot(as_q45(r, lane), xv);
-        if (q.cc == C.CS - 1 || u == C.U - 1) {
-            const float sum = wave_sum_dpp(q.acc);
-            if (lane == 0) part[(q.shared ? kMaxRowsWG : 0) + q.rc] = sum;
-            q.acc = 0.f;
-            q.shared = false;
-        }
+        const float v = C.fmt == kQ65 ? Traits<kQ65>::dot(as_q65(r, lane), xv)
+                                       : Traits<kQ45>::dot(as_q45(r, lane), xv);
+        const float sum = wave_sum_dpp(v);
+        if (lane == 0) part[q.cc * C.rows + q.rc] = sum;
         step(q.rc, q.cc, C.CS);
     }
 }
@@ -277,22 +274,22 @@ __device__ __forceinline__ void run_main(Raw (&buf)[kDD], const Span& C, Pos& q,
 #pragma unroll
         for (int d = 0; d < kDD; d++) {
             compute_unit(buf[d], C, g + d, q, xs, part);
-            load_unit(buf[d], C, q.rl, q.cl);
+            load_unit(buf[d], C, q.rl, q.cl, g + d + kDD < C.U);
             step(q.rl, q.cl, C.CS);
         }
     }
 }
 
 // The last kDD units of a phase: each slot is refilled with the next phase's
-// first units.
-__device__ __forceinline__ void run_tail(Raw (&buf)[kDD], const Span& C, const Span& Nx, Pos& q,
-                                         const uint32_t* xs, float* part) {
+// first units (with padding units after the last phase).
+__device__ __forceinline__ void run_tail(Raw (&buf)[kDD], const Span& C, const Span& Nx, bool last,
+                                         Pos& q, const uint32_t* xs, float* part) {
     const int g = C.Upad - kDD;
     int rn = Nx.row0, cn = Nx.cs0;
 #pragma unroll
     for (int d = 0; d < kDD; d++) {
         compute_unit(buf[d], C, g + d, q, xs, part);
-        load_unit(buf[d], Nx, rn, cn);
+        load_unit(buf[d], Nx, rn, cn, d < Nx.U && !last);
         step(rn, cn, Nx.CS);
     }
 }
@@ -455,30 +452,31 @@ struct Lds {
     float* x;
     float* g;
     uint32_t* xs;
-    float* part;     // [2][kMaxRowsWG]
+    float* part;     // [CS][rows] of the phase being computed
     float* red;
 };
 
-// Epilogue of phase f for this workgroup's rows (control wave).  part[0] holds
-// each row's first partial sum, part[1] the second (0 if the row was not
-// shared); part[1] is cleared for the next phase.
+// Epilogue of phase f for this workgroup's rows (control wave).  part holds
+// one sum per unit, part[cs][row]; a row's chunk steps are added in order.
 __device__ __forceinline__ void epilogue(const Ctx& c, const PhaseInfo& f, const Bufs& bf,
-                                         const Lds& s, float eps) {
-    (void)eps;
+                                         const Lds& s) {
     const int lane = threadIdx.x & (kWave - 1);
     int rb, rows;
     c.rows_of(f.kind, rb, rows);
-    float* p0 = s.part;
-    float* p1 = s.part + kMaxRowsWG;
+    auto row_sum = [&](int i) {
+        float v = s.part[i];
+        for (int cs = 1; cs < f.CS; cs++) v += s.part[cs * rows + i];
+        return v;
+    };
     if (f.kind == kGU) {
         float* m = bf.m + (int64_t)f.layer * bf.ms;
         for (int i = lane; i < rows / 2; i += kWave) {
-            const float g = p0[2 * i] + p1[2 * i], u = p0[2 * i + 1] + p1[2 * i + 1];
+            const float g = row_sum(2 * i), u = row_sum(2 * i + 1);
             coh_store(m + rb / 2 + i, g / (1.0f + expf(-g)) * u);
         }
     } else {
         for (int i = lane; i < rows; i += kWave) {
-            const float v = p0[i] + p1[i];
+            const float v = row_sum(i);
             const int n = rb + i;
             if (f.kind == kQKV) {
                 coh_store(bf.qkv + (int64_t)f.layer * bf.qs + n, v);
@@ -493,7 +491,6 @@ __device__ __forceinline__ void epilogue(const Ctx& c, const PhaseInfo& f, const
             }
         }
     }
-    for (int i = lane; i < rows; i += kWave) p1[i] = 0.f;
 }
 
 // Input of phase f into LDS (control wave): the fp32 vector, and gamma for
@@ -543,7 +540,6 @@ __global__ __launch_bounds__(kPT) void decode_persistent_kernel(
     c.G = G;
     if (c.P == 0) return;
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
-    for (int i = threadIdx.x; i < 2 * kMaxRowsWG; i += kPT) s.part[i] = 0.f;
 
     if (wave == kCW) {
         // ------------------------------------------------ control wave
@@ -559,7 +555,7 @@ __global__ __launch_bounds__(kPT) void decode_persistent_kernel(
             wg_barrier();                                  // phase q-1's partials are in LDS
             const PhaseInfo n = c.info(q);
             input_gamma(c, n, s);                          // independent of the barrier
-            epilogue(c, f, bf, s, eps);
+            epilogue(c, f, bf, s);
             __builtin_amdgcn_s_waitcnt(0);                 // own stores and gamma complete
             barrier_arrive(ctr, G, (uint32_t)(q - 1));
             barrier_wait(ctr, per_bar * (uint32_t)q, err);
@@ -571,7 +567,7 @@ __global__ __launch_bounds__(kPT) void decode_persistent_kernel(
             f = n;
         }
         wg_barrier();
-        epilogue(c, f, bf, s, eps);
+        epilogue(c, f, bf, s);
         return;
     }
 
@@ -592,13 +588,11 @@ __global__ __launch_bounds__(kPT) void decode_persistent_kernel(
         Pos q;
         q.rc = q.rl = C.row0;
         q.cc = q.cl = C.cs0;
-        q.shared = C.cs0 != 0;
-        q.acc = 0.f;
 #pragma unroll
         for (int d = 0; d < kDD; d++) step(q.rl, q.cl, C.CS);
         run_main(buf, C, q, s.xs, s.part);
-        // the last phase refills from itself (loads that are never used)
-        run_tail(buf, C, span_of(c, p + 1 < c.P ? p + 1 : p, wave), q, s.xs, s.part);
+        const bool last = p + 1 == c.P;
+        run_tail(buf, C, span_of(c, last ? p : p + 1, wave), last, q, s.xs, s.part);
     }
     wg_barrier();                                          // partials of the last phase
 }
@@ -629,13 +623,12 @@ hipError_t launch_decode_persistent(const DecTable* table, DecTable expect,
         return e;
     if (per_cu < 1) return hipErrorInvalidConfiguration;
     int G = cus;
-    // every phase's rows per workgroup must fit the LDS partials
-    auto fits = [&](int64_t n, int64_t q) { return q * ((n / q + G - 1) / G) <= kMaxRowsWG; };
-    if (!fits(vocab, 1) || !fits(nqkv, 1) || !fits(2 * kF, 2)) return hipErrorInvalidConfiguration;
-    // a row is shared by at most two waves (so its two partial sums add in
-    // either order to the same value): every wave takes at least CS - 1 = 5
-    // units of the down product's six-step rows
-    if ((kD / G) * 6 / kCW < 5) return hipErrorInvalidConfiguration;
+    // every phase's unit sums per workgroup must fit in LDS (CS x rows)
+    auto fits = [&](int64_t n, int64_t q, int64_t cs) {
+        return cs * q * ((n / q + G - 1) / G) <= 2 * kMaxRowsWG;
+    };
+    if (!fits(vocab, 1, 2) || !fits(nqkv, 1, 2) || !fits(2 * kF, 2, 2) || !fits(kD, 1, 6))
+        return hipErrorInvalidConfiguration;
     Bufs bf{h, db.hv, db.qkv, db.m, logits, db.hs, db.qs, db.ms};
     int nq = (int)nqkv, nv = (int)vocab;
     hipLaunchKernelGGL(decode_reset_kernel, dim3(1), dim3(64), 0, stream, ctr, err);
