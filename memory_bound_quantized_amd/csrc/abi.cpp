@@ -401,7 +401,8 @@ static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 static int check_decode(const mbq_decode_model* m, const char* fn) {
     if (!m) return fail(MBQ_EINVAL, "%s: model is NULL", fn);
-    if (m->n_layers < 0 || m->d <= 0 || m->dq < 0 || m->dkv < 0 || m->f <= 0 || m->vocab < 0)
+    if (m->n_layers < 0 || m->d <= 0 || m->dq < 0 || m->dkv < 0 || m->f < 0 ||
+        (m->n_layers > 0 && m->f == 0) || m->vocab < 0)
         return fail(MBQ_EINVAL, "%s: bad model dimensions", fn);
     if (!(m->eps >= 0.f) || m->eps == __builtin_inff()) return fail(MBQ_EINVAL, "%s: bad eps", fn);
     if (m->n_layers > 0 && !m->layers) return fail(MBQ_EINVAL, "%s: layers is NULL", fn);
@@ -591,7 +592,7 @@ int mbq_decode_step_persistent(const mbq_decode_model* m, float* h, float* logit
     int rc = check_decode(m, fn);
     if (rc) return rc;
     if ((rc = check_workspace(m, h, logits, workspace, workspace_bytes, fn))) return rc;
-    if (m->d != 4096 || m->dq != 4096 || m->f != 12288)
+    if (m->d != 4096 || (m->n_layers > 0 && (m->dq != 4096 || m->f != 12288)))
         return fail(MBQ_EUNSUPPORTED, "%s: the one-launch step needs d = dq = 4096 and f = 12288", fn);
     for (int l = 0; l < m->n_layers; l++) {
         const mbq_decode_layer& L = m->layers[l];

@@ -173,6 +173,39 @@ def test_persistent_step_matches_oracle_chain(layers, vocab):
     assert rel_l2(lg2.cpu().numpy(), logits.cpu().numpy()) <= 1e-4
 
 
+@pytest.mark.parametrize("layers,vocab,head", [(1, 1001, "q65"), (0, 777, "q65"), (2, 2048, "q45")])
+def test_persistent_step_edge_shapes(layers, vocab, head):
+    """An odd vocabulary (rows split unevenly over the workgroups, the last
+    ones short), no layers at all (the vocabulary product alone, h
+    untouched), and a Q45 vocabulary head after Q65 and Q45 down products:
+    each against the oracle chain and the launch chain."""
+    from memory_bound_quantized_amd.decode import DecodeModel
+    print("persistent edge layers=%d vocab=%d head=%s" % (layers, vocab, head), flush=True)
+    cfg = workloads.config3(layers=layers, vocab=vocab)
+    if head == "q45":
+        rng = np.random.default_rng(4545)
+        V = (workloads.Q45, vocab, 4096, workloads.weight_planes(rng, workloads.Q45, vocab, 4096))
+        cfg["vocab"] = V
+    model = DecodeModel(cfg["layers"], cfg["vocab"], cfg["g1"], cfg["g2"], cfg["gf"], cfg["eps"])
+    h = dev(cfg["h0"])
+    logits = torch.empty(vocab, device="cuda")
+    model.step_persistent(h, logits)
+    torch.cuda.synchronize()
+    assert model.status() == 0
+    h_ref, lg_ref = _oracle_chain(cfg)
+    e_h = rel_l2(h.cpu().numpy(), h_ref)
+    e_l = rel_l2(logits.cpu().numpy(), lg_ref)
+    print("  rel-L2 h %.2e logits %.2e" % (e_h, e_l), flush=True)
+    assert e_h <= 1e-4 and e_l <= 1e-4
+    if layers == 0:
+        assert np.array_equal(h.cpu().numpy(), cfg["h0"])
+    h2 = dev(cfg["h0"])
+    lg2 = torch.empty(vocab, device="cuda")
+    model.step(h2, lg2)
+    torch.cuda.synchronize()
+    assert rel_l2(lg2.cpu().numpy(), logits.cpu().numpy()) <= 1e-4
+
+
 def test_persistent_step_repeated_tokens_and_table_guard():
     """Several tokens in a row reuse the prepared table; a workspace prepared
     for another model is refused on the device (status bit 1, h untouched)."""
