@@ -341,18 +341,25 @@ static hipError_t launch_mfma_tr(DevPlanes P, int64_t N, int64_t K, const u4v* x
     }
 }
 
-// Row tiles per workgroup, from sweeps on MI355X (N = 4096 and 12288): one
-// workgroup per 192 tiles' worth of rows for one or two token tiles, per 128
-// for more, at most 4 (three would spill at 768 threads); MBQ_MFMA_TR
+// Row tiles per workgroup, from sweeps on MI355X (N = 4096 and 12288).
+// * One token tile: N / 4096 tiles, so 12288 rows take three and fill 256
+//   workgroups (16.0 us at 16 tokens, against 19.3 us with four tiles on 192
+//   workgroups).
+// * Two token tiles: one workgroup per 192 tiles' worth of rows.
+// * More: one per 128.
+// At most 4.  Three tiles keep their registers only with one or three token
+// tiles (two or four spill), so elsewhere three becomes four.  MBQ_MFMA_TR
 // overrides (tuning sweeps).
 template <int TT>
 static hipError_t launch_mfma_tt(DevPlanes P, int64_t N, int64_t K, const u4v* xt, const float* ts,
                                  int M, float* y, int64_t ldy, int accumulate, hipStream_t s) {
-    int64_t tr = TT <= 2 ? N / (16 * 192) : N / (16 * 128);
+    int64_t tr = TT == 1 ? N / (16 * 256) : TT == 2 ? N / (16 * 192) : N / (16 * 128);
     if (const char* e = tuning_var("MBQ_MFMA_TR")) tr = atoi(e);
-    switch (tr <= 1 ? 1 : tr == 2 ? 2 : 4) {
+    if (tr == 3 && (TT == 2 || TT == 4)) tr = 4;
+    switch (tr <= 1 ? 1 : tr == 2 ? 2 : tr == 3 ? 3 : 4) {
     case 1: return launch_mfma_tr<TT, 1>(P, N, K, xt, ts, M, y, ldy, accumulate, s);
     case 2: return launch_mfma_tr<TT, 2>(P, N, K, xt, ts, M, y, ldy, accumulate, s);
+    case 3: return launch_mfma_tr<TT, 3>(P, N, K, xt, ts, M, y, ldy, accumulate, s);
     default: return launch_mfma_tr<TT, 4>(P, N, K, xt, ts, M, y, ldy, accumulate, s);
     }
 }

@@ -118,14 +118,14 @@ def test_smallm_every_geometry_bitwise(fmt, M, N, K):
             assert np.array_equal(bits(y), bits(ref)), (R, G)
 
 
-@pytest.mark.parametrize("M,N,K", [(20, 1000, 4096), (40, 300, 2048), (64, 130, 1024)])
+@pytest.mark.parametrize("M,N,K", [(16, 1000, 4096), (20, 1000, 4096), (40, 300, 2048), (64, 130, 1024)])
 def test_mfma_every_geometry_matches_oracle(M, N, K):
     print("geometry mfma M=%d N=%d K=%d" % (M, N, K), flush=True)
     ow, dw = weights(1, N, K, 9990 + N)
     X = np.random.default_rng(M + N).normal(size=(M, K)).astype(np.float32)
     Xq = mbq().stage_x(1, dev(X))
     ref = oracle.gemv(ow, X)
-    for tr in (1, 2, 4):
+    for tr in (1, 2, 3, 4):
         for S in (2, 4):
             with env(MBQ_MFMA_TR=tr, MBQ_MFMA_S=S):
                 Y = mbq().gemv_xq(dw, Xq, M=M).cpu().numpy()
