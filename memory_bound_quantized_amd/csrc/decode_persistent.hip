@@ -304,7 +304,7 @@ __device__ __forceinline__ void wg_barrier() {
 }
 
 __device__ __forceinline__ float block_sum16(float v, float* red) {
-    v = wave_sum(v);
+    v = wave_sum_dpp(v);
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     if (lane == 0) red[wave] = v;
     wg_barrier();
@@ -323,6 +323,19 @@ __device__ __forceinline__ float block_sum16(float v, float* red) {
 // code serves every phase.  With a gamma, x is first replaced by
 // gamma * (x * r), r = 1/sqrt(mean(x^2) + eps) ([one-serial-kernel] "One
 // thread": the norm as a cooperative reduction).
+// Lane exchanges within aligned groups of four lanes by DPP quad
+// permutations (no LDS round trip): xor 1 = [1,0,3,2], xor 2 = [2,3,0,1].
+template <int CTRL>
+__device__ __forceinline__ int quad_swap(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ float quad_xor1(float v) {
+    return __builtin_bit_cast(float, quad_swap<0xB1>(__builtin_bit_cast(int, v)));
+}
+__device__ __forceinline__ float quad_xor2(float v) {
+    return __builtin_bit_cast(float, quad_swap<0x4E>(__builtin_bit_cast(int, v)));
+}
+
 __device__ __forceinline__ void stage_group_rt(const float* v, int og, bool ok, bool q65,
                                                uint32_t* xs) {
     constexpr int DW = Stride<kQ45>::DW;
@@ -330,8 +343,8 @@ __device__ __forceinline__ void stage_group_rt(const float* v, int og, bool ok, 
     float amax = 0.f;
 #pragma unroll
     for (int k = 0; k < 8; k++) amax = fmaxf(amax, fabsf(v[k]));
-    amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
-    amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
+    amax = fmaxf(amax, quad_xor1(amax));
+    amax = fmaxf(amax, quad_xor2(amax));
     const int e = chunk_exp(amax);
     const float up = pow2f(e);
     int32_t n[8];
@@ -349,8 +362,8 @@ __device__ __forceinline__ void stage_group_rt(const float* v, int og, bool ok, 
     int32_t B01[3], B23[3];
 #pragma unroll
     for (int p = 0; p < 3; p++) {
-        B01[p] = S[p] + __shfl_xor(S[p], 1, kWave);
-        B23[p] = __shfl_xor(B01[p], 2, kWave);
+        B01[p] = S[p] + quad_swap<0xB1>(S[p]);
+        B23[p] = quad_swap<0x4E>(B01[p]);
     }
     if (ok) {
         uint32_t* o = xs + DW * b + 6 * gi;
