@@ -345,11 +345,12 @@ def rows_bench(mbq, workloads, torch, dev, read_peak):
         kern_us = per_launch_us(lambda W: mbq.gemv_xq(W, Xq, M=M, out=Y), Ws)
         Xin = X if M > 1 else X[0]
         step_us = per_launch_us(lambda W: (mbq.stage_x(fmt, Xin, out=Xq), mbq.gemv_xq(W, Xq, M=M, out=Y)), Ws)
-        fp32_us = per_launch_us(lambda W: mbq.gemv_q(W, Xin, out=Y), Ws) if M <= 8 else None
+        fp32_us = per_launch_us(lambda W: mbq.gemv_q(W, Xin, out=Y), Ws)
         b = Ws[0].nbytes + 4 * M * (N + K)
         ent = {"stage_plus_product_us": round(step_us, 3), "product_us": round(kern_us, 3),
                "us_per_token": round(step_us / M, 3), "product_gbs": gbs(b, kern_us),
-               "path": "matrix cores" if M >= 6 else "vector units"}
+               "path": "matrix cores" if M >= 6 else "vector units",
+               "fp32_x_path": "matrix cores, x converted in the product" if M >= 6 else "vector units"}
         if fp32_us is not None:
             ent["fp32_x_us"] = round(fp32_us, 3)
         if M >= 6:

@@ -133,9 +133,13 @@ int mbq_unpack(int fmt, int64_t N, int64_t K, const void* const planes[4],
  * Arithmetic: weights exact in fp32, fp32 accumulation; the order of the sum
  * is unspecified.  Tokens run on the vector units, up to 8 per launch (as many
  * as fit staged in LDS: all 8 for K = 4096, 2 for K = 12288), each weight
- * read once per launch and unpacked once for all its tokens.  Matrix cores
- * take Q45 batches through mbq_stage_x + mbq_gemv_xq (from 16 tokens, and
- * from 6 when K % 1024 == 0).
+ * read once per launch and unpacked once for all its tokens.  Q45 batches of
+ * 6 or more tokens with K % 1024 == 0 (and 8-byte aligned scales) run on the
+ * matrix cores instead, 16 tokens per launch, with x split into fp16 high
+ * and low parts under a power of two per 32-weight block and token (the
+ * relative precision of the vector units' staged x).  Through mbq_stage_x +
+ * mbq_gemv_xq the matrix cores take Q45 batches from 16 tokens, and from 6
+ * when K % 1024 == 0, up to 64 per launch.
  * MBQ_EUNSUPPORTED for shapes without a kernel (K > 32768, or K > 16384 for
  * BF16; Q25 with K % 64 != 0; BF16 with K % 8 != 0).  M == 0 or N == 0
  * enqueue nothing; K == 0 writes zeros (or leaves y for accumulate = 1). */

@@ -322,6 +322,11 @@ int mbq_gemv_q(const mbq_qweight* W, const float* x, int64_t M, int64_t ldx, flo
         return hip_status(mbq::launch_gemv_m1(W->fmt, P, W->N, W->K, x, false, y, accumulate,
                                               nullptr, 1, g, s), fn);
     }
+    // Q45 batches of 6+ tokens with K % 1024 == 0: the matrix cores, fp32 x
+    // converted inside the product (passes of 16 tokens)
+    if (W->fmt == MBQ_FMT_Q45 && M >= 6 && W->K % 1024 == 0 && aligned(W->scales, 8))
+        return hip_status(mbq::launch_gemv_mfma_q45_f32x(P, W->N, W->K, x, ldx, M, y, ldy,
+                                                         accumulate, s), fn);
     // 2 <= M: passes of up to 8 tokens on the vector units, as many as the
     // LDS holds staged (a single token always fits: K <= kMaxK)
     int64_t mp = M < 8 ? M : 8;

@@ -18,6 +18,13 @@
 // order in which a lane unpacks the 8 codes of one dword); then one float per
 // token slot, 2^-e (0 for slots past M).
 //
+// fp32 x form (F32X, for mbq_gemv_q, one token tile per launch): the
+// workgroup converts fp32 x into the same slab layout while it fills LDS,
+// with one power of two per 32-weight block and token (the block's largest
+// |x| lands in [2^14, 2^15)) instead of one per token.  The block's factor
+// 2^-e joins its weight scale, so there is no staging launch and no staging
+// buffer.
+//
 // Kernel geometry: TR row tiles x S K parts of waves per workgroup (below).
 #include "device_common.h"
 #include "formats.h"
@@ -145,15 +152,59 @@ __device__ __forceinline__ h8 codes_to_a(uint32_t a) {
 // Requires K % 1024 == 0 and (nb / S) a multiple of kPG * kGB and of SB.
 constexpr int kPG = 4;                   // weight loads in flight per wave
 
-template <int TT, int TR, int S, int SB>
+// One (block, token) item of an fp32-x slab: 32 values of token m from k0,
+// as hi/lo fp16 halves of x * 2^e in the lane order of the tile form.
+struct XItem {
+    float4 v[8];
+};
+__device__ __forceinline__ void xitem_load(XItem& it, const float* __restrict__ x, int64_t ldx,
+                                           int m, int M, int k0) {
+    const float4* src = (const float4*)(x + (int64_t)(m < M ? m : 0) * ldx + k0);
+#pragma unroll
+    for (int q = 0; q < 8; q++) it.v[q] = m < M ? src[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+// Store item (t, lb, j) of part p into slab buffer sb: the hi and lo u4v of
+// lanes j + 16 g (g = 0..3), and 2^-e into ie.
+__device__ __forceinline__ void xitem_store(const XItem& it, u4v* sb, float* ie) {
+    float amax = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; q++)
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(it.v[q].x), fabsf(it.v[q].y)),
+                                 fmaxf(fabsf(it.v[q].z), fabsf(it.v[q].w))));
+    int e = 141 - (int)((__builtin_bit_cast(uint32_t, amax) >> 23) & 0xFFu);
+    e = e > 126 ? 126 : (e < -126 ? -126 : e);
+    const float up = __builtin_bit_cast(float, (uint32_t)(e + 127) << 23);
+    *ie = __builtin_bit_cast(float, (uint32_t)(127 - e) << 23);
+#pragma unroll
+    for (int g = 0; g < 4; g++) {
+        // values k = 8 g + {0, 4, 1, 5, 2, 6, 3, 7}
+        const float4 a = it.v[2 * g], b = it.v[2 * g + 1];
+        const float w[8] = {a.x, b.x, a.y, b.y, a.z, b.z, a.w, b.w};
+        h8 hi, lo;
+#pragma unroll
+        for (int q = 0; q < 8; q++) {
+            const float xs = w[q] * up;
+            hi[q] = (_Float16)xs;
+            lo[q] = (_Float16)(xs - (float)hi[q]);
+        }
+        sb[16 * g] = __builtin_bit_cast(u4v, hi);
+        sb[64 + 16 * g] = __builtin_bit_cast(u4v, lo);
+    }
+}
+
+template <int TT, int TR, int S, int SB, bool F32X>
 __global__ __launch_bounds__(kWave * TR * S) void gemv_mfma_q45_kernel(
         DevPlanes P, int64_t N, int K, const u4v* __restrict__ xt, const float* __restrict__ tscale,
+        const float* __restrict__ xf, int64_t ldx,
         int M, float* __restrict__ y, int64_t ldy, int accumulate) {
     constexpr int NW = TR * S;
     constexpr int NT = kWave * NW;
     constexpr int XSB = TT * SB * 128;                // uint4 per slab of one K part
     constexpr int XALL = S * XSB;                     // uint4 per slab step, all parts
-    constexpr int XPT = (XALL + NT - 1) / NT;         // per thread (last round guarded)
+    constexpr int XPT = F32X ? 1 : (XALL + NT - 1) / NT;   // per thread (last round guarded)
+    // fp32 x: items (part, tile, block, token) per slab step, per thread
+    constexpr int XIT = S * TT * SB * 16;
+    constexpr int IPT = F32X ? (XIT + NT - 1) / NT : 1;
     constexpr int GPS = SB / kGB;                     // weight groups per slab
     constexpr int kUS = kPG / GPS > 0 ? kPG / GPS : 1;   // slabs per unrolled body
     constexpr int RING = kUS * GPS;                  // ring slots (>= kPG)
@@ -165,6 +216,8 @@ __global__ __launch_bounds__(kWave * TR * S) void gemv_mfma_q45_kernel(
     const int tr = wave % TR, part = wave / TR;
     const int i = lane & 15, g = lane >> 4;
     uint32_t* scr = (uint32_t*)(lds + 2 * XALL) + wave * 16 * kScrStride;
+    // fp32 x: 2^-e of each (part, tile, block, token) of the two slab buffers
+    float* iex = (float*)(lds + 2 * XALL) + NW * 16 * kScrStride;
     const int nb = K / 32, nbp = nb / S;              // blocks per K part
     const int ngroups = nbp / kGB, nslab = nbp / SB;
     const int b0 = part * nbp;                        // first block of this wave's part
@@ -188,11 +241,56 @@ __global__ __launch_bounds__(kWave * TR * S) void gemv_mfma_q45_kernel(
     };
 
     u4v xr[XPT];
+    XItem xi[IPT];
+    // item it of slab step st: part, tile, block in slab, token
+    auto item_k0 = [&](int st, int it, int& m) {
+        const int p = it / (TT * SB * 16), r = it - p * (TT * SB * 16);
+        const int t = r / (SB * 16), r2 = r - t * (SB * 16);
+        const int lb = r2 / 16, j = r2 - lb * 16;
+        m = 16 * t + j;
+        return 32 * (p * nbp + st * SB + lb);
+    };
+    auto load_x = [&](int st) {
+        if constexpr (F32X) {
 #pragma unroll
-    for (int q = 0; q < XPT; q++) {
-        const int e = q * NT + tid;
-        if (XALL % NT == 0 || e < XALL) xr[q] = *xt_el(0, e);
-    }
+            for (int q = 0; q < IPT; q++) {
+                const int it = q * NT + tid;
+                if (XIT % NT == 0 || it < XIT) {
+                    int m;
+                    const int k0 = item_k0(st, it, m);
+                    xitem_load(xi[q], xf, ldx, m, M, k0);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < XPT; q++) {
+                const int e = q * NT + tid;
+                if (XALL % NT == 0 || e < XALL) xr[q] = *xt_el(st, e);
+            }
+        }
+    };
+    auto store_x = [&](int bsel) {
+        if constexpr (F32X) {
+#pragma unroll
+            for (int q = 0; q < IPT; q++) {
+                const int it = q * NT + tid;
+                if (XIT % NT == 0 || it < XIT) {
+                    const int p = it / (TT * SB * 16), r = it - p * (TT * SB * 16);
+                    const int t = r / (SB * 16), r2 = r - t * (SB * 16);
+                    const int lb = r2 / 16, j = r2 - lb * 16;
+                    u4v* sb = lds + bsel * XALL + p * XSB + (t * SB + lb) * 128 + j;
+                    xitem_store(xi[q], sb, iex + bsel * XIT + it);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < XPT; q++) {
+                const int e = q * NT + tid;
+                if (XALL % NT == 0 || e < XALL) lds[bsel * XALL + e] = xr[q];
+            }
+        }
+    };
+    load_x(0);
     u4v wr[RING];
     u2v sr[RING][4];
 #pragma unroll
@@ -202,11 +300,7 @@ __global__ __launch_bounds__(kWave * TR * S) void gemv_mfma_q45_kernel(
 #pragma unroll
         for (int v = 0; v < 4; v++) sr[t][v] = sq[v][tc];
     }
-#pragma unroll
-    for (int q = 0; q < XPT; q++) {
-        const int e = q * NT + tid;
-        if (XALL % NT == 0 || e < XALL) lds[e] = xr[q];
-    }
+    store_x(0);
     __syncthreads();
 
     f4v acc[TT];
@@ -221,11 +315,7 @@ __global__ __launch_bounds__(kWave * TR * S) void gemv_mfma_q45_kernel(
             constexpr int buf = su & 1;
             // next slab step (the last one reloads itself; it is not stored)
             const int sn = st + 1 < nslab ? st + 1 : st;
-#pragma unroll
-            for (int q = 0; q < XPT; q++) {
-                const int e = q * NT + tid;
-                if (XALL % NT == 0 || e < XALL) xr[q] = *xt_el(sn, e);
-            }
+            load_x(sn);
             static_for<0, GPS>([&](auto tg_c) {
                 constexpr int tg = decltype(tg_c)::value;
                 constexpr int tl = (su * GPS + tg) % RING;          // ring slot
@@ -256,16 +346,19 @@ __global__ __launch_bounds__(kWave * TR * S) void gemv_mfma_q45_kernel(
                         const h8 bl = __builtin_bit_cast(h8, bp[64 + lane]);
                         f4v d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bh, zero, 0, 0, 0);
                         d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bl, d, 0, 0, 0);
+                        if constexpr (F32X) {
+                            // the block's 2^-e for this lane's token column
+                            const float ie = iex[buf * XIT + ((part * TT + tt) * SB + lb) * 16 + (lane & 15)];
 #pragma unroll
-                        for (int v = 0; v < 4; v++) acc[tt][v] = fmaf(sv[v], d[v], acc[tt][v]);
+                            for (int v = 0; v < 4; v++) acc[tt][v] = fmaf(sv[v] * ie, d[v], acc[tt][v]);
+                        } else {
+#pragma unroll
+                            for (int v = 0; v < 4; v++) acc[tt][v] = fmaf(sv[v], d[v], acc[tt][v]);
+                        }
                     }
                 }
             });
-#pragma unroll
-            for (int q = 0; q < XPT; q++) {
-                const int e = q * NT + tid;
-                if (XALL % NT == 0 || e < XALL) lds[(buf ^ 1) * XALL + e] = xr[q];
-            }
+            store_x(buf ^ 1);
             __syncthreads();
         });
     }
@@ -296,7 +389,7 @@ __global__ __launch_bounds__(kWave * TR * S) void gemv_mfma_q45_kernel(
     for (int tt = 0; tt < TT; tt++) {
         const int m = 16 * tt + j;
         if (m >= M) continue;
-        const float ts = tscale[m];
+        const float ts = F32X ? 1.0f : tscale[m];
 #pragma unroll
         for (int v = 0; v < 4; v++) {
             const int64_t n = row0 + 4 * g + v;
@@ -309,15 +402,17 @@ __global__ __launch_bounds__(kWave * TR * S) void gemv_mfma_q45_kernel(
     }
 }
 
-template <int TT, int TR, int S, int SB>
+template <int TT, int TR, int S, int SB, bool F32X>
 static hipError_t launch_mfma_k(DevPlanes P, int64_t N, int64_t K, const u4v* xt, const float* ts,
-                                int M, float* y, int64_t ldy, int accumulate, hipStream_t stream) {
-    const size_t lds = (size_t)2 * S * TT * SB * 128 * 16 + (size_t)TR * S * 16 * kScrStride * 4;
-    auto kern = gemv_mfma_q45_kernel<TT, TR, S, SB>;
-    if (hipError_t e = ensure_lds<gemv_mfma_q45_kernel<TT, TR, S, SB>>(lds)) return e;
+                                const float* xf, int64_t ldx, int M, float* y, int64_t ldy,
+                                int accumulate, hipStream_t stream) {
+    const size_t lds = (size_t)2 * S * TT * SB * 128 * 16 + (size_t)TR * S * 16 * kScrStride * 4 +
+                       (F32X ? (size_t)2 * S * TT * SB * 16 * 4 : 0);
+    auto kern = gemv_mfma_q45_kernel<TT, TR, S, SB, F32X>;
+    if (hipError_t e = ensure_lds<gemv_mfma_q45_kernel<TT, TR, S, SB, F32X>>(lds)) return e;
     const int64_t grid = (N + 16 * TR - 1) / (16 * TR);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kWave * TR * S), lds, stream, P, N, (int)K,
-                       xt, ts, M, y, ldy, accumulate);
+                       xt, ts, xf, ldx, M, y, ldy, accumulate);
     return hipGetLastError();
 }
 
@@ -325,19 +420,20 @@ static hipError_t launch_mfma_k(DevPlanes P, int64_t N, int64_t K, const u4v* xt
 // token tiles take S = 4 parts when a workgroup has at most two row tiles,
 // else 2; three or four token tiles take 2; K = 1024 (32 blocks) takes 2.
 // MBQ_MFMA_S = 2 forces two parts (tuning sweeps).
-template <int TT, int TR>
+template <int TT, int TR, bool F32X>
 static hipError_t launch_mfma_tr(DevPlanes P, int64_t N, int64_t K, const u4v* xt, const float* ts,
-                                 int M, float* y, int64_t ldy, int accumulate, hipStream_t s) {
+                                 const float* xf, int64_t ldx, int M, float* y, int64_t ldy,
+                                 int accumulate, hipStream_t s) {
     bool four = TT <= 2 && TR <= 2 && (K / 32) % 64 == 0;
     if (const char* e = tuning_var("MBQ_MFMA_S")) four = TT <= 2 && (K / 32) % 64 == 0 && atoi(e) == 4;
     if constexpr (TT == 1) {
-        if (four) return launch_mfma_k<1, TR, 4, 8>(P, N, K, xt, ts, M, y, ldy, accumulate, s);
-        return launch_mfma_k<1, TR, 2, 8>(P, N, K, xt, ts, M, y, ldy, accumulate, s);
+        if (four) return launch_mfma_k<1, TR, 4, 8, F32X>(P, N, K, xt, ts, xf, ldx, M, y, ldy, accumulate, s);
+        return launch_mfma_k<1, TR, 2, 8, F32X>(P, N, K, xt, ts, xf, ldx, M, y, ldy, accumulate, s);
     } else if constexpr (TT == 2) {
-        if (four) return launch_mfma_k<2, TR, 4, 4>(P, N, K, xt, ts, M, y, ldy, accumulate, s);
-        return launch_mfma_k<2, TR, 2, 4>(P, N, K, xt, ts, M, y, ldy, accumulate, s);
+        if (four) return launch_mfma_k<2, TR, 4, 4, F32X>(P, N, K, xt, ts, xf, ldx, M, y, ldy, accumulate, s);
+        return launch_mfma_k<2, TR, 2, 4, F32X>(P, N, K, xt, ts, xf, ldx, M, y, ldy, accumulate, s);
     } else {
-        return launch_mfma_k<TT, TR, 2, 4>(P, N, K, xt, ts, M, y, ldy, accumulate, s);
+        return launch_mfma_k<TT, TR, 2, 4, F32X>(P, N, K, xt, ts, xf, ldx, M, y, ldy, accumulate, s);
     }
 }
 
@@ -350,17 +446,30 @@ static hipError_t launch_mfma_tr(DevPlanes P, int64_t N, int64_t K, const u4v* x
 // At most 4.  Three tiles keep their registers only with one or three token
 // tiles (two or four spill), so elsewhere three becomes four.  MBQ_MFMA_TR
 // overrides (tuning sweeps).
-template <int TT>
+template <int TT, bool F32X>
 static hipError_t launch_mfma_tt(DevPlanes P, int64_t N, int64_t K, const u4v* xt, const float* ts,
-                                 int M, float* y, int64_t ldy, int accumulate, hipStream_t s) {
+                                 const float* xf, int64_t ldx, int M, float* y, int64_t ldy,
+                                 int accumulate, hipStream_t s) {
     int64_t tr = TT == 1 ? N / (16 * 256) : TT == 2 ? N / (16 * 192) : N / (16 * 128);
     if (const char* e = tuning_var("MBQ_MFMA_TR")) tr = atoi(e);
     if (tr == 3 && (TT == 2 || TT == 4)) tr = 4;
     switch (tr <= 1 ? 1 : tr == 2 ? 2 : tr == 3 ? 3 : 4) {
-    case 1: return launch_mfma_tr<TT, 1>(P, N, K, xt, ts, M, y, ldy, accumulate, s);
-    case 2: return launch_mfma_tr<TT, 2>(P, N, K, xt, ts, M, y, ldy, accumulate, s);
-    case 3: return launch_mfma_tr<TT, 3>(P, N, K, xt, ts, M, y, ldy, accumulate, s);
-    default: return launch_mfma_tr<TT, 4>(P, N, K, xt, ts, M, y, ldy, accumulate, s);
+    case 1: return launch_mfma_tr<TT, 1, F32X>(P, N, K, xt, ts, xf, ldx, M, y, ldy, accumulate, s);
+    case 2: return launch_mfma_tr<TT, 2, F32X>(P, N, K, xt, ts, xf, ldx, M, y, ldy, accumulate, s);
+    case 3: return launch_mfma_tr<TT, 3, F32X>(P, N, K, xt, ts, xf, ldx, M, y, ldy, accumulate, s);
+    default: return launch_mfma_tr<TT, 4, F32X>(P, N, K, xt, ts, xf, ldx, M, y, ldy, accumulate, s);
+    }
+}
+
+template <bool F32X>
+static hipError_t launch_tt(int tt, DevPlanes P, int64_t N, int64_t K, const u4v* xt,
+                            const float* ts, const float* xf, int64_t ldx, int M, float* y,
+                            int64_t ldy, int accumulate, hipStream_t s) {
+    switch (tt) {
+    case 1: return launch_mfma_tt<1, F32X>(P, N, K, xt, ts, xf, ldx, M, y, ldy, accumulate, s);
+    case 2: return launch_mfma_tt<2, F32X>(P, N, K, xt, ts, xf, ldx, M, y, ldy, accumulate, s);
+    case 3: return launch_mfma_tt<3, F32X>(P, N, K, xt, ts, xf, ldx, M, y, ldy, accumulate, s);
+    default: return launch_mfma_tt<4, F32X>(P, N, K, xt, ts, xf, ldx, M, y, ldy, accumulate, s);
     }
 }
 
@@ -373,13 +482,22 @@ hipError_t launch_gemv_mfma_q45(DevPlanes P, int64_t N, int64_t K, const void* x
     for (int64_t m0 = 0; m0 < M; m0 += 64) {
         const int mg = (int)(M - m0 < 64 ? M - m0 : 64);
         const u4v* xg = (const u4v*)(base + (m0 / 16) * (K / 32) * 2048);
-        hipError_t e;
-        switch ((mg + 15) / 16) {
-        case 1: e = launch_mfma_tt<1>(P, N, K, xg, ts + m0, mg, y + m0 * ldy, ldy, accumulate, stream); break;
-        case 2: e = launch_mfma_tt<2>(P, N, K, xg, ts + m0, mg, y + m0 * ldy, ldy, accumulate, stream); break;
-        case 3: e = launch_mfma_tt<3>(P, N, K, xg, ts + m0, mg, y + m0 * ldy, ldy, accumulate, stream); break;
-        default: e = launch_mfma_tt<4>(P, N, K, xg, ts + m0, mg, y + m0 * ldy, ldy, accumulate, stream); break;
-        }
+        const hipError_t e = launch_tt<false>((mg + 15) / 16, P, N, K, xg, ts + m0, nullptr, 0, mg,
+                                              y + m0 * ldy, ldy, accumulate, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+// fp32 x: passes of 16 tokens (one token tile).  With more tiles the
+// converted slab items and the weight ring outgrow the registers.
+hipError_t launch_gemv_mfma_q45_f32x(DevPlanes P, int64_t N, int64_t K, const float* x,
+                                     int64_t ldx, int64_t M, float* y, int64_t ldy,
+                                     int accumulate, hipStream_t stream) {
+    for (int64_t m0 = 0; m0 < M; m0 += 16) {
+        const int mg = (int)(M - m0 < 16 ? M - m0 : 16);
+        const hipError_t e = launch_mfma_tt<1, true>(P, N, K, nullptr, nullptr, x + m0 * ldx, ldx,
+                                                     mg, y + m0 * ldy, ldy, accumulate, stream);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

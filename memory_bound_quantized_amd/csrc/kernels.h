@@ -110,6 +110,13 @@ hipError_t launch_stage_x_mfma(const float* x, int64_t M, int64_t ldx, int64_t K
                                hipStream_t stream);
 hipError_t launch_gemv_mfma_q45(DevPlanes P, int64_t N, int64_t K, const void* xt, int64_t M,
                                 float* y, int64_t ldy, int accumulate, hipStream_t stream);
+// The same product on fp32 x [M][ldx] (ldx % 4 == 0, 16-byte aligned rows),
+// converted while the slabs are filled, with a power of two per 32-weight
+// block and token: no staging launch or buffer.  K % 1024 == 0; passes of
+// 16 tokens.
+hipError_t launch_gemv_mfma_q45_f32x(DevPlanes P, int64_t N, int64_t K, const float* x,
+                                     int64_t ldx, int64_t M, float* y, int64_t ldy,
+                                     int accumulate, hipStream_t stream);
 
 // ---- one decode token in one launch (decode_persistent.hip) --------------
 // Device-side description of a decoder layer; the table lives in the

@@ -104,7 +104,7 @@ def test_fused_every_geometry_bitwise(fmt, N, K, silu):
             assert np.array_equal(bits(y), bits(ref)), (R, G)
 
 
-@pytest.mark.parametrize("fmt,M,N,K", [(1, 3, 1000, 4096), (1, 8, 1000, 4096), (2, 2, 300, 12288),
+@pytest.mark.parametrize("fmt,M,N,K", [(1, 3, 1000, 4096), (1, 8, 1000, 4160), (2, 2, 300, 12288),
                                        (3, 5, 300, 4096), (0, 4, 200, 4096), (1, 6, 100, 4160)])
 def test_smallm_every_geometry_bitwise(fmt, M, N, K):
     print("geometry smallm fmt=%d M=%d N=%d K=%d" % (fmt, M, N, K), flush=True)

@@ -1,12 +1,13 @@
-"""GPU parity of the small-batch products (2 <= M <= 8 tokens on the vector
-units) through the C ABI.
+"""GPU parity of the small-batch products through the C ABI: 2 <= M <= 8
+tokens on the vector units, and Q45 batches of 6+ tokens with K % 1024 == 0
+on the matrix cores (fp32 X through mbq_gemv_q, or tile-staged X).
 
-Bars: every token's row of Y is bit-identical to the M = 1 product of that
-token (same staging, same sums in the same order), so it inherits the M = 1
-parity with the oracle; each case is also checked against the oracle directly
-(fp32 forward-error bound, rel-L2 <= 1e-4).  Staged X (mbq_stage_x) gives the
-same bits as fp32 X, except Q45 batches of 6+ tokens with K % 1024 == 0,
-whose staged form goes to the matrix cores (held to the oracle's bar).
+Bars: on the vector units every token's row of Y is bit-identical to the
+M = 1 product of that token (same staging, same sums in the same order), so
+it inherits the M = 1 parity with the oracle; every case is also checked
+against the oracle directly (fp32 forward-error bound, rel-L2 <= 1e-4), which
+is the bar of the matrix-core cases.  Staged X (mbq_stage_x) gives the same
+bits as fp32 X on the vector units.
 """
 import numpy as np
 import pytest
@@ -50,9 +51,11 @@ def test_smallm_rows_equal_single_token_products(fmt, M, N, K):
     X = np.random.default_rng(M * K).normal(size=(M, ldx)).astype(np.float32)
     Xd = dev(X)[:, :K]                     # row stride ldx
     Y = mbq().gemv_q(dw, Xd).cpu().numpy()
-    for m in range(M):
-        y1 = mbq().gemv_q(dw, dev(X[m, :K])).cpu().numpy()
-        assert np.array_equal(Y[m].view(np.uint32), y1.view(np.uint32)), m
+    cores = fmt == 1 and M >= 6 and K % 1024 == 0          # matrix cores
+    if not cores:
+        for m in range(M):
+            y1 = mbq().gemv_q(dw, dev(X[m, :K])).cpu().numpy()
+            assert np.array_equal(Y[m].view(np.uint32), y1.view(np.uint32)), m
     ref = oracle.gemv(ow, X[:, :K])
     check_gemv(Y, ow, X[:, :K], ref)
     if fmt != 0:
@@ -82,8 +85,10 @@ def test_smallm_accumulate_and_row_stride_of_y():
 
 
 def test_workload4_full_size_small_batches():
-    """The 12288 x 4096 Q45 table against X[M, 4096] for M = 2, 4, 8."""
-    for M in (2, 4, 8):
+    """The 12288 x 4096 Q45 table against fp32 X[M, 4096] through mbq_gemv_q
+    for M = 2, 4 (vector units) and 8, 16, 64 (matrix cores)."""
+    for M in (2, 4, 8, 16, 64):
+        print("workload4 fp32 M=%d" % M, flush=True)
         cfg = workloads.config4(M)
         fmt, N, K, planes = cfg["W"]
         ow, dw = oracle.Planes(fmt, N, K, planes), mbq().QWeight.from_host(fmt, N, K, planes)
@@ -93,7 +98,8 @@ def test_workload4_full_size_small_batches():
 
 
 # --------------------------------------------------------------------------
-# M >= 16: Q45 on the matrix cores (tile-staged X), and fp32 X in passes of 8
+# Q45 on the matrix cores: tile-staged X (one power of two per token), and
+# fp32 X converted inside the product (one per 32-weight block and token)
 # --------------------------------------------------------------------------
 
 MFMA_CASES = [(16, 64, 4096), (17, 1000, 4096), (31, 130, 1024), (48, 64, 2048),
@@ -112,7 +118,8 @@ def test_mfma_matches_oracle(M, N, K):
     Y = mbq().gemv_xq(dw, Xt, M=M).cpu().numpy()
     ref = oracle.gemv_parallel(ow, X) if N * K > 1 << 24 else oracle.gemv(ow, X)
     check_gemv(Y, ow, X, ref)
-    # fp32 X runs passes of 8 tokens on the vector units: same bar
+    # fp32 X: the matrix cores in passes of 16 tokens, x converted in the
+    # product; same bar
     Yv = mbq().gemv_q(dw, Xd).cpu().numpy()
     check_gemv(Yv, ow, X, ref)
 
@@ -130,6 +137,19 @@ def test_mfma_token_scales_and_accumulate():
     X[5] = 0.0
     X[6, ::7] *= np.float32(2.0 ** 30)
     Y0 = rng.normal(size=(M, N)).astype(np.float32)
+    ref = oracle.gemv(ow, X, y0=Y0)
     Yd = dev(Y0)
     mbq().gemv_xq(dw, mbq().stage_x(1, dev(X)), M=M, out=Yd, accumulate=True)
-    check_gemv(Yd.cpu().numpy(), ow, X, oracle.gemv(ow, X, y0=Y0), y0=Y0)
+    check_gemv(Yd.cpu().numpy(), ow, X, ref, y0=Y0)
+    # fp32 X on the matrix cores (a power of two per block and token), with
+    # row strides on X and Y
+    ldx, ldy = K + 32, N + 8
+    Xs = np.zeros((M, ldx), np.float32)
+    Xs[:, :K] = X
+    Ys = np.full((M, ldy), 7.0, np.float32)
+    Ys[:, :N] = Y0
+    Ysd = dev(Ys)
+    mbq().gemv_q(dw, dev(Xs)[:, :K], out=Ysd[:, :N], accumulate=True)
+    Yf = Ysd.cpu().numpy()
+    assert np.all(Yf[:, N:] == 7.0)                          # padding untouched
+    check_gemv(Yf[:, :N], ow, X, ref, y0=Y0)
