@@ -357,8 +357,12 @@ __global__ __launch_bounds__(kWave * TR * S) void gemv_mfma_q45_kernel(
                         }
                     }
                 }
+                // fp32 x: convert the next slab into the other buffer (read
+                // only after the barrier below) between this step's matrix
+                // instructions
+                if constexpr (F32X && tg == (GPS - 1) / 2) store_x(buf ^ 1);
             });
-            store_x(buf ^ 1);
+            if constexpr (!F32X) store_x(buf ^ 1);
             __syncthreads();
         });
     }
