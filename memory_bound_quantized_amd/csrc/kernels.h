@@ -144,9 +144,6 @@ struct DecTable {
 };
 constexpr uint64_t kDecMagic = 0x31706564716d6266ull;
 
-// Requires d = dq = 4096, f = 12288, Q45 qkv/o/gate-up, Q45 or Q65 down and
-// lm head.  ctr and err are zeroed by a small kernel first; err != 0
-// afterwards means a barrier spin gave up (1) or the table did not match (2).
 // Activation buffers of the one-launch step, each written once per token:
 // h versions 1 .. 2L (after each residual add), q|k|v and m per layer.
 struct DecodeBuffers {
@@ -155,9 +152,16 @@ struct DecodeBuffers {
     float* m;
     int64_t hs, qs, ms;   // floats between consecutive versions / layers
 };
+// One token in one cooperative launch.  Requires d = dq = 4096 and f = 12288
+// when there are layers, Q45 qkv/o/gate-up, Q45 or Q65 down and lm head.
+// ctr (the barrier counters: global at 0, group g at 32 (g + 1)) and err are
+// zeroed by a small kernel first; err != 0 afterwards means a barrier spin
+// gave up (1) or the table did not match (2).  hipErrorInvalidConfiguration
+// if the device's compute units or the model's row counts do not fit.
 hipError_t launch_decode_persistent(const DecTable* table, DecTable expect, float eps, float* h,
-                                    float* logits, int64_t vocab, int64_t nqkv, const DecodeBuffers& bufs, uint32_t* ctr,
-                                    uint32_t* err, hipStream_t stream);
+                                    float* logits, int64_t vocab, int64_t nqkv,
+                                    const DecodeBuffers& bufs, uint32_t* ctr, uint32_t* err,
+                                    hipStream_t stream);
 
 // y[m][n] = 0 for the K == 0 case (rows of length ldy, first N entries).
 hipError_t launch_fill_zero(float* y, int64_t M, int64_t N, int64_t ldy, hipStream_t stream);
