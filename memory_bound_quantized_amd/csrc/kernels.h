@@ -154,10 +154,11 @@ struct DecodeBuffers {
 };
 // One token in one cooperative launch.  Requires d = dq = 4096 and f = 12288
 // when there are layers, Q45 qkv/o/gate-up, Q45 or Q65 down and lm head.
-// ctr (the barrier counters: global at 0, group g at 32 (g + 1)) and err are
-// zeroed by a small kernel first; err != 0 afterwards means a barrier spin
-// gave up (1) or the table did not match (2).  hipErrorInvalidConfiguration
-// if the device's compute units or the model's row counts do not fit.
+// ctr holds the barrier counters (uint32 index 0: global; 32 (g + 1):
+// group g).  ctr and err are zeroed by a small kernel first; err != 0
+// afterwards means a barrier spin gave up (1) or the table did not match
+// (2).  hipErrorInvalidConfiguration if the device's compute units or the
+// model's row counts do not fit.
 hipError_t launch_decode_persistent(const DecTable* table, DecTable expect, float eps, float* h,
                                     float* logits, int64_t vocab, int64_t nqkv,
                                     const DecodeBuffers& bufs, uint32_t* ctr, uint32_t* err,
