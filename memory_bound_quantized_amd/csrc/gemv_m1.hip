@@ -168,6 +168,23 @@ __global__ __launch_bounds__(kBlock * k_slices(CS)) void gemv_m1_kernel(DevPlane
         Slot<FMT, R> buf[DD];
 #pragma unroll
         for (int d = 0; d < DD; d++) load(buf[d], d);
+        // Row groups (see below): group g of this wave is rows
+        // ((blk * G + g) * 4 + wave) * R.  With the norm prologue, and for
+        // Q25 (one chunk per lane and group), the second group's loads are
+        // issued before x is staged as well, so that two groups of weights
+        // are in flight while x is normalised and staged.  A gather takes
+        // its rows through an index load first, and is slower so.
+        constexpr bool EARLY = GROUPED && (PRO == kProRms || (FMT == kQ25 && !GATHER));
+        const int64_t gstride = (int64_t)kWavesPerBlock * R;
+        const int64_t rbase = row0;
+        Slot<FMT, R> alt[DD];
+        auto load_group = [&](Slot<FMT, R>* b, int g) {
+            const int gc = g < G ? g : G - 1;
+            set_rows(rbase + (int64_t)gc * gstride);
+#pragma unroll
+            for (int d = 0; d < DD; d++) load(b[d], d);
+        };
+        if constexpr (EARLY) load_group(alt, 1);
         if constexpr (PRO == kProRms) {
             // RMSNorm of the row, as the stand-alone kernel: y = g * (x * inv)
             __shared__ float red[kWavesPerBlock * S];
@@ -192,24 +209,14 @@ __global__ __launch_bounds__(kBlock * k_slices(CS)) void gemv_m1_kernel(DevPlane
         XP::template store<NX, true>(xr, 0, npieces, xs);
         __syncthreads();
         if constexpr (GROUPED) {
-            // Row groups: group g of this wave is rows ((blk * G + g) * 4 + wave) * R,
-            // so the workgroup's rows are one contiguous block.  Each group's
+            // Row groups: the workgroup's rows are one contiguous block.  Each group's
             // chunks (of the wave's slice) are all in flight, two groups deep:
             // the loads of group g + 1 are issued before group g is computed
             // (the last group reloads itself; that copy is never used).  Slice
             // sums go to LDS and the block is written once at the end,
             // coalesced, so no store sits between the loads of the loop.
-            const int64_t gstride = (int64_t)kWavesPerBlock * R;
-            const int64_t rbase = row0;
             // G * 4 * R <= 1024 rows per workgroup (G <= 64, R <= 4)
             __shared__ float outs[S][kWavesPerBlock * 4 * 64];
-            Slot<FMT, R> alt[DD];
-            auto load_group = [&](Slot<FMT, R>* b, int g) {
-                const int gc = g < G ? g : G - 1;
-                set_rows(rbase + (int64_t)gc * gstride);
-#pragma unroll
-                for (int d = 0; d < DD; d++) load(b[d], d);
-            };
             auto finish = [&](int g) {
 #pragma unroll
                 for (int r = 0; r < R; r++) {
@@ -219,7 +226,7 @@ __global__ __launch_bounds__(kBlock * k_slices(CS)) void gemv_m1_kernel(DevPlane
                 }
             };
             for (int g = 0; g < G; g += 2) {
-                load_group(alt, g + 1);
+                if (!EARLY || g > 0) load_group(alt, g + 1);
 #pragma unroll
                 for (int c = 0; c < CSS; c++) compute(buf[c], c);
                 finish(g);
