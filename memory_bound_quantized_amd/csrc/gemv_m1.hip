@@ -70,7 +70,8 @@ __global__ __launch_bounds__(kBlock * k_slices(CS)) void gemv_m1_kernel(DevPlane
                                                          int rpe, const float* __restrict__ gamma,
                                                          float eps, int groups, int64_t nw) {
     using T = Traits<FMT>;
-    static_assert(PRO == kProNone || (CS > 0 && !XQ), "the norm prologue needs static K, fp32 x");
+    static_assert(PRO == kProNone || (grouped_form(CS) && !XQ),
+                  "the norm prologue needs the grouped form (static K), fp32 x");
     static_assert(EPI == kEpiStore || R == 2, "the silu epilogue pairs two rows per wave");
     constexpr bool GROUPED = grouped_form(CS);
     constexpr int S = k_slices(CS);                           // K slices per workgroup
@@ -185,9 +186,17 @@ __global__ __launch_bounds__(kBlock * k_slices(CS)) void gemv_m1_kernel(DevPlane
             for (int d = 0; d < DD; d++) load(b[d], d);
         };
         if constexpr (EARLY) load_group(alt, 1);
+        // RMSNorm of the row, y = g * (x * inv).  With a store or accumulate
+        // epilogue the prologue stages g * x and leaves each wave's share of
+        // sum(x^2) in LDS; inv = 1 / rms is formed from those shares, added
+        // in wave order, after the staging barrier and scales each row's
+        // total at the end (W (g x) inv), so no barrier of its own sits
+        // between the x loads and the staging.  The silu product, whose
+        // long row-group loop measured slower so, scales x by inv first.
+        constexpr bool DEFER = PRO == kProRms && EPI != kEpiSilu;
+        __shared__ float red[PRO == kProRms ? kWavesPerBlock * S : 1];
+        float inv = 1.0f;
         if constexpr (PRO == kProRms) {
-            // RMSNorm of the row, as the stand-alone kernel: y = g * (x * inv)
-            __shared__ float red[kWavesPerBlock * S];
             float ss = 0.f;
 #pragma unroll
             for (int i = 0; i < NX; i++) {
@@ -197,17 +206,29 @@ __global__ __launch_bounds__(kBlock * k_slices(CS)) void gemv_m1_kernel(DevPlane
                 ss = fmaf(v.z, v.z, ss);
                 ss = fmaf(v.w, v.w, ss);
             }
-            const float inv = 1.0f / sqrtf(block_sum<kWavesPerBlock * S>(ss, red) / (float)K + eps);
+            if constexpr (DEFER) {
+                ss = wave_sum_dpp(ss);
+                if (lane == 0) red[wid] = ss;
+            } else {
+                inv = 1.0f / sqrtf(block_sum<kWavesPerBlock * S>(ss, red) / (float)K + eps);
+            }
+            const float sx = DEFER ? 1.0f : inv;
 #pragma unroll
             for (int i = 0; i < NX; i++) {
                 const float4 v = __builtin_bit_cast(float4, xr[i]);
                 const float4 g = __builtin_bit_cast(float4, gr[i]);
-                xr[i] = __builtin_bit_cast(uint4, make_float4(g.x * (v.x * inv), g.y * (v.y * inv),
-                                                              g.z * (v.z * inv), g.w * (v.w * inv)));
+                xr[i] = __builtin_bit_cast(uint4, make_float4(g.x * (v.x * sx), g.y * (v.y * sx),
+                                                              g.z * (v.z * sx), g.w * (v.w * sx)));
             }
         }
         XP::template store<NX, true>(xr, 0, npieces, xs);
         __syncthreads();
+        if constexpr (DEFER) {
+            float t = red[0];
+#pragma unroll
+            for (int w = 1; w < kWavesPerBlock * S; w++) t += red[w];
+            inv = 1.0f / sqrtf(t / (float)K + eps);
+        }
         if constexpr (GROUPED) {
             // Row groups: the workgroup's rows are one contiguous block.  Each group's
             // chunks (of the wave's slice) are all in flight, two groups deep:
@@ -257,6 +278,7 @@ __global__ __launch_bounds__(kBlock * k_slices(CS)) void gemv_m1_kernel(DevPlane
                     float v = outs[0][t];
 #pragma unroll
                     for (int q = 1; q < S; q++) v += outs[q][t];
+                    if constexpr (DEFER) v *= inv;
                     const int64_t n = rwg + t;
                     if (n < N) y[n] = (accumulate ? y[n] : 0.f) + v;
                 }
