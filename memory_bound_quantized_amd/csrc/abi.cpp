@@ -389,7 +389,7 @@ int mbq_gemv_fused(const mbq_qweight* W, const float* x, const float* gamma, flo
     if ((rc = check_planes(W, fn))) return rc;
     if ((rc = check_kernel_shape(W, fn))) return rc;
     hipStream_t s = (hipStream_t)stream;
-    mbq::GemvGeom g = mbq::gemv_m1_default_geom(W->fmt, W->N, W->K, silu);
+    mbq::GemvGeom g = mbq::gemv_m1_default_geom(W->fmt, W->N, W->K, silu, gamma != nullptr);
     geom_override(&g);
     if (!gamma && !silu)
         return hip_status(mbq::launch_gemv_m1(W->fmt, planes_of(W), W->N, W->K, x, false, y,
@@ -498,8 +498,8 @@ int mbq_decode_step(const mbq_decode_model* m, float* h, float* logits, void* wo
     hipStream_t s = (hipStream_t)stream;
     float* qkv = (float*)((char*)workspace + lay.qkv);
     float* mm = (float*)((char*)workspace + lay.m);
-    auto geom = [](const mbq_qweight& W, bool pairs = false) {
-        mbq::GemvGeom g = mbq::gemv_m1_default_geom(W.fmt, W.N, W.K, pairs);
+    auto geom = [](const mbq_qweight& W, bool pairs = false, bool norm = false) {
+        mbq::GemvGeom g = mbq::gemv_m1_default_geom(W.fmt, W.N, W.K, pairs, norm);
         geom_override(&g);
         return g;
     };
@@ -508,7 +508,7 @@ int mbq_decode_step(const mbq_decode_model* m, float* h, float* logits, void* wo
         const mbq_decode_layer& L = m->layers[l];
         // a = rmsnorm(h, gamma1); q|k|v = Wqkv a
         e = mbq::launch_gemv_fused(L.qkv.fmt, planes_of(&L.qkv), L.qkv.N, L.qkv.K, h, L.gamma1,
-                                   m->eps, false, qkv, 0, geom(L.qkv), s);
+                                   m->eps, false, qkv, 0, geom(L.qkv, false, true), s);
         // h += Wo q   (the attention output stands in as q)
         if (e == hipSuccess)
             e = mbq::launch_gemv_m1(L.o.fmt, planes_of(&L.o), L.o.N, L.o.K, qkv, false, h, 1,
@@ -526,7 +526,7 @@ int mbq_decode_step(const mbq_decode_model* m, float* h, float* logits, void* wo
     // logits = Wvocab rmsnorm(h, gamma_f)
     if (e == hipSuccess && m->vocab > 0)
         e = mbq::launch_gemv_fused(m->lm_head.fmt, planes_of(&m->lm_head), m->vocab, m->d, h,
-                                   m->gamma_f, m->eps, false, logits, 0, geom(m->lm_head), s);
+                                   m->gamma_f, m->eps, false, logits, 0, geom(m->lm_head, false, true), s);
     return hip_status(e, fn);
 }
 

@@ -31,7 +31,9 @@ struct GemvGeom {
     int groups;          // row groups per wave (K = 4096-class tables; 1 otherwise)
 };
 
-GemvGeom gemv_m1_default_geom(int fmt, int64_t N, int64_t K, bool pairs = false);
+// pairs: the silu product's gate/up rows; norm: the RMSNorm prologue.
+GemvGeom gemv_m1_default_geom(int fmt, int64_t N, int64_t K, bool pairs = false,
+                              bool norm = false);
 
 // Geometry overrides for tuning sweeps (MBQ_GEMV_*, MBQ_SMALLM_*, MBQ_MFMA_*)
 // are read at each call only when MBQ_TUNING is set when the library first

@@ -41,12 +41,12 @@ def mat(fmt, N, K, seed):
     return (fmt, N, K, workloads.weight_planes(np.random.default_rng(seed), fmt, N, K))
 
 
-def check_after_norm(y, ow, a_ref, ref):
+def check_after_norm(y, ow, a_ref, ref, y0=None):
     """GEMV bar on the normalised input a_ref, widened by what the norm bar
     allows: the device's normalised value may differ from a_ref by 1e-5 per
     element, which moves output n by at most 1e-5 * sum_k |w[n][k]|."""
     absw = np.abs(oracle.dequant(ow).astype(np.float64))
-    check_gemv(y, ow, a_ref, ref, slack=1e-5 * absw.sum(axis=1))
+    check_gemv(y, ow, a_ref, ref, y0=y0, slack=1e-5 * absw.sum(axis=1))
 
 
 @pytest.mark.parametrize("fmt,N,K", [(1, 1000, 4096), (1, 6144, 4096), (2, 300, 4096),
@@ -61,6 +61,23 @@ def test_fused_rmsnorm_prologue(fmt, N, K):
     y = mbq().gemv_fused(dw, dev(x), dev(g), 1e-6).cpu().numpy()
     a = oracle.rmsnorm(x, g, 1e-6)[0]
     check_after_norm(y, ow, a, oracle.gemv(ow, a)[0])
+
+
+@pytest.mark.parametrize("fmt,N,K", [(1, 1000, 4096), (1, 6144, 4096), (2, 300, 12288)])
+def test_fused_rmsnorm_accumulate(fmt, N, K):
+    """y += W rmsnorm(x): the norm's 1/rms scales each row's total before the
+    add (ragged N, both K forms)."""
+    print("fused norm accumulate fmt=%d N=%d K=%d" % (fmt, N, K), flush=True)
+    W = mat(fmt, N, K, 8400 + N + fmt)
+    ow, dw = oracle.Planes(*W), mbq().QWeight.from_host(*W)
+    rng = np.random.default_rng(K + N + 7)
+    x = rng.normal(size=K).astype(np.float32)
+    g = rng.uniform(0.5, 1.5, K).astype(np.float32)
+    y0 = rng.normal(size=N).astype(np.float32)
+    yd = dev(y0)
+    mbq().gemv_fused(dw, dev(x), dev(g), 1e-6, mbq().EPI_ACCUMULATE, out=yd)
+    a = oracle.rmsnorm(x, g, 1e-6)[0]
+    check_after_norm(yd.cpu().numpy(), ow, a, oracle.gemv(ow, a, y0=y0)[0], y0=y0)
 
 
 @pytest.mark.parametrize("fmt,f,K,norm", [(1, 512, 4096, True), (1, 512, 4096, False),
