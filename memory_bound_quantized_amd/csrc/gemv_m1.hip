@@ -405,7 +405,8 @@ static hipError_t launch_f(const M1Args& a, bool xq, GemvGeom geom, hipStream_t 
 // 8 rows per wave.  Six-step K (12288) runs three K slices per workgroup
 // and N / 1024 single-row groups, at most 4.
 // Other K keep one group and 1, 2 or 4 rows per wave.  The silu product
-// (pairs) takes its rows two at a time, N / 4096 pairs per wave up to 6.
+// (pairs) takes its rows two at a time in N / 2048 groups, which is 256
+// workgroups (N / 4096 groups, 512 workgroups, past 8 groups; at most 8).
 // A Q45 product with the RMSNorm prologue at K = 4096 (below vocabulary
 // size) takes 2 rows per wave and N / 2048 groups up to 6: about 256
 // workgroups, so each CU normalises and stages x once (7-17 % faster for
@@ -427,7 +428,9 @@ GemvGeom gemv_m1_default_geom(int fmt, int64_t N, int64_t K, bool pairs, bool no
     }
     if (pairs) {
         g.rows_per_wave = 2;
-        g.groups = N / 4096 < 1 ? 1 : N / 4096 > 6 ? 6 : (int)(N / 4096);
+        int64_t gg = N / 2048;
+        if (gg > 8) gg = N / 4096;
+        g.groups = gg < 1 ? 1 : gg > 8 ? 8 : (int)gg;
         return g;
     }
     if (norm && fmt == kQ45 && steps == 2 && N < 65536) {
