@@ -411,7 +411,9 @@ static hipError_t launch_f(const M1Args& a, bool xq, GemvGeom geom, hipStream_t 
 // size) takes 2 rows per wave and N / 2048 groups up to 6: about 256
 // workgroups, so each CU normalises and stages x once (7-17 % faster for
 // N = 2048 ... 24576; Q65 at 2 rows per wave holds 202 VGPRs and gains
-// nothing).
+// nothing).  Q25 at K = 4096 (one chunk per lane, plain or gathered)
+// takes 2 rows per wave and N / 4096 groups up to 6, about 512 workgroups
+// (10-20 % faster at 12288 and 24576 rows).
 GemvGeom gemv_m1_default_geom(int fmt, int64_t N, int64_t K, bool pairs, bool norm) {
     GemvGeom g;
     g.groups = 1;
@@ -431,6 +433,11 @@ GemvGeom gemv_m1_default_geom(int fmt, int64_t N, int64_t K, bool pairs, bool no
         int64_t gg = N / 2048;
         if (gg > 8) gg = N / 4096;
         g.groups = gg < 1 ? 1 : gg > 8 ? 8 : (int)gg;
+        return g;
+    }
+    if (fmt == kQ25 && steps == 1 && N < 65536) {
+        g.rows_per_wave = 2;
+        g.groups = N / 4096 < 1 ? 1 : N / 4096 > 6 ? 6 : (int)(N / 4096);
         return g;
     }
     if (norm && fmt == kQ45 && steps == 2 && N < 65536) {
