@@ -20,7 +20,7 @@ import workloads
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-from checks import check_gemv  # noqa: E402
+from checks import GEMV_RTOL, check_gemv, rel_l2  # noqa: E402
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -98,9 +98,28 @@ def test_fused_every_geometry_bitwise(fmt, N, K, silu):
     epi = mbq().EPI_SILU_MUL if silu else mbq().EPI_STORE
     ref = mbq().gemv_fused(dw, x, g, 1e-6, epi)
     for R in (1, 2, 4):
-        for G in (1, 3, 4):
+        for G in (1, 3, 4, 6, 8):
             with env(MBQ_GEMV_ROWS=R, MBQ_GEMV_GROUPS=G):
                 y = mbq().gemv_fused(dw, x, g, 1e-6, epi)
+            assert np.array_equal(bits(y), bits(ref)), (R, G)
+
+
+def test_gather_every_geometry_bitwise():
+    """Q25 expert gather (one chunk per lane, rows of a group may come from
+    different experts): every geometry gives the default's bits."""
+    print("geometry gather q25", flush=True)
+    E, rpe, K = 8, 200, 4096
+    ow, dw = weights(3, E * rpe, K, 9990)
+    rng = np.random.default_rng(5)
+    idx = rng.choice(E, 5, replace=False).astype(np.int32)
+    x = rng.normal(size=K).astype(np.float32)
+    xd, idd = dev(x), dev(idx)
+    ref = mbq().gemv_q_gather(dw, rpe, idd, xd)
+    assert rel_l2(ref.cpu().numpy(), oracle.gather(ow, rpe, idx, x)) <= GEMV_RTOL
+    for R in (1, 2, 4):
+        for G in (1, 2, 3, 6):
+            with env(MBQ_GEMV_ROWS=R, MBQ_GEMV_GROUPS=G):
+                y = mbq().gemv_q_gather(dw, rpe, idd, xd)
             assert np.array_equal(bits(y), bits(ref)), (R, G)
 
 
