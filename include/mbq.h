@@ -165,7 +165,11 @@ int mbq_gemv_q_gather(const mbq_qweight* W_all, int64_t rows_per_expert,
  *
  * mbq_gemv_fused: M = 1.
  *   gamma == NULL:  a = x;  else a = rmsnorm(x; gamma, eps) (as mbq_rmsnorm),
- *                   computed inside every workgroup of the product.
+ *                   computed inside every workgroup of the product.  With
+ *                   the store and accumulate epilogues the 1/rms factor
+ *                   multiplies each row's sum, W[n] . (gamma x) / rms, which
+ *                   is W[n] . a up to rounding (one rounding per output in
+ *                   place of one per element of a).
  *   epilogue MBQ_EPI_STORE:      y[n]  = W[n] . a,           n < N
  *            MBQ_EPI_ACCUMULATE: y[n] += W[n] . a            (residual add)
  *            MBQ_EPI_SILU_MUL:   y[i]  = silu(W[2i] . a) * (W[2i+1] . a),
