@@ -168,6 +168,29 @@ def traffic_pass():
     print("traffic pass: %d launches of each GEMV, one %d-byte copy" % (ncopy, COPY_BYTES))
 
 
+def mfma_pass(reps: int = 8):
+    """Launches profiled by the matrix-core counter run: the staged-x product
+    of workload 4's 12288 x 4096 Q45 table at M = 16 and 64, each on cold
+    weights (one rotated copy per launch, no graph)."""
+    import torch
+    import memory_bound_quantized_amd as mbq
+    import workloads
+    dev = torch.device("cuda:0")
+    for M in (16, 64):
+        c4 = workloads.config4(M)
+        W0 = mbq.QWeight.from_host(*c4["W"])
+        Ws = rotated(W0)
+        X = torch.from_numpy(c4["X"]).to(dev)
+        Xq = mbq.stage_x(W0.fmt, X)
+        Y = torch.empty((M, W0.N), device=dev)
+        for i in range(reps):
+            mbq.gemv_xq(Ws[i % len(Ws)], Xq, M=M, out=Y)
+        torch.cuda.synchronize()
+        del Ws
+        torch.cuda.empty_cache()
+    print("mfma pass: %d launches at M = 16 and at M = 64" % reps)
+
+
 def write_traffic(fetch_dir: str, write_dir: str):
     """HBM bytes per launch from a FETCH_SIZE run and a WRITE_SIZE run of
     traffic_pass (rocprofv3 --pmc, KiB per dispatch), each scaled by what
@@ -403,6 +426,8 @@ def main():
     ap.add_argument("--no-rows", action="store_true", help="headline step only")
     ap.add_argument("--traffic-pass", action="store_true",
                     help="only the launches that the counter runs profile")
+    ap.add_argument("--mfma-pass", action="store_true",
+                    help="only the matrix-core launches that the counter runs profile")
     ap.add_argument("--decode-only", type=int, metavar="TOKENS", default=0,
                     help="only the 36-layer decode step, TOKENS graph replays (for profiling)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -418,6 +443,9 @@ def main():
 
     if args.traffic_pass:
         traffic_pass()
+        return
+    if args.mfma_pass:
+        mfma_pass()
         return
 
     import torch
