@@ -78,7 +78,10 @@ __global__ __launch_bounds__(kBlock * k_slices(CS)) void gemv_m1_kernel(DevPlane
     constexpr int CSS = CS / S;                               // chunk steps per slice
     constexpr int NT = kBlock * S;                            // threads per workgroup
     using XP = XPieces<FMT, XQ, NT>;
-    constexpr int D = 2;                                      // chunk steps in flight
+    // chunk steps in flight: two for a runtime K; a static K outside the
+    // grouped form (BF16, 8 steps) keeps its whole row in flight at 1 or 2
+    // rows per wave, half of it at 4
+    constexpr int D = CS > 0 && !GROUPED ? (R <= 2 ? CS : CS / 2) : 2;
     extern __shared__ float4 smem[];
     uint32_t* xs = (uint32_t*)smem;
 
