@@ -428,11 +428,11 @@ GemvGeom gemv_m1_default_geom(int fmt, int64_t N, int64_t K, bool pairs, bool no
     case kBF16: steps = static_steps<kBF16>(K); break;
     }
     if (!grouped_form(steps)) {
-        // A quantized runtime K of 16384 or more fills most of a CU's LDS
-        // with staged x (one 4-wave workgroup per CU), so each wave takes 4
-        // rows to keep enough weight bytes in flight.
+        // A runtime K of 16384 or more fills most of a CU's LDS with staged
+        // x (one 4-wave workgroup per CU), so each wave takes 4 rows to keep
+        // enough weight bytes in flight.
         const bool big = N * K >= ((int64_t)32 << 20);
-        g.rows_per_wave = N >= 65536 || (big && K >= 16384 && fmt != kBF16) ? 4 : big ? 2 : 1;
+        g.rows_per_wave = N >= 65536 || (big && K >= 16384) ? 4 : big ? 2 : 1;
         return g;
     }
     if (pairs) {

@@ -63,7 +63,7 @@ def bits(t):
 
 
 M1_CASES = [(1, 1000, 4096), (2, 300, 12288), (1, 130, 12288), (3, 500, 4096), (0, 200, 4096),
-            (1, 77, 4160)]
+            (1, 77, 4160), (0, 130, 4160)]
 
 
 @pytest.mark.parametrize("fmt,N,K", M1_CASES)
