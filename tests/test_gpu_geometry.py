@@ -149,3 +149,19 @@ def test_mfma_every_geometry_matches_oracle(M, N, K):
             with env(MBQ_MFMA_TR=tr, MBQ_MFMA_S=S):
                 Y = mbq().gemv_xq(dw, Xq, M=M).cpu().numpy()
             check_gemv(Y, ow, X, ref)
+
+
+@pytest.mark.parametrize("M,N,K", [(6, 1000, 4096), (16, 1000, 4096), (23, 300, 2048)])
+def test_mfma_f32x_every_geometry_matches_oracle(M, N, K):
+    """fp32 x through mbq_gemv_q on the matrix cores (x converted inside the
+    product, passes of 16 tokens) at every row-tile and K-part choice."""
+    print("geometry mfma fp32 x M=%d N=%d K=%d" % (M, N, K), flush=True)
+    ow, dw = weights(1, N, K, 9995 + N)
+    X = np.random.default_rng(M + N + 1).normal(size=(M, K)).astype(np.float32)
+    Xd = dev(X)
+    ref = oracle.gemv(ow, X)
+    for tr in (1, 2, 3, 4):
+        for S in (2, 4):
+            with env(MBQ_MFMA_TR=tr, MBQ_MFMA_S=S):
+                Y = mbq().gemv_q(dw, Xd).cpu().numpy()
+            check_gemv(Y, ow, X, ref)
