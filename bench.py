@@ -191,6 +191,74 @@ def mfma_pass(reps: int = 8):
     print("mfma pass: %d launches at M = 16 and at M = 64" % reps)
 
 
+def rows_traffic_pass(reps: int = 4):
+    """Launches profiled by the counter runs of the other rows: the BF16
+    512 x 4096 product, the fused-norm qkv (Q45 6144 x 4096) and vocabulary
+    (Q65 151936 x 4096) products, the gather of 8 Q25 experts, one RMSNorm
+    row of 4096 and LayerNorm 4096 x 2048, each reps times on its own copy of
+    the data (no graph), then one copy of COPY_BYTES bytes."""
+    import torch
+    import memory_bound_quantized_amd as mbq
+    import workloads
+    dev = torch.device("cuda:0")
+    alg = {}
+    c1 = workloads.config1()
+    Ws = [mbq.QWeight.from_host(*c1["W"]) for _ in range(reps)]
+    x = torch.from_numpy(c1["x"]).to(dev)
+    y = torch.empty(Ws[0].N, device=dev)
+    for W in Ws:
+        mbq.gemv_q(W, x, out=y)
+    alg["bf16_512x4096"] = Ws[0].nbytes + 4 * (Ws[0].N + Ws[0].K)
+    del Ws
+    rng = np.random.default_rng(77)
+    for name, fmt, N, K in (("qkv_6144x4096_q45_norm", 1, 6144, 4096),
+                            ("vocab_151936x4096_q65_norm", 2, 151936, 4096)):
+        W0 = mbq.QWeight.from_host(fmt, N, K, workloads.weight_planes(rng, fmt, N, K))
+        Ws = [W0] + [W0.clone() for _ in range(reps - 1)]
+        x = torch.randn(K, device=dev)
+        gam = torch.rand(K, device=dev) + 0.5
+        y = torch.empty(N, device=dev)
+        for W in Ws:
+            mbq.gemv_fused(W, x, gam, 1e-6, out=y)
+        alg[name] = W0.nbytes + 4 * (2 * K + N)
+        del Ws, W0
+        torch.cuda.empty_cache()
+    c5 = workloads.config5()
+    fmt, N, K, planes = c5["W"]
+    Ws = [mbq.QWeight.from_host(fmt, N, K, planes) for _ in range(reps)]
+    idx = torch.from_numpy(c5["idx"]).to(dev)
+    x = torch.from_numpy(c5["x"]).to(dev)
+    rpe, ns = c5["rows_per_expert"], len(c5["idx"])
+    y = torch.empty((ns, rpe), device=dev)
+    for W in Ws:
+        mbq.gemv_q_gather(W, rpe, idx, x, out=y)
+    alg["gather_8_of_64_q25_1536x4096"] = ns * Ws[0].nbytes // (N // rpe) + 4 * K + 4 * ns * rpe + 4 * ns
+    del Ws
+    xr = torch.from_numpy(c1["x"]).to(dev)
+    gr = torch.from_numpy(c1["gamma"]).to(dev)
+    yr = torch.empty_like(xr)
+    for _ in range(reps):
+        mbq.rmsnorm(xr, gr, c1["eps"], out=yr)
+    alg["rmsnorm_4096"] = 3 * 4 * xr.numel()
+    X = torch.from_numpy(c5["ln_x"]).to(dev)
+    Xs = [X] + [X.clone() for _ in range(reps - 1)]
+    gam = torch.from_numpy(c5["ln_gamma"]).to(dev)
+    bet = torch.from_numpy(c5["ln_beta"]).to(dev)
+    Yl = torch.empty_like(X)
+    for Xi in Xs:
+        mbq.layernorm(Xi, gam, bet, c5["ln_eps"], out=Yl)
+    alg["layernorm_4096x2048"] = 2 * X.numel() * 4 + 2 * X.shape[1] * 4
+    del Xs, X
+    torch.cuda.empty_cache()
+    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    mbq.probe_copy(dst, src)
+    torch.cuda.synchronize()
+    print("rows traffic pass: %d launches of each row, one %d-byte copy; algorithmic bytes per launch %s"
+          % (reps, COPY_BYTES, json.dumps(alg)))
+
+
 def write_traffic(fetch_dir: str, write_dir: str):
     """HBM bytes per launch from a FETCH_SIZE run and a WRITE_SIZE run of
     traffic_pass (rocprofv3 --pmc, KiB per dispatch), each scaled by what
@@ -426,6 +494,8 @@ def main():
     ap.add_argument("--no-rows", action="store_true", help="headline step only")
     ap.add_argument("--traffic-pass", action="store_true",
                     help="only the launches that the counter runs profile")
+    ap.add_argument("--rows-traffic-pass", action="store_true",
+                    help="only the other rows' launches that the counter runs profile")
     ap.add_argument("--mfma-pass", action="store_true",
                     help="only the matrix-core launches that the counter runs profile")
     ap.add_argument("--decode-only", type=int, metavar="TOKENS", default=0,
@@ -446,6 +516,9 @@ def main():
         return
     if args.mfma_pass:
         mfma_pass()
+        return
+    if args.rows_traffic_pass:
+        rows_traffic_pass()
         return
 
     import torch
