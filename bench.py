@@ -18,11 +18,17 @@ Every other step of the hot path is measured in the same run, in the same way
   * 8 gathered Q25 experts of 1536 x 4096; LayerNorm of 4096 rows of 2048;
   * one token through the 36-layer decode stream (ms per token, tokens/s,
     against the measured read ceiling).
-Also: the memory ceiling measured by a 4 GiB read probe, and the CPU oracle on
-a bounded sample of the headline step (cpu_baseline), which also checks the GPU
-result on that sample.
+Also: the measured ceilings (the larger of a 4 GiB read and a 2 GiB copy,
+memory latency from a pointer chase, matrix and vector issue rates), and the
+CPU oracle timed single-threaded and on every core on a bounded sample of the
+headline step (cpu_baseline); that leg also checks the GPU's headline
+products and its whole 36-layer decode token against the oracle, and the run
+fails instead of printing a line when they disagree.
 
-    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-rows]
+The timed region is exactly --steps steps (one replay of a graph of that
+many steps) after --warmup untimed ones.
+
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-rows] [--no-one-launch]
 """
 from __future__ import annotations
 
@@ -41,7 +47,7 @@ sys.path.insert(0, ROOT)
 METRIC = "achieved HBM GB/s (% of peak) for M=1 4.5-bpw GEMV; µs per 4096 RMSNorm row"
 PEAK_HBM_GBS = 8000.0           # MI355X published HBM3E bandwidth
 ROTATION_BYTES = 1 << 30        # >= 4x the 256 MB Infinity Cache
-MEASURED_READ_PEAK_GBS = 6080.0  # 4 GiB read on MI355X; the full run measures it live
+DEFAULT_PEAK_GBS = 6080.0  # the ceiling for --decode-only runs; a full run measures it live
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_m1.json")
 KERNEL_SOURCES = ["formats.h", "gemv_m1.hip", "staging.h", "device_common.h"]
 
@@ -73,17 +79,34 @@ def traffic_for(kernel_key: str):
     return None if ent is None else ent.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, y_up_gpu, y_down_gpu, budget_s: float = 12.0):
-    """The oracle on a bounded sample of the step, on the host cores."""
+def host_cores():
+    """Cores this process may run on, and the thread count the oracle legs
+    use: the affinity set, capped by OMP_NUM_THREADS when the job sets it
+    (the machine's CPU share)."""
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    cap = os.environ.get("OMP_NUM_THREADS")
+    use = min(avail, int(cap)) if cap and cap.isdigit() and int(cap) > 0 else avail
+    return {"nproc": os.cpu_count(), "affinity": avail, "omp_num_threads": cap, "threads": use}
+
+
+def cpu_baseline(cfg, y_up_gpu, y_down_gpu, decode=None, budget_s: float = 10.0):
+    """The oracle on the host cores: a bounded sample of the headline step,
+    timed single-threaded and row-parallel on every core the process has; and,
+    when the decode row ran, the oracle's whole 36-layer token, which checks
+    the GPU's token before its time is reported."""
+    import concurrent.futures as cf
     import oracle
-    threads = max(1, min(16, os.cpu_count() or 1))
+    cores = host_cores()
+    threads = cores["threads"]
     fmt_u, N_u, K_u, p_u = cfg["up"]
     fmt_d, N_d, K_d, p_d = cfg["down"]
     Wu = oracle.Planes(fmt_u, N_u, K_u, p_u)
     Wd = oracle.Planes(fmt_d, N_d, K_d, p_d)
-    # sample: the first 1/8 of each table's rows, one pass each
+    # sample: the first 1/8 of each table's rows
     ru, rd = N_u // 8, N_d // 8
-    import concurrent.futures as cf
     L = oracle.lib()
 
     def rows_job(W, x, y, r0, r1):
@@ -93,24 +116,29 @@ def cpu_baseline(cfg, y_up_gpu, y_down_gpu, budget_s: float = 12.0):
     xd = np.ascontiguousarray(cfg["x_down"], np.float32)
     yu = np.zeros(N_u, np.float32)
     yd = np.zeros(N_d, np.float32)
-    reps, t_total = 0, 0.0
-    while True:
-        t0 = time.perf_counter()
-        with cf.ThreadPoolExecutor(threads) as ex:
-            bu = np.linspace(0, ru, threads + 1).astype(int)
-            bd = np.linspace(0, rd, threads + 1).astype(int)
-            futs = [ex.submit(rows_job, Wu, xu, yu, int(bu[i]), int(bu[i + 1])) for i in range(threads)]
-            futs += [ex.submit(rows_job, Wd, xd, yd, int(bd[i]), int(bd[i + 1])) for i in range(threads)]
-            for f in futs:
-                f.result()
-        t_total += time.perf_counter() - t0
-        reps += 1
-        if t_total >= budget_s:
-            break
+
+    def leg(nthreads, budget):
+        reps, t_total = 0, 0.0
+        bu = np.linspace(0, ru, nthreads + 1).astype(int)
+        bd = np.linspace(0, rd, nthreads + 1).astype(int)
+        with cf.ThreadPoolExecutor(nthreads) as ex:
+            while t_total < budget:
+                t0 = time.perf_counter()
+                futs = [ex.submit(rows_job, Wu, xu, yu, int(bu[i]), int(bu[i + 1])) for i in range(nthreads)]
+                futs += [ex.submit(rows_job, Wd, xd, yd, int(bd[i]), int(bd[i + 1])) for i in range(nthreads)]
+                for f in futs:
+                    f.result()
+                t_total += time.perf_counter() - t0
+                reps += 1
+        return reps, t_total
+
     table_u = sum(p.nbytes for p in p_u if p is not None)
     table_d = sum(p.nbytes for p in p_d if p is not None)
     sample_bytes = table_u * ru // N_u + table_d * rd // N_d + 4 * (K_u + K_d + ru + rd)
-    gbs = sample_bytes * reps / t_total / 1e9
+    reps1, t1 = leg(1, budget_s / 2)
+    repsn, tn = leg(threads, budget_s)
+    gbs1 = sample_bytes * reps1 / t1 / 1e9
+    gbsn = sample_bytes * repsn / tn / 1e9
 
     def rel(a, b):
         a = np.asarray(a, np.float64)
@@ -119,11 +147,35 @@ def cpu_baseline(cfg, y_up_gpu, y_down_gpu, budget_s: float = 12.0):
 
     err_u = rel(y_up_gpu[:ru], yu[:ru])
     err_d = rel(y_down_gpu[:rd], yd[:rd])
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": "rows [0, N/8) of both tables (%d of %d Q45 rows, %d of %d Q65 rows), "
-                      "%d passes in %.1f s, fp64 oracle, row-parallel over %d threads"
-                      % (ru, N_u, rd, N_d, reps, t_total, threads),
-            "checked_rel_l2": {"q45_up": err_u, "q65_down": err_d}}
+    if max(err_u, err_d) > 1e-4:
+        raise SystemExit("headline products disagree with the oracle: rel-L2 %.3e, %.3e" % (err_u, err_d))
+    out = {"value": round(gbsn, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "sample": "rows [0, N/8) of both tables (%d of %d Q45 rows, %d of %d Q65 rows), "
+                     "%d passes in %.1f s, fp64 oracle, row-parallel over %d threads"
+                     % (ru, N_u, rd, N_d, repsn, tn, threads),
+           "single_thread": {"value": round(gbs1, 4), "unit": "GB/s", "passes": reps1,
+                             "seconds": round(t1, 2)},
+           "host": cores,
+           "checked_rel_l2": {"q45_up": err_u, "q65_down": err_d}}
+    if decode is not None:
+        # the whole token in the oracle (each product's rows over the threads)
+        t0 = time.perf_counter()
+        lay = [{k: oracle.Planes(*v) for k, v in e.items()} for e in decode["cfg"]["layers"]]
+        c3 = decode["cfg"]
+        h_ref, lg_ref = oracle.decode_token_parallel(lay, oracle.Planes(*c3["vocab"]), c3["g1"],
+                                                     c3["g2"], c3["gf"], c3["eps"], c3["h0"],
+                                                     threads=threads)
+        t_tok = time.perf_counter() - t0
+        errs = {}
+        for name, (h, lg) in decode["outputs"].items():
+            errs[name] = {"h": rel(h, h_ref), "logits": rel(lg, lg_ref)}
+        out["decode_token"] = {"seconds_per_token": round(t_tok, 3), "threads": threads,
+                               "checked_rel_l2": errs}
+        bad = [n for n, e in errs.items() if max(e["h"], e["logits"]) > 1e-4]
+        if bad:
+            raise SystemExit("decode token disagrees with the oracle chain (%s): %s"
+                             % (", ".join(bad), json.dumps(errs)))
+    return out
 
 
 COPY_BYTES = 1 << 29            # plain copy of known size that calibrates the counters
@@ -338,46 +390,62 @@ def rotated(W0, min_bytes=ROTATION_BYTES):
     return [W0] + [W0.clone() for _ in range(n - 1)]
 
 
-def decode_row(workloads, torch, dev, read_peak, ntok=20):
-    """Workload 3: ms per token of the 36-layer step, one HIP graph per token."""
+def decode_row(workloads, torch, dev, peak_gbs, ntok=20, one_launch=True, keep=None):
+    """Workload 3: ms per token of the 36-layer step, one HIP graph per token,
+    and the same token in one cooperative launch.  keep: a dict that receives
+    the host inputs and each form's h and logits after one token from h0, for
+    the oracle check in the CPU leg."""
     from memory_bound_quantized_amd.decode import DecodeModel
     c3 = workloads.config3()
     model = DecodeModel(c3["layers"], c3["vocab"], c3["g1"], c3["g2"], c3["gf"], c3["eps"])
-    del c3["layers"]
-    h = torch.from_numpy(c3["h0"]).to(dev)
+    h0 = torch.from_numpy(c3["h0"]).to(dev)
+    h = h0.clone()
     logits = torch.empty(model.vocab, device=dev)
     g = capture(lambda: model.step(h, logits))
+    h.copy_(h0)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    outputs = {"graph of launches": (h.cpu().numpy(), logits.cpu().numpy())}
     g.replay()
     ms = timed(g, ntok) / ntok
     B = model.weight_bytes + 4 * 36 * 2 * model.d + 4 * model.d
     B_all = B + 4 * (36 * (model.dq + 2 * model.dkv + model.f + 6 * model.d) + model.vocab)
-    floor_ms = B / (read_peak * 1e9) * 1e3
-    # the same token in one cooperative launch (not capturable: timed as
-    # back-to-back launches between HIP events on the current stream)
-    hp, lp = h.clone(), torch.empty_like(logits)
-    model.step_persistent(hp, lp)
-    torch.cuda.synchronize()
-    ok = model.status() == 0
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(ntok):
-        model.step_persistent(hp, lp)
-    b.record()
-    torch.cuda.synchronize()
-    ms_p = a.elapsed_time(b) / ntok
+    floor_ms = B / (peak_gbs * 1e9) * 1e3
     row = {"ms_per_token": round(ms, 4), "tokens_per_s": round(1e3 / ms, 1),
            "weight_bytes": model.weight_bytes, "bytes_per_token": int(B_all),
            "gbs": round(B_all / (ms * 1e-3) / 1e9, 1),
-           "floor_ms_at_read_peak": round(floor_ms, 4), "ratio_to_floor": round(ms / floor_ms, 3),
-           "launches_per_token": 4 * 36 + 1, "tokens_timed": ntok,
-           "one_launch": {"ms_per_token": round(ms_p, 4), "ratio_to_floor": round(ms_p / floor_ms, 3),
-                          "status_ok": ok}}
+           "floor_ms_at_measured_peak": round(floor_ms, 4), "ratio_to_floor": round(ms / floor_ms, 3),
+           "launches_per_token": 4 * 36 + 1, "tokens_timed": ntok}
+    if one_launch:
+        # the same token in one cooperative launch (not capturable: timed as
+        # back-to-back launches between HIP events on the current stream)
+        hp, lp = h0.clone(), torch.empty_like(logits)
+        model.step_persistent(hp, lp)
+        torch.cuda.synchronize()
+        ok_first = model.status() == 0
+        outputs["one launch"] = (hp.cpu().numpy(), lp.cpu().numpy())
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(ntok):
+            model.step_persistent(hp, lp)
+        b.record()
+        torch.cuda.synchronize()
+        ms_p = a.elapsed_time(b) / ntok
+        ok = ok_first and model.status() == 0
+        if not ok:
+            raise SystemExit("one-launch decode step reported status %d" % model.status())
+        row["one_launch"] = {"ms_per_token": round(ms_p, 4), "ratio_to_floor": round(ms_p / floor_ms, 3),
+                             "status_ok": ok}
+    if keep is not None:
+        keep["cfg"] = {k: v for k, v in c3.items()}
+        keep["outputs"] = outputs
     del model, g
     torch.cuda.empty_cache()
     return row
 
 
-def rows_bench(mbq, workloads, torch, dev, read_peak):
+def rows_bench(mbq, workloads, torch, dev, peak_gbs, one_launch=True, keep=None):
     """Every other step of the hot path, each on cold weights."""
     from memory_bound_quantized_amd.decode import DecodeModel, interleave_rows, concat_rows
     rows = {}
@@ -419,7 +487,7 @@ def rows_bench(mbq, workloads, torch, dev, read_peak):
         us = per_launch_us(f, Ws)
         b = W0.nbytes + 4 * (K + (N // 2 if kind == "silu" else N)) + (4 * K if kind in ("norm", "silu") else 0) \
             + (4 * N if kind == "acc" else 0)
-        per_shape[name] = {"us": round(us, 3), "gbs": gbs(b, us), "frac_of_read_peak": round(b / (us * 1e-6) / 1e9 / read_peak, 4)}
+        per_shape[name] = {"us": round(us, 3), "gbs": gbs(b, us), "frac_of_measured_peak": round(b / (us * 1e-6) / 1e9 / peak_gbs, 4)}
         del Ws, W0
         torch.cuda.empty_cache()
     rows["m1_decode_shapes"] = per_shape
@@ -481,17 +549,84 @@ def rows_bench(mbq, workloads, torch, dev, read_peak):
     torch.cuda.empty_cache()
 
     # ---- workload 3: one token through the 36-layer stream
-    rows["decode_36_layers"] = decode_row(workloads, torch, dev, read_peak)
+    rows["decode_36_layers"] = decode_row(workloads, torch, dev, peak_gbs, one_launch=one_launch,
+                                          keep=keep)
     return rows
+
+
+def ceilings(mbq, torch, dev, stream, full=True):
+    """The measured ceilings: HBM bandwidth as the larger of a 4 GiB read and
+    a 2 GiB in-device copy (read and write both counted), best of 5 each; the
+    memory latency from a dependent pointer chase over 2 GiB; the issue rates
+    of the fp16 matrix instructions, fp32 FMA and the int8 dot4 the vector
+    kernels use."""
+    def best_of(fn, n=5):
+        best = float("inf")
+        for _ in range(n):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            best = min(best, a.elapsed_time(b) * 1e-3)
+        return best
+
+    out = {}
+    buf = torch.empty(1 << 32, dtype=torch.uint8, device=dev)
+    sink = torch.empty(4096, device=dev)
+    mbq.probe_read(buf, sink, stream)
+    out["read_gbs"] = round(buf.numel() / best_of(lambda: mbq.probe_read(buf, sink, stream)) / 1e9, 1)
+    half = 1 << 31
+    src, dst = buf[:half], buf[half:]
+    mbq.probe_copy(dst, src, stream)
+    out["copy_gbs"] = round(2 * half / best_of(lambda: mbq.probe_copy(dst, src, stream)) / 1e9, 1)
+    out["peak_gbs"] = max(out["read_gbs"], out["copy_gbs"])
+    if full:
+        chase = buf[:half]
+        n = mbq.probe_chase_init(chase, stream)
+        isink = torch.empty(4, dtype=torch.int32, device=dev)
+        hops = 20000
+        mbq.probe_chase(chase, 1000, isink, stream)
+        t = best_of(lambda: mbq.probe_chase(chase, hops, isink, stream), 3)
+        lat_ns = t / hops * 1e9
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        out["latency"] = {"ns_per_hop": round(lat_ns, 1), "entries": n, "span_bytes": half,
+                          "bytes_in_flight_at_peak": int(out["peak_gbs"] * lat_ns),
+                          "bytes_in_flight_per_cu": int(out["peak_gbs"] * lat_ns / cus),
+                          "compute_units": cus}
+        psink = torch.empty(2048, device=dev)
+        rates = {}
+        for kind, name, iters in ((mbq.PEAK_MFMA_F16, "mfma_f16_tflops", 4000),
+                                  (mbq.PEAK_FMA_F32, "fma_f32_tflops", 20000),
+                                  (mbq.PEAK_DOT4_I8, "dot4_i8_tops", 20000)):
+            ops = mbq.probe_peak(kind, iters, psink, stream)
+            rates[name] = round(ops / best_of(lambda: mbq.probe_peak(kind, iters, psink, stream), 3) / 1e12, 2)
+        out.update(rates)
+        # M* = (w/16)(R/BW) for the 4.5-bit table at the measured bandwidth,
+        # with R the multiply-adds per second each path's arithmetic turns
+        # into useful sums: the matrix path issues two fp16 products per sum
+        # (x as high and low parts), the vector path three byte products per
+        # sum (x as three byte digits, four byte products per dot4)
+        bw = out["peak_gbs"] * 1e9
+        r_mfma = rates["mfma_f16_tflops"] * 1e12 / 2 / 2
+        r_vec = rates["dot4_i8_tops"] * 1e12 / 2 / 3
+        out["m_star_q45"] = {"matrix_cores": round(4.5 / 16 * r_mfma / bw, 2),
+                             "vector_units": round(4.5 / 16 * r_vec / bw, 2),
+                             "rule": "M* = (w/16)(R/BW), w = 4.5, R = multiply-adds/s of each path's arithmetic"}
+    del buf
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=160)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true", help="headline step only")
+    ap.add_argument("--no-one-launch", action="store_true",
+                    help="leave out the cooperative one-launch decode step (for profiled runs)")
     ap.add_argument("--traffic-pass", action="store_true",
                     help="only the launches that the counter runs profile")
     ap.add_argument("--rows-traffic-pass", action="store_true",
@@ -510,6 +645,9 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(every box has one MI355X); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        sys.exit(2)
 
     if args.traffic_pass:
         traffic_pass()
@@ -527,28 +665,15 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
-    if args.decode_only:
-        torch.cuda.set_device(dev)
-        print(json.dumps({"decode_36_layers": decode_row(workloads, torch, dev, MEASURED_READ_PEAK_GBS,
-                                                          ntok=args.decode_only)}))
-        return
     torch.cuda.set_device(dev)
+    if args.decode_only:
+        print(json.dumps({"decode_36_layers": decode_row(workloads, torch, dev, DEFAULT_PEAK_GBS,
+                                                          ntok=args.decode_only,
+                                                          one_launch=not args.no_one_launch)}))
+        return
     stream = torch.cuda.current_stream()
-
-    # measured memory ceiling: 4 GiB read, best of 5
-    buf = torch.empty(1 << 32, dtype=torch.uint8, device=dev)
-    sink = torch.empty(4096, device=dev)
-    mbq.probe_read(buf, sink, stream)
-    best = 0.0
-    for _ in range(5):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        mbq.probe_read(buf, sink, stream)
-        b.record(stream)
-        torch.cuda.synchronize()
-        best = max(best, buf.numel() / (a.elapsed_time(b) * 1e-3) / 1e9)
-    del buf
-    torch.cuda.empty_cache()
+    ceil = ceilings(mbq, torch, dev, stream, full=not args.no_rows)
+    peak = ceil["peak_gbs"]
 
     cfg = workloads.config2()
     fu, Nu, Ku, pu = cfg["up"]
@@ -564,38 +689,48 @@ def main():
     y_up = torch.empty(Nu, device=dev)
     y_dn = torch.empty(Nd, device=dev)
 
-    def pass_step():
-        for i in range(ncopy):
-            mbq.gemv_q(ups[i], x_up, out=y_up)
-            mbq.gemv_q(dns[i], x_dn, out=y_dn)
+    # step i uses weight copy i % ncopy: consecutive steps never share weights
+    def steps_graph(n, up=True, down=True):
+        def body():
+            for i in range(n):
+                if up:
+                    mbq.gemv_q(ups[i % ncopy], x_up, out=y_up)
+                if down:
+                    mbq.gemv_q(dns[i % ncopy], x_dn, out=y_dn)
+        return capture(body)
 
-    def pass_up():
-        for i in range(ncopy):
-            mbq.gemv_q(ups[i], x_up, out=y_up)
-
-    def pass_dn():
-        for i in range(ncopy):
-            mbq.gemv_q(dns[i], x_dn, out=y_dn)
-
-    g_step, g_up, g_dn = capture(pass_step), capture(pass_up), capture(pass_dn)
-    reps = max(1, -(-args.steps // ncopy))          # graph replays in the timed region
-    steps = reps * ncopy
-    warm_reps = max(1, -(-args.warmup // ncopy))
-    for _ in range(warm_reps):
-        g_step.replay()
+    K, W = args.steps, args.warmup
+    g_steps = steps_graph(K)
+    if W > 0:
+        g_warm = steps_graph(W)
+        g_warm.replay()
+        del g_warm
     torch.cuda.synchronize()
     y_up_first = y_up.cpu().numpy().copy()
     y_dn_first = y_dn.cpu().numpy().copy()
 
-    # timed region: `steps` steps = reps replays of the whole-step graph
-    total_ms = timed(g_step, reps, stream)
-    ms_per_step = total_ms / steps
-    # per-kernel averages: graphs of one kernel kind, same rotation
-    up_ms = timed(g_up, reps, stream) / steps
-    dn_ms = timed(g_dn, reps, stream) / steps
+    # timed region: exactly K steps (one replay of the K-step graph)
+    total_ms = timed(g_steps, 1, stream)
+    ms_per_step = total_ms / K
     b_up, b_dn = gemv_bytes(W_up0), gemv_bytes(W_dn0)
     value = (b_up + b_dn) / (ms_per_step * 1e-3) / 1e9
-    del g_step, g_up, g_dn, ups, dns
+
+    # ledger: 3 windows in alternating order of the step and each kernel kind
+    # alone (graphs of max(K, 2 ncopy) launches each), medians, and whether the
+    # windows agree within 3 %
+    nl = max(K, 2 * ncopy)
+    g_all, g_up, g_dn = steps_graph(nl), steps_graph(nl, down=False), steps_graph(nl, up=False)
+    wins = {"step": [], "up": [], "down": []}
+    orders = (("step", "up", "down"), ("down", "up", "step"), ("up", "step", "down"))
+    graphs = {"step": g_all, "up": g_up, "down": g_dn}
+    for order in orders:
+        for k in order:
+            graphs[k].replay()
+            wins[k].append(timed(graphs[k], 1, stream) / nl)
+    med = {k: float(np.median(v)) for k, v in wins.items()}
+    spread = {k: (max(v) - min(v)) / med[k] for k, v in wins.items()}
+    up_ms, dn_ms = med["up"], med["down"]
+    del g_steps, g_all, g_up, g_dn, ups, dns
 
     # RMSNorm of one 4096-wide row (the metric's second part), one row per launch
     c1 = workloads.config1()
@@ -615,7 +750,8 @@ def main():
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                 "traffic": traffic_for(dom), "algorithmic_bytes_per_launch": d_bytes,
                 "avg_launch_us": round(d_ms * 1e3, 3),
-                "frac_of_measured_read_peak": round(achieved / best, 4)}
+                "measured_peak_gbs": peak,
+                "frac_of_measured_peak": round(achieved / peak, 4)}
     # what a plain read of the same byte count achieves per launch, timed the
     # same way (graph of cold launches over >= 1 GiB of distinct buffers)
     rd_bytes = d_bytes
@@ -630,25 +766,36 @@ def main():
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
-        "steps": steps, "warmup": warm_reps * ncopy, "ms_per_step": round(ms_per_step, 5),
+        "steps": K, "warmup": W, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "M=1 GEMV: Q45 12288x4096 (4.5 bpw) + Q65 4096x12288 (6.5625 bpw), "
-                               "fp32 x and accumulation, weights rotated over %d copies (%.2f GB)"
+                               "fp32 x and accumulation, step i on weight copy i mod %d (%.2f GB)"
                                % (ncopy, ncopy * per_copy / 1e9),
                    "tokens_per_product": 1, "gpus": 1},
         "roofline": roofline,
         "kernels": {k: {"avg_us": round(v[1] * 1e3, 3), "gbs": round(v[0] / (v[1] * 1e-3) / 1e9, 1),
                         "frac_of_peak": round(v[0] / (v[1] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                        "frac_of_measured_read_peak": round(v[0] / (v[1] * 1e-3) / 1e9 / best, 4)}
+                        "frac_of_measured_peak": round(v[0] / (v[1] * 1e-3) / 1e9 / peak, 4)}
                     for k, v in kern.items()},
+        "ledger": {"launches_per_window": nl, "windows_ms_per_launch": {k: [round(x * 1e3, 3) for x in v]
+                                                                        for k, v in wins.items()},
+                   "spread": {k: round(v, 4) for k, v in spread.items()},
+                   "windows_agree_within_3pct": all(v <= 0.03 for v in spread.values())},
         "rmsnorm_us_per_4096_row": round(rms_us, 3),
-        "measured_read_peak_gbs": round(best, 1),
+        "ceilings": ceil,
     }
+    keep = {} if not args.no_rows else None
     if not args.no_rows:
-        out["rows"] = rows_bench(mbq, workloads, torch, dev, best)
+        out["rows"] = rows_bench(mbq, workloads, torch, dev, peak, one_launch=not args.no_one_launch,
+                                 keep=keep)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg, y_up_first, y_dn_first)
+        out["cpu_baseline"] = cpu_baseline(cfg, y_up_first, y_dn_first,
+                                           decode=keep if keep else None)
+        if "rows" in out:
+            out["rows"]["decode_36_layers"]["checked_against_oracle"] = True
+    elif "rows" in out:
+        out["rows"]["decode_36_layers"]["checked_against_oracle"] = False
     print(json.dumps(out))
 
 

@@ -361,6 +361,32 @@ int mbq_unpack_codes(const mbq_qweight* W, uint8_t* codes_out, void* stream);
 int mbq_probe_read(const void* buf, size_t bytes, float* sink, void* stream);
 int mbq_probe_copy(void* dst, const void* src, size_t bytes, void* stream);
 
+/* Memory latency ([roofline-holds] "How the breakouts tie out: Little and
+ * Volkov": bytes in flight = bandwidth x latency): a dependent random
+ * pointer chase.  mbq_probe_chase_init writes a chain of *entries =
+ * the largest power of two <= bytes / 256 entries into buf (device, 4-byte
+ * aligned, >= 256 bytes), one entry per 256 bytes, visiting every entry once
+ * per cycle in a scattered order.  mbq_probe_chase follows `hops` >= 1 hops
+ * of it with one lane (each hop one full memory round trip) and writes the
+ * last entry reached to sink (device uint32).  Time it with events:
+ * latency = time / hops.  MBQ_EINVAL for bytes < 256 or hops < 1. */
+int mbq_probe_chase_init(void* buf, size_t bytes, uint32_t* entries, void* stream);
+int mbq_probe_chase(const void* buf, int64_t hops, uint32_t* sink, void* stream);
+
+/* Issue-rate loops for the arithmetic ceilings ([roofline-holds] "The
+ * Math": M* = (w/16)(R/BW) needs the measured rate R; "How I ran it": peak
+ * loops with no memory traffic).  kind MBQ_PEAK_MFMA_F16: fp16 matrix
+ * instructions (16x16x32, fp32 accumulate); MBQ_PEAK_FMA_F32: fp32 fused
+ * multiply-add on the vector units (the packed two-wide form is not used in
+ * this library's code); MBQ_PEAK_DOT4_I8: the 4-way byte dot product the
+ * quantized vector kernels use.  Each launch runs `iters` >= 1 rounds on
+ * every wave; *ops (host) receives the operations executed (flops: two per
+ * multiply-add).  sink: device fp32, >= 2048 floats. */
+#define MBQ_PEAK_MFMA_F16 0
+#define MBQ_PEAK_FMA_F32  1
+#define MBQ_PEAK_DOT4_I8  2
+int mbq_probe_peak(int kind, int64_t iters, float* sink, int64_t* ops, void* stream);
+
 /* Static text for a status code, and the calling thread's last error detail
  * (empty string if none). */
 const char* mbq_status_str(int status);

@@ -261,3 +261,27 @@ def probe_read(buf, sink, stream=None):
 def probe_copy(dst, src, stream=None):
     check(lib.mbq_probe_copy(_ptr(dst), _ptr(src), src.numel() * src.element_size(),
                              _stream(stream)))
+
+
+def probe_chase_init(buf, stream=None) -> int:
+    """Write the pointer-chase chain into buf (a cuda tensor); returns the
+    number of entries."""
+    n = ctypes.c_uint32()
+    check(lib.mbq_probe_chase_init(_ptr(buf), buf.numel() * buf.element_size(), ctypes.byref(n),
+                                   _stream(stream)))
+    return int(n.value)
+
+
+def probe_chase(buf, hops: int, sink, stream=None):
+    """Follow `hops` hops of the chain in buf; the last entry goes to sink."""
+    check(lib.mbq_probe_chase(_ptr(buf), int(hops), _ptr(sink), _stream(stream)))
+
+
+PEAK_MFMA_F16, PEAK_FMA_F32, PEAK_DOT4_I8 = 0, 1, 2
+
+
+def probe_peak(kind: int, iters: int, sink, stream=None) -> int:
+    """One issue-rate launch; returns the operations it executes."""
+    ops = ctypes.c_int64()
+    check(lib.mbq_probe_peak(int(kind), int(iters), _ptr(sink), ctypes.byref(ops), _stream(stream)))
+    return int(ops.value)

@@ -21,7 +21,8 @@ EXPORTS = (
     "mbq_decode_prepare", "mbq_decode_step_persistent",
     "mbq_xq_bytes", "mbq_stage_x", "mbq_gemv_xq", "mbq_rmsnorm_xq",
     "mbq_silu_mul_xq", "mbq_rmsnorm", "mbq_layernorm", "mbq_silu_mul", "mbq_dequant_f32",
-    "mbq_unpack_codes", "mbq_probe_read", "mbq_probe_copy", "mbq_status_str",
+    "mbq_unpack_codes", "mbq_probe_read", "mbq_probe_copy", "mbq_probe_chase_init",
+    "mbq_probe_chase", "mbq_probe_peak", "mbq_status_str",
     "mbq_last_error", "mbq_version",
 )
 
@@ -96,6 +97,9 @@ def _load():
         "mbq_unpack_codes": (i32, [ctypes.POINTER(QWeightDesc), vp, vp]),
         "mbq_probe_read": (i32, [vp, sz, vp, vp]),
         "mbq_probe_copy": (i32, [vp, vp, sz, vp]),
+        "mbq_probe_chase_init": (i32, [vp, sz, ctypes.POINTER(ctypes.c_uint32), vp]),
+        "mbq_probe_chase": (i32, [vp, i64, vp, vp]),
+        "mbq_probe_peak": (i32, [i32, i64, vp, ctypes.POINTER(ctypes.c_int64), vp]),
         "mbq_status_str": (ctypes.c_char_p, [i32]),
         "mbq_last_error": (ctypes.c_char_p, []),
         "mbq_version": (i32, []),

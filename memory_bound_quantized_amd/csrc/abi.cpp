@@ -838,4 +838,30 @@ int mbq_probe_copy(void* dst, const void* src, size_t bytes, void* stream) {
     return hip_status(mbq::launch_probe_copy(dst, src, bytes, (hipStream_t)stream), fn);
 }
 
+int mbq_probe_chase_init(void* buf, size_t bytes, uint32_t* entries, void* stream) {
+    const char* fn = "mbq_probe_chase_init";
+    if (!buf || !entries) return fail(MBQ_EINVAL, "%s: NULL pointer", fn);
+    if (bytes < 256) return fail(MBQ_EINVAL, "%s: bytes < 256", fn);
+    if (!aligned(buf, 4)) return fail(MBQ_EALIGN, "%s: buf must be 4-byte aligned", fn);
+    *entries = mbq::chase_entries(bytes);
+    return hip_status(mbq::launch_chase_init(buf, bytes, (hipStream_t)stream), fn);
+}
+
+int mbq_probe_chase(const void* buf, int64_t hops, uint32_t* sink, void* stream) {
+    const char* fn = "mbq_probe_chase";
+    if (!buf || !sink) return fail(MBQ_EINVAL, "%s: NULL pointer", fn);
+    if (hops < 1) return fail(MBQ_EINVAL, "%s: hops < 1", fn);
+    if (!aligned(buf, 4) || !aligned(sink, 4)) return fail(MBQ_EALIGN, "%s: misaligned", fn);
+    return hip_status(mbq::launch_chase(buf, hops, sink, (hipStream_t)stream), fn);
+}
+
+int mbq_probe_peak(int kind, int64_t iters, float* sink, int64_t* ops, void* stream) {
+    const char* fn = "mbq_probe_peak";
+    if (kind < MBQ_PEAK_MFMA_F16 || kind > MBQ_PEAK_DOT4_I8) return fail(MBQ_EINVAL, "%s: unknown kind %d", fn, kind);
+    if (iters < 1 || !sink || !ops) return fail(MBQ_EINVAL, "%s: iters < 1 or NULL pointer", fn);
+    if (!aligned(sink, 4)) return fail(MBQ_EALIGN, "%s: sink must be 4-byte aligned", fn);
+    *ops = mbq::peak_ops(kind, iters);
+    return hip_status(mbq::launch_peak(kind, iters, sink, (hipStream_t)stream), fn);
+}
+
 }  // extern "C"

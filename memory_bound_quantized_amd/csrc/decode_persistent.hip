@@ -434,18 +434,27 @@ __device__ __forceinline__ void copy_to_lds(const float* src, float* dst, int n)
                                          COH ? 16 : 0);
 }
 
+// Arrival is a release at agent scope: the activations this workgroup stored
+// for the next phase (coh_store) happen before its count, and the group's
+// last arrival passes them on to the global counter with a second release
+// (a release sequence through the group counter's read-modify-writes).
 __device__ __forceinline__ void barrier_arrive(uint32_t* ctr, int G, uint32_t k) {
     if ((threadIdx.x & (kWave - 1)) == 0) {
         const int ng = G < kBarGroups ? G : kBarGroups;
         const int grp = (int)blockIdx.x % ng;
         const uint32_t members = (uint32_t)(G / ng + (grp < G % ng ? 1 : 0));
-        const uint32_t old = __hip_atomic_fetch_add(ctr + kBarStride * (1 + grp), 1u, __ATOMIC_RELAXED,
+        const uint32_t old = __hip_atomic_fetch_add(ctr + kBarStride * (1 + grp), 1u, __ATOMIC_ACQ_REL,
                                                     __HIP_MEMORY_SCOPE_AGENT);
         if (old == members * (k + 1) - 1)
-            __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
+// The wait polls with relaxed loads and ends with an agent-scope acquire
+// fence: once the global count shows every arrival, every workgroup's
+// released stores are visible to the loads this wave issues next (the
+// device-scope copies of h, q|k|v or m into LDS).  The spin is bounded; on
+// timeout it sets bit 0 of err and returns, so every wave still ends.
 __device__ __forceinline__ void barrier_wait(uint32_t* ctr, uint32_t target, uint32_t* err) {
     if ((threadIdx.x & (kWave - 1)) == 0) {
         uint32_t spins = 0;
@@ -458,6 +467,7 @@ __device__ __forceinline__ void barrier_wait(uint32_t* ctr, uint32_t target, uin
             }
         }
     }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
 struct Lds {

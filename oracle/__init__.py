@@ -175,19 +175,22 @@ def gemv(W: Planes, x: np.ndarray, y0: np.ndarray | None = None,
     return y
 
 
-def gemv_parallel(W: Planes, x: np.ndarray, threads: int | None = None) -> np.ndarray:
-    """Same result as gemv(); output rows split over threads (ctypes drops the GIL)."""
+def gemv_parallel(W: Planes, x: np.ndarray, threads: int | None = None,
+                  y0: np.ndarray | None = None) -> np.ndarray:
+    """Same result as gemv() (y0: the accumulate form); output rows split over
+    threads (ctypes drops the GIL).  Every output row is computed by the same
+    code in the same order as in gemv(), so the two agree bit for bit."""
     import concurrent.futures as cf
     x = _c(np.atleast_2d(x), np.float32)
     M = x.shape[0]
-    y = np.zeros((M, W.N), np.float32)
+    y = np.zeros((M, W.N), np.float32) if y0 is None else _c(np.atleast_2d(y0), np.float32).copy()
     threads = threads or os.cpu_count() or 1
     bounds = np.linspace(0, W.N, threads + 1).astype(np.int64)
     L = lib()
 
     def run(i):
-        L.oracle_gemv(W.fmt, W.cptr, W.N, W.K, _ptr(x), M, W.K, _ptr(y), W.N, 0,
-                      int(bounds[i]), int(bounds[i + 1]))
+        L.oracle_gemv(W.fmt, W.cptr, W.N, W.K, _ptr(x), M, W.K, _ptr(y), W.N,
+                      0 if y0 is None else 1, int(bounds[i]), int(bounds[i + 1]))
 
     with cf.ThreadPoolExecutor(threads) as ex:
         list(ex.map(run, range(threads)))
@@ -290,4 +293,31 @@ def decode_token(layers, vocab: Planes, g1, g2, gf, eps: float, h0,
                               _ptr(ws), _ptr(htr))
     if trace:
         return h, logits, htr[:L]
+    return h, logits
+
+
+def decode_token_parallel(layers, vocab: Planes, g1, g2, gf, eps: float, h0,
+                          threads: int | None = None):
+    """decode_token() with each matrix-vector product's output rows split over
+    threads: the same steps in the same order (oracle_rmsnorm, oracle_gemv,
+    oracle_silu_mul, fp32 between steps), so the result is decode_token()'s
+    bit for bit.  For the full-size stack, where the single-threaded chain
+    takes minutes.  Returns (h_final, logits)."""
+    d = vocab.K
+    h = _c(h0, np.float32).copy()
+    g1 = _c(g1, np.float32)
+    g2 = _c(g2, np.float32)
+    for l, lay in enumerate(layers):
+        a = rmsnorm(h, g1[l * d:(l + 1) * d], eps)[0]
+        q = gemv_parallel(lay["q"], a, threads)[0]
+        gemv_parallel(lay["k"], a, threads)          # computed, not consumed
+        gemv_parallel(lay["v"], a, threads)
+        h = gemv_parallel(lay["o"], q, threads, y0=h)[0]
+        b = rmsnorm(h, g2[l * d:(l + 1) * d], eps)[0]
+        g = gemv_parallel(lay["gate"], b, threads)[0]
+        u = gemv_parallel(lay["up"], b, threads)[0]
+        m = silu_mul(g, u)
+        h = gemv_parallel(lay["down"], m, threads, y0=h)[0]
+    z = rmsnorm(h, gf, eps)[0]
+    logits = gemv_parallel(vocab, z, threads)[0]
     return h, logits

@@ -279,3 +279,48 @@ def test_workload3_full_size_layers():
         print("  rel-L2 h %.2e logits %.2e" % (e_h, e_l), flush=True)
         assert e_h <= 1e-4 and e_l <= 1e-4
         del model
+
+
+def test_workload3_whole_token_both_forms():
+    """Workload 3 whole: one token through all 36 full-size layers and the
+    151936-row vocabulary product, as the launch chain (captured in a graph,
+    as the benchmark runs it) and as the one-launch step, against the
+    oracle's chain (decode_token_parallel: decode_token's result, each
+    product's rows split over threads).  Error builds up over 36 layers; the
+    bar is still rel-L2 <= 1e-4 on h and on the logits."""
+    import os
+    from memory_bound_quantized_amd.decode import DecodeModel
+    print("workload3 whole token: generating 4.65 GB of weights", flush=True)
+    cfg = workloads.config3()
+    model = DecodeModel(cfg["layers"], cfg["vocab"], cfg["g1"], cfg["g2"], cfg["gf"], cfg["eps"])
+    h = dev(cfg["h0"])
+    logits = torch.empty(model.vocab, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        model.step(h, logits)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    h.copy_(dev(cfg["h0"]))
+    with torch.cuda.graph(g):
+        model.step(h, logits)
+    h.copy_(dev(cfg["h0"]))
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    hp = dev(cfg["h0"])
+    lp = torch.empty(model.vocab, device="cuda")
+    model.step_persistent(hp, lp)
+    torch.cuda.synchronize()
+    assert model.status() == 0
+    print("workload3 whole token: oracle chain on %d threads" % min(16, os.cpu_count() or 1), flush=True)
+    lay = [{k: oracle.Planes(*v) for k, v in e.items()} for e in cfg["layers"]]
+    h_ref, lg_ref = oracle.decode_token_parallel(lay, oracle.Planes(*cfg["vocab"]), cfg["g1"], cfg["g2"],
+                                                 cfg["gf"], cfg["eps"], cfg["h0"],
+                                                 threads=min(16, os.cpu_count() or 1))
+    for name, hh, ll in (("graph of launches", h, logits), ("one launch", hp, lp)):
+        e_h = rel_l2(hh.cpu().numpy(), h_ref)
+        e_l = rel_l2(ll.cpu().numpy(), lg_ref)
+        print("  %s: rel-L2 h %.2e logits %.2e" % (name, e_h, e_l), flush=True)
+        assert e_h <= 1e-4 and e_l <= 1e-4, name

@@ -392,6 +392,26 @@ def test_decode_chain_is_the_composition_of_the_pinned_steps():
     assert np.array_equal(logits, oracle.gemv(vocab, oracle.rmsnorm(hh, gf, 1e-6))[0])
 
 
+def test_row_parallel_chain_equals_the_serial_chain_bit_for_bit():
+    """decode_token_parallel (each product's rows split over threads, used for
+    the full-size 36-layer token) is decode_token's result exactly."""
+    layers, vocab, g1, g2, gf, h0 = _tiny_model(L=3)
+    h, logits = oracle.decode_token(layers, vocab, g1, g2, gf, 1e-6, h0)
+    for threads in (1, 3, 8):
+        hp, lp = oracle.decode_token_parallel(layers, vocab, g1, g2, gf, 1e-6, h0, threads=threads)
+        assert np.array_equal(hp, h) and np.array_equal(lp, logits)
+
+
+def test_row_parallel_accumulate_equals_gemv():
+    import workloads
+    rng = np.random.default_rng(5)
+    for fmt, N, K in ((1, 300, 512), (2, 77, 512), (3, 50, 256), (0, 33, 64)):
+        W = oracle.Planes(fmt, N, K, workloads.weight_planes(rng, fmt, N, K))
+        x = rng.normal(size=K).astype(np.float32)
+        y0 = rng.normal(size=N).astype(np.float32)
+        assert np.array_equal(oracle.gemv_parallel(W, x, 5, y0=y0), oracle.gemv(W, x, y0=y0))
+
+
 def test_norms_per_token_match_page():
     """Two norms per layer plus one at the end: 73 for 36 layers
     ([one-serial-kernel] "One thread")."""
