@@ -584,10 +584,10 @@ def ceilings(mbq, torch, dev, stream, full=True):
     if full:
         chase = buf[:half]
         n = mbq.probe_chase_init(chase, stream)
-        isink = torch.empty(4, dtype=torch.int32, device=dev)
+        isink = torch.zeros(4, dtype=torch.int32, device=dev)
         hops = 20000
-        mbq.probe_chase(chase, 1000, isink, stream)
-        t = best_of(lambda: mbq.probe_chase(chase, hops, isink, stream), 3)
+        mbq.probe_chase(chase, n, 1000, isink, stream)
+        t = best_of(lambda: mbq.probe_chase(chase, n, hops, isink, stream), 3)
         lat_ns = t / hops * 1e9
         cus = torch.cuda.get_device_properties(dev).multi_processor_count
         out["latency"] = {"ns_per_hop": round(lat_ns, 1), "entries": n, "span_bytes": half,
@@ -597,6 +597,7 @@ def ceilings(mbq, torch, dev, stream, full=True):
         psink = torch.empty(2048, device=dev)
         rates = {}
         for kind, name, iters in ((mbq.PEAK_MFMA_F16, "mfma_f16_tflops", 4000),
+                                  (mbq.PEAK_MFMA_F16_32, "mfma_f16_32x32_tflops", 2000),
                                   (mbq.PEAK_FMA_F32, "fma_f32_tflops", 20000),
                                   (mbq.PEAK_DOT4_I8, "dot4_i8_tops", 20000)):
             ops = mbq.probe_peak(kind, iters, psink, stream)
@@ -723,9 +724,10 @@ def main():
     wins = {"step": [], "up": [], "down": []}
     orders = (("step", "up", "down"), ("down", "up", "step"), ("up", "step", "down"))
     graphs = {"step": g_all, "up": g_up, "down": g_dn}
+    for k in ("step", "up", "down"):
+        graphs[k].replay()
     for order in orders:
         for k in order:
-            graphs[k].replay()
             wins[k].append(timed(graphs[k], 1, stream) / nl)
     med = {k: float(np.median(v)) for k, v in wins.items()}
     spread = {k: (max(v) - min(v)) / med[k] for k, v in wins.items()}

@@ -134,12 +134,11 @@ int mbq_unpack(int fmt, int64_t N, int64_t K, const void* const planes[4],
  * is unspecified.  Tokens run on the vector units, up to 8 per launch (as many
  * as fit staged in LDS: all 8 for K = 4096, 2 for K = 12288), each weight
  * read once per launch and unpacked once for all its tokens.  Q45 batches of
- * 6 or more tokens with K % 1024 == 0 (and 8-byte aligned scales) run on the
- * matrix cores instead, 16 tokens per launch, with x split into fp16 high
- * and low parts under a power of two per 32-weight block and token (the
- * relative precision of the vector units' staged x).  Through mbq_stage_x +
- * mbq_gemv_xq the matrix cores take Q45 batches from 16 tokens, and from 6
- * when K % 1024 == 0, up to 64 per launch.
+ * 6 or more tokens with K % 128 == 0 (and 8-byte aligned scales) run on the
+ * matrix cores instead, all tokens in one launch, with x split into fp16
+ * high and low parts under a power of two per 32-weight block and token (the
+ * relative precision of the vector units' staged x); the same holds through
+ * mbq_stage_x + mbq_gemv_xq.
  * MBQ_EUNSUPPORTED for shapes without a kernel (K > 32768, or K > 16384 for
  * BF16; Q25 with K % 64 != 0; BF16 with K % 8 != 0).  M == 0 or N == 0
  * enqueue nothing; K == 0 writes zeros (or leaves y for accumulate = 1). */
@@ -279,17 +278,15 @@ int mbq_decode_step_persistent(const mbq_decode_model* model, float* h, float* l
  * the sums busy").  The form is opaque and format-specific: stage for the
  * format of the matrix that consumes it.  It takes 4 bytes per value
  * (mbq_xq_bytes), rows back to back; for BF16 it is x itself in fp32.
- * For Q45 with M >= 16 tokens, or 6 <= M < 16 and K % 1024 == 0, it is the
- * matrix-core tile form instead (one 16-token tile outruns the vector units
- * from about 6 tokens on MI355X): per
- * tile of 16 tokens and block of 32 values, each token scaled by a power of
- * two (its largest |x| in [2^14, 2^15)) and split into fp16 high and low
- * parts in the MFMA operand order, then one float 2^-e per token slot
- * (mbq_xq_bytes gives its size; it needs K % 1024 == 0).
+ * For Q45 with M >= 6 tokens and K % 128 == 0 it is the matrix-core tile
+ * form instead: per tile of 16 tokens and block of 32 values, each token's
+ * block scaled by a power of two (its largest |x| in [2^14, 2^15)) and split
+ * into fp16 high and low parts in the MFMA operand order, then the blocks'
+ * exponents as bytes (mbq_xq_bytes gives its size).
  */
 
 /* Bytes of staged x for M rows of K values: 4*M*K, or for the Q45 tile form
- * (M >= 16, or 6 <= M < 16 with K % 1024 == 0) ceil(M/16) * (K/32 * 2048 + 64).
+ * (M >= 6, K % 128 == 0) ceil(M/16) * (K/32 * 2048 + K/128 * 64).
  * Host only.  MBQ_EINVAL for an unknown
  * format or K not a multiple of the chunk (32; Q25 64; BF16 8). */
 int mbq_xq_bytes(int fmt, int64_t M, int64_t K, size_t* bytes);
@@ -305,8 +302,8 @@ int mbq_stage_x(int fmt, const float* x, int64_t M, int64_t ldx, int64_t K, void
  * for bit mbq_gemv_q's on the same x.  Q45 in the tile form runs on
  * the matrix cores ([roofline-holds] "The Math": past M* the sums, not the
  * bytes, bound the product): fp16 (q - 8) codes, which are exact, against
- * the fp16 high and low parts of x, fp32 results, each block's scale applied
- * to its fp32 block sum; it needs K % 1024 == 0 and 8-byte aligned scales.
+ * the fp16 high and low parts of x, fp32 results, each block's scale and
+ * 2^-e applied to its fp32 block sum; it needs 8-byte aligned scales.
  * xq: device, 16-byte aligned, must not overlap y. */
 int mbq_gemv_xq(const mbq_qweight* W, const void* xq, int64_t M, float* y, int64_t ldy,
                 int accumulate, void* stream);
@@ -367,24 +364,29 @@ int mbq_probe_copy(void* dst, const void* src, size_t bytes, void* stream);
  * the largest power of two <= bytes / 256 entries into buf (device, 4-byte
  * aligned, >= 256 bytes), one entry per 256 bytes, visiting every entry once
  * per cycle in a scattered order.  mbq_probe_chase follows `hops` >= 1 hops
- * of it with one lane (each hop one full memory round trip) and writes the
- * last entry reached to sink (device uint32).  Time it with events:
- * latency = time / hops.  MBQ_EINVAL for bytes < 256 or hops < 1. */
+ * of a chain of `entries` entries (the value the init call returned) with one
+ * lane, each hop one full memory round trip, starting at the entry *sink
+ * holds (device uint32, reduced modulo entries) and leaving the entry it
+ * reached in *sink, so consecutive calls walk on into entries no cache holds.
+ * Time it with events: latency = time / hops.  MBQ_EINVAL for bytes < 256,
+ * hops < 1 or entries not a power of two. */
 int mbq_probe_chase_init(void* buf, size_t bytes, uint32_t* entries, void* stream);
-int mbq_probe_chase(const void* buf, int64_t hops, uint32_t* sink, void* stream);
+int mbq_probe_chase(const void* buf, uint32_t entries, int64_t hops, uint32_t* sink, void* stream);
 
 /* Issue-rate loops for the arithmetic ceilings ([roofline-holds] "The
  * Math": M* = (w/16)(R/BW) needs the measured rate R; "How I ran it": peak
- * loops with no memory traffic).  kind MBQ_PEAK_MFMA_F16: fp16 matrix
- * instructions (16x16x32, fp32 accumulate); MBQ_PEAK_FMA_F32: fp32 fused
+ * loops with no memory traffic).  kind MBQ_PEAK_MFMA_F16 and
+ * MBQ_PEAK_MFMA_F16_32: fp16 matrix instructions (16x16x32 and 32x32x16,
+ * fp32 accumulate); MBQ_PEAK_FMA_F32: fp32 fused
  * multiply-add on the vector units (the packed two-wide form is not used in
  * this library's code); MBQ_PEAK_DOT4_I8: the 4-way byte dot product the
  * quantized vector kernels use.  Each launch runs `iters` >= 1 rounds on
  * every wave; *ops (host) receives the operations executed (flops: two per
  * multiply-add).  sink: device fp32, >= 2048 floats. */
-#define MBQ_PEAK_MFMA_F16 0
+#define MBQ_PEAK_MFMA_F16 0      /* 16x16x32 instructions */
 #define MBQ_PEAK_FMA_F32  1
 #define MBQ_PEAK_DOT4_I8  2
+#define MBQ_PEAK_MFMA_F16_32 3   /* 32x32x16 instructions */
 int mbq_probe_peak(int kind, int64_t iters, float* sink, int64_t* ops, void* stream);
 
 /* Static text for a status code, and the calling thread's last error detail

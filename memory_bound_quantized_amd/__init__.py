@@ -272,12 +272,13 @@ def probe_chase_init(buf, stream=None) -> int:
     return int(n.value)
 
 
-def probe_chase(buf, hops: int, sink, stream=None):
-    """Follow `hops` hops of the chain in buf; the last entry goes to sink."""
-    check(lib.mbq_probe_chase(_ptr(buf), int(hops), _ptr(sink), _stream(stream)))
+def probe_chase(buf, entries: int, hops: int, sink, stream=None):
+    """Follow `hops` hops of the chain of `entries` entries in buf, from the
+    entry sink holds; the entry reached goes back to sink."""
+    check(lib.mbq_probe_chase(_ptr(buf), int(entries), int(hops), _ptr(sink), _stream(stream)))
 
 
-PEAK_MFMA_F16, PEAK_FMA_F32, PEAK_DOT4_I8 = 0, 1, 2
+PEAK_MFMA_F16, PEAK_FMA_F32, PEAK_DOT4_I8, PEAK_MFMA_F16_32 = 0, 1, 2, 3
 
 
 def probe_peak(kind: int, iters: int, sink, stream=None) -> int:

@@ -98,7 +98,7 @@ def _load():
         "mbq_probe_read": (i32, [vp, sz, vp, vp]),
         "mbq_probe_copy": (i32, [vp, vp, sz, vp]),
         "mbq_probe_chase_init": (i32, [vp, sz, ctypes.POINTER(ctypes.c_uint32), vp]),
-        "mbq_probe_chase": (i32, [vp, i64, vp, vp]),
+        "mbq_probe_chase": (i32, [vp, ctypes.c_uint32, i64, vp, vp]),
         "mbq_probe_peak": (i32, [i32, i64, vp, ctypes.POINTER(ctypes.c_int64), vp]),
         "mbq_status_str": (ctypes.c_char_p, [i32]),
         "mbq_last_error": (ctypes.c_char_p, []),

@@ -102,14 +102,16 @@ int check_kernel_shape(const mbq_qweight* W, const char* fn) {
     return MBQ_OK;
 }
 
-// Staged x of M >= 16 Q45 tokens takes the matrix-core tile form.
-// Staged x takes the matrix-core tile form for Q45 batches from 16 tokens,
-// and from 6 tokens where the matrix-core kernel takes the shape (K % 1024
-// == 0): on MI355X one 16-token tile (19.7 us on 12288 x 4096) beats the
-// vector units from about 6 tokens (M = 6: 22 us, M = 8: 29 us).
-bool xq_tiled(int fmt, int64_t M, int64_t K) {
-    return fmt == MBQ_FMT_Q45 && (M >= 16 || (M >= 6 && K % 1024 == 0));
+// Q45 batches of kMfmaMinM or more tokens run on the matrix cores (staged x
+// then takes the tile form), for K % 128 == 0.  The vector units' digit
+// arithmetic has M* = (w/16)(R/BW) of about one token on MI355X (measured
+// R and BW), the matrix cores' about twelve, so from a few tokens on the
+// matrix cores carry the sums at the weight-read rate.
+constexpr int64_t kMfmaMinM = 6;
+bool mfma_shape(int fmt, int64_t M, int64_t K) {
+    return fmt == MBQ_FMT_Q45 && M >= kMfmaMinM && K % 128 == 0;
 }
+bool xq_tiled(int fmt, int64_t M, int64_t K) { return mfma_shape(fmt, M, K); }
 
 // Values per chunk of staged x (the unit of its fixed-point exponent).
 int64_t xq_chunk(int fmt) {
@@ -322,9 +324,9 @@ int mbq_gemv_q(const mbq_qweight* W, const float* x, int64_t M, int64_t ldx, flo
         return hip_status(mbq::launch_gemv_m1(W->fmt, P, W->N, W->K, x, false, y, accumulate,
                                               nullptr, 1, g, s), fn);
     }
-    // Q45 batches of 6+ tokens with K % 1024 == 0: the matrix cores, fp32 x
-    // converted inside the product (passes of 16 tokens)
-    if (W->fmt == MBQ_FMT_Q45 && M >= 6 && W->K % 1024 == 0 && aligned(W->scales, 8))
+    // Q45 batches on the matrix cores, fp32 x converted as each chunk of it
+    // enters LDS
+    if (mfma_shape(W->fmt, M, W->K) && aligned(W->scales, 8))
         return hip_status(mbq::launch_gemv_mfma_q45_f32x(P, W->N, W->K, x, ldx, M, y, ldy,
                                                          accumulate, s), fn);
     // 2 <= M: passes of up to 8 tokens on the vector units, as many as the
@@ -651,10 +653,8 @@ int mbq_stage_x(int fmt, const float* x, int64_t M, int64_t ldx, int64_t K, void
         return fail(MBQ_EALIGN, "%s: x and xq must be 16-byte aligned with ldx %% 4 == 0", fn);
     if (overlaps(x, (size_t)((M - 1) * ldx + K) * 4, xq, xqb))
         return fail(MBQ_EINVAL, "%s: x and xq overlap", fn);
-    if (xq_tiled(fmt, M, K)) {
-        if (K % 1024) return fail(MBQ_EUNSUPPORTED, "%s: the tile form needs K %% 1024 == 0", fn);
+    if (xq_tiled(fmt, M, K))
         return hip_status(mbq::launch_stage_x_mfma(x, M, ldx, K, xq, (hipStream_t)stream), fn);
-    }
     return hip_status(mbq::launch_stage_x(fmt, x, M, ldx, K, xq, (hipStream_t)stream), fn);
 }
 
@@ -688,7 +688,6 @@ int mbq_gemv_xq(const mbq_qweight* W, const void* xq, int64_t M, float* y, int64
                                               nullptr, 1, g, s), fn);
     }
     if (xq_tiled(W->fmt, M, W->K)) {
-        if (W->K % 1024) return fail(MBQ_EUNSUPPORTED, "%s: the matrix-core kernel needs K %% 1024 == 0", fn);
         if (!aligned(W->scales, 8)) return fail(MBQ_EALIGN, "%s: the matrix-core kernel needs 8-byte aligned scales", fn);
         return hip_status(mbq::launch_gemv_mfma_q45(P, W->N, W->K, xq, M, y, ldy, accumulate, s), fn);
     }
@@ -847,17 +846,18 @@ int mbq_probe_chase_init(void* buf, size_t bytes, uint32_t* entries, void* strea
     return hip_status(mbq::launch_chase_init(buf, bytes, (hipStream_t)stream), fn);
 }
 
-int mbq_probe_chase(const void* buf, int64_t hops, uint32_t* sink, void* stream) {
+int mbq_probe_chase(const void* buf, uint32_t entries, int64_t hops, uint32_t* sink, void* stream) {
     const char* fn = "mbq_probe_chase";
     if (!buf || !sink) return fail(MBQ_EINVAL, "%s: NULL pointer", fn);
     if (hops < 1) return fail(MBQ_EINVAL, "%s: hops < 1", fn);
+    if (entries == 0 || (entries & (entries - 1))) return fail(MBQ_EINVAL, "%s: entries must be a power of two", fn);
     if (!aligned(buf, 4) || !aligned(sink, 4)) return fail(MBQ_EALIGN, "%s: misaligned", fn);
-    return hip_status(mbq::launch_chase(buf, hops, sink, (hipStream_t)stream), fn);
+    return hip_status(mbq::launch_chase(buf, entries, hops, sink, (hipStream_t)stream), fn);
 }
 
 int mbq_probe_peak(int kind, int64_t iters, float* sink, int64_t* ops, void* stream) {
     const char* fn = "mbq_probe_peak";
-    if (kind < MBQ_PEAK_MFMA_F16 || kind > MBQ_PEAK_DOT4_I8) return fail(MBQ_EINVAL, "%s: unknown kind %d", fn, kind);
+    if (kind < MBQ_PEAK_MFMA_F16 || kind > MBQ_PEAK_MFMA_F16_32) return fail(MBQ_EINVAL, "%s: unknown kind %d", fn, kind);
     if (iters < 1 || !sink || !ops) return fail(MBQ_EINVAL, "%s: iters < 1 or NULL pointer", fn);
     if (!aligned(sink, 4)) return fail(MBQ_EALIGN, "%s: sink must be 4-byte aligned", fn);
     *ops = mbq::peak_ops(kind, iters);

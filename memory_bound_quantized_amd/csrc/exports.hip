@@ -177,8 +177,12 @@ __global__ __launch_bounds__(kBlock) void chase_init_kernel(uint32_t* __restrict
         buf[(size_t)i * kChaseStride] = (kChaseA * i + kChaseC) & mask;
 }
 
-__global__ void chase_kernel(const uint32_t* __restrict__ buf, int64_t hops, uint32_t* sink) {
-    uint32_t i = 0;
+// The chase starts at the entry sink holds (masked into the chain) and leaves
+// the entry it reached there, so consecutive launches walk on through the
+// cycle instead of revisiting entries a previous launch left in the caches.
+__global__ void chase_kernel(const uint32_t* __restrict__ buf, uint32_t n, int64_t hops,
+                             uint32_t* sink) {
+    uint32_t i = sink[0] & (n - 1);
     for (int64_t h = 0; h < hops; h++) i = __builtin_nontemporal_load(buf + (size_t)i * kChaseStride);
     sink[0] = i;
 }
@@ -197,8 +201,9 @@ hipError_t launch_chase_init(void* buf, size_t bytes, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_chase(const void* buf, int64_t hops, uint32_t* sink, hipStream_t stream) {
-    hipLaunchKernelGGL(chase_kernel, dim3(1), dim3(1), 0, stream, (const uint32_t*)buf, hops, sink);
+hipError_t launch_chase(const void* buf, uint32_t n, int64_t hops, uint32_t* sink,
+                        hipStream_t stream) {
+    hipLaunchKernelGGL(chase_kernel, dim3(1), dim3(1), 0, stream, (const uint32_t*)buf, n, hops, sink);
     return hipGetLastError();
 }
 
@@ -210,24 +215,52 @@ constexpr int kPeakBlocks = 2048;   // 8 per compute unit: 8 waves per SIMD
 typedef _Float16 ph8 __attribute__((ext_vector_type(8)));
 typedef float pf4 __attribute__((ext_vector_type(4)));
 
+// Each chain has its own B operand, so the compiler cannot fold chains
+// together or carry one chain's result into another.
+template <bool BIG>
 __global__ __launch_bounds__(kBlock) void peak_mfma_kernel(int64_t iters, float* sink) {
     const float t = (float)threadIdx.x * 1e-3f;
-    ph8 a, b;
+    ph8 a, b[kChains];
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-        a[i] = (_Float16)(t + i);
-        b[i] = (_Float16)(1.0f - t * i);
-    }
-    pf4 acc[kChains];
+    for (int i = 0; i < 8; i++) a[i] = (_Float16)(t + i);
 #pragma unroll
-    for (int c = 0; c < kChains; c++) acc[c] = pf4{0.f, 0.f, 0.f, (float)c};
-    for (int64_t r = 0; r < iters; r++) {
+    for (int c = 0; c < kChains; c++)
 #pragma unroll
-        for (int c = 0; c < kChains; c++) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[c], 0, 0, 0);
-    }
+        for (int i = 0; i < 8; i++) b[c][i] = (_Float16)(1.0f - t * (i + c));
+    typedef float pf16 __attribute__((ext_vector_type(16)));
     float s = 0.f;
+    if constexpr (BIG) {
+        pf16 acc[kChains];
 #pragma unroll
-    for (int c = 0; c < kChains; c++) s += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
+        for (int c = 0; c < kChains; c++)
+#pragma unroll
+            for (int i = 0; i < 16; i++) acc[c][i] = (float)c;
+        for (int64_t r = 0; r < iters; r++) {
+#pragma unroll
+            for (int c = 0; c < kChains; c++) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b[c], acc[c], 0, 0, 0);
+        }
+#pragma unroll
+        for (int c = 0; c < kChains; c++)
+#pragma unroll
+            for (int i = 0; i < 16; i++) s += acc[c][i];
+    } else {
+        // the product kernels' pattern: a pair of instructions from a zero
+        // accumulator (the second in place), then a vector add
+        pf4 acc[kChains];
+        const pf4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < kChains; c++) acc[c] = pf4{0.f, 0.f, 0.f, (float)c};
+        for (int64_t r = 0; r < iters; r += 2) {
+#pragma unroll
+            for (int c = 0; c < kChains; c++) {
+                pf4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[c], z, 0, 0, 0);
+                d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[(c + 1) % kChains], d, 0, 0, 0);
+                acc[c] += d;
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < kChains; c++) s += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
+    }
     s = wave_sum(s);
     __shared__ float red[kWavesPerBlock];
     if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = s;
@@ -275,17 +308,21 @@ __global__ __launch_bounds__(kBlock) void peak_dot4_kernel(int64_t iters, float*
     if (threadIdx.x == 0) sink[blockIdx.x] = red[0] + red[1] + red[2] + red[3];
 }
 
-// kind 0: fp16 matrix instructions (16x16x32, 2 * 16 * 16 * 32 flops each);
-// 1: fp32 FMA (2 flops per lane); 2: int8 dot4 (8 ops per lane).
+// kind 0: fp16 matrix instructions 16x16x32 (2 * 16 * 16 * 32 flops each);
+// 1: fp32 FMA (2 flops per lane); 2: int8 dot4 (8 ops per lane); 3: fp16
+// matrix instructions 32x32x16 (2 * 32 * 32 * 16 flops each).
 int64_t peak_ops(int kind, int64_t iters) {
     const int64_t waves = (int64_t)kPeakBlocks * kWavesPerBlock;
-    const int64_t per = kind == 0 ? 2 * 16 * 16 * 32 : (kind == 1 ? 2 * kWave : 8 * kWave);
+    if (kind == 0) iters = (iters + 1) / 2 * 2;    // rounds run in pairs
+    const int64_t per = kind == 0 || kind == 3 ? 2 * 16 * 16 * 32 * (kind == 3 ? 2 : 1)
+                                               : (kind == 1 ? 2 * kWave : 8 * kWave);
     return waves * iters * kChains * per;
 }
 
 hipError_t launch_peak(int kind, int64_t iters, float* sink, hipStream_t stream) {
     switch (kind) {
-    case 0: hipLaunchKernelGGL(peak_mfma_kernel, dim3(kPeakBlocks), dim3(kBlock), 0, stream, iters, sink); break;
+    case 0: hipLaunchKernelGGL(peak_mfma_kernel<false>, dim3(kPeakBlocks), dim3(kBlock), 0, stream, iters, sink); break;
+    case 3: hipLaunchKernelGGL(peak_mfma_kernel<true>, dim3(kPeakBlocks), dim3(kBlock), 0, stream, iters, sink); break;
     case 1: hipLaunchKernelGGL(peak_fma_kernel, dim3(kPeakBlocks), dim3(kBlock), 0, stream, iters, sink); break;
     default: hipLaunchKernelGGL(peak_dot4_kernel, dim3(kPeakBlocks), dim3(kBlock), 0, stream, iters, sink); break;
     }

@@ -171,6 +171,10 @@ struct Traits<kQ45> {
         for (int j = 0; j < NVEC; j++) acc_vec(s, v[j], xv + 3 * j);
         return (h2f(r.s) * as_f(xv[META])) * acc_value(s);
     }
+    // Lanes past the row: 2^-e to 0, so they add exactly 0.
+    __device__ static __forceinline__ void mask_meta(uint32_t* xv, bool ok) {
+        xv[META] = ok ? xv[META] : 0u;
+    }
     __device__ static __forceinline__ float dot(const Row& r, const uint32_t* xv) {
         uint32_t v[NVEC];
         unpack(r, v);
@@ -268,6 +272,10 @@ struct Traits<kQ65> {
         }
         return (h2f(r.d) * as_f(xv[META])) * fmaf(sc_f(r.sc, 1), t[1], sc_f(r.sc, 0) * t[0]);
     }
+    // Lanes past the row: 2^-e to 0, so they add exactly 0.
+    __device__ static __forceinline__ void mask_meta(uint32_t* xv, bool ok) {
+        xv[META] = ok ? xv[META] : 0u;
+    }
     __device__ static __forceinline__ float dot(const Row& r, const uint32_t* xv) {
         uint32_t v[NVEC];
         unpack(r, v);
@@ -302,7 +310,9 @@ struct Traits<kQ65> {
 // codes dword: weights 0-15, byte j holds 4j..4j+3 in bits 0-1, 2-3, 4-5, 6-7;
 // code vector m (m = 0..3) = (d >> 2m) & 0x03030303 holds weights
 // (m, 4+m, 8+m, 12+m).  Chunk x layout: 4 dwords x 4 vectors x 3 digits = 48
-// dwords, meta [48] = 2^-e, [49..51] offset terms of block 0, [52..54] block 1.
+// dwords, meta [48] = 2^-e of block 0, [49..51] offset terms of block 0,
+// [52..54] those of block 1, [55] = 2^-e of block 1 (each block of 32 values
+// keeps 22 bits relative to its own largest |x|).
 template <>
 struct Traits<kQ25> {
     static constexpr int WPC = 64;
@@ -350,7 +360,12 @@ struct Traits<kQ25> {
             for (int j = 0; j < 8; j++) acc_vec(s, v[8 * blk + j], xv + 24 * blk + 3 * j);
             t[blk] = acc_value(s);
         }
-        return as_f(xv[META]) * fmaf(h2f(r.s2 >> 16), t[1], h2f(r.s2) * t[0]);
+        return fmaf(h2f(r.s2 >> 16) * as_f(xv[META + 7]), t[1], (h2f(r.s2) * as_f(xv[META])) * t[0]);
+    }
+    // Lanes past the row: both blocks' 2^-e to 0, so they add exactly 0.
+    __device__ static __forceinline__ void mask_meta(uint32_t* xv, bool ok) {
+        xv[META] = ok ? xv[META] : 0u;
+        xv[META + 7] = ok ? xv[META + 7] : 0u;
     }
     __device__ static __forceinline__ float dot(const Row& r, const uint32_t* xv) {
         uint32_t v[NVEC];

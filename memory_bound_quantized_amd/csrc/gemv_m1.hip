@@ -154,7 +154,7 @@ __global__ __launch_bounds__(kBlock * k_slices(CS)) void gemv_m1_kernel(DevPlane
         uint32_t xv[4 * T::F4];
         read_x<FMT>(xs, ok ? b : 0, xv);
         if constexpr (T::INT) {
-            xv[T::META] = ok ? xv[T::META] : 0u;    // lanes past the row add exactly 0
+            T::mask_meta(xv, ok);    // lanes past the row add exactly 0
 #pragma unroll
             for (int r = 0; r < R; r++) acc[r] += T::dot(sl.row[r], xv);
         } else {

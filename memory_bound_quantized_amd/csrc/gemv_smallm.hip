@@ -156,7 +156,7 @@ __global__ __launch_bounds__(kSmBlock) void gemv_smallm_kernel(DevPlanes P, int6
             uint32_t xv[4 * T::F4];
             read_x<FMT>(xs + m * xs_row, bi, xv);
             if constexpr (T::INT) {
-                xv[T::META] = ok ? xv[T::META] : 0u;
+                T::mask_meta(xv, ok);
 #pragma unroll
                 for (int r = 0; r < R; r++) acc[r][m] += T::dot_vec(sl.row[r], v[r], xv);
             } else {

@@ -187,7 +187,8 @@ hipError_t launch_probe_copy(void* dst, const void* src, size_t bytes, hipStream
 // 256 bytes (a power of two; 0 if bytes < 256).
 uint32_t chase_entries(size_t bytes);
 hipError_t launch_chase_init(void* buf, size_t bytes, hipStream_t stream);
-hipError_t launch_chase(const void* buf, int64_t hops, uint32_t* sink, hipStream_t stream);
+hipError_t launch_chase(const void* buf, uint32_t n, int64_t hops, uint32_t* sink,
+                        hipStream_t stream);
 // Issue-rate loops (kind 0 fp16 matrix, 1 fp32 FMA, 2 int8 dot4); sink holds
 // kPeakSinkFloats floats; peak_ops gives the operations one launch executes.
 constexpr int kPeakSinkFloats = 2048;

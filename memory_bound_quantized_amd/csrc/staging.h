@@ -1,12 +1,14 @@
 // staging.h -- x in the form the quantized dot products consume ("staged x").
 //
 // For the quantized formats x is held per chunk (32 values, 64 for Q25) as
-// 24-bit fixed point: n = rint(x * 2^e), e chosen per chunk so that the
-// chunk's largest |x| maps into [2^21, 2^22), and n is split into the bytes
+// 24-bit fixed point: n = rint(x * 2^e), e chosen per 32-value block (one
+// per chunk, two per Q25 chunk) so that the block's largest |x| maps into
+// [2^21, 2^22), and n is split into the bytes
 // b0, b1 (unsigned) and b2 (signed) of its two's complement.  The bytes are
 // laid out as "digit words" in the order of the format's code vectors
 // (formats.h), followed by the chunk's metadata: 2^-e and the offset terms
-// -offset * (sum of each digit over an offset block).  BF16 keeps x as fp32.
+// -offset * (sum of each digit over an offset block); a Q25 chunk's second
+// block keeps its own 2^-e in metadata dword 7.  BF16 keeps x as fp32.
 //
 // A chunk takes Traits::F4 16-byte slots: 4 bytes per value for every format
 // (Q45/Q65: 24 digit dwords + 7 metadata dwords + 1 pad per 32 values; Q25:
@@ -93,12 +95,16 @@ __device__ __forceinline__ void stage_group(const float* v, int og, bool ok, con
                                __builtin_bit_cast(uint32_t, v[j + 2]), __builtin_bit_cast(uint32_t, v[j + 3]));
         }
     } else {
+        // one exponent per 32-value block: the chunk's four groups (Q45,
+        // Q65: one block), or each pair of groups (Q25: two blocks of 32)
+        constexpr bool TWO = T::BLK == 32 && T::WPC == 64;
         float amax = 0.f;
 #pragma unroll
         for (int k = 0; k < GX; k++) amax = fmaxf(amax, fabsf(v[k]));
         amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
-        amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
+        if constexpr (!TWO) amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
         const int e = chunk_exp(amax);
+        const int e_hi = TWO ? __shfl_xor(e, 2, kWave) : e;   // the second block's, in groups 0, 1
         const float up = pow2f(e);
         int32_t n[GX];
 #pragma unroll
@@ -137,6 +143,7 @@ __device__ __forceinline__ void stage_group(const float* v, int og, bool ok, con
 #pragma unroll
                 for (int t = 0; t < MD; t++) m[t] = 0u;
                 m[0] = __builtin_bit_cast(uint32_t, pow2f(-e));
+                if constexpr (TWO) m[7] = __builtin_bit_cast(uint32_t, pow2f(-e_hi));
                 if constexpr (T::BLK == 32 && T::WPC == 32) {   // one offset block per chunk
 #pragma unroll
                     for (int p = 0; p < 3; p++) m[1 + p] = (uint32_t)(-T::OFF * (B01[p] + B23[p]));

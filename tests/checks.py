@@ -15,7 +15,7 @@ def rel_l2(got, ref):
     return np.linalg.norm(got - ref) / (den if den > 0 else 1.0)
 
 
-X_CHUNK = {0: None, 1: 32, 2: 32, 3: 64}   # values per x rounding chunk, by format
+X_CHUNK = {0: None, 1: 32, 2: 32, 3: 32}   # values per x rounding block, by format
 
 
 def check_gemv(y, ow, x, ref, y0=None, slack=None):
@@ -23,8 +23,8 @@ def check_gemv(y, ow, x, ref, y0=None, slack=None):
     (1) every element lies within the forward-error bound of the kernel's
         arithmetic for any summation order: fp32 sums,
         (K + 4) 2^-24 sum_k |w_k x_k| (+ |y0|), plus, for the quantized formats,
-        x rounded to 22 bits relative to the largest |x| of its chunk
-        (32 values, 64 for Q25): 2^-22 sum_k |w_k| max_chunk(k) |x|;
+        x rounded to 22 bits relative to the largest |x| of its block of 32
+        values: 2^-22 sum_k |w_k| max_block(k) |x|;
     (2) the relative L2 error over the output vector is <= 1e-4 whenever the
         vector has at least 16 entries.  A single output can be arbitrarily
         ill-conditioned (its value near zero against large terms), so no fp32

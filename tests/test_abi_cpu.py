@@ -184,11 +184,14 @@ def test_staged_x_argument_checks():
     assert L.mbq_xq_bytes(3, 1, 96, ctypes.byref(sz)) == _lib.EINVAL       # Q25 chunk is 64
     assert L.mbq_xq_bytes(1, 1, 48, ctypes.byref(sz)) == _lib.EINVAL
     assert L.mbq_xq_bytes(9, 1, 64, ctypes.byref(sz)) == _lib.EINVAL
-    # Q45 with 16 or more tokens: the matrix-core tile form (2 KB per 16 tokens
-    # and 32 values, plus one float per token slot)
-    assert L.mbq_xq_bytes(1, 17, 4096, ctypes.byref(sz)) == _lib.OK and sz.value == 2 * (128 * 2048 + 64)
-    # Q45 tile form from 6 tokens when K % 1024 == 0; the row form otherwise
-    assert L.mbq_xq_bytes(1, 6, 4096, ctypes.byref(sz)) == _lib.OK and sz.value == 128 * 2048 + 64
+    # Q45 with 6 or more tokens and K % 128 == 0: the matrix-core tile form
+    # (2 KB per 16 tokens and 32 values, plus 64 exponent bytes per 16 tokens
+    # and 128 values); the row form otherwise
+    tile = lambda K: K // 32 * 2048 + K // 128 * 64
+    assert L.mbq_xq_bytes(1, 17, 4096, ctypes.byref(sz)) == _lib.OK and sz.value == 2 * tile(4096)
+    assert L.mbq_xq_bytes(1, 6, 4096, ctypes.byref(sz)) == _lib.OK and sz.value == tile(4096)
+    assert L.mbq_xq_bytes(1, 6, 640, ctypes.byref(sz)) == _lib.OK and sz.value == tile(640)
+    assert L.mbq_xq_bytes(1, 512, 4096, ctypes.byref(sz)) == _lib.OK and sz.value == 32 * tile(4096)
     assert L.mbq_xq_bytes(1, 5, 4096, ctypes.byref(sz)) == _lib.OK and sz.value == 5 * 4096 * 4
     assert L.mbq_xq_bytes(1, 8, 2080, ctypes.byref(sz)) == _lib.OK and sz.value == 8 * 2080 * 4
     assert L.mbq_xq_bytes(2, 17, 4096, ctypes.byref(sz)) == _lib.OK and sz.value == 17 * 4096 * 4
@@ -202,7 +205,8 @@ def test_staged_x_argument_checks():
     assert st(xq=xq + 8) == _lib.EALIGN
     assert st(xq=x + 4096) == _lib.EINVAL                                   # overlap
     assert st(K=65536, ldx=65536) == _lib.EUNSUPPORTED
-    assert st(M=16, K=2080, ldx=2080) == _lib.EUNSUPPORTED                  # tile form needs K % 1024
+    # K % 128 != 0: 16 tokens take the row form (4 bytes per value), not the tile form
+    assert L.mbq_xq_bytes(1, 16, 2080, ctypes.byref(sz)) == _lib.OK and sz.value == 16 * 2080 * 4
     gx = lambda d, xq=xq, M=1, y=BASE + 0x800000, acc=0: \
         L.mbq_gemv_xq(ctypes.byref(d), xq, M, y, d.N, acc, None)
     assert gx(_desc(), xq=None) == _lib.EINVAL
@@ -211,7 +215,6 @@ def test_staged_x_argument_checks():
     assert gx(_desc(), acc=3) == _lib.EINVAL
     assert gx(_desc(), M=0) == _lib.OK
     assert gx(_desc(fmt=3, K=96)) == _lib.EUNSUPPORTED
-    assert gx(_desc(K=2080), M=16) == _lib.EUNSUPPORTED                     # matrix cores: K % 1024
     d = _desc(K=4096)
     d.scales = BASE + 0x200004
     assert gx(d, M=16) == _lib.EALIGN                                       # 8-byte aligned scales

@@ -4,8 +4,9 @@ Within one output row the sums run in the same order whatever the geometry
 (a lane's chunks in order, one wave reduction per row, or per 4096-wide slice
 for K = 12288, then the final add), so the M = 1 and small-batch kernels must
 give bit-identical outputs for every rows-per-wave / row-group choice.  The
-matrix-core kernel's K parts change the order of the part sums, so its
-variants are held to the oracle's bar instead.  Geometries are chosen
+matrix-core kernel's token-tile count changes how K is split among its
+waves, and so the order of the partial sums, so its variants are held to the
+oracle's bar instead (and staged and fp32 x agree bit for bit in each).  Geometries are chosen
 through the library's tuning variables (read because MBQ_TUNING is set in
 conftest.py before the library loads).
 """
@@ -137,31 +138,42 @@ def test_smallm_every_geometry_bitwise(fmt, M, N, K):
             assert np.array_equal(bits(y), bits(ref)), (R, G)
 
 
-@pytest.mark.parametrize("M,N,K", [(16, 1000, 4096), (20, 1000, 4096), (40, 300, 2048), (64, 130, 1024)])
+MFMA_GEOM_CASES = [(16, 1000, 4096), (20, 1000, 4096), (40, 300, 2048), (64, 130, 1024),
+                   (6, 77, 640), (33, 200, 2176), (17, 50, 128)]
+
+
+@pytest.mark.parametrize("M,N,K", MFMA_GEOM_CASES)
 def test_mfma_every_geometry_matches_oracle(M, N, K):
+    """Staged x on the matrix cores at every row-tile count (1-4 row tiles
+    per workgroup) and token-tile count (1 or 2 per workgroup); K = 640 and
+    2176 leave the last chunk partial and some waves without a quad."""
     print("geometry mfma M=%d N=%d K=%d" % (M, N, K), flush=True)
     ow, dw = weights(1, N, K, 9990 + N)
     X = np.random.default_rng(M + N).normal(size=(M, K)).astype(np.float32)
     Xq = mbq().stage_x(1, dev(X))
     ref = oracle.gemv(ow, X)
-    for tr in (1, 2, 3, 4):
-        for S in (2, 4):
-            with env(MBQ_MFMA_TR=tr, MBQ_MFMA_S=S):
+    for rw in (1, 2, 3, 4):
+        for tt in (1, 2):
+            with env(MBQ_MFMA_RW=rw, MBQ_MFMA_TT=tt):
                 Y = mbq().gemv_xq(dw, Xq, M=M).cpu().numpy()
             check_gemv(Y, ow, X, ref)
 
 
-@pytest.mark.parametrize("M,N,K", [(6, 1000, 4096), (16, 1000, 4096), (23, 300, 2048)])
+@pytest.mark.parametrize("M,N,K", MFMA_GEOM_CASES)
 def test_mfma_f32x_every_geometry_matches_oracle(M, N, K):
-    """fp32 x through mbq_gemv_q on the matrix cores (x converted inside the
-    product, passes of 16 tokens) at every row-tile and K-part choice."""
+    """fp32 x through mbq_gemv_q on the matrix cores (x converted as each
+    chunk enters LDS) at every row-tile and token-tile count; the staged and
+    the fp32 forms give the same bits."""
     print("geometry mfma fp32 x M=%d N=%d K=%d" % (M, N, K), flush=True)
     ow, dw = weights(1, N, K, 9995 + N)
     X = np.random.default_rng(M + N + 1).normal(size=(M, K)).astype(np.float32)
     Xd = dev(X)
     ref = oracle.gemv(ow, X)
-    for tr in (1, 2, 3, 4):
-        for S in (2, 4):
-            with env(MBQ_MFMA_TR=tr, MBQ_MFMA_S=S):
+    Xq = mbq().stage_x(1, Xd)
+    for rw in (1, 2, 3, 4):
+        for tt in (1, 2):
+            with env(MBQ_MFMA_RW=rw, MBQ_MFMA_TT=tt):
                 Y = mbq().gemv_q(dw, Xd).cpu().numpy()
+                Ys = mbq().gemv_xq(dw, Xq, M=M).cpu().numpy()
             check_gemv(Y, ow, X, ref)
+            assert np.array_equal(Y.view(np.uint32), Ys.view(np.uint32)), (rw, tt)

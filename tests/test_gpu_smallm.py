@@ -98,12 +98,13 @@ def test_workload4_full_size_small_batches():
 
 
 # --------------------------------------------------------------------------
-# Q45 on the matrix cores: tile-staged X (one power of two per token), and
-# fp32 X converted inside the product (one per 32-weight block and token)
+# Q45 on the matrix cores: tile-staged X and fp32 X converted in the product
+# (both one power of two per 32-weight block and token)
 # --------------------------------------------------------------------------
 
-MFMA_CASES = [(16, 64, 4096), (17, 1000, 4096), (31, 130, 1024), (48, 64, 2048),
-              (64, 12288, 4096), (80, 300, 4096), (16, 4096, 12288)]
+MFMA_CASES = [(6, 300, 4096), (16, 64, 4096), (17, 1000, 4096), (31, 130, 1024), (48, 64, 2048),
+              (64, 12288, 4096), (80, 300, 4096), (16, 4096, 12288), (512, 1000, 4096),
+              (200, 777, 1152)]
 
 
 @pytest.mark.parametrize("M,N,K", MFMA_CASES)
@@ -118,15 +119,15 @@ def test_mfma_matches_oracle(M, N, K):
     Y = mbq().gemv_xq(dw, Xt, M=M).cpu().numpy()
     ref = oracle.gemv_parallel(ow, X) if N * K > 1 << 24 else oracle.gemv(ow, X)
     check_gemv(Y, ow, X, ref)
-    # fp32 X: the matrix cores in passes of 16 tokens, x converted in the
-    # product; same bar
+    # fp32 X: the same kernel converting x as it enters LDS; the same bits
     Yv = mbq().gemv_q(dw, Xd).cpu().numpy()
     check_gemv(Yv, ow, X, ref)
+    assert np.array_equal(Yv.view(np.uint32), Y.view(np.uint32))
 
 
 def test_mfma_token_scales_and_accumulate():
-    """Tokens of very different magnitudes (each has its own power-of-two
-    scale), an all-zero token, and the accumulate epilogue."""
+    """Tokens of very different magnitudes (each block of each token has its
+    own power-of-two scale), an all-zero token, and the accumulate epilogue."""
     M, N, K = 20, 256, 4096
     planes = workloads.weight_planes(np.random.default_rng(9600), 1, N, K)
     ow, dw = oracle.Planes(1, N, K, planes), mbq().QWeight.from_host(1, N, K, planes)
