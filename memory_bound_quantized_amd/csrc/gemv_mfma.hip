@@ -171,20 +171,34 @@ __device__ __forceinline__ u4v quad_transpose(u4v d) {
 typedef const void __attribute__((address_space(1)))* gvoid;
 typedef void __attribute__((address_space(3)))* lvoid;
 
-template <int TT, int RW, int QW, bool F32X>
+// s_waitcnt with vmcnt = n and the other counters left alone (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// NCH: chunks of K, known at compile time for the common widths (the whole
+// pipeline is then straight-line code and every wait names exactly the loads
+// it needs); 0 when K is known only at run time.
+template <int TT, int RW, int QW, int NCH, bool F32X>
 __global__ __launch_bounds__(kMT) void gemv_mfma_q45_kernel(
         DevPlanes P, int N, int K, const uint8_t* __restrict__ xt, const float* __restrict__ xf,
         int64_t ldx, int M, float* __restrict__ y, int64_t ldy, int accumulate) {
     constexpr int QPC = kMW * QW;                 // quads per chunk
     constexpr int NBC = 4 * QPC;                  // blocks per chunk
     constexpr int XB = TT * NBC * kTileBlockBytes;   // LDS bytes of x per chunk
+    // weight slots in registers: chunks whose loads are in flight or done
+    constexpr int NS = NCH == 0 ? 2 : (NCH < (F32X ? 2 : 3) ? NCH : (F32X ? 2 : 3));
+    constexpr int WLOADS = QW * RW * 2;           // load instructions of one chunk's weights
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int g = lane >> 4, j = lane & 15;
     const int nq = K / 128, nb = K / 32;
-    const int nchunks = (nq + QPC - 1) / QPC;
+    const int nchunks = NCH > 0 ? NCH : (nq + QPC - 1) / QPC;
     const int row0 = blockIdx.x * (16 * RW);
     const int tt0 = blockIdx.y * TT;               // first token tile
     const int ntt = (M + 15) / 16;
@@ -200,9 +214,9 @@ __global__ __launch_bounds__(kMT) void gemv_mfma_q45_kernel(
         co[rt] = (uint32_t)row * (uint32_t)(K / 2) + 16u * g;
         so[rt] = (uint32_t)row * (uint32_t)(K / 16);
     }
-    u4v wc[2][QW][RW];
-    u2v ws[2][QW][RW];
-    auto load_w = [&](auto slot_c, int c) {
+    u4v wc[NS][QW][RW];
+    u2v ws[NS][QW][RW];
+    auto load_w = [&](auto slot_c, int c) __attribute__((always_inline)) {
         constexpr int sl = decltype(slot_c)::value;
 #pragma unroll
         for (int i = 0; i < QW; i++) {
@@ -215,18 +229,25 @@ __global__ __launch_bounds__(kMT) void gemv_mfma_q45_kernel(
         }
     };
 
-    // x of chunk c into LDS: [tt][block][2 KB], then [tt][quad][64 B]
-    auto fill = [&](int c) {
+    // x of chunk c into LDS: [tt][block][2 KB], then [tt][quad][64 B].  The
+    // copy is issued (fill_issue) and completed (fill_finish) in two steps,
+    // so that loads issued between them stay in flight.
+    constexpr int ITEMS = TT * NBC * 64;
+    constexpr int IPT = F32X ? ITEMS / kMT : 1;
+    static_assert(!F32X || ITEMS % kMT == 0, "items per thread");
+    f4g va[IPT], vb[IPT];
+    // Every workgroup reads the same x: each starts at its own piece or
+    // block, so the workgroups of an XCD do not all ask one L2 channel for
+    // the same lines at the same moment.
+    const int rotb = (int)((blockIdx.x * 5u) % (unsigned)NBC);
+    auto blk = [&](int i) __attribute__((always_inline)) { const int b = (i >> 6) % NBC + rotb; return b < NBC ? b : b - NBC; };
+    auto fill_issue = [&](int c) __attribute__((always_inline)) {
         const int nbc = min(NBC, nb - c * NBC);        // valid blocks of this chunk
         if constexpr (F32X) {
-            constexpr int ITEMS = TT * NBC * 64;
-            constexpr int IPT = ITEMS / kMT;
-            static_assert(ITEMS % kMT == 0, "items per thread");
-            f4g va[IPT], vb[IPT];
 #pragma unroll
             for (int s = 0; s < IPT; s++) {
                 const int i = s * kMT + tid;
-                const int gg = i & 3, t = (i >> 2) & 15, b = (i >> 6) % NBC, tt = (i >> 6) / NBC;
+                const int gg = i & 3, t = (i >> 2) & 15, b = blk(i), tt = (i >> 6) / NBC;
                 const int m = (tt0 + tt) * 16 + t;
                 va[s] = f4g{0.f, 0.f, 0.f, 0.f};
                 vb[s] = va[s];
@@ -236,22 +257,15 @@ __global__ __launch_bounds__(kMT) void gemv_mfma_q45_kernel(
                     vb[s] = src[1];
                 }
             }
-#pragma unroll
-            for (int s = 0; s < IPT; s++) {
-                const int i = s * kMT + tid;
-                const int gg = i & 3, t = (i >> 2) & 15, b = (i >> 6) % NBC, tt = (i >> 6) / NBC;
-                const XConv v = convert_item(va[s], vb[s]);
-                uint8_t* tile = lds + tt * (NBC * kTileBlockBytes);
-                *(u4v*)(tile + xt_slot(b, gg, t)) = v.hi;
-                *(u4v*)(tile + xt_slot(b, gg, t) + 1024) = v.lo;
-                if (gg == 0) lds[XB + tt * (NBC * 16) + xt_exp_byte(b, t)] = (uint8_t)(int8_t)v.ne;
-            }
         } else {
             // copies of 1 KB pieces (one per wave instruction), straight into LDS
             const int pieces_x = nbc * 2;                  // per tile
             const int pieces_e = (nbc * 16 + 1023) / 1024;   // exponent bytes per tile: 16 per block
+            const int npc = TT * (pieces_x + pieces_e);
+            const int rot = (int)((blockIdx.x * 37u) % (unsigned)npc);
 #pragma unroll 1
-            for (int p = wave; p < TT * (pieces_x + pieces_e); p += kMW) {
+            for (int p0 = wave; p0 < npc; p0 += kMW) {
+                const int p = p0 + rot < npc ? p0 + rot : p0 + rot - npc;
                 const int tt = p / (pieces_x + pieces_e), q = p % (pieces_x + pieces_e);
                 const int ttg = min(tt0 + tt, ntt - 1);
                 const uint8_t* tile = xt + (int64_t)ttg * xt_tile_bytes(K);
@@ -265,8 +279,29 @@ __global__ __launch_bounds__(kMT) void gemv_mfma_q45_kernel(
                                                          (lvoid)(lds + XB + tt * (NBC * 16) + (q - pieces_x) * 1024), 16, 0, 0);
                 }
             }
-            __builtin_amdgcn_s_waitcnt(0);
         }
+    };
+    // PEND: weight loads issued after fill_issue that may stay in flight.
+    auto fill_finish = [&](auto pend_c) __attribute__((always_inline)) {
+        constexpr int PEND = decltype(pend_c)::value;
+        if constexpr (F32X) {
+#pragma unroll
+            for (int s = 0; s < IPT; s++) {
+                const int i = s * kMT + tid;
+                const int gg = i & 3, t = (i >> 2) & 15, b = blk(i), tt = (i >> 6) / NBC;
+                const XConv v = convert_item(va[s], vb[s]);
+                uint8_t* tile = lds + tt * (NBC * kTileBlockBytes);
+                *(u4v*)(tile + xt_slot(b, gg, t)) = v.hi;
+                *(u4v*)(tile + xt_slot(b, gg, t) + 1024) = v.lo;
+                if (gg == 0) lds[XB + tt * (NBC * 16) + xt_exp_byte(b, t)] = (uint8_t)(int8_t)v.ne;
+            }
+        } else {
+            wait_vm<PEND>();
+        }
+    };
+    auto fill = [&](int c) __attribute__((always_inline)) {
+        fill_issue(c);
+        fill_finish(IC<0>{});
     };
 
     f4v acc[RW][TT];
@@ -276,13 +311,13 @@ __global__ __launch_bounds__(kMT) void gemv_mfma_q45_kernel(
         for (int tt = 0; tt < TT; tt++) acc[rt][tt] = f4v{0.f, 0.f, 0.f, 0.f};
     const f4v zero = {0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](auto slot_c, int c) {
+    auto compute = [&](auto slot_c, int c) __attribute__((always_inline)) {
         constexpr int sl = decltype(slot_c)::value;
-        const int nqc = min(QPC, nq - c * QPC);            // quads of this chunk
+        const int nqc = NCH > 0 ? QPC : min(QPC, nq - c * QPC);   // quads of this chunk
 #pragma unroll
         for (int i = 0; i < QW; i++) {
             const int ql = wave * QW + i;                  // quad within the chunk
-            if (ql >= nqc) break;                          // the same in every lane
+            if (NCH == 0 && ql >= nqc) break;              // the same in every lane
             u4v cb[RW];
 #pragma unroll
             for (int rt = 0; rt < RW; rt++) cb[rt] = quad_transpose(wc[sl][i][rt]);
@@ -319,24 +354,55 @@ __global__ __launch_bounds__(kMT) void gemv_mfma_q45_kernel(
         }
     };
 
-    // chunk pipeline: the weights of chunk c + 1 load while chunk c computes
-    load_w(IC<0>{}, 0);
-    fill(0);
-    __syncthreads();
+    if constexpr (NCH > 0) {
+        // straight-line pipeline: NS chunks of weights in flight from the
+        // start; after chunk c computes, chunk c + 1's x is copied in and
+        // the slot chunk c used refills with chunk c + NS, whose loads go out
+        // after the copy so that completing the copy does not wait for them
+#pragma unroll
+        for (int c = 0; c < NS; c++) {
+            if (c == 0) load_w(IC<0>{}, 0);
+            if (c == 1) load_w(IC<1 % NS>{}, 1);
+            if (c == 2) load_w(IC<2 % NS>{}, 2);
+        }
+        fill(0);
+        __syncthreads();
+        static_for<0, NCH>([&](auto cc) __attribute__((always_inline)) {
+            constexpr int c = decltype(cc)::value;
+            compute(IC<c % NS>{}, c);
+            if constexpr (c + 1 < NCH) {
+                __syncthreads();
+                fill_issue(c + 1);
+                if constexpr (c + NS < NCH) {
+                    load_w(IC<c % NS>{}, c + NS);
+                    fill_finish(IC<WLOADS>{});
+                } else {
+                    fill_finish(IC<0>{});
+                }
+                __syncthreads();
+            }
+        });
+    } else {
+        // K known only at run time: two slots, chunk c + 1's weights load
+        // while chunk c computes
+        load_w(IC<0>{}, 0);
+        fill(0);
+        __syncthreads();
 #pragma unroll 1
-    for (int c = 0; c < nchunks; c += 2) {
-        if (c + 1 < nchunks) load_w(IC<1>{}, c + 1);
-        compute(IC<0>{}, c);
-        if (c + 1 >= nchunks) break;
-        __syncthreads();
-        fill(c + 1);
-        __syncthreads();
-        if (c + 2 < nchunks) load_w(IC<0>{}, c + 2);
-        compute(IC<1>{}, c + 1);
-        if (c + 2 >= nchunks) break;
-        __syncthreads();
-        fill(c + 2);
-        __syncthreads();
+        for (int c = 0; c < nchunks; c += 2) {
+            if (c + 1 < nchunks) load_w(IC<1>{}, c + 1);
+            compute(IC<0>{}, c);
+            if (c + 1 >= nchunks) break;
+            __syncthreads();
+            fill(c + 1);
+            __syncthreads();
+            if (c + 2 < nchunks) load_w(IC<0>{}, c + 2);
+            compute(IC<1>{}, c + 1);
+            if (c + 2 >= nchunks) break;
+            __syncthreads();
+            fill(c + 2);
+            __syncthreads();
+        }
     }
 
     // the 8 waves' partial tiles, added in wave order
@@ -370,7 +436,7 @@ __global__ __launch_bounds__(kMT) void gemv_mfma_q45_kernel(
     }
 }
 
-template <int TT, int RW, int QW, bool F32X>
+template <int TT, int RW, int QW, int NCH, bool F32X>
 static hipError_t launch_k(DevPlanes P, int64_t N, int64_t K, const uint8_t* xt, const float* xf,
                            int64_t ldx, int64_t M, float* y, int64_t ldy, int accumulate,
                            hipStream_t stream) {
@@ -378,13 +444,27 @@ static hipError_t launch_k(DevPlanes P, int64_t N, int64_t K, const uint8_t* xt,
     constexpr size_t xl = (size_t)TT * NBC * kTileBlockBytes + (size_t)TT * NBC * 16;
     constexpr size_t rl = (size_t)kMW * RW * TT * kWave * 16;
     constexpr size_t lds = xl > rl ? xl : rl;
-    auto kern = gemv_mfma_q45_kernel<TT, RW, QW, F32X>;
-    if (hipError_t e = ensure_lds<gemv_mfma_q45_kernel<TT, RW, QW, F32X>>(lds)) return e;
+    auto kern = gemv_mfma_q45_kernel<TT, RW, QW, NCH, F32X>;
+    if (hipError_t e = ensure_lds<gemv_mfma_q45_kernel<TT, RW, QW, NCH, F32X>>(lds)) return e;
     const int64_t ntt = (M + 15) / 16;
     const dim3 grid((unsigned)((N + 16 * RW - 1) / (16 * RW)), (unsigned)((ntt + TT - 1) / TT));
     hipLaunchKernelGGL(kern, grid, dim3(kMT), lds, stream, P, (int)N, (int)K, xt, xf, ldx, (int)M, y,
                        ldy, accumulate);
     return hipGetLastError();
+}
+
+template <int TT, int RW, bool F32X>
+static hipError_t launch_rw(DevPlanes P, int64_t N, int64_t K, const uint8_t* xt, const float* xf,
+                            int64_t ldx, int64_t M, float* y, int64_t ldy, int accumulate,
+                            hipStream_t s) {
+    constexpr int QW = TT == 1 ? 2 : 1;    // chunk of x: 128 KB of LDS
+    constexpr int KC = kMW * QW * 128;     // values per chunk
+    // fp32 x keeps the run-time loop: unrolled, its conversion registers and
+    // the weight slots outgrow the register file
+    if (F32X) return launch_k<TT, RW, QW, 0, F32X>(P, N, K, xt, xf, ldx, M, y, ldy, accumulate, s);
+    if (K == 4096) return launch_k<TT, RW, QW, 4096 / KC, F32X>(P, N, K, xt, xf, ldx, M, y, ldy, accumulate, s);
+    if (K == 12288) return launch_k<TT, RW, QW, 12288 / KC, F32X>(P, N, K, xt, xf, ldx, M, y, ldy, accumulate, s);
+    return launch_k<TT, RW, QW, 0, F32X>(P, N, K, xt, xf, ldx, M, y, ldy, accumulate, s);
 }
 
 // Row tiles per workgroup: about 256 workgroups per token-tile group (one
@@ -393,14 +473,13 @@ template <int TT, bool F32X>
 static hipError_t launch_tt(DevPlanes P, int64_t N, int64_t K, const uint8_t* xt, const float* xf,
                             int64_t ldx, int64_t M, float* y, int64_t ldy, int accumulate,
                             hipStream_t s) {
-    constexpr int QW = TT == 1 ? 2 : 1;    // chunk of x: 128 KB of LDS
     int64_t rw = (N + 16 * 256 - 1) / (16 * 256);
     if (const char* e = tuning_var("MBQ_MFMA_RW")) rw = atoi(e);
     switch (rw <= 1 ? 1 : rw == 2 ? 2 : rw == 3 ? 3 : 4) {
-    case 1: return launch_k<TT, 1, QW, F32X>(P, N, K, xt, xf, ldx, M, y, ldy, accumulate, s);
-    case 2: return launch_k<TT, 2, QW, F32X>(P, N, K, xt, xf, ldx, M, y, ldy, accumulate, s);
-    case 3: return launch_k<TT, 3, QW, F32X>(P, N, K, xt, xf, ldx, M, y, ldy, accumulate, s);
-    default: return launch_k<TT, 4, QW, F32X>(P, N, K, xt, xf, ldx, M, y, ldy, accumulate, s);
+    case 1: return launch_rw<TT, 1, F32X>(P, N, K, xt, xf, ldx, M, y, ldy, accumulate, s);
+    case 2: return launch_rw<TT, 2, F32X>(P, N, K, xt, xf, ldx, M, y, ldy, accumulate, s);
+    case 3: return launch_rw<TT, 3, F32X>(P, N, K, xt, xf, ldx, M, y, ldy, accumulate, s);
+    default: return launch_rw<TT, 4, F32X>(P, N, K, xt, xf, ldx, M, y, ldy, accumulate, s);
     }
 }
 

@@ -77,6 +77,12 @@ def lib():
                                               _vp, _vp]
         L.oracle_silu_mul.restype = None
         L.oracle_silu_mul.argtypes = [_vp, _vp, _i64, _vp]
+        L.oracle_f32_to_f16_sat.restype = ctypes.c_uint16
+        L.oracle_f32_to_f16_sat.argtypes = [ctypes.c_float]
+        L.oracle_f32_to_bf16.restype = ctypes.c_uint16
+        L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
+        L.oracle_quantize.restype = ctypes.c_int
+        L.oracle_quantize.argtypes = [ctypes.c_int, _i64, _i64, _vp, _i64, _vp, _vp, _vp]
         L.oracle_decode_token.restype = None
         L.oracle_decode_token.argtypes = [ctypes.c_int, _i64, _i64, _i64, _i64, _i64,
                                           _vp, _vp, _vp, _vp, _vp, ctypes.c_float,
@@ -321,3 +327,33 @@ def decode_token_parallel(layers, vocab: Planes, g1, g2, gf, eps: float, h0,
     z = rmsnorm(h, gf, eps)[0]
     logits = gemv_parallel(vocab, z, threads)[0]
     return h, logits
+
+
+def f32_to_f16(x: float) -> int:
+    """fp32 value -> binary16 bits (nearest even, saturating at 65504)."""
+    return int(lib().oracle_f32_to_f16_sat(float(np.float32(x))))
+
+
+def quantize(fmt: int, W: np.ndarray):
+    """fp32 weights [N, K] -> (codes [N, K] uint8 (BF16: uint16 words),
+    scales, supers) by the oracle's absmax rule (see oracle_quantize)."""
+    W = _c(np.atleast_2d(W), np.float32)
+    N, K = W.shape
+    if fmt == BF16:
+        codes = np.zeros((N, K), np.uint16)
+        sc = su = None
+    else:
+        codes = np.zeros((N, K), np.uint8)
+        sc = np.zeros(N * K // (16 if fmt == Q65 else 32), np.int8 if fmt == Q65 else np.uint16)
+        su = np.zeros(N * K // 256, np.uint16) if fmt == Q65 else None
+    rc = lib().oracle_quantize(fmt, N, K, _ptr(W), K, _ptr(codes), _ptr(sc), _ptr(su))
+    if rc:
+        raise ValueError("oracle_quantize: bad format or K")
+    return codes, sc, su
+
+
+def quantize_planes(fmt: int, W: np.ndarray) -> Planes:
+    """quantize() packed into the format's planes."""
+    codes, sc, su = quantize(fmt, W)
+    N, K = np.atleast_2d(W).shape
+    return pack(fmt, N, K, codes, sc, su)

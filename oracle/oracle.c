@@ -1,7 +1,8 @@
 /*
  * oracle.c -- plain, slow, obviously-correct CPU oracle for the decode-step
  * hot path: block-quantized GEMV (dequantize, dot product), RMSNorm,
- * two-pass LayerNorm, the SiLU-gated glue and the synthetic decode chain.
+ * two-pass LayerNorm, the SiLU-gated glue, the synthetic decode chain, the
+ * quantizer from fp32 weights and single-token attention over a KV cache.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, includes
  * or calls this file; it shares no header, table or helper with the GPU path.
@@ -449,4 +450,135 @@ void oracle_decode_token(int L, int64_t d, int64_t dq, int64_t dkv, int64_t f,
     oracle_rmsnorm(h, gf, eps, 1, d, a);
     oracle_gemv(W_(L, 0), V, d, a, 1, d, logits, V, 0, 0, V);
 #undef W_
+}
+
+
+/* ------------------------------------------------------------------------ */
+/* Quantizer: fp32 weights -> codes and scales                               */
+/* ------------------------------------------------------------------------ */
+
+/* fp32 -> IEEE binary16 bit pattern, rounding to nearest with ties to even,
+ * written out from the encoding; magnitudes that would round past the
+ * largest finite half (65504) saturate to it.  Subnormal halves (exponent
+ * 0, units of 2^-24) are produced where the value needs them. */
+uint16_t oracle_f32_to_f16_sat(float f)
+{
+    uint16_t sign = signbit(f) ? 0x8000 : 0;
+    double a = fabs((double)f);
+    if (a == 0.0)
+        return sign;
+    if (a >= 65504.0)
+        return (uint16_t)(sign | 0x7BFF);
+    if (a < ldexp(1.0, -14)) {
+        /* subnormal range: units of 2^-24; a * 2^24 is exact in double */
+        double m = nearbyint(a * 16777216.0);      /* ties to even (default mode) */
+        return (uint16_t)(sign | (uint16_t)m);      /* m = 1024 is the smallest normal */
+    }
+    int e;
+    double fr = frexp(a, &e);                       /* a = fr * 2^e, fr in [0.5, 1) */
+    e -= 1;                                         /* a = (2 fr) * 2^e, 2 fr in [1, 2) */
+    double m = nearbyint(ldexp(fr, 11));            /* 10 fraction bits: m in [1024, 2048] */
+    if (m == 2048.0) {
+        m = 1024.0;
+        e += 1;
+    }
+    if (e + 15 >= 31)
+        return (uint16_t)(sign | 0x7BFF);
+    return (uint16_t)(sign | (uint16_t)((e + 15) << 10) | (uint16_t)((int)m - 1024));
+}
+
+/* fp32 -> bfloat16 word, round to nearest with ties to even. */
+uint16_t oracle_f32_to_bf16(float f)
+{
+    uint32_t bits;
+    memcpy(&bits, &f, 4);
+    uint32_t low = bits & 0xFFFF, up = bits >> 16;
+    if (low > 0x8000 || (low == 0x8000 && (up & 1)))
+        up += 1;
+    return (uint16_t)up;
+}
+
+static int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+/* Symmetric absmax quantizer (this library's reading; the pages fix only the
+ * byte budgets of the formats, [roofline-holds] "The Math" and "The search
+ * space").  Every decision that yields an integer is made in fp32, in the
+ * order written:
+ *   Q45 / Q25, per block of 32:  s = half(max|w| / Qmax), Qmax = 7 / 1;
+ *     q = clamp(rint(w / s) + off, 0, 2^b - 1), off = 8 / 2; q = off if s = 0.
+ *   Q65, per super-block of 256 (16 sub-blocks of 16):
+ *     a_j = max_{sub-block j} |w| / 31;  d = half(max_j a_j / 127);
+ *     sc_j = clamp(rint(a_j / d), -128, 127)  (0 if d = 0);
+ *     q = clamp(rint(w / (d sc_j)) + 32, 0, 63)  (32 if d sc_j = 0).
+ *   BF16: round to nearest even.
+ * half() is oracle_f32_to_f16_sat, rint rounds half to even.
+ * Outputs: codes one byte per weight [N][K] (BF16: uint16 words),
+ * scales fp16 bits [N][K/32] (Q45, Q25) or int8 [N][K/16] (Q65),
+ * supers fp16 bits [N][K/256] (Q65).  Returns -1 for a bad format or K. */
+int oracle_quantize(int fmt, int64_t N, int64_t K, const float* w, int64_t ldw,
+                    void* codes, void* scales, uint16_t* supers)
+{
+    if (fmt == FMT_BF16) {
+        uint16_t* o = (uint16_t*)codes;
+        for (int64_t n = 0; n < N; n++)
+            for (int64_t k = 0; k < K; k++)
+                o[n * K + k] = oracle_f32_to_bf16(w[n * ldw + k]);
+        return 0;
+    }
+    uint8_t* q = (uint8_t*)codes;
+    if (fmt == FMT_Q45 || fmt == FMT_Q25) {
+        if (K % 32) return -1;
+        const int qmax = fmt == FMT_Q45 ? 7 : 1, off = fmt == FMT_Q45 ? 8 : 2;
+        const int top = fmt == FMT_Q45 ? 15 : 3;
+        uint16_t* sc = (uint16_t*)scales;
+        for (int64_t n = 0; n < N; n++)
+            for (int64_t b = 0; b < K / 32; b++) {
+                const float* wb = w + n * ldw + 32 * b;
+                float amax = 0.0f;
+                for (int k = 0; k < 32; k++)
+                    if (fabsf(wb[k]) > amax) amax = fabsf(wb[k]);
+                const float t = amax / (float)qmax;
+                const uint16_t sh = oracle_f32_to_f16_sat(t);
+                const float s = (float)oracle_f16_to_f64(sh);
+                sc[n * (K / 32) + b] = sh;
+                for (int k = 0; k < 32; k++) {
+                    int code = off;
+                    if (s != 0.0f) code = clampi((int)rintf(wb[k] / s) + off, 0, top);
+                    q[n * K + 32 * b + k] = (uint8_t)code;
+                }
+            }
+        return 0;
+    }
+    if (fmt == FMT_Q65) {
+        if (K % 256) return -1;
+        int8_t* sc = (int8_t*)scales;
+        for (int64_t n = 0; n < N; n++)
+            for (int64_t sb = 0; sb < K / 256; sb++) {
+                const float* ws = w + n * ldw + 256 * sb;
+                float a[16], amx = 0.0f;
+                for (int j = 0; j < 16; j++) {
+                    float m = 0.0f;
+                    for (int k = 0; k < 16; k++)
+                        if (fabsf(ws[16 * j + k]) > m) m = fabsf(ws[16 * j + k]);
+                    a[j] = m / 31.0f;
+                    if (a[j] > amx) amx = a[j];
+                }
+                const uint16_t dh = oracle_f32_to_f16_sat(amx / 127.0f);
+                const float d = (float)oracle_f16_to_f64(dh);
+                supers[n * (K / 256) + sb] = dh;
+                for (int j = 0; j < 16; j++) {
+                    int s8 = 0;
+                    if (d != 0.0f) s8 = clampi((int)rintf(a[j] / d), -128, 127);
+                    sc[n * (K / 16) + 16 * sb + j] = (int8_t)s8;
+                    const float step = d * (float)s8;     /* exact: 11 + 7 significant bits */
+                    for (int k = 0; k < 16; k++) {
+                        int code = 32;
+                        if (step != 0.0f) code = clampi((int)rintf(ws[16 * j + k] / step) + 32, 0, 63);
+                        q[n * K + 256 * sb + 16 * j + k] = (uint8_t)code;
+                    }
+                }
+            }
+        return 0;
+    }
+    return -1;
 }
