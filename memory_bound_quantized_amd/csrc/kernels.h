@@ -178,6 +178,10 @@ hipError_t launch_silu_mul(const float* g, const float* u, int64_t n, float* out
 
 hipError_t launch_dequant(int fmt, DevPlanes P, int64_t N, int64_t K, float* w_out,
                           hipStream_t stream);
+// fp32 w [N][ldw] -> planes of fmt (quantize.hip); the planes are written
+// through out's pointers.  K % 32 (Q45, Q25), K % 256 (Q65), K % 8 (BF16).
+hipError_t launch_quantize(int fmt, const float* w, int64_t ldw, int64_t N, int64_t K,
+                           DevPlanes out, hipStream_t stream);
 hipError_t launch_unpack_codes(int fmt, DevPlanes P, int64_t N, int64_t K, uint8_t* out,
                                hipStream_t stream);
 

@@ -83,6 +83,9 @@ def lib():
         L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
         L.oracle_quantize.restype = ctypes.c_int
         L.oracle_quantize.argtypes = [ctypes.c_int, _i64, _i64, _vp, _i64, _vp, _vp, _vp]
+        L.oracle_attention_decode.restype = None
+        L.oracle_attention_decode.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _i64, _vp,
+                                              _vp, _vp, _i64, _vp, _vp]
         L.oracle_decode_token.restype = None
         L.oracle_decode_token.argtypes = [ctypes.c_int, _i64, _i64, _i64, _i64, _i64,
                                           _vp, _vp, _vp, _vp, _vp, ctypes.c_float,
@@ -357,3 +360,24 @@ def quantize_planes(fmt: int, W: np.ndarray) -> Planes:
     codes, sc, su = quantize(fmt, W)
     N, K = np.atleast_2d(W).shape
     return pack(fmt, N, K, codes, sc, su)
+
+
+def attention_decode(q, kc, vc, n_heads: int, n_kv: int, d: int, T: int | None = None):
+    """One token's attention over a KV cache (see oracle_attention_decode).
+    q: float [n_heads * d]; kc, vc: fp16 values or uint16 bits, [T, n_kv * d]
+    (row stride = their second dimension).  Returns float [n_heads * d]."""
+    q = _c(q, np.float32).reshape(-1)
+    kc = np.ascontiguousarray(kc)
+    vc = np.ascontiguousarray(vc)
+    if kc.dtype == np.float16:
+        kc = kc.view(np.uint16)
+    if vc.dtype == np.float16:
+        vc = vc.view(np.uint16)
+    kc = kc.reshape(kc.shape[0], -1)
+    vc = vc.reshape(vc.shape[0], -1)
+    T = kc.shape[0] if T is None else int(T)
+    out = np.zeros(n_heads * d, np.float32)
+    scratch = np.zeros(max(T, 1), np.float64)
+    lib().oracle_attention_decode(n_heads, n_kv, d, T, _ptr(q), _ptr(kc), _ptr(vc), kc.shape[1],
+                                  _ptr(out), _ptr(scratch))
+    return out

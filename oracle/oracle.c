@@ -582,3 +582,50 @@ int oracle_quantize(int fmt, int64_t N, int64_t K, const float* w, int64_t ldw,
     }
     return -1;
 }
+
+
+/* ------------------------------------------------------------------------ */
+/* Single-token attention over a KV cache                                    */
+/* ------------------------------------------------------------------------ */
+
+/* One new token attends over T cached positions ([roofline-holds] "Said
+ * before the run": with 512 tokens loaded each token also reads the
+ * conversation's memory, 75.5 MB for the 36-layer model, i.e. 16-bit keys and
+ * values 1024 wide per layer).  Plain scaled dot-product attention, the
+ * reading this library takes (the pages name no positional encoding or
+ * normalisation of q and k):
+ *   head h of n_heads reads key/value head g = h / (n_heads / n_kv);
+ *   s_t = (q_h . k_{t,g}) / sqrt(d);  p_t = exp(s_t - max s) / sum exp(s - max s);
+ *   out_h = sum_t p_t v_{t,g}.
+ * q: float [n_heads * d]; kc, vc: fp16 bits, position t's row at t * ld
+ * (elements), head g at g * d within it; out: float [n_heads * d].
+ * fp64 throughout, one rounding to float per output. */
+void oracle_attention_decode(int n_heads, int n_kv, int d, int64_t T, const float* q,
+                             const uint16_t* kc, const uint16_t* vc, int64_t ld, float* out,
+                             double* scratch /* T doubles */)
+{
+    const int group = n_heads / n_kv;
+    const double scale = 1.0 / sqrt((double)d);
+    for (int h = 0; h < n_heads; h++) {
+        const int g = h / group;
+        double mx = -INFINITY;
+        for (int64_t t = 0; t < T; t++) {
+            double sdot = 0.0;
+            for (int i = 0; i < d; i++)
+                sdot += (double)q[h * d + i] * oracle_f16_to_f64(kc[t * ld + g * d + i]);
+            scratch[t] = sdot * scale;
+            if (scratch[t] > mx) mx = scratch[t];
+        }
+        double z = 0.0;
+        for (int64_t t = 0; t < T; t++) {
+            scratch[t] = exp(scratch[t] - mx);
+            z += scratch[t];
+        }
+        for (int i = 0; i < d; i++) {
+            double acc = 0.0;
+            for (int64_t t = 0; t < T; t++)
+                acc += scratch[t] * oracle_f16_to_f64(vc[t * ld + g * d + i]);
+            out[h * d + i] = (float)(acc / z);
+        }
+    }
+}
