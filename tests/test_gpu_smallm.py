@@ -61,9 +61,10 @@ def test_smallm_rows_equal_single_token_products(fmt, M, N, K):
     if fmt != 0:
         Xq = mbq().stage_x(fmt, dev(X[:, :K]))
         Ys = mbq().gemv_xq(dw, Xq, M=M).cpu().numpy()
-        if fmt == 1 and M >= 6 and K % 1024 == 0:
-            # the tile form: Q45 batches of 6+ tokens on the matrix cores
-            assert Xq.numel() * 4 == mbq().xq_bytes(1, M, K) == (K // 32) * 2048 + 64
+        if fmt == 1 and M >= 6 and K % 128 == 0:
+            # the tile form: Q45 batches of 6+ tokens on the matrix cores, per
+            # 16 tokens 2 KB per 32-value block plus 64 exponent bytes per 128
+            assert Xq.numel() * 4 == mbq().xq_bytes(1, M, K) == -(-M // 16) * ((K // 32) * 2048 + (K // 128) * 64)
             check_gemv(Ys, ow, X[:, :K], ref)
         else:
             assert np.array_equal(Ys.view(np.uint32), Y.view(np.uint32))
