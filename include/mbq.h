@@ -234,6 +234,19 @@ int mbq_decode_workspace_bytes(const mbq_decode_model* model, size_t* bytes);
 int mbq_decode_step(const mbq_decode_model* model, float* h, float* logits, void* workspace,
                     size_t workspace_bytes, void* stream);
 
+/* mbq_decode_step for callers that cannot allocate device memory (code under
+ * HIP graph capture that may not call hipMalloc, tight serving loops,
+ * harnesses that forbid allocation): the same launches, kernels and
+ * results bit for bit, with no workspace argument.  q|k|v and the gated
+ * activations live in a device array inside the library, 1 MiB per GPU,
+ * held until the process ends: align256(4 (dq + 2 dkv)) + align256(4 f)
+ * must fit in it (MBQ_EUNSUPPORTED otherwise).  Every call on a GPU shares
+ * that GPU's array, so calls that overlap on one GPU (two streams, two
+ * threads) race; calls on one stream are ordered.  Nothing in the array
+ * needs to start at zero: each step writes q|k|v and the activations before
+ * it reads them.  h, logits: as for mbq_decode_step.  Allocates nothing. */
+int mbq_decode_step_noalloc(const mbq_decode_model* model, float* h, float* logits, void* stream);
+
 /* The same token in ONE launch ([one-serial-kernel] "The kernel that was never
  * built": the token's pieces of work without a return to the host between
  * them; [roofline-holds] "Where the time goes": the per-kernel toll).  Every

@@ -18,7 +18,7 @@ BF16, Q45, Q65, Q25 = 0, 1, 2, 3
 EXPORTS = (
     "mbq_format_info", "mbq_plane_sizes", "mbq_pack", "mbq_unpack", "mbq_gemv_q",
     "mbq_gemv_q_gather", "mbq_gemv_fused", "mbq_decode_workspace_bytes", "mbq_decode_step",
-    "mbq_decode_prepare", "mbq_decode_step_persistent",
+    "mbq_decode_step_noalloc", "mbq_decode_prepare", "mbq_decode_step_persistent",
     "mbq_xq_bytes", "mbq_stage_x", "mbq_gemv_xq", "mbq_rmsnorm_xq",
     "mbq_silu_mul_xq", "mbq_rmsnorm", "mbq_layernorm", "mbq_silu_mul", "mbq_dequant_f32",
     "mbq_unpack_codes", "mbq_probe_read", "mbq_probe_copy", "mbq_probe_chase_init",
@@ -83,6 +83,7 @@ def _load():
         "mbq_gemv_fused": (i32, [ctypes.POINTER(QWeightDesc), vp, vp, f32, i32, vp, vp]),
         "mbq_decode_workspace_bytes": (i32, [ctypes.POINTER(DecodeModelDesc), ctypes.POINTER(sz)]),
         "mbq_decode_step": (i32, [ctypes.POINTER(DecodeModelDesc), vp, vp, vp, sz, vp]),
+        "mbq_decode_step_noalloc": (i32, [ctypes.POINTER(DecodeModelDesc), vp, vp, vp]),
         "mbq_decode_prepare": (i32, [ctypes.POINTER(DecodeModelDesc), vp, sz, vp]),
         "mbq_decode_step_persistent": (i32, [ctypes.POINTER(DecodeModelDesc), vp, vp, vp, sz, vp]),
         "mbq_xq_bytes": (i32, [i32, i64, i64, ctypes.POINTER(sz)]),

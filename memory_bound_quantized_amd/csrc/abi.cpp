@@ -3,8 +3,10 @@
 // enqueued unless every argument check passes.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <cstdlib>
 #include <cstring>
 #include <string>
@@ -490,16 +492,10 @@ static int check_workspace(const mbq_decode_model* m, const float* h, const floa
     return MBQ_OK;
 }
 
-int mbq_decode_step(const mbq_decode_model* m, float* h, float* logits, void* workspace,
-                    size_t workspace_bytes, void* stream) {
-    const char* fn = "mbq_decode_step";
-    int rc = check_decode(m, fn);
-    if (rc) return rc;
-    if ((rc = check_workspace(m, h, logits, workspace, workspace_bytes, fn))) return rc;
-    const DecodeLayout lay = decode_layout(m);
-    hipStream_t s = (hipStream_t)stream;
-    float* qkv = (float*)((char*)workspace + lay.qkv);
-    float* mm = (float*)((char*)workspace + lay.m);
+// The launch chain of one token: qkv holds q|k|v (dq + 2 dkv floats) and mm
+// the gated activations (f floats) between launches.
+static hipError_t decode_chain(const mbq_decode_model* m, float* h, float* logits, float* qkv,
+                               float* mm, hipStream_t s) {
     auto geom = [](const mbq_qweight& W, bool pairs = false, bool norm = false) {
         mbq::GemvGeom g = mbq::gemv_m1_default_geom(W.fmt, W.N, W.K, pairs, norm);
         geom_override(&g);
@@ -529,7 +525,52 @@ int mbq_decode_step(const mbq_decode_model* m, float* h, float* logits, void* wo
     if (e == hipSuccess && m->vocab > 0)
         e = mbq::launch_gemv_fused(m->lm_head.fmt, planes_of(&m->lm_head), m->vocab, m->d, h,
                                    m->gamma_f, m->eps, false, logits, 0, geom(m->lm_head, false, true), s);
-    return hip_status(e, fn);
+    return e;
+}
+
+int mbq_decode_step(const mbq_decode_model* m, float* h, float* logits, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    const char* fn = "mbq_decode_step";
+    int rc = check_decode(m, fn);
+    if (rc) return rc;
+    if ((rc = check_workspace(m, h, logits, workspace, workspace_bytes, fn))) return rc;
+    const DecodeLayout lay = decode_layout(m);
+    float* qkv = (float*)((char*)workspace + lay.qkv);
+    float* mm = (float*)((char*)workspace + lay.m);
+    return hip_status(decode_chain(m, h, logits, qkv, mm, (hipStream_t)stream), fn);
+}
+
+// ---- the same step without a workspace argument --------------------------
+// The activations between launches live in a file-scope device array, one
+// copy per GPU, held until the process ends.  Host code never passes the
+// array's name to a kernel (it is a host-side stand-in there): each device's
+// address comes from hipGetSymbolAddress, taken once per device with that
+// device current.
+constexpr size_t kScratchBytes = (size_t)1 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::atomic<void*> g_scratch_ptr[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+static int scratch_of_current_device(void** out, const char* fn) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, fn);
+    if (dev < 0 || dev >= kMaxDevices) return fail(MBQ_EUNSUPPORTED, "%s: device %d beyond %d", fn, dev, kMaxDevices);
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return hip_status(e, fn);
+            if (!p) return fail(MBQ_EHIP, "%s: no device address for the scratch array", fn);
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return MBQ_OK;
 }
 
 // Identity of a model's device pointers (FNV-1a over every plane and gamma).
@@ -624,6 +665,25 @@ int mbq_decode_step_persistent(const mbq_decode_model* m, float* h, float* logit
     if (e == hipErrorInvalidConfiguration)
         return fail(MBQ_EUNSUPPORTED, "%s: the model's row counts or this device's compute-unit count do not fit the one-launch step", fn);
     return hip_status(e, fn);
+}
+
+int mbq_decode_step_noalloc(const mbq_decode_model* m, float* h, float* logits, void* stream) {
+    const char* fn = "mbq_decode_step_noalloc";
+    int rc = check_decode(m, fn);
+    if (rc) return rc;
+    if (!h || !aligned(h, 16)) return fail(MBQ_EALIGN, "%s: h must be 16-byte aligned", fn);
+    if (m->vocab > 0 && (!logits || !aligned(logits, 4))) return fail(MBQ_EINVAL, "%s: bad logits", fn);
+    if (m->vocab > 0 && overlaps(logits, (size_t)m->vocab * 4, h, (size_t)m->d * 4))
+        return fail(MBQ_EINVAL, "%s: h and logits overlap", fn);
+    const size_t qb = align256((size_t)(m->dq + 2 * m->dkv) * 4), mb = align256((size_t)m->f * 4);
+    if (qb + mb > kScratchBytes)
+        return fail(MBQ_EUNSUPPORTED, "%s: dq + 2 dkv and f need %zu bytes of scratch; the limit is %zu",
+                    fn, qb + mb, kScratchBytes);
+    void* p = nullptr;
+    if ((rc = scratch_of_current_device(&p, fn))) return rc;
+    float* qkv = (float*)p;
+    float* mm = (float*)((char*)p + qb);
+    return hip_status(decode_chain(m, h, logits, qkv, mm, (hipStream_t)stream), fn);
 }
 
 int mbq_xq_bytes(int fmt, int64_t M, int64_t K, size_t* bytes) {

@@ -100,6 +100,14 @@ class DecodeModel:
                                   _ptr(self.workspace), self.workspace.numel(), _stream(stream)))
         return logits
 
+    def step_noalloc(self, h, logits, stream=None):
+        """One token without a workspace: mbq_decode_step_noalloc (the
+        library's own per-GPU array holds the activations; allocates
+        nothing)."""
+        check(lib.mbq_decode_step_noalloc(ctypes.byref(self.desc), _ptr(h), _ptr(logits),
+                                          _stream(stream)))
+        return logits
+
     def prepare(self, stream=None):
         """Write the layer table the one-launch step reads into the workspace."""
         check(lib.mbq_decode_prepare(ctypes.byref(self.desc), _ptr(self.workspace),
