@@ -363,6 +363,29 @@ int mbq_silu_mul(const float* g, const float* u, int64_t n, float* out, void* st
 int mbq_dequant_f32(const mbq_qweight* W, float* w_out, void* stream);
 int mbq_unpack_codes(const mbq_qweight* W, uint8_t* codes_out, void* stream);
 
+/* Device quantizer: fp32 weights w [N][ldw] (device, 16-byte aligned, ldw a
+ * multiple of 4, ldw >= K) -> the planes of format fmt (device pointers in
+ * planes[0..3], sizes and alignment as for mbq_qweight; NULL where
+ * mbq_plane_sizes gives 0).  The pages fix each format by its byte budget
+ * ([roofline-holds] "The Math"; "The search space"); the rule that picks
+ * codes and scales is this library's, with every decision in fp32:
+ *   Q45, Q25 (blocks of 32): s = half(max|w| / Qmax), Qmax = 7 or 1;
+ *       q = clamp(rint(w / s) + off, 0, 2^b - 1), off = 8 or 2 (q = off
+ *       where s = 0);
+ *   Q65 (super-blocks of 256, sub-blocks of 16): a_j = max_j|w| / 31,
+ *       d = half(max_j a_j / 127), sc_j = clamp(rint(a_j / d), -128, 127)
+ *       (0 where d = 0), q = clamp(rint(w / (d sc_j)) + 32, 0, 63) (32
+ *       where d sc_j = 0);
+ *   BF16: round to nearest even.
+ * half() rounds to binary16 nearest-even and saturates at 65504; division
+ * is correctly rounded fp32, rint rounds half to even.  One pass over w
+ * (4 bytes per weight read, bits/8 written).  MBQ_EINVAL for an unknown
+ * format, K not a multiple of the block length, NULL or overlapping
+ * buffers; MBQ_EALIGN as stated; MBQ_EUNSUPPORTED for BF16 with K % 8 != 0
+ * or N*K above 2^42. */
+int mbq_quantize(int fmt, const float* w, int64_t N, int64_t K, int64_t ldw, void* const planes[4],
+                 void* stream);
+
 /* Measurement kit ([roofline-holds] "The Math" and "How I ran it": measure
  * the ceiling, never quote it; a large in-device copy counts read and write).
  * mbq_probe_read: reads `bytes` (a multiple of 16, buffer 16-byte aligned)

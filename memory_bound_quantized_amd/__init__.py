@@ -253,6 +253,21 @@ def unpack_codes(W: QWeight, out=None, stream=None):
     return out
 
 
+def quantize(fmt: int, w, out: "QWeight | None" = None, stream=None) -> "QWeight":
+    """fp32 cuda weights [N, K] (row stride a multiple of 4) -> a QWeight of
+    format fmt made on the device (mbq_quantize).  out: a QWeight of the same
+    format and shape whose planes are overwritten."""
+    import torch
+    N, K = w.shape
+    if out is None:
+        sz = plane_sizes(fmt, N, K)
+        out = QWeight(fmt, N, K, [torch.empty(n, dtype=torch.uint8, device=w.device) if n else None
+                                  for n in sz])
+    arr = (_vp * 4)(*[None if p is None else p.data_ptr() for p in out.planes])
+    check(lib.mbq_quantize(fmt, _ptr(w), N, K, w.stride(0), arr, _stream(stream)))
+    return out
+
+
 def probe_read(buf, sink, stream=None):
     check(lib.mbq_probe_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
                              _stream(stream)))

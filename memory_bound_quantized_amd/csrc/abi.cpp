@@ -881,6 +881,38 @@ int mbq_unpack_codes(const mbq_qweight* W, uint8_t* codes_out, void* stream) {
     return hip_status(mbq::launch_unpack_codes(W->fmt, planes_of(W), W->N, W->K, codes_out, (hipStream_t)stream), fn);
 }
 
+int mbq_quantize(int fmt, const float* w, int64_t N, int64_t K, int64_t ldw, void* const planes[4],
+                 void* stream) {
+    const char* fn = "mbq_quantize";
+    if (!fmt_valid(fmt)) return fail(MBQ_EINVAL, "%s: unknown format %d", fn, fmt);
+    if (N < 0 || K < 0) return fail(MBQ_EINVAL, "%s: negative shape", fn);
+    if (K % block_len(fmt))
+        return fail(MBQ_EINVAL, "%s: K=%lld is not a multiple of the block length %lld", fn,
+                    (long long)K, (long long)block_len(fmt));
+    if (!planes) return fail(MBQ_EINVAL, "%s: planes is NULL", fn);
+    if (N == 0 || K == 0) return ok();
+    if (ldw < K) return fail(MBQ_EINVAL, "%s: ldw < K", fn);
+    if (fmt == MBQ_FMT_BF16 && K % 8) return fail(MBQ_EUNSUPPORTED, "%s: BF16 needs K %% 8 == 0", fn);
+    if (N * (K / 8) > ((int64_t)1 << 39)) return fail(MBQ_EUNSUPPORTED, "%s: N*K above 2^42", fn);
+    if (!w) return fail(MBQ_EINVAL, "%s: w is NULL", fn);
+    if (!aligned(w, 16) || ldw % 4) return fail(MBQ_EALIGN, "%s: w must be 16-byte aligned with ldw %% 4 == 0", fn);
+    size_t sz[4];
+    mbq_plane_sizes(fmt, N, K, sz);
+    for (int i = 0; i < 4; i++) {
+        if (sz[i] && !planes[i]) return fail(MBQ_EINVAL, "%s: a plane the format needs is NULL", fn);
+        if (sz[i] && !aligned(planes[i], i < 2 ? 16 : 4))
+            return fail(MBQ_EALIGN, "%s: planes 0 and 1 must be 16-byte aligned, 2 and 3 4-byte", fn);
+        if (sz[i] && overlaps(w, (size_t)((N - 1) * ldw + K) * 4, planes[i], sz[i]))
+            return fail(MBQ_EINVAL, "%s: w and plane %d overlap", fn, i);
+        for (int j = 0; j < i; j++)
+            if (overlaps(planes[i], sz[i], planes[j], sz[j]))
+                return fail(MBQ_EINVAL, "%s: planes %d and %d overlap", fn, j, i);
+    }
+    const mbq::DevPlanes out{(const uint8_t*)planes[0], (const uint8_t*)planes[1],
+                             (const uint8_t*)planes[2], (const uint8_t*)planes[3]};
+    return hip_status(mbq::launch_quantize(fmt, w, ldw, N, K, out, (hipStream_t)stream), fn);
+}
+
 int mbq_probe_read(const void* buf, size_t bytes, float* sink, void* stream) {
     const char* fn = "mbq_probe_read";
     if (!buf || !sink) return fail(MBQ_EINVAL, "%s: NULL pointer", fn);

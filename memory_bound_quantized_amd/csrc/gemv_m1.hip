@@ -1,8 +1,9 @@
 // gemv_m1.hip -- single-token matrix-vector product for block-quantized weights.
 //
 // y[n] (+)= sum_k w[n][k] x[k], the weight stream of one decode token
-// ([roofline-holds] "The Math": each weight is read once and used for two
-// sums, so the product is bound by memory, not by arithmetic).
+// ([roofline-holds] "The Math": every weight crosses the memory bus once per
+// token and enters a single multiply-add, a handful of flops per byte where
+// the chip could do hundreds, so the memory system sets the pace).
 //
 // Geometry (gfx950, wave64):
 //   * a workgroup of 4 waves puts x into LDS in its staged form (staging.h):

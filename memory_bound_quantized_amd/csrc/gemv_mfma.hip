@@ -16,7 +16,7 @@
 //     acc = fma(s, ldexp(D, -e), acc).
 //
 // Tile form of x (written by stage_x_mfma_kernel for the staged entry
-// points; the fp32-x entry point converts into LDS the same way).  Per tile
+// points; the fp32-x entry point converts in registers the same way).  Per tile
 // of 16 tokens:
 //   blocks b = 0 .. K/32-1, 2 KB each: [high part 1 KB][low part 1 KB]; lane
 //       l = 16 g + t of an instruction's A operand holds token t at
@@ -25,13 +25,17 @@
 //   then per quad of blocks u = 0 .. K/128-1, 64 bytes of exponents: byte
 //       16 g + 4 i + r holds -e of token 4 g + r in block 4 u + i (int8).
 //
-// Kernel geometry: a workgroup of 8 waves covers RW row tiles (16 rows each)
-// and TT token tiles.  K runs in chunks of 8 QW quads (128 values each): the
-// chunk's x is brought into LDS once (QW quads per wave, TT tiles), and each
-// wave multiplies its QW quads of the chunk against every row tile.  The
-// weights of the next chunk are in flight while a chunk computes; they are
-// the only vector-memory loads of the inner loop.  The 8 waves' partial tiles
-// are added in wave order through LDS at the end.
+// Kernel geometry: a workgroup of MW waves (16 for one token tile, 8 for
+// two) covers RW row tiles (16 rows each) and TT token tiles; the waves
+// split K.  Wave w takes quads (128 values of K) w, w + MW, w + 2 MW, ...:
+// for each it reads the RW row tiles' codes and scales and the TT tiles' x
+// straight into registers and multiplies every row tile by every token tile,
+// so each byte of x reaches the compute unit once and is used RW times, each
+// weight once and used TT times.  There is no barrier in the stream: the
+// next quad's weights are loaded as soon as the current ones are transposed,
+// and each block of its x as soon as the same block of the current quad is
+// used.  The waves' partial tiles are added in wave order through LDS at the
+// end, so the sums depend on MW but not on RW or TT.
 #include "device_common.h"
 #include "formats.h"
 #include "kernels.h"
@@ -45,8 +49,6 @@ typedef uint32_t u4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u2v __attribute__((ext_vector_type(2)));
 typedef float f4g __attribute__((ext_vector_type(4)));
 
-constexpr int kMW = 8;                        // waves per workgroup
-constexpr int kMT = kMW * kWave;              // threads per workgroup
 constexpr int kTileBlockBytes = 2048;         // one block of one token tile: high + low
 
 // Bytes of the tile form of one token tile of K values.
@@ -168,140 +170,184 @@ __device__ __forceinline__ u4v quad_transpose(u4v d) {
     return u4v{s01[0], s01[1], s23[0], s23[1]};
 }
 
-typedef const void __attribute__((address_space(1)))* gvoid;
-typedef void __attribute__((address_space(3)))* lvoid;
-
-// s_waitcnt with vmcnt = n and the other counters left alone (gfx9 encoding:
-// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
-template <int n>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(n >= 0 && n < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+// 4 x 4 transpose within each quad of lanes: register r of lane 4 q + i
+// becomes register i of lane 4 q + r.  Two rounds of 2 x 2 exchanges, with
+// the partner lane's value brought in by DPP (lane ^ 1, then lane ^ 2).
+__device__ __forceinline__ u4v lane_quad_transpose(u4v x, int lane) {
+    constexpr int kXor1 = 0xB1, kXor2 = 0x4E;     // quad_perm [1,0,3,2], [2,3,0,1]
+    const bool o1 = lane & 1, o2 = lane & 2;
+    auto dpp = [](uint32_t v, auto ctrl_c) __attribute__((always_inline)) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, decltype(ctrl_c)::value, 0xF, 0xF, false);
+    };
+    // lane bit 0 <-> register bit 0
+    const uint32_t a0 = dpp(x[0], IC<kXor1>{}), a1 = dpp(x[1], IC<kXor1>{});
+    const uint32_t a2 = dpp(x[2], IC<kXor1>{}), a3 = dpp(x[3], IC<kXor1>{});
+    const uint32_t t0 = o1 ? a1 : x[0], t1 = o1 ? x[1] : a0;
+    const uint32_t t2 = o1 ? a3 : x[2], t3 = o1 ? x[3] : a2;
+    // lane bit 1 <-> register bit 1
+    const uint32_t b0 = dpp(t0, IC<kXor2>{}), b1 = dpp(t1, IC<kXor2>{});
+    const uint32_t b2 = dpp(t2, IC<kXor2>{}), b3 = dpp(t3, IC<kXor2>{});
+    return u4v{o2 ? b2 : t0, o2 ? b3 : t1, o2 ? t2 : b0, o2 ? t3 : b1};
 }
 
-// NCH: chunks of K, known at compile time for the common widths (the whole
-// pipeline is then straight-line code and every wait names exactly the loads
-// it needs); 0 when K is known only at run time.
-template <int TT, int RW, int QW, int NCH, bool F32X>
-__global__ __launch_bounds__(kMT) void gemv_mfma_q45_kernel(
+// A copy of v that the compiler cannot prove equal to v.  The swaps below
+// take the same value twice, and the compiler folds a swap of two equal
+// operands into two equal results, which drops the exchange across lanes.
+__device__ __forceinline__ uint32_t opaque_copy(uint32_t v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+// Largest of the non-negative floats with bits v over lanes l, l ^ 16,
+// l ^ 32, l ^ 48 (the four k-groups of one token's block in the A-operand
+// layout).  Swapping a value with itself across halves, then rows, hands
+// each lane its own and its partner's value.  The maximum is taken on the
+// bits (for non-negative floats the same order): compiled as a float
+// maximum, the compiler dropped the swap's second result.
+__device__ __forceinline__ uint32_t max_over_rows(uint32_t v) {
+    auto h = __builtin_amdgcn_permlane32_swap(v, opaque_copy(v), false, false);
+    v = h[0] > h[1] ? h[0] : h[1];
+    auto q = __builtin_amdgcn_permlane16_swap(v, opaque_copy(v), false, false);
+    return q[0] > q[1] ? q[0] : q[1];
+}
+
+// The conversion of convert_item for a lane that holds token t's k-group g of
+// one block (lane 16 g + t): the block maximum combines the four lanes of
+// the token across 16-lane rows.  Same values, same results.
+__device__ __forceinline__ XConv convert_lane(f4g a, f4g b) {
+    float amax = fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
+                       fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
+    const uint32_t mbits = max_over_rows(__builtin_bit_cast(uint32_t, amax));
+    int e = 141 - (int)((mbits >> 23) & 0xFFu);
+    e = e > 126 ? 126 : (e < -126 ? -126 : e);
+    const float up = __builtin_bit_cast(float, (uint32_t)(e + 127) << 23);
+    const float w[8] = {a.x, b.x, a.y, b.y, a.z, b.z, a.w, b.w};
+    h8 hi, lo;
+#pragma unroll
+    for (int q = 0; q < 8; q++) {
+        const float xs = w[q] * up;
+        hi[q] = (_Float16)xs;
+        lo[q] = (_Float16)(xs - (float)hi[q]);
+    }
+    return XConv{__builtin_bit_cast(u4v, hi), __builtin_bit_cast(u4v, lo), -e};
+}
+
+// Sign-extended byte i of w.
+__device__ __forceinline__ int sbyte(uint32_t w, int i) { return ((int32_t)(w << (24 - 8 * i))) >> 24; }
+
+// One wave's operands for one quad (128 values of K) held in registers: the
+// codes of RW row tiles and, per token tile, the 4 blocks of x (high and low
+// parts; fp32 x in two halves before conversion).  Scales and exponents are
+// read from LDS.
+template <int TT, int RW, bool F32X>
+struct QuadOps {
+    u4v wc[RW];
+    u4v x0[4][TT], x1[4][TT];
+};
+
+// NSTEP: quads per wave when K is known at compile time (K = 1024 NSTEP),
+// so that the whole stream is straight-line code; 0 for K known only at run
+// time.
+// MW waves per workgroup, one workgroup per compute unit: MW / 4 waves per
+// SIMD is the occupancy it needs.  Telling the compiler so keeps it from
+// sinking the next quad's loads next to their uses to save registers for an
+// occupancy the grid never reaches.
+template <int MW, int TT, int RW, int NSTEP, bool F32X>
+__global__ __launch_bounds__(MW * kWave) __attribute__((amdgpu_waves_per_eu(MW / 4, MW / 4))) void gemv_mfma_q45_kernel(
         DevPlanes P, int N, int K, const uint8_t* __restrict__ xt, const float* __restrict__ xf,
         int64_t ldx, int M, float* __restrict__ y, int64_t ldy, int accumulate) {
-    constexpr int QPC = kMW * QW;                 // quads per chunk
-    constexpr int NBC = 4 * QPC;                  // blocks per chunk
-    constexpr int XB = TT * NBC * kTileBlockBytes;   // LDS bytes of x per chunk
-    // weight slots in registers: chunks whose loads are in flight or done
-    constexpr int NS = NCH == 0 ? 2 : (NCH < (F32X ? 2 : 3) ? NCH : (F32X ? 2 : 3));
-    constexpr int WLOADS = QW * RW * 2;           // load instructions of one chunk's weights
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int g = lane >> 4, j = lane & 15;
-    const int nq = K / 128, nb = K / 32;
-    const int nchunks = NCH > 0 ? NCH : (nq + QPC - 1) / QPC;
+    const int nq = K / 128;
+    const int nstep = NSTEP > 0 ? NSTEP : (nq + MW - 1) / MW;
     const int row0 = blockIdx.x * (16 * RW);
     const int tt0 = blockIdx.y * TT;               // first token tile
     const int ntt = (M + 15) / 16;
 
-    // weights: one resource per plane; lane (g, j) reads row j's block
-    // 4u + g (16 bytes) and the 4 scales of quad u (8 bytes)
+    // codes: a quad of lanes 4 a + b reads 64 contiguous bytes, blocks
+    // b = 0..3 of quad u of row tau(a) = 4 (a & 3) + (a >> 2) of the row tile
+    // (one cache line access per 4 lanes).  lane_quad_transpose then
+    // quad_transpose (lane bits 1..0 and 5..4 exchanged with the register
+    // index) leave lane 16 g + j with dword g of the 4 blocks of row j.
     const uint64_t nk = (uint64_t)N * (uint64_t)K;
-    const Rsrc rc = make_rsrc(P.p0, nk / 2), rs = make_rsrc(P.p2, nk / 16);
-    uint32_t co[RW], so[RW];
+    const Rsrc rc = make_rsrc(P.p0, nk / 2);
+    uint32_t co[RW];
+    {
+        const int a = lane >> 2, tau = 4 * (a & 3) + (a >> 2);
 #pragma unroll
-    for (int rt = 0; rt < RW; rt++) {
-        const int row = min(row0 + 16 * rt + j, N - 1);
-        co[rt] = (uint32_t)row * (uint32_t)(K / 2) + 16u * g;
-        so[rt] = (uint32_t)row * (uint32_t)(K / 16);
+        for (int rt = 0; rt < RW; rt++) {
+            const int row = min(row0 + 16 * rt + tau, N - 1);
+            co[rt] = (uint32_t)row * (uint32_t)(K / 2) + 16u * (uint32_t)(lane & 3);
+        }
     }
-    u4v wc[NS][QW][RW];
-    u2v ws[NS][QW][RW];
-    auto load_w = [&](auto slot_c, int c) __attribute__((always_inline)) {
-        constexpr int sl = decltype(slot_c)::value;
-#pragma unroll
-        for (int i = 0; i < QW; i++) {
-            const int u = min(c * QPC + wave * QW + i, nq - 1);
-#pragma unroll
-            for (int rt = 0; rt < RW; rt++) {
-                wc[sl][i][rt] = bload<u4v, true>(rc, co[rt], 64u * (uint32_t)u);
-                ws[sl][i][rt] = bload<u2v, true>(rs, so[rt], 8u * (uint32_t)u);
-            }
+    // LDS: the workgroup's scales [16 RW rows][K / 32] (fp16; rows padded by
+    // 8 bytes, so that the 16 rows a wave reads at once sit in different
+    // banks), then (staged x) the token tiles' exponents [TT][K / 128][64
+    // bytes]; both are read many times, so they come in once, in whole lines
+    const int srow = K / 16 + 8;
+    uint8_t* lds_s = lds;
+    uint8_t* lds_e = lds + 16 * RW * srow;
+    {
+        const Rsrc rs = make_rsrc(P.p2, nk / 16);
+        const int per_row = K / 128;                   // 8-byte quads of scales per row
+        for (int c = tid; c < 16 * RW * per_row; c += MW * kWave) {
+            const int r = c / per_row, q = c - r * per_row;
+            const int row = min(row0 + r, N - 1);
+            const u2v v = bload<u2v, false>(rs, 8u * (uint32_t)q, (uint32_t)row * (uint32_t)(K / 16));
+            *(u2v*)(lds_s + r * srow + 8 * q) = v;
         }
-    };
+    }
+    // x: staged, one resource per token tile (lane l reads the 16 bytes at
+    // 16 l of each kilobyte); fp32, lane (g, t) reads token t's 8 values of
+    // k-group g (rows past M repeat row M - 1: their sums are never stored)
+    Rsrc rx[TT];
+    const float* xr[TT];
+#pragma unroll
+    for (int tt = 0; tt < TT; tt++) {
+        const int ttg = min(tt0 + tt, ntt - 1);
+        if constexpr (F32X) {
+            const int m = min(ttg * 16 + j, M - 1);
+            xr[tt] = xf + (int64_t)m * ldx + 8 * g;
+        } else {
+            const int64_t tb = xt_tile_bytes(K);
+            rx[tt] = make_rsrc(xt + (int64_t)ttg * tb, (uint64_t)tb);
+        }
+    }
+    if constexpr (!F32X) {
+        const int per_tile = K / 128 * 4;              // 16-byte pieces of exponents per tile
+#pragma unroll
+        for (int tt = 0; tt < TT; tt++)
+            for (int q = tid; q < per_tile; q += MW * kWave) {
+                const u4v v = bload<u4v, true>(rx[tt], (uint32_t)(K / 32) * kTileBlockBytes + 16u * (uint32_t)q, 0u);
+                *(u4v*)(lds_e + tt * (K / 2) + 16 * q) = v;
+            }
+    }
 
-    // x of chunk c into LDS: [tt][block][2 KB], then [tt][quad][64 B].  The
-    // copy is issued (fill_issue) and completed (fill_finish) in two steps,
-    // so that loads issued between them stay in flight.
-    constexpr int ITEMS = TT * NBC * 64;
-    constexpr int IPT = F32X ? ITEMS / kMT : 1;
-    static_assert(!F32X || ITEMS % kMT == 0, "items per thread");
-    f4g va[IPT], vb[IPT];
-    // Every workgroup reads the same x: each starts at its own piece or
-    // block, so the workgroups of an XCD do not all ask one L2 channel for
-    // the same lines at the same moment.
-    const int rotb = (int)((blockIdx.x * 5u) % (unsigned)NBC);
-    auto blk = [&](int i) __attribute__((always_inline)) { const int b = (i >> 6) % NBC + rotb; return b < NBC ? b : b - NBC; };
-    auto fill_issue = [&](int c) __attribute__((always_inline)) {
-        const int nbc = min(NBC, nb - c * NBC);        // valid blocks of this chunk
-        if constexpr (F32X) {
+    typedef QuadOps<TT, RW, F32X> Q;
+    // quad of step s: the waves interleave, so that two adjacent waves read
+    // the two halves of each 128-byte line of a row at about the same time;
+    // past the end (run-time K only) the last quad is read again and not used
+    auto quad = [&](int s) __attribute__((always_inline)) { return min(wave + MW * s, nq - 1); };
+    auto load_w = [&](Q& q, int u) __attribute__((always_inline)) {
 #pragma unroll
-            for (int s = 0; s < IPT; s++) {
-                const int i = s * kMT + tid;
-                const int gg = i & 3, t = (i >> 2) & 15, b = blk(i), tt = (i >> 6) / NBC;
-                const int m = (tt0 + tt) * 16 + t;
-                va[s] = f4g{0.f, 0.f, 0.f, 0.f};
-                vb[s] = va[s];
-                if (m < M && b < nbc) {
-                    const f4g* src = (const f4g*)(xf + (int64_t)m * ldx + (int64_t)(c * NBC + b) * 32 + 8 * gg);
-                    va[s] = src[0];
-                    vb[s] = src[1];
-                }
-            }
-        } else {
-            // copies of 1 KB pieces (one per wave instruction), straight into LDS
-            const int pieces_x = nbc * 2;                  // per tile
-            const int pieces_e = (nbc * 16 + 1023) / 1024;   // exponent bytes per tile: 16 per block
-            const int npc = TT * (pieces_x + pieces_e);
-            const int rot = (int)((blockIdx.x * 37u) % (unsigned)npc);
-#pragma unroll 1
-            for (int p0 = wave; p0 < npc; p0 += kMW) {
-                const int p = p0 + rot < npc ? p0 + rot : p0 + rot - npc;
-                const int tt = p / (pieces_x + pieces_e), q = p % (pieces_x + pieces_e);
-                const int ttg = min(tt0 + tt, ntt - 1);
-                const uint8_t* tile = xt + (int64_t)ttg * xt_tile_bytes(K);
-                if (q < pieces_x) {
-                    __builtin_amdgcn_global_load_lds((gvoid)(tile + (int64_t)(c * NBC) * kTileBlockBytes + q * 1024 + 16 * lane),
-                                                     (lvoid)(lds + tt * (NBC * kTileBlockBytes) + q * 1024), 16, 0, 0);
-                } else {
-                    const int e0 = (q - pieces_x) * 1024 + 16 * lane;   // byte within the chunk's exponents
-                    if (e0 < nbc * 16)
-                        __builtin_amdgcn_global_load_lds((gvoid)(tile + (int64_t)nb * kTileBlockBytes + (int64_t)(c * NBC) * 16 + e0),
-                                                         (lvoid)(lds + XB + tt * (NBC * 16) + (q - pieces_x) * 1024), 16, 0, 0);
-                }
+        for (int rt = 0; rt < RW; rt++) q.wc[rt] = bload<u4v, true>(rc, co[rt], 64u * (uint32_t)u);
+    };
+    auto load_x = [&](Q& q, int b, int u) __attribute__((always_inline)) {
+#pragma unroll
+        for (int tt = 0; tt < TT; tt++) {
+            if constexpr (F32X) {
+                const f4g* src = (const f4g*)(xr[tt] + 32 * (4 * u + b));
+                q.x0[b][tt] = __builtin_bit_cast(u4v, src[0]);
+                q.x1[b][tt] = __builtin_bit_cast(u4v, src[1]);
+            } else {
+                const uint32_t off = (uint32_t)(4 * u + b) * kTileBlockBytes + 16u * lane;
+                q.x0[b][tt] = bload<u4v, true>(rx[tt], off, 0u);
+                q.x1[b][tt] = bload<u4v, true>(rx[tt], off + 1024u, 0u);
             }
         }
-    };
-    // PEND: weight loads issued after fill_issue that may stay in flight.
-    auto fill_finish = [&](auto pend_c) __attribute__((always_inline)) {
-        constexpr int PEND = decltype(pend_c)::value;
-        if constexpr (F32X) {
-#pragma unroll
-            for (int s = 0; s < IPT; s++) {
-                const int i = s * kMT + tid;
-                const int gg = i & 3, t = (i >> 2) & 15, b = blk(i), tt = (i >> 6) / NBC;
-                const XConv v = convert_item(va[s], vb[s]);
-                uint8_t* tile = lds + tt * (NBC * kTileBlockBytes);
-                *(u4v*)(tile + xt_slot(b, gg, t)) = v.hi;
-                *(u4v*)(tile + xt_slot(b, gg, t) + 1024) = v.lo;
-                if (gg == 0) lds[XB + tt * (NBC * 16) + xt_exp_byte(b, t)] = (uint8_t)(int8_t)v.ne;
-            }
-        } else {
-            wait_vm<PEND>();
-        }
-    };
-    auto fill = [&](int c) __attribute__((always_inline)) {
-        fill_issue(c);
-        fill_finish(IC<0>{});
     };
 
     f4v acc[RW][TT];
@@ -311,101 +357,82 @@ __global__ __launch_bounds__(kMT) void gemv_mfma_q45_kernel(
         for (int tt = 0; tt < TT; tt++) acc[rt][tt] = f4v{0.f, 0.f, 0.f, 0.f};
     const f4v zero = {0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](auto slot_c, int c) __attribute__((always_inline)) {
-        constexpr int sl = decltype(slot_c)::value;
-        const int nqc = NCH > 0 ? QPC : min(QPC, nq - c * QPC);   // quads of this chunk
+    // One step: multiply quad q (in cur) and load quad un into cur: the
+    // weights and exponents first (their registers are free once copied),
+    // then each block of x right after the same block of cur is used.
+    // LOAD false: the last step of a compile-time stream loads nothing.
+    auto step = [&](auto load_c, Q& cur, bool use, int uc, int un) __attribute__((always_inline)) {
+        constexpr bool LOAD = decltype(load_c)::value;
+        u4v cb[RW];
+        u2v sc[RW];
 #pragma unroll
-        for (int i = 0; i < QW; i++) {
-            const int ql = wave * QW + i;                  // quad within the chunk
-            if (NCH == 0 && ql >= nqc) break;              // the same in every lane
-            u4v cb[RW];
+        for (int rt = 0; rt < RW; rt++) {
+            cb[rt] = lane_quad_transpose(quad_transpose(cur.wc[rt]), lane);
+            sc[rt] = *(const u2v*)(lds_s + (16 * rt + j) * srow + 8 * uc);
+        }
+        u4v ed[TT];
+        if constexpr (!F32X) {
 #pragma unroll
-            for (int rt = 0; rt < RW; rt++) cb[rt] = quad_transpose(wc[sl][i][rt]);
-            u4v ed[TT];
+            for (int tt = 0; tt < TT; tt++) ed[tt] = *(const u4v*)(lds_e + tt * (K / 2) + 64 * uc + 16 * g);
+        }
+        if constexpr (LOAD) load_w(cur, un);
 #pragma unroll
-            for (int tt = 0; tt < TT; tt++) ed[tt] = *(const u4v*)(lds + XB + tt * (NBC * 16) + ql * 64 + 16 * g);
+        for (int b = 0; b < 4; b++) {
+            h8 xh[TT], xl[TT];
+            int ne[TT][4];
 #pragma unroll
-            for (int b = 0; b < 4; b++) {
-                const int bl = 4 * ql + b;
-                h8 xh[TT], xl[TT];
-                int ne[TT][4];
+            for (int tt = 0; tt < TT; tt++) {
+                if constexpr (F32X) {
+                    const XConv v = convert_lane(__builtin_bit_cast(f4g, cur.x0[b][tt]),
+                                                 __builtin_bit_cast(f4g, cur.x1[b][tt]));
+                    xh[tt] = __builtin_bit_cast(h8, v.hi);
+                    xl[tt] = __builtin_bit_cast(h8, v.lo);
+                    // -e of tokens 4 g + r sit in lanes 4 g + r
+#pragma unroll
+                    for (int r = 0; r < 4; r++) ne[tt][r] = __shfl(v.ne, 4 * g + r, kWave);
+                } else {
+                    xh[tt] = __builtin_bit_cast(h8, cur.x0[b][tt]);
+                    xl[tt] = __builtin_bit_cast(h8, cur.x1[b][tt]);
+#pragma unroll
+                    for (int r = 0; r < 4; r++) ne[tt][r] = sbyte(ed[tt][b], r);
+                }
+            }
+            if constexpr (LOAD) load_x(cur, b, un);
+            if (!use) continue;                        // the same in every lane
+#pragma unroll
+            for (int rt = 0; rt < RW; rt++) {
+                const h8 bw = codes_to_b(cb[rt][b]);
+                const float sv = h2f(sc[rt][b >> 1] >> (16 * (b & 1)));
 #pragma unroll
                 for (int tt = 0; tt < TT; tt++) {
-                    const uint8_t* xb = lds + tt * (NBC * kTileBlockBytes) + bl * kTileBlockBytes + 16 * lane;
-                    xh[tt] = __builtin_bit_cast(h8, *(const u4v*)xb);
-                    xl[tt] = __builtin_bit_cast(h8, *(const u4v*)(xb + 1024));
+                    f4v d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh[tt], bw, zero, 0, 0, 0);
+                    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl[tt], bw, d, 0, 0, 0);
 #pragma unroll
-                    for (int r = 0; r < 4; r++) ne[tt][r] = ((int32_t)(ed[tt][b] << (24 - 8 * r))) >> 24;
-                }
-#pragma unroll
-                for (int rt = 0; rt < RW; rt++) {
-                    const h8 bw = codes_to_b(cb[rt][b]);
-                    const float sv = h2f(ws[sl][i][rt][b >> 1] >> (16 * (b & 1)));
-#pragma unroll
-                    for (int tt = 0; tt < TT; tt++) {
-                        f4v d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh[tt], bw, zero, 0, 0, 0);
-                        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl[tt], bw, d, 0, 0, 0);
-#pragma unroll
-                        for (int r = 0; r < 4; r++)
-                            acc[rt][tt][r] = fmaf(sv, __builtin_ldexpf(d[r], ne[tt][r]), acc[rt][tt][r]);
-                    }
+                    for (int r = 0; r < 4; r++)
+                        acc[rt][tt][r] = fmaf(sv, __builtin_ldexpf(d[r], ne[tt][r]), acc[rt][tt][r]);
                 }
             }
         }
     };
 
-    if constexpr (NCH > 0) {
-        // straight-line pipeline: NS chunks of weights in flight from the
-        // start; after chunk c computes, chunk c + 1's x is copied in and
-        // the slot chunk c used refills with chunk c + NS, whose loads go out
-        // after the copy so that completing the copy does not wait for them
+    Q cur;
+    load_w(cur, quad(0));
 #pragma unroll
-        for (int c = 0; c < NS; c++) {
-            if (c == 0) load_w(IC<0>{}, 0);
-            if (c == 1) load_w(IC<1 % NS>{}, 1);
-            if (c == 2) load_w(IC<2 % NS>{}, 2);
-        }
-        fill(0);
-        __syncthreads();
-        static_for<0, NCH>([&](auto cc) __attribute__((always_inline)) {
-            constexpr int c = decltype(cc)::value;
-            compute(IC<c % NS>{}, c);
-            if constexpr (c + 1 < NCH) {
-                __syncthreads();
-                fill_issue(c + 1);
-                if constexpr (c + NS < NCH) {
-                    load_w(IC<c % NS>{}, c + NS);
-                    fill_finish(IC<WLOADS>{});
-                } else {
-                    fill_finish(IC<0>{});
-                }
-                __syncthreads();
-            }
+    for (int b = 0; b < 4; b++) load_x(cur, b, quad(0));
+    __syncthreads();                                       // scales and exponents in LDS
+    if constexpr (NSTEP > 0) {
+        // every wave has exactly NSTEP quads
+        static_for<0, NSTEP>([&](auto ss) __attribute__((always_inline)) {
+            constexpr int s = decltype(ss)::value;
+            step(IC<(s + 1 < NSTEP)>{}, cur, true, quad(s), quad(s + 1 < NSTEP ? s + 1 : s));
         });
     } else {
-        // K known only at run time: two slots, chunk c + 1's weights load
-        // while chunk c computes
-        load_w(IC<0>{}, 0);
-        fill(0);
-        __syncthreads();
 #pragma unroll 1
-        for (int c = 0; c < nchunks; c += 2) {
-            if (c + 1 < nchunks) load_w(IC<1>{}, c + 1);
-            compute(IC<0>{}, c);
-            if (c + 1 >= nchunks) break;
-            __syncthreads();
-            fill(c + 1);
-            __syncthreads();
-            if (c + 2 < nchunks) load_w(IC<0>{}, c + 2);
-            compute(IC<1>{}, c + 1);
-            if (c + 2 >= nchunks) break;
-            __syncthreads();
-            fill(c + 2);
-            __syncthreads();
-        }
+        for (int s = 0; s < nstep; s++) step(IC<1>{}, cur, wave + MW * s < nq, quad(s), quad(s + 1));
     }
 
-    // the 8 waves' partial tiles, added in wave order
+    // the waves' partial tiles, added in wave order (the LDS of the scales
+    // is reused once every wave is done with it)
     __syncthreads();
     f4v* red = (f4v*)lds;                                  // [wave][rt][tt][lane]
 #pragma unroll
@@ -414,11 +441,11 @@ __global__ __launch_bounds__(kMT) void gemv_mfma_q45_kernel(
         for (int tt = 0; tt < TT; tt++) red[((wave * RW + rt) * TT + tt) * kWave + lane] = acc[rt][tt];
     __syncthreads();
 #pragma unroll 1
-    for (int u = wave; u < RW * TT; u += kMW) {
+    for (int u = wave; u < RW * TT; u += MW) {
         const int rt = u / TT, tt = u % TT;
         f4v s = red[(rt * TT + tt) * kWave + lane];
 #pragma unroll
-        for (int w = 1; w < kMW; w++) {
+        for (int w = 1; w < MW; w++) {
             const f4v o = red[((w * RW + rt) * TT + tt) * kWave + lane];
             s += o;
         }
@@ -436,35 +463,53 @@ __global__ __launch_bounds__(kMT) void gemv_mfma_q45_kernel(
     }
 }
 
-template <int TT, int RW, int QW, int NCH, bool F32X>
+// LDS the stream fills: scales of 16 RW padded rows, and the exponents of
+// TT token tiles for staged x.
+static size_t mfma_fill_lds(int RW, int TT, int64_t K, bool f32x) {
+    return (size_t)16 * RW * (K / 16 + 8) + (f32x ? 0 : (size_t)TT * K / 2);
+}
+constexpr size_t kMaxLds = 160 * 1024;
+
+template <int MW, int TT, int RW, int NSTEP, bool F32X>
 static hipError_t launch_k(DevPlanes P, int64_t N, int64_t K, const uint8_t* xt, const float* xf,
                            int64_t ldx, int64_t M, float* y, int64_t ldy, int accumulate,
                            hipStream_t stream) {
-    constexpr int NBC = 4 * kMW * QW;
-    constexpr size_t xl = (size_t)TT * NBC * kTileBlockBytes + (size_t)TT * NBC * 16;
-    constexpr size_t rl = (size_t)kMW * RW * TT * kWave * 16;
-    constexpr size_t lds = xl > rl ? xl : rl;
-    auto kern = gemv_mfma_q45_kernel<TT, RW, QW, NCH, F32X>;
-    if (hipError_t e = ensure_lds<gemv_mfma_q45_kernel<TT, RW, QW, NCH, F32X>>(lds)) return e;
+    constexpr size_t red = (size_t)MW * RW * TT * kWave * 16;
+    const size_t fill = mfma_fill_lds(RW, TT, K, F32X);
+    const size_t lds = fill > red ? fill : red;
+    auto kern = gemv_mfma_q45_kernel<MW, TT, RW, NSTEP, F32X>;
+    if (hipError_t e = ensure_lds<gemv_mfma_q45_kernel<MW, TT, RW, NSTEP, F32X>>(lds)) return e;
     const int64_t ntt = (M + 15) / 16;
     const dim3 grid((unsigned)((N + 16 * RW - 1) / (16 * RW)), (unsigned)((ntt + TT - 1) / TT));
-    hipLaunchKernelGGL(kern, grid, dim3(kMT), lds, stream, P, (int)N, (int)K, xt, xf, ldx, (int)M, y,
-                       ldy, accumulate);
+    hipLaunchKernelGGL(kern, grid, dim3(MW * kWave), lds, stream, P, (int)N, (int)K, xt, xf, ldx,
+                       (int)M, y, ldy, accumulate);
     return hipGetLastError();
 }
 
+// Waves per workgroup: 16 for one token tile (4 per SIMD, twice the loads in
+// flight of 8) where the registers fit 128 without spilling (up to 3 row
+// tiles, 4 at K = 4096), else 8 (2 per SIMD); MBQ_MFMA_MW = 8 forces 8
+// (tuning).
 template <int TT, int RW, bool F32X>
 static hipError_t launch_rw(DevPlanes P, int64_t N, int64_t K, const uint8_t* xt, const float* xf,
                             int64_t ldx, int64_t M, float* y, int64_t ldy, int accumulate,
                             hipStream_t s) {
-    constexpr int QW = TT == 1 ? 2 : 1;    // chunk of x: 128 KB of LDS
-    constexpr int KC = kMW * QW * 128;     // values per chunk
-    // fp32 x keeps the run-time loop: unrolled, its conversion registers and
-    // the weight slots outgrow the register file
-    if (F32X) return launch_k<TT, RW, QW, 0, F32X>(P, N, K, xt, xf, ldx, M, y, ldy, accumulate, s);
-    if (K == 4096) return launch_k<TT, RW, QW, 4096 / KC, F32X>(P, N, K, xt, xf, ldx, M, y, ldy, accumulate, s);
-    if (K == 12288) return launch_k<TT, RW, QW, 12288 / KC, F32X>(P, N, K, xt, xf, ldx, M, y, ldy, accumulate, s);
-    return launch_k<TT, RW, QW, 0, F32X>(P, N, K, xt, xf, ldx, M, y, ldy, accumulate, s);
+    if constexpr (TT == 1) {
+        bool mw16 = RW <= 3 || K == 4096;
+        if (const char* e = tuning_var("MBQ_MFMA_MW")) mw16 = mw16 && atoi(e) != 8;
+        if (mw16) {
+            constexpr int MW = 16, KS = MW * 128;      // values per step of the workgroup
+            if (K == 4096) return launch_k<MW, TT, RW, 4096 / KS, F32X>(P, N, K, xt, xf, ldx, M, y, ldy, accumulate, s);
+            if constexpr (RW <= 3) {
+                if (K == 12288) return launch_k<MW, TT, RW, 12288 / KS, F32X>(P, N, K, xt, xf, ldx, M, y, ldy, accumulate, s);
+                return launch_k<MW, TT, RW, 0, F32X>(P, N, K, xt, xf, ldx, M, y, ldy, accumulate, s);
+            }
+        }
+    }
+    constexpr int MW = 8, KS = MW * 128;
+    if (K == 4096) return launch_k<MW, TT, RW, 4096 / KS, F32X>(P, N, K, xt, xf, ldx, M, y, ldy, accumulate, s);
+    if (K == 12288) return launch_k<MW, TT, RW, 12288 / KS, F32X>(P, N, K, xt, xf, ldx, M, y, ldy, accumulate, s);
+    return launch_k<MW, TT, RW, 0, F32X>(P, N, K, xt, xf, ldx, M, y, ldy, accumulate, s);
 }
 
 // Row tiles per workgroup: about 256 workgroups per token-tile group (one
@@ -475,6 +520,8 @@ static hipError_t launch_tt(DevPlanes P, int64_t N, int64_t K, const uint8_t* xt
                             hipStream_t s) {
     int64_t rw = (N + 16 * 256 - 1) / (16 * 256);
     if (const char* e = tuning_var("MBQ_MFMA_RW")) rw = atoi(e);
+    rw = rw < 1 ? 1 : (rw > 4 ? 4 : rw);
+    while (rw > 1 && mfma_fill_lds((int)rw, TT, K, F32X) > kMaxLds) rw--;   // the longest rows
     switch (rw <= 1 ? 1 : rw == 2 ? 2 : rw == 3 ? 3 : 4) {
     case 1: return launch_rw<TT, 1, F32X>(P, N, K, xt, xf, ldx, M, y, ldy, accumulate, s);
     case 2: return launch_rw<TT, 2, F32X>(P, N, K, xt, xf, ldx, M, y, ldy, accumulate, s);

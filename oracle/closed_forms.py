@@ -29,9 +29,9 @@ def weight_bytes(fmt: int, n_weights: int) -> Fraction:
 
 
 def sums_per_byte(bits_per_weight: float) -> float:
-    """Arithmetic intensity of one decode token: each weight is read once and
-    used for two sums (one multiply, one add) -> 2 / (w/8) sums per byte
-    ([roofline-holds] "The Math")."""
+    """Arithmetic intensity of one decode token: a weight of w bits costs w/8
+    bytes of traffic and contributes a multiply and an add, so 2 / (w/8)
+    operations per byte ([roofline-holds] "The Math")."""
     return 2.0 / (bits_per_weight / 8.0)
 
 
@@ -69,7 +69,8 @@ def bytes_in_flight(bytes_per_s: float, wait_s: float) -> float:
 # The per-token table census of the 36-layer model the pages measure
 # ([roofline-holds] "The Math": gate and up 12288 x 4096, attention 4096 x 4096
 # plus key and value 1024 x 4096, down 4096 x 12288, vocabulary 151936 x 4096;
-# gate, up and attention 4-bit; half the down tables and the vocabulary 6-bit).
+# 4-bit for gate, up and attention; 6-bit for the vocabulary and for the down
+# table of every other layer).
 # ---------------------------------------------------------------------------
 
 LAYERS = 36

@@ -30,7 +30,7 @@ def _declared_symbols():
 
 def test_library_exports_every_declared_symbol():
     declared = _declared_symbols()
-    assert len(declared) == 30
+    assert len(declared) == 31
     assert sorted(_lib.EXPORTS) == declared
     lib = ctypes.CDLL(_lib.LIB_PATH)
     for name in declared:
@@ -337,3 +337,33 @@ def test_one_hip_runtime_in_the_process():
     with open("/proc/self/maps") as fh:
         libs = set(re.findall(r"\S*libamdhip64\S*", fh.read()))
     assert len(libs) == 1, libs
+
+
+def _quantize(fmt=1, w=BASE, N=4, K=256, ldw=None, planes=None):
+    if planes is None:
+        ok = 0 <= fmt <= 3 and N >= 0 and K % (256 if fmt == 2 else 32) == 0
+        sz = mbq.plane_sizes(fmt, N, K) if ok else [1, 1, 1, 1]
+        planes = [BASE + 0x1000000 * (i + 1) if sz[i] else None for i in range(4)]
+    arr = (ctypes.c_void_p * 4)(*planes)
+    return L.mbq_quantize(fmt, w, N, K, K if ldw is None else ldw, arr, None)
+
+
+def test_quantize_argument_checks():
+    assert _quantize(fmt=9) == _lib.EINVAL
+    assert _quantize(N=-1) == _lib.EINVAL
+    assert _quantize(K=48) == _lib.EINVAL                       # not a block multiple
+    assert _quantize(fmt=2, K=128) == _lib.EINVAL
+    assert _quantize(N=0) == _lib.OK and _quantize(K=0) == _lib.OK   # empty: nothing enqueued
+    assert _quantize(ldw=100) == _lib.EINVAL                    # ldw < K
+    assert _quantize(w=0) == _lib.EINVAL
+    assert _quantize(w=BASE + 4) == _lib.EALIGN
+    assert _quantize(ldw=258) == _lib.EALIGN                    # ldw % 4
+    assert _quantize(fmt=0, K=12) == _lib.EUNSUPPORTED          # BF16 needs K % 8
+    assert _quantize(planes=[BASE + 0x1000000, None, None, None]) == _lib.EINVAL   # Q45 needs scales
+    assert _quantize(planes=[BASE + 0x1000008, None, BASE + 0x3000000, None]) == _lib.EALIGN
+    assert _quantize(planes=[BASE + 0x1000000, None, BASE + 0x3000002, None]) == _lib.EALIGN
+    # a plane inside w's rows
+    assert _quantize(planes=[BASE + 0x100, None, BASE + 0x3000000, None]) == _lib.EINVAL
+    # planes overlapping each other
+    assert _quantize(planes=[BASE + 0x1000000, None, BASE + 0x1000010, None]) == _lib.EINVAL
+    assert _quantize(fmt=2, planes=[BASE + 0x1000000, None, BASE + 0x3000000, BASE + 0x4000000]) == _lib.EINVAL
