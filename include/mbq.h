@@ -363,6 +363,31 @@ int mbq_silu_mul(const float* g, const float* u, int64_t n, float* out, void* st
 int mbq_dequant_f32(const mbq_qweight* W, float* w_out, void* stream);
 int mbq_unpack_codes(const mbq_qweight* W, uint8_t* codes_out, void* stream);
 
+/* One new token's attention over an fp16 KV cache ([roofline-holds] "Said
+ * before the run": each token also reads the keys and values of the loaded
+ * conversation, 75.5 MB at 512 positions for the 36-layer model, i.e. 2-byte
+ * values, 1024 per position and layer for each of K and V).  The pages name
+ * no positional encoding or normalisation; the reading here is plain scaled
+ * dot-product attention with grouped key/value heads:
+ *   query head h (0 <= h < n_heads) reads key/value head g = h / G,
+ *   G = n_heads / n_kv_heads;
+ *   s_t = q_h . k_{t,g} / sqrt(head_dim);  p_t = exp(s_t - max_t s) / sum;
+ *   out_h = sum_t p_t v_{t,g},  t = 0 .. T-1.
+ * q: device fp32 [n_heads][head_dim]; k_cache, v_cache: device fp16 bit
+ * patterns, position t's row at t * ld elements, head g at g * head_dim
+ * within it; out: device fp32 [n_heads][head_dim].  workspace: device,
+ * caller-owned, at least mbq_attention_workspace_bytes (partial maxima, sums
+ * and value sums per chunk of positions; contents need no initialisation and
+ * are meaningless afterwards).  Arithmetic in fp32.  Every pointer 16-byte
+ * aligned, ld a multiple of 8 (MBQ_EALIGN).  MBQ_EINVAL for T < 1, ld <
+ * n_kv_heads * head_dim, n_heads not a multiple of n_kv_heads, NULL or
+ * overlapping buffers, a short workspace; MBQ_EUNSUPPORTED for head_dim !=
+ * 128, G not in {1, 2, 4, 8}, T > 2^26. */
+int mbq_attention_workspace_bytes(int64_t T, int n_heads, int n_kv_heads, int head_dim, size_t* bytes);
+int mbq_attention_decode(const float* q, const void* k_cache, const void* v_cache, int64_t T,
+                         int64_t ld, int n_heads, int n_kv_heads, int head_dim, float* out,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
 /* Device quantizer: fp32 weights w [N][ldw] (device, 16-byte aligned, ldw a
  * multiple of 4, ldw >= K) -> the planes of format fmt (device pointers in
  * planes[0..3], sizes and alignment as for mbq_qweight; NULL where

@@ -268,6 +268,31 @@ def quantize(fmt: int, w, out: "QWeight | None" = None, stream=None) -> "QWeight
     return out
 
 
+def attention_workspace_bytes(T: int, n_heads: int, n_kv_heads: int, head_dim: int = 128) -> int:
+    out = ctypes.c_size_t()
+    check(lib.mbq_attention_workspace_bytes(T, n_heads, n_kv_heads, head_dim, ctypes.byref(out)))
+    return int(out.value)
+
+
+def attention_decode(q, k_cache, v_cache, n_heads: int, n_kv_heads: int, T: int | None = None,
+                     out=None, workspace=None, stream=None):
+    """One token's attention over an fp16 KV cache (mbq_attention_decode).
+    q: fp32 cuda [n_heads * 128]; k_cache, v_cache: fp16 (or int16) cuda
+    [capacity, >= n_kv_heads * 128] with the same row stride; T positions."""
+    import torch
+    T = k_cache.shape[0] if T is None else int(T)
+    if out is None:
+        out = torch.empty(n_heads * 128, dtype=torch.float32, device=q.device)
+    need = attention_workspace_bytes(T, n_heads, n_kv_heads)
+    if workspace is None:
+        workspace = torch.empty((need + 15) // 16 * 4, dtype=torch.float32, device=q.device)
+    assert k_cache.stride(0) == v_cache.stride(0)
+    check(lib.mbq_attention_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), T, k_cache.stride(0),
+                                   n_heads, n_kv_heads, 128, _ptr(out), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
 def probe_read(buf, sink, stream=None):
     check(lib.mbq_probe_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
                              _stream(stream)))

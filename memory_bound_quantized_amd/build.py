@@ -24,7 +24,7 @@ LIB = os.path.join(PKG, "libmbq.so")
 ARCH = "gfx950"
 
 SOURCES = ["abi.cpp", "gemv_m1.hip", "gemv_smallm.hip", "gemv_mfma.hip", "stage.hip", "decode_persistent.hip",
-           "norms.hip", "quantize.hip",
+           "norms.hip", "quantize.hip", "attention.hip",
            "exports.hip"]
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH, "-Wall", "-Wno-unused-function",

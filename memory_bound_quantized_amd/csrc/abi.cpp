@@ -913,6 +913,54 @@ int mbq_quantize(int fmt, const float* w, int64_t N, int64_t K, int64_t ldw, voi
     return hip_status(mbq::launch_quantize(fmt, w, ldw, N, K, out, (hipStream_t)stream), fn);
 }
 
+// Shape checks shared by the two attention entry points.
+static int check_attention_shape(int64_t T, int n_heads, int n_kv, int head_dim, const char* fn) {
+    if (T < 1) return fail(MBQ_EINVAL, "%s: T must be at least 1 (softmax over no position)", fn);
+    if (n_heads < 1 || n_kv < 1 || n_heads % n_kv)
+        return fail(MBQ_EINVAL, "%s: n_heads must be a positive multiple of n_kv_heads", fn);
+    if (head_dim != mbq::kAttD)
+        return fail(MBQ_EUNSUPPORTED, "%s: head_dim %d (kernels for %d only)", fn, head_dim, mbq::kAttD);
+    const int G = n_heads / n_kv;
+    if (G != 1 && G != 2 && G != 4 && G != 8)
+        return fail(MBQ_EUNSUPPORTED, "%s: %d query heads per key/value head (1, 2, 4 or 8)", fn, G);
+    if (T > ((int64_t)1 << 26) || n_kv > 65535 || n_heads > 65535)
+        return fail(MBQ_EUNSUPPORTED, "%s: T above 2^26 or more than 65535 heads", fn);
+    return MBQ_OK;
+}
+
+int mbq_attention_workspace_bytes(int64_t T, int n_heads, int n_kv_heads, int head_dim, size_t* bytes) {
+    const char* fn = "mbq_attention_workspace_bytes";
+    if (!bytes) return fail(MBQ_EINVAL, "%s: bytes is NULL", fn);
+    if (int rc = check_attention_shape(T, n_heads, n_kv_heads, head_dim, fn)) return rc;
+    *bytes = mbq::attention_workspace_bytes(T, n_heads, n_kv_heads);
+    return ok();
+}
+
+int mbq_attention_decode(const float* q, const void* k_cache, const void* v_cache, int64_t T,
+                         int64_t ld, int n_heads, int n_kv_heads, int head_dim, float* out,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "mbq_attention_decode";
+    if (int rc = check_attention_shape(T, n_heads, n_kv_heads, head_dim, fn)) return rc;
+    const int64_t width = (int64_t)n_kv_heads * head_dim;
+    if (ld < width) return fail(MBQ_EINVAL, "%s: ld < n_kv_heads * head_dim", fn);
+    if (!q || !k_cache || !v_cache || !out || !workspace) return fail(MBQ_EINVAL, "%s: NULL pointer", fn);
+    if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        !aligned(workspace, 16) || ld % 8)
+        return fail(MBQ_EALIGN, "%s: buffers must be 16-byte aligned and ld a multiple of 8", fn);
+    const size_t need = mbq::attention_workspace_bytes(T, n_heads, n_kv_heads);
+    if (workspace_bytes < need)
+        return fail(MBQ_EINVAL, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, need);
+    const size_t qb = (size_t)n_heads * head_dim * 4, cb = (size_t)((T - 1) * ld + width) * 2;
+    if (overlaps(out, qb, q, qb) || overlaps(out, qb, k_cache, cb) || overlaps(out, qb, v_cache, cb) ||
+        overlaps(out, qb, workspace, need) || overlaps(workspace, need, q, qb) ||
+        overlaps(workspace, need, k_cache, cb) || overlaps(workspace, need, v_cache, cb))
+        return fail(MBQ_EINVAL, "%s: out or workspace overlaps another buffer", fn);
+    return hip_status(mbq::launch_attention_decode(q, (const uint16_t*)k_cache, (const uint16_t*)v_cache,
+                                                   T, ld, n_heads, n_kv_heads, out, (float*)workspace,
+                                                   (hipStream_t)stream),
+                      fn);
+}
+
 int mbq_probe_read(const void* buf, size_t bytes, float* sink, void* stream) {
     const char* fn = "mbq_probe_read";
     if (!buf || !sink) return fail(MBQ_EINVAL, "%s: NULL pointer", fn);

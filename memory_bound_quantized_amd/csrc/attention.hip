@@ -1,0 +1,271 @@
+// attention.hip -- one new token attending over an fp16 KV cache.
+//
+// With the conversation loaded, every decode token also reads its keys and
+// values ([roofline-holds] "Said before the run": 75.5 MB per token at 512
+// positions for the 36-layer model, i.e. 2-byte values, 1024 per position and
+// layer for each of K and V).  The reading this library takes (plain scaled
+// dot-product attention; the pages name no positional encoding): query head h
+// reads key/value head h / G (G query heads per key/value head),
+//   s_t = q_h . k_t / sqrt(d),  p_t = exp(s_t - max s) / sum exp(s - max s),
+//   out_h = sum_t p_t v_t.
+// Like the weight stream it is a read of bytes used once, so it is split the
+// way long decode attention is split on GPUs with many compute units: the
+// positions are cut into chunks, each workgroup owns one key/value head and
+// one chunk and leaves (max, sum of exponentials, weighted sum of values)
+// for its G query heads, and a second launch combines the chunks.
+//
+// Layout: lane 16 p + i of a wave reads 16 bytes (dims 8 i .. 8 i + 7) of
+// position p of a group of 4, so a load instruction covers 4 positions' 256
+// bytes of one head, whole lines.  Scores are kept in base 2: q is scaled by
+// log2(e) / sqrt(d) once, and exp2 is taken of score differences.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace mbq {
+
+namespace {
+
+typedef float af4 __attribute__((ext_vector_type(4)));
+typedef uint32_t au4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+
+// Sum over the 16 lanes of each row (every lane of the row gets it).
+__device__ __forceinline__ float row_sum16(float v) {
+    v = dpp_add<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]
+    v = dpp_add<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]
+    v = dpp_add<0x141, 0xF>(v);   // row_half_mirror
+    v = dpp_add<0x140, 0xF>(v);   // row_mirror
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+// The 8 halves of a 16-byte load as floats (exact).
+__device__ __forceinline__ void halves(au4 w, float* f) {
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        f[2 * e] = h2f(w[e]);
+        f[2 * e + 1] = h2f(w[e] >> 16);
+    }
+}
+
+}  // namespace
+
+// Positions per workgroup: a multiple of 16 (4 waves x 4 positions), at
+// most 16 groups of 4 per wave (kMaxGroups) so that a wave holds all its
+// keys and values in registers, and otherwise T / 16, so that up to 4096
+// positions the combine step merges at most 16 chunks per head.
+constexpr int kMaxGroups = 16;
+int attention_chunk(int64_t T, int n_kv) {
+    (void)n_kv;
+    int64_t c = (T + 15) / 16;
+    c = (c + 15) / 16 * 16;
+    const int cmax = 16 * kMaxGroups;
+    return (int)(c < 16 ? 16 : (c > cmax ? cmax : c));
+}
+
+size_t attention_workspace_bytes(int64_t T, int n_heads, int n_kv) {
+    const int64_t nch = (T + attention_chunk(T, n_kv) - 1) / attention_chunk(T, n_kv);
+    return (size_t)n_heads * (size_t)nch * kAttRecord * sizeof(float);
+}
+
+// Workgroup (kv head, chunk): the chunk's partial record for each of the G
+// query heads of the group, at ws[((kv * nch) + chunk) * G + hl] (records of
+// kAttRecord floats: m, l, then d values of o; m and l in base 2).  Wave w
+// owns the groups of 4 positions w, w + 4, ...: it issues all their key and
+// value loads first, so the chunk costs one memory round trip.
+template <int G>
+__global__ __launch_bounds__(kThreads) void attn_partial_kernel(const float* __restrict__ q,
+                                                                const uint16_t* __restrict__ kc,
+                                                                const uint16_t* __restrict__ vc,
+                                                                int64_t T, int64_t ld, int C,
+                                                                float qscale, float* __restrict__ ws) {
+    extern __shared__ __attribute__((aligned(16))) float alds[];
+    float* sc = alds;                               // [G][C] scores, then weights
+    float* red = alds + G * C;                      // [16][G][d] partial outputs
+    float* mls = red + 16 * G * kAttD;              // [G][2] max and sum
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int p = lane >> 4, i = lane & 15;
+    const int kv = blockIdx.x, chunk = blockIdx.y, nch = gridDim.y;
+    const int64_t t0 = (int64_t)chunk * C;
+    const int tn = (int)min((int64_t)C, T - t0);    // >= 1
+    const int64_t hoff = (int64_t)kv * kAttD + 8 * i;
+
+    // keys and values of the wave's groups (positions past the chunk repeat
+    // its last one and are masked)
+    au4 kr[kMaxGroups], vr[kMaxGroups];
+#pragma unroll
+    for (int jg = 0; jg < kMaxGroups; jg++) {
+        const int base = 4 * (wave + kWaves * jg);
+        if (base < tn) {                            // the same in every lane of the wave
+            const int64_t row = t0 + min(base + p, tn - 1);
+            kr[jg] = *(const au4*)(kc + row * ld + hoff);
+            vr[jg] = *(const au4*)(vc + row * ld + hoff);
+        }
+    }
+
+    float qv[G][8];
+#pragma unroll
+    for (int h = 0; h < G; h++) {
+        const af4* src = (const af4*)(q + (int64_t)(kv * G + h) * kAttD + 8 * i);
+        const af4 a = src[0], b = src[1];
+        qv[h][0] = a.x * qscale; qv[h][1] = a.y * qscale; qv[h][2] = a.z * qscale; qv[h][3] = a.w * qscale;
+        qv[h][4] = b.x * qscale; qv[h][5] = b.y * qscale; qv[h][6] = b.z * qscale; qv[h][7] = b.w * qscale;
+    }
+
+    // scores; lane i < G of each row stores head i's score
+#pragma unroll
+    for (int jg = 0; jg < kMaxGroups; jg++) {
+        const int base = 4 * (wave + kWaves * jg);
+        if (base >= tn) break;
+        float k[8];
+        halves(kr[jg], k);
+#pragma unroll
+        for (int h = 0; h < G; h++) {
+            float s = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; e++) s = fmaf(qv[h][e], k[e], s);
+            s = row_sum16(s);
+            if (i == h && base + p < tn) sc[h * C + base + p] = s;
+        }
+    }
+    __syncthreads();
+
+    // per head: max, weights exp2(s - max), their sum
+    for (int h = wave; h < G; h += kWaves) {
+        float m = -INFINITY;
+        for (int t = lane; t < tn; t += kWave) m = fmaxf(m, sc[h * C + t]);
+        m = wave_max(m);
+        float l = 0.f;
+        for (int t = lane; t < tn; t += kWave) {
+            const float e = exp2f(sc[h * C + t] - m);
+            sc[h * C + t] = e;
+            l += e;
+        }
+        l = wave_sum(l);
+        if (lane == 0) {
+            mls[2 * h] = m;
+            mls[2 * h + 1] = l;
+        }
+    }
+    __syncthreads();
+
+    // weighted values: lane (p, i) sums its positions' dims 8 i .. 8 i + 7
+    float acc[G][8];
+#pragma unroll
+    for (int h = 0; h < G; h++)
+#pragma unroll
+        for (int e = 0; e < 8; e++) acc[h][e] = 0.f;
+#pragma unroll
+    for (int jg = 0; jg < kMaxGroups; jg++) {
+        const int base = 4 * (wave + kWaves * jg);
+        if (base >= tn) break;
+        const bool ok = base + p < tn;
+        const int t = min(base + p, tn - 1);
+        float v[8];
+        halves(vr[jg], v);
+#pragma unroll
+        for (int h = 0; h < G; h++) {
+            const float w = ok ? sc[h * C + t] : 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; e++) acc[h][e] = fmaf(w, v[e], acc[h][e]);
+        }
+    }
+    // the 16 (wave, p) partials through LDS, added in a fixed order
+    const int slot = wave * 4 + p;
+#pragma unroll
+    for (int h = 0; h < G; h++) {
+        af4* dst = (af4*)(red + (slot * G + h) * kAttD + 8 * i);
+        dst[0] = af4{acc[h][0], acc[h][1], acc[h][2], acc[h][3]};
+        dst[1] = af4{acc[h][4], acc[h][5], acc[h][6], acc[h][7]};
+    }
+    __syncthreads();
+    float* rec = ws + ((int64_t)(kv * nch + chunk) * G) * kAttRecord;
+    for (int o = tid; o < G * kAttD; o += kThreads) {
+        const int h = o / kAttD, dd = o % kAttD;
+        float s = 0.f;
+        for (int r = 0; r < 16; r++) s += red[(r * G + h) * kAttD + dd];
+        rec[h * kAttRecord + 2 + dd] = s;
+    }
+    if (tid < G) {
+        rec[tid * kAttRecord] = mls[2 * tid];
+        rec[tid * kAttRecord + 1] = mls[2 * tid + 1];
+    }
+}
+
+// Workgroup h (a query head), thread = dimension: the chunks' records merged
+// under their common maximum, in chunk order.  Records are read 16 at a time
+// so that their loads are in flight together.
+__global__ __launch_bounds__(kAttD) void attn_combine_kernel(const float* __restrict__ ws, int G,
+                                                             int nch, float* __restrict__ out) {
+    constexpr int B = 16;
+    const int h = blockIdx.x, dd = threadIdx.x;
+    const int kv = h / G, hl = h % G;
+    const float* r0 = ws + ((int64_t)kv * nch * G + hl) * kAttRecord;
+    const int64_t stride = (int64_t)G * kAttRecord;
+    float m = -INFINITY;
+    for (int c0 = 0; c0 < nch; c0 += B) {
+        float v[B];
+#pragma unroll
+        for (int u = 0; u < B; u++) v[u] = c0 + u < nch ? r0[(c0 + u) * stride] : -INFINITY;
+#pragma unroll
+        for (int u = 0; u < B; u++) m = fmaxf(m, v[u]);
+    }
+    float l = 0.f, o = 0.f;
+    for (int c0 = 0; c0 < nch; c0 += B) {
+        float mm[B], ll[B], oo[B];
+#pragma unroll
+        for (int u = 0; u < B; u++) {
+            const bool ok = c0 + u < nch;
+            const float* r = r0 + (ok ? c0 + u : 0) * stride;
+            mm[u] = ok ? r[0] : -INFINITY;
+            ll[u] = r[1];
+            oo[u] = r[2 + dd];
+        }
+#pragma unroll
+        for (int u = 0; u < B; u++) {
+            const float f = exp2f(mm[u] - m);         // 0 past the last chunk
+            l = fmaf(ll[u], f, l);
+            o = fmaf(oo[u], f, o);
+        }
+    }
+    out[(int64_t)h * kAttD + dd] = o / l;
+}
+
+hipError_t launch_attention_decode(const float* q, const uint16_t* kc, const uint16_t* vc, int64_t T,
+                                   int64_t ld, int n_heads, int n_kv, float* out, float* ws,
+                                   hipStream_t stream) {
+    const int G = n_heads / n_kv;
+    const int C = attention_chunk(T, n_kv);
+    const int nch = (int)((T + C - 1) / C);
+    const float qscale = (float)(1.4426950408889634 / 11.313708498984761);   // log2(e) / sqrt(128)
+    const size_t lds = ((size_t)G * C + 16 * (size_t)G * kAttD + 2 * (size_t)G) * sizeof(float);
+    const dim3 grid((unsigned)n_kv, (unsigned)nch);
+    switch (G) {
+#define MBQ_ATT_CASE(g)                                                                              \
+    case g:                                                                                          \
+        if (hipError_t e = ensure_lds<attn_partial_kernel<g>>(lds)) return e;                        \
+        hipLaunchKernelGGL(attn_partial_kernel<g>, grid, dim3(kThreads), lds, stream, q, kc, vc, T, \
+                           ld, C, qscale, ws);                                                       \
+        break;
+        MBQ_ATT_CASE(1)
+        MBQ_ATT_CASE(2)
+        MBQ_ATT_CASE(4)
+        MBQ_ATT_CASE(8)
+#undef MBQ_ATT_CASE
+    default: return hipErrorInvalidValue;
+    }
+    if (hipError_t e = hipGetLastError()) return e;
+    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)n_heads), dim3(kAttD), 0, stream, ws, G,
+                       nch, out);
+    return hipGetLastError();
+}
+
+}  // namespace mbq

@@ -148,13 +148,23 @@ __device__ __forceinline__ void static_for(F&& f) {
     }
 }
 
-// 8 codes of one dword as fp16 (q - 8), in the order {0,4,1,5,2,6,3,7}.
-__device__ __forceinline__ h8 codes_to_b(uint32_t a) {
+// (v & mask) | bits in one instruction.  Written out because the compiler
+// splits it into an and and an or whenever both constants are literals.
+__device__ __forceinline__ uint32_t and_or(uint32_t v, uint32_t mask, uint32_t bits) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(v), "s"(mask), "v"(bits));
+    return r;
+}
+
+// 8 codes of one dword as fp16 (q - 8), in the order {0,4,1,5,2,6,3,7}:
+// each pair of nibbles becomes the halves 1024 + q (bits 0x6400 | q), and
+// one packed subtraction of 1032 leaves q - 8 exactly.
+__device__ __forceinline__ h8 codes_to_b(uint32_t a, uint32_t exp_bits) {
     const h2v off = {(_Float16)1032.0f, (_Float16)1032.0f};
     h2v w[4];
 #pragma unroll
     for (int s = 0; s < 4; s++)
-        w[s] = __builtin_bit_cast(h2v, ((a >> (4 * s)) & 0x000F000Fu) | 0x64006400u) - off;
+        w[s] = __builtin_bit_cast(h2v, and_or(a >> (4 * s), 0x000F000Fu, exp_bits)) - off;
     return h8{w[0][0], w[0][1], w[1][0], w[1][1], w[2][0], w[2][1], w[3][0], w[3][1]};
 }
 
@@ -235,13 +245,14 @@ __device__ __forceinline__ XConv convert_lane(f4g a, f4g b) {
 // Sign-extended byte i of w.
 __device__ __forceinline__ int sbyte(uint32_t w, int i) { return ((int32_t)(w << (24 - 8 * i))) >> 24; }
 
-// One wave's operands for one quad (128 values of K) held in registers: the
-// codes of RW row tiles and, per token tile, the 4 blocks of x (high and low
-// parts; fp32 x in two halves before conversion).  Scales and exponents are
-// read from LDS.
+// One wave's operands for one quad (128 values of K): the codes and scales
+// of RW row tiles and, per token tile, the exponents and the 4 blocks of x
+// (high and low parts; fp32 x in two halves before conversion).
 template <int TT, int RW, bool F32X>
 struct QuadOps {
     u4v wc[RW];
+    u2v ws[RW];
+    u4v ed[TT];
     u4v x0[4][TT], x1[4][TT];
 };
 
@@ -283,23 +294,11 @@ __global__ __launch_bounds__(MW * kWave) __attribute__((amdgpu_waves_per_eu(MW /
             co[rt] = (uint32_t)row * (uint32_t)(K / 2) + 16u * (uint32_t)(lane & 3);
         }
     }
-    // LDS: the workgroup's scales [16 RW rows][K / 32] (fp16; rows padded by
-    // 8 bytes, so that the 16 rows a wave reads at once sit in different
-    // banks), then (staged x) the token tiles' exponents [TT][K / 128][64
-    // bytes]; both are read many times, so they come in once, in whole lines
-    const int srow = K / 16 + 8;
-    uint8_t* lds_s = lds;
-    uint8_t* lds_e = lds + 16 * RW * srow;
-    {
-        const Rsrc rs = make_rsrc(P.p2, nk / 16);
-        const int per_row = K / 128;                   // 8-byte quads of scales per row
-        for (int c = tid; c < 16 * RW * per_row; c += MW * kWave) {
-            const int r = c / per_row, q = c - r * per_row;
-            const int row = min(row0 + r, N - 1);
-            const u2v v = bload<u2v, false>(rs, 8u * (uint32_t)q, (uint32_t)row * (uint32_t)(K / 16));
-            *(u2v*)(lds_s + r * srow + 8 * q) = v;
-        }
-    }
+    // scales: lane (g, j) reads the 4 scales of quad u of row j (8 bytes)
+    const Rsrc rs = make_rsrc(P.p2, nk / 16);
+    uint32_t so[RW];
+#pragma unroll
+    for (int rt = 0; rt < RW; rt++) so[rt] = (uint32_t)min(row0 + 16 * rt + j, N - 1) * (uint32_t)(K / 16);
     // x: staged, one resource per token tile (lane l reads the 16 bytes at
     // 16 l of each kilobyte); fp32, lane (g, t) reads token t's 8 values of
     // k-group g (rows past M repeat row M - 1: their sums are never stored)
@@ -316,15 +315,7 @@ __global__ __launch_bounds__(MW * kWave) __attribute__((amdgpu_waves_per_eu(MW /
             rx[tt] = make_rsrc(xt + (int64_t)ttg * tb, (uint64_t)tb);
         }
     }
-    if constexpr (!F32X) {
-        const int per_tile = K / 128 * 4;              // 16-byte pieces of exponents per tile
-#pragma unroll
-        for (int tt = 0; tt < TT; tt++)
-            for (int q = tid; q < per_tile; q += MW * kWave) {
-                const u4v v = bload<u4v, true>(rx[tt], (uint32_t)(K / 32) * kTileBlockBytes + 16u * (uint32_t)q, 0u);
-                *(u4v*)(lds_e + tt * (K / 2) + 16 * q) = v;
-            }
-    }
+    const uint32_t eoff = (uint32_t)(K / 32) * kTileBlockBytes + 16u * g;
 
     typedef QuadOps<TT, RW, F32X> Q;
     // quad of step s: the waves interleave, so that two adjacent waves read
@@ -333,7 +324,14 @@ __global__ __launch_bounds__(MW * kWave) __attribute__((amdgpu_waves_per_eu(MW /
     auto quad = [&](int s) __attribute__((always_inline)) { return min(wave + MW * s, nq - 1); };
     auto load_w = [&](Q& q, int u) __attribute__((always_inline)) {
 #pragma unroll
-        for (int rt = 0; rt < RW; rt++) q.wc[rt] = bload<u4v, true>(rc, co[rt], 64u * (uint32_t)u);
+        for (int rt = 0; rt < RW; rt++) {
+            q.wc[rt] = bload<u4v, true>(rc, co[rt], 64u * (uint32_t)u);
+            q.ws[rt] = bload<u2v, true>(rs, so[rt], 8u * (uint32_t)u);
+        }
+        if constexpr (!F32X) {
+#pragma unroll
+            for (int tt = 0; tt < TT; tt++) q.ed[tt] = bload<u4v, true>(rx[tt], eoff, 64u * (uint32_t)u);
+        }
     };
     auto load_x = [&](Q& q, int b, int u) __attribute__((always_inline)) {
 #pragma unroll
@@ -356,25 +354,24 @@ __global__ __launch_bounds__(MW * kWave) __attribute__((amdgpu_waves_per_eu(MW /
 #pragma unroll
         for (int tt = 0; tt < TT; tt++) acc[rt][tt] = f4v{0.f, 0.f, 0.f, 0.f};
     const f4v zero = {0.f, 0.f, 0.f, 0.f};
+    const uint32_t exp_bits = opaque_copy(0x64006400u);    // kept in a register for and_or
 
     // One step: multiply quad q (in cur) and load quad un into cur: the
     // weights and exponents first (their registers are free once copied),
     // then each block of x right after the same block of cur is used.
     // LOAD false: the last step of a compile-time stream loads nothing.
-    auto step = [&](auto load_c, Q& cur, bool use, int uc, int un) __attribute__((always_inline)) {
+    auto step = [&](auto load_c, Q& cur, bool use, int un) __attribute__((always_inline)) {
         constexpr bool LOAD = decltype(load_c)::value;
         u4v cb[RW];
         u2v sc[RW];
 #pragma unroll
         for (int rt = 0; rt < RW; rt++) {
             cb[rt] = lane_quad_transpose(quad_transpose(cur.wc[rt]), lane);
-            sc[rt] = *(const u2v*)(lds_s + (16 * rt + j) * srow + 8 * uc);
+            sc[rt] = cur.ws[rt];
         }
         u4v ed[TT];
-        if constexpr (!F32X) {
 #pragma unroll
-            for (int tt = 0; tt < TT; tt++) ed[tt] = *(const u4v*)(lds_e + tt * (K / 2) + 64 * uc + 16 * g);
-        }
+        for (int tt = 0; tt < TT; tt++) ed[tt] = cur.ed[tt];
         if constexpr (LOAD) load_w(cur, un);
 #pragma unroll
         for (int b = 0; b < 4; b++) {
@@ -401,7 +398,7 @@ __global__ __launch_bounds__(MW * kWave) __attribute__((amdgpu_waves_per_eu(MW /
             if (!use) continue;                        // the same in every lane
 #pragma unroll
             for (int rt = 0; rt < RW; rt++) {
-                const h8 bw = codes_to_b(cb[rt][b]);
+                const h8 bw = codes_to_b(cb[rt][b], exp_bits);
                 const float sv = h2f(sc[rt][b >> 1] >> (16 * (b & 1)));
 #pragma unroll
                 for (int tt = 0; tt < TT; tt++) {
@@ -419,21 +416,18 @@ __global__ __launch_bounds__(MW * kWave) __attribute__((amdgpu_waves_per_eu(MW /
     load_w(cur, quad(0));
 #pragma unroll
     for (int b = 0; b < 4; b++) load_x(cur, b, quad(0));
-    __syncthreads();                                       // scales and exponents in LDS
     if constexpr (NSTEP > 0) {
         // every wave has exactly NSTEP quads
         static_for<0, NSTEP>([&](auto ss) __attribute__((always_inline)) {
             constexpr int s = decltype(ss)::value;
-            step(IC<(s + 1 < NSTEP)>{}, cur, true, quad(s), quad(s + 1 < NSTEP ? s + 1 : s));
+            step(IC<(s + 1 < NSTEP)>{}, cur, true, quad(s + 1 < NSTEP ? s + 1 : s));
         });
     } else {
 #pragma unroll 1
-        for (int s = 0; s < nstep; s++) step(IC<1>{}, cur, wave + MW * s < nq, quad(s), quad(s + 1));
+        for (int s = 0; s < nstep; s++) step(IC<1>{}, cur, wave + MW * s < nq, quad(s + 1));
     }
 
-    // the waves' partial tiles, added in wave order (the LDS of the scales
-    // is reused once every wave is done with it)
-    __syncthreads();
+    // the waves' partial tiles, added in wave order
     f4v* red = (f4v*)lds;                                  // [wave][rt][tt][lane]
 #pragma unroll
     for (int rt = 0; rt < RW; rt++)
@@ -463,20 +457,11 @@ __global__ __launch_bounds__(MW * kWave) __attribute__((amdgpu_waves_per_eu(MW /
     }
 }
 
-// LDS the stream fills: scales of 16 RW padded rows, and the exponents of
-// TT token tiles for staged x.
-static size_t mfma_fill_lds(int RW, int TT, int64_t K, bool f32x) {
-    return (size_t)16 * RW * (K / 16 + 8) + (f32x ? 0 : (size_t)TT * K / 2);
-}
-constexpr size_t kMaxLds = 160 * 1024;
-
 template <int MW, int TT, int RW, int NSTEP, bool F32X>
 static hipError_t launch_k(DevPlanes P, int64_t N, int64_t K, const uint8_t* xt, const float* xf,
                            int64_t ldx, int64_t M, float* y, int64_t ldy, int accumulate,
                            hipStream_t stream) {
-    constexpr size_t red = (size_t)MW * RW * TT * kWave * 16;
-    const size_t fill = mfma_fill_lds(RW, TT, K, F32X);
-    const size_t lds = fill > red ? fill : red;
+    constexpr size_t lds = (size_t)MW * RW * TT * kWave * 16;
     auto kern = gemv_mfma_q45_kernel<MW, TT, RW, NSTEP, F32X>;
     if (hipError_t e = ensure_lds<gemv_mfma_q45_kernel<MW, TT, RW, NSTEP, F32X>>(lds)) return e;
     const int64_t ntt = (M + 15) / 16;
@@ -486,29 +471,31 @@ static hipError_t launch_k(DevPlanes P, int64_t N, int64_t K, const uint8_t* xt,
     return hipGetLastError();
 }
 
-// Waves per workgroup: 16 for one token tile (4 per SIMD, twice the loads in
-// flight of 8) where the registers fit 128 without spilling (up to 3 row
-// tiles, 4 at K = 4096), else 8 (2 per SIMD); MBQ_MFMA_MW = 8 forces 8
-// (tuning).
+// Waves per workgroup: 16 for one token tile (4 per SIMD) where the
+// registers fit 128 without spilling (up to 3 row tiles, 4 at K = 4096),
+// else 8 (2 per SIMD); 4 (one per SIMD, up to 512 registers) for four token
+// tiles.  MBQ_MFMA_MW = 8 forces 8 for one tile (tuning).
 template <int TT, int RW, bool F32X>
 static hipError_t launch_rw(DevPlanes P, int64_t N, int64_t K, const uint8_t* xt, const float* xf,
                             int64_t ldx, int64_t M, float* y, int64_t ldy, int accumulate,
                             hipStream_t s) {
     if constexpr (TT == 1) {
-        bool mw16 = RW <= 3 || K == 4096;
+        bool mw16 = K == 4096 || (K == 12288 && RW <= 3) || RW <= 2;
         if (const char* e = tuning_var("MBQ_MFMA_MW")) mw16 = mw16 && atoi(e) != 8;
         if (mw16) {
             constexpr int MW = 16, KS = MW * 128;      // values per step of the workgroup
             if (K == 4096) return launch_k<MW, TT, RW, 4096 / KS, F32X>(P, N, K, xt, xf, ldx, M, y, ldy, accumulate, s);
-            if constexpr (RW <= 3) {
+            if constexpr (RW <= 3)
                 if (K == 12288) return launch_k<MW, TT, RW, 12288 / KS, F32X>(P, N, K, xt, xf, ldx, M, y, ldy, accumulate, s);
-                return launch_k<MW, TT, RW, 0, F32X>(P, N, K, xt, xf, ldx, M, y, ldy, accumulate, s);
-            }
+            if constexpr (RW <= 2) return launch_k<MW, TT, RW, 0, F32X>(P, N, K, xt, xf, ldx, M, y, ldy, accumulate, s);
         }
     }
-    constexpr int MW = 8, KS = MW * 128;
+    constexpr int MW = TT == 4 ? 4 : 8, KS = MW * 128;
     if (K == 4096) return launch_k<MW, TT, RW, 4096 / KS, F32X>(P, N, K, xt, xf, ldx, M, y, ldy, accumulate, s);
-    if (K == 12288) return launch_k<MW, TT, RW, 12288 / KS, F32X>(P, N, K, xt, xf, ldx, M, y, ldy, accumulate, s);
+    // four token tiles: the 24-step stream of K = 12288 takes minutes to
+    // compile for little gain over the loop
+    if constexpr (TT < 4)
+        if (K == 12288) return launch_k<MW, TT, RW, 12288 / KS, F32X>(P, N, K, xt, xf, ldx, M, y, ldy, accumulate, s);
     return launch_k<MW, TT, RW, 0, F32X>(P, N, K, xt, xf, ldx, M, y, ldy, accumulate, s);
 }
 
@@ -520,8 +507,6 @@ static hipError_t launch_tt(DevPlanes P, int64_t N, int64_t K, const uint8_t* xt
                             hipStream_t s) {
     int64_t rw = (N + 16 * 256 - 1) / (16 * 256);
     if (const char* e = tuning_var("MBQ_MFMA_RW")) rw = atoi(e);
-    rw = rw < 1 ? 1 : (rw > 4 ? 4 : rw);
-    while (rw > 1 && mfma_fill_lds((int)rw, TT, K, F32X) > kMaxLds) rw--;   // the longest rows
     switch (rw <= 1 ? 1 : rw == 2 ? 2 : rw == 3 ? 3 : 4) {
     case 1: return launch_rw<TT, 1, F32X>(P, N, K, xt, xf, ldx, M, y, ldy, accumulate, s);
     case 2: return launch_rw<TT, 2, F32X>(P, N, K, xt, xf, ldx, M, y, ldy, accumulate, s);
@@ -530,26 +515,36 @@ static hipError_t launch_tt(DevPlanes P, int64_t N, int64_t K, const uint8_t* xt
     }
 }
 
-// One or two token tiles per workgroup: one tile up to 16 tokens, else two
-// (the grid covers the rest); MBQ_MFMA_TT = 1 forces one (tuning).
+// Token tiles per workgroup: one up to 16 tokens, two up to 32, else four
+// (the grid covers the rest): each code a workgroup converts serves TT
+// tiles.  MBQ_MFMA_TT overrides (tuning).
 static int pick_tt(int64_t M) {
-    int tt = M <= 16 ? 1 : 2;
-    if (const char* e = tuning_var("MBQ_MFMA_TT")) tt = atoi(e) == 1 ? 1 : 2;
+    int tt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+    if (const char* e = tuning_var("MBQ_MFMA_TT")) {
+        const int v = atoi(e);
+        tt = v <= 1 ? 1 : (v == 2 ? 2 : 4);
+    }
     return tt;
 }
 
 hipError_t launch_gemv_mfma_q45(DevPlanes P, int64_t N, int64_t K, const void* xt, int64_t M,
                                 float* y, int64_t ldy, int accumulate, hipStream_t stream) {
     const uint8_t* x = (const uint8_t*)xt;
-    return pick_tt(M) == 1 ? launch_tt<1, false>(P, N, K, x, nullptr, 0, M, y, ldy, accumulate, stream)
-                           : launch_tt<2, false>(P, N, K, x, nullptr, 0, M, y, ldy, accumulate, stream);
+    switch (pick_tt(M)) {
+    case 1: return launch_tt<1, false>(P, N, K, x, nullptr, 0, M, y, ldy, accumulate, stream);
+    case 2: return launch_tt<2, false>(P, N, K, x, nullptr, 0, M, y, ldy, accumulate, stream);
+    default: return launch_tt<4, false>(P, N, K, x, nullptr, 0, M, y, ldy, accumulate, stream);
+    }
 }
 
 hipError_t launch_gemv_mfma_q45_f32x(DevPlanes P, int64_t N, int64_t K, const float* x,
                                      int64_t ldx, int64_t M, float* y, int64_t ldy,
                                      int accumulate, hipStream_t stream) {
-    return pick_tt(M) == 1 ? launch_tt<1, true>(P, N, K, nullptr, x, ldx, M, y, ldy, accumulate, stream)
-                           : launch_tt<2, true>(P, N, K, nullptr, x, ldx, M, y, ldy, accumulate, stream);
+    switch (pick_tt(M)) {
+    case 1: return launch_tt<1, true>(P, N, K, nullptr, x, ldx, M, y, ldy, accumulate, stream);
+    case 2: return launch_tt<2, true>(P, N, K, nullptr, x, ldx, M, y, ldy, accumulate, stream);
+    default: return launch_tt<4, true>(P, N, K, nullptr, x, ldx, M, y, ldy, accumulate, stream);
+    }
 }
 
 }  // namespace mbq

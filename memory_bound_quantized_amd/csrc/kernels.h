@@ -185,6 +185,18 @@ hipError_t launch_quantize(int fmt, const float* w, int64_t ldw, int64_t N, int6
 hipError_t launch_unpack_codes(int fmt, DevPlanes P, int64_t N, int64_t K, uint8_t* out,
                                hipStream_t stream);
 
+// One token's attention over an fp16 KV cache (attention.hip): head
+// dimension kAttD, n_heads / n_kv in {1, 2, 4, 8}, T >= 1.  The workspace
+// holds one record of kAttRecord floats per query head and chunk of
+// positions (attention_workspace_bytes).
+constexpr int kAttD = 128;
+constexpr int kAttRecord = 132;
+int attention_chunk(int64_t T, int n_kv);
+size_t attention_workspace_bytes(int64_t T, int n_heads, int n_kv);
+hipError_t launch_attention_decode(const float* q, const uint16_t* kc, const uint16_t* vc, int64_t T,
+                                   int64_t ld, int n_heads, int n_kv, float* out, float* ws,
+                                   hipStream_t stream);
+
 hipError_t launch_probe_read(const void* buf, size_t bytes, float* sink, hipStream_t stream);
 hipError_t launch_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
 // Pointer chase over `bytes` of buf: chase_entries(bytes) entries, one per

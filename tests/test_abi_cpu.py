@@ -30,7 +30,7 @@ def _declared_symbols():
 
 def test_library_exports_every_declared_symbol():
     declared = _declared_symbols()
-    assert len(declared) == 31
+    assert len(declared) == 33
     assert sorted(_lib.EXPORTS) == declared
     lib = ctypes.CDLL(_lib.LIB_PATH)
     for name in declared:
@@ -367,3 +367,27 @@ def test_quantize_argument_checks():
     # planes overlapping each other
     assert _quantize(planes=[BASE + 0x1000000, None, BASE + 0x1000010, None]) == _lib.EINVAL
     assert _quantize(fmt=2, planes=[BASE + 0x1000000, None, BASE + 0x3000000, BASE + 0x4000000]) == _lib.EINVAL
+
+
+def _attn(q=BASE, k=BASE + 0x1000000, v=BASE + 0x2000000, T=512, ld=1024, H=32, Hkv=8, d=128,
+          out=BASE + 0x3000000, ws=BASE + 0x4000000, wsb=1 << 24):
+    return L.mbq_attention_decode(q, k, v, T, ld, H, Hkv, d, out, ws, wsb, None)
+
+
+def test_attention_argument_checks():
+    sz = ctypes.c_size_t()
+    assert L.mbq_attention_workspace_bytes(512, 32, 8, 128, ctypes.byref(sz)) == _lib.OK
+    assert sz.value > 0
+    assert L.mbq_attention_workspace_bytes(0, 32, 8, 128, ctypes.byref(sz)) == _lib.EINVAL
+    assert L.mbq_attention_workspace_bytes(512, 32, 8, 64, ctypes.byref(sz)) == _lib.EUNSUPPORTED
+    assert L.mbq_attention_workspace_bytes(512, 24, 8, 128, ctypes.byref(sz)) == _lib.EUNSUPPORTED  # G = 3
+    assert L.mbq_attention_workspace_bytes(512, 30, 8, 128, ctypes.byref(sz)) == _lib.EINVAL        # not a multiple
+    assert _attn(T=0) == _lib.EINVAL
+    assert _attn(d=96) == _lib.EUNSUPPORTED
+    assert _attn(ld=1000) == _lib.EINVAL                       # ld < n_kv * d
+    assert _attn(ld=1028) == _lib.EALIGN                       # ld % 8
+    assert _attn(q=0) == _lib.EINVAL
+    assert _attn(q=BASE + 4) == _lib.EALIGN
+    assert _attn(wsb=16) == _lib.EINVAL                        # short workspace
+    assert _attn(out=BASE + 0x1000000 + 64) == _lib.EINVAL     # out inside the key cache
+    assert _attn(ws=BASE) == _lib.EINVAL                       # workspace over q

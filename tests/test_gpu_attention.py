@@ -1,0 +1,137 @@
+"""GPU decode attention (mbq_attention_decode) against the oracle's fp64
+attention over the same fp16 cache.
+
+Bar (derived from the arithmetic, fp32 throughout): a score s_t = q.k_t/sqrt(d)
+is a 128-term fp32 dot product of exact products, off by at most
+e_t = 130 * 2^-24 * sum_d |q_d k_td| / sqrt(d); a weight exp(s_t - max) then
+carries a relative error of at most about 2 max_t e_t plus a few ulp of the
+exponential, and so does the normalised output.  Per element:
+|out - ref| <= (2 max_t e_t + 2^-18) * max_t |v_t| + 2^-20 |ref|, and the
+relative L2 error over each head's output at most 1e-5 + 2 max_t e_t (the
+score error scales with |q| |k|: scores of several hundred carry errors of
+a few 1e-4).
+
+Cases: the 36-layer model's shape (32 query heads on 8 key/value heads of
+128) at 512 positions, one position, ragged counts across chunk edges, long
+contexts split into many chunks, every group size the kernels take, a row
+stride wider than the heads, scores of several hundred (the max shift), and
+equal keys (uniform weights).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import memory_bound_quantized_amd  # noqa: F401  (fails loudly if libmbq.so is missing)
+
+
+def mbq():
+    import memory_bound_quantized_amd as m
+    return m
+
+
+D = 128
+
+
+def run(q, kc, vc, H, Hkv, T=None):
+    qd = torch.from_numpy(q).cuda()
+    kd = torch.from_numpy(kc.view(np.int16)).cuda()
+    vd = torch.from_numpy(vc.view(np.int16)).cuda()
+    return mbq().attention_decode(qd, kd, vd, H, Hkv, T=T).cpu().numpy()
+
+
+def check(out, q, kc, vc, H, Hkv, T):
+    ref = oracle.attention_decode(q, kc[:T], vc[:T], H, Hkv, D).astype(np.float64)
+    G = H // Hkv
+    k = kc[:T].astype(np.float64).reshape(T, Hkv, D)
+    v = vc[:T].astype(np.float64).reshape(T, Hkv, D)
+    qq = q.astype(np.float64).reshape(H, D)
+    for h in range(H):
+        g = h // G
+        e = 130 * 2.0 ** -24 * (np.abs(k[:, g, :]) @ np.abs(qq[h])).max() / np.sqrt(D)
+        vmax = np.abs(v[:, g, :]).max()
+        o, r = out[h * D:(h + 1) * D].astype(np.float64), ref[h * D:(h + 1) * D]
+        bound = (2 * e + 2.0 ** -18) * vmax + 2.0 ** -20 * np.abs(r)
+        worst = (np.abs(o - r) / bound).max()
+        assert worst <= 1.0, "head %d: element outside the bound (ratio %.3g)" % (h, worst)
+        nr = np.linalg.norm(r)
+        if nr > 0:
+            assert np.linalg.norm(o - r) <= (1e-5 + 2 * e) * nr, h
+
+
+def cache(rng, T, width, scale=1.0):
+    return ((rng.normal(size=(T, width)) * scale).astype(np.float16),
+            rng.normal(size=(T, width)).astype(np.float16))
+
+
+@pytest.mark.parametrize("T", [1, 5, 16, 17, 100, 512, 1000, 4097])
+def test_model_shape_matches_oracle(T):
+    print("attention H=32 Hkv=8 T=%d" % T, flush=True)
+    rng = np.random.default_rng(T)
+    H, Hkv = 32, 8
+    kc, vc = cache(rng, T, Hkv * D)
+    q = rng.normal(size=H * D).astype(np.float32)
+    check(run(q, kc, vc, H, Hkv), q, kc, vc, H, Hkv, T)
+
+
+@pytest.mark.parametrize("H,Hkv", [(8, 8), (16, 8), (32, 4), (64, 8)])
+def test_every_group_size(H, Hkv):
+    print("attention H=%d Hkv=%d" % (H, Hkv), flush=True)
+    rng = np.random.default_rng(H * 100 + Hkv)
+    T = 300
+    kc, vc = cache(rng, T, Hkv * D)
+    q = rng.normal(size=H * D).astype(np.float32)
+    check(run(q, kc, vc, H, Hkv), q, kc, vc, H, Hkv, T)
+
+
+def test_long_context_many_chunks():
+    print("attention long T=40000", flush=True)
+    rng = np.random.default_rng(7)
+    H, Hkv, T = 32, 8, 40000
+    kc, vc = cache(rng, T, Hkv * D)
+    q = rng.normal(size=H * D).astype(np.float32)
+    check(run(q, kc, vc, H, Hkv), q, kc, vc, H, Hkv, T)
+
+
+def test_capacity_and_row_stride():
+    """A cache with room for more positions than T, rows wider than the heads."""
+    print("attention stride", flush=True)
+    rng = np.random.default_rng(8)
+    H, Hkv, T, cap, width = 32, 8, 333, 512, 8 * D + 64
+    kc, vc = cache(rng, cap, width)
+    q = rng.normal(size=H * D).astype(np.float32)
+    out = run(q, kc, vc, H, Hkv, T=T)
+    check(out, q, np.ascontiguousarray(kc[:, :Hkv * D]), np.ascontiguousarray(vc[:, :Hkv * D]), H, Hkv, T)
+
+
+def test_large_scores_take_the_max_shift():
+    """Scores in the hundreds: without the shift exp would overflow."""
+    print("attention large scores", flush=True)
+    rng = np.random.default_rng(9)
+    H, Hkv, T = 32, 8, 200
+    kc, vc = cache(rng, T, Hkv * D, scale=8.0)
+    q = (rng.normal(size=H * D) * 8).astype(np.float32)
+    out = run(q, kc, vc, H, Hkv)
+    assert np.all(np.isfinite(out))
+    check(out, q, kc, vc, H, Hkv, T)
+
+
+def test_equal_keys_average_the_values():
+    print("attention equal keys", flush=True)
+    rng = np.random.default_rng(10)
+    H, Hkv, T = 8, 2, 77
+    kc = np.tile(rng.normal(size=(1, Hkv * D)).astype(np.float16), (T, 1))
+    vc = rng.normal(size=(T, Hkv * D)).astype(np.float16)
+    q = rng.normal(size=H * D).astype(np.float32)
+    out = run(q, kc, vc, H, Hkv).reshape(H, D)
+    mean = vc.astype(np.float64).mean(axis=0).reshape(Hkv, D)
+    for h in range(H):
+        assert np.max(np.abs(out[h] - mean[h // 4])) <= 2.0 ** -18 * np.abs(vc).max()

@@ -139,21 +139,23 @@ def test_smallm_every_geometry_bitwise(fmt, M, N, K):
 
 
 MFMA_GEOM_CASES = [(16, 1000, 4096), (20, 1000, 4096), (40, 300, 2048), (64, 130, 1024),
-                   (6, 77, 640), (33, 200, 2176), (17, 50, 128)]
+                   (6, 77, 640), (33, 200, 2176), (17, 50, 128), (64, 300, 4096),
+                   (50, 100, 12288)]
 
 
 @pytest.mark.parametrize("M,N,K", MFMA_GEOM_CASES)
 def test_mfma_every_geometry_matches_oracle(M, N, K):
     """Staged x on the matrix cores at every row-tile count (1-4 row tiles
-    per workgroup) and token-tile count (1 or 2 per workgroup); K = 640 and
-    2176 leave the last chunk partial and some waves without a quad."""
+    per workgroup) and token-tile count (1, 2 or 4 per workgroup); K = 640
+    and 2176 leave some waves without a quad, K = 4096 and 12288 take the
+    compile-time streams."""
     print("geometry mfma M=%d N=%d K=%d" % (M, N, K), flush=True)
     ow, dw = weights(1, N, K, 9990 + N)
     X = np.random.default_rng(M + N).normal(size=(M, K)).astype(np.float32)
     Xq = mbq().stage_x(1, dev(X))
     ref = oracle.gemv(ow, X)
     for rw in (1, 2, 3, 4):
-        for tt in (1, 2):
+        for tt in (1, 2, 4):
             with env(MBQ_MFMA_RW=rw, MBQ_MFMA_TT=tt):
                 Y = mbq().gemv_xq(dw, Xq, M=M).cpu().numpy()
             check_gemv(Y, ow, X, ref)
@@ -171,7 +173,7 @@ def test_mfma_f32x_every_geometry_matches_oracle(M, N, K):
     ref = oracle.gemv(ow, X)
     Xq = mbq().stage_x(1, Xd)
     for rw in (1, 2, 3, 4):
-        for tt in (1, 2):
+        for tt in (1, 2, 4):
             with env(MBQ_MFMA_RW=rw, MBQ_MFMA_TT=tt):
                 Y = mbq().gemv_q(dw, Xd).cpu().numpy()
                 Ys = mbq().gemv_xq(dw, Xq, M=M).cpu().numpy()
