@@ -548,6 +548,64 @@ def rows_bench(mbq, workloads, torch, dev, peak_gbs, one_launch=True, keep=None)
     del Xs, X
     torch.cuda.empty_cache()
 
+    # ---- prefill-sized batch: 512 tokens of the 12288 x 4096 Q45 table on
+    # the matrix cores (staged x), and the separate staging launch
+    M = 512
+    c4 = workloads.config4(16)
+    fmt, N, K, planes = c4["W"]
+    W0 = mbq.QWeight.from_host(fmt, N, K, planes)
+    Ws = rotated(W0)
+    X = torch.from_numpy(np.random.default_rng(512).normal(size=(M, K)).astype(np.float32)).to(dev)
+    Xq = mbq.stage_x(fmt, X)
+    Y = torch.empty((M, N), device=dev)
+    kern_us = per_launch_us(lambda W: mbq.gemv_xq(W, Xq, M=M, out=Y), Ws, 40)
+    stage_us = per_launch_us(lambda W: mbq.stage_x(fmt, X, out=Xq), Ws, 40)
+    tf = 2.0 * M * N * K / (kern_us * 1e-6) / 1e12
+    rows["prefill_12288x4096_q45_m512"] = {
+        "product_us": round(kern_us, 2), "staging_us": round(stage_us, 2),
+        "useful_tflops": round(tf, 1),
+        "mfma_issue_frac_of_fp16_peak": round(2 * tf / 2500.0, 4)}
+    del Ws, W0, X, Xq, Y
+    torch.cuda.empty_cache()
+
+    # ---- the quantizer: fp32 weights to each format's planes, 12288 x 4096
+    # (two inputs of 201 MB alternate, so that neither stays in the 256 MB
+    # Infinity Cache)
+    wq = torch.from_numpy(np.random.default_rng(11).normal(0, 0.02, size=(12288, 4096)).astype(np.float32)).to(dev)
+    wqs = [wq, wq.clone()]
+    quant = {}
+    for fmt, name in ((1, "q45"), (2, "q65"), (3, "q25"), (0, "bf16")):
+        Q = mbq.quantize(fmt, wq)
+        us = per_launch_us(lambda w: mbq.quantize(fmt, w, out=Q), wqs * 4, 80)
+        b = wq.numel() * 4 + Q.nbytes
+        quant[name] = {"us": round(us, 2), "gbs": gbs(b, us), "bytes": b,
+                       "frac_of_measured_peak": round(b / (us * 1e-6) / 1e9 / peak_gbs, 4)}
+        del Q
+    rows["quantize_12288x4096"] = quant
+    del wq, wqs
+    torch.cuda.empty_cache()
+
+    # ---- decode attention, 32 query heads on 8 key/value heads of 128, cold
+    # fp16 caches of T positions
+    att = {}
+    H, Hkv = 32, 8
+    for T in (512, 4096, 32768):
+        rng = np.random.default_rng(T)
+        per = 2 * T * Hkv * 128 * 2
+        caches = []
+        for _ in range(max(2, min(64, ROTATION_BYTES // per))):
+            kc = torch.from_numpy(rng.normal(size=(T, Hkv * 128)).astype(np.float16).view(np.int16)).to(dev)
+            caches.append((kc, kc.clone()))
+        q = torch.from_numpy(rng.normal(size=H * 128).astype(np.float32)).to(dev)
+        o = torch.empty(H * 128, device=dev)
+        wsb = torch.empty(mbq.attention_workspace_bytes(T, H, Hkv) // 4 + 4, device=dev)
+        us = per_launch_us(lambda c: mbq.attention_decode(q, c[0], c[1], H, Hkv, out=o, workspace=wsb), caches)
+        att["T%d" % T] = {"us": round(us, 2), "gbs": gbs(per, us), "kv_bytes": per,
+                          "frac_of_measured_peak": round(per / (us * 1e-6) / 1e9 / peak_gbs, 4)}
+        del caches
+        torch.cuda.empty_cache()
+    rows["attention_h32_kv8_d128"] = att
+
     # ---- workload 3: one token through the 36-layer stream
     rows["decode_36_layers"] = decode_row(workloads, torch, dev, peak_gbs, one_launch=one_launch,
                                           keep=keep)
@@ -614,6 +672,30 @@ def ceilings(mbq, torch, dev, stream, full=True):
         out["m_star_q45"] = {"matrix_cores": round(4.5 / 16 * r_mfma / bw, 2),
                              "vector_units": round(4.5 / 16 * r_vec / bw, 2),
                              "rule": "M* = (w/16)(R/BW), w = 4.5, R = multiply-adds/s of each path's arithmetic"}
+        # per compute unit, the two streams of the 16-token matrix-core product
+        # (its 110 KB of weights from HBM, the 264 KB staged x every unit reads
+        # from L2), alone and together: whether they overlap or queue
+        dbytes, sbytes = 112 * 1024, 264 * 1024
+        dist = buf[:cus * dbytes]
+        shared = buf[half:half + sbytes]
+        msink = torch.empty(cus, device=dev)
+        mixed = {}
+        for mode, name in ((0, "hbm_distinct_112k_per_cu_us"), (1, "l2_shared_264k_us"),
+                           (2, "both_interleaved_us"), (3, "both_separate_waves_us")):
+            # the distinct data rotates over 16 regions so that it comes from HBM
+            regs = [buf[r * cus * dbytes:(r + 1) * cus * dbytes] for r in range(16)]
+            for rg in regs:
+                mbq.probe_mixed(rg, dbytes, shared, sbytes, mode, cus, msink, stream)
+            torch.cuda.synchronize()
+            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_.record(stream)
+            for k in range(4):
+                for rg in regs:
+                    mbq.probe_mixed(rg, dbytes, shared, sbytes, mode, cus, msink, stream)
+            b_.record(stream)
+            torch.cuda.synchronize()
+            mixed[name] = round(a_.elapsed_time(b_) * 1e3 / 64, 2)
+        out["per_cu_streams"] = mixed
     del buf
     torch.cuda.empty_cache()
     return out

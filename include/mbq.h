@@ -419,6 +419,19 @@ int mbq_quantize(int fmt, const float* w, int64_t N, int64_t K, int64_t ldw, voi
 int mbq_probe_read(const void* buf, size_t bytes, float* sink, void* stream);
 int mbq_probe_copy(void* dst, const void* src, size_t bytes, void* stream);
 
+/* Per-compute-unit streams: `blocks` workgroups of 16 waves (one per compute
+ * unit); workgroup b reads distinct_bytes of `distinct` from b *
+ * distinct_bytes on (the buffer holds blocks * distinct_bytes) and
+ * shared_bytes of `shared`, which every workgroup reads (it stays in L2).
+ * mode 0: distinct only; 1: shared only; 2: both, each wave interleaving
+ * 1 KB of distinct data with its share of shared data; 3: both, waves 0-3
+ * on distinct data, 4-15 on shared.  Timing modes 0 and 1 against 2 and 3
+ * shows whether a unit's HBM and L2 streams overlap or queue behind each
+ * other.  Sizes multiples of 1 KB, buffers 16-byte aligned; sink: device,
+ * >= blocks floats.  MBQ_EINVAL for a bad mode or block count. */
+int mbq_probe_mixed(const void* distinct, size_t distinct_bytes, const void* shared, size_t shared_bytes,
+                    int mode, int blocks, float* sink, void* stream);
+
 /* Memory latency ([roofline-holds] "How the breakouts tie out: Little and
  * Volkov": bytes in flight = bandwidth x latency): a dependent random
  * pointer chase.  mbq_probe_chase_init writes a chain of *entries =

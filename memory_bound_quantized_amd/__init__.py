@@ -293,6 +293,13 @@ def attention_decode(q, k_cache, v_cache, n_heads: int, n_kv_heads: int, T: int 
     return out
 
 
+def probe_mixed(distinct, distinct_bytes: int, shared, shared_bytes: int, mode: int, blocks: int,
+                sink, stream=None):
+    """Per-compute-unit HBM and L2 streams (mbq_probe_mixed)."""
+    check(lib.mbq_probe_mixed(_ptr(distinct), distinct_bytes, _ptr(shared), shared_bytes, mode, blocks,
+                              _ptr(sink), _stream(stream)))
+
+
 def probe_read(buf, sink, stream=None):
     check(lib.mbq_probe_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
                              _stream(stream)))

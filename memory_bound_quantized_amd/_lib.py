@@ -21,7 +21,7 @@ EXPORTS = (
     "mbq_decode_step_noalloc", "mbq_decode_prepare", "mbq_decode_step_persistent",
     "mbq_xq_bytes", "mbq_stage_x", "mbq_gemv_xq", "mbq_rmsnorm_xq",
     "mbq_silu_mul_xq", "mbq_rmsnorm", "mbq_layernorm", "mbq_silu_mul", "mbq_dequant_f32",
-    "mbq_unpack_codes", "mbq_quantize", "mbq_attention_workspace_bytes", "mbq_attention_decode", "mbq_probe_read", "mbq_probe_copy", "mbq_probe_chase_init",
+    "mbq_unpack_codes", "mbq_quantize", "mbq_attention_workspace_bytes", "mbq_attention_decode", "mbq_probe_read", "mbq_probe_copy", "mbq_probe_mixed", "mbq_probe_chase_init",
     "mbq_probe_chase", "mbq_probe_peak", "mbq_status_str",
     "mbq_last_error", "mbq_version",
 )
@@ -99,6 +99,7 @@ def _load():
         "mbq_quantize": (i32, [i32, vp, i64, i64, i64, ctypes.POINTER(vp), vp]),
         "mbq_attention_workspace_bytes": (i32, [i64, i32, i32, i32, ctypes.POINTER(sz)]),
         "mbq_attention_decode": (i32, [vp, vp, vp, i64, i64, i32, i32, i32, vp, vp, sz, vp]),
+        "mbq_probe_mixed": (i32, [vp, sz, vp, sz, i32, i32, vp, vp]),
         "mbq_probe_read": (i32, [vp, sz, vp, vp]),
         "mbq_probe_copy": (i32, [vp, vp, sz, vp]),
         "mbq_probe_chase_init": (i32, [vp, sz, ctypes.POINTER(ctypes.c_uint32), vp]),

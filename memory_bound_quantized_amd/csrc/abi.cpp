@@ -968,6 +968,20 @@ int mbq_probe_read(const void* buf, size_t bytes, float* sink, void* stream) {
     return hip_status(mbq::launch_probe_read(buf, bytes, sink, (hipStream_t)stream), fn);
 }
 
+int mbq_probe_mixed(const void* distinct, size_t distinct_bytes, const void* shared, size_t shared_bytes,
+                    int mode, int blocks, float* sink, void* stream) {
+    const char* fn = "mbq_probe_mixed";
+    if (mode < 0 || mode > 3) return fail(MBQ_EINVAL, "%s: mode %d", fn, mode);
+    if (blocks < 1 || blocks > 4096) return fail(MBQ_EINVAL, "%s: blocks must be 1..4096", fn);
+    if (!sink || (mode != 1 && !distinct) || (mode != 0 && !shared))
+        return fail(MBQ_EINVAL, "%s: NULL pointer", fn);
+    if (distinct_bytes % 1024 || shared_bytes % 1024 || !aligned(distinct, 16) || !aligned(shared, 16))
+        return fail(MBQ_EALIGN, "%s: 1 KB granularity, 16-byte aligned buffers", fn);
+    return hip_status(mbq::launch_probe_mixed(distinct, distinct_bytes, shared, shared_bytes, mode, blocks,
+                                              sink, (hipStream_t)stream),
+                      fn);
+}
+
 int mbq_probe_copy(void* dst, const void* src, size_t bytes, void* stream) {
     const char* fn = "mbq_probe_copy";
     if (!dst || !src) return fail(MBQ_EINVAL, "%s: NULL pointer", fn);

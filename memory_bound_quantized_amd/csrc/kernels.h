@@ -199,6 +199,8 @@ hipError_t launch_attention_decode(const float* q, const uint16_t* kc, const uin
 
 hipError_t launch_probe_read(const void* buf, size_t bytes, float* sink, hipStream_t stream);
 hipError_t launch_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+hipError_t launch_probe_mixed(const void* distinct, size_t dbytes, const void* shared, size_t sbytes,
+                              int mode, int blocks, float* sink, hipStream_t stream);
 // Pointer chase over `bytes` of buf: chase_entries(bytes) entries, one per
 // 256 bytes (a power of two; 0 if bytes < 256).
 uint32_t chase_entries(size_t bytes);
