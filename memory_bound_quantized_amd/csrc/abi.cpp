@@ -87,6 +87,18 @@ int check_planes(const mbq_qweight* W, const char* fn) {
     return MBQ_OK;
 }
 
+// An output buffer must not overlap any plane of the weights it is computed
+// from (the kernels read the planes while others write the output).
+int check_out_vs_planes(const mbq_qweight* W, const void* out, size_t out_bytes, const char* fn) {
+    size_t sz[4];
+    if (mbq_plane_sizes(W->fmt, W->N, W->K, sz) != MBQ_OK) return fail(MBQ_EINVAL, "%s: bad shape", fn);
+    const void* p[4] = {W->codes, W->codes_hi, W->scales, W->super_scales};
+    for (int i = 0; i < 4; i++)
+        if (p[i] && overlaps(out, out_bytes, p[i], sz[i]))
+            return fail(MBQ_EINVAL, "%s: the output overlaps weight plane %d", fn, i);
+    return MBQ_OK;
+}
+
 // Kernel limits common to the GEMV paths and the device exports.
 int check_kernel_shape(const mbq_qweight* W, const char* fn) {
     const int64_t kmax = W->fmt == MBQ_FMT_BF16 ? mbq::kMaxKBF16 : mbq::kMaxK;
@@ -318,6 +330,7 @@ int mbq_gemv_q(const mbq_qweight* W, const float* x, int64_t M, int64_t ldx, flo
     const size_t xbytes = (size_t)((M - 1) * ldx + W->K) * 4;
     if (overlaps(x, xbytes, y, ybytes)) return fail(MBQ_EINVAL, "%s: x and y overlap", fn);
     if ((rc = check_planes(W, fn))) return rc;
+    if ((rc = check_out_vs_planes(W, y, ybytes, fn))) return rc;
     if ((rc = check_kernel_shape(W, fn))) return rc;
     const mbq::DevPlanes P = planes_of(W);
     if (M == 1) {
@@ -326,8 +339,8 @@ int mbq_gemv_q(const mbq_qweight* W, const float* x, int64_t M, int64_t ldx, flo
         return hip_status(mbq::launch_gemv_m1(W->fmt, P, W->N, W->K, x, false, y, accumulate,
                                               nullptr, 1, g, s), fn);
     }
-    // Q45 batches on the matrix cores, fp32 x converted as each chunk of it
-    // enters LDS
+    // Q45 batches on the matrix cores, fp32 x converted in registers by the
+    // product
     if (mfma_shape(W->fmt, M, W->K) && aligned(W->scales, 8))
         return hip_status(mbq::launch_gemv_mfma_q45_f32x(P, W->N, W->K, x, ldx, M, y, ldy,
                                                          accumulate, s), fn);
@@ -364,6 +377,7 @@ int mbq_gemv_q_gather(const mbq_qweight* W_all, int64_t rows_per_expert, const i
     if (!aligned(x, 16)) return fail(MBQ_EALIGN, "%s: x must be 16-byte aligned", fn);
     if (overlaps(x, (size_t)W_all->K * 4, y, (size_t)n_out * 4)) return fail(MBQ_EINVAL, "%s: x and y overlap", fn);
     if ((rc = check_planes(W_all, fn))) return rc;
+    if ((rc = check_out_vs_planes(W_all, y, (size_t)n_out * 4, fn))) return rc;
     if ((rc = check_kernel_shape(W_all, fn))) return rc;
     mbq::GemvGeom g = mbq::gemv_m1_default_geom(W_all->fmt, n_out, W_all->K);
     geom_override(&g);
@@ -391,6 +405,7 @@ int mbq_gemv_fused(const mbq_qweight* W, const float* x, const float* gamma, flo
     if (overlaps(x, xb, y, yb) || (gamma && overlaps(gamma, xb, y, yb)))
         return fail(MBQ_EINVAL, "%s: y overlaps x or gamma", fn);
     if ((rc = check_planes(W, fn))) return rc;
+    if ((rc = check_out_vs_planes(W, y, yb, fn))) return rc;
     if ((rc = check_kernel_shape(W, fn))) return rc;
     hipStream_t s = (hipStream_t)stream;
     mbq::GemvGeom g = mbq::gemv_m1_default_geom(W->fmt, W->N, W->K, silu, gamma != nullptr);
@@ -739,6 +754,7 @@ int mbq_gemv_xq(const mbq_qweight* W, const void* xq, int64_t M, float* y, int64
     const size_t xqb = xq_tiled(W->fmt, M, W->K) ? (size_t)mbq::xt_bytes(M, W->K) : (size_t)(M * W->K) * 4;
     if (overlaps(xq, xqb, y, ybytes)) return fail(MBQ_EINVAL, "%s: xq and y overlap", fn);
     if ((rc = check_planes(W, fn))) return rc;
+    if ((rc = check_out_vs_planes(W, y, ybytes, fn))) return rc;
     if ((rc = check_kernel_shape(W, fn))) return rc;
     const mbq::DevPlanes P = planes_of(W);
     if (M == 1) {
@@ -865,6 +881,7 @@ int mbq_dequant_f32(const mbq_qweight* W, float* w_out, void* stream) {
     if (!w_out) return fail(MBQ_EINVAL, "%s: w_out is NULL", fn);
     if (!aligned(w_out, 16)) return fail(MBQ_EALIGN, "%s: w_out must be 16-byte aligned", fn);
     if ((rc = check_planes(W, fn))) return rc;
+    if ((rc = check_out_vs_planes(W, w_out, (size_t)(W->N * W->K) * 4, fn))) return rc;
     if ((rc = check_kernel_shape(W, fn))) return rc;
     return hip_status(mbq::launch_dequant(W->fmt, planes_of(W), W->N, W->K, w_out, (hipStream_t)stream), fn);
 }
@@ -877,6 +894,7 @@ int mbq_unpack_codes(const mbq_qweight* W, uint8_t* codes_out, void* stream) {
     if (W->N == 0 || W->K == 0) return ok();
     if (!codes_out) return fail(MBQ_EINVAL, "%s: codes_out is NULL", fn);
     if ((rc = check_planes(W, fn))) return rc;
+    if ((rc = check_out_vs_planes(W, codes_out, (size_t)(W->N * W->K), fn))) return rc;
     if ((rc = check_kernel_shape(W, fn))) return rc;
     return hip_status(mbq::launch_unpack_codes(W->fmt, planes_of(W), W->N, W->K, codes_out, (hipStream_t)stream), fn);
 }
