@@ -568,6 +568,27 @@ def rows_bench(mbq, workloads, torch, dev, peak_gbs, one_launch=True, keep=None)
     del Ws, W0, X, Xq, Y
     torch.cuda.empty_cache()
 
+    # ---- the 4096 x 12288 Q45 table (the down projection's shape): the
+    # matrix-core product with K whole per workgroup, and split in 4 along K
+    # through a workspace (mbq_gemv_xq_ws)
+    fmt, N, K = 1, 4096, 12288
+    W0 = mbq.QWeight.from_host(fmt, N, K, workloads.weight_planes(np.random.default_rng(4), fmt, N, K))
+    Ws = rotated(W0)
+    down = {}
+    for M in (16, 64, 512):
+        X = torch.from_numpy(np.random.default_rng(M).normal(size=(M, K)).astype(np.float32)).to(dev)
+        Xq = mbq.stage_x(fmt, X)
+        Y = torch.empty((M, N), device=dev)
+        ws = mbq.gemv_xq_workspace(W0, M)
+        whole_us = per_launch_us(lambda W: mbq.gemv_xq(W, Xq, M=M, out=Y), Ws, 60)
+        split_us = per_launch_us(lambda W: mbq.gemv_xq_ws(W, Xq, M, ws, out=Y), Ws, 60)
+        down["M%d" % M] = {"product_us": round(whole_us, 2), "split_product_us": round(split_us, 2),
+                           "split_useful_tflops": round(2.0 * M * N * K / (split_us * 1e-6) / 1e12, 1)}
+        del X, Xq, Y, ws
+    rows["down_4096x12288_q45_k_split"] = down
+    del Ws, W0
+    torch.cuda.empty_cache()
+
     # ---- the quantizer: fp32 weights to each format's planes, 12288 x 4096
     # (two inputs of 201 MB alternate, so that neither stays in the 256 MB
     # Infinity Cache)

@@ -321,6 +321,28 @@ int mbq_stage_x(int fmt, const float* x, int64_t M, int64_t ldx, int64_t K, void
 int mbq_gemv_xq(const mbq_qweight* W, const void* xq, int64_t M, float* y, int64_t ldy,
                 int accumulate, void* stream);
 
+/* Bytes of workspace mbq_gemv_xq_ws takes for W and M tokens: 0 where it
+ * does not split (then it is mbq_gemv_xq).  Host only.  MBQ_EINVAL for a
+ * NULL W or bytes, or a negative shape. */
+int mbq_gemv_xq_workspace_bytes(const mbq_qweight* W, int64_t M, size_t* bytes);
+
+/* mbq_gemv_xq for the matrix-core tile form with K split across workgroups
+ * ([roofline-holds] "The Math": the weights are read once whatever the
+ * batch; here each compute unit also reads only a share of the batch's x).
+ * S workgroups (S = 2 or 4) each cover S times the rows over 1/S of K and
+ * write their partial tile into the workspace; the last of them to finish
+ * adds the S partials in fixed order, so the result does not depend on
+ * timing.  Same sums as mbq_gemv_xq up to the rounding of that split (not
+ * bit for bit).  Where mbq_gemv_xq_workspace_bytes is 0 this is mbq_gemv_xq
+ * and the workspace is not touched.
+ * workspace: device, 256-byte aligned, at least mbq_gemv_xq_workspace_bytes
+ * bytes, overlapping none of xq, y and W's planes; it must be all zero before
+ * the first call (hipMemset once), and every call leaves it all zero.  Calls
+ * that overlap in time on one workspace race.  Other arguments and errors as
+ * mbq_gemv_xq; MBQ_EINVAL for a small workspace. */
+int mbq_gemv_xq_ws(const mbq_qweight* W, const void* xq, int64_t M, float* y, int64_t ldy,
+                   int accumulate, void* workspace, size_t workspace_bytes, void* stream);
+
 /* RMSNorm of one row of n values (as mbq_rmsnorm) that also writes its output
  * in staged form for fmt: the norm before a product, fused with the staging of
  * the product's input.  y: device fp32 [n] or NULL (then only xq is written);

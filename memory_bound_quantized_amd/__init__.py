@@ -183,6 +183,31 @@ def gemv_xq(W: QWeight, xq, M: int = 1, out=None, accumulate: bool = False, stre
     return out
 
 
+def gemv_xq_workspace_bytes(W: QWeight, M: int) -> int:
+    out = ctypes.c_size_t()
+    check(lib.mbq_gemv_xq_workspace_bytes(ctypes.byref(W.desc), M, ctypes.byref(out)))
+    return int(out.value)
+
+
+def gemv_xq_workspace(W: QWeight, M: int, device="cuda"):
+    """A zero-filled workspace for gemv_xq_ws (calls leave it zero)."""
+    import torch
+    n = max(gemv_xq_workspace_bytes(W, M), 256)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def gemv_xq_ws(W: QWeight, xq, M: int, workspace, out=None, accumulate: bool = False, stream=None):
+    """gemv_xq with K split across workgroups through a zero-filled workspace."""
+    import torch
+    if out is None:
+        out = torch.empty((M, W.N) if M > 1 else (W.N,), dtype=torch.float32, device=xq.device)
+    y2 = out if out.dim() == 2 else out.view(1, -1)
+    check(lib.mbq_gemv_xq_ws(ctypes.byref(W.desc), _ptr(xq), M, _ptr(y2),
+                             y2.stride(0) if M > 1 else W.N, int(bool(accumulate)), _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
 def rmsnorm_xq(x, gamma, eps: float, fmt: int, xq=None, out=None, write_y: bool = True,
                stream=None):
     """One row: y = rmsnorm(x) (unless write_y is False) and its staged form for fmt.

@@ -19,7 +19,8 @@ EXPORTS = (
     "mbq_format_info", "mbq_plane_sizes", "mbq_pack", "mbq_unpack", "mbq_gemv_q",
     "mbq_gemv_q_gather", "mbq_gemv_fused", "mbq_decode_workspace_bytes", "mbq_decode_step",
     "mbq_decode_step_noalloc", "mbq_decode_prepare", "mbq_decode_step_persistent",
-    "mbq_xq_bytes", "mbq_stage_x", "mbq_gemv_xq", "mbq_rmsnorm_xq",
+    "mbq_xq_bytes", "mbq_stage_x", "mbq_gemv_xq", "mbq_gemv_xq_workspace_bytes", "mbq_gemv_xq_ws",
+    "mbq_rmsnorm_xq",
     "mbq_silu_mul_xq", "mbq_rmsnorm", "mbq_layernorm", "mbq_silu_mul", "mbq_dequant_f32",
     "mbq_unpack_codes", "mbq_quantize", "mbq_attention_workspace_bytes", "mbq_attention_decode", "mbq_probe_read", "mbq_probe_copy", "mbq_probe_mixed", "mbq_probe_chase_init",
     "mbq_probe_chase", "mbq_probe_peak", "mbq_status_str",
@@ -89,6 +90,8 @@ def _load():
         "mbq_xq_bytes": (i32, [i32, i64, i64, ctypes.POINTER(sz)]),
         "mbq_stage_x": (i32, [i32, vp, i64, i64, i64, vp, vp]),
         "mbq_gemv_xq": (i32, [ctypes.POINTER(QWeightDesc), vp, i64, vp, i64, i32, vp]),
+        "mbq_gemv_xq_workspace_bytes": (i32, [ctypes.POINTER(QWeightDesc), i64, ctypes.POINTER(sz)]),
+        "mbq_gemv_xq_ws": (i32, [ctypes.POINTER(QWeightDesc), vp, i64, vp, i64, i32, vp, sz, vp]),
         "mbq_rmsnorm_xq": (i32, [vp, vp, f32, i64, vp, i32, vp, vp]),
         "mbq_silu_mul_xq": (i32, [vp, vp, i64, i32, vp, vp]),
         "mbq_rmsnorm": (i32, [vp, vp, f32, i64, i64, vp, vp]),

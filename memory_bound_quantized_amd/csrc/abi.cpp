@@ -785,6 +785,47 @@ int mbq_gemv_xq(const mbq_qweight* W, const void* xq, int64_t M, float* y, int64
     return ok();
 }
 
+int mbq_gemv_xq_workspace_bytes(const mbq_qweight* W, int64_t M, size_t* bytes) {
+    const char* fn = "mbq_gemv_xq_workspace_bytes";
+    if (!W) return fail(MBQ_EINVAL, "%s: W is NULL", fn);
+    if (!bytes) return fail(MBQ_EINVAL, "%s: bytes is NULL", fn);
+    if (M < 0 || W->N < 0 || W->K < 0) return fail(MBQ_EINVAL, "%s: negative shape", fn);
+    *bytes = mfma_shape(W->fmt, M, W->K) && W->N > 0 && M <= 65535
+                 ? mbq::mfma_split_workspace_bytes(W->N, W->K, M) : 0;
+    return ok();
+}
+
+int mbq_gemv_xq_ws(const mbq_qweight* W, const void* xq, int64_t M, float* y, int64_t ldy,
+                   int accumulate, void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "mbq_gemv_xq_ws";
+    int rc = check_weight(W, fn);
+    if (rc) return rc;
+    size_t need = 0;
+    if ((rc = mbq_gemv_xq_workspace_bytes(W, M, &need))) return fail(rc, "%s: %s", fn, g_err.c_str());
+    if (need == 0) return mbq_gemv_xq(W, xq, M, y, ldy, accumulate, stream);
+    if (ldy < W->N) return fail(MBQ_EINVAL, "%s: ldy < N", fn);
+    if (accumulate != 0 && accumulate != 1) return fail(MBQ_EINVAL, "%s: accumulate must be 0 or 1", fn);
+    if (!xq || !y) return fail(MBQ_EINVAL, "%s: xq or y is NULL", fn);
+    if (!workspace) return fail(MBQ_EINVAL, "%s: workspace is NULL", fn);
+    if (workspace_bytes < need)
+        return fail(MBQ_EINVAL, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, need);
+    if (!aligned(y, 4)) return fail(MBQ_EALIGN, "%s: y must be 4-byte aligned", fn);
+    if (!aligned(xq, 16) || !aligned(workspace, 256))
+        return fail(MBQ_EALIGN, "%s: xq must be 16-byte and workspace 256-byte aligned", fn);
+    const size_t ybytes = (size_t)((M - 1) * ldy + W->N) * 4;
+    const size_t xqb = (size_t)mbq::xt_bytes(M, W->K);
+    if (overlaps(xq, xqb, y, ybytes)) return fail(MBQ_EINVAL, "%s: xq and y overlap", fn);
+    if (overlaps(workspace, need, y, ybytes) || overlaps(workspace, need, xq, xqb))
+        return fail(MBQ_EINVAL, "%s: the workspace overlaps xq or y", fn);
+    if ((rc = check_planes(W, fn))) return rc;
+    if ((rc = check_out_vs_planes(W, y, ybytes, fn))) return rc;
+    if ((rc = check_out_vs_planes(W, workspace, need, fn))) return rc;
+    if ((rc = check_kernel_shape(W, fn))) return rc;
+    if (!aligned(W->scales, 8)) return fail(MBQ_EALIGN, "%s: the matrix-core kernel needs 8-byte aligned scales", fn);
+    return hip_status(mbq::launch_gemv_mfma_q45_ws(planes_of(W), W->N, W->K, xq, M, y, ldy, accumulate,
+                                                   workspace, (hipStream_t)stream), fn);
+}
+
 static int check_norm(const float* x, const float* gamma, const float* beta, bool need_beta,
                       float eps, int64_t rows, int64_t n, const float* y, const char* fn) {
     if (rows < 0 || n < 0) return fail(MBQ_EINVAL, "%s: negative shape", fn);

@@ -263,16 +263,19 @@ struct QuadOps {
 // SIMD is the occupancy it needs.  Telling the compiler so keeps it from
 // sinking the next quad's loads next to their uses to save registers for an
 // occupancy the grid never reaches.
-template <int MW, int TT, int RW, int NSTEP, bool F32X>
+template <int MW, int TT, int RW, int NSTEP, bool F32X, int S>
 __global__ __launch_bounds__(MW * kWave) __attribute__((amdgpu_waves_per_eu(MW / 4, MW / 4))) void gemv_mfma_q45_kernel(
         DevPlanes P, int N, int K, const uint8_t* __restrict__ xt, const float* __restrict__ xf,
-        int64_t ldx, int M, float* __restrict__ y, int64_t ldy, int accumulate) {
+        int64_t ldx, int M, float* __restrict__ y, int64_t ldy, int accumulate,
+        float* __restrict__ part, uint32_t* __restrict__ ctr) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int g = lane >> 4, j = lane & 15;
-    const int nq = K / 128;
+    // K split S ways (gridDim.z = S): workgroup z takes quads z nq .. z nq + nq - 1
+    const int z = S > 1 ? (int)blockIdx.z : 0;
+    const int nq = K / 128 / S, qbase = z * nq;
     const int nstep = NSTEP > 0 ? NSTEP : (nq + MW - 1) / MW;
     const int row0 = blockIdx.x * (16 * RW);
     const int tt0 = blockIdx.y * TT;               // first token tile
@@ -321,7 +324,7 @@ __global__ __launch_bounds__(MW * kWave) __attribute__((amdgpu_waves_per_eu(MW /
     // quad of step s: the waves interleave, so that two adjacent waves read
     // the two halves of each 128-byte line of a row at about the same time;
     // past the end (run-time K only) the last quad is read again and not used
-    auto quad = [&](int s) __attribute__((always_inline)) { return min(wave + MW * s, nq - 1); };
+    auto quad = [&](int s) __attribute__((always_inline)) { return qbase + min(wave + MW * s, nq - 1); };
     auto load_w = [&](Q& q, int u) __attribute__((always_inline)) {
 #pragma unroll
         for (int rt = 0; rt < RW; rt++) {
@@ -450,24 +453,87 @@ __global__ __launch_bounds__(MW * kWave) __attribute__((amdgpu_waves_per_eu(MW /
         for (int r = 0; r < 4; r++) {
             const int m = (tt0 + tt) * 16 + 4 * g + r;
             if (m < M) {
-                float* dst = y + (int64_t)m * ldy + n;
-                *dst = accumulate ? *dst + s[r] : s[r];
+                if constexpr (S > 1) {
+                    __hip_atomic_store(part + ((int64_t)z * M + m) * N + n, s[r], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                } else {
+                    float* dst = y + (int64_t)m * ldy + n;
+                    *dst = accumulate ? *dst + s[r] : s[r];
+                }
             }
         }
     }
+    if constexpr (S > 1) {
+        // K split: the last of the S workgroups of this tile to finish adds
+        // the partial tiles in split order (the sums do not depend on which
+        // one is last), then zeroes them and the tile's counter, so that
+        // every call leaves the workspace as it found it: all zero.
+        // Ordering without cache maintenance: the partials and the counter
+        // are only ever accessed as agent-scope atomics, which the compiler
+        // makes coherent across the compute dies by writing through and
+        // reading past their L2s; each wave waits for its partial stores to
+        // complete before the barrier that precedes the counter increment,
+        // and the last workgroup reads the partials only after the increment
+        // returns.  An agent-scope release/acquire pair would do the same by
+        // writing back and invalidating each die's whole L2, which throws
+        // away the L2-resident x of every other workgroup on that die.
+        __builtin_amdgcn_s_waitcnt(0);                   // every counter, stores included
+        __syncthreads();
+        uint32_t* c = ctr + (blockIdx.y * gridDim.x + blockIdx.x);
+        __shared__ int last;
+        if (tid == 0)
+            last = __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(S - 1);
+        __syncthreads();
+        if (!last) return;
+        // each thread's NOUT outputs: every load issued before any is used
+        // (one memory round trip); rows and tokens past the end read a
+        // clamped address of this tile and store nothing
+        constexpr int NOUT = 16 * RW * 16 * TT / (MW * kWave);
+        static_assert(NOUT * MW * kWave == 16 * RW * 16 * TT, "tile not a multiple of the workgroup");
+        float t[NOUT][S], y0[NOUT];
+        int64_t pi[NOUT], yi[NOUT];
+        bool ok[NOUT];
+#pragma unroll
+        for (int i = 0; i < NOUT; i++) {
+            const int o = tid + i * MW * kWave;
+            const int n = row0 + o % (16 * RW), m = tt0 * 16 + o / (16 * RW);
+            ok[i] = n < N && m < M;
+            const int nc = min(n, N - 1), mc = min(m, M - 1);
+            pi[i] = (int64_t)mc * N + nc;
+            yi[i] = (int64_t)mc * ldy + nc;
+#pragma unroll
+            for (int zz = 0; zz < S; zz++)
+                t[i][zz] = __hip_atomic_load(part + pi[i] + (int64_t)zz * M * N, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+            y0[i] = accumulate ? y[yi[i]] : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < NOUT; i++) {
+            if (!ok[i]) continue;
+            float v = t[i][0];
+#pragma unroll
+            for (int zz = 1; zz < S; zz++) v += t[i][zz];
+#pragma unroll
+            for (int zz = 0; zz < S; zz++)
+                __hip_atomic_store(part + pi[i] + (int64_t)zz * M * N, 0.f, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            y[yi[i]] = accumulate ? y0[i] + v : v;
+        }
+        if (tid == 0) __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
-template <int MW, int TT, int RW, int NSTEP, bool F32X>
+template <int MW, int TT, int RW, int NSTEP, bool F32X, int S = 1>
 static hipError_t launch_k(DevPlanes P, int64_t N, int64_t K, const uint8_t* xt, const float* xf,
                            int64_t ldx, int64_t M, float* y, int64_t ldy, int accumulate,
-                           hipStream_t stream) {
+                           hipStream_t stream, float* part = nullptr, uint32_t* ctr = nullptr) {
     constexpr size_t lds = (size_t)MW * RW * TT * kWave * 16;
-    auto kern = gemv_mfma_q45_kernel<MW, TT, RW, NSTEP, F32X>;
-    if (hipError_t e = ensure_lds<gemv_mfma_q45_kernel<MW, TT, RW, NSTEP, F32X>>(lds)) return e;
+    auto kern = gemv_mfma_q45_kernel<MW, TT, RW, NSTEP, F32X, S>;
+    if (hipError_t e = ensure_lds<gemv_mfma_q45_kernel<MW, TT, RW, NSTEP, F32X, S>>(lds)) return e;
     const int64_t ntt = (M + 15) / 16;
-    const dim3 grid((unsigned)((N + 16 * RW - 1) / (16 * RW)), (unsigned)((ntt + TT - 1) / TT));
+    const dim3 grid((unsigned)((N + 16 * RW - 1) / (16 * RW)), (unsigned)((ntt + TT - 1) / TT), (unsigned)S);
     hipLaunchKernelGGL(kern, grid, dim3(MW * kWave), lds, stream, P, (int)N, (int)K, xt, xf, ldx,
-                       (int)M, y, ldy, accumulate);
+                       (int)M, y, ldy, accumulate, part, ctr);
     return hipGetLastError();
 }
 
@@ -534,6 +600,103 @@ hipError_t launch_gemv_mfma_q45(DevPlanes P, int64_t N, int64_t K, const void* x
     case 1: return launch_tt<1, false>(P, N, K, x, nullptr, 0, M, y, ldy, accumulate, stream);
     case 2: return launch_tt<2, false>(P, N, K, x, nullptr, 0, M, y, ldy, accumulate, stream);
     default: return launch_tt<4, false>(P, N, K, x, nullptr, 0, M, y, ldy, accumulate, stream);
+    }
+}
+
+// ---- the K split (the workspace-taking entry point) -------------------------
+// Every compute unit of the stream above reads all of x for its rows.  Split
+// S ways along K, a workgroup covers S times the rows over 1/S of K, so it
+// reads 1/S of the x for the same weights; the S partial tiles meet in the
+// workspace, and the last workgroup of a tile adds them (about 2 us of
+// memory round trips at the end).  Shapes by the unsplit row tiles per
+// workgroup, rw1 = N / 4096 rounded up: rw1 = 1 splits in 4 (4 row tiles),
+// rw1 = 2 or 3 in 2 (4 or 6 row tiles), more rows not at all.  Where it
+// pays, measured on the 36-layer model's tables (graphs of cold launches):
+//   rw1 = 1: K >= 12288 (4096 x 12288: 19.5 -> 16.0 us at 16 tokens,
+//            49.6 -> 35.0 at 64, 310 -> 218 at 512), or more than 32 tokens
+//            (4096 x 4096: 16.7 -> 15.9 at 64, 100 -> 88 at 512; 8.1 -> 8.5
+//            at 16, where each part has one step per wave);
+//   rw1 = 2: more than 32 tokens (6144 x 4096: 21.4 -> 20.8 at 64, 108 ->
+//            102 at 512; 10.2 -> 11.6 at 16);
+//   rw1 = 3: K >= 12288 and more than 32 tokens (12288 x 12288: 88.5 ->
+//            81.9 at 64; 12288 x 4096 is slower split at every batch, 14.1
+//            -> 16.4 at 16 and 30.0 -> 35.7 at 64).
+// It also needs K / 128 to be a whole number of steps of every part.
+// MBQ_MFMA_SPLIT (tuning): 1 never splits, 2 splits every shape that has a
+// split form.
+SplitPlan mfma_split_plan(int64_t N, int64_t K, int64_t M) {
+    SplitPlan p{1, 0, 0, 0};
+    const int64_t ntt = (M + 15) / 16;
+    const int tt = pick_tt(M);
+    const int mw = tt == 4 ? 4 : 8;
+    const int64_t rw1 = (N + 16 * 256 - 1) / (16 * 256);
+    const int64_t nq = K / 128;
+    int S = rw1 == 1 ? 4 : (rw1 <= 3 ? 2 : 1);
+    bool want = rw1 == 1 ? (K >= 12288 || M > 32) : rw1 == 2 ? M > 32 : (K >= 12288 && M > 32);
+    if (const char* e = tuning_var("MBQ_MFMA_SPLIT")) {
+        const int v = atoi(e);
+        if (v == 1) want = false;
+        if (v == 2) want = true;
+    }
+    // two token tiles of 6 row tiles spill in the run-time-K loop
+    if (tt == 2 && rw1 == 3 && K != 4096 && K != 12288) want = false;
+    if (want && S > 1 && N > 0 && M > 0 && nq % (S * mw) == 0) {
+        p.S = S;
+        p.RW = (int)(S * rw1);
+        p.gx = (N + 16 * p.RW - 1) / (16 * p.RW);
+        p.gy = (ntt + tt - 1) / tt;
+    }
+    return p;
+}
+
+// Workspace: one counter per output tile, then the partial tiles
+// [S][M][N] fp32 from the next 256-byte boundary.
+static size_t split_ctr_bytes(const SplitPlan& p) {
+    return ((size_t)p.gx * (size_t)p.gy * 4 + 255) / 256 * 256;
+}
+
+size_t mfma_split_workspace_bytes(int64_t N, int64_t K, int64_t M) {
+    const SplitPlan p = mfma_split_plan(N, K, M);
+    if (p.S == 1) return 0;
+    return split_ctr_bytes(p) + (size_t)p.S * (size_t)M * (size_t)N * 4;
+}
+
+template <int TT, int RW, int S>
+static hipError_t launch_split_s(DevPlanes P, int64_t N, int64_t K, const uint8_t* xt, int64_t M, float* y,
+                                 int64_t ldy, int accumulate, hipStream_t s, float* part, uint32_t* ctr) {
+    constexpr int MW = TT == 4 ? 4 : 8, KS = S * MW * 128;   // values per step of all S parts
+    // four token tiles of 6 row tiles spill as a straight-line stream
+    if constexpr (TT == 4 && RW == 6) {
+        return launch_k<MW, TT, RW, 0, false, S>(P, N, K, xt, nullptr, 0, M, y, ldy, accumulate, s, part, ctr);
+    } else {
+        if constexpr (4096 % KS == 0)
+            if (K == 4096) return launch_k<MW, TT, RW, 4096 / KS, false, S>(P, N, K, xt, nullptr, 0, M, y, ldy, accumulate, s, part, ctr);
+        if constexpr (TT < 4 && 12288 % KS == 0)
+            if (K == 12288) return launch_k<MW, TT, RW, 12288 / KS, false, S>(P, N, K, xt, nullptr, 0, M, y, ldy, accumulate, s, part, ctr);
+        return launch_k<MW, TT, RW, 0, false, S>(P, N, K, xt, nullptr, 0, M, y, ldy, accumulate, s, part, ctr);
+    }
+}
+
+template <int TT>
+static hipError_t launch_split_tt(DevPlanes P, int64_t N, int64_t K, const uint8_t* xt, int64_t M, float* y,
+                                  int64_t ldy, int accumulate, hipStream_t s, float* part, uint32_t* ctr,
+                                  const SplitPlan& p) {
+    if (p.RW == 6) return launch_split_s<TT, 6, 2>(P, N, K, xt, M, y, ldy, accumulate, s, part, ctr);
+    if (p.S == 2) return launch_split_s<TT, 4, 2>(P, N, K, xt, M, y, ldy, accumulate, s, part, ctr);
+    return launch_split_s<TT, 4, 4>(P, N, K, xt, M, y, ldy, accumulate, s, part, ctr);
+}
+
+hipError_t launch_gemv_mfma_q45_ws(DevPlanes P, int64_t N, int64_t K, const void* xt, int64_t M, float* y,
+                                   int64_t ldy, int accumulate, void* ws, hipStream_t stream) {
+    const SplitPlan p = mfma_split_plan(N, K, M);
+    if (p.S == 1) return launch_gemv_mfma_q45(P, N, K, xt, M, y, ldy, accumulate, stream);
+    const uint8_t* x = (const uint8_t*)xt;
+    uint32_t* ctr = (uint32_t*)ws;
+    float* part = (float*)((uint8_t*)ws + split_ctr_bytes(p));
+    switch (pick_tt(M)) {
+    case 1: return launch_split_tt<1>(P, N, K, x, M, y, ldy, accumulate, stream, part, ctr, p);
+    case 2: return launch_split_tt<2>(P, N, K, x, M, y, ldy, accumulate, stream, part, ctr, p);
+    default: return launch_split_tt<4>(P, N, K, x, M, y, ldy, accumulate, stream, part, ctr, p);
     }
 }
 

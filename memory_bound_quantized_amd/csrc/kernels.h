@@ -116,6 +116,18 @@ hipError_t launch_gemv_mfma_q45(DevPlanes P, int64_t N, int64_t K, const void* x
 // converted while the slabs are filled, with a power of two per 32-weight
 // block and token: no staging launch or buffer.  K % 1024 == 0; passes of
 // 16 tokens.
+// The K-split form of the staged product (gemv_mfma.hip): the plan (S = 1:
+// no split) and its workspace, one counter per output tile then the partial
+// tiles; the workspace must be all zero before a call, and every call
+// leaves it all zero.
+struct SplitPlan {
+    int S, RW;
+    int64_t gx, gy;
+};
+SplitPlan mfma_split_plan(int64_t N, int64_t K, int64_t M);
+size_t mfma_split_workspace_bytes(int64_t N, int64_t K, int64_t M);
+hipError_t launch_gemv_mfma_q45_ws(DevPlanes P, int64_t N, int64_t K, const void* xt, int64_t M, float* y,
+                                   int64_t ldy, int accumulate, void* ws, hipStream_t stream);
 hipError_t launch_gemv_mfma_q45_f32x(DevPlanes P, int64_t N, int64_t K, const float* x,
                                      int64_t ldx, int64_t M, float* y, int64_t ldy,
                                      int accumulate, hipStream_t stream);

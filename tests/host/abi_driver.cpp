@@ -101,6 +101,22 @@ static void argument_checks() {
     CHECK(mbq_xq_bytes(1, 16, 100, &b) == MBQ_EINVAL);
     CHECK(mbq_xq_bytes(9, 16, 4096, &b) == MBQ_EINVAL);
     CHECK(mbq_stage_x(1, x, 2, 100, 4096, fake(0xA00000), nullptr) == MBQ_EINVAL);
+    {
+        // the K-split product: the workspace size is host arithmetic, the
+        // workspace is checked before any launch
+        mbq_qweight d = qw(1, 4096, 12288);
+        CHECK(mbq_gemv_xq_workspace_bytes(&d, 16, &b) == MBQ_OK && b == 256 + 4ull * 16 * 4096 * 4);
+        CHECK(mbq_gemv_xq_workspace_bytes(&d, 5, &b) == MBQ_OK && b == 0);
+        CHECK(mbq_gemv_xq_workspace_bytes(nullptr, 16, &b) == MBQ_EINVAL);
+        const size_t need = 256 + 4ull * 16 * 4096 * 4;
+        void* xq = fake(0x4000000);
+        float* yq = (float*)fake(0x5000000);
+        CHECK(mbq_gemv_xq_ws(&d, xq, 16, yq, 4096, 0, nullptr, need, nullptr) == MBQ_EINVAL);
+        CHECK(mbq_gemv_xq_ws(&d, xq, 16, yq, 4096, 0, fake(0x6000000), need - 1, nullptr) == MBQ_EINVAL);
+        CHECK(mbq_gemv_xq_ws(&d, xq, 16, yq, 4096, 0, fake(0x6000010), need, nullptr) == MBQ_EALIGN);
+        CHECK(mbq_gemv_xq_ws(&d, xq, 16, yq, 4096, 0, fake(0x5000100), need, nullptr) == MBQ_EINVAL);
+        CHECK(mbq_gemv_xq_ws(&d, xq, 16, yq, 4096, 0, fake(0), need, nullptr) == MBQ_EINVAL);
+    }
     CHECK(mbq_rmsnorm(x, (float*)fake(0x500000), -1.0f, 1, 4096, y, nullptr) == MBQ_EINVAL);
     CHECK(mbq_layernorm(x, nullptr, nullptr, 1e-5f, 1, 2048, y, nullptr) == MBQ_EINVAL);
     void* pl[4] = {fake(0x1000000), nullptr, fake(0x3000000), nullptr};

@@ -30,7 +30,7 @@ def _declared_symbols():
 
 def test_library_exports_every_declared_symbol():
     declared = _declared_symbols()
-    assert len(declared) == 34
+    assert len(declared) == 36
     assert sorted(_lib.EXPORTS) == declared
     lib = ctypes.CDLL(_lib.LIB_PATH)
     for name in declared:
@@ -234,6 +234,49 @@ def test_staged_x_argument_checks():
     assert sm(n=100) == _lib.EINVAL
     assert sm(g=BASE + 0x400008) == _lib.EALIGN
     assert sm(xq=BASE + 0x500000) == _lib.EINVAL                            # xq overlaps u
+
+
+def test_split_product_argument_checks():
+    """mbq_gemv_xq_workspace_bytes is host arithmetic: a counter per output
+    tile (rounded up to 256 bytes), then S partial tiles of M x N fp32; 0
+    where the plan does not split.  mbq_gemv_xq_ws checks its workspace
+    before any device call."""
+    sz = ctypes.c_size_t()
+    wb = lambda N, K, M: (L.mbq_gemv_xq_workspace_bytes(ctypes.byref(_desc(N=N, K=K)), M, ctypes.byref(sz)), sz.value)
+    r256 = lambda b: (b + 255) // 256 * 256
+    # 4096 x 12288: four parts of 4 row tiles (64 workgroups per part) at any batch
+    assert wb(4096, 12288, 16) == (_lib.OK, r256(64 * 4) + 4 * 16 * 4096 * 4)
+    assert wb(4096, 12288, 100) == (_lib.OK, r256(64 * 2 * 4) + 4 * 100 * 4096 * 4)
+    # 4096 x 4096 and 6144 x 4096: split above 32 tokens only
+    assert wb(4096, 4096, 16) == (_lib.OK, 0)
+    assert wb(4096, 4096, 64) == (_lib.OK, r256(64 * 4) + 4 * 64 * 4096 * 4)
+    assert wb(6144, 4096, 32) == (_lib.OK, 0)
+    assert wb(6144, 4096, 33) == (_lib.OK, r256(96 * 4) + 2 * 33 * 6144 * 4)
+    # 12288 rows: two parts of 6 row tiles, for K >= 12288 above 32 tokens
+    assert wb(12288, 12288, 64) == (_lib.OK, r256(128 * 4) + 2 * 64 * 12288 * 4)
+    assert wb(12288, 12288, 16) == (_lib.OK, 0)
+    assert wb(12288, 4096, 64) == (_lib.OK, 0)
+    assert wb(12288, 4096, 5) == (_lib.OK, 0)          # vector units
+    assert wb(1000, 8192, 64) == (_lib.OK, r256(16 * 4) + 4 * 64 * 1000 * 4)
+    assert wb(1000, 1024, 64) == (_lib.OK, 0)          # 8 quads: not a step of 4 parts of 4 waves
+    assert wb(20000, 12288, 64) == (_lib.OK, 0)        # 5 row tiles per unit
+    assert wb(4096, 12000, 16) == (_lib.OK, 0)         # K % 128 != 0: row form
+    assert L.mbq_gemv_xq_workspace_bytes(None, 16, ctypes.byref(sz)) == _lib.EINVAL
+    assert L.mbq_gemv_xq_workspace_bytes(ctypes.byref(_desc()), -1, ctypes.byref(sz)) == _lib.EINVAL
+    d = _desc(N=4096, K=12288)
+    need = 256 + 4 * 16 * 4096 * 4
+    xq, y, ws = BASE + 0x4000000, BASE + 0x5000000, BASE + 0x6000000
+    g = lambda xq=xq, y=y, ws=ws, wsb=need, acc=0, ldy=4096: \
+        L.mbq_gemv_xq_ws(ctypes.byref(d), xq, 16, y, ldy, acc, ws, wsb, None)
+    assert g(ws=None) == _lib.EINVAL
+    assert g(wsb=need - 1) == _lib.EINVAL
+    assert g(ws=ws + 16) == _lib.EALIGN
+    assert g(ws=y + 256) == _lib.EINVAL                                      # overlaps y
+    assert g(ws=xq) == _lib.EINVAL                                           # overlaps xq
+    assert g(ws=BASE) == _lib.EINVAL                                         # overlaps the codes
+    assert g(acc=2) == _lib.EINVAL
+    assert g(ldy=100) == _lib.EINVAL
+    assert g(xq=None) == _lib.EINVAL
 
 
 def test_fused_gemv_argument_checks():
