@@ -419,8 +419,13 @@ def _attn(q=BASE, k=BASE + 0x1000000, v=BASE + 0x2000000, T=512, ld=1024, H=32, 
 
 def test_attention_argument_checks():
     sz = ctypes.c_size_t()
+    # one 132-float record per query head and chunk: 512 positions in 16
+    # chunks of 32
     assert L.mbq_attention_workspace_bytes(512, 32, 8, 128, ctypes.byref(sz)) == _lib.OK
-    assert sz.value > 0
+    assert sz.value == 32 * 16 * 132 * 4
+    # 40000 positions: chunks of 256, 157 of them; 200 heads of their own
+    assert L.mbq_attention_workspace_bytes(40000, 200, 200, 128, ctypes.byref(sz)) == _lib.OK
+    assert sz.value == 200 * 157 * 132 * 4
     assert L.mbq_attention_workspace_bytes(0, 32, 8, 128, ctypes.byref(sz)) == _lib.EINVAL
     assert L.mbq_attention_workspace_bytes(512, 32, 8, 64, ctypes.byref(sz)) == _lib.EUNSUPPORTED
     assert L.mbq_attention_workspace_bytes(512, 24, 8, 128, ctypes.byref(sz)) == _lib.EUNSUPPORTED  # G = 3

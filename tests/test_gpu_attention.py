@@ -14,8 +14,9 @@ a few 1e-4).
 Cases: the 36-layer model's shape (32 query heads on 8 key/value heads of
 128) at 512 positions, one position, ragged counts across chunk edges, long
 contexts split into many chunks, every group size the kernels take, a row
-stride wider than the heads, scores of several hundred (the max shift), and
-equal keys (uniform weights).
+stride wider than the heads, scores of several hundred (the max shift),
+equal keys (uniform weights), and one workspace full of NaN serving calls
+of every length in turn (its contents need no initialisation).
 """
 import numpy as np
 import pytest
@@ -135,3 +136,22 @@ def test_equal_keys_average_the_values():
     mean = vc.astype(np.float64).mean(axis=0).reshape(Hkv, D)
     for h in range(H):
         assert np.max(np.abs(out[h] - mean[h // 4])) <= 2.0 ** -18 * np.abs(vc).max()
+
+
+def test_workspace_needs_no_initialisation():
+    """The workspace is scratch: one sized for the longest call, filled with
+    NaN and then used by calls of other lengths in turn, gives the oracle's
+    result every time."""
+    print("attention NaN workspace", flush=True)
+    rng = np.random.default_rng(11)
+    H, Hkv, Tmax = 32, 8, 5000
+    kc, vc = cache(rng, Tmax, Hkv * D)
+    q = rng.normal(size=H * D).astype(np.float32)
+    qd = torch.from_numpy(q).cuda()
+    kd = torch.from_numpy(kc.view(np.int16)).cuda()
+    vd = torch.from_numpy(vc.view(np.int16)).cuda()
+    nb = mbq().attention_workspace_bytes(Tmax, H, Hkv)
+    ws = torch.full(((nb + 15) // 16 * 4,), float("nan"), dtype=torch.float32, device="cuda")
+    for T in (5000, 17, 600, 1, 4096, 5000):
+        out = mbq().attention_decode(qd, kd, vd, H, Hkv, T=T, workspace=ws)
+        check(out.cpu().numpy(), q, kc, vc, H, Hkv, T)
