@@ -846,6 +846,13 @@ def main():
     g_norm = capture(lambda: [mbq.rmsnorm(xr, gr, c1["eps"], out=yr) for _ in range(nrm)])
     g_norm.replay()
     rms_us = timed(g_norm, 20, stream) / (20 * nrm) * 1e3
+    # the same graph of one-workgroup launches that read nothing: what a
+    # launch alone costs in this setting
+    sink1 = torch.zeros(4, device=dev)
+    g_null = capture(lambda: [mbq.probe_mixed(xr, 0, xr, 0, 0, 1, sink1) for _ in range(nrm)])
+    g_null.replay()
+    null_us = timed(g_null, 20, stream) / (20 * nrm) * 1e3
+    del g_norm, g_null
 
     kern = {"q45_up_12288x4096": (b_up, up_ms), "q65_down_4096x12288": (b_dn, dn_ms)}
     dom = max(kern, key=lambda k: kern[k][1])
@@ -888,6 +895,8 @@ def main():
                    "spread": {k: round(v, 4) for k, v in spread.items()},
                    "windows_agree_within_3pct": all(v <= 0.03 for v in spread.values())},
         "rmsnorm_us_per_4096_row": round(rms_us, 3),
+        "rmsnorm_row_vs_empty_launch": {"empty_launch_us": round(null_us, 3),
+                                        "above_empty_launch_us": round(rms_us - null_us, 3)},
         "ceilings": ceil,
     }
     keep = {} if not args.no_rows else None

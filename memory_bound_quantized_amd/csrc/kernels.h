@@ -197,6 +197,22 @@ hipError_t launch_quantize(int fmt, const float* w, int64_t ldw, int64_t N, int6
 hipError_t launch_unpack_codes(int fmt, DevPlanes P, int64_t N, int64_t K, uint8_t* out,
                                hipStream_t stream);
 
+// Threads per row and float4s per thread of the single-pass RMSNorm kernels
+// (mbq_rmsnorm, mbq_rmsnorm_xq), by the row's n (n % 4 == 0): 256 threads up
+// to 1024 values, else 1024 threads with 1, 2, 4 or 8 float4s each (up to
+// 32768 values); vec = 0 beyond.  Both kernels take the same geometry, so
+// they add the squares in the same order.
+struct NormGeom {
+    int vec, bt;
+};
+inline NormGeom norm_geom(int64_t n) {
+    const int64_t n4 = n >> 2;
+    if (n4 <= 256) return NormGeom{1, 256};
+    for (int v = 1; v <= 8; v *= 2)
+        if (n4 <= 1024 * v) return NormGeom{v, 1024};
+    return NormGeom{0, 256};
+}
+
 // One token's attention over an fp16 KV cache (attention.hip): head
 // dimension kAttD, n_heads / n_kv in {1, 2, 4, 8}, T >= 1.  The workspace
 // holds one record of kAttRecord floats per query head and chunk of

@@ -12,11 +12,14 @@
 
 namespace mbq {
 
-template <int VEC>
-__global__ __launch_bounds__(kBlock) void rmsnorm_vec_kernel(const float* x,
-                                                             const float* __restrict__ gamma,
-                                                             float eps, int n, float* y) {
-    __shared__ float red[kWavesPerBlock];
+// BT threads per row (norm_geom): 1024 from 1025 values, so that a single
+// row's latency chain (load, sum, scale, store) has as little serial work per
+// thread as possible.
+template <int VEC, int BT>
+__global__ __launch_bounds__(BT) void rmsnorm_vec_kernel(const float* x,
+                                                         const float* __restrict__ gamma,
+                                                         float eps, int n, float* y) {
+    __shared__ float red[BT / kWave];
     const int64_t row = blockIdx.x;
     const int n4 = n >> 2;
     const float4* xr = (const float4*)(x + row * n);
@@ -26,7 +29,7 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_vec_kernel(const float* x,
     float4 v[VEC], g[VEC];
 #pragma unroll
     for (int i = 0; i < VEC; i++) {
-        const int f = i * kBlock + (int)threadIdx.x;
+        const int f = i * BT + (int)threadIdx.x;
         v[i] = f < n4 ? xr[f] : make_float4(0.f, 0.f, 0.f, 0.f);
         g[i] = f < n4 ? g4[f] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
@@ -38,12 +41,12 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_vec_kernel(const float* x,
         ss = fmaf(v[i].z, v[i].z, ss);
         ss = fmaf(v[i].w, v[i].w, ss);
     }
-    const float tot = block_sum(ss, red);
+    const float tot = block_sum<BT / kWave>(ss, red);
     const float inv = 1.0f / sqrtf(tot / (float)n + eps);
     float4* yr = (float4*)(y + row * n);
 #pragma unroll
     for (int i = 0; i < VEC; i++) {
-        const int f = i * kBlock + (int)threadIdx.x;
+        const int f = i * BT + (int)threadIdx.x;
         if (f < n4)
             yr[f] = make_float4(g[i].x * (v[i].x * inv), g[i].y * (v[i].y * inv),
                                 g[i].z * (v[i].z * inv), g[i].w * (v[i].w * inv));
@@ -147,15 +150,17 @@ static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 hipError_t launch_rmsnorm(const float* x, const float* gamma, float eps, int64_t rows, int64_t n,
                           float* y, hipStream_t stream) {
-    const int vec = (n % 4 == 0 && aligned16(x) && aligned16(y) && aligned16(gamma)) ? vec_for(n) : 0;
-    const dim3 grid((unsigned)rows), block(kBlock);
-    switch (vec) {
-    case 1: hipLaunchKernelGGL(rmsnorm_vec_kernel<1>, grid, block, 0, stream, x, gamma, eps, (int)n, y); break;
-    case 2: hipLaunchKernelGGL(rmsnorm_vec_kernel<2>, grid, block, 0, stream, x, gamma, eps, (int)n, y); break;
-    case 4: hipLaunchKernelGGL(rmsnorm_vec_kernel<4>, grid, block, 0, stream, x, gamma, eps, (int)n, y); break;
-    case 8: hipLaunchKernelGGL(rmsnorm_vec_kernel<8>, grid, block, 0, stream, x, gamma, eps, (int)n, y); break;
-    default: hipLaunchKernelGGL(rmsnorm_any_kernel, grid, block, 0, stream, x, gamma, eps, n, y); break;
-    }
+    const bool vec = n % 4 == 0 && aligned16(x) && aligned16(y) && aligned16(gamma);
+    const NormGeom ng = vec ? norm_geom(n) : NormGeom{0, kBlock};
+    const dim3 grid((unsigned)rows);
+#define MBQ_RMS(V, B) hipLaunchKernelGGL((rmsnorm_vec_kernel<V, B>), grid, dim3(B), 0, stream, x, gamma, eps, (int)n, y)
+    if (ng.vec == 1 && ng.bt == kBlock) MBQ_RMS(1, kBlock);
+    else if (ng.vec == 1) MBQ_RMS(1, 1024);
+    else if (ng.vec == 2) MBQ_RMS(2, 1024);
+    else if (ng.vec == 4) MBQ_RMS(4, 1024);
+    else if (ng.vec == 8) MBQ_RMS(8, 1024);
+    else hipLaunchKernelGGL(rmsnorm_any_kernel, grid, dim3(kBlock), 0, stream, x, gamma, eps, n, y);
+#undef MBQ_RMS
     return hipGetLastError();
 }
 

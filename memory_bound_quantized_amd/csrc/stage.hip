@@ -54,17 +54,18 @@ hipError_t launch_stage_x(int fmt, const float* x, int64_t M, int64_t ldx, int64
 }
 
 // ---- RMSNorm of one row, emitting staged output ----------------------------
-// As the plain RMSNorm kernel (norms.hip): values in registers, one block-wide
-// sum; the normalised row then goes through LDS so each thread can stage a
-// group of GX consecutive values.  n <= 256 * 4 * VEC, n % 4 == 0.
-template <int FMT, int VEC>
-__global__ __launch_bounds__(kBlock) void rmsnorm_xq_kernel(const float* x,
-                                                            const float* __restrict__ gamma,
-                                                            float eps, int n, float* y,
-                                                            uint32_t* __restrict__ xq) {
+// As the plain RMSNorm kernel (norms.hip), in the same geometry (norm_geom),
+// so y is bit for bit mbq_rmsnorm's: values in registers, one block-wide sum;
+// the normalised row then goes through LDS so each thread can stage a group
+// of GX consecutive values.  n <= BT * 4 * VEC, n % 4 == 0.
+template <int FMT, int VEC, int BT>
+__global__ __launch_bounds__(BT) void rmsnorm_xq_kernel(const float* x,
+                                                        const float* __restrict__ gamma,
+                                                        float eps, int n, float* y,
+                                                        uint32_t* __restrict__ xq) {
     using T = Traits<FMT>;
-    __shared__ float red[kWavesPerBlock];
-    __shared__ float4 row[VEC * kBlock];
+    __shared__ float red[BT / kWave];
+    __shared__ float4 row[VEC * BT];
     const int n4 = n >> 2;
     const float4* x4 = (const float4*)x;
     const float4* g4 = (const float4*)gamma;
@@ -72,7 +73,7 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_xq_kernel(const float* x,
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < VEC; i++) {
-        const int f = i * kBlock + (int)threadIdx.x;
+        const int f = i * BT + (int)threadIdx.x;
         v[i] = f < n4 ? x4[f] : make_float4(0.f, 0.f, 0.f, 0.f);
         g[i] = f < n4 ? g4[f] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
@@ -83,11 +84,11 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_xq_kernel(const float* x,
         ss = fmaf(v[i].z, v[i].z, ss);
         ss = fmaf(v[i].w, v[i].w, ss);
     }
-    const float tot = block_sum(ss, red);
+    const float tot = block_sum<BT / kWave>(ss, red);
     const float inv = 1.0f / sqrtf(tot / (float)n + eps);
 #pragma unroll
     for (int i = 0; i < VEC; i++) {
-        const int f = i * kBlock + (int)threadIdx.x;
+        const int f = i * BT + (int)threadIdx.x;
         const float4 o = make_float4(g[i].x * (v[i].x * inv), g[i].y * (v[i].y * inv),
                                      g[i].z * (v[i].z * inv), g[i].w * (v[i].w * inv));
         row[f] = o;
@@ -96,9 +97,9 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_xq_kernel(const float* x,
     __syncthreads();
     constexpr int GF4 = T::GX / 4;
     const int ngroups = n / T::GX;
-    const int rounds = (ngroups + kBlock - 1) / kBlock;
+    const int rounds = (ngroups + BT - 1) / BT;
     for (int rd = 0; rd < rounds; rd++) {
-        const int og = rd * kBlock + (int)threadIdx.x;
+        const int og = rd * BT + (int)threadIdx.x;
         const bool ok = og < ngroups;
         float4 w[GF4];
 #pragma unroll
@@ -110,16 +111,15 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_xq_kernel(const float* x,
 template <int FMT>
 static hipError_t rmsnorm_xq_f(const float* x, const float* gamma, float eps, int64_t n, float* y,
                                void* xq, hipStream_t stream) {
-    const int64_t n4 = n >> 2;
-    const dim3 grid(1), block(kBlock);
-    if (n4 <= kBlock)
-        hipLaunchKernelGGL((rmsnorm_xq_kernel<FMT, 1>), grid, block, 0, stream, x, gamma, eps, (int)n, y, (uint32_t*)xq);
-    else if (n4 <= 2 * kBlock)
-        hipLaunchKernelGGL((rmsnorm_xq_kernel<FMT, 2>), grid, block, 0, stream, x, gamma, eps, (int)n, y, (uint32_t*)xq);
-    else if (n4 <= 4 * kBlock)
-        hipLaunchKernelGGL((rmsnorm_xq_kernel<FMT, 4>), grid, block, 0, stream, x, gamma, eps, (int)n, y, (uint32_t*)xq);
+    const NormGeom ng = norm_geom(n);                // n <= 8192: at most 2 float4s of 1024 threads
+    const dim3 grid(1);
+    uint32_t* q = (uint32_t*)xq;
+    if (ng.bt == 256)
+        hipLaunchKernelGGL((rmsnorm_xq_kernel<FMT, 1, 256>), grid, dim3(256), 0, stream, x, gamma, eps, (int)n, y, q);
+    else if (ng.vec == 1)
+        hipLaunchKernelGGL((rmsnorm_xq_kernel<FMT, 1, 1024>), grid, dim3(1024), 0, stream, x, gamma, eps, (int)n, y, q);
     else
-        hipLaunchKernelGGL((rmsnorm_xq_kernel<FMT, 8>), grid, block, 0, stream, x, gamma, eps, (int)n, y, (uint32_t*)xq);
+        hipLaunchKernelGGL((rmsnorm_xq_kernel<FMT, 2, 1024>), grid, dim3(1024), 0, stream, x, gamma, eps, (int)n, y, q);
     return hipGetLastError();
 }
 

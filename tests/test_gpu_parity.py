@@ -200,8 +200,12 @@ def test_gather_small_matches_oracle_gather():
 # --------------------------------------------------------------------------
 
 @pytest.mark.parametrize("rows,n", [(1, 4096), (3, 4096), (2, 2048), (5, 1000), (2, 8192),
-                                    (2, 10000), (1, 4), (1, 3), (64, 256)])
+                                    (2, 10000), (1, 4), (1, 3), (64, 256), (1, 1024), (1, 1028),
+                                    (2, 16384), (1, 32768), (1, 32772)])
 def test_rmsnorm_matches_oracle(rows, n):
+    """Every geometry of the single-pass kernel (256 threads up to 1024
+    values, then 1024 threads with 1, 2, 4 or 8 float4s each up to 32768)
+    and the any-n kernel beyond it or for n % 4 != 0."""
     rng = np.random.default_rng(rows * n)
     x = rng.normal(size=(rows, n)).astype(np.float32)
     g = rng.uniform(0.5, 1.5, n).astype(np.float32)

@@ -120,7 +120,7 @@ def test_stage_x_rows_are_independent():
 
 
 @pytest.mark.parametrize("fmt,n", [(1, 4096), (2, 4096), (3, 4096), (0, 4096), (1, 32), (3, 64),
-                                   (1, 2048), (2, 8192), (1, 1056)])
+                                   (1, 2048), (2, 8192), (1, 1056), (1, 1024), (3, 6144)])
 def test_rmsnorm_xq(fmt, n):
     print("rmsnorm_xq fmt=%d n=%d" % (fmt, n), flush=True)
     rng = np.random.default_rng(n + fmt)
