@@ -508,11 +508,11 @@ def rows_bench(mbq, workloads, torch, dev, peak_gbs, one_launch=True, keep=None)
         b = Ws[0].nbytes + 4 * M * (N + K)
         ent = {"stage_plus_product_us": round(step_us, 3), "product_us": round(kern_us, 3),
                "us_per_token": round(step_us / M, 3), "product_gbs": gbs(b, kern_us),
-               "path": "matrix cores" if M >= 6 else "vector units",
-               "fp32_x_path": "matrix cores, x converted in the product" if M >= 6 else "vector units"}
+               "path": "matrix cores" if M >= 4 else "vector units",
+               "fp32_x_path": "matrix cores, x converted in the product" if M >= 4 else "vector units"}
         if fp32_us is not None:
             ent["fp32_x_us"] = round(fp32_us, 3)
-        if M >= 6:
+        if M >= 4:
             tf = 2.0 * M * N * K / (kern_us * 1e-6) / 1e12
             ent["useful_tflops"] = round(tf, 2)
             # issued: 16-token tiles, two fp16 MFMAs (x high and low parts) per

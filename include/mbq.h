@@ -134,7 +134,7 @@ int mbq_unpack(int fmt, int64_t N, int64_t K, const void* const planes[4],
  * is unspecified.  Tokens run on the vector units, up to 8 per launch (as many
  * as fit staged in LDS: all 8 for K = 4096, 2 for K = 12288), each weight
  * read once per launch and unpacked once for all its tokens.  Q45 batches of
- * 6 or more tokens with K % 128 == 0 (and 8-byte aligned scales) run on the
+ * 4 or more tokens with K % 128 == 0 (and 8-byte aligned scales) run on the
  * matrix cores instead, all tokens in one launch, with x split into fp16
  * high and low parts under a power of two per 32-weight block and token (the
  * relative precision of the vector units' staged x); the same holds through
@@ -291,7 +291,7 @@ int mbq_decode_step_persistent(const mbq_decode_model* model, float* h, float* l
  * the sums busy").  The form is opaque and format-specific: stage for the
  * format of the matrix that consumes it.  It takes 4 bytes per value
  * (mbq_xq_bytes), rows back to back; for BF16 it is x itself in fp32.
- * For Q45 with M >= 6 tokens and K % 128 == 0 it is the matrix-core tile
+ * For Q45 with M >= 4 tokens and K % 128 == 0 it is the matrix-core tile
  * form instead: per tile of 16 tokens and block of 32 values, each token's
  * block scaled by a power of two (its largest |x| in [2^14, 2^15)) and split
  * into fp16 high and low parts in the MFMA operand order, then the blocks'
@@ -299,7 +299,7 @@ int mbq_decode_step_persistent(const mbq_decode_model* model, float* h, float* l
  */
 
 /* Bytes of staged x for M rows of K values: 4*M*K, or for the Q45 tile form
- * (M >= 6, K % 128 == 0) ceil(M/16) * (K/32 * 2048 + K/128 * 64).
+ * (M >= 4, K % 128 == 0) ceil(M/16) * (K/32 * 2048 + K/128 * 64).
  * Host only.  MBQ_EINVAL for an unknown
  * format or K not a multiple of the chunk (32; Q25 64; BF16 8). */
 int mbq_xq_bytes(int fmt, int64_t M, int64_t K, size_t* bytes);

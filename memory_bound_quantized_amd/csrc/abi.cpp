@@ -120,10 +120,21 @@ int check_kernel_shape(const mbq_qweight* W, const char* fn) {
 // then takes the tile form), for K % 128 == 0.  The vector units' digit
 // arithmetic has M* = (w/16)(R/BW) of about one token on MI355X (measured
 // R and BW), the matrix cores' about twelve, so from a few tokens on the
-// matrix cores carry the sums at the weight-read rate.
-constexpr int64_t kMfmaMinM = 6;
+// matrix cores carry the sums at the weight-read rate.  Measured crossover
+// (us, staged x, graphs of cold launches): 12288 x 4096 at 3 / 4 / 5 tokens
+// 13.9 / 16.0 / 18.6 on the vector units against 13.4 / 13.5 / 13.2 on the
+// matrix cores; 4096 x 12288 17.4 / 20.9 / 26.0 against 18.9 / 18.9 / 18.9.
+constexpr int64_t kMfmaMinM = 4;
+static int64_t mfma_min_m() {
+    static const int64_t v = [] {
+        const char* e = mbq::tuning_var("MBQ_MFMA_MIN_M");      // tuning: read once
+        const int64_t t = e ? atoll(e) : kMfmaMinM;
+        return t < 2 ? (int64_t)2 : t;
+    }();
+    return v;
+}
 bool mfma_shape(int fmt, int64_t M, int64_t K) {
-    return fmt == MBQ_FMT_Q45 && M >= kMfmaMinM && K % 128 == 0;
+    return fmt == MBQ_FMT_Q45 && M >= mfma_min_m() && K % 128 == 0;
 }
 bool xq_tiled(int fmt, int64_t M, int64_t K) { return mfma_shape(fmt, M, K); }
 

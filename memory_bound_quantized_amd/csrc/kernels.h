@@ -104,9 +104,9 @@ hipError_t launch_gemv_smallm(int fmt, DevPlanes P, int64_t N, int64_t K, const 
                               bool x_staged, int64_t M, int64_t ldx, float* y, int64_t ldy,
                               int accumulate, GemvGeom g, hipStream_t stream);
 
-// Matrix-core product for Q45 and M >= 16 tokens (gemv_mfma.hip).  X comes in
-// the staged tile form: xt_bytes(M, K) bytes written by launch_stage_x_mfma.
-// K % 1024 == 0; plane 2 8-byte aligned.
+// Matrix-core product for Q45 batches (gemv_mfma.hip; the dispatch sends
+// 4 or more tokens).  X comes in the staged tile form: xt_bytes(M, K) bytes
+// written by launch_stage_x_mfma.  K % 128 == 0; plane 2 8-byte aligned.
 int64_t xt_bytes(int64_t M, int64_t K);
 hipError_t launch_stage_x_mfma(const float* x, int64_t M, int64_t ldx, int64_t K, void* xt,
                                hipStream_t stream);

@@ -184,7 +184,7 @@ def test_staged_x_argument_checks():
     assert L.mbq_xq_bytes(3, 1, 96, ctypes.byref(sz)) == _lib.EINVAL       # Q25 chunk is 64
     assert L.mbq_xq_bytes(1, 1, 48, ctypes.byref(sz)) == _lib.EINVAL
     assert L.mbq_xq_bytes(9, 1, 64, ctypes.byref(sz)) == _lib.EINVAL
-    # Q45 with 6 or more tokens and K % 128 == 0: the matrix-core tile form
+    # Q45 with 4 or more tokens and K % 128 == 0: the matrix-core tile form
     # (2 KB per 16 tokens and 32 values, plus 64 exponent bytes per 16 tokens
     # and 128 values); the row form otherwise
     tile = lambda K: K // 32 * 2048 + K // 128 * 64
@@ -192,7 +192,8 @@ def test_staged_x_argument_checks():
     assert L.mbq_xq_bytes(1, 6, 4096, ctypes.byref(sz)) == _lib.OK and sz.value == tile(4096)
     assert L.mbq_xq_bytes(1, 6, 640, ctypes.byref(sz)) == _lib.OK and sz.value == tile(640)
     assert L.mbq_xq_bytes(1, 512, 4096, ctypes.byref(sz)) == _lib.OK and sz.value == 32 * tile(4096)
-    assert L.mbq_xq_bytes(1, 5, 4096, ctypes.byref(sz)) == _lib.OK and sz.value == 5 * 4096 * 4
+    assert L.mbq_xq_bytes(1, 4, 4096, ctypes.byref(sz)) == _lib.OK and sz.value == tile(4096)
+    assert L.mbq_xq_bytes(1, 3, 4096, ctypes.byref(sz)) == _lib.OK and sz.value == 3 * 4096 * 4
     assert L.mbq_xq_bytes(1, 8, 2080, ctypes.byref(sz)) == _lib.OK and sz.value == 8 * 2080 * 4
     assert L.mbq_xq_bytes(2, 17, 4096, ctypes.byref(sz)) == _lib.OK and sz.value == 17 * 4096 * 4
     x, xq = BASE, BASE + 0x100000
@@ -256,7 +257,7 @@ def test_split_product_argument_checks():
     assert wb(12288, 12288, 64) == (_lib.OK, r256(128 * 4) + 2 * 64 * 12288 * 4)
     assert wb(12288, 12288, 16) == (_lib.OK, 0)
     assert wb(12288, 4096, 64) == (_lib.OK, 0)
-    assert wb(12288, 4096, 5) == (_lib.OK, 0)          # vector units
+    assert wb(4096, 12288, 3) == (_lib.OK, 0)          # vector units
     assert wb(1000, 8192, 64) == (_lib.OK, r256(16 * 4) + 4 * 64 * 1000 * 4)
     assert wb(1000, 1024, 64) == (_lib.OK, 0)          # 8 quads: not a step of 4 parts of 4 waves
     assert wb(20000, 12288, 64) == (_lib.OK, 0)        # 5 row tiles per unit

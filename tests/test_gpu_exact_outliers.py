@@ -3,11 +3,11 @@
 Paths (all through the C ABI):
   m1         mbq_gemv_q, one token (the single-token kernel on fp32 x)
   m1_xq      mbq_stage_x + mbq_gemv_xq, one token (staged x)
-  vec        mbq_gemv_q, 2 and 4 tokens (vector units, fp32 x)
-  vec_xq     mbq_stage_x + mbq_gemv_xq, 4 tokens (vector units, staged x)
-  mfma       mbq_gemv_q, Q45, 6 and 16 tokens (matrix cores, fp32 x)
-  mfma_xq    mbq_stage_x + mbq_gemv_xq, Q45, 16 and 64 tokens (matrix cores,
-             staged tile form)
+  vec        mbq_gemv_q, 2 and 3 tokens (vector units, fp32 x)
+  vec_xq     mbq_stage_x + mbq_gemv_xq, 3 tokens (vector units, staged x)
+  mfma       mbq_gemv_q, Q45, 4 and 16 tokens (matrix cores, fp32 x)
+  mfma_xq    mbq_stage_x + mbq_gemv_xq, Q45, 4, 16 and 64 tokens (matrix
+             cores, staged tile form)
 
 Exact cases (the special cases of the product that have a plain closed form):
   * every code at its format's offset: every weight is 0, so y == 0 exactly;
@@ -56,8 +56,8 @@ def dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-PATHS = [("m1", 1), ("m1_xq", 1), ("vec", 2), ("vec", 4), ("vec_xq", 4),
-         ("mfma", 6), ("mfma", 16), ("mfma_xq", 16), ("mfma_xq", 64)]
+PATHS = [("m1", 1), ("m1_xq", 1), ("vec", 2), ("vec", 3), ("vec_xq", 3),
+         ("mfma", 4), ("mfma", 16), ("mfma_xq", 4), ("mfma_xq", 16), ("mfma_xq", 64)]
 
 
 def run_path(path, dw, X):

@@ -140,7 +140,7 @@ def test_smallm_every_geometry_bitwise(fmt, M, N, K):
 
 MFMA_GEOM_CASES = [(16, 1000, 4096), (20, 1000, 4096), (40, 300, 2048), (64, 130, 1024),
                    (6, 77, 640), (33, 200, 2176), (17, 50, 128), (64, 300, 4096),
-                   (50, 100, 12288)]
+                   (50, 100, 12288), (4, 300, 4096)]
 
 
 @pytest.mark.parametrize("M,N,K", MFMA_GEOM_CASES)

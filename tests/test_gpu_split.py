@@ -139,7 +139,7 @@ def test_one_workspace_serves_every_shape():
     assert not bool(shared.any())
 
 
-@pytest.mark.parametrize("M,N,K,force", [(5, 12288, 4096, 2), (1, 4096, 12288, 2), (16, 77, 1024, 2),
+@pytest.mark.parametrize("M,N,K,force", [(3, 12288, 4096, 2), (1, 4096, 12288, 2), (16, 77, 1024, 2),
                                          (20, 9000, 2048, 2), (16, 20000, 4096, 2),
                                          (16, 12288, 4096, 0), (64, 12288, 4096, 0), (16, 4096, 4096, 0),
                                          (64, 4096, 12288, 1)])
