@@ -39,6 +39,19 @@ __device__ __forceinline__ uint16_t half_bits(float v) {
     return __builtin_bit_cast(uint16_t, (_Float16)v);   // v is a half already
 }
 
+// rint(v / s) with v / s the correctly rounded fp32 quotient, for s > 0 with
+// 1/s a normal float (r = v_rcp_f32(s), within 1 ulp of 1/s).  t = v r is
+// within 1.5 2^-23 |t| of v / s, and the rounded quotient within 2^-24 |t|;
+// for |t| < 64 both errors are below 2^-16, so where t lies more than 2^-14
+// from the nearest k + 1/2 the two round to the same integer.  Only near a
+// tie (about 2^-13 of uniform quotients) is the exact division taken.
+__device__ __forceinline__ float rint_quot(float v, float s, float r) {
+    const float t = v * r;
+    const float f = rintf(t);
+    if (fabsf(t - f) < 0.5f - 0x1p-14f && fabsf(t) < 64.f) return f;
+    return rintf(v / s);
+}
+
 template <int FMT>
 __global__ __launch_bounds__(kBlock) void quantize_kernel(const float* __restrict__ w, int64_t ldw,
                                                           int64_t N, int64_t K, DevPlanes out,
@@ -84,9 +97,10 @@ __global__ __launch_bounds__(kBlock) void quantize_kernel(const float* __restric
         const float s = half_sat(m / QMAX);
         int q[8];
         const float sd = s != 0.f ? s : 1.0f;         // s = 0: every code is the offset
+        const float rd = __builtin_amdgcn_rcpf(sd);   // sd >= 2^-24: 1/sd is normal
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-            const int c = s != 0.f ? (int)rintf(v[i] / sd) + OFF : OFF;
+            const int c = s != 0.f ? (int)rint_quot(v[i], sd, rd) + OFF : OFF;
             q[i] = c < 0 ? 0 : (c > TOP ? TOP : c);
         }
         if (!ok) return;
@@ -118,9 +132,10 @@ __global__ __launch_bounds__(kBlock) void quantize_kernel(const float* __restric
         const float step = d * (float)sc;             // exact: 11 + 7 significant bits
         int q[8];
         const float stepd = step != 0.f ? step : 1.0f;
+        const float rs = __builtin_amdgcn_rcpf(stepd); // stepd in [2^-24, 65504 * 127]
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-            const int c = step != 0.f ? (int)rintf(v[i] / stepd) + 32 : 32;
+            const int c = step != 0.f ? (int)rint_quot(v[i], stepd, rs) + 32 : 32;
             q[i] = c < 0 ? 0 : (c > 63 ? 63 : c);
         }
         const int li = (int)(item & 31);               // lane within the super-block
