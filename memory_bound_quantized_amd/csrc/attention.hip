@@ -59,12 +59,18 @@ __device__ __forceinline__ void halves(au4 w, float* f) {
 
 // Positions per workgroup: a multiple of 16 (4 waves x 4 positions), at
 // most 16 groups of 4 per wave (kMaxGroups) so that a wave holds all its
-// keys and values in registers, and otherwise T / 16, so that up to 4096
-// positions the combine step merges at most 16 chunks per head.
+// keys and values in registers, and otherwise T / P: P = 16 chunks per head
+// below 4096 positions, where the call is latency-bound and each extra
+// chunk record costs the combine step, and P = 32 from 4096 on, where 16
+// chunks per head would leave half the compute units idle (8 heads of 32
+// query heads: 14.6 us against 17.5 at 4096 positions; 7.7 against 9.4 at
+// 512 with P = 16).  MBQ_ATT_CHUNKS overrides P (tuning).
 constexpr int kMaxGroups = 16;
 int attention_chunk(int64_t T, int n_kv) {
     (void)n_kv;
-    int64_t c = (T + 15) / 16;
+    int64_t P = T >= 4096 ? 32 : 16;
+    if (const char* e = tuning_var("MBQ_ATT_CHUNKS")) P = atoll(e) > 0 ? atoll(e) : P;
+    int64_t c = (T + P - 1) / P;
     c = (c + 15) / 16 * 16;
     const int cmax = 16 * kMaxGroups;
     return (int)(c < 16 ? 16 : (c > cmax ? cmax : c));

@@ -424,7 +424,10 @@ def test_attention_argument_checks():
     # chunks of 32
     assert L.mbq_attention_workspace_bytes(512, 32, 8, 128, ctypes.byref(sz)) == _lib.OK
     assert sz.value == 32 * 16 * 132 * 4
-    # 40000 positions: chunks of 256, 157 of them; 200 heads of their own
+    # 4096 positions: 32 chunks of 128 per head
+    assert L.mbq_attention_workspace_bytes(4096, 32, 8, 128, ctypes.byref(sz)) == _lib.OK
+    assert sz.value == 32 * 32 * 132 * 4
+    # 40000 positions: chunks of 256 (the most a workgroup holds), 157 of them
     assert L.mbq_attention_workspace_bytes(40000, 200, 200, 128, ctypes.byref(sz)) == _lib.OK
     assert sz.value == 200 * 157 * 132 * 4
     assert L.mbq_attention_workspace_bytes(0, 32, 8, 128, ctypes.byref(sz)) == _lib.EINVAL

@@ -18,6 +18,8 @@ stride wider than the heads, scores of several hundred (the max shift),
 equal keys (uniform weights), and one workspace full of NaN serving calls
 of every length in turn (its contents need no initialisation).
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -155,3 +157,24 @@ def test_workspace_needs_no_initialisation():
     for T in (5000, 17, 600, 1, 4096, 5000):
         out = mbq().attention_decode(qd, kd, vd, H, Hkv, T=T, workspace=ws)
         check(out.cpu().numpy(), q, kc, vc, H, Hkv, T)
+
+
+@pytest.mark.parametrize("P", [8, 32, 64])
+@pytest.mark.parametrize("T", [777, 1000, 5000])
+def test_every_chunking_of_the_positions(P, T):
+    """About T / P positions per workgroup (a multiple of 16, at most 256),
+    forced through MBQ_ATT_CHUNKS (read because MBQ_TUNING is set in
+    conftest.py): ragged last chunks and up to 64 records per head for the
+    combine step."""
+    print("attention chunks P=%d T=%d" % (P, T), flush=True)
+    assert os.environ.get("MBQ_TUNING"), "the override needs MBQ_TUNING"
+    rng = np.random.default_rng(100 * P + T)
+    H, Hkv = 32, 8
+    kc, vc = cache(rng, T, Hkv * D, scale=3.0)
+    q = rng.normal(size=H * D).astype(np.float32)
+    os.environ["MBQ_ATT_CHUNKS"] = str(P)
+    try:
+        out = run(q, kc, vc, H, Hkv)
+    finally:
+        os.environ.pop("MBQ_ATT_CHUNKS", None)
+    check(out, q, kc, vc, H, Hkv, T)
