@@ -207,42 +207,67 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const float* __r
 }
 
 // Workgroup h (a query head), thread = dimension: the chunks' records merged
-// under their common maximum, in chunk order.  Records are read 16 at a time
-// so that their loads are in flight together.
+// in blocks of 128 chunks.  Per block every load goes out at once: thread t
+// reads chunk t's maximum and sum, and every thread its dimension of the
+// block's value sums.  The block's maximum then updates the running one
+// (the sums so far rescaled by 2^(old - new), base 2), thread t leaves chunk
+// t's factor 2^(m_t - max) in LDS, and each thread adds its dimension in
+// chunk order.  One memory round trip per 128 chunks.
 __global__ __launch_bounds__(kAttD) void attn_combine_kernel(const float* __restrict__ ws, int G,
                                                              int nch, float* __restrict__ out) {
-    constexpr int B = 16;
-    const int h = blockIdx.x, dd = threadIdx.x;
+    constexpr int NT = kAttD;
+    __shared__ float fs[NT];
+    __shared__ float red[NT / kWave];
+    const int h = blockIdx.x, t = threadIdx.x, dd = t;
     const int kv = h / G, hl = h % G;
     const float* r0 = ws + ((int64_t)kv * nch * G + hl) * kAttRecord;
     const int64_t stride = (int64_t)G * kAttRecord;
-    float m = -INFINITY;
-    for (int c0 = 0; c0 < nch; c0 += B) {
-        float v[B];
+
+    float Mrun = -INFINITY, L = 0.f, acc = 0.f;
+    for (int cb = 0; cb < nch; cb += NT) {
+        const int n = min(NT, nch - cb);
+        constexpr int BU = 16;                         // loads issued in guarded groups of 16
+        float o[NT];
 #pragma unroll
-        for (int u = 0; u < B; u++) v[u] = c0 + u < nch ? r0[(c0 + u) * stride] : -INFINITY;
+        for (int u0 = 0; u0 < NT; u0 += BU) {
+            if (u0 < n) {                              // the same in the whole workgroup
 #pragma unroll
-        for (int u = 0; u < B; u++) m = fmaxf(m, v[u]);
-    }
-    float l = 0.f, o = 0.f;
-    for (int c0 = 0; c0 < nch; c0 += B) {
-        float mm[B], ll[B], oo[B];
-#pragma unroll
-        for (int u = 0; u < B; u++) {
-            const bool ok = c0 + u < nch;
-            const float* r = r0 + (ok ? c0 + u : 0) * stride;
-            mm[u] = ok ? r[0] : -INFINITY;
-            ll[u] = r[1];
-            oo[u] = r[2 + dd];
+                for (int u = u0; u < u0 + BU; u++) o[u] = u < n ? r0[(cb + u) * stride + 2 + dd] : 0.f;
+            }
         }
+        const bool mine = t < n;
+        const float* rt = r0 + (mine ? cb + t : cb) * stride;
+        const float mt = mine ? rt[0] : -INFINITY;
+        const float lt = rt[1];
+        float mb = wave_max(mt);
+        if ((t & (kWave - 1)) == 0) red[t / kWave] = mb;
+        __syncthreads();
 #pragma unroll
-        for (int u = 0; u < B; u++) {
-            const float f = exp2f(mm[u] - m);         // 0 past the last chunk
-            l = fmaf(ll[u], f, l);
-            o = fmaf(oo[u], f, o);
+        for (int w = 0; w < NT / kWave; w++) mb = fmaxf(mb, red[w]);
+        const float Mnew = fmaxf(Mrun, mb);
+        const float scale = exp2f(Mrun - Mnew);        // 0 on the first block
+        const float f = mine ? exp2f(mt - Mnew) : 0.f;
+        L = fmaf(L, scale, mine ? lt * f : 0.f);
+        acc *= scale;
+        Mrun = Mnew;
+        fs[t] = f;
+        __syncthreads();
+#pragma unroll
+        for (int u0 = 0; u0 < NT; u0 += BU) {
+            if (u0 < n) {
+#pragma unroll
+                for (int u = u0; u < u0 + BU; u++) acc = fmaf(o[u], fs[u], acc);
+            }
         }
+        __syncthreads();                               // fs and red are rewritten next
     }
-    out[(int64_t)h * kAttD + dd] = o / l;
+    L = wave_sum(L);
+    if ((t & (kWave - 1)) == 0) red[t / kWave] = L;
+    __syncthreads();
+    L = red[0];
+#pragma unroll
+    for (int w = 1; w < NT / kWave; w++) L += red[w];
+    out[(int64_t)h * kAttD + dd] = acc / L;
 }
 
 hipError_t launch_attention_decode(const float* q, const uint16_t* kc, const uint16_t* vc, int64_t T,
