@@ -220,15 +220,16 @@ def traffic_pass():
     print("traffic pass: %d launches of each GEMV, one %d-byte copy" % (ncopy, COPY_BYTES))
 
 
-def mfma_pass(reps: int = 8):
+def mfma_pass(reps: int = 8, tokens=(16, 64)):
     """Launches profiled by the matrix-core counter run: the staged-x product
-    of workload 4's 12288 x 4096 Q45 table at M = 16 and 64, each on cold
-    weights (one rotated copy per launch, no graph)."""
+    of workload 4's 12288 x 4096 Q45 table at each batch size in tokens
+    (16 and 64 by default), each on cold weights (one rotated copy per
+    launch, no graph)."""
     import torch
     import memory_bound_quantized_amd as mbq
     import workloads
     dev = torch.device("cuda:0")
-    for M in (16, 64):
+    for M in tokens:
         c4 = workloads.config4(M)
         W0 = mbq.QWeight.from_host(*c4["W"])
         Ws = rotated(W0)
@@ -240,7 +241,7 @@ def mfma_pass(reps: int = 8):
         torch.cuda.synchronize()
         del Ws
         torch.cuda.empty_cache()
-    print("mfma pass: %d launches at M = 16 and at M = 64" % reps)
+    print("mfma pass: %d launches at each of M = %s" % (reps, ", ".join(str(m) for m in tokens)))
 
 
 def rows_traffic_pass(reps: int = 4):
@@ -737,6 +738,8 @@ def main():
                     help="only the other rows' launches that the counter runs profile")
     ap.add_argument("--mfma-pass", action="store_true",
                     help="only the matrix-core launches that the counter runs profile")
+    ap.add_argument("--mfma-pass-tokens", default="16,64", metavar="M,M,...",
+                    help="batch sizes of --mfma-pass (default 16,64)")
     ap.add_argument("--decode-only", type=int, metavar="TOKENS", default=0,
                     help="only the 36-layer decode step, TOKENS graph replays (for profiling)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -757,7 +760,7 @@ def main():
         traffic_pass()
         return
     if args.mfma_pass:
-        mfma_pass()
+        mfma_pass(tokens=tuple(int(t) for t in args.mfma_pass_tokens.split(",")))
         return
     if args.rows_traffic_pass:
         rows_traffic_pass()
