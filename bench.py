@@ -379,9 +379,12 @@ def timed(graph, n, stream=None):
 
 
 def per_launch_us(make_launch, copies, launches_target=200):
-    """Average us of one launch: a graph of one launch per weight copy, replayed."""
+    """Average us of one launch: a graph of one launch per weight copy, replayed
+    (after at least two warm-up replays and 16 warm-up launches: the first
+    passes over freshly copied tables ran up to 13 % slower)."""
     g = capture(lambda: [make_launch(c) for c in copies])
-    g.replay()
+    for _ in range(max(2, -(-16 // len(copies)))):
+        g.replay()
     reps = max(2, -(-launches_target // len(copies)))
     return timed(g, reps) / (reps * len(copies)) * 1e3
 
