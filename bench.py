@@ -378,12 +378,15 @@ def timed(graph, n, stream=None):
     return a.elapsed_time(b)
 
 
-def per_launch_us(make_launch, copies, launches_target=200):
+def per_launch_us(make_launch, copies, launches_target=200, warm_ms=20.0):
     """Average us of one launch: a graph of one launch per weight copy, replayed
-    (after at least two warm-up replays and 16 warm-up launches: the first
-    passes over freshly copied tables ran up to 13 % slower)."""
+    after warm-up replays worth at least 16 launches and warm_ms of GPU time
+    (a row measured right after seconds of host-side setup ran up to 13 %
+    slower than the same launches a little later)."""
     g = capture(lambda: [make_launch(c) for c in copies])
-    for _ in range(max(2, -(-16 // len(copies)))):
+    once = timed(g, 1)
+    warm = max(2, -(-16 // len(copies)), int(warm_ms / max(once, 1e-3)) + 1)
+    for _ in range(min(warm, 10000)):
         g.replay()
     reps = max(2, -(-launches_target // len(copies)))
     return timed(g, reps) / (reps * len(copies)) * 1e3
