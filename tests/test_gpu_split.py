@@ -187,3 +187,37 @@ def test_small_workspace_is_rejected():
     ws = torch.zeros(need - 256, dtype=torch.uint8, device="cuda")
     with pytest.raises(RuntimeError, match="workspace"):
         mbq().gemv_xq_ws(dw, Xq, M, ws)
+
+
+def test_split_in_a_replayed_graph():
+    """The split product captured in a HIP graph (its counters and partials
+    need no clearing node: every call leaves them zero), replayed several
+    times with eager work and synchronizations in between; every replay
+    equals the eager result bit for bit."""
+    print("split graph replays", flush=True)
+    M, N, K = 16, 4096, 12288
+    _, dw = weights(N, K, 8300)
+    rng = np.random.default_rng(8301)
+    Xq = mbq().stage_x(1, dev(rng.normal(size=(M, K)).astype(np.float32)))
+    ws = mbq().gemv_xq_workspace(dw, M)
+    assert ws.numel() > 256
+    eager = mbq().gemv_xq_ws(dw, Xq, M, ws)
+    torch.cuda.synchronize()
+    out = torch.empty_like(eager)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        mbq().gemv_xq_ws(dw, Xq, M, ws, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mbq().gemv_xq_ws(dw, Xq, M, ws, out=out)
+    for i in range(4):
+        out.fill_(float("nan"))
+        mbq().gemv_xq(dw, Xq, M=M)                 # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out), bits(eager)), i
+        assert not bool(ws.any()), i
