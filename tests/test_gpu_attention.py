@@ -178,3 +178,39 @@ def test_every_chunking_of_the_positions(P, T):
     finally:
         os.environ.pop("MBQ_ATT_CHUNKS", None)
     check(out, q, kc, vc, H, Hkv, T)
+
+
+def test_attention_in_a_replayed_graph():
+    """Both launches captured in a HIP graph and replayed with eager work and
+    synchronizations in between; every replay equals the eager result bit for
+    bit (the workspace is scratch, rewritten by every call)."""
+    print("attention graph replays", flush=True)
+    rng = np.random.default_rng(12)
+    H, Hkv, T = 32, 8, 512
+    kc, vc = cache(rng, T, Hkv * D)
+    q = rng.normal(size=H * D).astype(np.float32)
+    qd = torch.from_numpy(q).cuda()
+    kd = torch.from_numpy(kc.view(np.int16)).cuda()
+    vd = torch.from_numpy(vc.view(np.int16)).cuda()
+    nb = mbq().attention_workspace_bytes(T, H, Hkv)
+    ws = torch.zeros((nb + 15) // 16 * 4, dtype=torch.float32, device="cuda")
+    eager = mbq().attention_decode(qd, kd, vd, H, Hkv, workspace=ws).clone()
+    out = torch.empty_like(eager)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        mbq().attention_decode(qd, kd, vd, H, Hkv, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mbq().attention_decode(qd, kd, vd, H, Hkv, out=out, workspace=ws)
+    for i in range(4):
+        out.fill_(float("nan"))
+        ws.fill_(float("nan"))
+        mbq().attention_decode(qd, kd, vd, H, Hkv)     # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), i
+    check(out.cpu().numpy(), q, kc, vc, H, Hkv, T)
