@@ -121,10 +121,15 @@ def test_mfma_matches_oracle(M, N, K):
     Y = mbq().gemv_xq(dw, Xt, M=M).cpu().numpy()
     ref = oracle.gemv_parallel(ow, X) if N * K > 1 << 24 else oracle.gemv(ow, X)
     check_gemv(Y, ow, X, ref)
-    # fp32 X: the same kernel converting x as it enters LDS; the same bits
+    # fp32 X: the same kernel converting x in registers; the same bits where
+    # both forms take the same geometry (above 32 tokens on tables of more
+    # than 4096 rows fp32 x takes two token tiles per workgroup where staged
+    # x takes four, which changes the waves' split of K; the geometry tests
+    # compare the two forms bit for bit at every forced geometry)
     Yv = mbq().gemv_q(dw, Xd).cpu().numpy()
     check_gemv(Yv, ow, X, ref)
-    assert np.array_equal(Yv.view(np.uint32), Y.view(np.uint32))
+    if M <= 32 or N <= 4096:
+        assert np.array_equal(Yv.view(np.uint32), Y.view(np.uint32))
 
 
 def test_mfma_token_scales_and_accumulate():
