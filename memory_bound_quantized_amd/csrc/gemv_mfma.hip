@@ -611,16 +611,18 @@ hipError_t launch_gemv_mfma_q45(DevPlanes P, int64_t N, int64_t K, const void* x
 // memory round trips at the end).  Shapes by the unsplit row tiles per
 // workgroup, rw1 = N / 4096 rounded up: rw1 = 1 splits in 4 (4 row tiles),
 // rw1 = 2 or 3 in 2 (4 or 6 row tiles), more rows not at all.  Where it
-// pays, measured on the 36-layer model's tables (graphs of cold launches):
-//   rw1 = 1: K >= 12288 (4096 x 12288: 19.5 -> 16.0 us at 16 tokens,
-//            49.6 -> 35.0 at 64, 310 -> 218 at 512), or more than 32 tokens
-//            (4096 x 4096: 16.7 -> 15.9 at 64, 100 -> 88 at 512; 8.1 -> 8.5
-//            at 16, where each part has one step per wave);
-//   rw1 = 2: more than 32 tokens (6144 x 4096: 21.4 -> 20.8 at 64, 108 ->
-//            102 at 512; 10.2 -> 11.6 at 16);
-//   rw1 = 3: K >= 12288 and more than 32 tokens (12288 x 12288: 88.5 ->
-//            81.9 at 64; 12288 x 4096 is slower split at every batch, 14.1
-//            -> 16.4 at 16 and 30.0 -> 35.7 at 64).
+// pays, measured on the 36-layer model's tables (graphs of cold launches,
+// warmed clocks, best of two in alternating order; us at 16 / 64 / 512
+// tokens, K whole -> split):
+//   rw1 = 1: K >= 12288 (4096 x 12288: 18.8 -> 15.3, 46.1 -> 32.8,
+//            309 -> 217), or more than 32 tokens (4096 x 4096: 16.2 ->
+//            15.7 and 98.8 -> 87.9; 8.0 -> 8.4 at 16, where each part has
+//            one step per wave);
+//   rw1 = 2: more than 32 tokens (6144 x 4096: 20.4 -> 20.2, 104 -> 101;
+//            10.0 -> 11.3 at 16);
+//   rw1 = 3: K >= 12288 and more than 32 tokens (12288 x 12288: 76.4 ->
+//            76.0, 556 -> 548; 12288 x 4096 is slower split at every
+//            batch, 13.2 -> 15.7, 26.7 -> 33.6, 184 -> 223).
 // It also needs K / 128 to be a whole number of steps of every part.
 // MBQ_MFMA_SPLIT (tuning): 1 never splits, 2 splits every shape that has a
 // split form.

@@ -75,8 +75,11 @@ def run_path(path, dw, X):
     return out.reshape(M, -1)
 
 
-def applicable(path, fmt):
-    return not path.startswith("mfma") or fmt == 1
+def cases(fmts):
+    """(fmt, path, M) for every path that takes the format: the matrix-core
+    paths take Q45 only."""
+    return [pytest.param(f, p, M, id="fmt%d-%s-M%d" % (f, p, M))
+            for f in fmts for p, M in PATHS if not p.startswith("mfma") or f == 1]
 
 
 def planes_from(fmt, codes, scales, supers=None):
@@ -96,11 +99,8 @@ def offset_weight(fmt, N, K, rng):
     return codes, workloads._fp16_uniform(rng, N * K // 32), None
 
 
-@pytest.mark.parametrize("path,M", PATHS)
-@pytest.mark.parametrize("fmt", [1, 2, 3])
-def test_codes_at_offset_give_exact_zero(path, M, fmt):
-    if not applicable(path, fmt):
-        pytest.skip("matrix-core paths are Q45 only")
+@pytest.mark.parametrize("fmt,path,M", cases([1, 2, 3]))
+def test_codes_at_offset_give_exact_zero(fmt, path, M):
     N, K = 300, 4096
     rng = np.random.default_rng(11 + fmt)
     codes, sc, d = offset_weight(fmt, N, K, rng)
@@ -116,13 +116,10 @@ def few_bit_x(rng, M, K):
     return (rng.integers(-255, 256, size=(M, K)) / 64.0).astype(np.float32)
 
 
-@pytest.mark.parametrize("path,M", PATHS)
-@pytest.mark.parametrize("fmt", [1, 2, 3])
-def test_one_hot_rows_are_exact(path, M, fmt):
+@pytest.mark.parametrize("fmt,path,M", cases([1, 2, 3]))
+def test_one_hot_rows_are_exact(fmt, path, M):
     """One code off the offset per row: y[n] = w[n][k_n] x[k_n], a single
     product that every path must deliver without rounding."""
-    if not applicable(path, fmt):
-        pytest.skip("matrix-core paths are Q45 only")
     N, K = 300, 4096
     rng = np.random.default_rng(21 + fmt + M)
     codes, sc, d = offset_weight(fmt, N, K, rng)
@@ -148,11 +145,8 @@ def test_one_hot_rows_are_exact(path, M, fmt):
         tuple(bad[0]), Y[tuple(bad[0])], expect[tuple(bad[0])])
 
 
-@pytest.mark.parametrize("path,M", PATHS)
-@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
-def test_power_of_two_scaling_is_exact(path, M, fmt):
-    if not applicable(path, fmt):
-        pytest.skip("matrix-core paths are Q45 only")
+@pytest.mark.parametrize("fmt,path,M", cases([0, 1, 2, 3]))
+def test_power_of_two_scaling_is_exact(fmt, path, M):
     N, K = 300, 4096
     rng = np.random.default_rng(31 + fmt + M)
     planes = workloads.weight_planes(rng, fmt, N, K)
@@ -216,11 +210,8 @@ def zero_rows_on(fmt, planes, codes, N, K, rows, chunks):
 
 
 @pytest.mark.parametrize("kind", ["outliers", "far_below", "very_far_below", "mixed"])
-@pytest.mark.parametrize("path,M", PATHS)
-@pytest.mark.parametrize("fmt", [1, 2, 3])
-def test_wide_range_tokens(kind, path, M, fmt):
-    if not applicable(path, fmt):
-        pytest.skip("matrix-core paths are Q45 only")
+@pytest.mark.parametrize("fmt,path,M", cases([1, 2, 3]))
+def test_wide_range_tokens(kind, fmt, path, M):
     N, K = 300, 4096
     print("wide-range %s path=%s M=%d fmt=%d" % (kind, path, M, fmt), flush=True)
     rng = np.random.default_rng(zlib.crc32(("%s %s %d %d" % (kind, path, M, fmt)).encode()))
