@@ -332,6 +332,51 @@ def decode_token_parallel(layers, vocab: Planes, g1, g2, gf, eps: float, h0,
     return h, logits
 
 
+def decode_token_kv(layers, vocab: Planes, g1, g2, gf, eps: float, h0, kcaches, vcaches,
+                    T: int, head_dim: int = 128, threads: int | None = None):
+    """One decode token with attention over a KV cache in place of the
+    stand-in ([roofline-holds] "Said before the run": each token also reads
+    the keys and values of the positions before it).  Per layer l, with
+    a = rmsnorm(h, g1[l]) and b = rmsnorm(h, g2[l]):
+        q = Wq a;  k = Wk a;  v = Wv a
+        K_l[T] = fp16(k);  V_l[T] = fp16(v)     (binary16, nearest even)
+        o = attention(q, K_l[0 .. T], V_l[0 .. T])   (T + 1 positions)
+        h += Wo o
+        h += Wd (silu(Wg b) * (Wu b))
+    then logits = Wvocab rmsnorm(h, gf).  The new position is stored before
+    it is attended to, so it enters the scores as fp16, like every cached
+    one.  kcaches[l], vcaches[l]: float16 arrays [capacity > T, >= dkv],
+    head g of a row at g * head_dim; row T of each is overwritten.  Every
+    step is the oracle's own (rmsnorm, gemv, silu_mul, attention_decode;
+    fp32 between steps); the products' rows are split over threads as in
+    gemv_parallel.  Returns (h_final, logits)."""
+    d = vocab.K
+    h = _c(h0, np.float32).copy()
+    g1 = _c(g1, np.float32)
+    g2 = _c(g2, np.float32)
+    for l, lay in enumerate(layers):
+        dq, dkv = lay["q"].N, lay["k"].N
+        kc, vc = kcaches[l], vcaches[l]
+        assert kc.dtype == np.float16 and vc.dtype == np.float16
+        assert kc.shape[0] > T and kc.shape[1] >= dkv and vc.shape == kc.shape
+        a = rmsnorm(h, g1[l * d:(l + 1) * d], eps)[0]
+        q = gemv_parallel(lay["q"], a, threads)[0]
+        k = gemv_parallel(lay["k"], a, threads)[0]
+        v = gemv_parallel(lay["v"], a, threads)[0]
+        kc[T, :dkv] = k.astype(np.float16)
+        vc[T, :dkv] = v.astype(np.float16)
+        o = attention_decode(q, kc[:T + 1], vc[:T + 1], dq // head_dim, dkv // head_dim, head_dim)
+        h = gemv_parallel(lay["o"], o, threads, y0=h)[0]
+        b = rmsnorm(h, g2[l * d:(l + 1) * d], eps)[0]
+        g = gemv_parallel(lay["gate"], b, threads)[0]
+        u = gemv_parallel(lay["up"], b, threads)[0]
+        m = silu_mul(g, u)
+        h = gemv_parallel(lay["down"], m, threads, y0=h)[0]
+    z = rmsnorm(h, gf, eps)[0]
+    logits = gemv_parallel(vocab, z, threads)[0]
+    return h, logits
+
+
 def f32_to_f16(x: float) -> int:
     """fp32 value -> binary16 bits (nearest even, saturating at 65504)."""
     return int(lib().oracle_f32_to_f16_sat(float(np.float32(x))))
