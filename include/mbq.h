@@ -234,6 +234,34 @@ int mbq_decode_workspace_bytes(const mbq_decode_model* model, size_t* bytes);
 int mbq_decode_step(const mbq_decode_model* model, float* h, float* logits, void* workspace,
                     size_t workspace_bytes, void* stream);
 
+/* The decode step with attention over per-layer KV caches in place of the
+ * stand-in ([roofline-holds] "Said before the run": a token of a loaded
+ * conversation also reads every earlier position's keys and values).  Per
+ * layer l, with T positions already cached:
+ *     q|k|v = Wqkv rmsnorm(h, gamma1)
+ *     K_l[T] = fp16(k), V_l[T] = fp16(v)       (nearest even)
+ *     att = attention(q, K_l[0 .. T], V_l[0 .. T])   (as mbq_attention_decode,
+ *                                                      T + 1 positions)
+ *     h += Wo att;  h += Wdown (silu(Wgate b) * (Wup b)), b = rmsnorm(h, gamma2)
+ * then logits as in mbq_decode_step.  Six launches per layer: the four of
+ * mbq_decode_step and the two of mbq_attention_decode_append between the qkv
+ * and o products.  The heads are dq / 128 query heads on dkv / 128
+ * key/value heads (head size 128, 1, 2, 4 or 8 query heads per key/value
+ * head; MBQ_EUNSUPPORTED otherwise).
+ * k_caches, v_caches: host arrays of n_layers device pointers to fp16
+ * caches, 16-byte aligned, row t at t * ld elements (ld >= dkv, a multiple
+ * of 8), room for at least T + 1 rows; row T of each is written, rows
+ * 0 .. T-1 are read.  The caches must not overlap h, logits, the workspace
+ * or each other.  workspace: device, 256-byte aligned, at least
+ * mbq_decode_kv_workspace_bytes(model, T) bytes (q|k|v, the gated
+ * activations, the attention output and its partial records; contents
+ * need no initialisation).  h, logits: as for mbq_decode_step.  MBQ_EINVAL
+ * for T < 0. */
+int mbq_decode_kv_workspace_bytes(const mbq_decode_model* model, int64_t T, size_t* bytes);
+int mbq_decode_step_kv(const mbq_decode_model* model, float* h, float* logits,
+                       void* const* k_caches, void* const* v_caches, int64_t T, int64_t ld,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* mbq_decode_step for callers that cannot allocate device memory (code under
  * HIP graph capture that may not call hipMalloc, tight serving loops,
  * harnesses that forbid allocation): the same launches, kernels and
@@ -409,6 +437,23 @@ int mbq_attention_workspace_bytes(int64_t T, int n_heads, int n_kv_heads, int he
 int mbq_attention_decode(const float* q, const void* k_cache, const void* v_cache, int64_t T,
                          int64_t ld, int n_heads, int n_kv_heads, int head_dim, float* out,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* mbq_attention_decode for a token whose own key and value are not cached
+ * yet (the decode step's order: the new position is stored, then attended
+ * to).  k_new, v_new: device fp32 [n_kv_heads][head_dim], 16-byte aligned:
+ * they are rounded to fp16 (nearest even) and written to row T of k_cache
+ * and v_cache, and the attention covers rows 0 .. T (T + 1 positions; T >= 0
+ * cached positions before the call, so the caches need room for T + 1
+ * rows).  One fused step: the partial launch takes the new position from
+ * k_new / v_new and its owning lanes store the row; no launch reads that
+ * row from the cache.  workspace: at least mbq_attention_workspace_bytes
+ * for T + 1 positions.  out, the workspace and the caches' rows 0 .. T must
+ * not overlap one another or q, k_new, v_new (MBQ_EINVAL); other arguments
+ * and errors as for mbq_attention_decode. */
+int mbq_attention_decode_append(const float* q, const float* k_new, const float* v_new,
+                                void* k_cache, void* v_cache, int64_t T, int64_t ld, int n_heads,
+                                int n_kv_heads, int head_dim, float* out, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /* Device quantizer: fp32 weights w [N][ldw] (device, 16-byte aligned, ldw a
  * multiple of 4, ldw >= K) -> the planes of format fmt (device pointers in

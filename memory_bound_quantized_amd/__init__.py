@@ -318,6 +318,31 @@ def attention_decode(q, k_cache, v_cache, n_heads: int, n_kv_heads: int, T: int 
     return out
 
 
+def attention_decode_append(q, k_new, v_new, k_cache, v_cache, T: int, n_heads: int,
+                            n_kv_heads: int, out=None, workspace=None, stream=None):
+    """The new token's key and value stored at row T of the caches, then its
+    attention over rows 0 .. T (mbq_attention_decode_append).  q: fp32 cuda
+    [n_heads * 128]; k_new, v_new: fp32 cuda [n_kv_heads * 128]; k_cache,
+    v_cache: fp16 (or int16) cuda [capacity > T, >= n_kv_heads * 128] with
+    the same row stride, updated in place."""
+    import torch
+    T = int(T)
+    if out is None:
+        out = torch.empty(n_heads * 128, dtype=torch.float32, device=q.device)
+    need = attention_workspace_bytes(T + 1, n_heads, n_kv_heads)
+    if workspace is None:
+        workspace = torch.empty((need + 15) // 16 * 4, dtype=torch.float32, device=q.device)
+    assert k_cache.stride(0) == v_cache.stride(0)
+    if k_cache.shape[0] <= T or v_cache.shape[0] <= T:
+        raise ValueError("the caches need room for row T")
+    check(lib.mbq_attention_decode_append(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                                          _ptr(v_cache), T, k_cache.stride(0), n_heads, n_kv_heads,
+                                          128, _ptr(out), _ptr(workspace),
+                                          workspace.numel() * workspace.element_size(),
+                                          _stream(stream)))
+    return out
+
+
 def probe_mixed(distinct, distinct_bytes: int, shared, shared_bytes: int, mode: int, blocks: int,
                 sink, stream=None):
     """Per-compute-unit HBM and L2 streams (mbq_probe_mixed)."""

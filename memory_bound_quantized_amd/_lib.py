@@ -18,11 +18,12 @@ BF16, Q45, Q65, Q25 = 0, 1, 2, 3
 EXPORTS = (
     "mbq_format_info", "mbq_plane_sizes", "mbq_pack", "mbq_unpack", "mbq_gemv_q",
     "mbq_gemv_q_gather", "mbq_gemv_fused", "mbq_decode_workspace_bytes", "mbq_decode_step",
-    "mbq_decode_step_noalloc", "mbq_decode_prepare", "mbq_decode_step_persistent",
+    "mbq_decode_kv_workspace_bytes", "mbq_decode_step_kv", "mbq_decode_step_noalloc", "mbq_decode_prepare", "mbq_decode_step_persistent",
     "mbq_xq_bytes", "mbq_stage_x", "mbq_gemv_xq", "mbq_gemv_xq_workspace_bytes", "mbq_gemv_xq_ws",
     "mbq_rmsnorm_xq",
     "mbq_silu_mul_xq", "mbq_rmsnorm", "mbq_layernorm", "mbq_silu_mul", "mbq_dequant_f32",
-    "mbq_unpack_codes", "mbq_quantize", "mbq_attention_workspace_bytes", "mbq_attention_decode", "mbq_probe_read", "mbq_probe_copy", "mbq_probe_mixed", "mbq_probe_chase_init",
+    "mbq_unpack_codes", "mbq_quantize", "mbq_attention_workspace_bytes", "mbq_attention_decode",
+    "mbq_attention_decode_append", "mbq_probe_read", "mbq_probe_copy", "mbq_probe_mixed", "mbq_probe_chase_init",
     "mbq_probe_chase", "mbq_probe_peak", "mbq_status_str",
     "mbq_last_error", "mbq_version",
 )
@@ -84,6 +85,9 @@ def _load():
         "mbq_gemv_fused": (i32, [ctypes.POINTER(QWeightDesc), vp, vp, f32, i32, vp, vp]),
         "mbq_decode_workspace_bytes": (i32, [ctypes.POINTER(DecodeModelDesc), ctypes.POINTER(sz)]),
         "mbq_decode_step": (i32, [ctypes.POINTER(DecodeModelDesc), vp, vp, vp, sz, vp]),
+        "mbq_decode_kv_workspace_bytes": (i32, [ctypes.POINTER(DecodeModelDesc), i64, ctypes.POINTER(sz)]),
+        "mbq_decode_step_kv": (i32, [ctypes.POINTER(DecodeModelDesc), vp, vp, ctypes.POINTER(vp),
+                                     ctypes.POINTER(vp), i64, i64, vp, sz, vp]),
         "mbq_decode_step_noalloc": (i32, [ctypes.POINTER(DecodeModelDesc), vp, vp, vp]),
         "mbq_decode_prepare": (i32, [ctypes.POINTER(DecodeModelDesc), vp, sz, vp]),
         "mbq_decode_step_persistent": (i32, [ctypes.POINTER(DecodeModelDesc), vp, vp, vp, sz, vp]),
@@ -102,6 +106,7 @@ def _load():
         "mbq_quantize": (i32, [i32, vp, i64, i64, i64, ctypes.POINTER(vp), vp]),
         "mbq_attention_workspace_bytes": (i32, [i64, i32, i32, i32, ctypes.POINTER(sz)]),
         "mbq_attention_decode": (i32, [vp, vp, vp, i64, i64, i32, i32, i32, vp, vp, sz, vp]),
+        "mbq_attention_decode_append": (i32, [vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, vp, vp, sz, vp]),
         "mbq_probe_mixed": (i32, [vp, sz, vp, sz, i32, i32, vp, vp]),
         "mbq_probe_read": (i32, [vp, sz, vp, vp]),
         "mbq_probe_copy": (i32, [vp, vp, sz, vp]),

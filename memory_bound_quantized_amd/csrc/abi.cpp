@@ -518,10 +518,22 @@ static int check_workspace(const mbq_decode_model* m, const float* h, const floa
     return MBQ_OK;
 }
 
+// Attention over per-layer KV caches inside the launch chain: row T of each
+// layer's caches takes the new key and value, the attention output (dq
+// floats) goes to att, and ws holds the partial records.
+struct KvChain {
+    void* const* kc;
+    void* const* vc;
+    int64_t T, ld;
+    float* att;
+    float* ws;
+};
+
 // The launch chain of one token: qkv holds q|k|v (dq + 2 dkv floats) and mm
-// the gated activations (f floats) between launches.
+// the gated activations (f floats) between launches.  Without kv the o
+// product reads q (the stand-in); with it, the attention output.
 static hipError_t decode_chain(const mbq_decode_model* m, float* h, float* logits, float* qkv,
-                               float* mm, hipStream_t s) {
+                               float* mm, hipStream_t s, const KvChain* kv = nullptr) {
     auto geom = [](const mbq_qweight& W, bool pairs = false, bool norm = false) {
         mbq::GemvGeom g = mbq::gemv_m1_default_geom(W.fmt, W.N, W.K, pairs, norm);
         geom_override(&g);
@@ -533,9 +545,18 @@ static hipError_t decode_chain(const mbq_decode_model* m, float* h, float* logit
         // a = rmsnorm(h, gamma1); q|k|v = Wqkv a
         e = mbq::launch_gemv_fused(L.qkv.fmt, planes_of(&L.qkv), L.qkv.N, L.qkv.K, h, L.gamma1,
                                    m->eps, false, qkv, 0, geom(L.qkv, false, true), s);
-        // h += Wo q   (the attention output stands in as q)
+        // att = attention(q, K[0..T], V[0..T]) after K[T] = k, V[T] = v
+        const float* o_in = qkv;
+        if (kv && e == hipSuccess) {
+            e = mbq::launch_attention_append(qkv, qkv + m->dq, qkv + m->dq + m->dkv,
+                                             (uint16_t*)kv->kc[l], (uint16_t*)kv->vc[l], kv->T,
+                                             kv->ld, (int)(m->dq / mbq::kAttD),
+                                             (int)(m->dkv / mbq::kAttD), kv->att, kv->ws, s);
+            o_in = kv->att;
+        }
+        // h += Wo att   (without a cache q stands in for the attention output)
         if (e == hipSuccess)
-            e = mbq::launch_gemv_m1(L.o.fmt, planes_of(&L.o), L.o.N, L.o.K, qkv, false, h, 1,
+            e = mbq::launch_gemv_m1(L.o.fmt, planes_of(&L.o), L.o.N, L.o.K, o_in, false, h, 1,
                                     nullptr, 1, geom(L.o), s);
         // b = rmsnorm(h, gamma2); m = silu(Wg b) * (Wu b)
         if (e == hipSuccess)
@@ -564,6 +585,83 @@ int mbq_decode_step(const mbq_decode_model* m, float* h, float* logits, void* wo
     float* qkv = (float*)((char*)workspace + lay.qkv);
     float* mm = (float*)((char*)workspace + lay.m);
     return hip_status(decode_chain(m, h, logits, qkv, mm, (hipStream_t)stream), fn);
+}
+
+// ---- the step with attention over KV caches -------------------------------
+static int check_attention_shape(int64_t T, int n_heads, int n_kv, int head_dim, const char* fn);
+
+// Workspace: q|k|v, the gated activations, the attention output, then the
+// attention's partial records for T + 1 positions.
+struct KvLayout {
+    size_t qkv, m, att, rec, total;
+};
+
+static KvLayout kv_layout(const mbq_decode_model* m, int64_t T) {
+    KvLayout L;
+    L.qkv = 0;
+    L.m = align256((size_t)(m->dq + 2 * m->dkv) * 4);
+    L.att = L.m + align256((size_t)m->f * 4);
+    L.rec = L.att + align256((size_t)m->dq * 4);
+    const int nkv = (int)(m->dkv / mbq::kAttD);
+    L.total = L.rec + align256(mbq::attention_workspace_bytes(T + 1, (int)(m->dq / mbq::kAttD),
+                                                              nkv > 0 ? nkv : 1));
+    return L;
+}
+
+static int check_kv_shape(const mbq_decode_model* m, int64_t T, const char* fn) {
+    if (m->dq <= 0 || m->dkv <= 0 || m->dq % mbq::kAttD || m->dkv % mbq::kAttD)
+        return fail(MBQ_EUNSUPPORTED, "%s: dq and dkv must be positive multiples of the head size %d",
+                    fn, mbq::kAttD);
+    if (T < 0) return fail(MBQ_EINVAL, "%s: T < 0", fn);
+    return check_attention_shape(T + 1, (int)(m->dq / mbq::kAttD), (int)(m->dkv / mbq::kAttD), mbq::kAttD, fn);
+}
+
+int mbq_decode_kv_workspace_bytes(const mbq_decode_model* m, int64_t T, size_t* bytes) {
+    const char* fn = "mbq_decode_kv_workspace_bytes";
+    if (!m || !bytes) return fail(MBQ_EINVAL, "%s: NULL pointer", fn);
+    if (m->n_layers < 0 || m->dq < 0 || m->dkv < 0 || m->f < 0)
+        return fail(MBQ_EINVAL, "%s: bad dimensions", fn);
+    if (int rc = check_kv_shape(m, T, fn)) return rc;
+    *bytes = kv_layout(m, T).total;
+    return ok();
+}
+
+int mbq_decode_step_kv(const mbq_decode_model* m, float* h, float* logits, void* const* k_caches,
+                       void* const* v_caches, int64_t T, int64_t ld, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    const char* fn = "mbq_decode_step_kv";
+    int rc = check_decode(m, fn);
+    if (rc) return rc;
+    if ((rc = check_kv_shape(m, T, fn))) return rc;
+    const KvLayout lay = kv_layout(m, T);
+    if (!h || !aligned(h, 16)) return fail(MBQ_EALIGN, "%s: h must be 16-byte aligned", fn);
+    if (m->vocab > 0 && (!logits || !aligned(logits, 4))) return fail(MBQ_EINVAL, "%s: bad logits", fn);
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < lay.total)
+        return fail(MBQ_EINVAL, "%s: workspace must be 256-byte aligned and >= %zu bytes", fn, lay.total);
+    const size_t hb = (size_t)m->d * 4, lb = m->vocab > 0 ? (size_t)m->vocab * 4 : 0;
+    if (overlaps(h, hb, workspace, lay.total) || (lb && (overlaps(logits, lb, h, hb) ||
+                                                         overlaps(logits, lb, workspace, lay.total))))
+        return fail(MBQ_EINVAL, "%s: h, logits and workspace must not overlap", fn);
+    if (ld < m->dkv) return fail(MBQ_EINVAL, "%s: ld < dkv", fn);
+    if (ld % 8) return fail(MBQ_EALIGN, "%s: ld must be a multiple of 8", fn);
+    if (m->n_layers > 0 && (!k_caches || !v_caches)) return fail(MBQ_EINVAL, "%s: cache arrays are NULL", fn);
+    const size_t cb = (size_t)(T * ld + m->dkv) * 2;    // rows 0 .. T
+    for (int l = 0; l < m->n_layers; l++) {
+        const void* kc = k_caches[l];
+        const void* vc = v_caches[l];
+        if (!kc || !vc) return fail(MBQ_EINVAL, "%s: layer %d's cache is NULL", fn, l);
+        if (!aligned(kc, 16) || !aligned(vc, 16))
+            return fail(MBQ_EALIGN, "%s: layer %d's caches must be 16-byte aligned", fn, l);
+        if (overlaps(kc, cb, vc, cb) || overlaps(kc, cb, workspace, lay.total) ||
+            overlaps(vc, cb, workspace, lay.total) || overlaps(kc, cb, h, hb) || overlaps(vc, cb, h, hb) ||
+            (lb && (overlaps(kc, cb, logits, lb) || overlaps(vc, cb, logits, lb))))
+            return fail(MBQ_EINVAL, "%s: layer %d's caches overlap each other or another buffer", fn, l);
+    }
+    char* w = (char*)workspace;
+    const KvChain kv{k_caches, v_caches, T, ld, (float*)(w + lay.att), (float*)(w + lay.rec)};
+    return hip_status(decode_chain(m, h, logits, (float*)(w + lay.qkv), (float*)(w + lay.m),
+                                   (hipStream_t)stream, &kv),
+                      fn);
 }
 
 // ---- the same step without a workspace argument --------------------------
@@ -1028,6 +1126,43 @@ int mbq_attention_decode(const float* q, const void* k_cache, const void* v_cach
     return hip_status(mbq::launch_attention_decode(q, (const uint16_t*)k_cache, (const uint16_t*)v_cache,
                                                    T, ld, n_heads, n_kv_heads, out, (float*)workspace,
                                                    (hipStream_t)stream),
+                      fn);
+}
+
+int mbq_attention_decode_append(const float* q, const float* k_new, const float* v_new,
+                                void* k_cache, void* v_cache, int64_t T, int64_t ld, int n_heads,
+                                int n_kv_heads, int head_dim, float* out, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    const char* fn = "mbq_attention_decode_append";
+    if (T < 0) return fail(MBQ_EINVAL, "%s: T < 0", fn);
+    if (int rc = check_attention_shape(T + 1, n_heads, n_kv_heads, head_dim, fn)) return rc;
+    const int64_t width = (int64_t)n_kv_heads * head_dim;
+    if (ld < width) return fail(MBQ_EINVAL, "%s: ld < n_kv_heads * head_dim", fn);
+    if (!q || !k_new || !v_new || !k_cache || !v_cache || !out || !workspace)
+        return fail(MBQ_EINVAL, "%s: NULL pointer", fn);
+    if (!aligned(q, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(out, 16) ||
+        !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(workspace, 16) || ld % 8)
+        return fail(MBQ_EALIGN, "%s: buffers must be 16-byte aligned and ld a multiple of 8", fn);
+    const size_t need = mbq::attention_workspace_bytes(T + 1, n_heads, n_kv_heads);
+    if (workspace_bytes < need)
+        return fail(MBQ_EINVAL, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, need);
+    const size_t qb = (size_t)n_heads * head_dim * 4, nb = (size_t)width * 4;
+    const size_t cb = (size_t)(T * ld + width) * 2;     // rows 0 .. T
+    const void* wr[4] = {out, workspace, k_cache, v_cache};
+    const size_t wb[4] = {qb, need, cb, cb};
+    const void* rd[3] = {q, k_new, v_new};
+    const size_t rb[3] = {qb, nb, nb};
+    for (int a = 0; a < 4; a++) {
+        for (int b = a + 1; b < 4; b++)
+            if (overlaps(wr[a], wb[a], wr[b], wb[b]))
+                return fail(MBQ_EINVAL, "%s: out, workspace and the caches must not overlap", fn);
+        for (int b = 0; b < 3; b++)
+            if (overlaps(wr[a], wb[a], rd[b], rb[b]))
+                return fail(MBQ_EINVAL, "%s: q, k_new or v_new overlaps a buffer the call writes", fn);
+    }
+    return hip_status(mbq::launch_attention_append(q, k_new, v_new, (uint16_t*)k_cache,
+                                                   (uint16_t*)v_cache, T, ld, n_heads, n_kv_heads,
+                                                   out, (float*)workspace, (hipStream_t)stream),
                       fn);
 }
 

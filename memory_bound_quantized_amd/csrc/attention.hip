@@ -81,17 +81,37 @@ size_t attention_workspace_bytes(int64_t T, int n_heads, int n_kv) {
     return (size_t)n_heads * (size_t)nch * kAttRecord * sizeof(float);
 }
 
+// 8 fp32 values -> the 16 bytes of fp16 a cache row holds for them (each
+// rounded to nearest even; the order `halves` unpacks).
+__device__ __forceinline__ au4 to_halves(const float* __restrict__ src) {
+    const af4 a = *(const af4*)src, b = *(const af4*)(src + 4);
+    const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    au4 w;
+#pragma unroll
+    for (int e = 0; e < 4; e++)
+        w[e] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f[2 * e]) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f[2 * e + 1]) << 16);
+    return w;
+}
+
 // Workgroup (kv head, chunk): the chunk's partial record for each of the G
 // query heads of the group, at ws[((kv * nch) + chunk) * G + hl] (records of
 // kAttRecord floats: m, l, then d values of o; m and l in base 2).  Wave w
 // owns the groups of 4 positions w, w + 4, ...: it issues all their key and
 // value loads first, so the chunk costs one memory round trip.
-template <int G>
+// APPEND: position T - 1 is the new one.  Its key and value come from knew
+// and vnew (fp32, rounded to fp16 here exactly as the cache stores them),
+// and the lanes that own it write that row of the caches (kw, vw); no
+// workgroup reads the row from the cache.
+template <int G, bool APPEND>
 __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const float* __restrict__ q,
                                                                 const uint16_t* __restrict__ kc,
                                                                 const uint16_t* __restrict__ vc,
                                                                 int64_t T, int64_t ld, int C,
-                                                                float qscale, float* __restrict__ ws) {
+                                                                float qscale, float* __restrict__ ws,
+                                                                const float* __restrict__ knew,
+                                                                const float* __restrict__ vnew,
+                                                                uint16_t* kw, uint16_t* vw) {
     extern __shared__ __attribute__((aligned(16))) float alds[];
     float* sc = alds;                               // [G][C] scores, then weights
     float* red = alds + G * C;                      // [16][G][d] partial outputs
@@ -112,8 +132,17 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const float* __r
         const int base = 4 * (wave + kWaves * jg);
         if (base < tn) {                            // the same in every lane of the wave
             const int64_t row = t0 + min(base + p, tn - 1);
-            kr[jg] = *(const au4*)(kc + row * ld + hoff);
-            vr[jg] = *(const au4*)(vc + row * ld + hoff);
+            if (APPEND && row == T - 1) {           // only in the last chunk's last group
+                kr[jg] = to_halves(knew + hoff);
+                vr[jg] = to_halves(vnew + hoff);
+                if (base + p == tn - 1) {           // one lane per 16 bytes writes the row
+                    *(au4*)(kw + row * ld + hoff) = kr[jg];
+                    *(au4*)(vw + row * ld + hoff) = vr[jg];
+                }
+            } else {
+                kr[jg] = *(const au4*)(kc + row * ld + hoff);
+                vr[jg] = *(const au4*)(vc + row * ld + hoff);
+            }
         }
     }
 
@@ -270,8 +299,10 @@ __global__ __launch_bounds__(kAttD) void attn_combine_kernel(const float* __rest
     out[(int64_t)h * kAttD + dd] = acc / L;
 }
 
-hipError_t launch_attention_decode(const float* q, const uint16_t* kc, const uint16_t* vc, int64_t T,
+template <bool APPEND>
+static hipError_t launch_attention(const float* q, const uint16_t* kc, const uint16_t* vc, int64_t T,
                                    int64_t ld, int n_heads, int n_kv, float* out, float* ws,
+                                   const float* knew, const float* vnew, uint16_t* kw, uint16_t* vw,
                                    hipStream_t stream) {
     const int G = n_heads / n_kv;
     const int C = attention_chunk(T, n_kv);
@@ -282,9 +313,9 @@ hipError_t launch_attention_decode(const float* q, const uint16_t* kc, const uin
     switch (G) {
 #define MBQ_ATT_CASE(g)                                                                              \
     case g:                                                                                          \
-        if (hipError_t e = ensure_lds<attn_partial_kernel<g>>(lds)) return e;                        \
-        hipLaunchKernelGGL(attn_partial_kernel<g>, grid, dim3(kThreads), lds, stream, q, kc, vc, T, \
-                           ld, C, qscale, ws);                                                       \
+        if (hipError_t e = ensure_lds<attn_partial_kernel<g, APPEND>>(lds)) return e;                \
+        hipLaunchKernelGGL((attn_partial_kernel<g, APPEND>), grid, dim3(kThreads), lds, stream, q,  \
+                           kc, vc, T, ld, C, qscale, ws, knew, vnew, kw, vw);                       \
         break;
         MBQ_ATT_CASE(1)
         MBQ_ATT_CASE(2)
@@ -297,6 +328,22 @@ hipError_t launch_attention_decode(const float* q, const uint16_t* kc, const uin
     hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)n_heads), dim3(kAttD), 0, stream, ws, G,
                        nch, out);
     return hipGetLastError();
+}
+
+hipError_t launch_attention_decode(const float* q, const uint16_t* kc, const uint16_t* vc, int64_t T,
+                                   int64_t ld, int n_heads, int n_kv, float* out, float* ws,
+                                   hipStream_t stream) {
+    return launch_attention<false>(q, kc, vc, T, ld, n_heads, n_kv, out, ws, nullptr, nullptr,
+                                   nullptr, nullptr, stream);
+}
+
+// T cached positions plus the new one (T + 1 in all): the partial launch
+// takes the new key and value from knew / vnew and writes them to row T.
+hipError_t launch_attention_append(const float* q, const float* knew, const float* vnew,
+                                   uint16_t* kc, uint16_t* vc, int64_t T, int64_t ld, int n_heads,
+                                   int n_kv, float* out, float* ws, hipStream_t stream) {
+    return launch_attention<true>(q, kc, vc, T + 1, ld, n_heads, n_kv, out, ws, knew, vnew, kc, vc,
+                                  stream);
 }
 
 }  // namespace mbq

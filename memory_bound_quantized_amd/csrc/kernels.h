@@ -224,6 +224,12 @@ size_t attention_workspace_bytes(int64_t T, int n_heads, int n_kv);
 hipError_t launch_attention_decode(const float* q, const uint16_t* kc, const uint16_t* vc, int64_t T,
                                    int64_t ld, int n_heads, int n_kv, float* out, float* ws,
                                    hipStream_t stream);
+// The new token's key and value (fp32, knew / vnew, head g at g * kAttD)
+// rounded to fp16 and written to row T of the caches, then attention over
+// rows 0 .. T (workspace: attention_workspace_bytes(T + 1, ...)).
+hipError_t launch_attention_append(const float* q, const float* knew, const float* vnew,
+                                   uint16_t* kc, uint16_t* vc, int64_t T, int64_t ld, int n_heads,
+                                   int n_kv, float* out, float* ws, hipStream_t stream);
 
 hipError_t launch_probe_read(const void* buf, size_t bytes, float* sink, hipStream_t stream);
 hipError_t launch_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);

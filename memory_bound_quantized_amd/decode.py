@@ -100,6 +100,32 @@ class DecodeModel:
                                   _ptr(self.workspace), self.workspace.numel(), _stream(stream)))
         return logits
 
+    def kv_workspace(self, T: int):
+        """A workspace for step_kv at T cached positions (mbq_decode_kv_workspace_bytes)."""
+        import torch
+        nb = ctypes.c_size_t()
+        check(lib.mbq_decode_kv_workspace_bytes(ctypes.byref(self.desc), int(T), ctypes.byref(nb)))
+        return torch.empty(max(int(nb.value), 256), dtype=torch.uint8, device=self.device)
+
+    def step_kv(self, h, logits, k_caches, v_caches, T: int, workspace=None, stream=None):
+        """One token with attention over the per-layer KV caches
+        (mbq_decode_step_kv): row T of every cache takes the token's key and
+        value, and attention covers rows 0 .. T.  k_caches, v_caches: lists of
+        fp16 cuda tensors [capacity > T, >= dkv], one per layer, all with one
+        row stride; updated in place."""
+        L = len(self.layer_w)
+        assert len(k_caches) == L and len(v_caches) == L
+        ld = k_caches[0].stride(0) if L else self.dkv
+        for c in list(k_caches) + list(v_caches):
+            assert c.stride(0) == ld and c.shape[0] > T
+        kp = (ctypes.c_void_p * max(L, 1))(*[c.data_ptr() for c in k_caches])
+        vp = (ctypes.c_void_p * max(L, 1))(*[c.data_ptr() for c in v_caches])
+        if workspace is None:
+            workspace = self.kv_workspace(T)
+        check(lib.mbq_decode_step_kv(ctypes.byref(self.desc), _ptr(h), _ptr(logits), kp, vp, int(T),
+                                     ld, _ptr(workspace), workspace.numel(), _stream(stream)))
+        return logits
+
     def step_noalloc(self, h, logits, stream=None):
         """One token without a workspace: mbq_decode_step_noalloc (the
         library's own per-GPU array holds the activations; allocates

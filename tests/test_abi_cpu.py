@@ -30,7 +30,7 @@ def _declared_symbols():
 
 def test_library_exports_every_declared_symbol():
     declared = _declared_symbols()
-    assert len(declared) == 36
+    assert len(declared) == 39
     assert sorted(_lib.EXPORTS) == declared
     lib = ctypes.CDLL(_lib.LIB_PATH)
     for name in declared:
@@ -343,6 +343,70 @@ def test_decode_argument_checks():
     q65o.layers[0].o.super_scales = BASE + 0xA00000
     assert ps(q65o) == _lib.EUNSUPPORTED                                    # o must be Q45
     assert L.mbq_decode_prepare(ctypes.byref(m), ws + 16, nb.value, None) == _lib.EINVAL
+    assert L.mbq_last_error()
+
+
+def test_decode_kv_argument_checks():
+    m = _model(L=2)
+    nb = ctypes.c_size_t()
+    # q|k|v, the gated activations, the attention output, then one record per
+    # query head and chunk for T + 1 = 512 positions (16 chunks of 32)
+    assert L.mbq_decode_kv_workspace_bytes(ctypes.byref(m), 511, ctypes.byref(nb)) == _lib.OK
+    assert nb.value == (4096 + 2048) * 4 + 12288 * 4 + 4096 * 4 + 32 * 16 * 132 * 4
+    assert L.mbq_decode_kv_workspace_bytes(ctypes.byref(m), -1, ctypes.byref(nb)) == _lib.EINVAL
+    assert L.mbq_decode_kv_workspace_bytes(ctypes.byref(_model(dq=4096, dkv=1000)), 5,
+                                           ctypes.byref(nb)) == _lib.EUNSUPPORTED   # not whole heads
+    assert L.mbq_decode_kv_workspace_bytes(ctypes.byref(_model(dkv=384)), 5,
+                                           ctypes.byref(nb)) == _lib.EINVAL          # 32 on 3 heads
+    assert L.mbq_decode_kv_workspace_bytes(ctypes.byref(_model(dq=3072)), 5,
+                                           ctypes.byref(nb)) == _lib.EUNSUPPORTED   # 24 on 8: G = 3
+    assert L.mbq_decode_kv_workspace_bytes(ctypes.byref(m), 511, ctypes.byref(nb)) == _lib.OK
+    h, lg, ws = BASE + 0x7000000000, BASE + 0x7100000000, BASE + 0x7200000000
+    kc = [BASE + 0x7300000000, BASE + 0x7400000000]
+    vc = [BASE + 0x7500000000, BASE + 0x7600000000]
+
+    def st(m=m, h=h, lg=lg, ws=ws, n=nb.value, k=kc, v=vc, T=511, ld=1024):
+        ka = (ctypes.c_void_p * 2)(*k)
+        va = (ctypes.c_void_p * 2)(*v)
+        return L.mbq_decode_step_kv(ctypes.byref(m), h, lg, ka, va, T, ld, ws, n, None)
+
+    assert st(n=nb.value - 1) == _lib.EINVAL                                # workspace too small
+    assert st(ws=ws + 16) == _lib.EINVAL                                    # 256-byte alignment
+    assert st(h=h + 4) == _lib.EALIGN
+    assert st(T=-1) == _lib.EINVAL
+    assert st(ld=1000) == _lib.EINVAL                                       # ld < dkv
+    assert st(ld=1028) == _lib.EALIGN                                       # ld % 8
+    assert st(k=[kc[0], 0]) == _lib.EINVAL                                  # a NULL cache
+    assert st(v=[vc[0], vc[1] + 8]) == _lib.EALIGN
+    assert st(v=[kc[0] + 1024, vc[1]]) == _lib.EINVAL                       # V inside K's rows
+    assert st(k=[ws + 4096, kc[1]]) == _lib.EINVAL                          # K over the workspace
+    assert st(k=[kc[0], h - 64]) == _lib.EINVAL                             # K's rows reach h
+    assert L.mbq_decode_step_kv(ctypes.byref(m), h, lg, None, None, 511, 1024, ws, nb.value,
+                                None) == _lib.EINVAL
+    assert L.mbq_last_error()
+
+
+def _attn_append(q=BASE, kn=BASE + 0x10000, vn=BASE + 0x20000, k=BASE + 0x1000000,
+                 v=BASE + 0x2000000, T=511, ld=1024, H=32, Hkv=8, d=128, out=BASE + 0x3000000,
+                 ws=BASE + 0x4000000, wsb=1 << 24):
+    return L.mbq_attention_decode_append(q, kn, vn, k, v, T, ld, H, Hkv, d, out, ws, wsb, None)
+
+
+def test_attention_append_argument_checks():
+    assert _attn_append(T=-1) == _lib.EINVAL
+    assert _attn_append(d=96) == _lib.EUNSUPPORTED
+    assert _attn_append(H=24) == _lib.EUNSUPPORTED                          # G = 3
+    assert _attn_append(ld=1000) == _lib.EINVAL
+    assert _attn_append(ld=1028) == _lib.EALIGN
+    assert _attn_append(kn=0) == _lib.EINVAL
+    assert _attn_append(vn=BASE + 0x20004) == _lib.EALIGN
+    # the workspace covers T + 1 positions: 512 at T = 511 (16 chunks of 32)
+    assert _attn_append(wsb=32 * 16 * 132 * 4 - 4) == _lib.EINVAL
+    assert _attn_append(kn=BASE + 0x1000000 + 511 * 2048) == _lib.EINVAL    # k_new on the row written
+    assert _attn_append(vn=BASE + 0x3000000 + 64) == _lib.EINVAL            # v_new under out
+    assert _attn_append(v=BASE + 0x1000000 + 1024) == _lib.EINVAL           # V inside K's rows
+    assert _attn_append(ws=BASE + 0x2000000 + 4096) == _lib.EINVAL          # workspace over V
+    assert _attn_append(out=BASE) == _lib.EINVAL                            # out over q
     assert L.mbq_last_error()
 
 

@@ -214,3 +214,128 @@ def test_attention_in_a_replayed_graph():
         torch.cuda.synchronize()
         assert torch.equal(out, eager), i
     check(out.cpu().numpy(), q, kc, vc, H, Hkv, T)
+
+
+# --------------------------------------------------------------------------
+# the new position stored, then attended to (mbq_attention_decode_append)
+# --------------------------------------------------------------------------
+
+def append_case(T, H=32, Hkv=8, extra_rows=2, pad=64, seed=0):
+    rng = np.random.default_rng(1000 + T + seed)
+    width = Hkv * D + pad
+    kc, vc = cache(rng, T + 1 + extra_rows, width)
+    q = rng.normal(size=H * D).astype(np.float32)
+    kn = rng.normal(size=Hkv * D).astype(np.float32)
+    vn = rng.normal(size=Hkv * D).astype(np.float32)
+    return q, kn, vn, kc, vc
+
+
+def run_append(q, kn, vn, kc, vc, T, H, Hkv, workspace=None):
+    kd = torch.from_numpy(kc.view(np.int16)).cuda()
+    vd = torch.from_numpy(vc.view(np.int16)).cuda()
+    out = mbq().attention_decode_append(dev(q), dev(kn), dev(vn), kd, vd, T, H, Hkv,
+                                        workspace=workspace)
+    return out.cpu().numpy(), kd.cpu().numpy().view(np.float16), vd.cpu().numpy().view(np.float16)
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+@pytest.mark.parametrize("T", [0, 1, 15, 16, 511, 4095, 5000])
+def test_append_stores_the_row_and_matches_oracle(T):
+    """Row T takes fp16 of k_new and v_new (numpy's conversion, nearest
+    even); every other row and the columns past the heads keep their bits;
+    the output is the oracle's attention over rows 0 .. T of the updated
+    caches."""
+    print("attention append T=%d" % T, flush=True)
+    H, Hkv = 32, 8
+    q, kn, vn, kc, vc = append_case(T)
+    out, k2, v2 = run_append(q, kn, vn, kc, vc, T, H, Hkv)
+    keep = np.ones(kc.shape[0], bool)
+    keep[T] = False
+    assert np.array_equal(k2[keep].view(np.uint16), kc[keep].view(np.uint16))
+    assert np.array_equal(v2[keep].view(np.uint16), vc[keep].view(np.uint16))
+    assert np.array_equal(k2[T, Hkv * D:].view(np.uint16), kc[T, Hkv * D:].view(np.uint16))
+    assert np.array_equal(k2[T, :Hkv * D].view(np.uint16), kn.astype(np.float16).view(np.uint16))
+    assert np.array_equal(v2[T, :Hkv * D].view(np.uint16), vn.astype(np.float16).view(np.uint16))
+    w = Hkv * D
+    check(out, q, np.ascontiguousarray(k2[:, :w]), np.ascontiguousarray(v2[:, :w]), H, Hkv, T + 1)
+
+
+@pytest.mark.parametrize("T,H,Hkv", [(0, 32, 8), (300, 8, 8), (777, 16, 8), (2000, 64, 8), (40, 32, 4)])
+def test_append_equals_attention_over_the_stored_row(T, H, Hkv):
+    """The fused call and mbq_attention_decode over the caches it leaves
+    (T + 1 positions) read the same values in the same order: equal bits."""
+    print("attention append vs plain H=%d Hkv=%d T=%d" % (H, Hkv, T), flush=True)
+    q, kn, vn, kc, vc = append_case(T, H, Hkv, seed=1)
+    out, k2, v2 = run_append(q, kn, vn, kc, vc, T, H, Hkv)
+    kd = torch.from_numpy(k2.view(np.int16)).cuda()
+    vd = torch.from_numpy(v2.view(np.int16)).cuda()
+    plain = mbq().attention_decode(dev(q), kd, vd, H, Hkv, T=T + 1).cpu().numpy()
+    assert np.array_equal(out.view(np.uint32), plain.view(np.uint32))
+
+
+def test_append_rounds_like_binary16():
+    """k_new and v_new values at binary16 ties (both parities), just off
+    them, in the subnormal range, at the largest finite half and past it
+    (to infinity, as an IEEE conversion does): the stored bits equal
+    numpy's float16 conversion.  Only the stored row is compared (infinite
+    keys make the scores meaningless)."""
+    print("attention append rounding", flush=True)
+    H, Hkv, T = 8, 8, 3
+    rng = np.random.default_rng(77)
+    n = Hkv * D
+    one = np.float32(1.0)
+    vals = np.concatenate([
+        one + np.float32(2.0 ** -11) * np.arange(1, 200, 2, dtype=np.float32),    # ties
+        one + np.float32(2.0 ** -11) * np.arange(1, 200, 2, dtype=np.float32) + np.float32(2.0 ** -23),
+        np.float32(2.0 ** -24) * rng.uniform(0, 1024, 100).astype(np.float32),     # subnormal halves
+        np.array([65504.0, 65519.0, 65520.0, 70000.0, 1e30, 6e-8, 3e-8, 2.9e-8], np.float32),
+    ])
+    vals = vals * np.where(rng.random(vals.size) < 0.5, -1, 1).astype(np.float32)
+    kn = np.resize(vals, n).astype(np.float32)
+    vn = np.resize(vals[::-1], n).astype(np.float32)
+    q, _, _, kc, vc = append_case(T, H, Hkv, seed=2)
+    _, k2, v2 = run_append(q, kn, vn, kc, vc, T, H, Hkv)
+    with np.errstate(over="ignore"):                             # past 65520: infinity, as intended
+        k16, v16 = kn.astype(np.float16), vn.astype(np.float16)
+    assert np.isinf(k16).any()
+    assert np.array_equal(k2[T, :n].view(np.uint16), k16.view(np.uint16))
+    assert np.array_equal(v2[T, :n].view(np.uint16), v16.view(np.uint16))
+
+
+def test_append_in_a_replayed_graph():
+    """The fused call captured in a HIP graph, replayed with eager work and
+    synchronizations in between; each replay stores the same row and gives
+    the eager result bit for bit."""
+    print("attention append graph replays", flush=True)
+    H, Hkv, T = 32, 8, 512
+    q, kn, vn, kc, vc = append_case(T, H, Hkv, seed=3)
+    qd, knd, vnd = dev(q), dev(kn), dev(vn)
+    kd = torch.from_numpy(kc.view(np.int16)).cuda()
+    vd = torch.from_numpy(vc.view(np.int16)).cuda()
+    ws = torch.zeros((mbq().attention_workspace_bytes(T + 1, H, Hkv) + 15) // 16 * 4,
+                     dtype=torch.float32, device="cuda")
+    eager = mbq().attention_decode_append(qd, knd, vnd, kd, vd, T, H, Hkv, workspace=ws).clone()
+    k_eager = kd.clone()
+    out = torch.empty_like(eager)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        mbq().attention_decode_append(qd, knd, vnd, kd, vd, T, H, Hkv, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mbq().attention_decode_append(qd, knd, vnd, kd, vd, T, H, Hkv, out=out, workspace=ws)
+    for i in range(4):
+        out.fill_(float("nan"))
+        ws.fill_(float("nan"))
+        kd[T, :Hkv * D].fill_(0)                                  # the row the call writes
+        mbq().attention_decode(qd, kd, vd, H, Hkv, T=T)          # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), i
+        assert torch.equal(kd, k_eager), i

@@ -147,3 +147,18 @@ def config5(experts: int = 64, rows: int = 1536, k: int = 4096, n_sel: int = 8,
     return dict(W=W, rows_per_expert=rows, idx=idx, x=x, ln_x=X,
                 ln_gamma=uniform(r[4], ln_n, 0.5, 1.5), ln_beta=normal(r[5], ln_n, 0.0, 0.1),
                 ln_eps=1e-5)
+
+
+def kv_caches(layers: int, rows: int, width: int, seed: int = 3000):
+    """Per-layer fp16 key and value caches [rows, width] for the decode step
+    with attention: entries N(0, 1) rounded to fp16, like the keys and values
+    a 36-layer model of this width leaves for earlier positions (the pages
+    give only their byte count, 2 bytes per value).  Returns (k_caches,
+    v_caches), lists of float16 arrays; layer l's pair comes from children
+    2 l and 2 l + 1 of SeedSequence(seed)."""
+    rngs = [np.random.default_rng(s) for s in np.random.SeedSequence(seed).spawn(2 * layers)]
+    ks = [rngs[2 * l].standard_normal((rows, width), dtype=np.float32).astype(np.float16)
+          for l in range(layers)]
+    vs = [rngs[2 * l + 1].standard_normal((rows, width), dtype=np.float32).astype(np.float16)
+          for l in range(layers)]
+    return ks, vs
