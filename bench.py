@@ -175,6 +175,23 @@ def cpu_baseline(cfg, y_up_gpu, y_down_gpu, decode=None, budget_s: float = 10.0)
         if bad:
             raise SystemExit("decode token disagrees with the oracle chain (%s): %s"
                              % (", ".join(bad), json.dumps(errs)))
+        if "kv" in decode:
+            # the token with attention over the cache (the oracle updates its
+            # own copies of the caches' row T)
+            kv = decode["kv"]
+            t0 = time.perf_counter()
+            kc = [c.copy() for c in kv["k"]]
+            vc = [c.copy() for c in kv["v"]]
+            h_ref, lg_ref = oracle.decode_token_kv(lay, oracle.Planes(*c3["vocab"]), c3["g1"], c3["g2"],
+                                                   c3["gf"], c3["eps"], c3["h0"], kc, vc, kv["T"],
+                                                   threads=threads)
+            t_kv = time.perf_counter() - t0
+            h, lg = kv["out"]
+            e = {"h": rel(h, h_ref), "logits": rel(lg, lg_ref)}
+            out["decode_token_with_attention_512"] = {"seconds_per_token": round(t_kv, 3),
+                                                      "threads": threads, "checked_rel_l2": e}
+            if max(e.values()) > 1e-4:
+                raise SystemExit("decode token with attention disagrees with the oracle: %s" % json.dumps(e))
     return out
 
 
@@ -444,10 +461,41 @@ def decode_row(workloads, torch, dev, peak_gbs, ntok=20, one_launch=True, keep=N
             raise SystemExit("one-launch decode step reported status %d" % model.status())
         row["one_launch"] = {"ms_per_token": round(ms_p, 4), "ratio_to_floor": round(ms_p / floor_ms, 3),
                              "status_ok": ok}
+    # the same token with attention over 512 cached positions in every layer
+    # (mbq_decode_step_kv: the cache append fused into the attention's first
+    # launch), captured in one graph; row 512 of each cache is rewritten with
+    # the same values by every replay
+    T = 512
+    kh, vh = workloads.kv_caches(36, T + 1, model.dkv, seed=3000)
+    kd = [torch.from_numpy(c.view(np.int16)).to(dev) for c in kh]
+    vd = [torch.from_numpy(c.view(np.int16)).to(dev) for c in vh]
+    ws = model.kv_workspace(T)
+    hk, lk = h0.clone(), torch.empty_like(logits)
+    gk = capture(lambda: model.step_kv(hk, lk, kd, vd, T, workspace=ws))
+    hk.copy_(h0)
+    torch.cuda.synchronize()
+    gk.replay()
+    torch.cuda.synchronize()
+    kv_out = (hk.cpu().numpy(), lk.cpu().numpy())
+    gk.replay()
+    ms_kv = timed(gk, ntok) / ntok
+    kv_read = 36 * 2 * T * model.dkv * 2                 # rows 0 .. 511 of K and V, every layer
+    kv_write = 36 * 2 * model.dkv * 2                    # row 512
+    Bk = B + kv_read + kv_write
+    Bk_all = B_all + kv_read + kv_write + 4 * 36 * model.dq     # + the attention outputs
+    floor_kv = Bk / (peak_gbs * 1e9) * 1e3
+    row["with_attention_512"] = {
+        "ms_per_token": round(ms_kv, 4), "tokens_per_s": round(1e3 / ms_kv, 1),
+        "kv_bytes_per_token": kv_read + kv_write, "bytes_per_token": int(Bk_all),
+        "gbs": round(Bk_all / (ms_kv * 1e-3) / 1e9, 1),
+        "floor_ms_at_measured_peak": round(floor_kv, 4), "ratio_to_floor": round(ms_kv / floor_kv, 3),
+        "attention_ms_per_token": round(ms_kv - ms, 4),
+        "launches_per_token": 6 * 36 + 1, "tokens_timed": ntok}
     if keep is not None:
         keep["cfg"] = {k: v for k, v in c3.items()}
         keep["outputs"] = outputs
-    del model, g
+        keep["kv"] = {"T": T, "k": kh, "v": vh, "out": kv_out}
+    del model, g, gk, kd, vd, ws
     torch.cuda.empty_cache()
     return row
 
@@ -917,8 +965,10 @@ def main():
                                            decode=keep if keep else None)
         if "rows" in out:
             out["rows"]["decode_36_layers"]["checked_against_oracle"] = True
+            out["rows"]["decode_36_layers"]["with_attention_512"]["checked_against_oracle"] = True
     elif "rows" in out:
         out["rows"]["decode_36_layers"]["checked_against_oracle"] = False
+        out["rows"]["decode_36_layers"]["with_attention_512"]["checked_against_oracle"] = False
     print(json.dumps(out))
 
 
