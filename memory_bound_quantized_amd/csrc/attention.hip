@@ -57,21 +57,25 @@ __device__ __forceinline__ void halves(au4 w, float* f) {
 
 }  // namespace
 
-// Positions per workgroup: a multiple of 16 (4 waves x 4 positions), at
-// most 16 groups of 4 per wave (kMaxGroups) so that a wave holds all its
-// keys and values in registers, and otherwise T / P: P = 16 chunks per head
-// below 4096 positions, where the call is latency-bound and each extra
-// chunk record costs the combine step, and P = 32 from 4096 on, where 16
-// chunks per head would leave half the compute units idle (8 heads of 32
-// query heads: 14.6 us against 17.5 at 4096 positions; 7.7 against 9.4 at
-// 512 with P = 16).  MBQ_ATT_CHUNKS overrides P (tuning).
+// Positions per workgroup: T / P rounded to the nearest multiple of 16 (4
+// waves x 4 positions), at least 16 and at most 16 groups of 4 per wave
+// (kMaxGroups) so that a wave holds all its keys and values in registers.
+// P = 16 chunks per head below 1024 positions, where the call is
+// latency-bound and each extra chunk record costs the combine step, and P =
+// 32 from 1024 on, where more workgroups stream the cache (µs, 32 on 8
+// heads, P = 16 against 32: 12.1 against 10.8 at 2048 positions, 9.3
+// either way at 1024; at 4096, 16 chunks per head leave half the compute
+// units idle: 17.5 against 14.6).  Rounding to the nearest multiple keeps
+// 513 positions (512 cached and the new one) at 17 chunks of 32, 8.3 µs,
+// where rounding up gave 11 chunks of 48 and 8.7 µs.  MBQ_ATT_CHUNKS
+// overrides P (tuning).
 constexpr int kMaxGroups = 16;
 int attention_chunk(int64_t T, int n_kv) {
     (void)n_kv;
-    int64_t P = T >= 4096 ? 32 : 16;
+    int64_t P = T >= 1024 ? 32 : 16;
     if (const char* e = tuning_var("MBQ_ATT_CHUNKS")) P = atoll(e) > 0 ? atoll(e) : P;
-    int64_t c = (T + P - 1) / P;
-    c = (c + 15) / 16 * 16;
+    int64_t c = (T + P / 2) / P;                  // T / P to the nearest position
+    c = (c + 8) / 16 * 16;                        // to the nearest multiple of 16
     const int cmax = 16 * kMaxGroups;
     return (int)(c < 16 ? 16 : (c > cmax ? cmax : c));
 }
