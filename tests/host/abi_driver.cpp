@@ -131,11 +131,52 @@ static void argument_checks() {
                                fake(0x4000000), 1 << 24, nullptr) == MBQ_EALIGN);
     CHECK(mbq_attention_decode(x, fake(0x1000000), fake(0x2000000), 512, 1024, 32, 8, 128, y,
                                fake(0x4000000), 16, nullptr) == MBQ_EINVAL);
+    // the fused append: T counts cached positions, the workspace covers T + 1
+    CHECK(mbq_attention_decode_append(x, (float*)fake(0x10000), (float*)fake(0x20000), fake(0x1000000),
+                                      fake(0x2000000), -1, 1024, 32, 8, 128, y, fake(0x4000000), 1 << 24,
+                                      nullptr) == MBQ_EINVAL);
+    CHECK(mbq_attention_decode_append(x, (float*)fake(0x10004), (float*)fake(0x20000), fake(0x1000000),
+                                      fake(0x2000000), 511, 1024, 32, 8, 128, y, fake(0x4000000), 1 << 24,
+                                      nullptr) == MBQ_EALIGN);
+    CHECK(mbq_attention_decode_append(x, (float*)fake(0x10000), (float*)fake(0x20000), fake(0x1000000),
+                                      fake(0x2000000), 511, 1024, 32, 8, 128, y, fake(0x4000000),
+                                      32 * 16 * 132 * 4 - 4, nullptr) == MBQ_EINVAL);
+    CHECK(mbq_attention_decode_append(x, (float*)fake(0x1000000 + 511 * 2048), (float*)fake(0x20000),
+                                      fake(0x1000000), fake(0x2000000), 511, 1024, 32, 8, 128, y,
+                                      fake(0x4000000), 1 << 24, nullptr) == MBQ_EINVAL);
     mbq_decode_model m;
     std::memset(&m, 0, sizeof m);
     CHECK(mbq_decode_workspace_bytes(nullptr, &b) == MBQ_EINVAL);
     m.n_layers = -1;
     CHECK(mbq_decode_workspace_bytes(&m, &b) == MBQ_EINVAL);
+    // the step with attention over the caches: size queries and argument
+    // checks on a model without layers (nothing reaches a launch)
+    m.n_layers = 0;
+    m.eps = 1e-6f;
+    m.d = 4096;
+    m.dq = 4096;
+    m.dkv = 1024;
+    m.gamma_f = (const float*)fake(0x700000);
+    CHECK(mbq_decode_kv_workspace_bytes(&m, 511, &b) == MBQ_OK &&
+          b == (4096 + 2048) * 4 + 4096 * 4 + 32 * 16 * 132 * 4);
+    CHECK(mbq_decode_kv_workspace_bytes(&m, -1, &b) == MBQ_EINVAL);
+    CHECK(mbq_decode_kv_workspace_bytes(nullptr, 5, &b) == MBQ_EINVAL);
+    m.dkv = 1000;
+    CHECK(mbq_decode_kv_workspace_bytes(&m, 5, &b) == MBQ_EUNSUPPORTED);
+    m.dkv = 1024;
+    const size_t kvb = b;
+    float* hh = (float*)fake(0x8000000);
+    CHECK(mbq_decode_step_kv(&m, hh, nullptr, nullptr, nullptr, -1, 1024, fake(0x9000000), 1 << 24,
+                             nullptr) == MBQ_EINVAL);
+    CHECK(mbq_decode_step_kv(&m, (float*)fake(0x8000004), nullptr, nullptr, nullptr, 511, 1024,
+                             fake(0x9000000), 1 << 24, nullptr) == MBQ_EALIGN);
+    CHECK(mbq_decode_step_kv(&m, hh, nullptr, nullptr, nullptr, 511, 1024, fake(0x9000000), kvb - 1,
+                             nullptr) == MBQ_EINVAL);
+    CHECK(mbq_decode_step_kv(&m, hh, nullptr, nullptr, nullptr, 511, 1020, fake(0x9000000), 1 << 24,
+                             nullptr) == MBQ_EINVAL);
+    CHECK(mbq_decode_step_kv(&m, hh, nullptr, nullptr, nullptr, 511, 1028, fake(0x9000000), 1 << 24,
+                             nullptr) == MBQ_EALIGN);
+    std::memset(&m, 0, sizeof m);
     CHECK(mbq_probe_mixed(nullptr, 1024, nullptr, 1024, 5, 256, y, nullptr) == MBQ_EINVAL);
     CHECK(mbq_probe_read(fake(0), 15, y, nullptr) == MBQ_EALIGN);
     CHECK(std::strlen(mbq_status_str(MBQ_EINVAL)) > 0);
