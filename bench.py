@@ -12,18 +12,22 @@ Every other step of the hot path is measured in the same run, in the same way
 (graph replays, cold weights), under "rows":
   * RMSNorm of one 4096 row (us per row) and the bf16 512 x 4096 product;
   * M = 1 products at each decode table shape, fused forms included;
-  * small batches M = 1 .. 64 of the 12288 x 4096 Q45 table (staged x on the
-    vector units below M = 6, on the matrix cores from M = 6; fp32 x on the
-    vector units up to M = 8);
+  * small batches M = 1 .. 64 of the 12288 x 4096 Q45 table (the vector
+    units below M = 4, the matrix cores from M = 4, staged x and fp32 x),
+    the 512-token batch, and the 4096 x 12288 table with K whole and split;
   * 8 gathered Q25 experts of 1536 x 4096; LayerNorm of 4096 rows of 2048;
+  * the quantizer into each format; decode attention at 512, 4096 and 32768
+    positions;
   * one token through the 36-layer decode stream (ms per token, tokens/s,
-    against the measured read ceiling).
+    against the measured read ceiling) as a graph of launches, in one
+    launch, and with attention over 512 cached positions in every layer.
 Also: the measured ceilings (the larger of a 4 GiB read and a 2 GiB copy,
 memory latency from a pointer chase, matrix and vector issue rates), and the
 CPU oracle timed single-threaded and on every core on a bounded sample of the
 headline step (cpu_baseline); that leg also checks the GPU's headline
-products and its whole 36-layer decode token against the oracle, and the run
-fails instead of printing a line when they disagree.
+products and its whole 36-layer decode token, with and without attention,
+against the oracle, and the run fails instead of printing a line when they
+disagree.
 
 The timed region is exactly --steps steps (one replay of a graph of that
 many steps) after --warmup untimed ones.
