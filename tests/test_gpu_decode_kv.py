@@ -13,7 +13,7 @@ are still in the workspace, to numpy's conversion of them bit for bit.
 
 Cases: two full-width layers (32 query heads on 8 key/value heads of 128)
 at T = 0 (the new position alone), 37 and 600 (ragged chunks); rows wider
-than the heads; three tokens in a row growing the same caches; the step
+than the heads; one layer at 8, 2 and 1 query heads per key/value head; three tokens in a row growing the same caches; the step
 captured in a HIP graph; and the whole 36-layer model at 512 cached
 positions, the configuration the benchmark times.
 """
@@ -128,6 +128,27 @@ def test_step_kv_matches_oracle(T, pad):
     assert e_h <= 1e-4 and e_l <= 1e-4
     check_caches(to_host(kd), to_host(vd), kh, vh, kb, vb, T)
     last_layer_row_is_fp16_of_its_products(model, kd[-1], vd[-1], T)
+
+
+@pytest.mark.parametrize("dq,dkv,T", [(4096, 512, 40), (2048, 1024, 300), (4096, 4096, 9)])
+def test_step_kv_other_head_groups(dq, dkv, T):
+    """Query heads per key/value head other than the model's 4: 8 (32 on 4),
+    2 (16 on 8) and 1 (32 on 32), one layer each, caches as wide as dkv."""
+    print("decode kv dq=%d dkv=%d T=%d" % (dq, dkv, T), flush=True)
+    cfg = workloads.config3(layers=1, dq=dq, dkv=dkv, vocab=512)
+    model = model_of(cfg)
+    kh, vh = host_caches(1, T + 1, dkv, 9400 + dkv)
+    kb, vb = [c.copy() for c in kh], [c.copy() for c in vh]
+    kd, vd = to_dev(kh), to_dev(vh)
+    h, logits = run_step(model, cfg, kd, vd, T)
+    h_ref, lg_ref = oracle_token(cfg, kh, vh, T)
+    e_h, e_l = rel_l2(h, h_ref), rel_l2(logits, lg_ref)
+    print("  rel-L2 h %.2e logits %.2e" % (e_h, e_l), flush=True)
+    assert e_h <= 1e-4 and e_l <= 1e-4
+    got_k, got_v = to_host(kd), to_host(vd)
+    for got, ref, before in ((got_k[0], kh[0], kb[0]), (got_v[0], vh[0], vb[0])):
+        assert np.array_equal(got[:T].view(np.uint16), before[:T].view(np.uint16))
+        assert close_after_rounding(got[T], ref[T]).all()
 
 
 def test_three_tokens_grow_the_caches():
