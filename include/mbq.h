@@ -445,8 +445,8 @@ int mbq_attention_decode(const float* q, const void* k_cache, const void* v_cach
  * and v_cache, and the attention covers rows 0 .. T (T + 1 positions; T >= 0
  * cached positions before the call, so the caches need room for T + 1
  * rows).  One fused step: the partial launch takes the new position from
- * k_new / v_new and its owning lanes store the row; no launch reads that
- * row from the cache.  workspace: at least mbq_attention_workspace_bytes
+ * k_new / v_new and its owning lanes store the row; whatever row T held
+ * before the call is never used.  workspace: at least mbq_attention_workspace_bytes
  * for T + 1 positions.  out, the workspace and the caches' rows 0 .. T must
  * not overlap one another or q, k_new, v_new (MBQ_EINVAL); other arguments
  * and errors as for mbq_attention_decode. */
