@@ -116,6 +116,58 @@ __global__ __launch_bounds__(kBlock) void layernorm_vec_kernel(const float* x,
     }
 }
 
+// One row per wave for rows of 64 * 4 * NV values (256 ... 4096): lane l
+// holds float4s l, l + 64, ... of the row, and both statistics are wave
+// reductions (DPP), with no workgroup barrier.  gamma and beta are loaded
+// with x, so the row's single round trip covers all three.  Against one
+// workgroup per row (µs, 8.4 M values, graphs of cold launches, same run):
+// 4096 x 2048 12.65 against 14.3; rows of 256 14.2 against 29.2, of 512
+// 12.7 against 19.4, of 1024 12.6 against 14.5, of 4096 13.1 against 14.8.
+// MBQ_LN_WAVE=0 (tuning) keeps the workgroup-per-row kernels.
+template <int NV>
+__global__ __launch_bounds__(kBlock) void layernorm_wave_kernel(const float* x,
+                                                                const float* __restrict__ gamma,
+                                                                const float* __restrict__ beta,
+                                                                float eps, int n, int64_t rows,
+                                                                float* y) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t row = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+    if (row >= rows) return;                                  // the whole wave
+    const float4* xr = (const float4*)(x + row * n);
+    const float4* g4 = (const float4*)gamma;
+    const float4* b4 = (const float4*)beta;
+    float4 v[NV], g[NV], b[NV];
+#pragma unroll
+    for (int i = 0; i < NV; i++) v[i] = xr[lane + kWave * i];
+#pragma unroll
+    for (int i = 0; i < NV; i++) {
+        g[i] = g4[lane + kWave * i];
+        b[i] = b4[lane + kWave * i];
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; i++) s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+    const float mean = wave_sum_dpp(s) / (float)n;
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; i++) {
+        const float a = v[i].x - mean, c = v[i].y - mean, d = v[i].z - mean, e = v[i].w - mean;
+        q = fmaf(a, a, q);
+        q = fmaf(c, c, q);
+        q = fmaf(d, d, q);
+        q = fmaf(e, e, q);
+    }
+    const float var = wave_sum_dpp(q) / (float)n;
+    const float inv = 1.0f / sqrtf(var + eps);
+    float4* yr = (float4*)(y + row * n);
+#pragma unroll
+    for (int i = 0; i < NV; i++)
+        yr[lane + kWave * i] = make_float4(fmaf((v[i].x - mean) * inv, g[i].x, b[i].x),
+                                           fmaf((v[i].y - mean) * inv, g[i].y, b[i].y),
+                                           fmaf((v[i].z - mean) * inv, g[i].z, b[i].z),
+                                           fmaf((v[i].w - mean) * inv, g[i].w, b[i].w));
+}
+
 __global__ __launch_bounds__(kBlock) void layernorm_any_kernel(const float* x,
                                                                const float* __restrict__ gamma,
                                                                const float* __restrict__ beta,
@@ -166,8 +218,20 @@ hipError_t launch_rmsnorm(const float* x, const float* gamma, float eps, int64_t
 
 hipError_t launch_layernorm(const float* x, const float* gamma, const float* beta, float eps,
                             int64_t rows, int64_t n, float* y, hipStream_t stream) {
-    const int vec = (n % 4 == 0 && aligned16(x) && aligned16(y) && aligned16(gamma) &&
-                     aligned16(beta)) ? vec_for(n) : 0;
+    const bool al = n % 4 == 0 && aligned16(x) && aligned16(y) && aligned16(gamma) && aligned16(beta);
+    const int64_t nv = n / (4 * kWave);
+    const bool wave = al && n % (4 * kWave) == 0 && (nv == 1 || nv == 2 || nv == 4 || nv == 8 || nv == 16) &&
+                      !(tuning_var("MBQ_LN_WAVE") && atoi(tuning_var("MBQ_LN_WAVE")) == 0);
+    if (wave) {
+        const dim3 wgrid((unsigned)((rows + kWavesPerBlock - 1) / kWavesPerBlock));
+        switch (nv) {
+#define MBQ_LNW(V) case V: hipLaunchKernelGGL(layernorm_wave_kernel<V>, wgrid, dim3(kBlock), 0, stream, x, gamma, beta, eps, (int)n, rows, y); break;
+        MBQ_LNW(1) MBQ_LNW(2) MBQ_LNW(4) MBQ_LNW(8) MBQ_LNW(16)
+#undef MBQ_LNW
+        }
+        return hipGetLastError();
+    }
+    const int vec = al ? vec_for(n) : 0;
     const dim3 grid((unsigned)rows), block(kBlock);
     switch (vec) {
     case 1: hipLaunchKernelGGL(layernorm_vec_kernel<1>, grid, block, 0, stream, x, gamma, beta, eps, (int)n, y); break;
