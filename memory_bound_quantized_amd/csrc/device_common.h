@@ -75,18 +75,20 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
-// Sum over the 256 threads of a workgroup through LDS (red holds 4 floats).
-// Every thread receives the total.  Contains two barriers.
-template <int NW = kWavesPerBlock>
+// Sum over the NW waves of a workgroup: a DPP wave reduction, then the wave
+// sums through LDS (red holds NW floats), added in wave order.  Every thread
+// receives the total.  A second barrier after the read lets the caller use
+// red again; a kernel that sums once passes REUSE = false and skips it.
+template <int NW = kWavesPerBlock, bool REUSE = true>
 __device__ __forceinline__ float block_sum(float v, float* red) {
-    v = wave_sum(v);
+    v = wave_sum_dpp(v);
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     if (lane == 0) red[wave] = v;
     __syncthreads();
     float t = red[0];
 #pragma unroll
     for (int w = 1; w < NW; w++) t += red[w];
-    __syncthreads();
+    if constexpr (REUSE) __syncthreads();
     return t;
 }
 

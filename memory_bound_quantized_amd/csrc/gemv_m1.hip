@@ -214,7 +214,7 @@ __global__ __launch_bounds__(kBlock * k_slices(CS)) void gemv_m1_kernel(DevPlane
                 ss = wave_sum_dpp(ss);
                 if (lane == 0) red[wid] = ss;
             } else {
-                inv = 1.0f / sqrtf(block_sum<kWavesPerBlock * S>(ss, red) / (float)K + eps);
+                inv = 1.0f / sqrtf(block_sum<kWavesPerBlock * S, false>(ss, red) / (float)K + eps);
             }
             const float sx = DEFER ? 1.0f : inv;
 #pragma unroll

@@ -41,7 +41,7 @@ __global__ __launch_bounds__(BT) void rmsnorm_vec_kernel(const float* x,
         ss = fmaf(v[i].z, v[i].z, ss);
         ss = fmaf(v[i].w, v[i].w, ss);
     }
-    const float tot = block_sum<BT / kWave>(ss, red);
+    const float tot = block_sum<BT / kWave, false>(ss, red);
     const float inv = 1.0f / sqrtf(tot / (float)n + eps);
     float4* yr = (float4*)(y + row * n);
 #pragma unroll
@@ -62,7 +62,7 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_any_kernel(const float* x,
     const float* xr = x + row * n;
     float ss = 0.f;
     for (int64_t i = threadIdx.x; i < n; i += kBlock) ss = fmaf(xr[i], xr[i], ss);
-    const float tot = block_sum(ss, red);
+    const float tot = block_sum<kWavesPerBlock, false>(ss, red);
     const float inv = 1.0f / sqrtf(tot / (float)n + eps);
     float* yr = y + row * n;
     for (int64_t i = threadIdx.x; i < n; i += kBlock) yr[i] = gamma[i] * (xr[i] * inv);
@@ -98,7 +98,7 @@ __global__ __launch_bounds__(kBlock) void layernorm_vec_kernel(const float* x,
             q = fmaf(d, d, q);
         }
     }
-    const float var = block_sum(q, red) / (float)n;
+    const float var = block_sum<kWavesPerBlock, false>(q, red) / (float)n;
     const float inv = 1.0f / sqrtf(var + eps);
     float4* yr = (float4*)(y + row * n);
     const float4* g4 = (const float4*)gamma;
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(kBlock) void layernorm_any_kernel(const float* x,
         const float a = xr[i] - mean;
         q = fmaf(a, a, q);
     }
-    const float inv = 1.0f / sqrtf(block_sum(q, red) / (float)n + eps);
+    const float inv = 1.0f / sqrtf(block_sum<kWavesPerBlock, false>(q, red) / (float)n + eps);
     float* yr = y + row * n;
     for (int64_t i = threadIdx.x; i < n; i += kBlock)
         yr[i] = fmaf((xr[i] - mean) * inv, gamma[i], beta[i]);

@@ -84,7 +84,7 @@ __global__ __launch_bounds__(BT) void rmsnorm_xq_kernel(const float* x,
         ss = fmaf(v[i].z, v[i].z, ss);
         ss = fmaf(v[i].w, v[i].w, ss);
     }
-    const float tot = block_sum<BT / kWave>(ss, red);
+    const float tot = block_sum<BT / kWave, false>(ss, red);
     const float inv = 1.0f / sqrtf(tot / (float)n + eps);
 #pragma unroll
     for (int i = 0; i < VEC; i++) {
