@@ -40,10 +40,24 @@ __device__ __forceinline__ float row_sum16(float v) {
     return v;
 }
 
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_max(float v) {
+    // lanes of rows outside ROW_MASK keep their own value (old = v)
+    const int s = __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v),
+                                              CTRL, ROW_MASK, 0xF, false);
+    return fmaxf(v, __builtin_bit_cast(float, s));
+}
+
+// Maximum over the 64 lanes with DPP row operations (the pattern of
+// wave_sum_dpp); the result is wave-uniform (read from lane 63).
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-    return v;
+    v = dpp_max<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]
+    v = dpp_max<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]
+    v = dpp_max<0x141, 0xF>(v);   // row_half_mirror
+    v = dpp_max<0x140, 0xF>(v);   // row_mirror
+    v = dpp_max<0x142, 0xA>(v);   // row_bcast:15 into rows 1, 3
+    v = dpp_max<0x143, 0xC>(v);   // row_bcast:31 into rows 2, 3
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 // The 8 halves of a 16-byte load as floats (exact).
@@ -233,7 +247,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const float* __r
             sc[h * C + t] = e;
             l += e;
         }
-        l = wave_sum(l);
+        l = wave_sum_dpp(l);
         if (lane == 0) {
             mls[2 * h] = m;
             mls[2 * h + 1] = l;
@@ -347,7 +361,7 @@ __global__ __launch_bounds__(kAttD) void attn_combine_kernel(const float* __rest
         }
         __syncthreads();                               // fs and red are rewritten next
     }
-    L = wave_sum(L);
+    L = wave_sum_dpp(L);
     if ((t & (kWave - 1)) == 0) red[t / kWave] = L;
     __syncthreads();
     L = red[0];
