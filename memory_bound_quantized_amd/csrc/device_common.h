@@ -55,6 +55,29 @@ __device__ __forceinline__ float dpp_add(float v) {
     return v + __builtin_bit_cast(float, s);
 }
 
+// Lane exchanges by DPP (a vector move, no LDS traffic).  Every lane of the
+// group involved must be active.
+template <int CTRL>
+__device__ __forceinline__ int dpp_mov(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ int lane_xor1(int v) { return dpp_mov<0xB1>(v); }      // quad_perm [1,0,3,2]
+__device__ __forceinline__ int lane_xor2(int v) { return dpp_mov<0x4E>(v); }      // quad_perm [2,3,0,1]
+__device__ __forceinline__ int lane_mirror8(int v) { return dpp_mov<0x141>(v); }  // lane 7 - i of 8
+__device__ __forceinline__ int lane_mirror16(int v) { return dpp_mov<0x140>(v); } // lane 15 - i of 16
+__device__ __forceinline__ float lane_xor1(float v) {
+    return __builtin_bit_cast(float, lane_xor1(__builtin_bit_cast(int, v)));
+}
+__device__ __forceinline__ float lane_xor2(float v) {
+    return __builtin_bit_cast(float, lane_xor2(__builtin_bit_cast(int, v)));
+}
+__device__ __forceinline__ float lane_mirror8(float v) {
+    return __builtin_bit_cast(float, lane_mirror8(__builtin_bit_cast(int, v)));
+}
+__device__ __forceinline__ float lane_mirror16(float v) {
+    return __builtin_bit_cast(float, lane_mirror16(__builtin_bit_cast(int, v)));
+}
+
 // Sum over the 64 lanes of a wave with DPP row operations; the total is
 // returned as a wave-uniform value (read from lane 63).
 __device__ __forceinline__ float wave_sum_dpp(float v) {

@@ -69,8 +69,8 @@ struct XConv {
 __device__ __forceinline__ XConv convert_item(f4g a, f4g b) {
     float amax = fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
                        fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
-    amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
-    amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
+    amax = fmaxf(amax, lane_xor1(amax));
+    amax = fmaxf(amax, lane_xor2(amax));
     // 2^e puts the largest |x| into [2^14, 2^15); e within the normal range
     int e = 141 - (int)((__builtin_bit_cast(uint32_t, amax) >> 23) & 0xFFu);
     e = e > 126 ? 126 : (e < -126 ? -126 : e);

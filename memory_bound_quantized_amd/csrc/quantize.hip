@@ -92,8 +92,8 @@ __global__ __launch_bounds__(kBlock) void quantize_kernel(const float* __restric
     if constexpr (FMT == kQ45 || FMT == kQ25) {
         constexpr float QMAX = FMT == kQ45 ? 7.0f : 1.0f;
         constexpr int OFF = FMT == kQ45 ? 8 : 2, TOP = FMT == kQ45 ? 15 : 3;
-        m = fmaxf(m, __shfl_xor(m, 1, kWave));
-        m = fmaxf(m, __shfl_xor(m, 2, kWave));
+        m = fmaxf(m, lane_xor1(m));
+        m = fmaxf(m, lane_xor2(m));
         const float s = half_sat(m / QMAX);
         int q[8];
         const float sd = s != 0.f ? s : 1.0f;         // s = 0: every code is the offset
@@ -119,10 +119,14 @@ __global__ __launch_bounds__(kBlock) void quantize_kernel(const float* __restric
         }
         if (g == 0) *(uint16_t*)((uint8_t*)out.p2 + 2 * (row * (K / 32) + b)) = half_bits(s);
     } else {   // Q65
-        const float a = fmaxf(m, __shfl_xor(m, 1, kWave)) / 31.0f;   // this sub-block's a_j
-        float amx = a;
-#pragma unroll
-        for (int o = 2; o <= 16; o <<= 1) amx = fmaxf(amx, __shfl_xor(amx, o, kWave));
+        const float a = fmaxf(m, lane_xor1(m)) / 31.0f;   // this sub-block's a_j
+        // the maximum over the super-block's 32 lanes: quads, eights and
+        // sixteens by DPP (a mirror pairs each half with the other one),
+        // then the two halves of the 32
+        float amx = fmaxf(a, lane_xor2(a));
+        amx = fmaxf(amx, lane_mirror8(amx));
+        amx = fmaxf(amx, lane_mirror16(amx));
+        amx = fmaxf(amx, __shfl_xor(amx, 16, kWave));
         const float d = half_sat(amx / 127.0f);
         int sc = 0;
         if (d != 0.f) {
@@ -146,7 +150,7 @@ __global__ __launch_bounds__(kBlock) void quantize_kernel(const float* __restric
             lo |= (uint32_t)(q[i] & 15) << (4 * i);
             hi |= (uint32_t)(q[i] >> 4) << kQ65HiPos[8 * part + i];
         }
-        hi |= (uint32_t)__shfl_xor((int)hi, 1, kWave);
+        hi |= (uint32_t)lane_xor1((int)hi);
         if (!ok) return;
         *(uint32_t*)(p0 + (row * K + k0) / 2) = lo;
         if (part == 0) {

@@ -101,10 +101,10 @@ __device__ __forceinline__ void stage_group(const float* v, int og, bool ok, con
         float amax = 0.f;
 #pragma unroll
         for (int k = 0; k < GX; k++) amax = fmaxf(amax, fabsf(v[k]));
-        amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
-        if constexpr (!TWO) amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
+        amax = fmaxf(amax, lane_xor1(amax));
+        if constexpr (!TWO) amax = fmaxf(amax, lane_xor2(amax));
         const int e = chunk_exp(amax);
-        const int e_hi = TWO ? __shfl_xor(e, 2, kWave) : e;   // the second block's, in groups 0, 1
+        const int e_hi = TWO ? lane_xor2(e) : e;              // the second block's, in groups 0, 1
         const float up = pow2f(e);
         int32_t n[GX];
 #pragma unroll
@@ -129,8 +129,8 @@ __device__ __forceinline__ void stage_group(const float* v, int og, bool ok, con
         int32_t B01[3], B23[3];
 #pragma unroll
         for (int p = 0; p < 3; p++) {
-            B01[p] = S[p] + __shfl_xor(S[p], 1, kWave);     // groups 0+1 (or 2+3)
-            B23[p] = __shfl_xor(B01[p], 2, kWave);         // the other pair
+            B01[p] = S[p] + lane_xor1(S[p]);               // groups 0+1 (or 2+3)
+            B23[p] = lane_xor2(B01[p]);                    // the other pair
         }
         if (ok) {
             uint32_t* o = dst.at(b, 3 * NV * gi);            // 8-byte aligned
