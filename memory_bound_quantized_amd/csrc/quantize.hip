@@ -38,6 +38,12 @@ __device__ __forceinline__ float half_sat(float t) {
 __device__ __forceinline__ uint16_t half_bits(float v) {
     return __builtin_bit_cast(uint16_t, (_Float16)v);   // v is a half already
 }
+// v, through an empty asm: without it the compiler folds a lane swap of a
+// value with itself into two equal results and drops the exchange.
+static __device__ __forceinline__ uint32_t distinct_copy(uint32_t v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
 
 // rint(v / s) with v / s the correctly rounded fp32 quotient, for s > 0 with
 // 1/s a normal float (r = v_rcp_f32(s), within 1 ulp of 1/s).  t = v r is
@@ -122,11 +128,18 @@ __global__ __launch_bounds__(kBlock) void quantize_kernel(const float* __restric
         const float a = fmaxf(m, lane_xor1(m)) / 31.0f;   // this sub-block's a_j
         // the maximum over the super-block's 32 lanes: quads, eights and
         // sixteens by DPP (a mirror pairs each half with the other one),
-        // then the two halves of the 32
+        // then the two halves of the 32 (rows 2i and 2i + 1 of the wave) by
+        // a row swap of the value with itself, which hands each lane its
+        // partner's value; that maximum is taken on the bits (the same
+        // order for non-negative floats)
         float amx = fmaxf(a, lane_xor2(a));
         amx = fmaxf(amx, lane_mirror8(amx));
         amx = fmaxf(amx, lane_mirror16(amx));
-        amx = fmaxf(amx, __shfl_xor(amx, 16, kWave));
+        {
+            const uint32_t b = __builtin_bit_cast(uint32_t, amx);
+            auto h = __builtin_amdgcn_permlane16_swap(b, distinct_copy(b), false, false);
+            amx = __builtin_bit_cast(float, h[0] > h[1] ? h[0] : h[1]);
+        }
         const float d = half_sat(amx / 127.0f);
         int sc = 0;
         if (d != 0.f) {
